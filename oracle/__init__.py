@@ -1,0 +1,161 @@
+"""fp64 CPU oracle of the multi-head TTT layer.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only users.  The product package never
+imports this module, and this module never imports the product package: the
+two share no code.  Callers hand in the exact (already quantised) inputs as
+arrays; they are widened to float64 here and every result is float64.
+
+The arithmetic lives in ``ttt_oracle.c`` (plain loops, OpenMP over
+independent slices), whose header lists the passages of the pages each
+function follows and the readings taken where the pages are silent.
+
+Every function below is pinned by the ``-m "not gpu"`` tests in
+``tests/test_oracle_*.py`` against closed forms, finite differences,
+brute-force im2col gradients and the pages' worked example.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ttt_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libttt_oracle.so")
+_lib = None
+
+FORWARD_BACKWARD_AVG = 0
+FORWARD_ONLY = 1
+BACKWARD_ONLY = 2
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, OpenMP)."""
+    if not force and os.path.exists(_LIB_PATH) and \
+            os.path.getmtime(_LIB_PATH) >= os.path.getmtime(_SRC):
+        return _LIB_PATH
+    tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"]
+    subprocess.check_call(cmd)
+    os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        lib.oracle_linear_fullbatch.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_dwconv3x3_fullbatch.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_minibatch.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_fullbatch_bwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                                    dp, dp, dp, dp, dp, i]
+        lib.oracle_num_chunks.argtypes = [i, i]
+        lib.oracle_max_threads.argtypes = []
+        for f in (lib.oracle_linear_fullbatch, lib.oracle_dwconv3x3_fullbatch,
+                  lib.oracle_linear_minibatch, lib.oracle_linear_fullbatch_bwd,
+                  lib.oracle_num_chunks, lib.oracle_max_threads):
+            f.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+    return a
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _check(rc, name):
+    if rc != 0:
+        raise ValueError("oracle %s rejected its arguments" % name)
+
+
+def max_threads() -> int:
+    return int(_load().oracle_max_threads())
+
+
+def num_chunks(N: int, b: int) -> int:
+    """Mini-batches per scan direction: ceil(N / b)."""
+    rc = _load().oracle_num_chunks(int(N), int(b))
+    if rc < 0:
+        raise ValueError("bad N or b")
+    return rc
+
+
+def linear_fullbatch(K, Q, V, W0, eta, threads: int = 0):
+    """One full-batch L2 step of the linear inner model, then z = W1 q.
+
+    K, Q, V: [B,H,N,d]; W0: [H,d,d]; eta: [H].  Returns (Z, G) in float64,
+    Z: [B,H,N,d], G: [B,H,d,d] (the full-batch gradient at W0).
+    """
+    K, Q, V, W0, eta = map(_f64, (K, Q, V, W0, eta))
+    B, H, N, d = K.shape
+    Z = np.empty_like(K)
+    G = np.empty((B, H, d, d))
+    _check(_load().oracle_linear_fullbatch(B, H, N, d, _p(K), _p(Q), _p(V), _p(W0), _p(eta),
+                                           _p(Z), _p(G), int(threads)), "linear_fullbatch")
+    return Z, G
+
+
+def dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, threads: int = 0):
+    """One full-batch L2 step of the depthwise 3x3 inner model, then apply.
+
+    K, Q, V: [B,H,N,d] with N = grid_h*grid_w (row-major grid); w0: [H,d,3,3];
+    eta: [H].  Returns (Z, g): Z [B,H,N,d], g [B,H,d,3,3].
+    """
+    K, Q, V, w0, eta = map(_f64, (K, Q, V, w0, eta))
+    B, H, N, d = K.shape
+    if grid_h * grid_w != N:
+        raise ValueError("grid_h*grid_w != N")
+    Z = np.empty_like(K)
+    g = np.empty((B, H, d, 3, 3))
+    _check(_load().oracle_dwconv3x3_fullbatch(B, H, grid_h, grid_w, d, _p(K), _p(Q), _p(V),
+                                              _p(w0), _p(eta), _p(Z), _p(g), int(threads)),
+           "dwconv3x3_fullbatch")
+    return Z, g
+
+
+def linear_minibatch(K, Q, V, W0, eta, minibatch: int, mode: int = FORWARD_BACKWARD_AVG,
+                     threads: int = 0):
+    """Causal mini-batch scans of the linear inner model.
+
+    mode 0 averages the forward scan and the reverse scan (mapped back to
+    token positions); 1 and 2 return one direction.  Returns Z [B,H,N,d].
+    """
+    K, Q, V, W0, eta = map(_f64, (K, Q, V, W0, eta))
+    B, H, N, d = K.shape
+    Z = np.empty_like(K)
+    _check(_load().oracle_linear_minibatch(B, H, N, d, int(minibatch), int(mode), _p(K), _p(Q),
+                                           _p(V), _p(W0), _p(eta), _p(Z), int(threads)),
+           "linear_minibatch")
+    return Z
+
+
+def linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, threads: int = 0):
+    """Gradients of sum(dZ * Z) through the full-batch linear layer.
+
+    Returns (dK, dQ, dV, dW0, deta); dW0 [H,d,d] and deta [H] are summed over
+    the batch.
+    """
+    K, Q, V, W0, eta, dZ = map(_f64, (K, Q, V, W0, eta, dZ))
+    B, H, N, d = K.shape
+    dK = np.empty_like(K)
+    dQ = np.empty_like(K)
+    dV = np.empty_like(K)
+    dW0 = np.empty((H, d, d))
+    deta = np.empty((H,))
+    _check(_load().oracle_linear_fullbatch_bwd(B, H, N, d, _p(K), _p(Q), _p(V), _p(W0), _p(eta),
+                                               _p(dZ), _p(dK), _p(dQ), _p(dV), _p(dW0),
+                                               _p(deta), int(threads)), "linear_fullbatch_bwd")
+    return dK, dQ, dV, dW0, deta
