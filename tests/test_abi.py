@@ -1,0 +1,222 @@
+"""The C-ABI library on the host, no GPU: it loads, exports every symbol
+include/ttt.h declares, sizes workspaces, and rejects each class of bad
+argument with its status code before any HIP call (fake device addresses
+are never dereferenced on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import vision_test_sequence_amd as vt
+from vision_test_sequence_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ttt.h")
+
+MB = 1 << 20
+BASE = 0x7f0000000000  # fake, 16-byte aligned device addresses, 64 MiB apart
+
+
+def addr(i):
+    return BASE + i * 64 * MB
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:ttt_status|size_t|const char\*)\s+(ttt_\w+)\s*\(", txt, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for f in ("ttt_linear_fullbatch", "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir",
+              "ttt_linear_fullbatch_bwd", "ttt_workspace_size", "ttt_status_string"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = vt.lib()
+    for f in declared_functions():
+        assert hasattr(L, f), f
+    out = subprocess.run(["nm", "-D", "--defined-only", vt.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (ttt_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def test_status_strings():
+    L = vt.lib()
+    for i, n in enumerate(bd.STATUS_NAMES):
+        assert L.ttt_status_string(i).decode() == n
+
+
+def P(B=2, H=3, N=100, d=64, dtype=bd.TTT_BF16, gh=10, gw=10, b=16, mode=0):
+    return bd.Problem(B, H, N, d, dtype, gh, gw, b, mode)
+
+
+def V(i, B=2, H=3, N=100, d=64):
+    return bd.View(addr(i), H * N * d, N * d, d)
+
+
+def lin(p, K=None, Q=None, Vv=None, W0=addr(10), eta=addr(11), Z=None, saved=None,
+        ws=None, wsb=None):
+    L = vt.lib()
+    K = K or V(0, p.B, p.H, p.N)
+    Q = Q or V(1, p.B, p.H, p.N)
+    Vv = Vv or V(2, p.B, p.H, p.N)
+    Z = Z or V(3, p.B, p.H, p.N)
+    need = L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p))
+    if ws is None:
+        ws = addr(20) if need else None
+    if wsb is None:
+        wsb = need
+    return L.ttt_linear_fullbatch(ctypes.byref(p), K, Q, Vv, W0, eta, Z, saved, ws, wsb, None)
+
+
+def test_workspace_sizes():
+    L = vt.lib()
+    ws = lambda op, p: L.ttt_workspace_size(op, ctypes.byref(p))
+    # large single slice is split over workgroups: it needs partials
+    assert ws(bd.OP_LINEAR_FULLBATCH, P(B=8, H=2, N=6084)) > 0
+    # many short slices run one workgroup each: no workspace
+    assert ws(bd.OP_LINEAR_FULLBATCH, P(B=128, H=2, N=196)) == 0
+    assert ws(bd.OP_LINEAR_FULLBATCH, P(N=0)) == 0
+    assert ws(bd.OP_LINEAR_FULLBATCH, P(d=32)) == 0
+    assert ws(bd.OP_DWCONV3X3_FULLBATCH, P(N=99)) == 0  # grid mismatch
+    assert L.ttt_workspace_size(0, None) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(N=0), "TTT_ERR_BAD_SHAPE"),
+    (dict(N=-5), "TTT_ERR_BAD_SHAPE"),
+    (dict(B=-1), "TTT_ERR_BAD_SHAPE"),
+    (dict(d=0), "TTT_ERR_BAD_SHAPE"),
+    (dict(d=32), "TTT_ERR_UNSUPPORTED"),
+    (dict(dtype=7), "TTT_ERR_UNSUPPORTED"),
+])
+def test_linear_shape_errors(kw, code):
+    assert bd.STATUS_NAMES[lin(P(**kw))] == code
+
+
+def test_empty_batch_is_ok_without_launch():
+    assert lin(P(B=0)) == 0
+    assert lin(P(H=0)) == 0
+
+
+def test_null_pointers():
+    L = vt.lib()
+    p = P()
+    assert bd.STATUS_NAMES[L.ttt_linear_fullbatch(None, V(0), V(1), V(2), addr(10), addr(11), V(3),
+                                                  None, None, 0, None)] == "TTT_ERR_NULL_POINTER"
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(None, 1, 1, 64))] == "TTT_ERR_NULL_POINTER"
+    assert bd.STATUS_NAMES[lin(p, W0=None)] == "TTT_ERR_NULL_POINTER"
+    assert bd.STATUS_NAMES[lin(p, eta=None)] == "TTT_ERR_NULL_POINTER"
+
+
+def test_bad_strides():
+    p = P()
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(addr(0), -64, 6400, 64))] == "TTT_ERR_BAD_STRIDE"
+    # two tokens on top of each other
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(addr(0), 3 * 100 * 64, 100 * 64, 32))] == "TTT_ERR_BAD_STRIDE"
+    # heads overlapping
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(addr(0), 3 * 100 * 64, 50 * 64, 64))] == "TTT_ERR_BAD_STRIDE"
+    # token-major [B,N,H,d] is fine
+    assert lin(P(B=0), K=bd.View(addr(0), 100 * 3 * 64, 64, 3 * 64)) == 0
+
+
+def test_misalignment():
+    p = P()
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(addr(0) + 8, 3 * 100 * 64, 100 * 64, 64))] == "TTT_ERR_MISALIGNED"
+    assert bd.STATUS_NAMES[lin(p, K=bd.View(addr(0), 3 * 100 * 72, 100 * 72, 68))] == "TTT_ERR_MISALIGNED"
+    assert bd.STATUS_NAMES[lin(p, W0=addr(10) + 4)] == "TTT_ERR_MISALIGNED"
+    assert bd.STATUS_NAMES[lin(p, eta=addr(11) + 2)] == "TTT_ERR_MISALIGNED"
+
+
+def test_aliasing():
+    p = P()
+    # Z on top of K
+    assert bd.STATUS_NAMES[lin(p, Z=V(0))] == "TTT_ERR_ALIASING"
+    # saved overlapping Z
+    assert bd.STATUS_NAMES[lin(p, saved=addr(3) + 4096)] == "TTT_ERR_ALIASING"
+    # saved overlapping W0
+    assert bd.STATUS_NAMES[lin(p, saved=addr(10))] == "TTT_ERR_ALIASING"
+
+
+def test_q_may_alias_k():
+    # only checks validation passes up to the workspace test
+    p = P(B=8, H=2, N=6084)
+    assert bd.STATUS_NAMES[lin(p, K=V(0, 8, 2, 6084), Q=V(0, 8, 2, 6084), wsb=0)] == \
+        "TTT_ERR_WORKSPACE_TOO_SMALL"
+
+
+def test_workspace_errors():
+    p = P(B=8, H=2, N=6084)
+    assert bd.STATUS_NAMES[lin(p, wsb=100)] == "TTT_ERR_WORKSPACE_TOO_SMALL"
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p))
+    assert bd.STATUS_NAMES[lin(p, ws=0, wsb=need)] == "TTT_ERR_NULL_POINTER"
+    # workspace overlapping an input
+    assert bd.STATUS_NAMES[lin(p, ws=addr(0), wsb=need)] == "TTT_ERR_ALIASING"
+
+
+def conv(p, **kw):
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_DWCONV3X3_FULLBATCH, ctypes.byref(p))
+    return L.ttt_dwconv3x3_fullbatch(ctypes.byref(p), V(0, p.B, p.H, p.N), V(1, p.B, p.H, p.N),
+                                     V(2, p.B, p.H, p.N), kw.get("w0", addr(10)), addr(11),
+                                     kw.get("Z", V(3, p.B, p.H, p.N)), kw.get("saved"),
+                                     addr(20) if need else None, kw.get("wsb", need), None)
+
+
+def test_conv_errors():
+    assert bd.STATUS_NAMES[conv(P(gh=9, gw=10))] == "TTT_ERR_BAD_SHAPE"
+    assert bd.STATUS_NAMES[conv(P(gh=0, gw=10))] == "TTT_ERR_BAD_SHAPE"
+    assert bd.STATUS_NAMES[conv(P(), w0=None)] == "TTT_ERR_NULL_POINTER"
+    assert bd.STATUS_NAMES[conv(P(), Z=V(1))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[conv(P(), saved=addr(2))] == "TTT_ERR_ALIASING"
+    assert conv(P(B=0)) == 0
+
+
+def scan(p, **kw):
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(p))
+    return L.ttt_linear_minibatch_bidir(ctypes.byref(p), V(0, p.B, p.H, p.N), V(1, p.B, p.H, p.N),
+                                        V(2, p.B, p.H, p.N), addr(10), addr(11),
+                                        kw.get("Z", V(3, p.B, p.H, p.N)),
+                                        addr(20) if need else None, kw.get("wsb", need), None)
+
+
+def test_scan_errors():
+    assert bd.STATUS_NAMES[scan(P(b=0))] == "TTT_ERR_BAD_SHAPE"
+    assert bd.STATUS_NAMES[scan(P(b=17))] == "TTT_ERR_UNSUPPORTED"
+    assert bd.STATUS_NAMES[scan(P(mode=3))] == "TTT_ERR_UNSUPPORTED"
+    assert bd.STATUS_NAMES[scan(P(), Z=V(2))] == "TTT_ERR_ALIASING"
+    assert scan(P(B=0)) == 0
+
+
+def bwd(p, **kw):
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH_BWD, ctypes.byref(p))
+    g = lambda n, i: kw.get(n, V(i, p.B, p.H, p.N))
+    return L.ttt_linear_fullbatch_bwd(ctypes.byref(p), g("K", 0), g("Q", 1), g("V", 2), addr(10),
+                                      addr(11), g("dZ", 4), kw.get("saved"), g("dK", 5), g("dQ", 6),
+                                      g("dV", 7), kw.get("dW0", addr(12)), kw.get("deta", addr(13)),
+                                      addr(20) if need else None, kw.get("wsb", need), None)
+
+
+def test_bwd_errors():
+    assert bd.STATUS_NAMES[bwd(P(N=0))] == "TTT_ERR_BAD_SHAPE"
+    assert bd.STATUS_NAMES[bwd(P(), dK=V(0))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[bwd(P(), dQ=V(5))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[bwd(P(), dW0=addr(10))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[bwd(P(), dW0=None)] == "TTT_ERR_NULL_POINTER"
+    assert bd.STATUS_NAMES[bwd(P(), saved=addr(7))] == "TTT_ERR_ALIASING"
+    assert bwd(P(B=0)) == 0
+
+
+def test_python_binding_rejects_bad_params_before_the_library():
+    import torch
+    K = torch.zeros(1, 1, 16, 64)
+    with pytest.raises(ValueError):
+        vt.ttt_linear_fullbatch(K, K, K, torch.zeros(1, 64, 32), torch.ones(1))

@@ -1,0 +1,21 @@
+"""MI355X (gfx950) multi-head test-time-training layer.
+
+The compute lives in ``libttt.so`` (hand-written HIP kernels behind the C ABI
+of ``include/ttt.h``); ``binding`` marshals torch tensors into that ABI and
+nothing else.  There is no CPU fallback: calling an entry point without the
+built library or without a GPU raises.
+"""
+from .binding import (  # noqa: F401
+    TTT_BF16,
+    TTT_F32,
+    TTTError,
+    BIDIR_AVG,
+    FORWARD_ONLY,
+    BACKWARD_ONLY,
+    lib,
+    library_path,
+    ttt_dwconv3x3_fullbatch,
+    ttt_linear_fullbatch,
+    ttt_linear_fullbatch_bwd,
+    ttt_linear_minibatch_bidir,
+)

@@ -1,0 +1,238 @@
+"""ctypes binding of libttt.so (include/ttt.h).
+
+Argument marshalling only: torch tensors are turned into device pointers,
+element strides and the current HIP stream; the workspace is a zero-filled
+torch byte tensor kept per (device, op).  Every step of the layer runs in
+the library's HIP kernels.  A missing library raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Dict, Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libttt.so")
+
+TTT_F32 = 0
+TTT_BF16 = 1
+BIDIR_AVG = 0
+FORWARD_ONLY = 1
+BACKWARD_ONLY = 2
+OP_LINEAR_FULLBATCH = 0
+OP_DWCONV3X3_FULLBATCH = 1
+OP_LINEAR_MINIBATCH_BIDIR = 2
+OP_LINEAR_FULLBATCH_BWD = 3
+
+STATUS_NAMES = [
+    "TTT_OK", "TTT_ERR_NULL_POINTER", "TTT_ERR_BAD_SHAPE", "TTT_ERR_BAD_STRIDE",
+    "TTT_ERR_MISALIGNED", "TTT_ERR_UNSUPPORTED", "TTT_ERR_ALIASING",
+    "TTT_ERR_WORKSPACE_TOO_SMALL", "TTT_ERR_HIP",
+]
+
+EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_linear_fullbatch",
+            "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd")
+
+
+class TTTError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        name = STATUS_NAMES[status] if 0 <= status < len(STATUS_NAMES) else str(status)
+        super().__init__(f"{where}: {name}")
+        self.name = name
+
+
+class View(ctypes.Structure):
+    _fields_ = [("ptr", ctypes.c_void_p), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("d", ctypes.c_int32), ("dtype", ctypes.c_int), ("grid_h", ctypes.c_int32),
+                ("grid_w", ctypes.c_int32), ("minibatch", ctypes.c_int32), ("mode", ctypes.c_int)]
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded libttt.so with argument types declared (raises if not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH):
+                raise RuntimeError(
+                    f"{_LIB_PATH} is missing: build it with `python -m vision_test_sequence_amd.build`"
+                    " (there is no CPU fallback)")
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, sz, fp = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+            P = ctypes.POINTER(Problem)
+            L.ttt_workspace_size.argtypes = [ctypes.c_int, P]
+            L.ttt_workspace_size.restype = sz
+            L.ttt_status_string.argtypes = [ctypes.c_int]
+            L.ttt_status_string.restype = ctypes.c_char_p
+            L.ttt_linear_fullbatch.argtypes = [P, View, View, View, fp, fp, View, fp, vp, sz, vp]
+            L.ttt_dwconv3x3_fullbatch.argtypes = [P, View, View, View, fp, fp, View, fp, vp, sz, vp]
+            L.ttt_linear_minibatch_bidir.argtypes = [P, View, View, View, fp, fp, View, vp, sz, vp]
+            L.ttt_linear_fullbatch_bwd.argtypes = [P, View, View, View, fp, fp, View, fp, View, View,
+                                                   View, fp, fp, vp, sz, vp]
+            for f in EXPORTED[2:]:
+                getattr(L, f).restype = ctypes.c_int
+            _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------ marshalling --
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TTT_F32
+    if t.dtype == torch.bfloat16:
+        return TTT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def view(t: torch.Tensor) -> View:
+    if t.dim() != 4:
+        raise ValueError("views are [B,H,N,d] tensors")
+    if t.stride(3) != 1 and t.shape[3] > 1:
+        raise ValueError("the d channels of a view must be contiguous")
+    s = t.stride()
+    return View(t.data_ptr(), s[0], s[1], s[2])
+
+
+def problem(K: torch.Tensor, grid: Tuple[int, int] = (0, 0), minibatch: int = 0,
+            mode: int = BIDIR_AVG) -> Problem:
+    B, H, N, d = K.shape
+    return Problem(B, H, N, d, _dtype_code(K), grid[0], grid[1], minibatch, mode)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+
+
+def workspace(op: int, prob: Problem, device: torch.device) -> Tuple[Optional[int], int]:
+    """Zero-filled scratch for `op`, cached per (device, op); grows on demand.
+    The library leaves its counters at zero after every call, so one buffer
+    serves consecutive calls of that op on one stream."""
+    need = int(lib().ttt_workspace_size(op, ctypes.byref(prob)))
+    if need == 0:
+        return None, 0
+    key = (device.index if device.index is not None else torch.cuda.current_device(), op)
+    buf = _ws.get(key)
+    if buf is None or buf.numel() < need:
+        buf = torch.zeros(need, dtype=torch.uint8, device=device)
+        _ws[key] = buf
+    return buf.data_ptr(), buf.numel()
+
+
+def _check(st: int, where: str) -> None:
+    if st != 0:
+        raise TTTError(st, where)
+
+
+def _param(t: torch.Tensor, shape, name: str) -> torch.Tensor:
+    if t.dtype != torch.float32 or tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 tensor of shape {tuple(shape)}")
+    return t
+
+
+# ------------------------------------------------------------ entry points --
+def ttt_linear_fullbatch(K, Q, V, W0, eta, *, Z=None, saved=None):
+    """One full-batch L2 step of the linear inner model, then Z = W1 q per token.
+
+    K, Q, V: [B,H,N,64] float32/bfloat16 on the GPU; W0 [H,64,64] and eta [H]
+    float32.  Z (optional) receives the output; saved (optional, float32
+    [B,H,2,64,64]) receives A then G per slice.  Returns Z.
+    """
+    B, H, N, d = K.shape
+    _param(W0, (H, d, d), "W0")
+    _param(eta, (H,), "eta")
+    if Z is None:
+        Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    p = problem(K)
+    ws, wsb = workspace(OP_LINEAR_FULLBATCH, p, K.device)
+    st = lib().ttt_linear_fullbatch(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
+                                    eta.data_ptr(), view(Z), _ptr(saved), ws, wsb,
+                                    _stream(K.device))
+    _check(st, "ttt_linear_fullbatch")
+    return Z
+
+
+def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=None, saved=None):
+    """One full-batch L2 step of the 3x3 depthwise-conv inner model, then apply.
+
+    Tokens form a row-major grid_h x grid_w map.  w0 [H,64,3,3], eta [H]
+    float32; saved (optional, float32 [B,H,64,3,3]) receives g.  Returns Z.
+    """
+    B, H, N, d = K.shape
+    _param(w0, (H, d, 3, 3), "w0")
+    _param(eta, (H,), "eta")
+    if Z is None:
+        Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    p = problem(K, grid=(grid_h, grid_w))
+    ws, wsb = workspace(OP_DWCONV3X3_FULLBATCH, p, K.device)
+    st = lib().ttt_dwconv3x3_fullbatch(ctypes.byref(p), view(K), view(Q), view(V), w0.data_ptr(),
+                                       eta.data_ptr(), view(Z), _ptr(saved), ws, wsb,
+                                       _stream(K.device))
+    _check(st, "ttt_dwconv3x3_fullbatch")
+    return Z
+
+
+def ttt_linear_minibatch_bidir(K, Q, V, W0, eta, minibatch: int, mode: int = BIDIR_AVG, *, Z=None):
+    """Causal mini-batch scans (forward, reverse or their average). Returns Z."""
+    B, H, N, d = K.shape
+    _param(W0, (H, d, d), "W0")
+    _param(eta, (H,), "eta")
+    if Z is None:
+        Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    p = problem(K, minibatch=minibatch, mode=mode)
+    ws, wsb = workspace(OP_LINEAR_MINIBATCH_BIDIR, p, K.device)
+    st = lib().ttt_linear_minibatch_bidir(ctypes.byref(p), view(K), view(Q), view(V),
+                                          W0.data_ptr(), eta.data_ptr(), view(Z), ws, wsb,
+                                          _stream(K.device))
+    _check(st, "ttt_linear_minibatch_bidir")
+    return Z
+
+
+def ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, *, saved=None, dK=None, dQ=None, dV=None,
+                             dW0=None, deta=None):
+    """Backward of ttt_linear_fullbatch for L = sum(dZ * Z).
+
+    Returns (dK, dQ, dV, dW0, deta); dW0 [H,64,64] and deta [H] are float32
+    sums over the batch.
+    """
+    B, H, N, d = K.shape
+    _param(W0, (H, d, d), "W0")
+    _param(eta, (H,), "eta")
+    mk = lambda: torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    dK = mk() if dK is None else dK
+    dQ = mk() if dQ is None else dQ
+    dV = mk() if dV is None else dV
+    dW0 = torch.empty((H, d, d), dtype=torch.float32, device=K.device) if dW0 is None else dW0
+    deta = torch.empty((H,), dtype=torch.float32, device=K.device) if deta is None else deta
+    p = problem(K)
+    ws, wsb = workspace(OP_LINEAR_FULLBATCH_BWD, p, K.device)
+    st = lib().ttt_linear_fullbatch_bwd(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
+                                        eta.data_ptr(), view(dZ), _ptr(saved), view(dK), view(dQ),
+                                        view(dV), dW0.data_ptr(), deta.data_ptr(), ws, wsb,
+                                        _stream(K.device))
+    _check(st, "ttt_linear_fullbatch_bwd")
+    return dK, dQ, dV, dW0, deta

@@ -1,0 +1,297 @@
+// api.cpp -- the C ABI of ttt.h: argument validation (before any HIP call),
+// workspace sizing, launch planning and dispatch to the gfx950 kernels.
+#include "ttt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <stdint.h>
+
+#include "internal.hpp"
+
+using namespace ttt;
+
+namespace {
+
+struct Span {
+    uintptr_t lo = 0, hi = 0;
+    bool valid = false;
+};
+
+bool overlap(const Span& a, const Span& b) {
+    return a.valid && b.valid && a.lo < b.hi && b.lo < a.hi;
+}
+
+size_t esize(ttt_dtype t) { return t == TTT_BF16 ? 2 : 4; }
+
+// Shape checks common to every op.  *noop is set when B or H is zero.
+ttt_status check_problem(const ttt_problem* p, bool* noop) {
+    *noop = false;
+    if (!p) return TTT_ERR_NULL_POINTER;
+    if (p->B < 0 || p->H < 0 || p->N <= 0 || p->d <= 0) return TTT_ERR_BAD_SHAPE;
+    if (p->dtype != TTT_F32 && p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
+    if (p->d != 64) return TTT_ERR_UNSUPPORTED;
+    if ((int64_t)p->B * p->H > (int64_t)1 << 24) return TTT_ERR_UNSUPPORTED;
+    if (p->B == 0 || p->H == 0) *noop = true;
+    return TTT_OK;
+}
+
+// A [B,H,N,d] view: non-null, non-negative strides, no two elements at one
+// address (strides sorted ascending must each clear the span of the smaller
+// dimensions), 16-byte alignment of the pointer and of each stride.
+ttt_status check_view(const ttt_view& v, const ttt_problem& p, Span* sp) {
+    if (!v.ptr) return TTT_ERR_NULL_POINTER;
+    if (v.stride_b < 0 || v.stride_h < 0 || v.stride_n < 0) return TTT_ERR_BAD_STRIDE;
+    struct Dim {
+        int64_t ext, st;
+    } dims[3] = {{p.B, v.stride_b}, {p.H, v.stride_h}, {p.N, v.stride_n}};
+    std::sort(dims, dims + 3, [](const Dim& x, const Dim& y) { return x.st < y.st; });
+    const int64_t lim = (int64_t)1 << 60;
+    int64_t span = p.d;
+    for (const Dim& dm : dims) {
+        if (dm.ext <= 1) continue;
+        if (dm.st < span) return TTT_ERR_BAD_STRIDE;
+        if (dm.st > lim / dm.ext) return TTT_ERR_BAD_STRIDE;
+        span += dm.st * (dm.ext - 1);
+        if (span > lim) return TTT_ERR_BAD_STRIDE;
+    }
+    const size_t es = esize(p.dtype);
+    if ((uintptr_t)v.ptr % 16) return TTT_ERR_MISALIGNED;
+    for (const Dim& dm : dims)
+        if (dm.ext > 1 && (dm.st * (int64_t)es) % 16) return TTT_ERR_MISALIGNED;
+    sp->lo = (uintptr_t)v.ptr;
+    sp->hi = sp->lo + (uintptr_t)(span * (int64_t)es);
+    sp->valid = true;
+    return TTT_OK;
+}
+
+ttt_status check_buf(const void* ptr, size_t bytes, size_t align, Span* sp) {
+    if (!ptr) return TTT_ERR_NULL_POINTER;
+    if ((uintptr_t)ptr % align) return TTT_ERR_MISALIGNED;
+    sp->lo = (uintptr_t)ptr;
+    sp->hi = sp->lo + bytes;
+    sp->valid = true;
+    return TTT_OK;
+}
+
+// Every output span must be disjoint from every input span and from every
+// other output span.
+ttt_status check_aliasing(const Span* in, int nin, const Span* out, int nout) {
+    for (int i = 0; i < nout; ++i) {
+        for (int j = 0; j < nin; ++j)
+            if (overlap(out[i], in[j])) return TTT_ERR_ALIASING;
+        for (int j = i + 1; j < nout; ++j)
+            if (overlap(out[i], out[j])) return TTT_ERR_ALIASING;
+    }
+    return TTT_OK;
+}
+
+ttt_status check_ws(void* ws, size_t ws_bytes, size_t need, Span* sp) {
+    if (ws_bytes < need) return TTT_ERR_WORKSPACE_TOO_SMALL;
+    if (need == 0) return TTT_OK;
+    return check_buf(ws, need, 256, sp);
+}
+
+View4 v4(const ttt_view& v) { return View4{v.ptr, v.stride_b, v.stride_h, v.stride_n}; }
+
+// Resident-workgroup capacity of the current device for a kernel, cached
+// per device.  Slices that are split over several workgroups meet at a
+// barrier, so their grid must not exceed this.
+constexpr int kMaxDev = 64;
+std::atomic<int> g_cus[kMaxDev];
+
+int device_cus() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 0;
+    int c = g_cus[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+        g_cus[dev].store(c, std::memory_order_relaxed);
+    }
+    return c;
+}
+
+ttt_status hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
+
+} // namespace
+
+extern "C" {
+
+const char* ttt_status_string(ttt_status s) {
+    switch (s) {
+    case TTT_OK: return "TTT_OK";
+    case TTT_ERR_NULL_POINTER: return "TTT_ERR_NULL_POINTER";
+    case TTT_ERR_BAD_SHAPE: return "TTT_ERR_BAD_SHAPE";
+    case TTT_ERR_BAD_STRIDE: return "TTT_ERR_BAD_STRIDE";
+    case TTT_ERR_MISALIGNED: return "TTT_ERR_MISALIGNED";
+    case TTT_ERR_UNSUPPORTED: return "TTT_ERR_UNSUPPORTED";
+    case TTT_ERR_ALIASING: return "TTT_ERR_ALIASING";
+    case TTT_ERR_WORKSPACE_TOO_SMALL: return "TTT_ERR_WORKSPACE_TOO_SMALL";
+    case TTT_ERR_HIP: return "TTT_ERR_HIP";
+    }
+    return "TTT_ERR_UNKNOWN";
+}
+
+size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
+    bool noop = false;
+    if (check_problem(p, &noop) != TTT_OK || noop) return 0;
+    switch (op) {
+    case TTT_OP_LINEAR_FULLBATCH: return lin_fwd_ws_bytes(p->B, p->H, p->N);
+    case TTT_OP_DWCONV3X3_FULLBATCH:
+        if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N) return 0;
+        return conv_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
+    case TTT_OP_LINEAR_MINIBATCH_BIDIR: return scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
+    case TTT_OP_LINEAR_FULLBATCH_BWD: return lin_bwd_ws_bytes(p->B, p->H, p->N);
+    }
+    return 0;
+}
+
+ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                const float* W0, const float* eta, ttt_view Z, float* saved,
+                                void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK || noop) return st;
+    Span in[5], out[3];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    if (saved && (st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &out[1])) != TTT_OK)
+        return st;
+    const size_t need = lin_fwd_ws_bytes(p->B, p->H, p->N);
+    if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
+
+    LinFwdLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    a.W0 = W0; a.eta = eta; a.saved = saved;
+    a.B = p->B; a.H = p->H; a.N = p->N;
+    a.bf16 = p->dtype == TTT_BF16;
+    const long long slices = (long long)p->B * p->H;
+    int S = lin_fwd_max_splits(p->B, p->H, p->N);
+    if (S > 1) {
+        const int cap = device_cus() * lin_fwd_resident_per_cu(a.bf16);
+        S = std::min<long long>(S, cap / slices);
+        if (S < 2) S = 1;
+    }
+    a.S = S;
+    a.xcd = (S > 1 && slices % 8 == 0) ? 1 : 0;
+    if (S > 1) {
+        char* base = (char*)ws;
+        const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
+        const int Smax = lin_fwd_max_splits(p->B, p->H, p->N);
+        a.cnt = (unsigned*)base;
+        a.part = (float*)(base + cnt);
+        a.w1 = (float*)(base + cnt + (size_t)slices * Smax * 8192 * 4);
+    }
+    return hip_status(launch_lin_fwd(a, (hipStream_t)stream, 0));
+}
+
+ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                   const float* w0, const float* eta, ttt_view Z, float* saved,
+                                   void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N)
+        return TTT_ERR_BAD_SHAPE;
+    if (noop) return TTT_OK;
+    Span in[5], out[3];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(w0, (size_t)p->H * p->d * 9 * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    if (saved && (st = check_buf(saved, (size_t)p->B * p->H * p->d * 9 * 4, 4, &out[1])) != TTT_OK)
+        return st;
+    const size_t need = conv_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
+    if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
+
+    ConvLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    a.w0 = w0; a.eta = eta; a.saved = saved;
+    a.B = p->B; a.H = p->H; a.gh = p->grid_h; a.gw = p->grid_w;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    a.cap = device_cus() * conv_resident_per_cu(a.bf16);
+    return hip_status(launch_conv(a, (hipStream_t)stream));
+}
+
+ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                      const float* W0, const float* eta, ttt_view Z, void* ws,
+                                      size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (p->minibatch < 1) return TTT_ERR_BAD_SHAPE;
+    if (p->mode != TTT_BIDIR_AVG && p->mode != TTT_FORWARD_ONLY && p->mode != TTT_BACKWARD_ONLY)
+        return TTT_ERR_UNSUPPORTED;
+    if (p->minibatch > 16) return TTT_ERR_UNSUPPORTED;
+    if (noop) return TTT_OK;
+    Span in[5], out[2];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    const size_t need = scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
+    if ((st = check_ws(ws, ws_bytes, need, &out[1])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 5, out, 2)) != TTT_OK) return st;
+
+    ScanLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    a.W0 = W0; a.eta = eta;
+    a.B = p->B; a.H = p->H; a.N = p->N; a.b = p->minibatch; a.mode = (int)p->mode;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    return hip_status(launch_scan(a, (hipStream_t)stream));
+}
+
+ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                    const float* W0, const float* eta, ttt_view dZ,
+                                    const float* saved, ttt_view dK, ttt_view dQ, ttt_view dV,
+                                    float* dW0, float* deta, void* ws, size_t ws_bytes,
+                                    ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK || noop) return st;
+    Span in[7], out[6];
+    int nin = 6;
+    if ((st = check_buf(dW0, (size_t)p->H * p->d * p->d * 4, 4, &out[3])) != TTT_OK) return st;
+    if ((st = check_buf(deta, (size_t)p->H * 4, 4, &out[4])) != TTT_OK) return st;
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(dZ, *p, &in[5])) != TTT_OK) return st;
+    if (saved) {
+        if ((st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &in[6])) != TTT_OK)
+            return st;
+        nin = 7;
+    }
+    if ((st = check_view(dK, *p, &out[0])) != TTT_OK) return st;
+    if ((st = check_view(dQ, *p, &out[1])) != TTT_OK) return st;
+    if ((st = check_view(dV, *p, &out[2])) != TTT_OK) return st;
+    const size_t need = lin_bwd_ws_bytes(p->B, p->H, p->N);
+    if ((st = check_ws(ws, ws_bytes, need, &out[5])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, nin, out, 6)) != TTT_OK) return st;
+
+    LinBwdLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.dZ = v4(dZ);
+    a.dK = v4(dK); a.dQ = v4(dQ); a.dV = v4(dV);
+    a.W0 = W0; a.eta = eta; a.saved = saved; a.dW0 = dW0; a.deta = deta;
+    a.B = p->B; a.H = p->H; a.N = p->N;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    return hip_status(launch_lin_bwd(a, (hipStream_t)stream));
+}
+
+} // extern "C"

@@ -1,0 +1,125 @@
+// common.hpp -- device helpers shared by the gfx950 TTT kernels: element
+// types, bf16 conversion, matrix-core (MFMA) wrappers, the per-slice
+// workgroup barrier and the XCD-aware slice mapping.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ttt {
+
+constexpr int kD = 64;        // head dimension handled by these kernels
+constexpr int kThreads = 256; // 4 waves of 64 lanes per workgroup
+
+typedef uint16_t bf16_t; // bf16 storage
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4))); // native 16-byte vector
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- bf16 --
+__device__ __forceinline__ float bf2f(bf16_t h) {
+    return __uint_as_float(((uint32_t)h) << 16);
+}
+__device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (bf16_t)(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+// ----------------------------------------------------------------- MFMA --
+// 16x16 output tile, fp32 accumulate.  Lane l of the wave holds
+//   A[m = l%16][k],  B[k][n = l%16],  D[rows 4*(l/16)+i, i=0..3][col l%16].
+// mfma32: k = 8*(l/16) + j, j = 0..7 (bf16 operands, 16x16x32).
+__device__ __forceinline__ v4f mfma32(const v8bf& a, const v8bf& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// mfma16: k = 4*(l/16) + i, i = 0..3 (bf16 operands, 16x16x16).
+__device__ __forceinline__ v4f mfma16(const v4s& a, const v4s& b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+// mfma4: k = l/16 (fp32 operands, 16x16x4).
+__device__ __forceinline__ v4f mfma4(float a, float b, const v4f& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8bf as_v8bf(const u32x4& u) {
+    return __builtin_bit_cast(v8bf, u);
+}
+__device__ __forceinline__ v4s as_v4s(const u32x2& u) {
+    return __builtin_bit_cast(v4s, u);
+}
+
+// ------------------------------------------------------- LDS barrier --
+// Workgroup barrier that orders LDS accesses only.  Unlike __syncthreads()
+// it does not wait for outstanding global loads, so register prefetches
+// stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ------------------------------------------------------ slice barrier --
+// Workgroups that cooperate on one slice meet at a counter in the
+// workspace.  The counter only grows during a launch (targets S, 2S, ...);
+// after the last barrier every workgroup adds one more and the one that
+// brings it to (nbarriers+1)*S resets it to zero, so the next call on the
+// same workspace starts from zero.  All workgroups of a slice must be
+// co-resident: the host guarantees grid <= resident capacity.
+__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target) {
+    // every wave publishes its own global writes, then one lane signals
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target)
+            __builtin_amdgcn_s_sleep(1);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    }
+    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+
+__device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned total) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == total - 1)
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+// --------------------------------------------------- slice mapping ------
+// Workgroup i runs on XCD i % 8.  When the slice count is a multiple of 8,
+// the S workgroups of one slice are given indices with equal i % 8, so
+// their partial sums meet in one XCD's L2.
+struct SliceSplit {
+    int slice, split;
+};
+__device__ __forceinline__ SliceSplit map_block(int blk, int S, int xcd_aware) {
+    SliceSplit r;
+    if (xcd_aware) {
+        int x = blk & 7, j = blk >> 3;
+        r.slice = (j / S) * 8 + x;
+        r.split = j % S;
+    } else {
+        r.slice = blk / S;
+        r.split = blk % S;
+    }
+    return r;
+}
+
+} // namespace ttt

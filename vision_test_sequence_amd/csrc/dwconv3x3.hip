@@ -1,0 +1,354 @@
+// dwconv3x3.hip -- one full-batch L2 gradient step of the 3x3 depthwise-
+// convolution inner model, then apply (ViT3 article, observation 6: a conv
+// inner model keeps the global K/V information in its kernel; the layer
+// recipe uses one depthwise 3x3 head).
+//
+// Per slice and channel c, on the row-major token grid with zero padding:
+//   P = conv(K, w0), R = P - V,
+//   g[c][i][j] = (2/N) sum_{y,x} R[y][x] K[y+i-1][x+j-1],
+//   w1 = w0 - eta g,  Z = conv(Q, w1).
+// The work is HBM-bound element-wise stencil arithmetic on the vector ALUs
+// (no dense contraction): one channel per lane (d = 64 = wavefront width),
+// so every LDS access of a wave is one contiguous 128-byte (bf16) pixel.
+//
+// A slice's grid is cut into rectangular tiles of R rows x TW columns; a
+// workgroup owns one or more consecutive tiles of one slice.
+//   phase 1  the K halo tile ((R+2) x (TW+2) pixels), the V tile and (for
+//            single-tile workgroups) the Q halo tile are staged into LDS
+//            with direct global->LDS 16-byte loads; each wave slides a 3x3
+//            window along x over its row segments, forms P and R, and
+//            accumulates its lane's 9 tap sums; the 4 waves are summed in a
+//            fixed order;
+//   phase 2  with S > 1 workgroups per slice the 64 x 9 partials meet in the
+//            workspace (per-slice barrier), each workgroup reduces a few
+//            channels over the S partials in order and writes those w1
+//            rows, a second barrier, every workgroup reads w1;
+//   phase 3  the same sliding window over Q with w1 writes Z.
+#include "common.hpp"
+#include "internal.hpp"
+
+#include <atomic>
+
+namespace ttt {
+namespace {
+
+constexpr int kTileBytes = 147456;           // K halo + V + Q halo regions
+constexpr int kRedFloats = 4 * 64 * 9;       // per-wave tap sums
+constexpr int kSeg = 16;                     // pixels per row segment
+
+struct ConvArgs {
+    View4 K, Q, V, Z;
+    const float* w0;
+    const float* eta;
+    float* saved;
+    float* part;       // [slices][S][64][9]
+    float* w1;         // [slices][64][9]
+    unsigned* cnt;     // [slices]
+    int H, gh, gw;
+    int R, TW;         // tile rows / columns
+    int ny, nx;        // tiles per slice along y / x
+    int S;             // workgroups per slice
+    int tpw;           // tiles per workgroup
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <bool BF> struct ConvT;
+template <> struct ConvT<true> {
+    static constexpr int esz = 2;
+    __device__ static float ld(const char* p) { return __uint_as_float((uint32_t)*(const uint16_t*)p << 16); }
+    __device__ static void st(char* p, float v) { *(uint16_t*)p = f2bf(v); }
+};
+template <> struct ConvT<false> {
+    static constexpr int esz = 4;
+    __device__ static float ld(const char* p) { return *(const float*)p; }
+    __device__ static void st(char* p, float v) { *(float*)p = v; }
+};
+
+// Stage a (rows x cols) block of pixels whose top-left grid position is
+// (ya, xa) into LDS at dst (row-major, pixel-contiguous).  Positions outside
+// the grid load a clamped in-grid pixel; readers mask them to zero.
+template <bool BF>
+__device__ __forceinline__ void stage(char* dst, const char* src, long long sn, int ya, int xa,
+                                      int rows, int cols, int gh, int gw) {
+    constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
+    const int total = rows * cols * cpp;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    for (int base = w * 64; base < total; base += kThreads) {
+        const int q = base + lane;
+        const int qq = q < total ? q : total - 1;
+        const int px = qq / cpp, sub = qq % cpp;
+        const int y = min(max(ya + px / cols, 0), gh - 1);
+        const int x = min(max(xa + px % cols, 0), gw - 1);
+        const char* g = src + ((long long)y * gw + x) * sn + sub * 16;
+        // a partial last instruction writes its tail lanes past `total`
+        // chunks, inside the region's slack (regions are padded by 1 KB)
+        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + base * 16), 16, 0, 0);
+    }
+}
+
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
+    using T = ConvT<BF>;
+    constexpr int pb = 64 * T::esz; // bytes per pixel
+    __shared__ __attribute__((aligned(16))) char lds[kTileBytes + 3 * 1024];
+    __shared__ float red[kRedFloats];
+    __shared__ float w1s[64 * 9];
+
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const SliceSplit ss = map_block(blockIdx.x, a.S, (a.S > 1 && ((gridDim.x / a.S) & 7) == 0) ? 1 : 0);
+    const int slice = ss.slice, split = ss.split;
+    const int b = slice / a.H, h = slice % a.H;
+    const int gh = a.gh, gw = a.gw, N = gh * gw;
+    const int ntile = a.ny * a.nx;
+    const int tb = split * a.tpw, te = min(ntile, tb + a.tpw);
+
+    const char* Kp = (const char*)a.K.ptr + (b * a.K.sb + h * a.K.sh) * (long long)T::esz;
+    const char* Vp = (const char*)a.V.ptr + (b * a.V.sb + h * a.V.sh) * (long long)T::esz;
+    const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)T::esz;
+    char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)T::esz;
+    const long long Ksn = a.K.sn * T::esz, Vsn = a.V.sn * T::esz;
+    const long long Qsn = a.Q.sn * T::esz, Zsn = a.Z.sn * T::esz;
+
+    const int HW = a.TW + 2;
+    const int khalo = (a.R + 2) * HW;
+    char* Ks = lds;
+    char* Vs = lds + khalo * pb + 1024;
+    char* Qs = Vs + a.R * a.TW * pb + 1024;
+    const bool q_early = (te - tb) == 1;
+
+    const float* w0c = a.w0 + ((long long)h * 64 + lane) * 9;
+    float wt[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wt[t] = w0c[t];
+    float gacc[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) gacc[t] = 0.f;
+
+    // ------------------------------------------------------------ phase 1
+    for (int tile = tb; tile < te; ++tile) {
+        const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
+        const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
+        stage<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
+        stage<BF>(Vs, Vp, Vsn, y0, x0, rr, tw, gh, gw);
+        if (q_early) stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
+        __syncthreads(); // waits for the direct-to-LDS loads
+        const int nsx = (tw + kSeg - 1) / kSeg;
+        for (int sgi = w; sgi < rr * nsx; sgi += 4) {
+            const int r = sgi / nsx, xs = (sgi % nsx) * kSeg, xe = min(tw, xs + kSeg);
+            const int y = y0 + r;
+            bool rowok[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) rowok[i] = (y + i - 1 >= 0) && (y + i - 1 < gh);
+            auto kval = [&](int i, int hx) -> float { // halo row r+i, halo column hx
+                const int x = x0 - 1 + hx;
+                const bool ok = rowok[i] && x >= 0 && x < gw;
+                const float v = T::ld(Ks + (((r + i) * HW + hx) * 64 + lane) * T::esz);
+                return ok ? v : 0.f;
+            };
+            float kw[3][3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                kw[i][0] = kval(i, xs);
+                kw[i][1] = kval(i, xs + 1);
+            }
+            for (int xl = xs; xl < xe; ++xl) {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) kw[i][2] = kval(i, xl + 2);
+                float p = 0.f;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) p += wt[i * 3 + j] * kw[i][j];
+                const float rv = p - T::ld(Vs + ((r * a.TW + xl) * 64 + lane) * T::esz);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) gacc[i * 3 + j] += rv * kw[i][j];
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    kw[i][0] = kw[i][1];
+                    kw[i][1] = kw[i][2];
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // fixed-order sum of the 4 waves' tap sums
+#pragma unroll
+    for (int t = 0; t < 9; ++t) red[(w * 64 + lane) * 9 + t] = gacc[t];
+    __syncthreads();
+    const float eta = a.eta[h];
+    const float scale = 2.0f / (float)N;
+    if (a.S == 1) {
+        if (w == 0) {
+            for (int t = 0; t < 9; ++t) {
+                const float s = ((red[lane * 9 + t] + red[(64 + lane) * 9 + t]) + red[(128 + lane) * 9 + t]) +
+                                red[(192 + lane) * 9 + t];
+                const float gv = scale * s;
+                w1s[lane * 9 + t] = wt[t] - eta * gv;
+                if (a.saved) a.saved[((long long)slice * 64 + lane) * 9 + t] = gv;
+            }
+        }
+        __syncthreads();
+    } else {
+        float* P = a.part + ((long long)slice * a.S + split) * 576;
+        for (int e = tid; e < 576; e += kThreads) {
+            const int c = e / 9, t = e % 9;
+            P[e] = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) + red[(192 + c) * 9 + t];
+        }
+        slice_barrier(a.cnt + slice, (unsigned)a.S);
+        const int e0 = (576 * split) / a.S, e1 = (576 * (split + 1)) / a.S;
+        const float* P0 = a.part + (long long)slice * a.S * 576;
+        float* w1g = a.w1 + (long long)slice * 576;
+        for (int e = e0 + tid; e < e1; e += kThreads) {
+            float s = 0.f;
+            for (int sp = 0; sp < a.S; ++sp) s += P0[(long long)sp * 576 + e];
+            const float gv = scale * s;
+            w1g[e] = a.w0[(long long)h * 576 + e] - eta * gv;
+            if (a.saved) a.saved[(long long)slice * 576 + e] = gv;
+        }
+        slice_barrier(a.cnt + slice, 2u * a.S);
+        for (int e = tid; e < 576; e += kThreads) w1s[e] = w1g[e];
+        slice_barrier_release(a.cnt + slice, 3u * a.S);
+        __syncthreads();
+    }
+    float wq[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wq[t] = w1s[lane * 9 + t];
+
+    // ------------------------------------------------------------ phase 3
+    for (int tile = tb; tile < te; ++tile) {
+        const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
+        const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
+        if (!q_early) {
+            stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
+            __syncthreads();
+        }
+        const int nsx = (tw + kSeg - 1) / kSeg;
+        for (int sgi = w; sgi < rr * nsx; sgi += 4) {
+            const int r = sgi / nsx, xs = (sgi % nsx) * kSeg, xe = min(tw, xs + kSeg);
+            const int y = y0 + r;
+            bool rowok[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) rowok[i] = (y + i - 1 >= 0) && (y + i - 1 < gh);
+            auto qval = [&](int i, int hx) -> float {
+                const int x = x0 - 1 + hx;
+                const bool ok = rowok[i] && x >= 0 && x < gw;
+                const float v = T::ld(Qs + (((r + i) * HW + hx) * 64 + lane) * T::esz);
+                return ok ? v : 0.f;
+            };
+            float qw[3][3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) {
+                qw[i][0] = qval(i, xs);
+                qw[i][1] = qval(i, xs + 1);
+            }
+            for (int xl = xs; xl < xe; ++xl) {
+#pragma unroll
+                for (int i = 0; i < 3; ++i) qw[i][2] = qval(i, xl + 2);
+                float z = 0.f;
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) z += wq[i * 3 + j] * qw[i][j];
+                T::st(Zp + ((long long)y * gw + x0 + xl) * Zsn + lane * T::esz, z);
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    qw[i][0] = qw[i][1];
+                    qw[i][1] = qw[i][2];
+                }
+            }
+        }
+        if (!q_early) __syncthreads();
+    }
+}
+
+struct ConvPlan {
+    int R, TW, ny, nx, S, tpw;
+};
+
+// Tile the grid so that the slices x S workgroups fill (but do not exceed)
+// one MI355X (256 resident workgroups) and a tile's staging fits in LDS.
+ConvPlan plan_conv(int slices, int gh, int gw, int esz, int cap) {
+    const int pb = 64 * esz;
+    auto fits = [&](int R, int TW) {
+        return ((long long)2 * (R + 2) * (TW + 2) + (long long)R * TW) * pb + 3 * 1024 <= kTileBytes + 3 * 1024;
+    };
+    ConvPlan p{};
+    long long target = cap > 0 ? cap / slices : 1;
+    if (target < 1) target = 1;
+    // widest tiles first: full rows when they fit, else column bands
+    int TW = gw;
+    while (!fits(1, TW)) TW = (TW + 1) / 2;
+    int nx = (gw + TW - 1) / TW;
+    TW = (gw + nx - 1) / nx;
+    long long ny = target / nx;
+    if (ny < 1) ny = 1;
+    if (ny > gh) ny = gh;
+    int R = (int)((gh + ny - 1) / ny);
+    while (!fits(R, TW)) --R;
+    ny = (gh + R - 1) / R;
+    const long long ntile = ny * (long long)nx;
+    // one workgroup per tile when that stays resident, else one per slice
+    int S = (int)ntile;
+    if ((long long)slices * S > (cap > 0 ? cap : 1)) S = 1;
+    p.R = R; p.TW = TW; p.ny = (int)ny; p.nx = nx; p.S = S;
+    p.tpw = (int)((ntile + S - 1) / S);
+    return p;
+}
+
+} // namespace
+
+size_t conv_ws_bytes(int B, int H, int gh, int gw) {
+    const long long slices = (long long)B * H;
+    if (slices <= 0 || gh <= 0 || gw <= 0) return 0;
+    // sized for the largest split the planner can choose on a 256-CU device
+    const ConvPlan p = plan_conv((int)slices, gh, gw, 2, 256);
+    const ConvPlan q = plan_conv((int)slices, gh, gw, 4, 256);
+    const int S = p.S > q.S ? p.S : q.S;
+    if (S <= 1) return 0;
+    const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
+    return cnt + (size_t)slices * S * 576 * 4 + (size_t)slices * 576 * 4;
+}
+
+int conv_resident_per_cu(int bf16) {
+    static std::atomic<int> cached[2];
+    int n = cached[bf16 ? 1 : 0].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<true>, kThreads, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<false>, kThreads, 0);
+    if (e != hipSuccess || n < 0) return 0;
+    cached[bf16 ? 1 : 0].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
+    const long long slices = (long long)l.B * l.H;
+    const int esz = l.bf16 ? 2 : 4;
+    const int cap = l.cap < 256 ? l.cap : 256; // the workspace is sized for 256
+    ConvPlan p = plan_conv((int)slices, l.gh, l.gw, esz, cap);
+    ConvArgs a{};
+    a.K = l.K; a.Q = l.Q; a.V = l.V; a.Z = l.Z;
+    a.w0 = l.w0; a.eta = l.eta; a.saved = l.saved;
+    a.H = l.H; a.gh = l.gh; a.gw = l.gw;
+    a.R = p.R; a.TW = p.TW; a.ny = p.ny; a.nx = p.nx; a.S = p.S; a.tpw = p.tpw;
+    if (p.S > 1) {
+        // workspace layout as conv_ws_bytes: counters, partials, w1
+        const ConvPlan p2 = plan_conv((int)slices, l.gh, l.gw, 2, 256);
+        const ConvPlan p4 = plan_conv((int)slices, l.gh, l.gw, 4, 256);
+        const int Smax = p2.S > p4.S ? p2.S : p4.S;
+        char* base = (char*)l.ws;
+        const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
+        a.cnt = (unsigned*)base;
+        a.part = (float*)(base + cnt);
+        a.w1 = (float*)(base + cnt + (size_t)slices * Smax * 576 * 4);
+    }
+    const dim3 grid((unsigned)(slices * p.S)), block(kThreads);
+    void* args[] = {&a};
+    const void* fn = l.bf16 ? (const void*)conv_kernel<true> : (const void*)conv_kernel<false>;
+    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+} // namespace ttt
