@@ -129,9 +129,11 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
     for (int tile = tb; tile < te; ++tile) {
         const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
         const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
-        stage<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
-        stage<BF>(Vs, Vp, Vsn, y0, x0, rr, tw, gh, gw);
-        if (q_early) stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
+        // always the nominal tile shape, so the LDS pitches are fixed; the
+        // part of an edge tile outside the grid is masked when read
+        stage<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
+        stage<BF>(Vs, Vp, Vsn, y0, x0, a.R, a.TW, gh, gw);
+        if (q_early) stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
         __syncthreads(); // waits for the direct-to-LDS loads
         const int nsx = (tw + kSeg - 1) / kSeg;
         for (int sgi = w; sgi < rr * nsx; sgi += 4) {
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
         const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
         const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
         if (!q_early) {
-            stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, rr + 2, tw + 2, gh, gw);
+            stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
             __syncthreads();
         }
         const int nsx = (tw + kSeg - 1) / kSeg;
