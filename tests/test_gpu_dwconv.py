@@ -88,3 +88,14 @@ def test_deterministic():
     Z2 = vt.ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, gh, gw)
     torch.cuda.synchronize()
     assert torch.equal(Z1, Z2)
+
+
+def test_workspace_shared_across_shapes():
+    # calls of different shapes reuse one cached workspace: partial sums of
+    # one shape must never land on the barrier counters of another
+    banner("dwconv workspace shared across shapes")
+    d = _dev()
+    cases = [(8, 78, 78, 501), (128, 14, 14, 502), (3, 33, 20, 503), (8, 78, 78, 504), (128, 14, 14, 505)]
+    for B, gh, gw, seed in cases:
+        inp = wl.draw(B, 1, gh * gw, seed=seed, dtype="bf16", unit_rows=True)
+        _check(inp["K"].to(d), inp["Q"].to(d), inp["V"].to(d), inp["w0"].to(d), inp["eta"].to(d), gh, gw)

@@ -157,3 +157,12 @@ def test_nan_stays_in_its_slice():
     assert torch.isnan(Z[1, 0]).any()
     for b, h in [(0, 0), (0, 1), (1, 1)]:
         assert torch.isfinite(Z[b, h]).all()
+
+
+def test_workspace_shared_across_shapes():
+    banner("linear workspace shared across shapes")
+    d = _dev()
+    for B, H, N, seed in [(8, 2, 6084, 601), (3, 7, 1000, 602), (16, 1, 4096, 603), (8, 2, 6084, 604),
+                          (1, 1, 300, 605), (3, 7, 1000, 606)]:
+        inp = wl.draw(B, H, N, seed=seed, dtype="bf16", unit_rows=True)
+        _check(inp["K"].to(d), inp["Q"].to(d), inp["V"].to(d), inp["W0"].to(d), inp["eta"].to(d))

@@ -9,6 +9,7 @@
 #include <stdint.h>
 
 #include "internal.hpp"
+#include "common.hpp"
 
 using namespace ttt;
 
@@ -114,6 +115,11 @@ int device_cus() {
 
 ttt_status hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// The XCD-local exchange relies on MI355X's whole-device (SPX) layout: 256
+// CUs in 8 XCDs, workgroup i on XCD i % 8.  The kernels also check the XCC
+// id of every workgroup and poison their outputs with NaN if it differs.
+bool xcd_local_ok() { return device_cus() == 256; }
+
 } // namespace
 
 extern "C" {
@@ -173,22 +179,23 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
     a.bf16 = p->dtype == TTT_BF16;
     const long long slices = (long long)p->B * p->H;
     int S = lin_fwd_max_splits(p->B, p->H, p->N);
+    const long long padded = (slices + 7) / 8 * 8;
     if (S > 1) {
         const int cap = device_cus() * lin_fwd_resident_per_cu(a.bf16);
-        S = std::min<long long>(S, cap / slices);
-        if (S < 2) S = 1;
+        while (S > 1 && (long long)S * padded > cap) S /= 2; // stays a power of two
     }
     a.S = S;
-    a.xcd = (S > 1 && slices % 8 == 0) ? 1 : 0;
+    a.xcd = (S > 1 && xcd_local_ok()) ? 1 : 0;
     if (S > 1) {
+        // workspace: [fixed counter block][partials, Smax per slice][W1 per slice]
         char* base = (char*)ws;
-        const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
         const int Smax = lin_fwd_max_splits(p->B, p->H, p->N);
+        if (slices > kMaxBarrierSlices) return TTT_ERR_UNSUPPORTED; // unreachable: S > 1 => slices <= 128
         a.cnt = (unsigned*)base;
-        a.part = (float*)(base + cnt);
-        a.w1 = (float*)(base + cnt + (size_t)slices * Smax * 8192 * 4);
+        a.part = (float*)(base + kCounterBytes);
+        a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 8192 * 4);
     }
-    return hip_status(launch_lin_fwd(a, (hipStream_t)stream, 0));
+    return hip_status(launch_lin_fwd(a, (hipStream_t)stream, lin_fwd_is_resident(p->N, S, a.bf16) ? 1 : 0));
 }
 
 ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
@@ -220,6 +227,7 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
     a.cap = device_cus() * conv_resident_per_cu(a.bf16);
+    a.xcd_ok = xcd_local_ok() ? 1 : 0;
     return hip_status(launch_conv(a, (hipStream_t)stream));
 }
 

@@ -28,16 +28,14 @@ __device__ __forceinline__ float bf2f(bf16_t h) {
 __device__ __forceinline__ float bflo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bfhi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16, round to nearest even (NaN stays NaN).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (bf16_t)(u >> 16);
-}
+// fp32 -> bf16 with the hardware packed conversion (v_cvt_pk_bf16_f32:
+// round to nearest even, NaN stays NaN).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{lo, hi}), bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return (bf16_t)(pack_bf2(f, 0.f) & 0xffffu); }
 
 // ----------------------------------------------------------------- MFMA --
 // 16x16 output tile, fp32 accumulate.  Lane l of the wave holds
@@ -73,24 +71,62 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // ------------------------------------------------------ slice barrier --
-// Workgroups that cooperate on one slice meet at a counter in the
-// workspace.  The counter only grows during a launch (targets S, 2S, ...);
-// after the last barrier every workgroup adds one more and the one that
-// brings it to (nbarriers+1)*S resets it to zero, so the next call on the
-// same workspace starts from zero.  All workgroups of a slice must be
-// co-resident: the host guarantees grid <= resident capacity.
+// Workgroups that cooperate on one slice exchange small partial results
+// through the workspace, meeting at a per-slice counter.  Two protocols:
+//  * XCD-local: all workgroups of the slice run on one XCD (see map_block),
+//    so its L2 is their coherence point.  Data moves with ordinary 16-byte
+//    stores and loads; a reader invalidates only its own CU's L1 after the
+//    barrier.  Every exchanged address is written before it is read within
+//    one launch, by workgroups of that one XCD.
+//  * device-wide: data moves with device-scope relaxed atomics (xstore /
+//    xload), performed at the device coherence point.
+// Neither needs an L2-wide writeback or invalidate.
+__device__ __forceinline__ void xstore(float* p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float xload(const float* p) {
+    return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+__device__ __forceinline__ unsigned xcc_id() {
+    return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); // HW_REG_XCC_ID[3:0]
+}
+
+// Every workspace starts with a fixed block of kMaxBarrierSlices counters,
+// whatever the problem shape, so partial sums of one call can never land on
+// the counters another call relies on being zero.  Each counter has a
+// 256-byte line of its own: slices polling neighbouring counters would
+// otherwise serialise on one line.  Slices only meet at barriers when
+// S >= 2 workgroups share a slice, which the resident-grid limit (256
+// workgroups) confines to at most 128 slices.
+constexpr int kMaxBarrierSlices = 256;
+constexpr int kCounterStride = 64; // unsigned ints
+constexpr size_t kCounterBytes = (size_t)kMaxBarrierSlices * kCounterStride * sizeof(unsigned);
+__device__ __forceinline__ unsigned* counter_at(unsigned* base, int slice) {
+    return base + (size_t)slice * kCounterStride;
+}
+
+// Barrier of the S workgroups of one slice at its counter.  The counter
+// only grows during a launch (targets S, 2S, ...); after the last barrier
+// every workgroup adds one more and the one that brings it to
+// (nbarriers+1)*S resets it to zero, so the next call on the same workspace
+// starts from zero.  All workgroups of a slice must be co-resident: the
+// host keeps the grid within the device's resident capacity.
+// Each wave first drains its vector-memory counter, so its exchange stores
+// have completed before lane 0 signals (a workgroup barrier alone does not
+// wait for global stores); the __syncthreads() after the wait keeps later
+// exchange loads behind it.
+__device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 __device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target) {
-    // every wave publishes its own global writes, then one lane signals
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    drain_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
-        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target)
             __builtin_amdgcn_s_sleep(1);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
 }
 
 __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned total) {
@@ -103,9 +139,11 @@ __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned to
 }
 
 // --------------------------------------------------- slice mapping ------
-// Workgroup i runs on XCD i % 8.  When the slice count is a multiple of 8,
-// the S workgroups of one slice are given indices with equal i % 8, so
-// their partial sums meet in one XCD's L2.
+// Workgroup i runs on XCD i % 8 on MI355X (8 XCDs, round-robin dispatch).
+// XCD-aware mapping: slice s lives on XCD s % 8 and its S workgroups are
+// blocks {8*(S*(s/8) + j) + s%8 : j < S}; the grid is padded to
+// 8 * ceil(slices/8) * S blocks and blocks of padding slices (>= slices)
+// have no work.  Plain mapping: slice = block / S.
 struct SliceSplit {
     int slice, split;
 };

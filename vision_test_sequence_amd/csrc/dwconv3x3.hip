@@ -49,6 +49,8 @@ struct ConvArgs {
     int ny, nx;        // tiles per slice along y / x
     int S;             // workgroups per slice
     int tpw;           // tiles per workgroup
+    int slices;        // B * H
+    int xcd;           // XCD-aware grid and XCD-local exchange
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -96,8 +98,10 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
     __shared__ float w1s[64 * 9];
 
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const SliceSplit ss = map_block(blockIdx.x, a.S, (a.S > 1 && ((gridDim.x / a.S) & 7) == 0) ? 1 : 0);
+    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
     const int slice = ss.slice, split = ss.split;
+    if (slice >= a.slices) return; // padding block of the XCD-aware grid
+    const bool poison = a.xcd && ((xcc_id() & 7) != (blockIdx.x & 7));
     const int b = slice / a.H, h = slice % a.H;
     const int gh = a.gh, gw = a.gw, N = gh * gw;
     const int ntile = a.ny * a.nx;
@@ -196,24 +200,64 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
         __syncthreads();
     } else {
         float* P = a.part + ((long long)slice * a.S + split) * 576;
+        unsigned* cnt = counter_at(a.cnt, slice);
         for (int e = tid; e < 576; e += kThreads) {
             const int c = e / 9, t = e % 9;
-            P[e] = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) + red[(192 + c) * 9 + t];
+            const float v = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) +
+                            red[(192 + c) * 9 + t];
+            if (a.xcd) P[e] = v;
+            else xstore(P + e, v);
         }
-        slice_barrier(a.cnt + slice, (unsigned)a.S);
-        const int e0 = (576 * split) / a.S, e1 = (576 * (split + 1)) / a.S;
+        slice_barrier(cnt, (unsigned)a.S);
+        if (a.xcd) l1_invalidate();
+        // Gather elements [e0, e1) of all S partials with every load in
+        // flight at once (the wave-sum buffer is free now), then sum each
+        // element over the splits in split order.
+        const int e0 = (576 * split) / a.S, e1 = (576 * (split + 1)) / a.S, ne = e1 - e0;
+        const int tot = ne * a.S; // <= 576 + S <= kRedFloats
         const float* P0 = a.part + (long long)slice * a.S * 576;
+        for (int base = 0; base < tot; base += 4 * kThreads) {
+            float v[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int f = base + k * kThreads + tid;
+                const float* src = P0 + (long long)(f / ne) * 576 + e0 + f % ne;
+                v[k] = f < tot ? (a.xcd ? *src : xload(src)) : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int f = base + k * kThreads + tid;
+                if (f < tot) red[f] = v[k];
+            }
+        }
+        __syncthreads();
         float* w1g = a.w1 + (long long)slice * 576;
-        for (int e = e0 + tid; e < e1; e += kThreads) {
-            float s = 0.f;
-            for (int sp = 0; sp < a.S; ++sp) s += P0[(long long)sp * 576 + e];
-            const float gv = scale * s;
-            w1g[e] = a.w0[(long long)h * 576 + e] - eta * gv;
+        for (int i = tid; i < ne; i += kThreads) {
+            float sacc = 0.f;
+            for (int sp = 0; sp < a.S; ++sp) sacc += red[sp * ne + i];
+            const int e = e0 + i;
+            const float gv = scale * sacc;
+            const float w1v = a.w0[(long long)h * 576 + e] - eta * gv;
+            if (a.xcd) w1g[e] = w1v;
+            else xstore(w1g + e, w1v);
             if (a.saved) a.saved[(long long)slice * 576 + e] = gv;
         }
-        slice_barrier(a.cnt + slice, 2u * a.S);
-        for (int e = tid; e < 576; e += kThreads) w1s[e] = w1g[e];
-        slice_barrier_release(a.cnt + slice, 3u * a.S);
+        slice_barrier(cnt, 2u * a.S);
+        if (a.xcd) l1_invalidate();
+        {
+            float v[3];
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int e = k * kThreads + tid;
+                v[k] = e < 576 ? (a.xcd ? w1g[e] : xload(w1g + e)) : 0.f;
+            }
+#pragma unroll
+            for (int k = 0; k < 3; ++k) {
+                const int e = k * kThreads + tid;
+                if (e < 576) w1s[e] = v[k];
+            }
+        }
+        slice_barrier_release(cnt, 3u * a.S);
         __syncthreads();
     }
     float wq[9];
@@ -255,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
                     for (int j = 0; j < 3; ++j) z += wq[i * 3 + j] * qw[i][j];
-                T::st(Zp + ((long long)y * gw + x0 + xl) * Zsn + lane * T::esz, z);
+                T::st(Zp + ((long long)y * gw + x0 + xl) * Zsn + lane * T::esz, poison ? __builtin_nanf("") : z);
 #pragma unroll
                 for (int i = 0; i < 3; ++i) {
                     qw[i][0] = qw[i][1];
@@ -273,7 +317,8 @@ struct ConvPlan {
 
 // Tile the grid so that the slices x S workgroups fill (but do not exceed)
 // one MI355X (256 resident workgroups) and a tile's staging fits in LDS.
-ConvPlan plan_conv(int slices, int gh, int gw, int esz, int cap) {
+ConvPlan plan_conv(int nslices, int gh, int gw, int esz, int cap) {
+    const long long slices = (nslices + 7) / 8 * 8; // XCD-aware grids round slices up to 8
     const int pb = 64 * esz;
     auto fits = [&](int R, int TW) {
         return ((long long)2 * (R + 2) * (TW + 2) + (long long)R * TW) * pb + 3 * 1024 <= kTileBytes + 3 * 1024;
@@ -296,6 +341,7 @@ ConvPlan plan_conv(int slices, int gh, int gw, int esz, int cap) {
     // one workgroup per tile when that stays resident, else one per slice
     int S = (int)ntile;
     if ((long long)slices * S > (cap > 0 ? cap : 1)) S = 1;
+    (void)nslices;
     p.R = R; p.TW = TW; p.ny = (int)ny; p.nx = nx; p.S = S;
     p.tpw = (int)((ntile + S - 1) / S);
     return p;
@@ -311,8 +357,7 @@ size_t conv_ws_bytes(int B, int H, int gh, int gw) {
     const ConvPlan q = plan_conv((int)slices, gh, gw, 4, 256);
     const int S = p.S > q.S ? p.S : q.S;
     if (S <= 1) return 0;
-    const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
-    return cnt + (size_t)slices * S * 576 * 4 + (size_t)slices * 576 * 4;
+    return kCounterBytes + (size_t)slices * S * 576 * 4 + (size_t)slices * 576 * 4;
 }
 
 int conv_resident_per_cu(int bf16) {
@@ -336,18 +381,21 @@ hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
     a.w0 = l.w0; a.eta = l.eta; a.saved = l.saved;
     a.H = l.H; a.gh = l.gh; a.gw = l.gw;
     a.R = p.R; a.TW = p.TW; a.ny = p.ny; a.nx = p.nx; a.S = p.S; a.tpw = p.tpw;
+    a.slices = (int)slices;
+    a.xcd = (p.S > 1 && l.xcd_ok) ? 1 : 0;
     if (p.S > 1) {
-        // workspace layout as conv_ws_bytes: counters, partials, w1
+        // workspace layout as conv_ws_bytes: fixed counter block, partials, w1
         const ConvPlan p2 = plan_conv((int)slices, l.gh, l.gw, 2, 256);
         const ConvPlan p4 = plan_conv((int)slices, l.gh, l.gw, 4, 256);
         const int Smax = p2.S > p4.S ? p2.S : p4.S;
+        if (slices > kMaxBarrierSlices) return hipErrorInvalidValue; // unreachable: S > 1
         char* base = (char*)l.ws;
-        const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
         a.cnt = (unsigned*)base;
-        a.part = (float*)(base + cnt);
-        a.w1 = (float*)(base + cnt + (size_t)slices * Smax * 576 * 4);
+        a.part = (float*)(base + kCounterBytes);
+        a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 576 * 4);
     }
-    const dim3 grid((unsigned)(slices * p.S)), block(kThreads);
+    const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
+    const dim3 grid((unsigned)(gslices * p.S)), block(kThreads);
     void* args[] = {&a};
     const void* fn = l.bf16 ? (const void*)conv_kernel<true> : (const void*)conv_kernel<false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);

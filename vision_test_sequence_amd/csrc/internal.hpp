@@ -29,8 +29,9 @@ struct LinFwdLaunch {
 };
 size_t lin_fwd_ws_bytes(int B, int H, int N);
 int lin_fwd_max_splits(int B, int H, int N);
-hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident_wgs);
+hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident);
 int lin_fwd_resident_per_cu(int bf16);
+bool lin_fwd_is_resident(int N, int S, int bf16);
 
 // ---- depthwise 3x3 ----------------------------------------------------
 struct ConvLaunch {
@@ -42,6 +43,7 @@ struct ConvLaunch {
     int bf16;
     void* ws;         // conv_ws_bytes(...) bytes, zero-filled before first use
     int cap;          // resident workgroups of the device for the conv kernel
+    int xcd_ok;       // the device is an MI355X in whole-device (SPX) mode
 };
 size_t conv_ws_bytes(int B, int H, int gh, int gw);
 hipError_t launch_conv(ConvLaunch a, hipStream_t stream);

@@ -11,19 +11,26 @@
 //
 // One launch does everything.  A slice is split over S workgroups along
 // the tokens (the grid is slices x S, every workgroup resident):
-//   phase 1  each workgroup streams 128-token K/V tiles through registers
-//            (3 tiles in flight) into double-buffered LDS and accumulates
-//            its partial [A; C] with 16x16x32 bf16 MFMAs, 4 waves over
-//            disjoint tokens, then sums the 4 waves in a fixed order;
-//            Q tiles for the apply are prefetched into registers;
-//   phase 2  (S > 1) partials go to the workspace, a per-slice barrier,
-//            each workgroup reduces 64/S columns of [A; C] over the S
-//            partials in split order, forms those columns of G and W1,
-//            a second barrier, every workgroup reads W1;
-//            (S == 1) the workgroup forms G and W1 itself;
+//   phase 1  partial [A; C] of the workgroup's tokens with 16x16x32 bf16
+//            MFMAs (4 waves over disjoint tokens, summed in a fixed order);
+//   phase 2  (S > 1) partials meet in the workspace at a per-slice barrier,
+//            each workgroup reduces 64/S columns over the S partials in
+//            split order and forms those columns of G and W1, a second
+//            barrier, every workgroup reads W1; (S == 1) the workgroup
+//            forms G and W1 itself;
 //   phase 3  Z^T = W1 Q^T with W1 rows as the MFMA A operand, so each
 //            lane's outputs are 8 contiguous channels of one token.
-// fp32 inputs take the same path with 16x16x4 fp32 MFMAs.
+// Two variants of phase 1 / 3:
+//   resident  (a workgroup owns <= 384 bf16 tokens): every K, V and Q byte
+//             of the workgroup is requested at kernel start with direct
+//             global->LDS loads and W0 is prefetched into registers, so no
+//             load is issued after the start -- the latency of the whole
+//             range overlaps, and the exchange in phase 2 never queues
+//             behind streaming traffic;
+//   streaming (longer ranges): 128-token K/V tiles flow through registers
+//             (3 in flight) into double-buffered LDS; Q is loaded per
+//             apply step with a short prefetch.
+// fp32 inputs take the same paths with 16x16x4 fp32 MFMAs.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -32,41 +39,36 @@
 namespace ttt {
 namespace {
 
+constexpr int MP = 68; // pitch (floats) of 64x64 fp32 matrices in LDS
+
 template <bool BF> struct LinCfg;
 template <> struct LinCfg<true> {
     static constexpr int esz = 2;
-    static constexpr int tile = 128;     // tokens per LDS stage
     static constexpr int row_slots = 8;  // 16-byte slots per token row
-    static constexpr int qpre = 2;       // apply steps prefetched per wave
+    static constexpr int tile = 128;     // streaming: tokens per LDS stage
+    static constexpr int qpre = 2;       // streaming: apply steps prefetched per wave
+    static constexpr int tmax = 384;     // resident: tokens per workgroup
 };
 template <> struct LinCfg<false> {
     static constexpr int esz = 4;
-    static constexpr int tile = 64;
     static constexpr int row_slots = 16;
+    static constexpr int tile = 64;
     static constexpr int qpre = 2;
+    static constexpr int tmax = 192;
 };
 
-constexpr int kStages = 3;                          // tiles in flight (registers)
-constexpr int kStageBytes = 32768;                  // K tile + V tile
-constexpr int kLdsFloats = 2 * kStageBytes / 4;     // double-buffered: 64 KB
-constexpr int MP = 68;                              // pitch of 64x64 fp32 matrices in LDS
-// float offsets of the phase-2 LDS regions (the staging buffers are dead by then)
-constexpr int RED = 0;        // 26 tiles x 256 floats
-constexpr int MAT_A = 6656;
-constexpr int MAT_C = MAT_A + 64 * MP;
-// After the wave reduction: W0 is staged over the dead reduction buffer and
-// W1 overwrites C in place (each W1 element is written by the thread that
-// last reads the C element at the same position; A stays intact).
-constexpr int MAT_W = MAT_C;
-constexpr int W0S = 0;
-static_assert(MAT_C + 64 * MP <= kLdsFloats, "LDS layout");
-static_assert(W0S + 64 * MP <= MAT_A, "W0 staging must not overlap A");
-
-// XOR swizzle of the 16-byte slots of a staged row: keeps the transposed
-// (token-major per lane) fragment reads free of bank conflicts.
-template <bool BF> __device__ __forceinline__ int swz(int row);
-template <> __device__ __forceinline__ int swz<true>(int row) { return ((row >> 2) & 3) << 1; }
-template <> __device__ __forceinline__ int swz<false>(int row) { return (row & 3) << 2; }
+// XOR swizzles of the 16-byte slots of a staged token row.
+// K and V (Gram reads: the 4 lane groups read rows 8 apart inside a 32-row
+// step): bf16 flips slot bits 1-2 by (row / 8) % 4, so each group reads a
+// different 32-byte band, and a lane's addresses are 4 fixed bases plus
+// row offsets.  Q (apply reads: 16 consecutive rows, one slot each):
+// slot ^ (row % 8) (bf16) / (row % 16) (fp32).
+template <bool BF> __device__ __forceinline__ int swz_kv(int row);
+template <> __device__ __forceinline__ int swz_kv<true>(int row) { return ((row >> 3) & 3) << 1; }
+template <> __device__ __forceinline__ int swz_kv<false>(int row) { return (row & 3) << 2; }
+template <bool BF> __device__ __forceinline__ int swz_q(int row);
+template <> __device__ __forceinline__ int swz_q<true>(int row) { return row & 7; }
+template <> __device__ __forceinline__ int swz_q<false>(int row) { return row & 15; }
 
 __device__ __forceinline__ int perm_row(int rb, int m) {
     // MFMA row m of output block rb -> output channel; lane (g, .) then owns
@@ -74,28 +76,568 @@ __device__ __forceinline__ int perm_row(int rb, int m) {
     return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
 }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// ------------------------------------------------------------- Gram step --
+// One k-step of [A; C] from a swizzled row-major K/V region in LDS whose
+// rows past the valid range hold zeros.
+// bf16: the wave takes token rows [r0, r0+32) (r0 % 32 == 0); lane (g, m)
+// gathers rows r0 + 8g + j (j = 0..7) of channel 16cb + m -- the k-major
+// operand layout of the 16x16x32 MFMA.  With the K/V swizzle that element
+// sits at byte (r0 + j)*128 + kb[cb], kb[cb] = 1024g + 32(cb ^ g) + 2m.
+// fp32: rows [r0, r0+16) as 4 sub-steps of the 16x16x4 MFMA.
+struct GramLanes {
+    int kb[4];
+};
+__device__ __forceinline__ GramLanes gram_lanes(int g, int m) {
+    GramLanes l;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) l.kb[cb] = 1024 * g + 32 * (cb ^ g) + 2 * m;
+    return l;
+}
 template <bool BF>
-__global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
+__device__ __forceinline__ void gram_step(const char* sK, const char* sV, int r0, const GramLanes& gl,
+                                          v4f* accC, v4f* accA, int g, int m) {
+    if constexpr (BF) {
+        v8bf kf[4], vf[4];
+        const char* k0 = sK + r0 * 128;
+        const char* v0 = sV + r0 * 128;
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            v8s kv, vv;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                kv[j] = *reinterpret_cast<const short*>(k0 + gl.kb[cb] + j * 128);
+                vv[j] = *reinterpret_cast<const short*>(v0 + gl.kb[cb] + j * 128);
+            }
+            kf[cb] = __builtin_bit_cast(v8bf, kv);
+            vf[cb] = __builtin_bit_cast(v8bf, vv);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) accC[rb * 4 + cb] = mfma32(vf[rb], kf[cb], accC[rb * 4 + cb]);
+        int t = 0;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cb = rb; cb < 4; ++cb, ++t) accA[t] = mfma32(kf[rb], kf[cb], accA[t]);
+    } else {
+        (void)gl;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const int row = r0 + 4 * s + g;
+            float kf[4], vf[4];
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int c = 16 * cb + m;
+                const int addr = (row * 16 + ((c >> 2) ^ swz_kv<false>(row))) * 16 + (c & 3) * 4;
+                kf[cb] = *reinterpret_cast<const float*>(sK + addr);
+                vf[cb] = *reinterpret_cast<const float*>(sV + addr);
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) accC[rb * 4 + cb] = mfma4(vf[rb], kf[cb], accC[rb * 4 + cb]);
+            int t = 0;
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = rb; cb < 4; ++cb, ++t) accA[t] = mfma4(kf[rb], kf[cb], accA[t]);
+        }
+    }
+}
+
+// Tile t of [A; C] in MFMA layout: t < 16 is C block (t/4, t%4); t >= 16 the
+// upper-triangle A blocks (0,0),(0,1),(0,2),(0,3),(1,1),...,(3,3).
+__device__ __forceinline__ void tile_blocks(int t, int& mat, int& rb, int& cb) {
+    if (t < 16) {
+        mat = 1; rb = t >> 2; cb = t & 3;
+    } else {
+        const int u = t - 16; // 0..9
+        mat = 0;
+        rb = u < 4 ? 0 : (u < 7 ? 1 : (u < 9 ? 2 : 3));
+        const int first = rb == 0 ? 0 : (rb == 1 ? 4 : (rb == 2 ? 7 : 9));
+        cb = rb + (u - first);
+    }
+}
+// Write one final tile as row-major 64x64 (A blocks also mirrored).
+__device__ __forceinline__ void write_tile(const v4f& v, int t, float* mA, float* mC, int g, int m) {
+    int mat, rb, cb;
+    tile_blocks(t, mat, rb, cb);
+    float* M = mat ? mC : mA;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[(16 * rb + 4 * g + i) * MP + 16 * cb + m] = v[i];
+    if (!mat && rb < cb) *reinterpret_cast<f32x4*>(mA + (16 * cb + m) * MP + 16 * rb + 4 * g) = v;
+}
+
+// ------------------------------------------------------------- phase 2 --
+// From the workgroup's [A; C] (mA, mC: full 64x64, pitch MP) to W1 in LDS.
+// w0r: this thread's 4 x 16 bytes of W0[h] (floats 4*tid + 1024*k).
+// LDS use, S == 1: W0 staged at w0s_one (disjoint from mA, mC); W1 written
+//   over mC in place (each element read, then written, by one thread).
+// LDS use, S > 1: scratch [0, 8192) floats (may overlap mA / mC: they are
+//   consumed before the first barrier), W0 at w0s_split >= 8192.
+// Returns W1 in LDS (pitch MP) when S == 1; nullptr when S > 1, where W1 is
+// complete in the workspace at a.w1 + slice*4096 on return.
+__device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
+                             float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r) {
+    const int tid = threadIdx.x;
+    const float eta = a.eta[h];
+    const float scale = 2.0f / (float)a.N;
+    auto stage_w0 = [&](float* dst) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = 4 * tid + 1024 * k, r = e >> 6, c = e & 63;
+            *reinterpret_cast<f32x4*>(dst + r * MP + c) = w0r[k];
+        }
+    };
+    if (a.S == 1) {
+        stage_w0(w0s_one);
+        lds_barrier();
+        const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
+        float acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[i][k] = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < 64; ++j) {
+            float av[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) av[i] = w0s_one[(r0 + i) * MP + j];
+            const f32x4 bv = *reinterpret_cast<const f32x4*>(mA + j * MP + c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[i][k] += av[i] * bv[k];
+        }
+        float* sv = a.saved ? a.saved + (long long)slice * 8192 : nullptr;
+        lds_barrier(); // every thread has read mA / W0 rows before W1 replaces C
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = r0 + i, c = c0 + k;
+                const float gv = scale * (acc[i][k] - mC[r * MP + c]);
+                mC[r * MP + c] = w0s_one[r * MP + c] - eta * gv;
+                if (sv) {
+                    sv[r * 64 + c] = mA[r * MP + c];
+                    sv[4096 + r * 64 + c] = gv;
+                }
+            }
+        lds_barrier();
+        return mC;
+    }
+
+    // S > 1: publish this workgroup's partial in reducer-major order,
+    // part[slice][j][sp][mat][r][cc] with column c = j*nc + cc: the block a
+    // reducer j gathers is then one contiguous run of S*128*nc floats.
+    const int nc = 64 / a.S, c0 = split * nc;
+    const long long sb = (long long)slice * a.S * 8192;
+    unsigned* cnt = counter_at(a.cnt, slice);
+    auto pidx = [&](int j, int sp, int mat, int r, int cc) {
+        return sb + ((long long)(j * a.S + sp) * 2 + mat) * 64 * nc + r * nc + cc;
+    };
+    if (a.xcd && nc >= 4) {
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            const int e4 = f * kThreads + tid, mat = e4 >> 10, r = (e4 >> 4) & 63, c4 = (e4 & 15) * 4;
+            *reinterpret_cast<f32x4*>(a.part + pidx(c4 / nc, split, mat, r, c4 % nc)) =
+                *reinterpret_cast<const f32x4*>((mat ? mC : mA) + r * MP + c4);
+        }
+    } else {
+#pragma unroll 8
+        for (int f = 0; f < 32; ++f) {
+            const int e = f * kThreads + tid, mat = e >> 12, r = (e >> 6) & 63, c = e & 63;
+            float* dst = a.part + pidx(c / nc, split, mat, r, c % nc);
+            const float v = (mat ? mC : mA)[r * MP + c];
+            if (a.xcd) *dst = v;
+            else xstore(dst, v);
+        }
+    }
+    slice_barrier(cnt, (unsigned)a.S);
+    if (a.xcd) l1_invalidate();
+
+    // Sum this workgroup's block of all S partials over the splits, in split
+    // order, straight from memory: the block is contiguous, value (sp, e) at
+    // blk[sp*nel + e] with e = (mat*64 + r)*nc + cc; thread t sums elements
+    // t + 256k (k < 32/S) and has all of its 32 loads in flight together.
+    const float* blk = a.part + pidx(split, 0, 0, 0, 0);
+    const int nel = 128 * nc; // >= 256 since S <= 32
+    float* res = lds;         // [mat][64][nc] reduced block
+    {
+        const int lg = __builtin_ctz(a.S); // S is a power of two
+        float v[32];
+#pragma unroll
+        for (int f = 0; f < 32; ++f) {
+            const int k = f >> lg, sp = f & (a.S - 1);
+            const float* src = blk + sp * nel + tid + k * kThreads;
+            v[f] = a.xcd ? *src : xload(src);
+        }
+        float acc = 0.f;
+#pragma unroll
+        for (int f = 0; f < 32; ++f) {
+            acc += v[f];
+            if (((f + 1) & (a.S - 1)) == 0) {
+                res[tid + (f >> lg) * kThreads] = acc;
+                acc = 0.f;
+            }
+        }
+    }
+    stage_w0(w0s_split);
+    lds_barrier();
+    float* sv = a.saved ? a.saved + (long long)slice * 8192 : nullptr;
+    float* w1g = a.w1 + (long long)slice * 4096;
+    for (int e = tid; e < 64 * nc; e += kThreads) {
+        const int r = e / nc, cc = e % nc, c = c0 + cc;
+        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < 64; j += 4) {
+            const f32x4 wv = *reinterpret_cast<const f32x4*>(w0s_split + r * MP + j);
+            acc0 += wv[0] * res[(j + 0) * nc + cc];
+            acc1 += wv[1] * res[(j + 1) * nc + cc];
+            acc2 += wv[2] * res[(j + 2) * nc + cc];
+            acc3 += wv[3] * res[(j + 3) * nc + cc];
+        }
+        const float gv = scale * (((acc0 + acc1) + (acc2 + acc3)) - res[(64 + r) * nc + cc]);
+        const float w1v = w0s_split[r * MP + c] - eta * gv;
+        if (a.xcd) w1g[r * 64 + c] = w1v;
+        else xstore(w1g + r * 64 + c, w1v);
+        if (sv) {
+            sv[r * 64 + c] = res[r * nc + cc];
+            sv[4096 + r * 64 + c] = gv;
+        }
+    }
+    slice_barrier(cnt, 2u * a.S);
+    if (a.xcd) l1_invalidate();
+    return nullptr; // W1 is complete in the workspace at a.w1 + slice*4096
+}
+
+// Counter release after the last barrier: the increment's result is only
+// needed at the very end of the kernel (reset by the last workgroup).
+__device__ __forceinline__ unsigned release_begin(const LinFwdLaunch& a, int slice) {
+    unsigned old = 0;
+    if (a.S > 1 && threadIdx.x == 0)
+        old = __hip_atomic_fetch_add(counter_at(a.cnt, slice), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return old;
+}
+__device__ __forceinline__ void release_end(const LinFwdLaunch& a, int slice, unsigned old) {
+    if (a.S > 1 && threadIdx.x == 0 && old == 3u * a.S - 1)
+        __hip_atomic_store(counter_at(a.cnt, slice), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ------------------------------------------------------------- phase 3 --
+// W1 fragments: A operand rows perm_row(rb, m) of W1 (LDS, pitch MP).
+struct W1FragsBF {
+    v8bf f[4][2];
+};
+__device__ __forceinline__ W1FragsBF w1_frags_bf(const float* mW, int g, int m) {
+    W1FragsBF w;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = perm_row(rb, m);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const float* src = mW + r * MP + 32 * hh + 8 * g;
+            u32x4 u;
+            u[0] = pack_bf2(src[0], src[1]);
+            u[1] = pack_bf2(src[2], src[3]);
+            u[2] = pack_bf2(src[4], src[5]);
+            u[3] = pack_bf2(src[6], src[7]);
+            w.f[rb][hh] = as_v8bf(u);
+        }
+    }
+    return w;
+}
+// The same fragments loaded straight from the workspace copy of W1
+// (row-major 64x64 fp32; plain loads in the XCD-local protocol).
+__device__ __forceinline__ W1FragsBF w1_frags_bf_global(const float* w1g, bool xcd, int g, int m) {
+    W1FragsBF w;
+    f32x4 v[4][2][2];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const float* src = w1g + perm_row(rb, m) * 64 + 32 * hh + 8 * g + 4 * k;
+                if (xcd) v[rb][hh][k] = *reinterpret_cast<const f32x4*>(src);
+                else v[rb][hh][k] = f32x4{xload(src), xload(src + 1), xload(src + 2), xload(src + 3)};
+            }
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const f32x4 lo = v[rb][hh][0], hi = v[rb][hh][1];
+            u32x4 u{pack_bf2(lo[0], lo[1]), pack_bf2(lo[2], lo[3]), pack_bf2(hi[0], hi[1]), pack_bf2(hi[2], hi[3])};
+            w.f[rb][hh] = as_v8bf(u);
+        }
+    return w;
+}
+struct W1FragsF32 {
+    float f[4][16];
+};
+__device__ __forceinline__ W1FragsF32 w1_frags_f32_global(const float* w1g, bool xcd, int g, int m) {
+    W1FragsF32 w;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            const float* src = w1g + perm_row(rb, m) * 64 + 16 * hh + 4 * g;
+            const f32x4 v = xcd ? *reinterpret_cast<const f32x4*>(src)
+                                : f32x4{xload(src), xload(src + 1), xload(src + 2), xload(src + 3)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w.f[rb][hh * 4 + i] = v[i];
+        }
+    return w;
+}
+__device__ __forceinline__ W1FragsF32 w1_frags_f32(const float* mW, int g, int m) {
+    W1FragsF32 w;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int r = perm_row(rb, m);
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) w.f[rb][hh * 4 + i] = mW[r * MP + 16 * hh + 4 * g + i];
+    }
+    return w;
+}
+
+// 16 tokens of Z from the lane's Q fragment q (bf16: channels 32h+8g..+8 of
+// token row m for h = 0,1; fp32: channels 16h+4g..+4 for h = 0..3).
+__device__ __forceinline__ void apply_bf(const W1FragsBF& w, const u32x4* q, char* zrow, bool ok, int g,
+                                         bool poison) {
+    v4f d[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+        d[rb] = mfma32(w.f[rb][0], as_v8bf(q[0]), d[rb]);
+        d[rb] = mfma32(w.f[rb][1], as_v8bf(q[1]), d[rb]);
+        if (poison) d[rb] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    if (ok) {
+        u32x4 o0{pack_bf2(d[0][0], d[0][1]), pack_bf2(d[0][2], d[0][3]), pack_bf2(d[1][0], d[1][1]),
+                 pack_bf2(d[1][2], d[1][3])};
+        u32x4 o1{pack_bf2(d[2][0], d[2][1]), pack_bf2(d[2][2], d[2][3]), pack_bf2(d[3][0], d[3][1]),
+                 pack_bf2(d[3][2], d[3][3])};
+        *reinterpret_cast<u32x4*>(zrow + (8 * g) * 2) = o0;
+        *reinterpret_cast<u32x4*>(zrow + (32 + 8 * g) * 2) = o1;
+    }
+}
+__device__ __forceinline__ void apply_f32(const W1FragsF32& w, const u32x4* q, char* zrow, bool ok, int g,
+                                          bool poison) {
+    v4f d[4];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) {
+            const f32x4 qv = __builtin_bit_cast(f32x4, q[hh]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) d[rb] = mfma4(w.f[rb][hh * 4 + i], qv[i], d[rb]);
+        }
+        if (poison) d[rb] = v4f{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+    }
+    if (ok) {
+        float* zr = reinterpret_cast<float*>(zrow);
+        *reinterpret_cast<f32x4*>(zr + 8 * g) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
+        *reinterpret_cast<f32x4*>(zr + 8 * g + 4) = f32x4{d[1][0], d[1][1], d[1][2], d[1][3]};
+        *reinterpret_cast<f32x4*>(zr + 32 + 8 * g) = f32x4{d[2][0], d[2][1], d[2][2], d[2][3]};
+        *reinterpret_cast<f32x4*>(zr + 36 + 8 * g) = f32x4{d[3][0], d[3][1], d[3][2], d[3][3]};
+    }
+}
+
+struct SliceCtx {
+    int slice, split, b, h, t0, t1;
+    bool poison; // XCD-local exchange assumed a placement that did not hold
+    const char *Kp, *Vp, *Qp;
+    char* Zp;
+    long long Ksn, Vsn, Qsn, Zsn;
+};
+template <bool BF> __device__ __forceinline__ SliceCtx slice_ctx(const LinFwdLaunch& a) {
+    constexpr int esz = LinCfg<BF>::esz;
+    SliceCtx c;
+    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
+    c.slice = ss.slice;
+    c.split = ss.split;
+    c.b = c.slice / a.H;
+    c.h = c.slice % a.H;
+    const int per = (((a.N + a.S - 1) / a.S) + 15) & ~15;
+    c.t0 = min(a.N, c.split * per);
+    c.t1 = min(a.N, c.t0 + per);
+    c.Kp = (const char*)a.K.ptr + (c.b * a.K.sb + c.h * a.K.sh) * (long long)esz;
+    c.Vp = (const char*)a.V.ptr + (c.b * a.V.sb + c.h * a.V.sh) * (long long)esz;
+    c.Qp = (const char*)a.Q.ptr + (c.b * a.Q.sb + c.h * a.Q.sh) * (long long)esz;
+    c.Zp = (char*)a.Z.ptr + (c.b * a.Z.sb + c.h * a.Z.sh) * (long long)esz;
+    c.Ksn = a.K.sn * esz;
+    c.Vsn = a.V.sn * esz;
+    c.Qsn = a.Q.sn * esz;
+    c.Zsn = a.Z.sn * esz;
+    c.poison = a.xcd && ((xcc_id() & 7) != (blockIdx.x & 7));
+    return c;
+}
+
+__device__ __forceinline__ void load_w0(const LinFwdLaunch& a, int h, f32x4* w0r) {
+    const float* W0h = a.W0 + (long long)h * 4096;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w0r[k] = *reinterpret_cast<const f32x4*>(W0h + 4 * threadIdx.x + 1024 * k);
+}
+
+// Sum the four waves' 26 tiles.  Wave (t % 4) owns tile t: the other
+// waves leave their copy in `red` (3 slots per tile, 78 KB), the owner adds
+// them to its own in the fixed order ((w0 + w1) + w2) + w3 and writes the
+// result as row-major matrices mA / mC (which may overlap `red`: they are
+// written after a barrier).
+__device__ __forceinline__ void reduce_waves(v4f* accC, v4f* accA, float* red, float* mA, float* mC,
+                                             int w, int lane, int g, int m, bool overlap) {
+    auto tile_ref = [&](int t) -> v4f& { return t < 16 ? accC[t] : accA[t - 16]; };
+    auto slot = [&](int t, int src) { return (t * 3 + (src < (t & 3) ? src : src - 1)) * 256 + lane * 4; };
+#pragma unroll
+    for (int t = 0; t < 26; ++t)
+        if ((t & 3) != w) *reinterpret_cast<v4f*>(red + slot(t, w)) = tile_ref(t);
+    lds_barrier();
+#pragma unroll
+    for (int t = 0; t < 26; ++t) {
+        if ((t & 3) == w) {
+            v4f parts[4];
+#pragma unroll
+            for (int src = 0; src < 4; ++src)
+                parts[src] = src == w ? tile_ref(t) : *reinterpret_cast<const v4f*>(red + slot(t, src));
+            tile_ref(t) = ((parts[0] + parts[1]) + parts[2]) + parts[3];
+        }
+    }
+    if (overlap) lds_barrier(); // mA / mC overlap `red`
+#pragma unroll
+    for (int t = 0; t < 26; ++t)
+        if ((t & 3) == w) write_tile(tile_ref(t), t, mA, mC, g, m);
+    lds_barrier();
+}
+
+// ------------------------------------------------------ resident kernel --
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) {
     using Cfg = LinCfg<BF>;
-    __shared__ __attribute__((aligned(16))) float lds[kLdsFloats];
+    constexpr int RS = Cfg::row_slots;
+    constexpr int TB = Cfg::tmax * RS * 16; // bytes of one tensor region
+    constexpr int SPARE = 16384;            // lets [A; C] sit beside the wave sums
+    __shared__ __attribute__((aligned(16))) char lds[3 * TB + SPARE];
+    float* ldsf = reinterpret_cast<float*>(lds);
+    char* Ks = lds;
+    char* Vs = lds + TB;
+    char* Qs = lds + 2 * TB + SPARE;
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    const SliceCtx c = slice_ctx<BF>(a);
+    if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    const int T = c.t1 - c.t0;
+
+    // ---- every load of the workgroup, issued up front
+    if (T > 0) {
+        const int rows = (T + 31) & ~31;
+        const int ninstr = rows * RS / 64; // 1 KB per wave instruction
+        for (int q = w; q < ninstr; q += 4) {
+            const int p = q * 64 + lane;
+            const int row = p / RS;
+            const int okv = ((p % RS) ^ swz_kv<BF>(row)) * 16;
+            const int oq = ((p % RS) ^ swz_q<BF>(row)) * 16;
+            const long long tok = c.t0 + min(row, T - 1);
+            __builtin_amdgcn_global_load_lds((const void*)(c.Kp + tok * c.Ksn + okv), (lds_void*)(Ks + q * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(c.Vp + tok * c.Vsn + okv), (lds_void*)(Vs + q * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds((const void*)(c.Qp + tok * c.Qsn + oq), (lds_void*)(Qs + q * 1024), 16, 0, 0);
+        }
+    }
+    f32x4 w0r[4];
+    load_w0(a, c.h, w0r);
+    __syncthreads(); // waits for the direct-to-LDS loads
+    // rows past the range hold clamped copies: zero them in K and V so the
+    // Gram fragments need no masking
+    {
+        const int rows = (T + 31) & ~31;
+        for (int e = tid; e < (rows - T) * RS; e += kThreads) {
+            const int off = (T + e / RS) * RS * 16 + (e % RS) * 16;
+            *reinterpret_cast<u32x4*>(Ks + off) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Vs + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+        lds_barrier();
+    }
+
+    // ---- phase 1: Gram blocks
+    v4f accC[16], accA[10];
+#pragma unroll
+    for (int t = 0; t < 16; ++t) accC[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 10; ++t) accA[t] = v4f{0.f, 0.f, 0.f, 0.f};
+    constexpr int KS = BF ? 32 : 16; // tokens per wave k-step
+    const GramLanes gl = gram_lanes(g, m);
+    for (int r0 = w * KS; r0 < T; r0 += 4 * KS) gram_step<BF>(Ks, Vs, r0, gl, accC, accA, g, m);
+    lds_barrier();
+    // K/V regions are free now: 3 x 26 tiles of wave sums at the bottom,
+    // [A; C] right above them; the Q region stays intact for phase 3
+    float* mA = ldsf + 3 * 26 * 256;
+    float* mC = mA + 64 * MP;
+    reduce_waves(accC, accA, ldsf, mA, mC, w, lane, g, m, false);
+
+    // ---- phase 2
+    float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r);
+
+    // ---- phase 3: Z from the resident Q region
+    const int nsteps = (T + 15) / 16;
+    const float* w1g = a.w1 + (long long)c.slice * 4096;
+    if constexpr (BF) {
+        const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
+        const unsigned rel = release_begin(a, c.slice);
+#pragma unroll 2
+        for (int step = w; step < nsteps; step += 4) {
+            const int row = step * 16 + m;
+            u32x4 q[2];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+                q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 8 + ((4 * hh + g) ^ swz_q<true>(row))) * 16);
+            apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+        }
+        release_end(a, c.slice, rel);
+    } else {
+        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
+        const unsigned rel = release_begin(a, c.slice);
+        for (int step = w; step < nsteps; step += 4) {
+            const int row = step * 16 + m;
+            u32x4 q[4];
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh)
+                q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 16 + ((4 * hh + g) ^ swz_q<false>(row))) * 16);
+            apply_f32(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+        }
+        release_end(a, c.slice, rel);
+    }
+}
+
+// resident kernel, floats below the Q region: wave sums + [A; C] (phase 1),
+// gather staging / W0 / W1 (phase 2)
+static_assert(3 * 26 * 256 + 2 * 64 * MP <= (2 * LinCfg<true>::tmax * 8 * 16 + 16384) / 4, "resident LDS (bf16)");
+static_assert(3 * 26 * 256 + 2 * 64 * MP <= (2 * LinCfg<false>::tmax * 16 * 16 + 16384) / 4, "resident LDS (fp32)");
+static_assert(8192 + 128 + 64 * MP <= 3 * 26 * 256, "phase-2 regions below [A; C]");
+
+// ----------------------------------------------------- streaming kernel --
+constexpr int kStages = 3;         // K/V tiles in flight (registers)
+constexpr int kStageBytes = 32768; // K tile + V tile
+
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
+    using Cfg = LinCfg<BF>;
+    // 64 KB of double-buffered K/V tiles during phase 1; the 78 KB of wave
+    // sums need the rest afterwards
+    __shared__ __attribute__((aligned(16))) float lds[20480]; // 80 KB
     char* ldsb = reinterpret_cast<char*>(lds);
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, m = lane & 15;
-    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
-    const int slice = ss.slice, split = ss.split;
-    const int b = slice / a.H, h = slice % a.H;
-    const int N = a.N;
-    const int per = (((N + a.S - 1) / a.S) + 15) & ~15;
-    const int t0 = min(N, split * per), t1 = min(N, t0 + per);
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    const SliceCtx c = slice_ctx<BF>(a);
+    if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    const int t0 = c.t0, t1 = c.t1;
 
-    const char* Kp = (const char*)a.K.ptr + (b * a.K.sb + h * a.K.sh) * (long long)Cfg::esz;
-    const char* Vp = (const char*)a.V.ptr + (b * a.V.sb + h * a.V.sh) * (long long)Cfg::esz;
-    const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)Cfg::esz;
-    char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)Cfg::esz;
-    const long long Ksn = a.K.sn * Cfg::esz, Vsn = a.V.sn * Cfg::esz;
-    const long long Qsn = a.Q.sn * Cfg::esz, Zsn = a.Z.sn * Cfg::esz;
-
-    // ------------------------------------------------------------ phase 1
     v4f accC[16], accA[10];
 #pragma unroll
     for (int t = 0; t < 16; ++t) accC[t] = v4f{0.f, 0.f, 0.f, 0.f};
@@ -115,73 +657,21 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
             const int p = j * kThreads + tid;
             const int row = min(p / Cfg::row_slots, nvalid - 1);
             const int off = (p % Cfg::row_slots) * 16;
-            r[j] = *reinterpret_cast<const u32x4*>(Kp + (long long)(tb + row) * Ksn + off);
-            r[4 + j] = *reinterpret_cast<const u32x4*>(Vp + (long long)(tb + row) * Vsn + off);
+            r[j] = *reinterpret_cast<const u32x4*>(c.Kp + (long long)(tb + row) * c.Ksn + off);
+            r[4 + j] = *reinterpret_cast<const u32x4*>(c.Vp + (long long)(tb + row) * c.Vsn + off);
         }
     };
-    auto store_tile = [&](const u32x4* r, char* st) __attribute__((always_inline)) {
+    // rows past the range (clamped copies) are stored as zeros
+    auto store_tile = [&](const u32x4* r, char* st, int nvalid) __attribute__((always_inline)) {
+        const u32x4 z{0u, 0u, 0u, 0u};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int p = j * kThreads + tid;
             const int row = p / Cfg::row_slots;
-            const int slot = row * Cfg::row_slots + ((p % Cfg::row_slots) ^ swz<BF>(row));
-            *reinterpret_cast<u32x4*>(st + slot * 16) = r[j];
-            *reinterpret_cast<u32x4*>(st + 16384 + slot * 16) = r[4 + j];
-        }
-    };
-    auto compute_tile = [&](int it, const char* sK) __attribute__((always_inline)) {
-        const char* sV = sK + 16384;
-        const int nvalid = t1 - (t0 + it * Cfg::tile);
-        if constexpr (BF) {
-            // lane (g, m) gathers tokens 32w + 8g + j (j = 0..7) of channel
-            // 16cb + m: the k-major operand layout of the 16x16x32 MFMA
-            v8bf kf[4], vf[4];
-#pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int c = 16 * cb + m;
-                v8s kv, vv;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int row = 32 * w + 8 * g + j;
-                    const int addr = (row * 8 + ((c >> 3) ^ swz<true>(row))) * 16 + (c & 7) * 2;
-                    const bool ok = row < nvalid;
-                    kv[j] = ok ? *reinterpret_cast<const short*>(sK + addr) : (short)0;
-                    vv[j] = ok ? *reinterpret_cast<const short*>(sV + addr) : (short)0;
-                }
-                kf[cb] = __builtin_bit_cast(v8bf, kv);
-                vf[cb] = __builtin_bit_cast(v8bf, vv);
-            }
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) accC[rb * 4 + cb] = mfma32(vf[rb], kf[cb], accC[rb * 4 + cb]);
-            int t = 0;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = rb; cb < 4; ++cb, ++t) accA[t] = mfma32(kf[rb], kf[cb], accA[t]);
-        } else {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int row = 16 * w + 4 * s + g;
-                float kf[4], vf[4];
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb) {
-                    const int c = 16 * cb + m;
-                    const int addr = (row * 16 + ((c >> 2) ^ swz<false>(row))) * 16 + (c & 3) * 4;
-                    kf[cb] = row < nvalid ? *reinterpret_cast<const float*>(sK + addr) : 0.f;
-                    vf[cb] = row < nvalid ? *reinterpret_cast<const float*>(sV + addr) : 0.f;
-                }
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                    for (int cb = 0; cb < 4; ++cb) accC[rb * 4 + cb] = mfma4(vf[rb], kf[cb], accC[rb * 4 + cb]);
-                int t = 0;
-#pragma unroll
-                for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                    for (int cb = rb; cb < 4; ++cb, ++t) accA[t] = mfma4(kf[rb], kf[cb], accA[t]);
-            }
+            const int slot = row * Cfg::row_slots + ((p % Cfg::row_slots) ^ swz_kv<BF>(row));
+            const bool ok = row < nvalid;
+            *reinterpret_cast<u32x4*>(st + slot * 16) = ok ? r[j] : z;
+            *reinterpret_cast<u32x4*>(st + 16384 + slot * 16) = ok ? r[4 + j] : z;
         }
     };
 
@@ -189,10 +679,8 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
 #pragma unroll
         for (int s = 0; s < kStages; ++s) load_tile(min(s, ntiles - 1), R[s]);
     }
-
-    // Prefetch this wave's first Q tiles for the apply (16 tokens per step,
-    // steps w, w+4, ...).  Token rows are clamped into the range (a clamped
-    // step is never applied), so the loads are unconditional.
+    // Prefetch this wave's first Q steps (16 tokens each, steps w, w+4, ...);
+    // rows are clamped into the range, so the loads are unconditional.
     const int nsteps = (t1 - t0 + 15) / 16;
     constexpr int QV = BF ? 2 : 4; // 16-byte loads per lane per step
     u32x4 qpre[Cfg::qpre][QV];
@@ -203,10 +691,12 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
 #pragma unroll
             for (int hh = 0; hh < QV; ++hh) {
                 const int ch = BF ? (32 * hh + 8 * g) : (16 * hh + 4 * g);
-                qpre[k][hh] = *reinterpret_cast<const u32x4*>(Qp + tok * Qsn + ch * Cfg::esz);
+                qpre[k][hh] = *reinterpret_cast<const u32x4*>(c.Qp + tok * c.Qsn + ch * Cfg::esz);
             }
         }
     }
+    f32x4 w0r[4];
+    load_w0(a, c.h, w0r);
 
     // Pipelined tile loop: tile it is written from its registers into LDS
     // buffer it&1, the registers are refilled with tile it+3, then the
@@ -214,12 +704,14 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
     // unconditional inside the main loop and the first loads are clamped
     // duplicates for short ranges, so the compiler's load counters stay
     // exact and three tiles remain in flight.
+    const GramLanes gl = gram_lanes(g, m);
     auto step = [&](int it, u32x4* r, bool reload) __attribute__((always_inline)) {
         char* st = ldsb + (it & 1) * kStageBytes;
-        store_tile(r, st);
+        store_tile(r, st, t1 - (t0 + it * Cfg::tile));
         lds_barrier();
         if (reload) load_tile(it + kStages, r);
-        compute_tile(it, st);
+        constexpr int KS = BF ? 32 : 16;
+        gram_step<BF>(st, st + 16384, w * KS, gl, accC, accA, g, m);
     };
     if (ntiles > 0) {
         int it = 0;
@@ -235,277 +727,115 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_kernel(LinFwdLaunch a) {
         }
     }
     lds_barrier();
+    // staging buffers are free: wave sums, then [A; C] over them (wave 0
+    // reads every sum before it writes the matrices)
+    float* mA = lds;
+    float* mC = lds + 64 * MP;
+    reduce_waves(accC, accA, lds, mA, mC, w, lane, g, m, true);
 
-    // ------------------------------------------------ wave reduction of [A;C]
-    // Fixed order ((w3 + w2) + w1) + w0 through one 26-tile LDS buffer.
-    {
-        float* red = lds + RED;
-        auto tile_ref = [&](int t) -> v4f& { return t < 16 ? accC[t] : accA[t - 16]; };
-#pragma unroll
-        for (int src = 3; src >= 1; --src) {
-            if (w == src) {
-#pragma unroll
-                for (int t = 0; t < 26; ++t) {
-                    if (src < 3) tile_ref(t) += *reinterpret_cast<const v4f*>(red + t * 256 + lane * 4);
-                    *reinterpret_cast<v4f*>(red + t * 256 + lane * 4) = tile_ref(t);
-                }
-            }
-            lds_barrier();
-        }
-        if (w == 0) {
-            float* mA = lds + MAT_A;
-            float* mC = lds + MAT_C;
-#pragma unroll
-            for (int t = 0; t < 26; ++t)
-                tile_ref(t) += *reinterpret_cast<const v4f*>(red + t * 256 + lane * 4);
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        mC[(16 * rb + 4 * g + i) * MP + 16 * cb + m] = accC[rb * 4 + cb][i];
-            int t = 0;
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-                for (int cb = rb; cb < 4; ++cb, ++t)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float v = accA[t][i];
-                        mA[(16 * rb + 4 * g + i) * MP + 16 * cb + m] = v;
-                        if (rb < cb) mA[(16 * cb + m) * MP + 16 * rb + 4 * g + i] = v;
-                    }
-        }
-        lds_barrier();
-    }
+    float* W1 = lin_update(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r);
 
-    // ----------------------------------------------- phase 2: G and W1
-    const float* W0h = a.W0 + (long long)h * 4096;
-    const float eta = a.eta[h];
-    const float scale = 2.0f / (float)N;
-    float* mA = lds + MAT_A;
-    float* mC = lds + MAT_C;
-    float* mW = lds + MAT_W;
-    float* W0s = lds + W0S;
-    auto stage_w0 = [&]() {
-        for (int e = tid; e < 1024; e += kThreads) {
-            const int r = e >> 4, c4 = (e & 15) * 4;
-            *reinterpret_cast<f32x4*>(W0s + r * MP + c4) = *reinterpret_cast<const f32x4*>(W0h + r * 64 + c4);
-        }
-    };
-    if (a.S == 1) {
-        stage_w0();
-        lds_barrier();
-        const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
-        float acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) acc[i][k] = 0.f;
-        for (int j = 0; j < 64; ++j) {
-            float av[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) av[i] = W0s[(r0 + i) * MP + j];
-            const f32x4 bv = *reinterpret_cast<const f32x4*>(mA + j * MP + c0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                acc[i][0] += av[i] * bv.x;
-                acc[i][1] += av[i] * bv.y;
-                acc[i][2] += av[i] * bv.z;
-                acc[i][3] += av[i] * bv.w;
-            }
-        }
-        float* sv = a.saved ? a.saved + (long long)slice * 8192 : nullptr;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int r = r0 + i, c = c0 + k;
-                const float gv = scale * (acc[i][k] - mC[r * MP + c]);
-                mW[r * MP + c] = W0s[r * MP + c] - eta * gv;
-                if (sv) {
-                    sv[r * 64 + c] = mA[r * MP + c];
-                    sv[4096 + r * 64 + c] = gv;
-                }
-            }
-        lds_barrier();
-    } else {
-        float* P = a.part + ((long long)slice * a.S + split) * 8192;
-        for (int e = tid; e < 2048; e += kThreads) {
-            const int mat = e >> 10, idx = e & 1023, r = idx >> 4, c4 = (idx & 15) * 4;
-            const float* src = (mat ? mC : mA) + r * MP + c4;
-            *reinterpret_cast<f32x4*>(P + mat * 4096 + r * 64 + c4) = *reinterpret_cast<const f32x4*>(src);
-        }
-        slice_barrier(a.cnt + slice, (unsigned)a.S);
-        const int c0 = (64 * split) / a.S, c1 = (64 * (split + 1)) / a.S, nc = c1 - c0;
-        const float* P0 = a.part + (long long)slice * a.S * 8192;
-        for (int e = tid; e < 2 * 64 * nc; e += kThreads) {
-            const int mat = e / (64 * nc), rem = e % (64 * nc), r = rem / nc, c = c0 + rem % nc;
-            const float* src = P0 + mat * 4096 + r * 64 + c;
-            float s = 0.f;
-            for (int sp = 0; sp < a.S; ++sp) s += src[(long long)sp * 8192];
-            (mat ? mC : mA)[r * MP + c] = s;
-        }
-        stage_w0();
-        lds_barrier();
-        float* sv = a.saved ? a.saved + (long long)slice * 8192 : nullptr;
-        float* w1g = a.w1 + (long long)slice * 4096;
-        for (int e = tid; e < 64 * nc; e += kThreads) {
-            const int r = e / nc, c = c0 + e % nc;
-            float acc = 0.f;
-            for (int j = 0; j < 64; ++j) acc += W0s[r * MP + j] * mA[j * MP + c];
-            const float gv = scale * (acc - mC[r * MP + c]);
-            w1g[r * 64 + c] = W0s[r * MP + c] - eta * gv;
-            if (sv) {
-                sv[r * 64 + c] = mA[r * MP + c];
-                sv[4096 + r * 64 + c] = gv;
-            }
-        }
-        slice_barrier(a.cnt + slice, 2u * a.S);
-        for (int e = tid; e < 1024; e += kThreads) {
-            const int r = e >> 4, c4 = (e & 15) * 4;
-            *reinterpret_cast<f32x4*>(mW + r * MP + c4) = *reinterpret_cast<const f32x4*>(w1g + r * 64 + c4);
-        }
-        slice_barrier_release(a.cnt + slice, 3u * a.S);
-        lds_barrier();
-    }
-
-    // ------------------------------------------------------ phase 3: apply
+    const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
-        v8bf wf[4][2];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int r = perm_row(rb, m);
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-                const float* src = mW + r * MP + 32 * hh + 8 * g;
-                u32x4 u;
-                u.x = pack_bf2(src[0], src[1]);
-                u.y = pack_bf2(src[2], src[3]);
-                u.z = pack_bf2(src[4], src[5]);
-                u.w = pack_bf2(src[6], src[7]);
-                wf[rb][hh] = as_v8bf(u);
-            }
-        }
-        auto apply = [&](int step, const u32x4* q) {
-            v4f d[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-                d[rb] = mfma32(wf[rb][0], as_v8bf(q[0]), d[rb]);
-                d[rb] = mfma32(wf[rb][1], as_v8bf(q[1]), d[rb]);
-            }
-            const int tok = t0 + step * 16 + m;
-            if (tok < t1) {
-                u32x4 o0{pack_bf2(d[0][0], d[0][1]), pack_bf2(d[0][2], d[0][3]),
-                         pack_bf2(d[1][0], d[1][1]), pack_bf2(d[1][2], d[1][3])};
-                u32x4 o1{pack_bf2(d[2][0], d[2][1]), pack_bf2(d[2][2], d[2][3]),
-                         pack_bf2(d[3][0], d[3][1]), pack_bf2(d[3][2], d[3][3])};
-                *reinterpret_cast<u32x4*>(Zp + tok * Zsn + (8 * g) * 2) = o0;
-                *reinterpret_cast<u32x4*>(Zp + tok * Zsn + (32 + 8 * g) * 2) = o1;
-            }
-        };
+        const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
+        const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
-            const int step = w + 4 * k;
-            if (step < nsteps) apply(step, qpre[k]);
+            const int st = w + 4 * k;
+            const int tok = t0 + st * 16 + m;
+            if (st < nsteps) apply_bf(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
         }
-        for (int step = w + 4 * Cfg::qpre; step < nsteps; step += 4) {
-            const int tok = min(t0 + step * 16 + m, t1 - 1);
+        for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
+            const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
             u32x4 q[2];
-            q[0] = *reinterpret_cast<const u32x4*>(Qp + tok * Qsn + (8 * g) * 2);
-            q[1] = *reinterpret_cast<const u32x4*>(Qp + tok * Qsn + (32 + 8 * g) * 2);
-            apply(step, q);
+            q[0] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (8 * g) * 2);
+            q[1] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (32 + 8 * g) * 2);
+            apply_bf(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
         }
+        release_end(a, c.slice, rel);
     } else {
-        float wf[4][16];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-            const int r = perm_row(rb, m);
-#pragma unroll
-            for (int hh = 0; hh < 4; ++hh)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) wf[rb][hh * 4 + i] = mW[r * MP + 16 * hh + 4 * g + i];
-        }
-        auto apply = [&](int step, const u32x4* q) {
-            v4f d[4];
-#pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int hh = 0; hh < 4; ++hh) {
-                    const f32x4 qv = __builtin_bit_cast(f32x4, q[hh]);
-                    d[rb] = mfma4(wf[rb][hh * 4 + 0], qv.x, d[rb]);
-                    d[rb] = mfma4(wf[rb][hh * 4 + 1], qv.y, d[rb]);
-                    d[rb] = mfma4(wf[rb][hh * 4 + 2], qv.z, d[rb]);
-                    d[rb] = mfma4(wf[rb][hh * 4 + 3], qv.w, d[rb]);
-                }
-            }
-            const int tok = t0 + step * 16 + m;
-            if (tok < t1) {
-                float* zr = reinterpret_cast<float*>(Zp + tok * Zsn);
-                *reinterpret_cast<f32x4*>(zr + 8 * g) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
-                *reinterpret_cast<f32x4*>(zr + 8 * g + 4) = f32x4{d[1][0], d[1][1], d[1][2], d[1][3]};
-                *reinterpret_cast<f32x4*>(zr + 32 + 8 * g) = f32x4{d[2][0], d[2][1], d[2][2], d[2][3]};
-                *reinterpret_cast<f32x4*>(zr + 36 + 8 * g) = f32x4{d[3][0], d[3][1], d[3][2], d[3][3]};
-            }
-        };
+        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
+        const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
-            const int step = w + 4 * k;
-            if (step < nsteps) apply(step, qpre[k]);
+            const int st = w + 4 * k;
+            const int tok = t0 + st * 16 + m;
+            if (st < nsteps) apply_f32(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
         }
-        for (int step = w + 4 * Cfg::qpre; step < nsteps; step += 4) {
-            const int tok = min(t0 + step * 16 + m, t1 - 1);
+        for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
+            const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
             u32x4 q[4];
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh)
-                q[hh] = *reinterpret_cast<const u32x4*>(Qp + tok * Qsn + (16 * hh + 4 * g) * 4);
-            apply(step, q);
+                q[hh] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (16 * hh + 4 * g) * 4);
+            apply_f32(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
         }
+        release_end(a, c.slice, rel);
     }
+}
+
+int pow2_floor(long long s) {
+    int p = 1;
+    while (2LL * p <= s) p *= 2;
+    return p;
+}
+
+int occupancy(const void* fn, std::atomic<int>& cache) {
+    int n = cache.load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) != hipSuccess || n < 0) return 0;
+    cache.store(n, std::memory_order_relaxed);
+    return n;
 }
 
 } // namespace
 
 int lin_fwd_max_splits(int B, int H, int N) {
+    // a power of two (the reduction gathers 64/S columns), at most 64, about
+    // 128 tokens per split, and no more workgroups than one MI355X keeps
+    // resident (256 CUs x 1)
     const long long slices = (long long)B * H;
     if (slices <= 0 || N <= 0) return 1;
-    // at most 64 splits, at least ~128 tokens each, and no more workgroups
-    // than one MI355X keeps resident (256 CUs x 1)
+    const long long padded = (slices + 7) / 8 * 8; // XCD-aware grids round slices up to 8
     long long s = (N + 127) / 128;
-    if (s > 64) s = 64;
-    const long long cap = 256 / slices;
-    if (s > cap) s = cap;
-    return s < 1 ? 1 : (int)s;
+    if (s > 32) s = 32; // the reduction sums 32/S elements per thread
+    int p = pow2_floor(s);
+    if (p < s) p *= 2;
+    while (p > 1 && p * padded > 256) p /= 2;
+    return p;
 }
 
 size_t lin_fwd_ws_bytes(int B, int H, int N) {
     const long long slices = (long long)B * H;
     const int S = lin_fwd_max_splits(B, H, N);
     if (S <= 1) return 0;
-    const size_t cnt = ((size_t)slices * 4 + 255) & ~(size_t)255;
-    return cnt + (size_t)slices * S * 8192 * 4 + (size_t)slices * 4096 * 4;
+    return kCounterBytes + (size_t)slices * S * 8192 * 4 + (size_t)slices * 4096 * 4;
 }
 
 int lin_fwd_resident_per_cu(int bf16) {
-    static std::atomic<int> cached[2];
-    int n = cached[bf16 ? 1 : 0].load(std::memory_order_relaxed);
-    if (n > 0) return n;
-    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lin_fwd_kernel<true>, kThreads, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, lin_fwd_kernel<false>, kThreads, 0);
-    if (e != hipSuccess || n < 0) return 0;
-    cached[bf16 ? 1 : 0].store(n, std::memory_order_relaxed);
-    return n;
+    static std::atomic<int> cache[4];
+    const int r = bf16 ? occupancy((const void*)lin_fwd_resident<true>, cache[0])
+                       : occupancy((const void*)lin_fwd_resident<false>, cache[1]);
+    const int s = bf16 ? occupancy((const void*)lin_fwd_stream<true>, cache[2])
+                       : occupancy((const void*)lin_fwd_stream<false>, cache[3]);
+    return r < s ? r : s;
 }
 
-hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident_wgs) {
+bool lin_fwd_is_resident(int N, int S, int bf16) {
+    const int per = (((N + S - 1) / S) + 15) & ~15;
+    return per <= (bf16 ? LinCfg<true>::tmax : LinCfg<false>::tmax);
+}
+
+hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     const long long slices = (long long)a.B * a.H;
-    (void)resident_wgs;
-    const dim3 grid((unsigned)(slices * a.S)), block(kThreads);
+    const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
+    const dim3 grid((unsigned)(gslices * a.S)), block(kThreads);
     void* args[] = {&a};
-    const void* fn = a.bf16 ? (const void*)lin_fwd_kernel<true> : (const void*)lin_fwd_kernel<false>;
+    const void* fn;
+    if (resident)
+        fn = a.bf16 ? (const void*)lin_fwd_resident<true> : (const void*)lin_fwd_resident<false>;
+    else
+        fn = a.bf16 ? (const void*)lin_fwd_stream<true> : (const void*)lin_fwd_stream<false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
