@@ -191,6 +191,14 @@ def test_scan_errors():
     assert bd.STATUS_NAMES[scan(P(b=0))] == "TTT_ERR_BAD_SHAPE"
     assert bd.STATUS_NAMES[scan(P(b=17))] == "TTT_ERR_UNSUPPORTED"
     assert bd.STATUS_NAMES[scan(P(mode=3))] == "TTT_ERR_UNSUPPORTED"
+    # the scan runs bf16 matrix-core products only
+    assert bd.STATUS_NAMES[scan(P(dtype=bd.TTT_F32))] == "TTT_ERR_UNSUPPORTED"
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P()))
+    assert bd.STATUS_NAMES[scan(P(), wsb=need - 1)] == "TTT_ERR_WORKSPACE_TOO_SMALL"
+    # the averaged scan keeps one fp32 output per token and direction
+    one = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P(mode=1)))
+    assert need - one >= 2 * 2 * 3 * 100 * 64 * 4
     assert bd.STATUS_NAMES[scan(P(), Z=V(2))] == "TTT_ERR_ALIASING"
     assert scan(P(B=0)) == 0
 

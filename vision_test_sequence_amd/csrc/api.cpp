@@ -241,6 +241,7 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     if (p->mode != TTT_BIDIR_AVG && p->mode != TTT_FORWARD_ONLY && p->mode != TTT_BACKWARD_ONLY)
         return TTT_ERR_UNSUPPORTED;
     if (p->minibatch > 16) return TTT_ERR_UNSUPPORTED;
+    if (p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
     if (noop) return TTT_OK;
     Span in[5], out[2];
     if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
