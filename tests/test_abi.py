@@ -220,6 +220,11 @@ def test_bwd_errors():
     assert bd.STATUS_NAMES[bwd(P(), dW0=addr(10))] == "TTT_ERR_ALIASING"
     assert bd.STATUS_NAMES[bwd(P(), dW0=None)] == "TTT_ERR_NULL_POINTER"
     assert bd.STATUS_NAMES[bwd(P(), saved=addr(7))] == "TTT_ERR_ALIASING"
+    L = vt.lib()
+    need = L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH_BWD, ctypes.byref(P()))
+    # per-slice dW1 shares, dW1 and M, dW0 and deta terms, recomputed A and G
+    assert need >= 2 * 3 * (8192 + 4096 + 8192 + 4096) * 4
+    assert bd.STATUS_NAMES[bwd(P(), wsb=need - 1)] == "TTT_ERR_WORKSPACE_TOO_SMALL"
     assert bwd(P(B=0)) == 0
 
 

@@ -153,27 +153,12 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     return 0;
 }
 
-ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
-                                const float* W0, const float* eta, ttt_view Z, float* saved,
-                                void* ws, size_t ws_bytes, ttt_stream_t stream) {
-    bool noop = false;
-    ttt_status st = check_problem(p, &noop);
-    if (st != TTT_OK || noop) return st;
-    Span in[5], out[3];
-    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
-    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
-    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
-    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
-    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
-    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
-    if (saved && (st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &out[1])) != TTT_OK)
-        return st;
-    const size_t need = lin_fwd_ws_bytes(p->B, p->H, p->N);
-    if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
-    if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
-
+// Plan and launch the full-batch forward (validated arguments).  A null Z
+// computes only A and G into `saved`.
+static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* W0,
+                                   const float* eta, float* saved, void* ws, hipStream_t stream) {
     LinFwdLaunch a{};
-    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    a.K = K; a.Q = Q; a.V = V; a.Z = Z;
     a.W0 = W0; a.eta = eta; a.saved = saved;
     a.B = p->B; a.H = p->H; a.N = p->N;
     a.bf16 = p->dtype == TTT_BF16;
@@ -195,7 +180,29 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
         a.part = (float*)(base + kCounterBytes);
         a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 8192 * 4);
     }
-    return hip_status(launch_lin_fwd(a, (hipStream_t)stream, lin_fwd_is_resident(p->N, S, a.bf16) ? 1 : 0));
+    return hip_status(launch_lin_fwd(a, stream, lin_fwd_is_resident(p->N, S, a.bf16) ? 1 : 0));
+}
+
+ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                const float* W0, const float* eta, ttt_view Z, float* saved,
+                                void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK || noop) return st;
+    Span in[5], out[3];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    if (saved && (st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &out[1])) != TTT_OK)
+        return st;
+    const size_t need = lin_fwd_ws_bytes(p->B, p->H, p->N);
+    if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
+
+    return launch_fullbatch(p, v4(K), v4(Q), v4(V), v4(Z), W0, eta, saved, ws, (hipStream_t)stream);
 }
 
 ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
@@ -300,6 +307,14 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
     a.B = p->B; a.H = p->H; a.N = p->N;
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
+    if (!saved) {
+        // recompute A and G with the forward's Gram pass, into the workspace
+        float* sv = lin_bwd_saved_region(ws, p->B, p->H, p->N);
+        const View4 none{nullptr, 0, 0, 0};
+        st = launch_fullbatch(p, a.K, a.K, a.V, none, W0, eta, sv, ws, (hipStream_t)stream);
+        if (st != TTT_OK) return st;
+        a.saved = sv;
+    }
     return hip_status(launch_lin_bwd(a, (hipStream_t)stream));
 }
 

@@ -144,6 +144,14 @@ __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned to
 // blocks {8*(S*(s/8) + j) + s%8 : j < S}; the grid is padded to
 // 8 * ceil(slices/8) * S blocks and blocks of padding slices (>= slices)
 // have no work.  Plain mapping: slice = block / S.
+// Output-row permutation of the 16x16 apply products: MFMA row m of output
+// block rb -> output channel, so that lane (g, .) owns the contiguous
+// channels [8g, 8g+8) (blocks 0,1) and [32+8g, 32+8g+8) (blocks 2,3) and
+// stores them as whole 16-byte (bf16) or 32-byte (fp32) runs.
+__device__ __forceinline__ int perm_row(int rb, int m) {
+    return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
+}
+
 struct SliceSplit {
     int slice, split;
 };

@@ -74,6 +74,8 @@ struct LinBwdLaunch {
     void* ws;         // lin_bwd_ws_bytes(...) bytes
 };
 size_t lin_bwd_ws_bytes(int B, int H, int N);
+// A and G recomputed by the forward's Gram pass when the caller saved none
+float* lin_bwd_saved_region(void* ws, int B, int H, int N);
 hipError_t launch_lin_bwd(LinBwdLaunch a, hipStream_t stream);
 
 } // namespace ttt

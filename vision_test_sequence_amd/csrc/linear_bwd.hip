@@ -1,6 +1,529 @@
+// linear_bwd.hip -- gradient of the full-batch linear TTT step, gfx950.
+//
+// Forward (ViT^3 page, the inner linear model and its one full-batch
+// gradient step; the gradient itself is what end-to-end training needs,
+// the page's section on the "gradient of the gradient"):
+//   G = (2/N) (W0 A - C),  A = K^T K,  C = V^T K,  W1 = W0 - eta G,  Z = Q W1^T.
+// Backward of L(dZ) = <dZ, Z>, with beta = 2 eta / N:
+//   dW1 = dZ^T Q                          (reduction over the tokens)
+//   dQ  = dZ W1
+//   M   = W0^T dW1 + dW1^T W0             (symmetric)
+//   dK  = beta (V dW1 - K M)
+//   dV  = beta K dW1^T
+//   dW0 = sum_b dW1 (I - beta A),  deta = -sum_b <dW1, G>.
+// Four launches (plus the forward's Gram pass when A and G were not saved):
+//   pass 1   per (slice, split): dQ for its tokens and its share of dW1;
+//   reduce   per slice: dW1, M, the slice's dW0 and deta terms;
+//   pass 2   per (slice, split): dK, dV for its tokens;
+//   batch    per head: dW0 and deta summed over b in ascending order.
+// Every reduction has a fixed order, so results are bitwise reproducible.
+//
+// Products on the matrix cores (16x16 tiles, lane l = 16 g + m):
+//  * per-token products (dQ, dK, dV) take the 64x64 operator as the A
+//    operand with output rows permuted by perm_row, and the token rows as
+//    the B operand straight from memory; a lane then stores 8 contiguous
+//    channels of its token.
+//  * dW1 = dZ^T Q contracts over tokens: each wave writes its 32-token rows
+//    of dZ and Q to a private LDS area and reads them back transposed with
+//    ds_read_b64_tr_b16 (bf16) or single-element reads (fp32).
+// bf16 inputs use 16x16x32 bf16 products with fp32 accumulation; fp32
+// inputs use 16x16x4 fp32 products throughout.
 #include "common.hpp"
 #include "internal.hpp"
+
 namespace ttt {
-size_t lin_bwd_ws_bytes(int, int, int) { return 0; }
-hipError_t launch_lin_bwd(LinBwdLaunch, hipStream_t) { return hipErrorNotSupported; }
+namespace {
+
+constexpr int MB = 68;     // pitch (floats) of 64x64 fp32 matrices in LDS
+constexpr int kRowB = 72;  // pitch (bf16) of a staged bf16 token row (144 bytes)
+constexpr int kRowF = 68;  // pitch (floats) of a staged fp32 token row (272 bytes)
+
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+struct BwdArgs {
+    View4 X0, X1;     // pass 1: dZ, Q.   pass 2: K, V
+    View4 O0, O1;     // pass 1: dQ.      pass 2: dK, dV
+    const float* W0;
+    const float* eta;
+    const float* saved; // [slices][2][64][64]: A then G
+    float* part;        // [slices][S][64][64]: dW1 shares
+    float* dm;          // [slices][2][64][64]: dW1 then M
+    float* dW0s;        // [slices][64][64]
+    float* detas;       // [slices]
+    float* dW0;         // [H][64][64]
+    float* deta;        // [H]
+    int B, H, N, S, per, xcd;
+};
+
+// ------------------------------------------------------------ fragments --
+template <bool BF> struct Frags;
+template <> struct Frags<true> {
+    v8bf f[4][2];
+};
+template <> struct Frags<false> {
+    float f[4][16];
+};
+template <bool BF> struct Row;
+template <> struct Row<true> {
+    u32x4 x[2]; // channels 32 kb + 8 g .. +7
+};
+template <> struct Row<false> {
+    u32x4 x[4]; // channels 16 hh + 4 g .. +3
+};
+
+// A operand of Wt[o][k] = s * (tr ? M[k][o] : M[o][k]) with output rows
+// o = perm_row(rb, m); M is 64x64 fp32 in LDS (pitch MB).
+template <bool BF>
+__device__ __forceinline__ Frags<BF> make_frags(const float* M, bool tr, float s, int g, int m) {
+    Frags<BF> F;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        const int o = perm_row(rb, m);
+        auto at = [&](int k) { return s * (tr ? M[k * MB + o] : M[o * MB + k]); };
+        if constexpr (BF) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int k0 = 32 * kb + 8 * g;
+                u32x4 u{pack_bf2(at(k0), at(k0 + 1)), pack_bf2(at(k0 + 2), at(k0 + 3)),
+                        pack_bf2(at(k0 + 4), at(k0 + 5)), pack_bf2(at(k0 + 6), at(k0 + 7))};
+                F.f[rb][kb] = as_v8bf(u);
+            }
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) F.f[rb][4 * hh + i] = at(16 * hh + 4 * g + i);
+        }
+    }
+    return F;
 }
+
+template <bool BF>
+__device__ __forceinline__ Row<BF> load_row(const char* row, int g) {
+    Row<BF> r;
+    if constexpr (BF) {
+        r.x[0] = *reinterpret_cast<const u32x4*>(row + (8 * g) * 2);
+        r.x[1] = *reinterpret_cast<const u32x4*>(row + (32 + 8 * g) * 2);
+    } else {
+#pragma unroll
+        for (int hh = 0; hh < 4; ++hh) r.x[hh] = *reinterpret_cast<const u32x4*>(row + (16 * hh + 4 * g) * 4);
+    }
+    return r;
+}
+template <bool BF> __device__ __forceinline__ void zero_row(Row<BF>& r) {
+#pragma unroll
+    for (int i = 0; i < (BF ? 2 : 4); ++i) r.x[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// d[rb] += Wt x  for the lane's token row x
+template <bool BF>
+__device__ __forceinline__ void mac(const Frags<BF>& F, const Row<BF>& x, v4f* d) {
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb) {
+        if constexpr (BF) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) d[rb] = mfma32(F.f[rb][kb], as_v8bf(x.x[kb]), d[rb]);
+        } else {
+#pragma unroll
+            for (int hh = 0; hh < 4; ++hh) {
+                const f32x4 xv = __builtin_bit_cast(f32x4, x.x[hh]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) d[rb] = mfma4(F.f[rb][4 * hh + i], xv[i], d[rb]);
+            }
+        }
+    }
+}
+
+// lane (g, m) holds out[token m][perm_row(rb, 4g+i)]: channels 8g..8g+7 and
+// 32+8g..32+8g+7
+template <bool BF> __device__ __forceinline__ void store_row(char* row, const v4f* d, int g) {
+    if constexpr (BF) {
+        const u32x4 o0{pack_bf2(d[0][0], d[0][1]), pack_bf2(d[0][2], d[0][3]), pack_bf2(d[1][0], d[1][1]),
+                       pack_bf2(d[1][2], d[1][3])};
+        const u32x4 o1{pack_bf2(d[2][0], d[2][1]), pack_bf2(d[2][2], d[2][3]), pack_bf2(d[3][0], d[3][1]),
+                       pack_bf2(d[3][2], d[3][3])};
+        *reinterpret_cast<u32x4*>(row + (8 * g) * 2) = o0;
+        *reinterpret_cast<u32x4*>(row + (32 + 8 * g) * 2) = o1;
+    } else {
+        float* r = reinterpret_cast<float*>(row);
+        *reinterpret_cast<f32x4*>(r + 8 * g) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
+        *reinterpret_cast<f32x4*>(r + 8 * g + 4) = f32x4{d[1][0], d[1][1], d[1][2], d[1][3]};
+        *reinterpret_cast<f32x4*>(r + 32 + 8 * g) = f32x4{d[2][0], d[2][1], d[2][2], d[2][3]};
+        *reinterpret_cast<f32x4*>(r + 36 + 8 * g) = f32x4{d[3][0], d[3][1], d[3][2], d[3][3]};
+    }
+}
+
+struct Ctx {
+    int slice, split, b, h, t0, t1;
+};
+__device__ __forceinline__ Ctx ctx_of(const BwdArgs& a) {
+    Ctx c;
+    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
+    c.slice = ss.slice;
+    c.split = ss.split;
+    c.b = c.slice / a.H;
+    c.h = c.slice % a.H;
+    c.t0 = min(a.N, c.split * a.per);
+    c.t1 = min(a.N, c.t0 + a.per);
+    return c;
+}
+template <int ESZ> __device__ __forceinline__ const char* base_of(const View4& v, const Ctx& c) {
+    return (const char*)v.ptr + (c.b * v.sb + c.h * v.sh) * (long long)ESZ;
+}
+
+// ---------------------------------------------------------------- pass 1 --
+// dQ = dZ W1 for the workgroup's tokens and its share of dW1 = dZ^T Q.
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) void bwd_pass1(BwdArgs a) {
+    constexpr int ESZ = BF ? 2 : 4;
+    constexpr int WAVE_BYTES = BF ? 2 * 32 * kRowB * 2 : 2 * 32 * kRowF * 4; // dZ + Q rows
+    constexpr int LDS_BYTES = 4 * 64 * 64 * 4 > 4 * WAVE_BYTES ? 4 * 64 * 64 * 4 : 4 * WAVE_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    float* ldsf = reinterpret_cast<float*>(lds);
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Ctx c = ctx_of(a);
+    if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+
+    // W1 = W0 - eta G in LDS, then the A operand of dQ^T = W1^T dZ^T
+    {
+        const float eta = a.eta[c.h];
+        const float* W0 = a.W0 + (long long)c.h * 4096;
+        const float* G = a.saved + (long long)c.slice * 8192 + 4096;
+        for (int e = tid; e < 4096; e += kThreads) ldsf[(e >> 6) * MB + (e & 63)] = W0[e] - eta * G[e];
+    }
+    __syncthreads();
+    const Frags<BF> F = make_frags<BF>(ldsf, true, 1.0f, g, m);
+    __syncthreads();
+
+    const char* dZp = base_of<ESZ>(a.X0, c);
+    const char* Qp = base_of<ESZ>(a.X1, c);
+    char* dQp = (char*)base_of<ESZ>(a.O0, c);
+    const long long sz = a.X0.sn * ESZ, sq = a.X1.sn * ESZ, so = a.O0.sn * ESZ;
+    char* wz = lds + w * WAVE_BYTES;       // this wave's 32 dZ rows
+    char* wq = wz + WAVE_BYTES / 2;        // and 32 Q rows
+
+    v4f acc[16]; // dW1 tile (rb, cb) = acc[4 rb + cb]: [16rb + 4g + i][16cb + m]
+#pragma unroll
+    for (int t = 0; t < 16; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    // wave steps of 32 tokens: wave w takes tokens t0 + 128 s + 32 w + [0, 32)
+    const int nst = (c.t1 - c.t0 + 127) / 128;
+    for (int s = 0; s < nst; ++s) {
+        const int tb = c.t0 + 128 * s + 32 * w;
+        Row<BF> z[2], q[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int t = tb + 16 * h + m;
+            const int tc = min(t, c.t1 - 1);
+            z[h] = load_row<BF>(dZp + tc * sz, g);
+            q[h] = load_row<BF>(Qp + tc * sq, g);
+            if (t >= c.t1) {
+                zero_row<BF>(z[h]);
+                zero_row<BF>(q[h]);
+            }
+        }
+        // dQ for both halves
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            v4f d[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+            mac<BF>(F, z[h], d);
+            const int t = tb + 16 * h + m;
+            if (t < c.t1) store_row<BF>(dQp + t * so, d, g);
+        }
+        // dW1 += dZ^T Q over these 32 tokens
+        if constexpr (BF) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    const int off = ((16 * h + m) * kRowB + 32 * kb + 8 * g) * 2;
+                    *reinterpret_cast<u32x4*>(wz + off) = z[h].x[kb];
+                    *reinterpret_cast<u32x4*>(wq + off) = q[h].x[kb];
+                }
+            // transposed operand reads: lane (g, 4e + a) points at token
+            // 8g + e (+4), channels 16 blk + 4a .. +3
+            const int e = (lane & 15) >> 2, aa = lane & 3;
+            v8bf A[4], Bq[4];
+#pragma unroll
+            for (int blk = 0; blk < 4; ++blk) {
+                const int o0 = ((8 * g + e) * kRowB + 16 * blk + 4 * aa) * 2;
+                const int o1 = o0 + 4 * kRowB * 2;
+                const v4s_t a0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wz + o0));
+                const v4s_t a1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wz + o1));
+                const v4s_t b0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wq + o0));
+                const v4s_t b1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(wq + o1));
+                A[blk] = __builtin_bit_cast(v8bf, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+                Bq[blk] = __builtin_bit_cast(v8bf, __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7));
+            }
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) acc[4 * rb + cb] = mfma32(A[rb], Bq[cb], acc[4 * rb + cb]);
+        } else {
+            float* fz = reinterpret_cast<float*>(wz);
+            float* fq = reinterpret_cast<float*>(wq);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    const int off = (16 * h + m) * kRowF + 16 * hh + 4 * g;
+                    *reinterpret_cast<u32x4*>(fz + off) = z[h].x[hh];
+                    *reinterpret_cast<u32x4*>(fq + off) = q[h].x[hh];
+                }
+#pragma unroll 2
+            for (int kk = 0; kk < 8; ++kk) {
+                const int t = 4 * kk + g;
+                float av[4], bv[4];
+#pragma unroll
+                for (int blk = 0; blk < 4; ++blk) {
+                    av[blk] = fz[t * kRowF + 16 * blk + m];
+                    bv[blk] = fq[t * kRowF + 16 * blk + m];
+                }
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) acc[4 * rb + cb] = mfma4(av[rb], bv[cb], acc[4 * rb + cb]);
+            }
+        }
+    }
+
+    // sum the four waves' shares (fixed order) and publish this split's dW1
+    __syncthreads();
+    float* red = ldsf + w * 4096;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[(16 * rb + 4 * g + i) * 64 + 16 * cb + m] = acc[4 * rb + cb][i];
+    __syncthreads();
+    float* dst = a.part + ((long long)c.slice * a.S + c.split) * 4096;
+#pragma unroll 4
+    for (int e = tid; e < 4096; e += kThreads)
+        dst[e] = ((ldsf[e] + ldsf[4096 + e]) + ldsf[8192 + e]) + ldsf[12288 + e];
+}
+
+// ---------------------------------------------------------------- reduce --
+// Per slice: dW1 (splits summed in order), M = P + P^T with P = W0^T dW1,
+// the slice's dW0 term dW1 - beta dW1 A and deta term -<dW1, G>.
+__global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) float D[64 * MB];
+    __shared__ __attribute__((aligned(16))) float W[64 * MB];
+    __shared__ __attribute__((aligned(16))) float Am[64 * MB];
+    __shared__ float red[kThreads];
+    const int tid = threadIdx.x;
+    const int slice = blockIdx.x;
+    const int h = slice % a.H;
+    const float beta = 2.0f * a.eta[h] / (float)a.N;
+    const float* W0 = a.W0 + (long long)h * 4096;
+    const float* A = a.saved + (long long)slice * 8192;
+    const float* G = A + 4096;
+    const float* part = a.part + (long long)slice * a.S * 4096;
+    float dsum = 0.f;
+    for (int e = tid; e < 4096; e += kThreads) {
+        float v = part[e];
+        for (int s = 1; s < a.S; ++s) v += part[(long long)s * 4096 + e];
+        const int r = e >> 6, cc = e & 63;
+        D[r * MB + cc] = v;
+        W[r * MB + cc] = W0[e];
+        Am[r * MB + cc] = A[e];
+        dsum += v * G[e];
+    }
+    red[tid] = dsum;
+    __syncthreads();
+    const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
+    float P[4][4], Q2[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) P[i][j] = Q2[i][j] = 0.f;
+#pragma unroll 4
+    for (int k = 0; k < 64; ++k) {
+        const f32x4 wv = *reinterpret_cast<const f32x4*>(W + k * MB + r0);  // W0[k][r0..]
+        const f32x4 dv = *reinterpret_cast<const f32x4*>(D + k * MB + c0);  // dW1[k][c0..]
+        const f32x4 av = *reinterpret_cast<const f32x4*>(Am + k * MB + c0); // A[k][c0..]
+        float d2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) d2[i] = D[(r0 + i) * MB + k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                P[i][j] += wv[i] * dv[j];  // (W0^T dW1)[r0+i][c0+j]
+                Q2[i][j] += d2[i] * av[j]; // (dW1 A)[r0+i][c0+j]
+            }
+    }
+    float* dm = a.dm + (long long)slice * 8192;
+    float* dW0s = a.dW0s + (long long)slice * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        f32x4 dw, d1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            d1[j] = D[r * MB + c0 + j];
+            dw[j] = d1[j] - beta * Q2[i][j];
+        }
+        *reinterpret_cast<f32x4*>(dW0s + r * 64 + c0) = dw;
+        *reinterpret_cast<f32x4*>(dm + r * 64 + c0) = d1;
+    }
+    __syncthreads(); // every thread has read D and W
+    // M = P + P^T through LDS (W's space is free now)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) W[(r0 + i) * MB + c0 + j] = P[i][j];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = r0 + i;
+        f32x4 mv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mv[j] = W[r * MB + c0 + j] + W[(c0 + j) * MB + r];
+        *reinterpret_cast<f32x4*>(dm + 4096 + r * 64 + c0) = mv;
+    }
+    // deta term: fixed-order tree over the threads' partial sums
+    for (int s = kThreads / 2; s > 0; s >>= 1) {
+        if (tid < s) red[tid] += red[tid + s];
+        __syncthreads();
+    }
+    if (tid == 0) a.detas[slice] = -red[0];
+}
+
+// ---------------------------------------------------------------- pass 2 --
+// dK = beta (V dW1 - K M), dV = beta K dW1^T for the workgroup's tokens.
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) void bwd_pass2(BwdArgs a) {
+    constexpr int ESZ = BF ? 2 : 4;
+    __shared__ __attribute__((aligned(16))) float mats[2 * 64 * MB];
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const Ctx c = ctx_of(a);
+    if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+
+    const float beta = 2.0f * a.eta[c.h] / (float)a.N;
+    {
+        const float* src = a.dm + (long long)c.slice * 8192;
+        for (int e = tid; e < 8192; e += kThreads) mats[(e >> 6) * MB + (e & 63)] = src[e];
+    }
+    __syncthreads();
+    const float* dW1 = mats;
+    const float* Mm = mats + 64 * MB;
+    const Frags<BF> F1 = make_frags<BF>(dW1, true, beta, g, m);  // beta dW1^T
+    const Frags<BF> F2 = make_frags<BF>(Mm, false, -beta, g, m); // -beta M
+    const Frags<BF> F3 = make_frags<BF>(dW1, false, beta, g, m); // beta dW1
+
+    const char* Kp = base_of<ESZ>(a.X0, c);
+    const char* Vp = base_of<ESZ>(a.X1, c);
+    char* dKp = (char*)base_of<ESZ>(a.O0, c);
+    char* dVp = (char*)base_of<ESZ>(a.O1, c);
+    const long long sk = a.X0.sn * ESZ, sv = a.X1.sn * ESZ, sdk = a.O0.sn * ESZ, sdv = a.O1.sn * ESZ;
+
+    // 16-token steps, wave w takes steps w, w + 4, ...
+    const int nst = (c.t1 - c.t0 + 15) / 16;
+    for (int s = w; s < nst; s += 4) {
+        const int t = c.t0 + 16 * s + m;
+        const int tc = min(t, c.t1 - 1);
+        const Row<BF> k = load_row<BF>(Kp + tc * sk, g);
+        const Row<BF> v = load_row<BF>(Vp + tc * sv, g);
+        v4f dk[4], dv[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) dk[rb] = dv[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+        mac<BF>(F1, v, dk);
+        mac<BF>(F2, k, dk);
+        mac<BF>(F3, k, dv);
+        if (t < c.t1) {
+            store_row<BF>(dKp + t * sdk, dk, g);
+            store_row<BF>(dVp + t * sdv, dv, g);
+        }
+    }
+}
+
+// ------------------------------------------------------------ batch sums --
+__global__ __launch_bounds__(kThreads, 1) void bwd_batch(BwdArgs a) {
+    const int h = blockIdx.x, tid = threadIdx.x;
+    for (int e = tid; e < 4096; e += kThreads) {
+        float v = 0.f;
+        for (int b = 0; b < a.B; ++b) v += a.dW0s[((long long)b * a.H + h) * 4096 + e];
+        a.dW0[(long long)h * 4096 + e] = v;
+    }
+    if (tid == 0) {
+        float v = 0.f;
+        for (int b = 0; b < a.B; ++b) v += a.detas[(long long)b * a.H + h];
+        a.deta[h] = v;
+    }
+}
+
+// workgroups per slice: enough workgroups for the device, at least 128
+// tokens each
+int bwd_splits(int B, int H, int N) {
+    const long long slices = (long long)B * H;
+    long long s = (1024 + slices - 1) / slices;
+    const long long maxs = (N + 127) / 128;
+    if (s > maxs) s = maxs;
+    if (s > 64) s = 64;
+    return (int)(s < 1 ? 1 : s);
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+} // namespace
+
+// Workspace: [forward's workspace | A, G per slice (when not saved)] then
+// [dW1 shares | dW1, M | dW0 terms | deta terms].
+size_t lin_bwd_ws_bytes(int B, int H, int N) {
+    const size_t slices = (size_t)B * H;
+    const size_t S = bwd_splits(B, H, N);
+    size_t bytes = align256(lin_fwd_ws_bytes(B, H, N));
+    bytes += align256(slices * 8192 * 4);     // recomputed A, G
+    bytes += align256(slices * S * 4096 * 4); // dW1 shares
+    bytes += align256(slices * 8192 * 4);     // dW1, M
+    bytes += align256(slices * 4096 * 4);     // dW0 terms
+    bytes += align256(slices * 4);            // deta terms
+    return bytes;
+}
+
+float* lin_bwd_saved_region(void* ws, int B, int H, int N) {
+    return (float*)((char*)ws + align256(lin_fwd_ws_bytes(B, H, N)));
+}
+
+hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
+    BwdArgs a{};
+    a.W0 = s.W0;
+    a.eta = s.eta;
+    a.saved = s.saved;
+    a.dW0 = s.dW0;
+    a.deta = s.deta;
+    a.B = s.B; a.H = s.H; a.N = s.N;
+    a.S = bwd_splits(s.B, s.H, s.N);
+    a.per = (((s.N + a.S - 1) / a.S) + 15) & ~15;
+    a.xcd = 1;
+    const size_t slices = (size_t)s.B * s.H;
+    char* p = (char*)lin_bwd_saved_region(s.ws, s.B, s.H, s.N) + align256(slices * 8192 * 4);
+    a.part = (float*)p;
+    p += align256(slices * a.S * 4096 * 4);
+    a.dm = (float*)p;
+    p += align256(slices * 8192 * 4);
+    a.dW0s = (float*)p;
+    p += align256(slices * 4096 * 4);
+    a.detas = (float*)p;
+
+    const long long padded = ((long long)slices + 7) / 8 * 8;
+    const dim3 grid((unsigned)(padded * a.S)), block(kThreads);
+    a.X0 = s.dZ; a.X1 = s.Q; a.O0 = s.dQ;
+    if (s.bf16) hipLaunchKernelGGL(bwd_pass1<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
+    a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
+    if (s.bf16) hipLaunchKernelGGL(bwd_pass2<true>, grid, block, 0, stream, a);
+    else hipLaunchKernelGGL(bwd_pass2<false>, grid, block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H), block, 0, stream, a);
+    return hipGetLastError();
+}
+
+} // namespace ttt

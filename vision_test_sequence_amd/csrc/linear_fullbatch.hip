@@ -70,11 +70,6 @@ template <bool BF> __device__ __forceinline__ int swz_q(int row);
 template <> __device__ __forceinline__ int swz_q<true>(int row) { return row & 7; }
 template <> __device__ __forceinline__ int swz_q<false>(int row) { return row & 15; }
 
-__device__ __forceinline__ int perm_row(int rb, int m) {
-    // MFMA row m of output block rb -> output channel; lane (g, .) then owns
-    // channels [8g, 8g+8) (blocks 0,1) and [32+8g, 32+8g+8) (blocks 2,3).
-    return 32 * (rb >> 1) + 8 * (m >> 2) + 4 * (rb & 1) + (m & 3);
-}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -546,7 +541,8 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
             const long long tok = c.t0 + min(row, T - 1);
             __builtin_amdgcn_global_load_lds((const void*)(c.Kp + tok * c.Ksn + okv), (lds_void*)(Ks + q * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(c.Vp + tok * c.Vsn + okv), (lds_void*)(Vs + q * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(c.Qp + tok * c.Qsn + oq), (lds_void*)(Qs + q * 1024), 16, 0, 0);
+            if (a.Z.ptr)
+                __builtin_amdgcn_global_load_lds((const void*)(c.Qp + tok * c.Qsn + oq), (lds_void*)(Qs + q * 1024), 16, 0, 0);
         }
     }
     f32x4 w0r[4];
@@ -583,7 +579,12 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     // ---- phase 2
     float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r);
 
-    // ---- phase 3: Z from the resident Q region
+    // ---- phase 3: Z from the resident Q region (skipped when only A and G
+    // are wanted)
+    if (!a.Z.ptr) {
+        release_end(a, c.slice, release_begin(a, c.slice));
+        return;
+    }
     const int nsteps = (T + 15) / 16;
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
@@ -684,7 +685,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     const int nsteps = (t1 - t0 + 15) / 16;
     constexpr int QV = BF ? 2 : 4; // 16-byte loads per lane per step
     u32x4 qpre[Cfg::qpre][QV];
-    if (ntiles > 0) {
+    if (ntiles > 0 && a.Z.ptr) {
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int tok = min(t0 + (w + 4 * k) * 16 + m, t1 - 1);
@@ -734,6 +735,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     reduce_waves(accC, accA, lds, mA, mC, w, lane, g, m, true);
 
     float* W1 = lin_update(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r);
+    if (!a.Z.ptr) { // only A and G wanted
+        release_end(a, c.slice, release_begin(a, c.slice));
+        return;
+    }
 
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
