@@ -9,16 +9,21 @@ inner model (ttt_dwconv3x3_fullbatch), each followed by its apply.
 
 Inputs are resident in HBM before timing and rotate over 5 independent sets
 (> 256 MB together, so the 256 MB Infinity Cache cannot hold them between
-uses).  Prints one JSON line: whole-layer tokens/s plus the roofline of the
-dominant kernel (the linear step) and the fp64 oracle timed on the host.
+uses).  Prints one JSON line: whole-layer tokens/s, the roofline of the
+dominant kernel (the linear step), the other rows of the path on their own
+workloads (the mini-batch bidirectional scan at 1280x1280, the forward and
+backward of the linear step at ViT-B 1024x1024), and the fp64 oracle timed
+on the host.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -26,8 +31,18 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix cores
 
 WORKLOAD = "vit3t_1248_bf16"
+SCAN_WORKLOAD = "vittt_s_1280_bf16"
+BWD_WORKLOAD = "vitb_1024_fwdbwd_bf16"
 METRIC = "TTT-layer tokens/s at N=6084, H=3, d=64 bf16; % MFMA / HBM roofline"
 NSETS = 5
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per launch of the linear kernel from rocprofv3 FETCH_SIZE /
+# WRITE_SIZE runs, stored with the hash of the sources they were taken on
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lin_fwd_resident_vit3t_1248_traffic.md")
+LIN_SOURCES = ["vision_test_sequence_amd/csrc/linear_fullbatch.hip",
+               "vision_test_sequence_amd/csrc/common.hpp",
+               "vision_test_sequence_amd/csrc/api.cpp"]
+COPY_BYTES = 256 << 20           # plain copy kernel run once for the counter scale
 
 
 def parse():
@@ -36,11 +51,34 @@ def parse():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="skip the scan and backward rows")
     return ap.parse_args()
 
 
-def algorithmic(w):
-    """Bytes and flops one step must move / perform (per launch kind)."""
+def lin_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in LIN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed counter summary, or None if
+    the kernel sources changed since the counters were taken."""
+    try:
+        txt = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    m = re.search(r"source-hash:\s*([0-9a-f]+)", txt)
+    t = re.search(r"traffic-bytes-per-launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != lin_source_hash():
+        return None
+    return float(t.group(1))
+
+
+def layer_algorithmic(w):
+    """Bytes and flops one layer step must move / perform (per kernel)."""
     N, d, B = w.N, w.d, w.B
     lin_heads = len(w.head_indices("linear"))
     conv_heads = len(w.head_indices("dwconv3x3"))
@@ -50,6 +88,73 @@ def algorithmic(w):
     lin_flops = B * lin_heads * (6 * N * d * d + 2 * d ** 3)  # Gram 4Nd^2, apply 2Nd^2, W0 A
     conv_flops = B * conv_heads * 55 * N * d
     return lin_bytes, conv_bytes, lin_flops, conv_flops
+
+
+def time_calls(torch, fn, n):
+    """Average wall time of n back-to-back calls on the current stream
+    (HIP events around the whole run), in ms."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(n):
+        fn(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def rows(torch, vt, wl, dev):
+    """The scan and the backward on their own workloads."""
+    out = {}
+    w = wl.WORKLOADS[SCAN_WORKLOAD]
+    inp = wl.make(SCAN_WORKLOAD)
+    K, Q, V, W0, eta = (inp[k].to(dev) for k in ("K", "Q", "V", "W0", "eta"))
+    Z = torch.empty_like(Q)
+    f = lambda i: vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, w.minibatch, 0, Z=Z)
+    for i in range(3):
+        f(i)
+    ms = time_calls(torch, f, 20)
+    nbytes = 4 * w.B * w.H * w.N * w.d * 2
+    flops = w.B * w.H * w.N * 2 * (6 * w.d ** 2 + 4 * w.minibatch * w.d)
+    out["scan_bidir"] = {
+        "workload": f"{SCAN_WORKLOAD}: B={w.B}, H={w.H}, {w.grid_h}x{w.grid_w} N={w.N}, "
+                    f"b={w.minibatch}, both directions averaged",
+        "us_per_call": ms * 1e3, "tokens_per_s": w.B * w.N / (ms * 1e-3),
+        "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tflops": flops / (ms * 1e-3) / 1e12,
+    }
+    del K, Q, V, Z
+    w = wl.WORKLOADS[BWD_WORKLOAD]
+    inp = wl.make(BWD_WORKLOAD)
+    K, Q, V, dZ = (inp[k].to(dev) for k in ("K", "Q", "V", "dZ"))
+    W0, eta = inp["W0"].to(dev), inp["eta"].to(dev)
+    B, H, N, d = K.shape
+    saved = torch.empty((B, H, 2, d, d), dtype=torch.float32, device=dev)
+    Z = torch.empty_like(Q)
+    outs = [torch.empty_like(K) for _ in range(3)]
+    dW0 = torch.empty((H, d, d), dtype=torch.float32, device=dev)
+    deta = torch.empty((H,), dtype=torch.float32, device=dev)
+    fw = lambda i: vt.ttt_linear_fullbatch(K, Q, V, W0, eta, Z=Z, saved=saved)
+    bw = lambda i: vt.ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, saved=saved, dK=outs[0],
+                                               dQ=outs[1], dV=outs[2], dW0=dW0, deta=deta)
+    for i in range(3):
+        fw(i)
+        bw(i)
+    ms_f = time_calls(torch, fw, 20)
+    ms_b = time_calls(torch, bw, 20)
+    fb = 4 * B * H * N * d * 2
+    bb = 7 * B * H * N * d * 2
+    out["fwd_bwd"] = {
+        "workload": f"{BWD_WORKLOAD}: B={B}, H={H}, {w.grid_h}x{w.grid_w} N={N}, forward saves "
+                    "A and G, backward returns dK, dQ, dV, dW0, deta",
+        "fwd_us": ms_f * 1e3, "bwd_us": ms_b * 1e3,
+        "fwd_gbs": fb / (ms_f * 1e-3) / 1e9, "bwd_gbs": bb / (ms_b * 1e-3) / 1e9,
+        "hbm_frac": (fb + bb) / ((ms_f + ms_b) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "tokens_per_s": B * N / ((ms_f + ms_b) * 1e-3),
+    }
+    return out
 
 
 def main():
@@ -80,58 +185,50 @@ def main():
         inp = wl.make(WORKLOAD, seed_offset=1000 * s)
         g = {k: v.to(dev) for k, v in inp.items()}
         g["Z"] = torch.empty_like(g["Q"])
-        sets.append((inp, g))
-    torch.cuda.synchronize()
-
-    def step(g, ev=None):
-        if ev is not None:
-            ev[0].record()
-        vt.ttt_linear_fullbatch(g["K"][:, l0:l1], g["Q"][:, l0:l1], g["V"][:, l0:l1],
-                                g["W0l"], g["etal"], Z=g["Z"][:, l0:l1])
-        if ev is not None:
-            ev[1].record()
-        vt.ttt_dwconv3x3_fullbatch(g["K"][:, c0:c1], g["Q"][:, c0:c1], g["V"][:, c0:c1],
-                                   g["w0c"], g["etac"], w.grid_h, w.grid_w, Z=g["Z"][:, c0:c1])
-        if ev is not None:
-            ev[2].record()
-
-    for _, g in sets:
         g["W0l"] = g["W0"][l0:l1].contiguous()
         g["etal"] = g["eta"][l0:l1].contiguous()
         g["w0c"] = g["w0"][c0:c1].contiguous()
         g["etac"] = g["eta"][c0:c1].contiguous()
+        sets.append((inp, g))
+    torch.cuda.synchronize()
+
+    def linear(g):
+        vt.ttt_linear_fullbatch(g["K"][:, l0:l1], g["Q"][:, l0:l1], g["V"][:, l0:l1],
+                                g["W0l"], g["etal"], Z=g["Z"][:, l0:l1])
+
+    def conv(g):
+        vt.ttt_dwconv3x3_fullbatch(g["K"][:, c0:c1], g["Q"][:, c0:c1], g["V"][:, c0:c1],
+                                   g["w0c"], g["etac"], w.grid_h, w.grid_w, Z=g["Z"][:, c0:c1])
+
+    def step(g):
+        linear(g)
+        conv(g)
 
     for i in range(args.warmup):
         step(sets[i % NSETS][1])
     torch.cuda.synchronize()
 
-    # timed region: K steps rotating over the input sets; per-launch events
-    # on the launch stream (torch's current stream) give each kernel's time
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(sets[i % NSETS][1], evs[i])
-    t_end.record()
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    lin_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    conv_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-
+    # timed region: K layer steps rotating over the input sets, bracketed by
+    # a synchronisation and HIP events on the launch stream
+    ms_step = time_calls(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
+    # each kernel on its own: back-to-back launches on the same stream,
+    # rotating over the same sets (average launch duration)
+    nk = max(args.steps, 200)
+    lin_ms = time_calls(torch, lambda i: linear(sets[i % NSETS][1]), nk)
+    conv_ms = time_calls(torch, lambda i: conv(sets[i % NSETS][1]), nk)
     # warm reference: the same buffers every step (Infinity-Cache resident)
+    warm_ms_step = time_calls(torch, lambda i: step(sets[0][1]), args.steps)
+
+    # one plain device copy of known size: the scale for the HBM byte
+    # counters of the profiled runs
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
     torch.cuda.synchronize()
-    t_start.record()
-    for i in range(args.steps):
-        step(sets[0][1])
-    t_end.record()
-    torch.cuda.synchronize()
-    warm_ms_step = t_start.elapsed_time(t_end) / args.steps
+    del src, dst
 
     tokens = w.B * w.N
-    lin_bytes, conv_bytes, lin_flops, conv_flops = algorithmic(w)
+    lin_bytes, conv_bytes, lin_flops, conv_flops = layer_algorithmic(w)
     achieved = lin_bytes / (lin_ms * 1e-3) / 1e9
     out = {
         "metric": METRIC,
@@ -154,13 +251,13 @@ def main():
             "input_sets_rotated": NSETS,
         },
         "roofline": {
-            "kernel": "lin_fwd_kernel (ttt_linear_fullbatch, heads 0-1)",
+            "kernel": "lin_fwd_resident (ttt_linear_fullbatch, heads 0-1, B=8, N=6084)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes": lin_bytes,
             "avg_launch_us": lin_ms * 1e3,
         },
@@ -175,6 +272,8 @@ def main():
             "warm_ms_per_step": warm_ms_step,
         },
     }
+    if not args.no_rows:
+        out["rows"] = rows(torch, vt, wl, dev)
 
     # CPU baseline: the fp64 oracle, as it stands, on input set 0 of the
     # same workload, repeated until a few seconds have accumulated; its
