@@ -58,11 +58,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <bool BF> struct ConvT;
 template <> struct ConvT<true> {
     static constexpr int esz = 2;
+    typedef uint16_t raw_t;
+    __device__ static raw_t raw(const char* p) { return *(const uint16_t*)p; }
+    __device__ static float cvt(raw_t v) { return __uint_as_float((uint32_t)v << 16); }
     __device__ static float ld(const char* p) { return __uint_as_float((uint32_t)*(const uint16_t*)p << 16); }
     __device__ static void st(char* p, float v) { *(uint16_t*)p = f2bf(v); }
 };
 template <> struct ConvT<false> {
     static constexpr int esz = 4;
+    typedef float raw_t;
+    __device__ static raw_t raw(const char* p) { return *(const float*)p; }
+    __device__ static float cvt(raw_t v) { return v; }
     __device__ static float ld(const char* p) { return *(const float*)p; }
     __device__ static void st(char* p, float v) { *(float*)p = v; }
 };
@@ -89,15 +95,44 @@ __device__ __forceinline__ void stage(char* dst, const char* src, long long sn, 
     }
 }
 
+// Zero the pixels of a staged (rows x cols) halo block that lie outside the
+// grid, so the stencil loops read zero padding without masks.  Called after
+// the loads have landed.  A wave takes a row: the whole row when it lies
+// outside the grid, else only its columns left of 0 and from gw on.
 template <bool BF>
-__global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
+__device__ __forceinline__ void zero_outside(char* blk, int ya, int xa, int rows, int cols, int gh, int gw) {
+    constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
+    const int nl = xa < 0 ? -xa : 0;                        // pixels left of the grid
+    const int nr = xa + cols > gw ? xa + cols - max(gw, xa) : 0; // pixels right of it
+    const bool rows_out = ya < 0 || ya + rows > gh;
+    if (!(nl || nr || rows_out)) return;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const u32x4 z{0u, 0u, 0u, 0u};
+    for (int r = w; r < rows; r += kThreads / 64) {
+        char* row = blk + (long long)r * cols * cpp * 16;
+        const int y = ya + r;
+        if (y < 0 || y >= gh) {
+            for (int q = lane; q < cols * cpp; q += 64) *reinterpret_cast<u32x4*>(row + q * 16) = z;
+        } else {
+            for (int q = lane; q < nl * cpp; q += 64) *reinterpret_cast<u32x4*>(row + q * 16) = z;
+            char* right = row + (cols - nr) * cpp * 16;
+            for (int q = lane; q < nr * cpp; q += 64) *reinterpret_cast<u32x4*>(right + q * 16) = z;
+        }
+    }
+}
+
+// One workgroup per CU (its LDS), so one wave per SIMD: registers are
+// plentiful and the schedule should favour latency over occupancy.
+template <bool BF>
+__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_kernel(ConvArgs a) {
     using T = ConvT<BF>;
     constexpr int pb = 64 * T::esz; // bytes per pixel
     __shared__ __attribute__((aligned(16))) char lds[kTileBytes + 3 * 1024];
     __shared__ float red[kRedFloats];
     __shared__ float w1s[64 * 9];
 
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
     const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
     const int slice = ss.slice, split = ss.split;
     if (slice >= a.slices) return; // padding block of the XCD-aware grid
@@ -114,11 +149,14 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
     const long long Ksn = a.K.sn * T::esz, Vsn = a.V.sn * T::esz;
     const long long Qsn = a.Q.sn * T::esz, Zsn = a.Z.sn * T::esz;
 
-    const int HW = a.TW + 2;
+    // LDS rows are at least kSeg pixels wide (plus the halo), so a row
+    // segment of kSeg pixels never reads past its row; columns beyond the
+    // grid are zero (K, Q) or masked (V)
+    const int TWp = max(a.TW, kSeg), HW = TWp + 2;
     const int khalo = (a.R + 2) * HW;
     char* Ks = lds;
     char* Vs = lds + khalo * pb + 1024;
-    char* Qs = Vs + a.R * a.TW * pb + 1024;
+    char* Qs = Vs + a.R * TWp * pb + 1024;
     const bool q_early = (te - tb) == 1;
 
     const float* w0c = a.w0 + ((long long)h * 64 + lane) * 9;
@@ -136,46 +174,52 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
         // always the nominal tile shape, so the LDS pitches are fixed; the
         // part of an edge tile outside the grid is masked when read
         stage<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-        stage<BF>(Vs, Vp, Vsn, y0, x0, a.R, a.TW, gh, gw);
+        stage<BF>(Vs, Vp, Vsn, y0, x0, a.R, TWp, gh, gw);
         if (q_early) stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
         __syncthreads(); // waits for the direct-to-LDS loads
+        zero_outside<BF>(Ks, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
+        if (q_early) zero_outside<BF>(Qs, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
+        __syncthreads();
         const int nsx = (tw + kSeg - 1) / kSeg;
         for (int sgi = w; sgi < rr * nsx; sgi += 4) {
-            const int r = sgi / nsx, xs = (sgi % nsx) * kSeg, xe = min(tw, xs + kSeg);
-            const int y = y0 + r;
-            bool rowok[3];
+            // Segment k of a row covers pixels [16k, 16k+16); the last one is
+            // shifted left to end at the row's end (its first pixels, done by
+            // the previous segment, are masked) -- or, in a row narrower than
+            // a segment, starts at 0 and masks the pixels past the row.  Every
+            // LDS value a segment needs is read up front at fixed offsets
+            // from one base, then the 3x3 window slides in registers.
+            const int r = sgi / nsx, k = sgi % nsx;
+            const int xs = min(k * kSeg, max(tw - kSeg, 0));
+            const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
+            const char* kb = Ks + ((r * HW + xs) * 64 + lane) * T::esz;
+            const char* vb = Vs + ((r * TWp + xs) * 64 + lane) * T::esz;
+            typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) rowok[i] = (y + i - 1 >= 0) && (y + i - 1 < gh);
-            auto kval = [&](int i, int hx) -> float { // halo row r+i, halo column hx
-                const int x = x0 - 1 + hx;
-                const bool ok = rowok[i] && x >= 0 && x < gw;
-                const float v = T::ld(Ks + (((r + i) * HW + hx) * 64 + lane) * T::esz);
-                return ok ? v : 0.f;
-            };
-            float kw[3][3];
+            for (int i = 0; i < 3; ++i)
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                kw[i][0] = kval(i, xs);
-                kw[i][1] = kval(i, xs + 1);
-            }
-            for (int xl = xs; xl < xe; ++xl) {
+                for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * HW + j) * 64) * T::esz);
 #pragma unroll
-                for (int i = 0; i < 3; ++i) kw[i][2] = kval(i, xl + 2);
+            for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
+            __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
+            float kr[3][kSeg + 2], vv[kSeg];
+#pragma unroll
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
+#pragma unroll
+            for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
+#pragma unroll
+            for (int x = 0; x < kSeg; ++x) {
                 float p = 0.f;
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int j = 0; j < 3; ++j) p += wt[i * 3 + j] * kw[i][j];
-                const float rv = p - T::ld(Vs + ((r * a.TW + xl) * 64 + lane) * T::esz);
+                    for (int jj = 0; jj < 3; ++jj) p += wt[i * 3 + jj] * kr[i][x + jj];
+                const float rv = (x >= lo && x < hi) ? p - vv[x] : 0.f;
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int j = 0; j < 3; ++j) gacc[i * 3 + j] += rv * kw[i][j];
-#pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                    kw[i][0] = kw[i][1];
-                    kw[i][1] = kw[i][2];
-                }
+                    for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] += rv * kr[i][x + jj];
             }
         }
         __syncthreads();
@@ -271,40 +315,36 @@ __global__ __launch_bounds__(kThreads, 1) void conv_kernel(ConvArgs a) {
         if (!q_early) {
             stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
             __syncthreads();
+            zero_outside<BF>(Qs, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
+            __syncthreads();
         }
         const int nsx = (tw + kSeg - 1) / kSeg;
         for (int sgi = w; sgi < rr * nsx; sgi += 4) {
-            const int r = sgi / nsx, xs = (sgi % nsx) * kSeg, xe = min(tw, xs + kSeg);
+            const int r = sgi / nsx, k = sgi % nsx; // segments as in phase 1
+            const int xs = min(k * kSeg, max(tw - kSeg, 0));
+            const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
             const int y = y0 + r;
-            bool rowok[3];
+            const char* qb = Qs + ((r * HW + xs) * 64 + lane) * T::esz;
+            char* zrow = Zp + ((long long)y * gw + x0 + xs) * Zsn + lane * T::esz;
+            typename T::raw_t qraw[3][kSeg + 2];
 #pragma unroll
-            for (int i = 0; i < 3; ++i) rowok[i] = (y + i - 1 >= 0) && (y + i - 1 < gh);
-            auto qval = [&](int i, int hx) -> float {
-                const int x = x0 - 1 + hx;
-                const bool ok = rowok[i] && x >= 0 && x < gw;
-                const float v = T::ld(Qs + (((r + i) * HW + hx) * 64 + lane) * T::esz);
-                return ok ? v : 0.f;
-            };
-            float qw[3][3];
+            for (int i = 0; i < 3; ++i)
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                qw[i][0] = qval(i, xs);
-                qw[i][1] = qval(i, xs + 1);
-            }
-            for (int xl = xs; xl < xe; ++xl) {
+                for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * HW + j) * 64) * T::esz);
+            __builtin_amdgcn_sched_barrier(0);
+            float qr[3][kSeg + 2];
 #pragma unroll
-                for (int i = 0; i < 3; ++i) qw[i][2] = qval(i, xl + 2);
+            for (int i = 0; i < 3; ++i)
+#pragma unroll
+                for (int j = 0; j < kSeg + 2; ++j) qr[i][j] = T::cvt(qraw[i][j]);
+#pragma unroll
+            for (int x = 0; x < kSeg; ++x) {
                 float z = 0.f;
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int j = 0; j < 3; ++j) z += wq[i * 3 + j] * qw[i][j];
-                T::st(Zp + ((long long)y * gw + x0 + xl) * Zsn + lane * T::esz, poison ? __builtin_nanf("") : z);
-#pragma unroll
-                for (int i = 0; i < 3; ++i) {
-                    qw[i][0] = qw[i][1];
-                    qw[i][1] = qw[i][2];
-                }
+                    for (int jj = 0; jj < 3; ++jj) z += wq[i * 3 + jj] * qr[i][x + jj];
+                if (x >= lo && x < hi) T::st(zrow + x * Zsn, poison ? __builtin_nanf("") : z);
             }
         }
         if (!q_early) __syncthreads();
@@ -321,7 +361,8 @@ ConvPlan plan_conv(int nslices, int gh, int gw, int esz, int cap) {
     const long long slices = (nslices + 7) / 8 * 8; // XCD-aware grids round slices up to 8
     const int pb = 64 * esz;
     auto fits = [&](int R, int TW) {
-        return ((long long)2 * (R + 2) * (TW + 2) + (long long)R * TW) * pb + 3 * 1024 <= kTileBytes + 3 * 1024;
+        const long long TWp = TW > kSeg ? TW : kSeg; // LDS rows hold at least one segment
+        return ((long long)2 * (R + 2) * (TWp + 2) + (long long)R * TWp) * pb + 3 * 1024 <= kTileBytes + 3 * 1024;
     };
     ConvPlan p{};
     long long target = cap > 0 ? cap / slices : 1;

@@ -445,17 +445,28 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass2(BwdArgs a) {
 }
 
 // ------------------------------------------------------------ batch sums --
+// 16 workgroups per head, one dW0 element per thread; the B terms of an
+// element are loaded together and added in ascending b.
 __global__ __launch_bounds__(kThreads, 1) void bwd_batch(BwdArgs a) {
-    const int h = blockIdx.x, tid = threadIdx.x;
-    for (int e = tid; e < 4096; e += kThreads) {
-        float v = 0.f;
-        for (int b = 0; b < a.B; ++b) v += a.dW0s[((long long)b * a.H + h) * 4096 + e];
-        a.dW0[(long long)h * 4096 + e] = v;
+    const int h = blockIdx.x >> 4, tid = threadIdx.x;
+    const int e = (blockIdx.x & 15) * kThreads + tid;
+    const float* src = a.dW0s + (long long)h * 4096 + e;
+    const long long step = (long long)a.H * 4096;
+    float v = 0.f;
+    int b = 0;
+    for (; b + 8 <= a.B; b += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = src[(b + i) * step];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += t[i];
     }
-    if (tid == 0) {
-        float v = 0.f;
-        for (int b = 0; b < a.B; ++b) v += a.detas[(long long)b * a.H + h];
-        a.deta[h] = v;
+    for (; b < a.B; ++b) v += src[b * step];
+    a.dW0[(long long)h * 4096 + e] = v;
+    if ((blockIdx.x & 15) == 0 && tid == 0) {
+        float d = 0.f;
+        for (int bb = 0; bb < a.B; ++bb) d += a.detas[(long long)bb * a.H + h];
+        a.deta[h] = d;
     }
 }
 
@@ -522,7 +533,7 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
     if (s.bf16) hipLaunchKernelGGL(bwd_pass2<true>, grid, block, 0, stream, a);
     else hipLaunchKernelGGL(bwd_pass2<false>, grid, block, 0, stream, a);
-    hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H), block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H * 16), block, 0, stream, a);
     return hipGetLastError();
 }
 

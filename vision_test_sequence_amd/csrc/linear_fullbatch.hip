@@ -541,7 +541,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
             const long long tok = c.t0 + min(row, T - 1);
             __builtin_amdgcn_global_load_lds((const void*)(c.Kp + tok * c.Ksn + okv), (lds_void*)(Ks + q * 1024), 16, 0, 0);
             __builtin_amdgcn_global_load_lds((const void*)(c.Vp + tok * c.Vsn + okv), (lds_void*)(Vs + q * 1024), 16, 0, 0);
-            if (a.Z.ptr)
+            if (a.Z.ptr && a.S == 1)
                 __builtin_amdgcn_global_load_lds((const void*)(c.Qp + tok * c.Qsn + oq), (lds_void*)(Qs + q * 1024), 16, 0, 0);
         }
     }
@@ -577,7 +577,30 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     reduce_waves(accC, accA, ldsf, mA, mC, w, lane, g, m, false);
 
     // ---- phase 2
+    // With S > 1 the Q tile is loaded once the exchange is over, together
+    // with W1: K and V have the memory system to themselves at the start,
+    // and Q's latency overlaps W1's.  These loads are written as inline
+    // assembly so that the compiler does not make the exchange's LDS reads
+    // wait for them; the wait for the W1 loads issued after them (in-order
+    // completion) and a barrier complete them before phase 3 reads the Q
+    // region.
+    auto issue_q = [&]() {
+        if (!a.Z.ptr || T <= 0) return;
+        const int rows = (T + 31) & ~31;
+        const int ninstr = rows * RS / 64;
+        for (int q = w; q < ninstr; q += 4) {
+            const int p = q * 64 + lane;
+            const int row = p / RS;
+            const int oq = ((p % RS) ^ swz_q<BF>(row)) * 16;
+            const long long tok = c.t0 + min(row, T - 1);
+            const uint32_t dst = __builtin_amdgcn_readfirstlane(
+                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(Qs + q * 1024));
+            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                         :: "v"(c.Qp + tok * c.Qsn + oq), "s"(dst) : "memory", "m0");
+        }
+    };
     float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r);
+    if (a.S > 1) issue_q();
 
     // ---- phase 3: Z from the resident Q region (skipped when only A and G
     // are wanted)
@@ -589,6 +612,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
         const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
+        if (a.S > 1) { // every wave's Q loads have landed (see issue_q)
+            drain_vmem();
+            lds_barrier();
+        }
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll 2
         for (int step = w; step < nsteps; step += 4) {
@@ -602,6 +629,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         release_end(a, c.slice, rel);
     } else {
         const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
+        if (a.S > 1) { // every wave's Q loads have landed (see issue_q)
+            drain_vmem();
+            lds_barrier();
+        }
         const unsigned rel = release_begin(a, c.slice);
         for (int step = w; step < nsteps; step += 4) {
             const int row = step * 16 + m;
