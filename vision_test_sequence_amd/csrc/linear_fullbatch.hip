@@ -67,7 +67,7 @@ template <bool BF> __device__ __forceinline__ int swz_kv(int row);
 template <> __device__ __forceinline__ int swz_kv<true>(int row) { return ((row >> 3) & 3) << 1; }
 template <> __device__ __forceinline__ int swz_kv<false>(int row) { return (row & 3) << 2; }
 template <bool BF> __device__ __forceinline__ int swz_q(int row);
-template <> __device__ __forceinline__ int swz_q<true>(int row) { return row & 7; }
+template <> __device__ __forceinline__ int swz_q<true>(int row) { return (row >> 1) & 7; }
 template <> __device__ __forceinline__ int swz_q<false>(int row) { return row & 15; }
 
 
@@ -176,7 +176,8 @@ __device__ __forceinline__ void write_tile(const v4f& v, int t, float* mA, float
 // Returns W1 in LDS (pitch MP) when S == 1; nullptr when S > 1, where W1 is
 // complete in the workspace at a.w1 + slice*4096 on return.
 __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
-                             float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r) {
+                             float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r,
+                             bool published = false) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
@@ -226,29 +227,30 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     }
 
     // S > 1: publish this workgroup's partial in reducer-major order,
-    // part[slice][j][sp][mat][r][cc] with column c = j*nc + cc: the block a
-    // reducer j gathers is then one contiguous run of S*128*nc floats.
+    // part[slice][j][sp][mat][cc][r] with column c = j*nc + cc: the block a
+    // reducer j gathers is then one contiguous run of S*128*nc floats, and
+    // four consecutive rows of one column are one 16-byte store.
     const int nc = 64 / a.S, c0 = split * nc;
     const long long sb = (long long)slice * a.S * 8192;
     unsigned* cnt = counter_at(a.cnt, slice);
-    auto pidx = [&](int j, int sp, int mat, int r, int cc) {
-        return sb + ((long long)(j * a.S + sp) * 2 + mat) * 64 * nc + r * nc + cc;
+    auto pidx = [&](int j, int sp, int mat, int cc, int r) {
+        return sb + ((long long)(j * a.S + sp) * 2 + mat) * 64 * nc + cc * 64 + r;
     };
-    if (a.xcd && nc >= 4) {
+    if (published) {
+        // the caller stored this workgroup's partial from its registers
+    } else if (a.xcd) {
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
-            const int e4 = f * kThreads + tid, mat = e4 >> 10, r = (e4 >> 4) & 63, c4 = (e4 & 15) * 4;
-            *reinterpret_cast<f32x4*>(a.part + pidx(c4 / nc, split, mat, r, c4 % nc)) =
-                *reinterpret_cast<const f32x4*>((mat ? mC : mA) + r * MP + c4);
+            const int q = f * kThreads + tid, mat = q >> 10, c = (q >> 4) & 63, r4 = (q & 15) * 4;
+            const float* M = mat ? mC : mA;
+            *reinterpret_cast<f32x4*>(a.part + pidx(c / nc, split, mat, c % nc, r4)) =
+                f32x4{M[r4 * MP + c], M[(r4 + 1) * MP + c], M[(r4 + 2) * MP + c], M[(r4 + 3) * MP + c]};
         }
     } else {
 #pragma unroll 8
         for (int f = 0; f < 32; ++f) {
             const int e = f * kThreads + tid, mat = e >> 12, r = (e >> 6) & 63, c = e & 63;
-            float* dst = a.part + pidx(c / nc, split, mat, r, c % nc);
-            const float v = (mat ? mC : mA)[r * MP + c];
-            if (a.xcd) *dst = v;
-            else xstore(dst, v);
+            xstore(a.part + pidx(c / nc, split, mat, c % nc, r), (mat ? mC : mA)[r * MP + c]);
         }
     }
     slice_barrier(cnt, (unsigned)a.S);
@@ -256,11 +258,11 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
 
     // Sum this workgroup's block of all S partials over the splits, in split
     // order, straight from memory: the block is contiguous, value (sp, e) at
-    // blk[sp*nel + e] with e = (mat*64 + r)*nc + cc; thread t sums elements
+    // blk[sp*nel + e] with e = (mat*nc + cc)*64 + r; thread t sums elements
     // t + 256k (k < 32/S) and has all of its 32 loads in flight together.
     const float* blk = a.part + pidx(split, 0, 0, 0, 0);
     const int nel = 128 * nc; // >= 256 since S <= 32
-    float* res = lds;         // [mat][64][nc] reduced block
+    float* res = lds;         // [mat][nc][64] reduced block
     {
         const int lg = __builtin_ctz(a.S); // S is a power of two
         float v[32];
@@ -286,21 +288,23 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     float* w1g = a.w1 + (long long)slice * 4096;
     for (int e = tid; e < 64 * nc; e += kThreads) {
         const int r = e / nc, cc = e % nc, c = c0 + cc;
+        const float* acol = res + cc * 64; // A[.][c]
         float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
 #pragma unroll 4
         for (int j = 0; j < 64; j += 4) {
             const f32x4 wv = *reinterpret_cast<const f32x4*>(w0s_split + r * MP + j);
-            acc0 += wv[0] * res[(j + 0) * nc + cc];
-            acc1 += wv[1] * res[(j + 1) * nc + cc];
-            acc2 += wv[2] * res[(j + 2) * nc + cc];
-            acc3 += wv[3] * res[(j + 3) * nc + cc];
+            const f32x4 av = *reinterpret_cast<const f32x4*>(acol + j);
+            acc0 += wv[0] * av[0];
+            acc1 += wv[1] * av[1];
+            acc2 += wv[2] * av[2];
+            acc3 += wv[3] * av[3];
         }
-        const float gv = scale * (((acc0 + acc1) + (acc2 + acc3)) - res[(64 + r) * nc + cc]);
+        const float gv = scale * (((acc0 + acc1) + (acc2 + acc3)) - res[(nc + cc) * 64 + r]);
         const float w1v = w0s_split[r * MP + c] - eta * gv;
         if (a.xcd) w1g[r * 64 + c] = w1v;
         else xstore(w1g + r * 64 + c, w1v);
         if (sv) {
-            sv[r * 64 + c] = res[r * nc + cc];
+            sv[r * 64 + c] = acol[r];
             sv[4096 + r * 64 + c] = gv;
         }
     }
@@ -510,6 +514,137 @@ __device__ __forceinline__ void reduce_waves(v4f* accC, v4f* accA, float* red, f
     lds_barrier();
 }
 
+// K and V rows of the resident bf16 kernel, read with transposing loads:
+// one half-wave of such a read covers rows 8g + e, 8(g+1) + e (e = 0..3,
+// g even), 32 bytes each; the swizzle gives the four rows of each parity
+// four different slot pairs, so the half-wave touches every LDS bank once.
+__device__ __forceinline__ int swz_tr(int row) { return 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1); }
+
+// ------------------------------------------- Gram by tile ownership (bf16) --
+// Wave w accumulates rows 16w..16w+15 of C = V^T K and of A = K^T K over
+// every token of the split (16 + 16 tiles of which it owns 4 + 4), so the
+// four waves never add partial sums.  Token-contracted operands come from
+// the staged rows with ds_read_b64_tr_b16: in each 16-lane group, lane
+// 4e + a points at token 8g + e (second read: + 4), channels 16 blk + 4a,
+// and lane m of the group receives channel 16 blk + m of those four tokens,
+// which is the MFMA operand layout (k = token).  Rows are XOR-swizzled by
+// swz_tr (the same for the two reads of a pair).
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+__device__ __forceinline__ int tr_off(int lane, int blk) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, aa = lane & 3;
+    return (8 * g + e) * 128 + (((2 * blk + (aa >> 1)) ^ swz_tr(8 * g + e)) << 4) + (aa & 1) * 8;
+}
+__device__ __forceinline__ v8bf tr_pair(const char* p) {
+    const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * 128));
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// K, V: staged bf16 rows (128 bytes, swz_tr), rows T.. up to a multiple of
+// 32 zeroed.  Leaves rows 16W.. of C and A in accC / accA: lane (g, m)
+// holds [16W + 4g + i][16cb + m].  W is the wave index (compile time, so
+// the wave's own K block is one of the four it reads).
+template <int W>
+__device__ __forceinline__ void gram_owned_bf(const char* Ks, const char* Vs, int T, int lane, v4f* accC, v4f* accA) {
+    int off[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) off[blk] = tr_off(lane, blk);
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) accC[cb] = accA[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    const int rows = (T + 31) & ~31;
+    // two operand sets in turn: the reads of one 32-token step are in
+    // flight while the products of the previous one run (a re-read of the
+    // last step past the end is in bounds and unused)
+    struct Ops {
+        v8bf k[4], vown;
+    };
+    auto fetch = [&](int r0, Ops& o) __attribute__((always_inline)) {
+        const char* kp = Ks + r0 * 128;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) o.k[blk] = tr_pair(kp + off[blk]);
+        o.vown = tr_pair(Vs + r0 * 128 + off[W]);
+    };
+    auto products = [&](const Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            accC[cb] = mfma32(o.vown, o.k[cb], accC[cb]);
+            accA[cb] = mfma32(o.k[W], o.k[cb], accA[cb]);
+        }
+    };
+    Ops A, B;
+    fetch(0, A);
+    int r0 = 0;
+    for (; r0 + 64 <= rows; r0 += 64) {
+        fetch(r0 + 32, B);
+        products(A);
+        fetch(min(r0 + 64, rows - 32), A);
+        products(B);
+    }
+    if (r0 < rows) products(A);
+}
+// The owned rows into full row-major [A; C] in LDS (pitch MP).
+__device__ __forceinline__ void write_owned(const v4f* accC, const v4f* accA, int w, int lane, float* mA, float* mC) {
+    lds_barrier(); // mA / mC overlap the K and V regions other waves read
+    const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 16 * w + 4 * g + i, c = 16 * cb + m;
+            mC[r * MP + c] = accC[cb][i];
+            mA[r * MP + c] = accA[cb][i];
+        }
+    lds_barrier();
+}
+// The owned rows straight into this split's partial in the exchange layout
+// of lin_update (reducer-major: part[slice][j][split][mat][cc][r] with
+// column c = j*nc + cc): a lane's four rows of one column are one 16-byte
+// store.
+__device__ __forceinline__ void publish_owned(const LinFwdLaunch& a, int slice, int split, const v4f* accC,
+                                              const v4f* accA, int w, int lane) {
+    const int nc = 64 / a.S;
+    const long long sb = (long long)slice * a.S * 8192;
+    const int g = lane >> 4, m = lane & 15;
+#pragma unroll
+    for (int mat = 0; mat < 2; ++mat)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int c = 16 * cb + m, r0 = 16 * w + 4 * g;
+            float* dst = a.part + sb + ((long long)((c / nc) * a.S + split) * 2 + mat) * 64 * nc + (c % nc) * 64 + r0;
+            const v4f v = mat ? accC[cb] : accA[cb];
+            if (a.xcd) {
+                *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) xstore(dst + i, v[i]);
+            }
+        }
+}
+
+// Direct global->LDS 16-byte load per lane (lane l writes 16 bytes at
+// lds_off + 16 l), written as inline assembly: the compiler neither sees it
+// nor makes later LDS reads wait for it, so the kernel waits for exactly
+// the loads it needs with vmcnt_at_most().  lds_off must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off)
+                 : "memory", "m0");
+}
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (they complete in issue order).  n above 15 waits for all.
+__device__ __forceinline__ void vmcnt_at_most(int n) {
+    switch (n) {
+#define TTT_VMCNT(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        TTT_VMCNT(1) TTT_VMCNT(2) TTT_VMCNT(3) TTT_VMCNT(4) TTT_VMCNT(5) TTT_VMCNT(6) TTT_VMCNT(7)
+        TTT_VMCNT(8) TTT_VMCNT(9) TTT_VMCNT(10) TTT_VMCNT(11) TTT_VMCNT(12) TTT_VMCNT(13) TTT_VMCNT(14)
+        TTT_VMCNT(15)
+#undef TTT_VMCNT
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
 // ------------------------------------------------------ resident kernel --
 template <bool BF>
 __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) {
@@ -529,25 +664,36 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
     const int T = c.t1 - c.t0;
 
-    // ---- every load of the workgroup, issued up front
+    // ---- every load of the workgroup, issued up front: all of K and V,
+    // then all of Q, so K and V land first and Q streams in during the Gram
+    // phase.  The Gram phase waits for K and V only.
+    f32x4 w0r[4];
+    load_w0(a, c.h, w0r);
+    int nq = 0; // Q loads of this wave still allowed in flight
     if (T > 0) {
         const int rows = (T + 31) & ~31;
         const int ninstr = rows * RS / 64; // 1 KB per wave instruction
         for (int q = w; q < ninstr; q += 4) {
             const int p = q * 64 + lane;
             const int row = p / RS;
-            const int okv = ((p % RS) ^ swz_kv<BF>(row)) * 16;
-            const int oq = ((p % RS) ^ swz_q<BF>(row)) * 16;
+            const int okv = ((p % RS) ^ (BF ? swz_tr(row) : swz_kv<BF>(row))) * 16;
             const long long tok = c.t0 + min(row, T - 1);
-            __builtin_amdgcn_global_load_lds((const void*)(c.Kp + tok * c.Ksn + okv), (lds_void*)(Ks + q * 1024), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds((const void*)(c.Vp + tok * c.Vsn + okv), (lds_void*)(Vs + q * 1024), 16, 0, 0);
-            if (a.Z.ptr && a.S == 1)
-                __builtin_amdgcn_global_load_lds((const void*)(c.Qp + tok * c.Qsn + oq), (lds_void*)(Qs + q * 1024), 16, 0, 0);
+            dma16(c.Kp + tok * c.Ksn + okv, Ks + q * 1024);
+            dma16(c.Vp + tok * c.Vsn + okv, Vs + q * 1024);
+        }
+        if (a.Z.ptr) {
+            for (int q = w; q < ninstr; q += 4) {
+                const int p = q * 64 + lane;
+                const int row = p / RS;
+                const int oq = ((p % RS) ^ swz_q<BF>(row)) * 16;
+                const long long tok = c.t0 + min(row, T - 1);
+                dma16(c.Qp + tok * c.Qsn + oq, Qs + q * 1024);
+                ++nq;
+            }
         }
     }
-    f32x4 w0r[4];
-    load_w0(a, c.h, w0r);
-    __syncthreads(); // waits for the direct-to-LDS loads
+    vmcnt_at_most(nq); // this wave's K, V (and W0) loads have landed
+    __syncthreads();   // ... and every wave's
     // rows past the range hold clamped copies: zero them in K and V so the
     // Gram fragments need no masking
     {
@@ -560,47 +706,44 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         lds_barrier();
     }
 
-    // ---- phase 1: Gram blocks
-    v4f accC[16], accA[10];
-#pragma unroll
-    for (int t = 0; t < 16; ++t) accC[t] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < 10; ++t) accA[t] = v4f{0.f, 0.f, 0.f, 0.f};
-    constexpr int KS = BF ? 32 : 16; // tokens per wave k-step
-    const GramLanes gl = gram_lanes(g, m);
-    for (int r0 = w * KS; r0 < T; r0 += 4 * KS) gram_step<BF>(Ks, Vs, r0, gl, accC, accA, g, m);
-    lds_barrier();
-    // K/V regions are free now: 3 x 26 tiles of wave sums at the bottom,
-    // [A; C] right above them; the Q region stays intact for phase 3
+    // ---- phase 1: Gram blocks.  K/V regions are free afterwards: (fp32)
+    // 3 x 26 tiles of wave sums at the bottom, [A; C] right above them; the
+    // Q region stays intact for phase 3
     float* mA = ldsf + 3 * 26 * 256;
     float* mC = mA + 64 * MP;
-    reduce_waves(accC, accA, ldsf, mA, mC, w, lane, g, m, false);
+    bool published = false;
+    if constexpr (BF) {
+        v4f oC[4], oA[4];
+        switch (w) {
+        case 0: gram_owned_bf<0>(Ks, Vs, T, lane, oC, oA); break;
+        case 1: gram_owned_bf<1>(Ks, Vs, T, lane, oC, oA); break;
+        case 2: gram_owned_bf<2>(Ks, Vs, T, lane, oC, oA); break;
+        default: gram_owned_bf<3>(Ks, Vs, T, lane, oC, oA); break;
+        }
+        if (a.S > 1) {
+            publish_owned(a, c.slice, c.split, oC, oA, w, lane);
+            published = true;
+        } else {
+            write_owned(oC, oA, w, lane, mA, mC);
+        }
+    } else {
+        v4f accC[16], accA[10];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) accC[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 10; ++t) accA[t] = v4f{0.f, 0.f, 0.f, 0.f};
+        constexpr int KS = 16; // tokens per wave k-step
+        const GramLanes gl = gram_lanes(g, m);
+        for (int r0 = w * KS; r0 < T; r0 += 4 * KS) gram_step<BF>(Ks, Vs, r0, gl, accC, accA, g, m);
+        lds_barrier();
+        reduce_waves(accC, accA, ldsf, mA, mC, w, lane, g, m, false);
+    }
 
     // ---- phase 2
-    // With S > 1 the Q tile is loaded once the exchange is over, together
-    // with W1: K and V have the memory system to themselves at the start,
-    // and Q's latency overlaps W1's.  These loads are written as inline
-    // assembly so that the compiler does not make the exchange's LDS reads
-    // wait for them; the wait for the W1 loads issued after them (in-order
-    // completion) and a barrier complete them before phase 3 reads the Q
-    // region.
-    auto issue_q = [&]() {
-        if (!a.Z.ptr || T <= 0) return;
-        const int rows = (T + 31) & ~31;
-        const int ninstr = rows * RS / 64;
-        for (int q = w; q < ninstr; q += 4) {
-            const int p = q * 64 + lane;
-            const int row = p / RS;
-            const int oq = ((p % RS) ^ swz_q<BF>(row)) * 16;
-            const long long tok = c.t0 + min(row, T - 1);
-            const uint32_t dst = __builtin_amdgcn_readfirstlane(
-                (uint32_t)(uintptr_t)(__attribute__((address_space(3))) char*)(Qs + q * 1024));
-            asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                         :: "v"(c.Qp + tok * c.Qsn + oq), "s"(dst) : "memory", "m0");
-        }
-    };
-    float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r);
-    if (a.S > 1) issue_q();
+    float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published);
+    // every wave's Q loads have landed (normally long since)
+    drain_vmem();
+    lds_barrier();
 
     // ---- phase 3: Z from the resident Q region (skipped when only A and G
     // are wanted)
@@ -612,10 +755,6 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
         const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
-        if (a.S > 1) { // every wave's Q loads have landed (see issue_q)
-            drain_vmem();
-            lds_barrier();
-        }
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll 2
         for (int step = w; step < nsteps; step += 4) {
@@ -629,10 +768,6 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         release_end(a, c.slice, rel);
     } else {
         const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
-        if (a.S > 1) { // every wave's Q loads have landed (see issue_q)
-            drain_vmem();
-            lds_barrier();
-        }
         const unsigned rel = release_begin(a, c.slice);
         for (int step = w; step < nsteps; step += 4) {
             const int row = step * 16 + m;
