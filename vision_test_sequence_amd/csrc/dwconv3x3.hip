@@ -62,7 +62,7 @@ template <> struct ConvT<true> {
     __device__ static raw_t raw(const char* p) { return *(const uint16_t*)p; }
     __device__ static float cvt(raw_t v) { return __uint_as_float((uint32_t)v << 16); }
     __device__ static float ld(const char* p) { return __uint_as_float((uint32_t)*(const uint16_t*)p << 16); }
-    __device__ static void st(char* p, float v) { *(uint16_t*)p = f2bf(v); }
+    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(f2bf(v), (uint16_t*)p); }
 };
 template <> struct ConvT<false> {
     static constexpr int esz = 4;
@@ -70,7 +70,7 @@ template <> struct ConvT<false> {
     __device__ static raw_t raw(const char* p) { return *(const float*)p; }
     __device__ static float cvt(raw_t v) { return v; }
     __device__ static float ld(const char* p) { return *(const float*)p; }
-    __device__ static void st(char* p, float v) { *(float*)p = v; }
+    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(v, (float*)p); }
 };
 
 // Stage a (rows x cols) block of pixels whose top-left grid position is

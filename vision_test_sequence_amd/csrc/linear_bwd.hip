@@ -143,14 +143,15 @@ template <bool BF> __device__ __forceinline__ void store_row(char* row, const v4
                        pack_bf2(d[1][2], d[1][3])};
         const u32x4 o1{pack_bf2(d[2][0], d[2][1]), pack_bf2(d[2][2], d[2][3]), pack_bf2(d[3][0], d[3][1]),
                        pack_bf2(d[3][2], d[3][3])};
-        *reinterpret_cast<u32x4*>(row + (8 * g) * 2) = o0;
-        *reinterpret_cast<u32x4*>(row + (32 + 8 * g) * 2) = o1;
+        // streaming stores: the gradients are not read again here
+        __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(row + (8 * g) * 2));
+        __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(row + (32 + 8 * g) * 2));
     } else {
         float* r = reinterpret_cast<float*>(row);
-        *reinterpret_cast<f32x4*>(r + 8 * g) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
-        *reinterpret_cast<f32x4*>(r + 8 * g + 4) = f32x4{d[1][0], d[1][1], d[1][2], d[1][3]};
-        *reinterpret_cast<f32x4*>(r + 32 + 8 * g) = f32x4{d[2][0], d[2][1], d[2][2], d[2][3]};
-        *reinterpret_cast<f32x4*>(r + 36 + 8 * g) = f32x4{d[3][0], d[3][1], d[3][2], d[3][3]};
+        __builtin_nontemporal_store(f32x4{d[0][0], d[0][1], d[0][2], d[0][3]}, reinterpret_cast<f32x4*>(r + 8 * g));
+        __builtin_nontemporal_store(f32x4{d[1][0], d[1][1], d[1][2], d[1][3]}, reinterpret_cast<f32x4*>(r + 8 * g + 4));
+        __builtin_nontemporal_store(f32x4{d[2][0], d[2][1], d[2][2], d[2][3]}, reinterpret_cast<f32x4*>(r + 32 + 8 * g));
+        __builtin_nontemporal_store(f32x4{d[3][0], d[3][1], d[3][2], d[3][3]}, reinterpret_cast<f32x4*>(r + 36 + 8 * g));
     }
 }
 

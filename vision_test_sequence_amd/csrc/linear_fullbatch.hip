@@ -421,8 +421,9 @@ __device__ __forceinline__ void apply_bf(const W1FragsBF& w, const u32x4* q, cha
                  pack_bf2(d[1][2], d[1][3])};
         u32x4 o1{pack_bf2(d[2][0], d[2][1]), pack_bf2(d[2][2], d[2][3]), pack_bf2(d[3][0], d[3][1]),
                  pack_bf2(d[3][2], d[3][3])};
-        *reinterpret_cast<u32x4*>(zrow + (8 * g) * 2) = o0;
-        *reinterpret_cast<u32x4*>(zrow + (32 + 8 * g) * 2) = o1;
+        // streaming stores: Z is not read again by this kernel
+        __builtin_nontemporal_store(o0, reinterpret_cast<u32x4*>(zrow + (8 * g) * 2));
+        __builtin_nontemporal_store(o1, reinterpret_cast<u32x4*>(zrow + (32 + 8 * g) * 2));
     }
 }
 __device__ __forceinline__ void apply_f32(const W1FragsF32& w, const u32x4* q, char* zrow, bool ok, int g,
@@ -441,10 +442,10 @@ __device__ __forceinline__ void apply_f32(const W1FragsF32& w, const u32x4* q, c
     }
     if (ok) {
         float* zr = reinterpret_cast<float*>(zrow);
-        *reinterpret_cast<f32x4*>(zr + 8 * g) = f32x4{d[0][0], d[0][1], d[0][2], d[0][3]};
-        *reinterpret_cast<f32x4*>(zr + 8 * g + 4) = f32x4{d[1][0], d[1][1], d[1][2], d[1][3]};
-        *reinterpret_cast<f32x4*>(zr + 32 + 8 * g) = f32x4{d[2][0], d[2][1], d[2][2], d[2][3]};
-        *reinterpret_cast<f32x4*>(zr + 36 + 8 * g) = f32x4{d[3][0], d[3][1], d[3][2], d[3][3]};
+        __builtin_nontemporal_store(f32x4{d[0][0], d[0][1], d[0][2], d[0][3]}, reinterpret_cast<f32x4*>(zr + 8 * g));
+        __builtin_nontemporal_store(f32x4{d[1][0], d[1][1], d[1][2], d[1][3]}, reinterpret_cast<f32x4*>(zr + 8 * g + 4));
+        __builtin_nontemporal_store(f32x4{d[2][0], d[2][1], d[2][2], d[2][3]}, reinterpret_cast<f32x4*>(zr + 32 + 8 * g));
+        __builtin_nontemporal_store(f32x4{d[3][0], d[3][1], d[3][2], d[3][3]}, reinterpret_cast<f32x4*>(zr + 36 + 8 * g));
     }
 }
 

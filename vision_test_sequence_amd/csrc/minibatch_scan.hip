@@ -223,7 +223,8 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const Lane& L, bf1
             const long long poff = (long long)p * 64 + 16 * L.rt + 4 * g;
             if (a.ndir == 1) {
                 bf16_t* dz = valid ? L.Z + zoff : reinterpret_cast<bf16_t*>(L.sink);
-                *reinterpret_cast<u32x2*>(dz) = u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
+                __builtin_nontemporal_store(u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])},
+                                            reinterpret_cast<u32x2*>(dz));
             } else {
                 const int jp = partner_chunk(a, L.dir, p);
                 const bool first = j < jp || (j == jp && L.dir == 0);
@@ -233,9 +234,9 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, const Lane& L, bf1
                 const bool fin = valid && !first && !defer;
                 const f32x4 o = r.pp;
                 bf16_t* dz = fin ? L.Z + zoff : reinterpret_cast<bf16_t*>(L.sink + 4);
-                *reinterpret_cast<u32x2*>(dz) =
-                    u32x2{pack_bf2(0.5f * (Zt[0] + o[0]), 0.5f * (Zt[1] + o[1])),
-                          pack_bf2(0.5f * (Zt[2] + o[2]), 0.5f * (Zt[3] + o[3]))};
+                __builtin_nontemporal_store(u32x2{pack_bf2(0.5f * (Zt[0] + o[0]), 0.5f * (Zt[1] + o[1])),
+                                                  pack_bf2(0.5f * (Zt[2] + o[2]), 0.5f * (Zt[3] + o[3]))},
+                                            reinterpret_cast<u32x2*>(dz));
                 // partner's stores of steps <= j - kPre are complete: publish
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_s_barrier();
