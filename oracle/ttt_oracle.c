@@ -22,7 +22,7 @@
  *    model), observation 1 (end-to-end training differentiates the inner
  *    gradient: the "gradient of the gradient").
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent (the kernels use the same ones):
  *  - full-batch loss is the token mean: L(W) = (1/N) sum_i ||W k_i - v_i||^2,
  *    so G = (2/N) sum_i (W0 k_i - v_i) k_i^T;
  *  - a mini-batch of n_c tokens scales each G_s by 1/n_c, gradients are taken

@@ -99,3 +99,12 @@ def test_fp32_inputs_are_rejected():
     K, Q, V, W0, eta = _on(wl.draw(1, 1, 64, seed=980, dtype="f32"))
     with pytest.raises(TTTError):
         vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 16, BIDIR)
+
+
+def test_workspace_shared_across_shapes():
+    # calls of different shapes reuse one cached workspace: the empty-slot
+    # rows it keeps must stay zero whatever an earlier call stored
+    banner("scan workspace shared across shapes")
+    for B, H, N, b, seed in [(4, 6, 6400, 16, 990), (2, 3, 196, 4, 991), (2, 2, 2000, 16, 992),
+                             (1, 1, 37, 5, 993), (4, 6, 6400, 16, 994), (3, 1, 300, 7, 995)]:
+        _check(*_on(wl.draw(B, H, N, seed=seed, dtype="bf16", unit_rows=True)), b, BIDIR)
