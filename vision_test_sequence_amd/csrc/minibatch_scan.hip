@@ -27,29 +27,47 @@
 //    rows.  V is transposed the same way for the initial value of R.
 //  * tril(Q_c K_c^T)^T comes straight out of K_c Q_c^T's accumulator.
 //
-// Bidirectional average: the forward and backward waves of a column block
-// share a workgroup and step in lockstep.  For each token, the direction
-// that reaches it first stores its fp32 output in the workspace; the other
-// one reads it back kPre chunks ahead of use (register prefetch), averages
-// and stores the bf16 result.  Visibility: vector-memory operations of a
-// wave complete in issue order, so a wave that has received the data of
-// chunk j (loaded after its stores of step j - kPre) has completed those
-// stores; a workgroup barrier then publishes them to its partner.  A
-// prefetch issued at step j may therefore read outputs stored at steps
-// <= j - kPre, i.e. tokens whose two arrivals are >= 2 kPre chunks apart.
-// Tokens closer to the middle of the sequence are averaged after the scan
-// from both stored fp32 outputs.
+// Two waves per (slice, direction, column block): the chain wave carries
+// the recurrence alone (R, R', the X update: the serial path of the scan)
+// and publishes each chunk's K rows, bf16 chunk-start X and R' in LDS; the
+// output wave, one chunk behind, forms Z from them.  One workgroup barrier
+// per chunk hands a chunk from chain wave to output wave (double-buffered
+// LDS).
+//
+// Bidirectional average: the two directions of a column block share a
+// workgroup and step in lockstep.  For each token, the direction that
+// reaches it first stores its fp32 output in the workspace; the other one
+// reads it back kPre chunks ahead of use (register prefetch), averages and
+// stores the bf16 result.  Visibility: vector-memory operations of a wave
+// complete in issue order, so an output wave that has received the data of
+// chunk j (loaded after its stores of chunk j - kPre) has completed those
+// stores, and the next workgroup barrier publishes them to its partner.  A
+// prefetch issued for chunk jj after barrier jj - kPre may therefore read
+// outputs stored for chunks <= jj - 2 kPre - 1: tokens whose two arrivals
+// are more than 2 kPre chunks apart.  Tokens closer to the middle of the
+// sequence are averaged after the scan from both stored fp32 outputs.
 #include "common.hpp"
 #include "internal.hpp"
 
 namespace ttt {
 namespace {
 
-constexpr int kPre = 4;    // chunks in flight per wave (register prefetch depth)
+constexpr int kPre = 12;   // chunks in flight per wave (register prefetch depth)
+static_assert(kPre % 6 == 0, "buffer rotation: j % 2 and j % 3 follow the unrolled index");
 constexpr int kChunk = 16; // token slots of one chunk (MFMA tile rows)
 constexpr int kKRow = 144; // bytes per staged K row (64 channels + pad)
 constexpr int kVRow = 48;  // bytes per staged V row (this block's 16 channels + pad)
-constexpr int kWaveLds = kChunk * (kKRow + kVRow);
+constexpr int kXLane = 48; // bytes per lane of a published chunk: X (32) and R' (8)
+// LDS per direction: K rows x3 (chunk j+1 is staged while the output wave
+// reads chunk j and chunk j+2 waits), V rows x2 (chain wave only),
+// published X/R' x2.  The prefetch depth is a multiple of 6 so that buffer
+// indices are compile-time constants in the unrolled loop.
+constexpr int kKBuf = kChunk * kKRow;
+constexpr int kVBuf = kChunk * kVRow;
+constexpr int kXBuf = 64 * kXLane;
+constexpr int kDirLds = 3 * kKBuf + 2 * kVBuf + 2 * kXBuf;
+constexpr int kXOff = 3 * kKBuf + 2 * kVBuf;
+
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4s_t lds_v4s;
@@ -58,20 +76,11 @@ struct ScanArgs {
     View4 K, Q, V, Z;
     const float* W0;
     const float* eta;
-    float* P;     // [slices][N][64] fp32: first-arrival outputs
-    float* P2;    // [slices][N][64] fp32: second-arrival outputs near the middle
-    float* dummy; // [blocks][2 waves][64 lanes][8] fp32: sink of masked-off stores
+    float* P;          // [slices][N][64] fp32: first-arrival outputs
+    float* P2;         // [slices][N][64] fp32: second-arrival outputs near the middle
+    float* dummy;      // [blocks][2 directions][64 lanes][8] fp32: sink of masked-off stores
     const char* zeros; // 256 zero bytes (never written): the rows of empty slots
     int H, N, b, nch, slices, mode, ndir, xcd;
-};
-
-// One chunk's operands of one lane (token slot m): K and Q channels
-// 32 kb + 8 g .. +7, V channels 16 rt + 4 g .. +3, and the partner's fp32
-// output for the same token and channels (bidirectional mode).
-struct ChunkRegs {
-    u32x4 k[2], q[2];
-    u32x2 v;
-    f32x4 pp;
 };
 
 // Per-lane walk of one chain.  Token slot m of chunk j is token
@@ -79,66 +88,39 @@ struct ChunkRegs {
 // partner direction meets that token is c0 - j with c0 = (N-1-m) / b, in
 // both directions.
 struct Walk {
-    int g, m, rt, dir, b, N, nch;
-    int c0;                   // partner chunk of slot m at chunk 0
-    long long step;           // +-1 token per chunk step of b tokens, as +-b
-    const char *K, *Q, *V;    // token 0 row + this lane's channel offset
-    const char *Kn, *Qn, *Vn; // running: rows of the next chunk to load
-    long long Ksn, Qsn, Vsn;  // bytes per token
-    const float* Pn;          // running: partner's output of the next chunk
-    const float* Pbase;
-    const char* zeros;
-    char* Z;                  // token 0 + channel offset (bytes)
-    long long Zsn;
-    float *P, *P2;            // token 0 + channel offset
-    float* sink;
+    int g, m, rt, dir, b, N, nch, c0;
+    long long step; // token step per chunk: +-b
 };
-
 __device__ __forceinline__ int token_of(const Walk& L, int rho) { return L.dir ? L.N - 1 - rho : rho; }
-__device__ __forceinline__ bool defer_d(int d) { return d < 2 * kPre && d > -2 * kPre; }
-
-__device__ __forceinline__ void issue_loads(const ScanArgs& a, Walk& L, int jj, ChunkRegs& r) {
-    const char *kp, *qp, *vp;
-    const float* pp = L.sink;
-    const bool inrange = jj < L.nch - 1 || (jj == L.nch - 1 && jj * L.b + kChunk - 1 < L.N);
-    if (inrange && L.m < L.b) { // every slot a token of this chunk (uniform but for m)
-        kp = L.Kn;
-        qp = L.Qn;
-        vp = L.Vn;
-        if (a.ndir == 2 && 2 * jj - L.c0 >= 2 * kPre) pp = L.Pn;
-    } else { // ragged or past the end: clamp to a valid token
-        const int jc = min(jj, L.nch - 1);
-        const int rho = jc * L.b + L.m;
-        const bool valid = jj < L.nch && L.m < L.b && rho < L.N;
-        const int p = token_of(L, valid ? rho : 0);
-        // a slot without a token reads zero rows: it then adds nothing to
-        // the state or to the other slots' outputs
-        kp = valid ? L.K + p * L.Ksn : L.zeros;
-        qp = valid ? L.Q + p * L.Qsn : L.zeros;
-        vp = valid ? L.V + p * L.Vsn : L.zeros;
-        if (a.ndir == 2 && valid && jj < L.nch && 2 * jc - L.c0 >= 2 * kPre) pp = L.Pbase + (long long)p * 64;
-    }
-    r.k[0] = *reinterpret_cast<const u32x4*>(kp);
-    r.k[1] = *reinterpret_cast<const u32x4*>(kp + 64);
-    r.q[0] = *reinterpret_cast<const u32x4*>(qp);
-    r.q[1] = *reinterpret_cast<const u32x4*>(qp + 64); // (the zero block is 256 bytes)
-    r.v = *reinterpret_cast<const u32x2*>(vp);
-    if (a.ndir == 2) r.pp = *reinterpret_cast<const f32x4*>(pp);
-    L.Kn += L.step * L.Ksn;
-    L.Qn += L.step * L.Qsn;
-    L.Vn += L.step * L.Vsn;
-    L.Pn += L.step * 64;
+__device__ __forceinline__ bool defer_d(int d) { return d <= 2 * kPre && d >= -2 * kPre; }
+// slot m of chunk jj holds a token
+__device__ __forceinline__ bool slot_valid(const Walk& L, int jj) {
+    return jj < L.nch && L.m < L.b && jj * L.b + L.m < L.N;
 }
-
+// Loads are branch-free (so the compiler can schedule them into the
+// matrix-core latencies): a slot's row pointer advances by one chunk per
+// call and is used only when the slot holds a token; an empty slot reads
+// the zero block.
 __device__ __forceinline__ v4s_t tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
 }
+// Workgroup barrier for the chunk hand-over: LDS writes before it are
+// visible to LDS reads after it (lds_barrier waits for this wave's LDS
+// operations, not for its global loads), and the compiler moves no global
+// access across it.
+__device__ __forceinline__ void chunk_barrier() {
+    asm volatile("" ::: "memory");
+    lds_barrier();
+    asm volatile("" ::: "memory");
+}
 
+// ------------------------------------------------------------ chain wave --
 template <int D>
-__device__ __forceinline__ void scan_chain(const ScanArgs& a, Walk& L, char* kt, char* vt, const float* W0h,
-                                           float eta) {
+__device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
+                           long long Vsn, const float* W0h, float eta, char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
-
+    const int e = (lane & 15) >> 2, aa = lane & 3;
+    char* vbuf = lds + 3 * kKBuf;
     // X = W0^T in accumulator layout
     v4f X[4];
     {
@@ -151,176 +133,239 @@ __device__ __forceinline__ void scan_chain(const ScanArgs& a, Walk& L, char* kt,
             X[2 * kb + 1] = v4f{hi[0], hi[1], hi[2], hi[3]};
         }
     }
-    // LDS addresses.  Writes: this lane's K row chunks and V row piece.
-    // Transposing reads (in each 16-lane group, lane 4e + a points at a
-    // 4-element row piece; lane m of the group receives element m % 4 of
-    // the pieces of lanes 4e + m/4, e = 0..3):
-    //  * update operand of X tile ct: lane (g, 4e + a) points at token
-    //    4g + e, channels pi(ct, 4a) .. +3 = 32(ct>>1) + 8a + 4(ct&1);
-    //  * initial R (= -V^T): token 4g + e, channels 4a .. +3 of the block.
-    const int e = (lane & 15) >> 2, aa = lane & 3;
-    char* kw = kt + m * kKRow + 16 * g;
-    char* vw = vt + m * kVRow + 8 * g;
-    const char* kr = kt + (4 * g + e) * kKRow + 16 * aa;
-    const char* vr = vt + (4 * g + e) * kVRow + 8 * aa;
-
-    ChunkRegs cr[D];
+    const int p0 = token_of(L, m); // may lie outside the slice: then never used
+    const char* kn = K + p0 * Ksn; // running row pointers of the next chunk to load
+    const char* vn = V + p0 * Vsn;
+    const long long kst = L.step * Ksn, vst = L.step * Vsn;
+    struct Regs {
+        u32x4 k[2];
+        u32x2 v;
+    } cr[D];
+    auto issue = [&](int jj, Regs& r) __attribute__((always_inline)) {
+        const bool ok = slot_valid(L, jj);
+        const char* kp = ok ? kn : a.zeros;
+        const char* vp = ok ? vn : a.zeros;
+        r.k[0] = *reinterpret_cast<const u32x4*>(kp);
+        r.k[1] = *reinterpret_cast<const u32x4*>(kp + 64);
+        r.v = *reinterpret_cast<const u32x2*>(vp);
+        kn += kst;
+        vn += vst;
+    };
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue_loads(a, L, u, cr[u]);
+    for (int u = 0; u < D; ++u) issue(u, cr[u]);
 
     const float alpha_full = -2.0f * eta / (float)L.b;
-    const int nlast = L.N - (L.nch - 1) * L.b;
-    const float alpha_last = -2.0f * eta / (float)nlast;
-    const bool ragged_all = L.b < kChunk;
-    // running output pointers of chunk j
-    const long long zst = L.step * L.Zsn;
-    char* zp = L.Z + (long long)token_of(L, m) * L.Zsn;
-    float* p1 = L.P + (long long)token_of(L, m) * 64;
-    float* p2 = L.P2 + (long long)token_of(L, m) * 64;
-    const long long pst = L.step * 64;
+    const float alpha_last = -2.0f * eta / (float)(L.N - (L.nch - 1) * L.b);
+    // LDS addresses: this lane's K row chunks and V row piece; transposing
+    // reads (in each 16-lane group lane 4e + a points at a 4-element row
+    // piece, lane m of the group receives element m % 4 of the pieces of
+    // lanes 4e + m/4, e = 0..3): the update operand of X tile ct is token
+    // 4g + e, channels pi(ct, 4a) .. +3; -V^T is token 4g + e, channels
+    // 4a .. +3 of the block.
+    const int kw = m * kKRow + 16 * g, kr = (4 * g + e) * kKRow + 16 * aa;
+    const int vw = m * kVRow + 8 * g, vr = (4 * g + e) * kVRow + 8 * aa;
+    // stage chunk jj (registers r) in K buffer jj % 3 / V buffer jj % 2 and
+    // read its transposed operands back
+    auto stage = [&](const Regs& r, int kbi, int vbi, v4s_t* ktA, v4s_t& vin) __attribute__((always_inline)) {
+        char* kb = lds + kbi * kKBuf;
+        char* vb = vbuf + vbi * kVBuf;
+        *reinterpret_cast<u32x4*>(kb + kw) = r.k[0];
+        *reinterpret_cast<u32x4*>(kb + kw + 64) = r.k[1];
+        *reinterpret_cast<u32x2*>(vb + vw) = r.v;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) ktA[ct] = tr_read(kb + kr + 64 * (ct >> 1) + 8 * (ct & 1));
+        vin = tr_read(vb + vr);
+    };
+    v4s_t ktA[4], vin;
+    stage(cr[0], 0, 0, ktA, vin);
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
             const int j = j0 + u;
-            ChunkRegs& r = cr[u];
-            // slots without a token hold zero rows (see issue_loads)
-            const bool valid = (!ragged_all && j < L.nch - 1) || (j < L.nch && m < L.b && j * L.b + m < L.N);
+            Regs& r = cr[u];
+            char* xo = lds + kXOff + (u & 1) * kXBuf + lane * kXLane;
+            // the next chunk's operands, one step ahead of their use
+            v4s_t ktN[4], vinN;
+            stage(cr[(u + 1) % D], (u + 1) % 3, (u + 1) & 1, ktN, vinN);
             const float alpha = j < L.nch - 1 ? alpha_full : (j == L.nch - 1 ? alpha_last : 0.f);
 
-            // this chunk's K rows and V piece into the wave's LDS, read back
-            // transposed
-            *reinterpret_cast<u32x4*>(kw) = r.k[0];
-            *reinterpret_cast<u32x4*>(kw + 64) = r.k[1];
-            *reinterpret_cast<u32x2*>(vw) = r.v;
-            v4s_t ktA[4];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) ktA[ct] = tr_read(kr + 64 * (ct >> 1) + 8 * (ct & 1));
-            const v4s_t vin = tr_read(vr);
-
             // bf16 copy of the chunk-start state
-            v8bf xb[2];
+            u32x4 xu[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const u32x4 u4{pack_bf2(X[2 * kb][0], X[2 * kb][1]), pack_bf2(X[2 * kb][2], X[2 * kb][3]),
-                               pack_bf2(X[2 * kb + 1][0], X[2 * kb + 1][1]),
-                               pack_bf2(X[2 * kb + 1][2], X[2 * kb + 1][3])};
-                xb[kb] = as_v8bf(u4);
-            }
-            // R = K X - V
-            v4f R;
+            for (int kb2 = 0; kb2 < 2; ++kb2)
+                xu[kb2] = u32x4{pack_bf2(X[2 * kb2][0], X[2 * kb2][1]), pack_bf2(X[2 * kb2][2], X[2 * kb2][3]),
+                                pack_bf2(X[2 * kb2 + 1][0], X[2 * kb2 + 1][1]),
+                                pack_bf2(X[2 * kb2 + 1][2], X[2 * kb2 + 1][3])};
+            // R = K X - V ;  R' = alpha R.  The two halves of the channel
+            // contraction are independent products added on the vector unit:
+            // a chained accumulation would wait for the first to finish.
+            v4f Rv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R[i] = -bf2f((bf16_t)vin[i]);
-            R = mfma32(as_v8bf(r.k[0]), xb[0], R);
-            R = mfma32(as_v8bf(r.k[1]), xb[1], R);
+            for (int i = 0; i < 4; ++i) Rv[i] = -bf2f((bf16_t)vin[i]);
+            const v4f Ra = mfma32(as_v8bf(r.k[0]), as_v8bf(xu[0]), Rv);
+            const v4f Rb = mfma32(as_v8bf(r.k[1]), as_v8bf(xu[1]), v4f{0.f, 0.f, 0.f, 0.f});
+            const v4f R = Ra + Rb;
             const u32x2 rp2{pack_bf2(alpha * R[0], alpha * R[1]), pack_bf2(alpha * R[2], alpha * R[3])};
-            const v4s rp = as_v4s(rp2);
             // X += K^T R'
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) X[ct] = mfma16(ktA[ct], rp, X[ct]);
+            for (int ct = 0; ct < 4; ++ct) X[ct] = mfma16(ktA[ct], as_v4s(rp2), X[ct]);
+            // publish the chunk for the output wave
+            *reinterpret_cast<u32x4*>(xo) = xu[0];
+            *reinterpret_cast<u32x4*>(xo + 16) = xu[1];
+            *reinterpret_cast<u32x2*>(xo + 32) = rp2;
+            chunk_barrier();
+            issue(j + D, r);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) ktA[ct] = ktN[ct];
+            vin = vinN;
+        }
+    }
+}
 
-            // Z^T = X^T Q^T + R'^T tril(Q K^T)^T   (chunk-start X)
-            v4f S = v4f{0.f, 0.f, 0.f, 0.f};
-            S = mfma32(as_v8bf(r.k[0]), as_v8bf(r.q[0]), S);
-            S = mfma32(as_v8bf(r.k[1]), as_v8bf(r.q[1]), S);
+// ----------------------------------------------------------- output wave --
+template <int D>
+__device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
+                            long long Zsn, float* P, float* P2, float* sink, const char* lds) {
+    const int g = L.g, m = L.m, lane = 16 * g + m;
+    const bool bidir = a.ndir == 2;
+    const int p0 = token_of(L, m); // may lie outside the slice: then never used
+    const char* qn = Q + p0 * Qsn;
+    const float* pn = bidir ? P + (long long)p0 * 64 : sink;
+    const long long qst = L.step * Qsn, pst = L.step * 64;
+    struct Regs {
+        u32x4 q[2];
+        f32x4 pp;
+    } cr[D];
+    auto issue = [&](int jj, Regs& r) __attribute__((always_inline)) {
+        const bool ok = slot_valid(L, jj);
+        const char* qp = ok ? qn : a.zeros;
+        r.q[0] = *reinterpret_cast<const u32x4*>(qp);
+        r.q[1] = *reinterpret_cast<const u32x4*>(qp + 64);
+        if (bidir) {
+            // the partner's fp32 output of this token, when it was stored
+            // long enough before (see the header)
+            const float* src = ok && 2 * jj - L.c0 > 2 * kPre ? pn : sink;
+            r.pp = *reinterpret_cast<const f32x4*>(src);
+        }
+        qn += qst;
+        pn += pst;
+    };
+#pragma unroll
+    for (int u = 0; u < D; ++u) issue(u, cr[u]);
+
+    char* zp = Z + (long long)token_of(L, m) * Zsn; // running output pointers of chunk j
+    float* p1 = bidir ? P + (long long)token_of(L, m) * 64 : sink;
+    float* p2 = bidir ? P2 + (long long)token_of(L, m) * 64 : sink;
+    const long long zst = L.step * Zsn;
+    const int nsteps = ((L.nch + D - 1) / D) * D;
+    for (int j0 = 0; j0 < nsteps; j0 += D) {
+#pragma unroll
+        for (int u = 0; u < D; ++u) {
+            const int j = j0 + u;
+            Regs& r = cr[u];
+            chunk_barrier(); // chunk j published
+            const char* kb = lds + (u % 3) * kKBuf + m * kKRow + 16 * g;
+            const char* xi = lds + kXOff + (u & 1) * kXBuf + lane * kXLane;
+            const u32x4 k0 = *reinterpret_cast<const u32x4*>(kb);
+            const u32x4 k1 = *reinterpret_cast<const u32x4*>(kb + 64);
+            const u32x4 x0 = *reinterpret_cast<const u32x4*>(xi);
+            const u32x4 x1 = *reinterpret_cast<const u32x4*>(xi + 16);
+            const u32x2 rp2 = *reinterpret_cast<const u32x2*>(xi + 32);
+
+            // Z^T = X^T Q^T + R'^T tril(Q K^T)^T   (chunk-start X), as
+            // independent products summed on the vector unit
+            const v4f zero4{0.f, 0.f, 0.f, 0.f};
+            const v4f Sa = mfma32(as_v8bf(k0), as_v8bf(r.q[0]), zero4);
+            const v4f Sb = mfma32(as_v8bf(k1), as_v8bf(r.q[1]), zero4);
+            const v4f Za = mfma32(as_v8bf(x0), as_v8bf(r.q[0]), zero4);
+            const v4f Zb = mfma32(as_v8bf(x1), as_v8bf(r.q[1]), zero4);
+            v4f S = Sa + Sb;
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 if (4 * g + i > m) S[i] = 0.f;
             const u32x2 sb2{pack_bf2(S[0], S[1]), pack_bf2(S[2], S[3])};
-            v4f Zt = v4f{0.f, 0.f, 0.f, 0.f};
-            Zt = mfma32(xb[0], as_v8bf(r.q[0]), Zt);
-            Zt = mfma32(xb[1], as_v8bf(r.q[1]), Zt);
-            Zt = mfma16(rp, as_v4s(sb2), Zt);
+            const v4f Zc = mfma16(as_v4s(rp2), as_v4s(sb2), zero4);
+            const v4f Zt = (Za + Zb) + Zc;
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3
-            if (a.ndir == 1) {
-                bf16_t* dz = valid ? reinterpret_cast<bf16_t*>(zp) : reinterpret_cast<bf16_t*>(L.sink);
+            const bool valid = slot_valid(L, j);
+            if (!bidir) {
+                char* dz = valid ? zp : reinterpret_cast<char*>(sink);
                 __builtin_nontemporal_store(u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])},
                                             reinterpret_cast<u32x2*>(dz));
             } else {
                 const int d = 2 * j - L.c0; // own chunk minus the partner's
                 const bool first = d < 0 || (d == 0 && L.dir == 0);
                 const bool defer = defer_d(d);
-                float* dp = !valid ? L.sink : (first ? p1 : (defer ? p2 : L.sink));
+                float* dp = !valid ? sink : (first ? p1 : (defer ? p2 : sink));
                 *reinterpret_cast<f32x4*>(dp) = f32x4{Zt[0], Zt[1], Zt[2], Zt[3]};
                 const bool fin = valid && !first && !defer;
                 const f32x4 o = r.pp;
-                bf16_t* dz = fin ? reinterpret_cast<bf16_t*>(zp) : reinterpret_cast<bf16_t*>(L.sink + 4);
+                char* dz = fin ? zp : reinterpret_cast<char*>(sink + 4);
                 __builtin_nontemporal_store(u32x2{pack_bf2(0.5f * (Zt[0] + o[0]), 0.5f * (Zt[1] + o[1])),
                                                   pack_bf2(0.5f * (Zt[2] + o[2]), 0.5f * (Zt[3] + o[3]))},
                                             reinterpret_cast<u32x2*>(dz));
-                // partner's stores of steps <= j - kPre are complete: publish
-                asm volatile("" ::: "memory");
-                __builtin_amdgcn_s_barrier();
-                asm volatile("" ::: "memory");
             }
+            asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
             zp += zst;
             p1 += pst;
             p2 += pst;
-            issue_loads(a, L, j + D, r);
+            issue(j + D, r);
         }
     }
 }
 
-__global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kWaveLds];
+__global__ __launch_bounds__(256, 1) void scan_kernel(ScanArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kDirLds];
     const SliceSplit ss = map_block(blockIdx.x, 4, a.xcd);
     if (ss.slice >= a.slices) return; // padding block of the XCD-aware grid
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (w >= a.ndir) return;
+    const int role = w & 1, ds = w >> 1; // chain / output wave of direction slot ds
     const int lane = threadIdx.x & 63;
     Walk L;
     L.g = lane >> 4;
     L.m = lane & 15;
     L.rt = ss.split;
-    L.dir = a.ndir == 2 ? w : (a.mode == 2 ? 1 : 0);
+    L.dir = a.ndir == 2 ? ds : (a.mode == 2 ? 1 : 0);
     L.b = a.b;
     L.N = a.N;
     L.nch = a.nch;
     L.c0 = (a.N - 1 - L.m) / a.b;
     L.step = L.dir ? -(long long)a.b : (long long)a.b;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
-    L.Ksn = a.K.sn * 2;
-    L.Qsn = a.Q.sn * 2;
-    L.Vsn = a.V.sn * 2;
-    L.Zsn = a.Z.sn * 2;
-    L.K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2 + 16 * L.g;
-    L.Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
-    L.V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2 + (16 * L.rt + 4 * L.g) * 2;
-    L.Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2 + (16 * L.rt + 4 * L.g) * 2;
-    const int ch = 16 * L.rt + 4 * L.g;
-    L.P = a.P ? a.P + (long long)ss.slice * a.N * 64 + ch : nullptr;
-    L.P2 = a.P2 ? a.P2 + (long long)ss.slice * a.N * 64 + ch : nullptr;
-    L.Pbase = L.P;
-    L.zeros = a.zeros;
-    L.sink = a.dummy + ((long long)blockIdx.x * 2 + w) * 512 + lane * 8;
-    // running load pointers start at chunk 0, slot m (clamped when slot m
-    // holds no token of chunk 0; the ragged path never uses them then)
-    const int p0 = L.dir ? max(a.N - 1 - L.m, 0) : min(L.m, a.N - 1);
-    L.Kn = L.K + p0 * L.Ksn;
-    L.Qn = L.Q + p0 * L.Qsn;
-    L.Vn = L.V + p0 * L.Vsn;
-    L.Pn = L.P ? L.P + (long long)p0 * 64 : L.sink;
-    char* kt = lds + w * kWaveLds;
-    scan_chain<kPre>(a, L, kt, kt + kChunk * kKRow, a.W0 + (long long)h * 4096, a.eta[h]);
+    const int ch = 16 * L.rt + 4 * L.g; // this lane's output / V channels
+    char* lds_d = lds + ds * kDirLds;
+    float* sink = a.dummy + ((long long)blockIdx.x * 2 + ds) * 512 + lane * 8;
+    if (role == 0) {
+        const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2 + 16 * L.g;
+        const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh + ch) * 2;
+        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, a.W0 + (long long)h * 4096, a.eta[h], lds_d);
+    } else {
+        const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
+        char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh + ch) * 2;
+        float* P = a.P ? a.P + (long long)ss.slice * a.N * 64 + ch : nullptr;
+        float* P2 = a.P2 ? a.P2 + (long long)ss.slice * a.N * 64 + ch : nullptr;
+        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, P2, sink, lds_d);
+    }
 
     if (a.ndir == 2) {
-        // tokens whose two arrivals are < 2 kPre chunks apart: average the
-        // two stored fp32 outputs
+        // tokens whose two arrivals are at most 2 kPre chunks apart: average
+        // the two stored fp32 outputs
         drain_vmem();
         __syncthreads();
-        const int span = (2 * kPre + 1) * a.b;
+        const int span = (2 * kPre + 2) * a.b;
         const int lo = max(0, (a.N - 1) / 2 - span), hi = min(a.N, a.N / 2 + span + 1);
         const float* P = a.P + (long long)ss.slice * a.N * 64;
         const float* P2 = a.P2 + (long long)ss.slice * a.N * 64;
-        bf16_t* Z = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh;
-        for (int e2 = threadIdx.x; e2 < (hi - lo) * 4; e2 += 64 * a.ndir) {
+        bf16_t* Zb = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh;
+        for (int e2 = threadIdx.x; e2 < (hi - lo) * 4; e2 += blockDim.x) {
             const int p = lo + (e2 >> 2), c = 16 * L.rt + 4 * (e2 & 3);
             const int jf = p / a.b, jb = (a.N - 1 - p) / a.b;
             if (!defer_d(jf - jb)) continue;
             const f32x4 x = *reinterpret_cast<const f32x4*>(P + (long long)p * 64 + c);
             const f32x4 y = *reinterpret_cast<const f32x4*>(P2 + (long long)p * 64 + c);
-            *reinterpret_cast<u32x2*>(Z + (long long)p * a.Z.sn + c) =
+            *reinterpret_cast<u32x2*>(Zb + (long long)p * a.Z.sn + c) =
                 u32x2{pack_bf2(0.5f * (x[0] + y[0]), 0.5f * (x[1] + y[1])),
                       pack_bf2(0.5f * (x[2] + y[2]), 0.5f * (x[3] + y[3]))};
         }
@@ -362,7 +407,7 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
         a.P = a.dummy + blocks * 2 * 512;
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(64 * a.ndir), 0, stream, a);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(128 * a.ndir), 0, stream, a);
     return hipGetLastError();
 }
 
