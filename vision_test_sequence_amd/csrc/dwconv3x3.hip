@@ -33,7 +33,9 @@ namespace ttt {
 namespace {
 
 constexpr int kTileBytes = 147456;           // K halo + V + Q halo regions
-constexpr int kRedFloats = 4 * 64 * 9;       // per-wave tap sums
+constexpr int kCT = 512;                     // threads per workgroup: 8 waves, 2 per SIMD
+constexpr int kCW = kCT / 64;
+constexpr int kRedFloats = 4 * 64 * 9;       // tap sums of 4 waves (the 8 are paired first)
 constexpr int kSeg = 16;                     // pixels per row segment
 
 struct ConvArgs {
@@ -82,7 +84,7 @@ __device__ __forceinline__ void stage(char* dst, const char* src, long long sn, 
     constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
     const int total = rows * cols * cpp;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int base = w * 64; base < total; base += kThreads) {
+    for (int base = w * 64; base < total; base += kCT) {
         const int q = base + lane;
         const int qq = q < total ? q : total - 1;
         const int px = qq / cpp, sub = qq % cpp;
@@ -108,7 +110,7 @@ __device__ __forceinline__ void zero_outside(char* blk, int ya, int xa, int rows
     if (!(nl || nr || rows_out)) return;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const u32x4 z{0u, 0u, 0u, 0u};
-    for (int r = w; r < rows; r += kThreads / 64) {
+    for (int r = w; r < rows; r += kCW) {
         char* row = blk + (long long)r * cols * cpp * 16;
         const int y = ya + r;
         if (y < 0 || y >= gh) {
@@ -121,10 +123,10 @@ __device__ __forceinline__ void zero_outside(char* blk, int ya, int xa, int rows
     }
 }
 
-// One workgroup per CU (its LDS), so one wave per SIMD: registers are
-// plentiful and the schedule should favour latency over occupancy.
+// One workgroup per CU (its LDS) of 8 waves, two per SIMD: while one
+// waits for its LDS reads the other computes.
 template <bool BF>
-__global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 1))) void conv_kernel(ConvArgs a) {
+__global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     using T = ConvT<BF>;
     constexpr int pb = 64 * T::esz; // bytes per pixel
     __shared__ __attribute__((aligned(16))) char lds[kTileBytes + 3 * 1024];
@@ -181,7 +183,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         if (q_early) zero_outside<BF>(Qs, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
         __syncthreads();
         const int nsx = (tw + kSeg - 1) / kSeg;
-        for (int sgi = w; sgi < rr * nsx; sgi += 4) {
+        for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
             // Segment k of a row covers pixels [16k, 16k+16); the last one is
             // shifted left to end at the row's end (its first pixels, done by
             // the previous segment, are masked) -- or, in a row narrower than
@@ -225,9 +227,17 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         __syncthreads();
     }
 
-    // fixed-order sum of the 4 waves' tap sums
+    // fixed-order sum of the 8 waves' tap sums: waves w and w + 4 first,
+    // then the four pair sums
+    if (w >= 4) {
 #pragma unroll
-    for (int t = 0; t < 9; ++t) red[(w * 64 + lane) * 9 + t] = gacc[t];
+        for (int t = 0; t < 9; ++t) red[((w - 4) * 64 + lane) * 9 + t] = gacc[t];
+    }
+    __syncthreads();
+    if (w < 4) {
+#pragma unroll
+        for (int t = 0; t < 9; ++t) red[(w * 64 + lane) * 9 + t] = gacc[t] + red[(w * 64 + lane) * 9 + t];
+    }
     __syncthreads();
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)N;
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
     } else {
         float* P = a.part + ((long long)slice * a.S + split) * 576;
         unsigned* cnt = counter_at(a.cnt, slice);
-        for (int e = tid; e < 576; e += kThreads) {
+        for (int e = tid; e < 576; e += kCT) {
             const int c = e / 9, t = e % 9;
             const float v = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) +
                             red[(192 + c) * 9 + t];
@@ -260,23 +270,23 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         const int e0 = (576 * split) / a.S, e1 = (576 * (split + 1)) / a.S, ne = e1 - e0;
         const int tot = ne * a.S; // <= 576 + S <= kRedFloats
         const float* P0 = a.part + (long long)slice * a.S * 576;
-        for (int base = 0; base < tot; base += 4 * kThreads) {
+        for (int base = 0; base < tot; base += 4 * kCT) {
             float v[4];
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int f = base + k * kThreads + tid;
+                const int f = base + k * kCT + tid;
                 const float* src = P0 + (long long)(f / ne) * 576 + e0 + f % ne;
                 v[k] = f < tot ? (a.xcd ? *src : xload(src)) : 0.f;
             }
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int f = base + k * kThreads + tid;
+                const int f = base + k * kCT + tid;
                 if (f < tot) red[f] = v[k];
             }
         }
         __syncthreads();
         float* w1g = a.w1 + (long long)slice * 576;
-        for (int i = tid; i < ne; i += kThreads) {
+        for (int i = tid; i < ne; i += kCT) {
             float sacc = 0.f;
             for (int sp = 0; sp < a.S; ++sp) sacc += red[sp * ne + i];
             const int e = e0 + i;
@@ -289,15 +299,15 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
         slice_barrier(cnt, 2u * a.S);
         if (a.xcd) l1_invalidate();
         {
-            float v[3];
+            float v[2];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int e = k * kThreads + tid;
+            for (int k = 0; k < 2; ++k) {
+                const int e = k * kCT + tid;
                 v[k] = e < 576 ? (a.xcd ? w1g[e] : xload(w1g + e)) : 0.f;
             }
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                const int e = k * kThreads + tid;
+            for (int k = 0; k < 2; ++k) {
+                const int e = k * kCT + tid;
                 if (e < 576) w1s[e] = v[k];
             }
         }
@@ -319,7 +329,7 @@ __global__ __launch_bounds__(kThreads, 1) __attribute__((amdgpu_waves_per_eu(1, 
             __syncthreads();
         }
         const int nsx = (tw + kSeg - 1) / kSeg;
-        for (int sgi = w; sgi < rr * nsx; sgi += 4) {
+        for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
             const int r = sgi / nsx, k = sgi % nsx; // segments as in phase 1
             const int xs = min(k * kSeg, max(tw - kSeg, 0));
             const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
@@ -405,8 +415,8 @@ int conv_resident_per_cu(int bf16) {
     static std::atomic<int> cached[2];
     int n = cached[bf16 ? 1 : 0].load(std::memory_order_relaxed);
     if (n > 0) return n;
-    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<true>, kThreads, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<false>, kThreads, 0);
+    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<true>, kCT, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<false>, kCT, 0);
     if (e != hipSuccess || n < 0) return 0;
     cached[bf16 ? 1 : 0].store(n, std::memory_order_relaxed);
     return n;
@@ -436,7 +446,7 @@ hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
         a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 576 * 4);
     }
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
-    const dim3 grid((unsigned)(gslices * p.S)), block(kThreads);
+    const dim3 grid((unsigned)(gslices * p.S)), block(kCT);
     void* args[] = {&a};
     const void* fn = l.bf16 ? (const void*)conv_kernel<true> : (const void*)conv_kernel<false>;
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
