@@ -75,9 +75,14 @@ __device__ __forceinline__ void lds_barrier() {
 // through the workspace, meeting at a per-slice counter.  Two protocols:
 //  * XCD-local: all workgroups of the slice run on one XCD (see map_block),
 //    so its L2 is their coherence point.  Data moves with ordinary 16-byte
-//    stores and loads; a reader invalidates only its own CU's L1 after the
-//    barrier.  Every exchanged address is written before it is read within
-//    one launch, by workgroups of that one XCD.
+//    stores and loads.  A CU's L1 is not coherent with the other CUs' stores
+//    and cannot be invalidated cheaply (a workgroup-scope invalidate leaves
+//    it as it is, measured on MI355X), so the protocol keeps exchanged
+//    lines out of the reader's L1 until they are final: every exchanged
+//    line is read with plain loads only after the barrier that follows its
+//    last store, by workgroups that have not loaded it earlier in the
+//    launch (L1 starts clean at each launch); earlier touches, such as L2
+//    prefetches, use device-scope loads, which do not fill L1.
 //  * device-wide: data moves with device-scope relaxed atomics (xstore /
 //    xload), performed at the device coherence point.
 // Neither needs an L2-wide writeback or invalidate.
@@ -87,7 +92,6 @@ __device__ __forceinline__ void xstore(float* p, float v) {
 __device__ __forceinline__ float xload(const float* p) {
     return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
 __device__ __forceinline__ unsigned xcc_id() {
     return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20); // HW_REG_XCC_ID[3:0]
 }

@@ -263,7 +263,6 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             else xstore(P + e, v);
         }
         slice_barrier(cnt, (unsigned)a.S);
-        if (a.xcd) l1_invalidate();
         // Gather elements [e0, e1) of all S partials with every load in
         // flight at once (the wave-sum buffer is free now), then sum each
         // element over the splits in split order.
@@ -297,7 +296,6 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             if (a.saved) a.saved[(long long)slice * 576 + e] = gv;
         }
         slice_barrier(cnt, 2u * a.S);
-        if (a.xcd) l1_invalidate();
         {
             float v[2];
 #pragma unroll

@@ -167,6 +167,33 @@ __device__ __forceinline__ void write_tile(const v4f& v, int t, float* mA, float
 }
 
 // ------------------------------------------------------------- phase 2 --
+// A store from one CU to a line that is not in its XCD's L2 goes on to
+// memory without allocating the line there, so a later load of it from
+// another CU of the XCD misses too (measured on MI355X: about 0.6 us for
+// 32 KB, against 0.3 us for L2 hits).  A store to a line that is present
+// updates it in place.  Each workgroup therefore touches one word of every
+// line it will read after the slice barriers -- its gather block of the
+// partials and its share of W1 -- before the writers store them, with
+// device-scope loads: those fill the XCD's L2 but not the CU's L1 (plain
+// loads would leave a copy in L1 that the post-barrier reads would hit,
+// stale).  Touching a line after its writer stored it is harmless: the
+// load then fetches the new contents.  The returned value only keeps the
+// loads alive (keep_alive()).
+template <bool BF, bool XC>
+__device__ __forceinline__ float exchange_prefetch(const LinFwdLaunch& a, int slice, int split) {
+    if constexpr (!XC) return 0.f; // device-wide protocol: atomics at the coherence point
+    const int tid = threadIdx.x;
+    // gather block: S * 128 * (64 / S) floats = 256 lines of 32 floats
+    const float* blk = a.part + (long long)slice * a.S * 8192 + (long long)split * 8192;
+    float v = xload(blk + tid * 32);
+    // W1 (bf16 fragments: 64 lines; fp32: 128 lines), spread over the
+    // slice's S workgroups
+    const int per = (BF ? 64 : 128) / a.S;
+    if (tid < per) v += xload(a.w1 + (long long)slice * 4096 + (split * per + tid) * 32);
+    return v;
+}
+__device__ __forceinline__ void keep_alive(float v) { asm volatile("" ::"v"(v)); }
+
 // From the workgroup's [A; C] (mA, mC: full 64x64, pitch MP) to W1 in LDS.
 // w0r: this thread's 4 x 16 bytes of W0[h] (floats 4*tid + 1024*k).
 // LDS use, S == 1: W0 staged at w0s_one (disjoint from mA, mC); W1 written
@@ -175,9 +202,61 @@ __device__ __forceinline__ void write_tile(const v4f& v, int t, float* mA, float
 //   consumed before the first barrier), W0 at w0s_split >= 8192.
 // Returns W1 in LDS (pitch MP) when S == 1; nullptr when S > 1, where W1 is
 // complete in the workspace at a.w1 + slice*4096 on return.
+// Sum this workgroup's block of the S partials over the splits, in split
+// order, straight from memory: the block is contiguous, split sp's part at
+// blk[sp * 8192 / S ...] (2048 / S float4s).  Every load of a thread is in
+// flight at once; res receives the reduced block (same layout).
+template <int S, bool XC>
+__device__ __forceinline__ void gather_sum(const float* blk, float* res) {
+    constexpr int n4 = 2048 / S;
+    const int tid = threadIdx.x;
+    const f32x4* b4 = reinterpret_cast<const f32x4*>(blk);
+    auto ld = [&](int i) {
+        if constexpr (XC) return b4[i];
+        const float* p = blk + 4 * i;
+        return f32x4{xload(p), xload(p + 1), xload(p + 2), xload(p + 3)};
+    };
+    if constexpr (n4 >= kThreads) {
+        constexpr int per = n4 / kThreads;
+        f32x4 v[per][S];
+#pragma unroll
+        for (int k = 0; k < per; ++k)
+#pragma unroll
+            for (int sp = 0; sp < S; ++sp) v[k][sp] = ld(sp * n4 + k * kThreads + tid);
+#pragma unroll
+        for (int k = 0; k < per; ++k) {
+            f32x4 acc = v[k][0];
+#pragma unroll
+            for (int sp = 1; sp < S; ++sp) acc += v[k][sp];
+            reinterpret_cast<f32x4*>(res)[k * kThreads + tid] = acc;
+        }
+    } else if (tid < n4) {
+        f32x4 v[S];
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) v[sp] = ld(sp * n4 + tid);
+        f32x4 acc = v[0];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp) acc += v[sp];
+        reinterpret_cast<f32x4*>(res)[tid] = acc;
+    }
+}
+
+// Index of W1[r][c] in the bf16 fragment copy of W1 that the XCD-local
+// exchange hands to the apply phase: 16-byte piece (rb, hh, lane) holds
+// W1[perm_row(rb, m)][32 hh + 8 g + j], j = 0..7, lane = 16 g + m, at
+// piece index (rb * 2 + hh) * 64 + lane -- so a lane's eight operand
+// registers are eight 16-byte loads, each wave instruction one contiguous
+// kilobyte.
+__device__ __forceinline__ int w1_frag_index(int r, int c) {
+    const int rb = 2 * (r >> 5) + ((r >> 2) & 1), m = 4 * ((r >> 3) & 3) + (r & 3);
+    const int hh = c >> 5, g = (c >> 3) & 3;
+    return ((rb * 2 + hh) * 64 + 16 * g + m) * 8 + (c & 7);
+}
+
+template <bool BF, bool XC>
 __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
                              float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r,
-                             bool published = false) {
+                             bool published = false, float pf = 0.f) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
@@ -238,7 +317,9 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     };
     if (published) {
         // the caller stored this workgroup's partial from its registers
-    } else if (a.xcd) {
+        // (and prefetched the lines it reads below)
+    } else if constexpr (XC) {
+        pf = exchange_prefetch<BF, XC>(a, slice, split);
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             const int q = f * kThreads + tid, mat = q >> 10, c = (q >> 4) & 63, r4 = (q & 15) * 4;
@@ -254,33 +335,15 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
         }
     }
     slice_barrier(cnt, (unsigned)a.S);
-    if (a.xcd) l1_invalidate();
 
-    // Sum this workgroup's block of all S partials over the splits, in split
-    // order, straight from memory: the block is contiguous, value (sp, e) at
-    // blk[sp*nel + e] with e = (mat*nc + cc)*64 + r; thread t sums elements
-    // t + 256k (k < 32/S) and has all of its 32 loads in flight together.
     const float* blk = a.part + pidx(split, 0, 0, 0, 0);
-    const int nel = 128 * nc; // >= 256 since S <= 32
-    float* res = lds;         // [mat][nc][64] reduced block
-    {
-        const int lg = __builtin_ctz(a.S); // S is a power of two
-        float v[32];
-#pragma unroll
-        for (int f = 0; f < 32; ++f) {
-            const int k = f >> lg, sp = f & (a.S - 1);
-            const float* src = blk + sp * nel + tid + k * kThreads;
-            v[f] = a.xcd ? *src : xload(src);
-        }
-        float acc = 0.f;
-#pragma unroll
-        for (int f = 0; f < 32; ++f) {
-            acc += v[f];
-            if (((f + 1) & (a.S - 1)) == 0) {
-                res[tid + (f >> lg) * kThreads] = acc;
-                acc = 0.f;
-            }
-        }
+    float* res = lds; // [mat][nc][64] reduced block
+    switch (a.S) {
+    case 2: gather_sum<2, XC>(blk, res); break;
+    case 4: gather_sum<4, XC>(blk, res); break;
+    case 8: gather_sum<8, XC>(blk, res); break;
+    case 16: gather_sum<16, XC>(blk, res); break;
+    default: gather_sum<32, XC>(blk, res); break;
     }
     stage_w0(w0s_split);
     lds_barrier();
@@ -301,7 +364,8 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
         }
         const float gv = scale * (((acc0 + acc1) + (acc2 + acc3)) - res[(nc + cc) * 64 + r]);
         const float w1v = w0s_split[r * MP + c] - eta * gv;
-        if (a.xcd) w1g[r * 64 + c] = w1v;
+        if constexpr (BF && XC) reinterpret_cast<bf16_t*>(w1g)[w1_frag_index(r, c)] = f2bf(w1v);
+        else if constexpr (XC) w1g[r * 64 + c] = w1v;
         else xstore(w1g + r * 64 + c, w1v);
         if (sv) {
             sv[r * 64 + c] = acol[r];
@@ -309,8 +373,10 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
         }
     }
     slice_barrier(cnt, 2u * a.S);
-    if (a.xcd) l1_invalidate();
-    return nullptr; // W1 is complete in the workspace at a.w1 + slice*4096
+    keep_alive(pf);
+    // W1 is complete in the workspace at a.w1 + slice*4096 (bf16 fragments
+    // for BF && XC, else row-major fp32)
+    return nullptr;
 }
 
 // Counter release after the last barrier: the increment's result is only
@@ -351,7 +417,8 @@ __device__ __forceinline__ W1FragsBF w1_frags_bf(const float* mW, int g, int m) 
 }
 // The same fragments loaded straight from the workspace copy of W1
 // (row-major 64x64 fp32; plain loads in the XCD-local protocol).
-__device__ __forceinline__ W1FragsBF w1_frags_bf_global(const float* w1g, bool xcd, int g, int m) {
+template <bool XC>
+__device__ __forceinline__ W1FragsBF w1_frags_bf_global(const float* w1g, int g, int m) {
     W1FragsBF w;
     f32x4 v[4][2][2];
 #pragma unroll
@@ -361,7 +428,7 @@ __device__ __forceinline__ W1FragsBF w1_frags_bf_global(const float* w1g, bool x
 #pragma unroll
             for (int k = 0; k < 2; ++k) {
                 const float* src = w1g + perm_row(rb, m) * 64 + 32 * hh + 8 * g + 4 * k;
-                if (xcd) v[rb][hh][k] = *reinterpret_cast<const f32x4*>(src);
+                if constexpr (XC) v[rb][hh][k] = *reinterpret_cast<const f32x4*>(src);
                 else v[rb][hh][k] = f32x4{xload(src), xload(src + 1), xload(src + 2), xload(src + 3)};
             }
 #pragma unroll
@@ -374,18 +441,30 @@ __device__ __forceinline__ W1FragsBF w1_frags_bf_global(const float* w1g, bool x
         }
     return w;
 }
+// The fragments from the bf16 fragment copy (w1_frag_index).
+__device__ __forceinline__ W1FragsBF w1_frags_bf_packed(const float* w1g, int lane) {
+    W1FragsBF w;
+    const u32x4* src = reinterpret_cast<const u32x4*>(w1g) + lane;
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) w.f[rb][hh] = as_v8bf(src[(rb * 2 + hh) * 64]);
+    return w;
+}
 struct W1FragsF32 {
     float f[4][16];
 };
-__device__ __forceinline__ W1FragsF32 w1_frags_f32_global(const float* w1g, bool xcd, int g, int m) {
+template <bool XC>
+__device__ __forceinline__ W1FragsF32 w1_frags_f32_global(const float* w1g, int g, int m) {
     W1FragsF32 w;
 #pragma unroll
     for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
         for (int hh = 0; hh < 4; ++hh) {
             const float* src = w1g + perm_row(rb, m) * 64 + 16 * hh + 4 * g;
-            const f32x4 v = xcd ? *reinterpret_cast<const f32x4*>(src)
-                                : f32x4{xload(src), xload(src + 1), xload(src + 2), xload(src + 3)};
+            f32x4 v;
+            if constexpr (XC) v = *reinterpret_cast<const f32x4*>(src);
+            else v = f32x4{xload(src), xload(src + 1), xload(src + 2), xload(src + 3)};
 #pragma unroll
             for (int i = 0; i < 4; ++i) w.f[rb][hh * 4 + i] = v[i];
         }
@@ -456,10 +535,10 @@ struct SliceCtx {
     char* Zp;
     long long Ksn, Vsn, Qsn, Zsn;
 };
-template <bool BF> __device__ __forceinline__ SliceCtx slice_ctx(const LinFwdLaunch& a) {
+template <bool BF, bool XC> __device__ __forceinline__ SliceCtx slice_ctx(const LinFwdLaunch& a) {
     constexpr int esz = LinCfg<BF>::esz;
     SliceCtx c;
-    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
+    const SliceSplit ss = map_block(blockIdx.x, a.S, XC);
     c.slice = ss.slice;
     c.split = ss.split;
     c.b = c.slice / a.H;
@@ -475,7 +554,7 @@ template <bool BF> __device__ __forceinline__ SliceCtx slice_ctx(const LinFwdLau
     c.Vsn = a.V.sn * esz;
     c.Qsn = a.Q.sn * esz;
     c.Zsn = a.Z.sn * esz;
-    c.poison = a.xcd && ((xcc_id() & 7) != (blockIdx.x & 7));
+    c.poison = XC && ((xcc_id() & 7) != (blockIdx.x & 7));
     return c;
 }
 
@@ -602,6 +681,7 @@ __device__ __forceinline__ void write_owned(const v4f* accC, const v4f* accA, in
 // of lin_update (reducer-major: part[slice][j][split][mat][cc][r] with
 // column c = j*nc + cc): a lane's four rows of one column are one 16-byte
 // store.
+template <bool XC>
 __device__ __forceinline__ void publish_owned(const LinFwdLaunch& a, int slice, int split, const v4f* accC,
                                               const v4f* accA, int w, int lane) {
     const int nc = 64 / a.S;
@@ -614,7 +694,7 @@ __device__ __forceinline__ void publish_owned(const LinFwdLaunch& a, int slice, 
             const int c = 16 * cb + m, r0 = 16 * w + 4 * g;
             float* dst = a.part + sb + ((long long)((c / nc) * a.S + split) * 2 + mat) * 64 * nc + (c % nc) * 64 + r0;
             const v4f v = mat ? accC[cb] : accA[cb];
-            if (a.xcd) {
+            if constexpr (XC) {
                 *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
             } else {
 #pragma unroll
@@ -647,7 +727,7 @@ __device__ __forceinline__ void vmcnt_at_most(int n) {
 }
 
 // ------------------------------------------------------ resident kernel --
-template <bool BF>
+template <bool BF, bool XC>
 __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) {
     using Cfg = LinCfg<BF>;
     constexpr int RS = Cfg::row_slots;
@@ -661,7 +741,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const SliceCtx c = slice_ctx<BF>(a);
+    const SliceCtx c = slice_ctx<BF, XC>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
     const int T = c.t1 - c.t0;
 
@@ -713,6 +793,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     float* mA = ldsf + 3 * 26 * 256;
     float* mC = mA + 64 * MP;
     bool published = false;
+    float pf = 0.f;
     if constexpr (BF) {
         v4f oC[4], oA[4];
         switch (w) {
@@ -722,7 +803,8 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         default: gram_owned_bf<3>(Ks, Vs, T, lane, oC, oA); break;
         }
         if (a.S > 1) {
-            publish_owned(a, c.slice, c.split, oC, oA, w, lane);
+            pf = exchange_prefetch<BF, XC>(a, c.slice, c.split);
+            publish_owned<XC>(a, c.slice, c.split, oC, oA, w, lane);
             published = true;
         } else {
             write_owned(oC, oA, w, lane, mA, mC);
@@ -741,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     }
 
     // ---- phase 2
-    float* W1 = lin_update(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published);
+    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published, pf);
     // every wave's Q loads have landed (normally long since)
     drain_vmem();
     lds_barrier();
@@ -755,7 +837,9 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     const int nsteps = (T + 15) / 16;
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
-        const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
+        const W1FragsBF wf = W1   ? w1_frags_bf(W1, g, m)
+                             : XC ? w1_frags_bf_packed(w1g, lane)
+                                  : w1_frags_bf_global<XC>(w1g, g, m);
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll 2
         for (int step = w; step < nsteps; step += 4) {
@@ -768,7 +852,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         }
         release_end(a, c.slice, rel);
     } else {
-        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
+        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global<XC>(w1g, g, m);
         const unsigned rel = release_begin(a, c.slice);
         for (int step = w; step < nsteps; step += 4) {
             const int row = step * 16 + m;
@@ -792,7 +876,7 @@ static_assert(8192 + 128 + 64 * MP <= 3 * 26 * 256, "phase-2 regions below [A; C
 constexpr int kStages = 3;         // K/V tiles in flight (registers)
 constexpr int kStageBytes = 32768; // K tile + V tile
 
-template <bool BF>
+template <bool BF, bool XC>
 __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     using Cfg = LinCfg<BF>;
     // 64 KB of double-buffered K/V tiles during phase 1; the 78 KB of wave
@@ -802,7 +886,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const SliceCtx c = slice_ctx<BF>(a);
+    const SliceCtx c = slice_ctx<BF, XC>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
     const int t0 = c.t0, t1 = c.t1;
 
@@ -901,7 +985,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     float* mC = lds + 64 * MP;
     reduce_waves(accC, accA, lds, mA, mC, w, lane, g, m, true);
 
-    float* W1 = lin_update(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r);
+    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r);
     if (!a.Z.ptr) { // only A and G wanted
         release_end(a, c.slice, release_begin(a, c.slice));
         return;
@@ -909,7 +993,9 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
 
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
-        const W1FragsBF wf = W1 ? w1_frags_bf(W1, g, m) : w1_frags_bf_global(w1g, a.xcd, g, m);
+        const W1FragsBF wf = W1   ? w1_frags_bf(W1, g, m)
+                             : XC ? w1_frags_bf_packed(w1g, lane)
+                                  : w1_frags_bf_global<XC>(w1g, g, m);
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
@@ -926,7 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
         }
         release_end(a, c.slice, rel);
     } else {
-        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global(w1g, a.xcd, g, m);
+        const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global<XC>(w1g, g, m);
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
@@ -986,10 +1072,11 @@ size_t lin_fwd_ws_bytes(int B, int H, int N) {
 
 int lin_fwd_resident_per_cu(int bf16) {
     static std::atomic<int> cache[4];
-    const int r = bf16 ? occupancy((const void*)lin_fwd_resident<true>, cache[0])
-                       : occupancy((const void*)lin_fwd_resident<false>, cache[1]);
-    const int s = bf16 ? occupancy((const void*)lin_fwd_stream<true>, cache[2])
-                       : occupancy((const void*)lin_fwd_stream<false>, cache[3]);
+    // the kernels of both exchange protocols have the same LDS footprint
+    const int r = bf16 ? occupancy((const void*)lin_fwd_resident<true, true>, cache[0])
+                       : occupancy((const void*)lin_fwd_resident<false, true>, cache[1]);
+    const int s = bf16 ? occupancy((const void*)lin_fwd_stream<true, true>, cache[2])
+                       : occupancy((const void*)lin_fwd_stream<false, true>, cache[3]);
     return r < s ? r : s;
 }
 
@@ -1004,10 +1091,13 @@ hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     const dim3 grid((unsigned)(gslices * a.S)), block(kThreads);
     void* args[] = {&a};
     const void* fn;
-    if (resident)
-        fn = a.bf16 ? (const void*)lin_fwd_resident<true> : (const void*)lin_fwd_resident<false>;
-    else
-        fn = a.bf16 ? (const void*)lin_fwd_stream<true> : (const void*)lin_fwd_stream<false>;
+    if (resident) {
+        if (a.xcd) fn = a.bf16 ? (const void*)lin_fwd_resident<true, true> : (const void*)lin_fwd_resident<false, true>;
+        else fn = a.bf16 ? (const void*)lin_fwd_resident<true, false> : (const void*)lin_fwd_resident<false, false>;
+    } else {
+        if (a.xcd) fn = a.bf16 ? (const void*)lin_fwd_stream<true, true> : (const void*)lin_fwd_stream<false, true>;
+        else fn = a.bf16 ? (const void*)lin_fwd_stream<true, false> : (const void*)lin_fwd_stream<false, false>;
+    }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
