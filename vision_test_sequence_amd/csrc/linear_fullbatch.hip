@@ -177,22 +177,27 @@ __device__ __forceinline__ void write_tile(const v4f& v, int t, float* mA, float
 // device-scope loads: those fill the XCD's L2 but not the CU's L1 (plain
 // loads would leave a copy in L1 that the post-barrier reads would hit,
 // stale).  Touching a line after its writer stored it is harmless: the
-// load then fetches the new contents.  The returned value only keeps the
-// loads alive (keep_alive()).
+// load then fetches the new contents.  The returned values only keep the
+// loads alive (keep_alive(), placed after the last barrier: nothing waits
+// for them before).
+struct Prefetch {
+    float blk, w1;
+};
 template <bool BF, bool XC>
-__device__ __forceinline__ float exchange_prefetch(const LinFwdLaunch& a, int slice, int split) {
-    if constexpr (!XC) return 0.f; // device-wide protocol: atomics at the coherence point
+__device__ __forceinline__ Prefetch exchange_prefetch(const LinFwdLaunch& a, int slice, int split, bool gx) {
+    if constexpr (!XC) return Prefetch{0.f, 0.f}; // device-wide protocol: atomics at the coherence point
     const int tid = threadIdx.x;
-    // gather block: S * 128 * (64 / S) floats = 256 lines of 32 floats
-    const float* blk = a.part + (long long)slice * a.S * 8192 + (long long)split * 8192;
-    float v = xload(blk + tid * 32);
+    // gather block: [A; C] exchange S * 128 * (64 / S) floats = 256 lines
+    // of 32 floats; G exchange 4096 floats = 128 lines
+    const float* blk = gx ? a.part + (long long)slice * a.S * 4096 + (long long)split * 4096 + min(tid, 127) * 32
+                          : a.part + (long long)slice * a.S * 8192 + (long long)split * 8192 + tid * 32;
     // W1 (bf16 fragments: 64 lines; fp32: 128 lines), spread over the
-    // slice's S workgroups
-    const int per = (BF ? 64 : 128) / a.S;
-    if (tid < per) v += xload(a.w1 + (long long)slice * 4096 + (split * per + tid) * 32);
-    return v;
+    // slice's S workgroups; threads past the share repeat its last line
+    const int per = (BF ? 64 : 128) >> __builtin_ctz(a.S);
+    const int line = split * per + min(tid, per - 1);
+    return Prefetch{xload(blk), xload(a.w1 + (long long)slice * 4096 + line * 32)};
 }
-__device__ __forceinline__ void keep_alive(float v) { asm volatile("" ::"v"(v)); }
+__device__ __forceinline__ void keep_alive(const Prefetch& p) { asm volatile("" ::"v"(p.blk), "v"(p.w1)); }
 
 // From the workgroup's [A; C] (mA, mC: full 64x64, pitch MP) to W1 in LDS.
 // w0r: this thread's 4 x 16 bytes of W0[h] (floats 4*tid + 1024*k).
@@ -256,7 +261,7 @@ __device__ __forceinline__ int w1_frag_index(int r, int c) {
 template <bool BF, bool XC>
 __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
                              float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r,
-                             bool published = false, float pf = 0.f) {
+                             bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
@@ -309,7 +314,8 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     // part[slice][j][sp][mat][cc][r] with column c = j*nc + cc: the block a
     // reducer j gathers is then one contiguous run of S*128*nc floats, and
     // four consecutive rows of one column are one 16-byte store.
-    const int nc = 64 / a.S, c0 = split * nc;
+    const int lgnc = 6 - __builtin_ctz(a.S); // S is a power of two
+    const int nc = 1 << lgnc, c0 = split * nc;
     const long long sb = (long long)slice * a.S * 8192;
     unsigned* cnt = counter_at(a.cnt, slice);
     auto pidx = [&](int j, int sp, int mat, int cc, int r) {
@@ -317,21 +323,19 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     };
     if (published) {
         // the caller stored this workgroup's partial from its registers
-        // (and prefetched the lines it reads below)
     } else if constexpr (XC) {
-        pf = exchange_prefetch<BF, XC>(a, slice, split);
 #pragma unroll
         for (int f = 0; f < 8; ++f) {
             const int q = f * kThreads + tid, mat = q >> 10, c = (q >> 4) & 63, r4 = (q & 15) * 4;
             const float* M = mat ? mC : mA;
-            *reinterpret_cast<f32x4*>(a.part + pidx(c / nc, split, mat, c % nc, r4)) =
+            *reinterpret_cast<f32x4*>(a.part + pidx(c >> lgnc, split, mat, c & (nc - 1), r4)) =
                 f32x4{M[r4 * MP + c], M[(r4 + 1) * MP + c], M[(r4 + 2) * MP + c], M[(r4 + 3) * MP + c]};
         }
     } else {
 #pragma unroll 8
         for (int f = 0; f < 32; ++f) {
             const int e = f * kThreads + tid, mat = e >> 12, r = (e >> 6) & 63, c = e & 63;
-            xstore(a.part + pidx(c / nc, split, mat, c % nc, r), (mat ? mC : mA)[r * MP + c]);
+            xstore(a.part + pidx(c >> lgnc, split, mat, c & (nc - 1), r), (mat ? mC : mA)[r * MP + c]);
         }
     }
     slice_barrier(cnt, (unsigned)a.S);
@@ -350,7 +354,7 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
     float* sv = a.saved ? a.saved + (long long)slice * 8192 : nullptr;
     float* w1g = a.w1 + (long long)slice * 4096;
     for (int e = tid; e < 64 * nc; e += kThreads) {
-        const int r = e / nc, cc = e % nc, c = c0 + cc;
+        const int r = e >> lgnc, cc = e & (nc - 1), c = c0 + cc;
         const float* acol = res + cc * 64; // A[.][c]
         float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
 #pragma unroll 4
@@ -684,7 +688,7 @@ __device__ __forceinline__ void write_owned(const v4f* accC, const v4f* accA, in
 template <bool XC>
 __device__ __forceinline__ void publish_owned(const LinFwdLaunch& a, int slice, int split, const v4f* accC,
                                               const v4f* accA, int w, int lane) {
-    const int nc = 64 / a.S;
+    const int lgnc = 6 - __builtin_ctz(a.S), nc = 1 << lgnc; // S is a power of two
     const long long sb = (long long)slice * a.S * 8192;
     const int g = lane >> 4, m = lane & 15;
 #pragma unroll
@@ -692,7 +696,8 @@ __device__ __forceinline__ void publish_owned(const LinFwdLaunch& a, int slice, 
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int c = 16 * cb + m, r0 = 16 * w + 4 * g;
-            float* dst = a.part + sb + ((long long)((c / nc) * a.S + split) * 2 + mat) * 64 * nc + (c % nc) * 64 + r0;
+            float* dst =
+                a.part + sb + ((long long)((c >> lgnc) * a.S + split) * 2 + mat) * 64 * nc + (c & (nc - 1)) * 64 + r0;
             const v4f v = mat ? accC[cb] : accA[cb];
             if constexpr (XC) {
                 *reinterpret_cast<f32x4*>(dst) = f32x4{v[0], v[1], v[2], v[3]};
@@ -723,6 +728,126 @@ __device__ __forceinline__ void vmcnt_at_most(int n) {
         TTT_VMCNT(15)
 #undef TTT_VMCNT
     default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
+// ------------------------------------------------------- G exchange --
+// bf16, XCD-local, when A and G are not wanted: each split publishes
+// G_s = W0 A_s - C_s (16 KB) instead of [A_s; C_s] (32 KB), so the
+// reducers only add the S partials and apply W1 = W0 - eta (2/N) G
+// elementwise.  (G is linear in A and C, so the sum of the G_s is G.)
+//
+// Publish order of the 4096 entries P = 256 q + e: chunk q = 4 rb + 2 hh
+// + jh holds rows perm_row(rb, m') (m' = 0..15) x columns 32 hh + 16 jh +
+// cl (cl = 0..15); inside a chunk e = 128 p + 64 gh + 4 cl + i stands for
+// m' = 8 p + 4 gh + i.  Wave w's lanes (g, m) hold G rows 16 w + 4 g + i,
+// column 16 cb + m, i.e. chunk 8 (w>>1) + 4 (g&1) + cb, p = w&1, gh = g>>1,
+// cl = m: one store instruction writes two runs of 512 contiguous bytes
+// (whole cache lines, no partial-line traffic).  The W1 fragment pieces of
+// chunk q are pieces 32 q .. 32 q + 31.  With R = 4096 / S, reducer j sums
+// entries [j R, (j+1) R); split sp stores its part of them at
+// part[slice][j][sp][R].
+__device__ __forceinline__ void split_bf(const float* v, v8bf& hi, v8bf& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        h[k] = pack_bf2(v[2 * k], v[2 * k + 1]);
+        l[k] = pack_bf2(v[2 * k] - bflo(h[k]), v[2 * k + 1] - bfhi(h[k]));
+    }
+    hi = as_v8bf(h);
+    lo = as_v8bf(l);
+}
+constexpr int kAP = 72; // pitch (bf16) of the A planes
+// Wave w's rows of G_s from its owned rows of A_s and C_s.  The product
+// W0 A runs in bf16 with both factors split hi + lo (the lo x lo term is
+// below fp32 rounding) and fp32 accumulation.  A's planes go through LDS:
+// lane (g, m) stores its A[16 w + 4 g + i][16 cb + m] as row 16 cb + m,
+// columns 16 w + 4 g + i of the planes (A is symmetric); W0 is staged from
+// the registers w0r (floats 4 tid + 1024 k of W0[h]).
+__device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int split, const v4f* oC,
+                                          const v4f* oA, const f32x4* w0r, char* lds, int w, int lane) {
+    const int tid = threadIdx.x, g = lane >> 4, m = lane & 15;
+    bf16_t* ahi = reinterpret_cast<bf16_t*>(lds);
+    bf16_t* alo = ahi + 64 * kAP;
+    float* w0s = reinterpret_cast<float*>(lds + 4 * 64 * kAP);
+    lds_barrier(); // the planes overlap the K and V regions other waves read
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 4 * tid + 1024 * k, r = e >> 6, c = e & 63;
+        *reinterpret_cast<f32x4*>(w0s + r * MP + c) = w0r[k];
+    }
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const v4f v = oA[cb];
+        const uint32_t h01 = pack_bf2(v[0], v[1]), h23 = pack_bf2(v[2], v[3]);
+        const uint32_t l01 = pack_bf2(v[0] - bflo(h01), v[1] - bfhi(h01));
+        const uint32_t l23 = pack_bf2(v[2] - bflo(h23), v[3] - bfhi(h23));
+        const int off = (16 * cb + m) * kAP + 16 * w + 4 * g;
+        *reinterpret_cast<u32x2*>(ahi + off) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(alo + off) = u32x2{l01, l23};
+    }
+    lds_barrier();
+    v8bf wh[2], wl[2]; // A operand: W0[16 w + m][32 kk + 8 g + (0..7)]
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        const float* src = w0s + (16 * w + m) * MP + 32 * kk + 8 * g;
+        const f32x4 a0 = *reinterpret_cast<const f32x4*>(src), a1 = *reinterpret_cast<const f32x4*>(src + 4);
+        const float wv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        split_bf(wv, wh[kk], wl[kk]);
+    }
+    v4f G[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) G[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            // B operand A[32 kk + 8 g + j][16 cb + m] = A[16 cb + m][32 kk + 8 g + j]
+            const int off = (16 * cb + m) * kAP + 32 * kk + 8 * g;
+            const v8bf bh = as_v8bf(*reinterpret_cast<const u32x4*>(ahi + off));
+            const v8bf bl = as_v8bf(*reinterpret_cast<const u32x4*>(alo + off));
+            G[cb] = mfma32(wh[kk], bh, G[cb]);
+            G[cb] = mfma32(wh[kk], bl, G[cb]);
+            G[cb] = mfma32(wl[kk], bh, G[cb]);
+        }
+    const int lgS = __builtin_ctz(a.S), lgR = 12 - lgS, R = 1 << lgR;
+    const long long sb = (long long)slice * a.S * 4096;
+    const int e = 128 * (w & 1) + 64 * (g >> 1) + 4 * m;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const v4f gv = G[cb] - oC[cb];
+        const int P = (8 * (w >> 1) + 4 * (g & 1) + cb) * 256 + e;
+        float* dst = a.part + sb + (long long)(((P >> lgR) << lgS) + split) * R + (P & (R - 1));
+        *reinterpret_cast<f32x4*>(dst) = f32x4{gv[0], gv[1], gv[2], gv[3]};
+    }
+}
+// Reducer `split`: sum its R entries over the S splits (split order), form
+// W1 = W0 - eta (2/N) G and store them as bf16 fragments (w1_frag_index).
+template <int S>
+__device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h) {
+    constexpr int R = 4096 / S, n4 = R / 4;
+    const int tid = threadIdx.x;
+    const float eta = a.eta[h];
+    const float scale = 2.0f / (float)a.N;
+    const f32x4* blk = reinterpret_cast<const f32x4*>(a.part + (long long)slice * S * 4096 + (long long)split * S * R);
+    const float* W0h = a.W0 + (long long)h * 4096;
+    bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
+#pragma unroll
+    for (int t4 = tid; t4 < n4; t4 += kThreads) {
+        f32x4 v[S];
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) v[sp] = blk[sp * n4 + t4];
+        const int P = split * R + 4 * t4, q = P >> 8, e = P & 255;
+        const int mq = 8 * (e >> 7) + 4 * ((e >> 6) & 1); // m' of the first of four rows
+        const int rb = q >> 2, c = 32 * ((q >> 1) & 1) + 16 * (q & 1) + ((e >> 2) & 15), r0 = perm_row(rb, mq);
+        float w0v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w0v[i] = W0h[(r0 + i) * 64 + c];
+        f32x4 acc = v[0];
+#pragma unroll
+        for (int sp = 1; sp < S; ++sp) acc += v[sp];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) w1b[w1_frag_index(r0 + i, c)] = f2bf(w0v[i] - eta * (scale * acc[i]));
     }
 }
 
@@ -775,6 +900,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     }
     vmcnt_at_most(nq); // this wave's K, V (and W0) loads have landed
     __syncthreads();   // ... and every wave's
+    // G exchange: bf16, XCD-local, S > 1, A and G not wanted
+    const bool gx = BF && XC && a.S > 1 && !a.saved;
+    // lines read after the slice barriers, into L2 while the Gram runs
+    Prefetch pf{0.f, 0.f};
+    if (a.S > 1) pf = exchange_prefetch<BF, XC>(a, c.slice, c.split, gx);
     // rows past the range hold clamped copies: zero them in K and V so the
     // Gram fragments need no masking
     {
@@ -793,7 +923,6 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     float* mA = ldsf + 3 * 26 * 256;
     float* mC = mA + 64 * MP;
     bool published = false;
-    float pf = 0.f;
     if constexpr (BF) {
         v4f oC[4], oA[4];
         switch (w) {
@@ -802,8 +931,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         case 2: gram_owned_bf<2>(Ks, Vs, T, lane, oC, oA); break;
         default: gram_owned_bf<3>(Ks, Vs, T, lane, oC, oA); break;
         }
-        if (a.S > 1) {
-            pf = exchange_prefetch<BF, XC>(a, c.slice, c.split);
+        if (gx) {
+            publish_g(a, c.slice, c.split, oC, oA, w0r, lds, w, lane);
+            published = true;
+        } else if (a.S > 1) {
             publish_owned<XC>(a, c.slice, c.split, oC, oA, w, lane);
             published = true;
         } else {
@@ -823,7 +954,22 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     }
 
     // ---- phase 2
-    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published, pf);
+    float* W1 = nullptr;
+    if (gx) {
+        unsigned* cnt = counter_at(a.cnt, c.slice);
+        slice_barrier(cnt, (unsigned)a.S);
+        switch (a.S) {
+        case 2: reduce_g<2>(a, c.slice, c.split, c.h); break;
+        case 4: reduce_g<4>(a, c.slice, c.split, c.h); break;
+        case 8: reduce_g<8>(a, c.slice, c.split, c.h); break;
+        case 16: reduce_g<16>(a, c.slice, c.split, c.h); break;
+        default: reduce_g<32>(a, c.slice, c.split, c.h); break;
+        }
+        slice_barrier(cnt, 2u * a.S);
+        keep_alive(pf);
+    } else {
+        W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published, pf);
+    }
     // every wave's Q loads have landed (normally long since)
     drain_vmem();
     lds_barrier();
