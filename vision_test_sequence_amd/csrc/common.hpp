@@ -122,8 +122,10 @@ __device__ __forceinline__ unsigned* counter_at(unsigned* base, int slice) {
 // exchange loads behind it.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target) {
-    drain_vmem();
+// A wave that made no exchange stores since the last barrier may pass
+// drain = false, keeping its loads in flight.
+__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true) {
+    if (drain) drain_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -629,17 +629,20 @@ __device__ __forceinline__ v8bf tr_pair(const char* p) {
 // 32 zeroed.  Leaves rows 16W.. of C and A in accC / accA: lane (g, m)
 // holds [16W + 4g + i][16cb + m].  W is the wave index (compile time, so
 // the wave's own K block is one of the four it reads).
-template <int W>
-__device__ __forceinline__ void gram_owned_bf(const char* Ks, const char* Vs, int T, int lane, v4f* accC, v4f* accA) {
+// Rows [r0, r1) (multiples of 32) only, when r1 > r0.  DC / DA select the
+// C and A parts (a wave may accumulate only one of them).
+template <int W, bool DC = true, bool DA = true>
+__device__ __forceinline__ void gram_owned_bf(const char* Ks, const char* Vs, int r0, int r1, int lane, v4f* accC,
+                                              v4f* accA) {
     int off[4];
 #pragma unroll
     for (int blk = 0; blk < 4; ++blk) off[blk] = tr_off(lane, blk);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) accC[cb] = accA[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-    const int rows = (T + 31) & ~31;
+    if (r1 <= r0) return;
     // two operand sets in turn: the reads of one 32-token step are in
     // flight while the products of the previous one run (a re-read of the
-    // last step past the end is in bounds and unused)
+    // last step of the range is in bounds and unused)
     struct Ops {
         v8bf k[4], vown;
     };
@@ -647,25 +650,25 @@ __device__ __forceinline__ void gram_owned_bf(const char* Ks, const char* Vs, in
         const char* kp = Ks + r0 * 128;
 #pragma unroll
         for (int blk = 0; blk < 4; ++blk) o.k[blk] = tr_pair(kp + off[blk]);
-        o.vown = tr_pair(Vs + r0 * 128 + off[W]);
+        if constexpr (DC) o.vown = tr_pair(Vs + r0 * 128 + off[W]);
     };
     auto products = [&](const Ops& o) __attribute__((always_inline)) {
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
-            accC[cb] = mfma32(o.vown, o.k[cb], accC[cb]);
-            accA[cb] = mfma32(o.k[W], o.k[cb], accA[cb]);
+            if constexpr (DC) accC[cb] = mfma32(o.vown, o.k[cb], accC[cb]);
+            if constexpr (DA) accA[cb] = mfma32(o.k[W], o.k[cb], accA[cb]);
         }
     };
     Ops A, B;
-    fetch(0, A);
-    int r0 = 0;
-    for (; r0 + 64 <= rows; r0 += 64) {
-        fetch(r0 + 32, B);
+    fetch(r0, A);
+    int r = r0;
+    for (; r + 64 <= r1; r += 64) {
+        fetch(r + 32, B);
         products(A);
-        fetch(min(r0 + 64, rows - 32), A);
+        fetch(min(r + 64, r1 - 32), A);
         products(B);
     }
-    if (r0 < rows) products(A);
+    if (r < r1) products(A);
 }
 // The owned rows into full row-major [A; C] in LDS (pitch MP).
 __device__ __forceinline__ void write_owned(const v4f* accC, const v4f* accA, int w, int lane, float* mA, float* mC) {
@@ -764,18 +767,23 @@ constexpr int kAP = 72; // pitch (bf16) of the A planes
 // lane (g, m) stores its A[16 w + 4 g + i][16 cb + m] as row 16 cb + m,
 // columns 16 w + 4 g + i of the planes (A is symmetric); W0 is staged from
 // the registers w0r (floats 4 tid + 1024 k of W0[h]).
-__device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int split, const v4f* oC,
-                                          const v4f* oA, const f32x4* w0r, char* lds, int w, int lane) {
-    const int tid = threadIdx.x, g = lane >> 4, m = lane & 15;
-    bf16_t* ahi = reinterpret_cast<bf16_t*>(lds);
-    bf16_t* alo = ahi + 64 * kAP;
-    float* w0s = reinterpret_cast<float*>(lds + 4 * 64 * kAP);
-    lds_barrier(); // the planes overlap the K and V regions other waves read
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int e = 4 * tid + 1024 * k, r = e >> 6, c = e & 63;
-        *reinterpret_cast<f32x4*>(w0s + r * MP + c) = w0r[k];
-    }
+// LDS layout of the G phase (inside the K and V regions, free after the
+// Gram): A's hi and lo planes (bf16, pitch kAP), then W0 (fp32, pitch MP).
+struct GLds {
+    bf16_t *ahi, *alo;
+    float* w0s;
+};
+__device__ __forceinline__ GLds g_lds(char* lds) {
+    GLds L;
+    L.ahi = reinterpret_cast<bf16_t*>(lds);
+    L.alo = L.ahi + 64 * kAP;
+    L.w0s = reinterpret_cast<float*>(lds + 4 * 64 * kAP);
+    return L;
+}
+// Lane (g, m) of wave w (w < 4) stores its A[16 w + 4 g + i][16 cb + m] as
+// row 16 cb + m, columns 16 w + 4 g + i of the planes (A is symmetric).
+__device__ __forceinline__ void g_write_a(const GLds& L, const v4f* oA, int w, int lane) {
+    const int g = lane >> 4, m = lane & 15;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const v4f v = oA[cb];
@@ -783,14 +791,19 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
         const uint32_t l01 = pack_bf2(v[0] - bflo(h01), v[1] - bfhi(h01));
         const uint32_t l23 = pack_bf2(v[2] - bflo(h23), v[3] - bfhi(h23));
         const int off = (16 * cb + m) * kAP + 16 * w + 4 * g;
-        *reinterpret_cast<u32x2*>(ahi + off) = u32x2{h01, h23};
-        *reinterpret_cast<u32x2*>(alo + off) = u32x2{l01, l23};
+        *reinterpret_cast<u32x2*>(L.ahi + off) = u32x2{h01, h23};
+        *reinterpret_cast<u32x2*>(L.alo + off) = u32x2{l01, l23};
     }
-    lds_barrier();
+}
+// Wave w's rows of G_s = W0 A_s - C_s from the staged planes and W0, stored
+// in publish order.
+__device__ __forceinline__ void g_rows_store(const LinFwdLaunch& a, int slice, int split, const v4f* oC,
+                                             const GLds& L, int w, int lane) {
+    const int g = lane >> 4, m = lane & 15;
     v8bf wh[2], wl[2]; // A operand: W0[16 w + m][32 kk + 8 g + (0..7)]
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-        const float* src = w0s + (16 * w + m) * MP + 32 * kk + 8 * g;
+        const float* src = L.w0s + (16 * w + m) * MP + 32 * kk + 8 * g;
         const f32x4 a0 = *reinterpret_cast<const f32x4*>(src), a1 = *reinterpret_cast<const f32x4*>(src + 4);
         const float wv[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
         split_bf(wv, wh[kk], wl[kk]);
@@ -804,8 +817,8 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
         for (int cb = 0; cb < 4; ++cb) {
             // B operand A[32 kk + 8 g + j][16 cb + m] = A[16 cb + m][32 kk + 8 g + j]
             const int off = (16 * cb + m) * kAP + 32 * kk + 8 * g;
-            const v8bf bh = as_v8bf(*reinterpret_cast<const u32x4*>(ahi + off));
-            const v8bf bl = as_v8bf(*reinterpret_cast<const u32x4*>(alo + off));
+            const v8bf bh = as_v8bf(*reinterpret_cast<const u32x4*>(L.ahi + off));
+            const v8bf bl = as_v8bf(*reinterpret_cast<const u32x4*>(L.alo + off));
             G[cb] = mfma32(wh[kk], bh, G[cb]);
             G[cb] = mfma32(wh[kk], bl, G[cb]);
             G[cb] = mfma32(wl[kk], bh, G[cb]);
@@ -821,9 +834,24 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
         *reinterpret_cast<f32x4*>(dst) = f32x4{gv[0], gv[1], gv[2], gv[3]};
     }
 }
+// Four-wave form: w0r holds floats 4 tid + 1024 k of W0[h].
+__device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int split, const v4f* oC,
+                                          const v4f* oA, const f32x4* w0r, char* lds, int w, int lane) {
+    const int tid = threadIdx.x;
+    const GLds L = g_lds(lds);
+    lds_barrier(); // the planes overlap the K and V regions other waves read
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 4 * tid + 1024 * k, r = e >> 6, c = e & 63;
+        *reinterpret_cast<f32x4*>(L.w0s + r * MP + c) = w0r[k];
+    }
+    g_write_a(L, oA, w, lane);
+    lds_barrier();
+    g_rows_store(a, slice, split, oC, L, w, lane);
+}
 // Reducer `split`: sum its R entries over the S splits (split order), form
 // W1 = W0 - eta (2/N) G and store them as bf16 fragments (w1_frag_index).
-template <int S>
+template <int S, int NT>
 __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h) {
     constexpr int R = 4096 / S, n4 = R / 4;
     const int tid = threadIdx.x;
@@ -833,7 +861,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
     const float* W0h = a.W0 + (long long)h * 4096;
     bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
 #pragma unroll
-    for (int t4 = tid; t4 < n4; t4 += kThreads) {
+    for (int t4 = tid; t4 < n4; t4 += NT) {
         f32x4 v[S];
 #pragma unroll
         for (int sp = 0; sp < S; ++sp) v[sp] = blk[sp * n4 + t4];
@@ -926,10 +954,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     if constexpr (BF) {
         v4f oC[4], oA[4];
         switch (w) {
-        case 0: gram_owned_bf<0>(Ks, Vs, T, lane, oC, oA); break;
-        case 1: gram_owned_bf<1>(Ks, Vs, T, lane, oC, oA); break;
-        case 2: gram_owned_bf<2>(Ks, Vs, T, lane, oC, oA); break;
-        default: gram_owned_bf<3>(Ks, Vs, T, lane, oC, oA); break;
+        case 0: gram_owned_bf<0>(Ks, Vs, 0, (T + 31) & ~31, lane, oC, oA); break;
+        case 1: gram_owned_bf<1>(Ks, Vs, 0, (T + 31) & ~31, lane, oC, oA); break;
+        case 2: gram_owned_bf<2>(Ks, Vs, 0, (T + 31) & ~31, lane, oC, oA); break;
+        default: gram_owned_bf<3>(Ks, Vs, 0, (T + 31) & ~31, lane, oC, oA); break;
         }
         if (gx) {
             publish_g(a, c.slice, c.split, oC, oA, w0r, lds, w, lane);
@@ -959,11 +987,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         unsigned* cnt = counter_at(a.cnt, c.slice);
         slice_barrier(cnt, (unsigned)a.S);
         switch (a.S) {
-        case 2: reduce_g<2>(a, c.slice, c.split, c.h); break;
-        case 4: reduce_g<4>(a, c.slice, c.split, c.h); break;
-        case 8: reduce_g<8>(a, c.slice, c.split, c.h); break;
-        case 16: reduce_g<16>(a, c.slice, c.split, c.h); break;
-        default: reduce_g<32>(a, c.slice, c.split, c.h); break;
+        case 2: reduce_g<2, kThreads>(a, c.slice, c.split, c.h); break;
+        case 4: reduce_g<4, kThreads>(a, c.slice, c.split, c.h); break;
+        case 8: reduce_g<8, kThreads>(a, c.slice, c.split, c.h); break;
+        case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
+        default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
         }
         slice_barrier(cnt, 2u * a.S);
         keep_alive(pf);
@@ -1011,6 +1039,140 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         release_end(a, c.slice, rel);
     }
 }
+
+// ------------------------------------- resident kernel, G exchange --
+// The bf16 XCD-local case without saved A and G (the common one) with 8
+// waves, two per SIMD, so one wave's LDS reads overlap the other's matrix
+// products.  Waves 0-3 accumulate C_s, waves 4-7 A_s (rows 16 (w % 4)..
+// each); the first four form and publish G_s, and all eight share the
+// apply.
+constexpr int kThreads8 = 512;
+
+__global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch a) {
+    using Cfg = LinCfg<true>;
+    constexpr int RS = Cfg::row_slots;
+    constexpr int TB = Cfg::tmax * RS * 16;
+    constexpr int SPARE = 16384;
+    __shared__ __attribute__((aligned(16))) char lds[3 * TB + SPARE];
+    char* Ks = lds;
+    char* Vs = lds + TB;
+    char* Qs = lds + 2 * TB + SPARE;
+
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index 0..7, uniform
+    const SliceCtx c = slice_ctx<true, true>(a);
+    if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    const int T = c.t1 - c.t0;
+
+    // ---- loads: W0 (floats 4 tid + 2048 k) and all of K and V now; Q is
+    // loaded by waves 4-7 after the Gram, while the exchange leaves HBM idle
+    f32x4 w0r[2];
+    {
+        const float* W0h = a.W0 + (long long)c.h * 4096;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) w0r[k] = *reinterpret_cast<const f32x4*>(W0h + 4 * tid + 2048 * k);
+    }
+    const int rows = (T + 31) & ~31;
+    const int ninstr = rows * RS / 64; // 1 KB per wave instruction
+    for (int q = w; q < ninstr; q += 8) {
+        const int p = q * 64 + lane;
+        const int row = p / RS;
+        const int okv = ((p % RS) ^ swz_tr(row)) * 16;
+        const long long tok = c.t0 + min(row, T - 1);
+        dma16(c.Kp + tok * c.Ksn + okv, Ks + q * 1024);
+        dma16(c.Vp + tok * c.Vsn + okv, Vs + q * 1024);
+    }
+    drain_vmem(); // this wave's K, V (and W0) loads have landed
+    // W0 counts as arrived from here on: no later wait for it (which would
+    // also wait for the Q loads issued after the Gram)
+    asm volatile("" ::"v"(w0r[0]), "v"(w0r[1]));
+    __syncthreads(); // ... and every wave's loads have landed
+    Prefetch pf{0.f, 0.f};
+    if (w < 4) pf = exchange_prefetch<true, true>(a, c.slice, c.split, true);
+    for (int e = tid; e < (rows - T) * RS; e += kThreads8) { // zero the clamped rows
+        const int off = (T + e / RS) * RS * 16 + (e % RS) * 16;
+        *reinterpret_cast<u32x4*>(Ks + off) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(Vs + off) = u32x4{0u, 0u, 0u, 0u};
+    }
+    lds_barrier();
+
+    // ---- phase 1: waves 0-3 accumulate rows 16 w.. of C, waves 4-7 rows
+    // 16 (w - 4).. of A, each over all of the split's tokens
+    const int W = w & 3;
+    v4f oC[4], oA[4];
+    switch (w) {
+    case 0: gram_owned_bf<0, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 1: gram_owned_bf<1, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 2: gram_owned_bf<2, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 3: gram_owned_bf<3, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 4: gram_owned_bf<0, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 5: gram_owned_bf<1, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 6: gram_owned_bf<2, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    default: gram_owned_bf<3, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    }
+    // A's owners write its planes, W0 is staged, then the C owners form
+    // and publish their rows of G_s
+    const GLds L = g_lds(lds);
+    lds_barrier(); // every Gram is done with K and V
+    if (w >= 4) g_write_a(L, oA, W, lane);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int e = 4 * tid + 2048 * k, r = e >> 6, cc = e & 63;
+        *reinterpret_cast<f32x4*>(L.w0s + r * MP + cc) = w0r[k];
+    }
+    lds_barrier();
+    if (w < 4) {
+        g_rows_store(a, c.slice, c.split, oC, L, w, lane);
+    } else if (a.Z.ptr) {
+        // Q, by the waves that do not publish or reduce (their loads stay
+        // in flight across the slice barriers)
+        for (int q = w - 4; q < ninstr; q += 4) {
+            const int p = q * 64 + lane;
+            const int row = p / RS;
+            const int oq = ((p % RS) ^ swz_q<true>(row)) * 16;
+            const long long tok = c.t0 + min(row, T - 1);
+            dma16(c.Qp + tok * c.Qsn + oq, Qs + q * 1024);
+        }
+    }
+
+    // ---- phase 2: reduce this workgroup's block of G, W1 as bf16 fragments
+    unsigned* cnt = counter_at(a.cnt, c.slice);
+    slice_barrier(cnt, (unsigned)a.S, w < 4);
+    // waves 0-3 reduce (waves 4-7 have Q loads in flight, which a gather of
+    // theirs would queue behind)
+    if (w < 4) {
+        switch (a.S) {
+        case 2: reduce_g<2, kThreads>(a, c.slice, c.split, c.h); break;
+        case 4: reduce_g<4, kThreads>(a, c.slice, c.split, c.h); break;
+        case 8: reduce_g<8, kThreads>(a, c.slice, c.split, c.h); break;
+        case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
+        default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
+        }
+    }
+    slice_barrier(cnt, 2u * a.S, w < 4);
+    keep_alive(pf);
+    drain_vmem();    // this wave's Q loads have landed
+    __syncthreads(); // ... and every wave's
+
+    // ---- phase 3: Z from the resident Q region
+    if (!a.Z.ptr) {
+        release_end(a, c.slice, release_begin(a, c.slice));
+        return;
+    }
+    const int nsteps = (T + 15) / 16;
+    const W1FragsBF wf = w1_frags_bf_packed(a.w1 + (long long)c.slice * 4096, lane);
+    const unsigned rel = release_begin(a, c.slice);
+    for (int step = w; step < nsteps; step += 8) {
+        const int row = step * 16 + m;
+        u32x4 q[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 8 + ((4 * hh + g) ^ swz_q<true>(row))) * 16);
+        apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+    }
+    release_end(a, c.slice, rel);
+}
+static_assert(4 * 64 * kAP + 64 * MP * 4 <= 2 * LinCfg<true>::tmax * 8 * 16, "G-phase LDS inside the K/V regions");
 
 // resident kernel, floats below the Q region: wave sums + [A; C] (phase 1),
 // gather staging / W0 / W1 (phase 2)
@@ -1184,10 +1346,10 @@ int pow2_floor(long long s) {
     return p;
 }
 
-int occupancy(const void* fn, std::atomic<int>& cache) {
+int occupancy(const void* fn, std::atomic<int>& cache, int threads = kThreads) {
     int n = cache.load(std::memory_order_relaxed);
     if (n > 0) return n;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, kThreads, 0) != hipSuccess || n < 0) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, 0) != hipSuccess || n < 0) return 0;
     cache.store(n, std::memory_order_relaxed);
     return n;
 }
@@ -1217,12 +1379,16 @@ size_t lin_fwd_ws_bytes(int B, int H, int N) {
 }
 
 int lin_fwd_resident_per_cu(int bf16) {
-    static std::atomic<int> cache[4];
+    static std::atomic<int> cache[5];
     // the kernels of both exchange protocols have the same LDS footprint
-    const int r = bf16 ? occupancy((const void*)lin_fwd_resident<true, true>, cache[0])
-                       : occupancy((const void*)lin_fwd_resident<false, true>, cache[1]);
+    int r = bf16 ? occupancy((const void*)lin_fwd_resident<true, true>, cache[0])
+                 : occupancy((const void*)lin_fwd_resident<false, true>, cache[1]);
     const int s = bf16 ? occupancy((const void*)lin_fwd_stream<true, true>, cache[2])
                        : occupancy((const void*)lin_fwd_stream<false, true>, cache[3]);
+    if (bf16) {
+        const int x = occupancy((const void*)lin_fwd_resident_gx, cache[4], kThreads8);
+        r = r < x ? r : x;
+    }
     return r < s ? r : s;
 }
 
@@ -1234,10 +1400,14 @@ bool lin_fwd_is_resident(int N, int S, int bf16) {
 hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     const long long slices = (long long)a.B * a.H;
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
-    const dim3 grid((unsigned)(gslices * a.S)), block(kThreads);
+    const dim3 grid((unsigned)(gslices * a.S));
+    dim3 block(kThreads);
     void* args[] = {&a};
     const void* fn;
-    if (resident) {
+    if (resident && a.xcd && a.bf16 && a.S > 1 && !a.saved) {
+        fn = (const void*)lin_fwd_resident_gx;
+        block = dim3(kThreads8);
+    } else if (resident) {
         if (a.xcd) fn = a.bf16 ? (const void*)lin_fwd_resident<true, true> : (const void*)lin_fwd_resident<false, true>;
         else fn = a.bf16 ? (const void*)lin_fwd_resident<true, false> : (const void*)lin_fwd_resident<false, false>;
     } else {
