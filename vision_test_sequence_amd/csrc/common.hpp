@@ -144,6 +144,30 @@ __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned to
     }
 }
 
+// ------------------------------------------------- direct-to-LDS load --
+// Direct global->LDS 16-byte load per lane (lane l writes 16 bytes at
+// lds_off + 16 l), written as inline assembly: the compiler neither sees it
+// nor makes later LDS reads wait for it, so the kernel waits for exactly
+// the loads it needs with vmcnt_at_most().  lds_off must be wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
+    const uint32_t off = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)lds_dst);
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(off)
+                 : "memory", "m0");
+}
+// Wait until at most n of this wave's vector-memory operations are
+// outstanding (they complete in issue order).  n above 15 waits for all.
+__device__ __forceinline__ void vmcnt_at_most(int n) {
+    switch (n) {
+#define TTT_VMCNT(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+        TTT_VMCNT(1) TTT_VMCNT(2) TTT_VMCNT(3) TTT_VMCNT(4) TTT_VMCNT(5) TTT_VMCNT(6) TTT_VMCNT(7)
+        TTT_VMCNT(8) TTT_VMCNT(9) TTT_VMCNT(10) TTT_VMCNT(11) TTT_VMCNT(12) TTT_VMCNT(13) TTT_VMCNT(14)
+        TTT_VMCNT(15)
+#undef TTT_VMCNT
+    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    }
+}
+
 // --------------------------------------------------- slice mapping ------
 // Workgroup i runs on XCD i % 8 on MI355X (8 XCDs, round-robin dispatch).
 // XCD-aware mapping: slice s lives on XCD s % 8 and its S workgroups are
