@@ -38,7 +38,7 @@ NSETS = 5
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # HBM bytes per launch of the linear kernel from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE runs, stored with the hash of the sources they were taken on
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lin_fwd_resident_vit3t_1248_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lin_fwd_resident_gx_vit3t_1248_traffic.md")
 LIN_SOURCES = ["vision_test_sequence_amd/csrc/linear_fullbatch.hip",
                "vision_test_sequence_amd/csrc/common.hpp",
                "vision_test_sequence_amd/csrc/api.cpp"]
@@ -251,7 +251,7 @@ def main():
             "input_sets_rotated": NSETS,
         },
         "roofline": {
-            "kernel": "lin_fwd_resident (ttt_linear_fullbatch, heads 0-1, B=8, N=6084)",
+            "kernel": "lin_fwd_resident_gx (ttt_linear_fullbatch, heads 0-1, B=8, N=6084)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
