@@ -20,9 +20,8 @@
 //            accumulates its lane's 9 tap sums; the 4 waves are summed in a
 //            fixed order;
 //   phase 2  with S > 1 workgroups per slice the 64 x 9 partials meet in the
-//            workspace (per-slice barrier), each workgroup reduces a few
-//            channels over the S partials in order and writes those w1
-//            rows, a second barrier, every workgroup reads w1;
+//            workspace (one per-slice barrier) and every workgroup sums all
+//            S of them in split order into w1 (so all form the same w1);
 //   phase 3  the same sliding window over Q with w1 writes Z.
 #include "common.hpp"
 #include "internal.hpp"
@@ -44,7 +43,6 @@ struct ConvArgs {
     const float* eta;
     float* saved;
     float* part;       // [slices][S][64][9]
-    float* w1;         // [slices][64][9]
     unsigned* cnt;     // [slices]
     int H, gh, gw;
     int R, TW;         // tile rows / columns
@@ -125,7 +123,7 @@ __device__ __forceinline__ void zero_outside(char* blk, int ya, int xa, int rows
 
 // One workgroup per CU (its LDS) of 8 waves, two per SIMD: while one
 // waits for its LDS reads the other computes.
-template <bool BF>
+template <bool BF, bool XC>
 __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     using T = ConvT<BF>;
     constexpr int pb = 64 * T::esz; // bytes per pixel
@@ -135,10 +133,10 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const SliceSplit ss = map_block(blockIdx.x, a.S, a.xcd);
+    const SliceSplit ss = map_block(blockIdx.x, a.S, XC);
     const int slice = ss.slice, split = ss.split;
     if (slice >= a.slices) return; // padding block of the XCD-aware grid
-    const bool poison = a.xcd && ((xcc_id() & 7) != (blockIdx.x & 7));
+    const bool poison = XC && ((xcc_id() & 7) != (blockIdx.x & 7));
     const int b = slice / a.H, h = slice % a.H;
     const int gh = a.gh, gw = a.gw, N = gh * gw;
     const int ntile = a.ny * a.nx;
@@ -259,57 +257,51 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             const int c = e / 9, t = e % 9;
             const float v = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) +
                             red[(192 + c) * 9 + t];
-            if (a.xcd) P[e] = v;
+            if constexpr (XC) P[e] = v;
             else xstore(P + e, v);
         }
         slice_barrier(cnt, (unsigned)a.S);
-        // Gather elements [e0, e1) of all S partials with every load in
-        // flight at once (the wave-sum buffer is free now), then sum each
-        // element over the splits in split order.
-        const int e0 = (576 * split) / a.S, e1 = (576 * (split + 1)) / a.S, ne = e1 - e0;
-        const int tot = ne * a.S; // <= 576 + S <= kRedFloats
-        const float* P0 = a.part + (long long)slice * a.S * 576;
-        for (int base = 0; base < tot; base += 4 * kCT) {
-            float v[4];
+        // Every workgroup sums all S partials itself (576 floats each, in
+        // split order, so all of them form the same w1): one barrier, and
+        // no second round trip for w1.  Thread t < 144 owns elements
+        // 4t..4t+3, all S loads in flight (S <= 32: the grid holds at most
+        // 256 workgroups of >= 8 slices).
+        if (tid < 144) {
+            const float* src = a.part + (long long)slice * a.S * 576 + 4 * tid;
+            // loads in chunks of 8 splits, one uniform branch per chunk
+            // (indices past the last split repeat it and are not added)
+            f32x4 v[32];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                if (8 * ch < a.S) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const float* q = src + min(8 * ch + k, a.S - 1) * 576;
+                        if constexpr (XC) v[8 * ch + k] = *reinterpret_cast<const f32x4*>(q);
+                        else v[8 * ch + k] = f32x4{xload(q), xload(q + 1), xload(q + 2), xload(q + 3)};
+                    }
+                }
+            }
+            f32x4 acc = v[0];
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) {
+                if (8 * ch < a.S) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) {
+                        const int sp = 8 * ch + k;
+                        if (sp > 0 && sp < a.S) acc += v[sp];
+                    }
+                }
+            }
+            const float* w0e = a.w0 + (long long)h * 576 + 4 * tid;
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const int f = base + k * kCT + tid;
-                const float* src = P0 + (long long)(f / ne) * 576 + e0 + f % ne;
-                v[k] = f < tot ? (a.xcd ? *src : xload(src)) : 0.f;
-            }
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int f = base + k * kCT + tid;
-                if (f < tot) red[f] = v[k];
+                const float gv = scale * acc[k];
+                w1s[4 * tid + k] = w0e[k] - eta * gv;
+                if (a.saved && split == 0) a.saved[(long long)slice * 576 + 4 * tid + k] = gv;
             }
         }
-        __syncthreads();
-        float* w1g = a.w1 + (long long)slice * 576;
-        for (int i = tid; i < ne; i += kCT) {
-            float sacc = 0.f;
-            for (int sp = 0; sp < a.S; ++sp) sacc += red[sp * ne + i];
-            const int e = e0 + i;
-            const float gv = scale * sacc;
-            const float w1v = a.w0[(long long)h * 576 + e] - eta * gv;
-            if (a.xcd) w1g[e] = w1v;
-            else xstore(w1g + e, w1v);
-            if (a.saved) a.saved[(long long)slice * 576 + e] = gv;
-        }
-        slice_barrier(cnt, 2u * a.S);
-        {
-            float v[2];
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int e = k * kCT + tid;
-                v[k] = e < 576 ? (a.xcd ? w1g[e] : xload(w1g + e)) : 0.f;
-            }
-#pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int e = k * kCT + tid;
-                if (e < 576) w1s[e] = v[k];
-            }
-        }
-        slice_barrier_release(cnt, 3u * a.S);
+        slice_barrier_release(cnt, 2u * a.S);
         __syncthreads();
     }
     float wq[9];
@@ -406,15 +398,15 @@ size_t conv_ws_bytes(int B, int H, int gh, int gw) {
     const ConvPlan q = plan_conv((int)slices, gh, gw, 4, 256);
     const int S = p.S > q.S ? p.S : q.S;
     if (S <= 1) return 0;
-    return kCounterBytes + (size_t)slices * S * 576 * 4 + (size_t)slices * 576 * 4;
+    return kCounterBytes + (size_t)slices * S * 576 * 4;
 }
 
 int conv_resident_per_cu(int bf16) {
     static std::atomic<int> cached[2];
     int n = cached[bf16 ? 1 : 0].load(std::memory_order_relaxed);
     if (n > 0) return n;
-    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<true>, kCT, 0)
-                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<false>, kCT, 0);
+    hipError_t e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<true, true>, kCT, 0)
+                        : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, conv_kernel<false, true>, kCT, 0);
     if (e != hipSuccess || n < 0) return 0;
     cached[bf16 ? 1 : 0].store(n, std::memory_order_relaxed);
     return n;
@@ -433,20 +425,17 @@ hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
     a.slices = (int)slices;
     a.xcd = (p.S > 1 && l.xcd_ok) ? 1 : 0;
     if (p.S > 1) {
-        // workspace layout as conv_ws_bytes: fixed counter block, partials, w1
-        const ConvPlan p2 = plan_conv((int)slices, l.gh, l.gw, 2, 256);
-        const ConvPlan p4 = plan_conv((int)slices, l.gh, l.gw, 4, 256);
-        const int Smax = p2.S > p4.S ? p2.S : p4.S;
+        // workspace layout as conv_ws_bytes: fixed counter block, partials
         if (slices > kMaxBarrierSlices) return hipErrorInvalidValue; // unreachable: S > 1
         char* base = (char*)l.ws;
         a.cnt = (unsigned*)base;
         a.part = (float*)(base + kCounterBytes);
-        a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 576 * 4);
     }
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
     const dim3 grid((unsigned)(gslices * p.S)), block(kCT);
     void* args[] = {&a};
-    const void* fn = l.bf16 ? (const void*)conv_kernel<true> : (const void*)conv_kernel<false>;
+    const void* fn = a.xcd ? (l.bf16 ? (const void*)conv_kernel<true, true> : (const void*)conv_kernel<false, true>)
+                           : (l.bf16 ? (const void*)conv_kernel<true, false> : (const void*)conv_kernel<false, false>);
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
 }
 
