@@ -325,15 +325,41 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     const float* A = a.saved + (long long)slice * 8192;
     const float* G = A + 4096;
     const float* part = a.part + (long long)slice * a.S * 4096;
+    // thread t owns float4s t + 256 k (k < 4); every load of a chunk of
+    // eight splits is in flight at once, the splits are added in order
+    const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
+    f32x4 w0v[4], av[4], gv[4], acc[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int q = tid + kThreads * k;
+        w0v[k] = reinterpret_cast<const f32x4*>(W0)[q];
+        av[k] = reinterpret_cast<const f32x4*>(A)[q];
+        gv[k] = reinterpret_cast<const f32x4*>(G)[q];
+        acc[k] = p4[q];
+    }
+    for (int s0 = 1; s0 < a.S; s0 += 8) {
+        f32x4 v[8][4];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                v[j][k] = p4[(long long)min(s0 + j, a.S - 1) * 1024 + tid + kThreads * k];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            if (s0 + j < a.S) {
+#pragma unroll
+                for (int k = 0; k < 4; ++k) acc[k] += v[j][k];
+            }
+    }
     float dsum = 0.f;
-    for (int e = tid; e < 4096; e += kThreads) {
-        float v = part[e];
-        for (int s = 1; s < a.S; ++s) v += part[(long long)s * 4096 + e];
-        const int r = e >> 6, cc = e & 63;
-        D[r * MB + cc] = v;
-        W[r * MB + cc] = W0[e];
-        Am[r * MB + cc] = A[e];
-        dsum += v * G[e];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int e = 4 * (tid + kThreads * k), r = e >> 6, cc = e & 63;
+        *reinterpret_cast<f32x4*>(D + r * MB + cc) = acc[k];
+        *reinterpret_cast<f32x4*>(W + r * MB + cc) = w0v[k];
+        *reinterpret_cast<f32x4*>(Am + r * MB + cc) = av[k];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsum += acc[k][i] * gv[k][i];
     }
     red[tid] = dsum;
     __syncthreads();
@@ -425,22 +451,31 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass2(BwdArgs a) {
     char* dVp = (char*)base_of<ESZ>(a.O1, c);
     const long long sk = a.X0.sn * ESZ, sv = a.X1.sn * ESZ, sdk = a.O0.sn * ESZ, sdv = a.O1.sn * ESZ;
 
-    // 16-token steps, wave w takes steps w, w + 4, ...
+    // 16-token steps, wave w takes steps w, w + 4, ...: four steps per
+    // round, their K and V rows loaded together (rows past the range are
+    // clamped copies, loaded unconditionally and not stored)
     const int nst = (c.t1 - c.t0 + 15) / 16;
-    for (int s = w; s < nst; s += 4) {
-        const int t = c.t0 + 16 * s + m;
-        const int tc = min(t, c.t1 - 1);
-        const Row<BF> k = load_row<BF>(Kp + tc * sk, g);
-        const Row<BF> v = load_row<BF>(Vp + tc * sv, g);
-        v4f dk[4], dv[4];
+    for (int s0 = w; s0 < nst; s0 += 16) {
+        Row<BF> k[4], v[4];
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb) dk[rb] = dv[rb] = v4f{0.f, 0.f, 0.f, 0.f};
-        mac<BF>(F1, v, dk);
-        mac<BF>(F2, k, dk);
-        mac<BF>(F3, k, dv);
-        if (t < c.t1) {
-            store_row<BF>(dKp + t * sdk, dk, g);
-            store_row<BF>(dVp + t * sdv, dv, g);
+        for (int u = 0; u < 4; ++u) {
+            const int tc = min(c.t0 + 16 * (s0 + 4 * u) + m, c.t1 - 1);
+            k[u] = load_row<BF>(Kp + tc * sk, g);
+            v[u] = load_row<BF>(Vp + tc * sv, g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            v4f dk[4], dv[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) dk[rb] = dv[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+            mac<BF>(F1, v[u], dk);
+            mac<BF>(F2, k[u], dk);
+            mac<BF>(F3, k[u], dv);
+            const int t = c.t0 + 16 * (s0 + 4 * u) + m;
+            if (t < c.t1) {
+                store_row<BF>(dKp + t * sdk, dk, g);
+                store_row<BF>(dVp + t * sdv, dv, g);
+            }
         }
     }
 }
@@ -471,15 +506,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_batch(BwdArgs a) {
     }
 }
 
-// workgroups per slice: enough workgroups for the device, at least 128
-// tokens each
+// Workgroups per slice: at least 1024 workgroups in all (several rounds
+// of the device's 512 resident slots: two per CU), each with at least 128
+// tokens; among split counts up to twice that minimum, the one whose grid
+// fills its last round of slots best (a partly filled last round costs a
+// whole round).
 int bwd_splits(int B, int H, int N) {
     const long long slices = (long long)B * H;
-    long long s = (1024 + slices - 1) / slices;
-    const long long maxs = (N + 127) / 128;
-    if (s > maxs) s = maxs;
-    if (s > 64) s = 64;
-    return (int)(s < 1 ? 1 : s);
+    constexpr long long kSlots = 512;
+    long long maxs = (N + 127) / 128;
+    if (maxs > 64) maxs = 64;
+    if (maxs < 1) maxs = 1;
+    long long s0 = (1024 + slices - 1) / slices;
+    if (s0 > maxs) s0 = maxs;
+    if (s0 < 1) s0 = 1;
+    long long best = s0;
+    double best_fill = 0.0;
+    for (long long s = s0; s <= 2 * s0 && s <= maxs; ++s) {
+        const long long wgs = slices * s;
+        const long long rounds = (wgs + kSlots - 1) / kSlots;
+        const double fill = (double)wgs / (double)(rounds * kSlots);
+        if (fill > best_fill + 1e-9) {
+            best_fill = fill;
+            best = s;
+        }
+    }
+    return (int)best;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
