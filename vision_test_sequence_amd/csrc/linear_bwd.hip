@@ -53,8 +53,11 @@ struct BwdArgs {
     float* detas;       // [slices]
     float* dW0;         // [H][64][64]
     float* deta;        // [H]
+    u32x4* fr;          // [slices][3][8][64]: bf16 fragments of beta dW1^T, -beta M, beta dW1
     int B, H, N, S, per, xcd;
+    int S2, per2;       // bf16 pass 2: splits per slice, tokens per split (<= kP2Tok)
 };
+constexpr int kP2Tok = 256; // bf16 pass 2: tokens per workgroup, resident in LDS
 
 // ------------------------------------------------------------ fragments --
 template <bool BF> struct Frags;
@@ -413,6 +416,25 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) mv[j] = W[r * MB + c0 + j] + W[(c0 + j) * MB + r];
         *reinterpret_cast<f32x4*>(dm + 4096 + r * 64 + c0) = mv;
+        *reinterpret_cast<f32x4*>(Am + r * MB + c0) = mv; // A's space is free now
+    }
+    __syncthreads();
+    // bf16 operator fragments for pass 2 (A operand of Wt[o][k] with output
+    // rows o = perm_row(rb, m)): piece (f, rb, kb, lane) holds
+    // k = 32 kb + 8 g + (0..7); f = 0: beta dW1^T, 1: -beta M, 2: beta dW1
+    if (a.fr) {
+        u32x4* fr = a.fr + (long long)slice * 1536;
+        for (int pc = tid; pc < 1536; pc += kThreads) {
+            const int f = pc >> 9, rb = (pc >> 7) & 3, kb = (pc >> 6) & 1, ln = pc & 63;
+            const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = k0 + j;
+                v[j] = f == 0 ? beta * D[k * MB + o] : (f == 1 ? -beta * Am[o * MB + k] : beta * D[o * MB + k]);
+            }
+            fr[pc] = u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+        }
     }
     // deta term: fixed-order tree over the threads' partial sums
     for (int s = kThreads / 2; s > 0; s >>= 1) {
@@ -478,6 +500,99 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass2(BwdArgs a) {
             }
         }
     }
+}
+
+// ------------------------------------------------------- pass 2 (bf16) --
+// The same products with the workgroup's K and V rows (kP2Tok tokens)
+// resident in LDS: every row is issued at once as direct-to-LDS loads, and
+// the operators come as ready bf16 fragments from the reduce.  Two
+// workgroups per CU, and the first 128 rows are processed while the rest
+// land.  Rows
+// are 128 bytes, 16-byte slots XOR-swizzled by (row / 2) % 8 so the 16
+// rows one operand read covers touch different banks.
+__global__ __launch_bounds__(kThreads, 2) void bwd_pass2_bf(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kP2Tok * 128];
+    char* Ks = lds;
+    char* Vs = lds + kP2Tok * 128;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slice = blockIdx.x / a.S2, split = blockIdx.x % a.S2;
+    if (slice >= a.B * a.H) return;
+    const int b = slice / a.H, h = slice % a.H;
+    const int t0 = min(a.N, split * a.per2), t1 = min(a.N, t0 + a.per2), T = t1 - t0;
+    const char* Kp = (const char*)a.X0.ptr + (b * a.X0.sb + h * a.X0.sh) * 2LL;
+    const char* Vp = (const char*)a.X1.ptr + (b * a.X1.sb + h * a.X1.sh) * 2LL;
+    char* dKp = (char*)a.O0.ptr + (b * a.O0.sb + h * a.O0.sh) * 2LL;
+    char* dVp = (char*)a.O1.ptr + (b * a.O1.sb + h * a.O1.sh) * 2LL;
+    const long long sk = a.X0.sn * 2, sv = a.X1.sn * 2, sdk = a.O0.sn * 2, sdv = a.O1.sn * 2;
+    auto swz = [](int row) { return (row >> 1) & 7; };
+
+    // rows: instruction q covers rows 8q .. 8q + 7 (clamped into the range);
+    // q < 16 is the first half (rows < 128)
+    const int rows = (T + 15) & ~15, ninstr = rows / 8;
+    auto issue = [&](int q_begin, int q_end) __attribute__((always_inline)) {
+        for (int q = q_begin + w; q < q_end; q += 4) {
+            const int p = q * 64 + lane, row = p >> 3;
+            const int off = ((p & 7) ^ swz(row)) * 16;
+            const long long tk = t0 + min(row, T - 1);
+            dma16(Kp + tk * sk + off, Ks + q * 1024);
+            dma16(Vp + tk * sv + off, Vs + q * 1024);
+        }
+    };
+    issue(0, min(ninstr, 16));
+    // operator fragments; the asm operand makes the compiler wait for them
+    // here (together with the first half's rows), so no wait at their use
+    // covers the second half's loads, issued next
+    const u32x4* fr = a.fr + (long long)slice * 1536 + lane;
+    v8bf F[3][4][2];
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) F[f][rb][kb] = as_v8bf(fr[(f * 8 + rb * 2 + kb) * 64]);
+    drain_vmem();
+#pragma unroll
+    for (int f = 0; f < 3; ++f)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(F[f][rb][kb]));
+    issue(16, ninstr);
+    const int nst = rows / 16;
+    auto steps = [&](int s_begin, int s_end) __attribute__((always_inline)) {
+        for (int st = s_begin + w; st < s_end; st += 4) {
+            const int row = 16 * st + m;
+            u32x4 kx[2], vx[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int off = (row * 8 + ((4 * kb + g) ^ swz(row))) * 16;
+                kx[kb] = *reinterpret_cast<const u32x4*>(Ks + off);
+                vx[kb] = *reinterpret_cast<const u32x4*>(Vs + off);
+            }
+            v4f dk[4], dv[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                dk[rb] = dv[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    dk[rb] = mfma32(F[0][rb][kb], as_v8bf(vx[kb]), dk[rb]);
+                    dk[rb] = mfma32(F[1][rb][kb], as_v8bf(kx[kb]), dk[rb]);
+                    dv[rb] = mfma32(F[2][rb][kb], as_v8bf(kx[kb]), dv[rb]);
+                }
+            }
+            const int t = t0 + row;
+            if (row < T) {
+                store_row<true>(dKp + t * sdk, dk, g);
+                store_row<true>(dVp + t * sdv, dv, g);
+            }
+        }
+    };
+    __syncthreads(); // every wave's first-half rows have landed
+    steps(0, min(nst, 8));
+    drain_vmem();
+    __syncthreads();
+    steps(8, nst);
 }
 
 // ------------------------------------------------------------ batch sums --
@@ -549,6 +664,7 @@ size_t lin_bwd_ws_bytes(int B, int H, int N) {
     bytes += align256(slices * 8192 * 4);     // dW1, M
     bytes += align256(slices * 4096 * 4);     // dW0 terms
     bytes += align256(slices * 4);            // deta terms
+    bytes += align256(slices * 1536 * 16);    // bf16 operator fragments
     return bytes;
 }
 
@@ -576,6 +692,11 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.dW0s = (float*)p;
     p += align256(slices * 4096 * 4);
     a.detas = (float*)p;
+    p += align256(slices * 4);
+    a.fr = s.bf16 ? (u32x4*)p : nullptr;
+    a.S2 = (s.N + kP2Tok - 1) / kP2Tok;
+    if (a.S2 < 1) a.S2 = 1;
+    a.per2 = (((s.N + a.S2 - 1) / a.S2) + 15) & ~15; // <= kP2Tok
 
     const long long padded = ((long long)slices + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * a.S)), block(kThreads);
@@ -584,7 +705,7 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     else hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
     hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
     a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
-    if (s.bf16) hipLaunchKernelGGL(bwd_pass2<true>, grid, block, 0, stream, a);
+    if (s.bf16) hipLaunchKernelGGL(bwd_pass2_bf, dim3((unsigned)(slices * a.S2)), block, 0, stream, a);
     else hipLaunchKernelGGL(bwd_pass2<false>, grid, block, 0, stream, a);
     hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H * 16), block, 0, stream, a);
     return hipGetLastError();
