@@ -168,6 +168,78 @@ __device__ __forceinline__ void vmcnt_at_most(int n) {
     }
 }
 
+// ------------------------------------------ transposing LDS reads --
+// Staged bf16 token rows (128 bytes) read with transposing loads:
+// one half-wave of such a read covers rows 8g + e, 8(g+1) + e (e = 0..3,
+// g even), 32 bytes each; the swizzle gives the four rows of each parity
+// four different slot pairs, so the half-wave touches every LDS bank once.
+__device__ __forceinline__ int swz_tr(int row) { return 2 * ((row >> 1) & 1) + 4 * ((row >> 3) & 1); }
+
+// ------------------------------------------- Gram by tile ownership (bf16) --
+// Wave w accumulates rows 16w..16w+15 of C = V^T K and of A = K^T K over
+// every token of the split (16 + 16 tiles of which it owns 4 + 4), so the
+// four waves never add partial sums.  Token-contracted operands come from
+// the staged rows with ds_read_b64_tr_b16: in each 16-lane group, lane
+// 4e + a points at token 8g + e (second read: + 4), channels 16 blk + 4a,
+// and lane m of the group receives channel 16 blk + m of those four tokens,
+// which is the MFMA operand layout (k = token).  Rows are XOR-swizzled by
+// swz_tr (the same for the two reads of a pair).
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s;
+
+__device__ __forceinline__ int tr_off(int lane, int blk) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, aa = lane & 3;
+    return (8 * g + e) * 128 + (((2 * blk + (aa >> 1)) ^ swz_tr(8 * g + e)) << 4) + (aa & 1) * 8;
+}
+__device__ __forceinline__ v8bf tr_pair(const char* p) {
+    const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * 128));
+    return __builtin_bit_cast(v8bf, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+// K, V: staged bf16 rows (128 bytes, swz_tr), rows past the data zeroed up
+// to a multiple of 32.  Adds rows [r0, r1) (multiples of 32) of the
+// products to rows 16W.. of C and A in accC / accA: lane (g, m) holds
+// [16W + 4g + i][16cb + m].  W is the wave's block (compile time, so its
+// own K block is one of the four it reads); DC / DA select the C and A
+// parts.
+template <int W, bool DC = true, bool DA = true>
+__device__ __forceinline__ void gram_owned_bf(const char* Ks, const char* Vs, int r0, int r1, int lane, v4f* accC,
+                                              v4f* accA) {
+    int off[4];
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) off[blk] = tr_off(lane, blk);
+    if (r1 <= r0) return;
+    // two operand sets in turn: the reads of one 32-token step are in
+    // flight while the products of the previous one run (a re-read of the
+    // last step of the range is in bounds and unused)
+    struct Ops {
+        v8bf k[4], vown;
+    };
+    auto fetch = [&](int r0, Ops& o) __attribute__((always_inline)) {
+        const char* kp = Ks + r0 * 128;
+#pragma unroll
+        for (int blk = 0; blk < 4; ++blk) o.k[blk] = tr_pair(kp + off[blk]);
+        if constexpr (DC) o.vown = tr_pair(Vs + r0 * 128 + off[W]);
+    };
+    auto products = [&](const Ops& o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            if constexpr (DC) accC[cb] = mfma32(o.vown, o.k[cb], accC[cb]);
+            if constexpr (DA) accA[cb] = mfma32(o.k[W], o.k[cb], accA[cb]);
+        }
+    };
+    Ops A, B;
+    fetch(r0, A);
+    int r = r0;
+    for (; r + 64 <= r1; r += 64) {
+        fetch(r + 32, B);
+        products(A);
+        fetch(min(r + 64, r1 - 32), A);
+        products(B);
+    }
+    if (r < r1) products(A);
+}
+
 // --------------------------------------------------- slice mapping ------
 // Workgroup i runs on XCD i % 8 on MI355X (8 XCDs, round-robin dispatch).
 // XCD-aware mapping: slice s lives on XCD s % 8 and its S workgroups are

@@ -31,6 +31,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <algorithm>
+
 namespace ttt {
 namespace {
 
@@ -38,8 +40,6 @@ constexpr int MB = 68;     // pitch (floats) of 64x64 fp32 matrices in LDS
 constexpr int kRowB = 72;  // pitch (bf16) of a staged bf16 token row (144 bytes)
 constexpr int kRowF = 68;  // pitch (floats) of a staged fp32 token row (272 bytes)
 
-typedef short v4s_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4s_t lds_v4s;
 
 struct BwdArgs {
     View4 X0, X1;     // pass 1: dZ, Q.   pass 2: K, V
@@ -54,10 +54,12 @@ struct BwdArgs {
     float* dW0;         // [H][64][64]
     float* deta;        // [H]
     u32x4* fr;          // [slices][3][8][64]: bf16 fragments of beta dW1^T, -beta M, beta dW1
+    u32x4* w1f;         // [slices][8][64]: bf16 fragments of W1^T (bf16 pass 1)
     int B, H, N, S, per, xcd;
     int S2, per2;       // bf16 pass 2: splits per slice, tokens per split (<= kP2Tok)
 };
 constexpr int kP2Tok = 256; // bf16 pass 2: tokens per workgroup, resident in LDS
+constexpr int kP1Tok = 512; // bf16 pass 1: tokens per workgroup, resident in LDS
 
 // ------------------------------------------------------------ fragments --
 template <bool BF> struct Frags;
@@ -310,6 +312,135 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass1(BwdArgs a) {
 #pragma unroll 4
     for (int e = tid; e < 4096; e += kThreads)
         dst[e] = ((ldsf[e] + ldsf[4096 + e]) + ldsf[8192 + e]) + ldsf[12288 + e];
+}
+
+// ------------------------------------------------------ pass 1 (bf16) --
+// W1^T as bf16 A-operand fragments per slice (W1 = W0 - eta G from the
+// saved G): piece (rb, kb, lane) holds W1[k][o], o = perm_row(rb, m),
+// k = 32 kb + 8 g + (0..7).
+__global__ __launch_bounds__(kThreads, 1) void bwd_prep(BwdArgs a) {
+    const int slice = blockIdx.x, h = slice % a.H;
+    const float eta = a.eta[h];
+    const float* W0 = a.W0 + (long long)h * 4096;
+    const float* G = a.saved + (long long)slice * 8192 + 4096;
+    for (int pc = threadIdx.x; pc < 512; pc += kThreads) {
+        const int rb = pc >> 7, kb = (pc >> 6) & 1, ln = pc & 63;
+        const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = W0[(k0 + j) * 64 + o] - eta * G[(k0 + j) * 64 + o];
+        a.w1f[(long long)slice * 512 + pc] =
+            u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+    }
+}
+
+// dQ = dZ W1 and the split's dW1 = dZ^T Q with the split's dZ and Q rows
+// (kP1Tok tokens) resident in LDS, staged by direct-to-LDS loads with the
+// swz_tr swizzle; the first half is processed while the second lands.
+// dW1 by row ownership: wave w accumulates rows 16w.. over every token (dZ
+// block w against all Q blocks, transposed reads), so the waves add
+// nothing up; each stores its rows of the split's share.
+__global__ __launch_bounds__(kThreads, 1) void bwd_pass1_bf(BwdArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[2 * kP1Tok * 128];
+    char* Zs = lds;
+    char* Qs = lds + kP1Tok * 128;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int slice = blockIdx.x / a.S, split = blockIdx.x % a.S;
+    if (slice >= a.B * a.H) return;
+    const int b = slice / a.H, h = slice % a.H;
+    const int t0 = min(a.N, split * a.per), t1 = min(a.N, t0 + a.per), T = t1 - t0;
+    const char* Zp = (const char*)a.X0.ptr + (b * a.X0.sb + h * a.X0.sh) * 2LL;
+    const char* Qp = (const char*)a.X1.ptr + (b * a.X1.sb + h * a.X1.sh) * 2LL;
+    char* dQp = (char*)a.O0.ptr + (b * a.O0.sb + h * a.O0.sh) * 2LL;
+    const long long sz = a.X0.sn * 2, sq = a.X1.sn * 2, so = a.O0.sn * 2;
+
+    const int rows = (T + 31) & ~31, ninstr = rows / 8;
+    auto issue = [&](int q_begin, int q_end) __attribute__((always_inline)) {
+        for (int q = q_begin + w; q < q_end; q += 4) {
+            const int p = q * 64 + lane, row = p >> 3;
+            const int off = ((p & 7) ^ swz_tr(row)) * 16;
+            const long long tk = t0 + min(row, T - 1);
+            dma16(Zp + tk * sz + off, Zs + q * 1024);
+            dma16(Qp + tk * sq + off, Qs + q * 1024);
+        }
+    };
+    const int half = min(ninstr, kP1Tok / 16); // rows < kP1Tok / 2
+    issue(0, half);
+    // W1^T fragments; the asm operand puts the compiler's wait for them
+    // here (it covers the first half's rows too), not at their first use
+    const u32x4* wf = a.w1f + (long long)slice * 512 + lane;
+    v8bf F[4][2];
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) F[rb][kb] = as_v8bf(wf[(rb * 2 + kb) * 64]);
+    drain_vmem();
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(F[rb][kb]));
+    issue(half, ninstr);
+
+    v4f acc[4], unused[4];
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) acc[cb] = unused[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    // rows [r0, r1): dQ of its 16-token steps (wave w: steps = w mod 4),
+    // then dW1 rows 16w.. over the rows
+    auto process = [&](int r0, int r1) __attribute__((always_inline)) {
+        for (int st = r0 / 16 + w; st < r1 / 16; st += 4) {
+            const int row = 16 * st + m;
+            u32x4 zx[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                zx[kb] = *reinterpret_cast<const u32x4*>(Zs + (row * 8 + ((4 * kb + g) ^ swz_tr(row))) * 16);
+            v4f d[4];
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) d[rb] = mfma32(F[rb][kb], as_v8bf(zx[kb]), d[rb]);
+            }
+            if (row < T) store_row<true>(dQp + (t0 + row) * so, d, g);
+        }
+        switch (w) {
+        case 0: gram_owned_bf<0, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+        case 1: gram_owned_bf<1, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+        case 2: gram_owned_bf<2, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+        default: gram_owned_bf<3, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+        }
+    };
+    // rows past T hold clamped copies: zeroed (after their loads) so the
+    // Gram adds nothing for them
+    auto zero_tail = [&]() __attribute__((always_inline)) {
+        for (int e = tid; e < (rows - T) * 8; e += kThreads) {
+            const int off = (T + (e >> 3)) * 128 + (e & 7) * 16;
+            *reinterpret_cast<u32x4*>(Zs + off) = u32x4{0u, 0u, 0u, 0u};
+            *reinterpret_cast<u32x4*>(Qs + off) = u32x4{0u, 0u, 0u, 0u};
+        }
+    };
+    const int rh = min(rows, kP1Tok / 2);
+    __syncthreads(); // every wave's first-half rows have landed
+    if (rows == rh && T < rows) {
+        zero_tail();
+        __syncthreads();
+    }
+    process(0, rh);
+    drain_vmem();
+    __syncthreads();
+    if (rows > rh) {
+        if (T < rows) {
+            zero_tail();
+            __syncthreads();
+        }
+        process(rh, rows);
+    }
+    // this split's share of dW1, rows 16w.. (row-major)
+    float* dst = a.part + ((long long)slice * a.S + split) * 4096;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(16 * w + 4 * g + i) * 64 + 16 * cb + m] = acc[cb][i];
 }
 
 // ---------------------------------------------------------------- reduce --
@@ -649,6 +780,9 @@ int bwd_splits(int B, int H, int N) {
     return (int)best;
 }
 
+// bf16 pass 1: splits of at most kP1Tok tokens
+int bwd_splits_bf(int N) { return std::max(1, (N + kP1Tok - 1) / kP1Tok); }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 } // namespace
@@ -657,7 +791,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // [dW1 shares | dW1, M | dW0 terms | deta terms].
 size_t lin_bwd_ws_bytes(int B, int H, int N) {
     const size_t slices = (size_t)B * H;
-    const size_t S = bwd_splits(B, H, N);
+    const size_t S = std::max(bwd_splits(B, H, N), bwd_splits_bf(N));
     size_t bytes = align256(lin_fwd_ws_bytes(B, H, N));
     bytes += align256(slices * 8192 * 4);     // recomputed A, G
     bytes += align256(slices * S * 4096 * 4); // dW1 shares
@@ -665,6 +799,7 @@ size_t lin_bwd_ws_bytes(int B, int H, int N) {
     bytes += align256(slices * 4096 * 4);     // dW0 terms
     bytes += align256(slices * 4);            // deta terms
     bytes += align256(slices * 1536 * 16);    // bf16 operator fragments
+    bytes += align256(slices * 512 * 16);     // bf16 W1^T fragments
     return bytes;
 }
 
@@ -680,13 +815,15 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.dW0 = s.dW0;
     a.deta = s.deta;
     a.B = s.B; a.H = s.H; a.N = s.N;
-    a.S = bwd_splits(s.B, s.H, s.N);
+    // pass 1 splits: bf16 tokens resident in LDS (<= kP1Tok per split)
+    a.S = s.bf16 ? bwd_splits_bf(s.N) : bwd_splits(s.B, s.H, s.N);
     a.per = (((s.N + a.S - 1) / a.S) + 15) & ~15;
     a.xcd = 1;
     const size_t slices = (size_t)s.B * s.H;
+    const size_t Smax = std::max(bwd_splits(s.B, s.H, s.N), bwd_splits_bf(s.N));
     char* p = (char*)lin_bwd_saved_region(s.ws, s.B, s.H, s.N) + align256(slices * 8192 * 4);
     a.part = (float*)p;
-    p += align256(slices * a.S * 4096 * 4);
+    p += align256(slices * Smax * 4096 * 4);
     a.dm = (float*)p;
     p += align256(slices * 8192 * 4);
     a.dW0s = (float*)p;
@@ -694,6 +831,8 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.detas = (float*)p;
     p += align256(slices * 4);
     a.fr = s.bf16 ? (u32x4*)p : nullptr;
+    p += align256(slices * 1536 * 16);
+    a.w1f = s.bf16 ? (u32x4*)p : nullptr;
     a.S2 = (s.N + kP2Tok - 1) / kP2Tok;
     if (a.S2 < 1) a.S2 = 1;
     a.per2 = (((s.N + a.S2 - 1) / a.S2) + 15) & ~15; // <= kP2Tok
@@ -701,8 +840,12 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     const long long padded = ((long long)slices + 7) / 8 * 8;
     const dim3 grid((unsigned)(padded * a.S)), block(kThreads);
     a.X0 = s.dZ; a.X1 = s.Q; a.O0 = s.dQ;
-    if (s.bf16) hipLaunchKernelGGL(bwd_pass1<true>, grid, block, 0, stream, a);
-    else hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
+    if (s.bf16) {
+        hipLaunchKernelGGL(bwd_prep, dim3((unsigned)slices), block, 0, stream, a);
+        hipLaunchKernelGGL(bwd_pass1_bf, dim3((unsigned)(slices * a.S)), block, 0, stream, a);
+    } else {
+        hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
+    }
     hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
     a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
     if (s.bf16) hipLaunchKernelGGL(bwd_pass2_bf, dim3((unsigned)(slices * a.S2)), block, 0, stream, a);
