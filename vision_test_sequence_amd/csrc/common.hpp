@@ -73,7 +73,7 @@ __device__ __forceinline__ void lds_barrier() {
 // ------------------------------------------------------ slice barrier --
 // Workgroups that cooperate on one slice exchange small partial results
 // through the workspace, meeting at a per-slice counter.  Two protocols:
-//  * XCD-local: all workgroups of the slice run on one XCD (see map_block),
+//  * XCD-local: all workgroups of the slice run on one XCD (see map_block_xcc),
 //    so its L2 is their coherence point.  Data moves with ordinary 16-byte
 //    stores and loads.  A CU's L1 is not coherent with the other CUs' stores
 //    and cannot be invalidated cheaply (a workgroup-scope invalidate leaves
@@ -122,26 +122,77 @@ __device__ __forceinline__ unsigned* counter_at(unsigned* base, int slice) {
 // exchange loads behind it.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// The wait is bounded (about a second of polling): a slice whose workgroups
+// never all arrive -- co-residency broken by other work on the device, or
+// a dispatch that placed two workgroups on one split (see map_block_xcc) --
+// marks its counter line as failed instead of hanging; every later check
+// of that line (slice_check) reports it, in this call and in every later
+// call on the same workspace.
+constexpr unsigned kSpinLimit = 1u << 21;
+// The slice's placement word (see placement_note) and the failure word
+// share the counter's line.
+__device__ __forceinline__ unsigned long long* placement_at(unsigned* cnt) {
+    return reinterpret_cast<unsigned long long*>(cnt + 2);
+}
+__device__ __forceinline__ unsigned* failed_at(unsigned* cnt) { return cnt + 4; }
+
+// Outcome of the exchange for thread 0, after the slice's last waiting
+// barrier: true when the line has failed or, for an XCD-local exchange
+// (S > 0), when the splits that arrived are not exactly 0..S-1 once each.
+__device__ __forceinline__ bool slice_check(unsigned* cnt, int S) {
+    const unsigned failed = __hip_atomic_load(failed_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (S <= 0) return failed != 0;
+    const unsigned long long w = __hip_atomic_load(placement_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return failed != 0 || w != (0x5555555555555555ull >> (64 - 2 * S));
+}
+
 // A wave that made no exchange stores since the last barrier may pass
-// drain = false, keeping its loads in flight.
-__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true) {
+// drain = false, keeping its loads in flight.  With `check` (a shared
+// variable), thread 0 stores slice_check(cnt, S) there before the closing
+// workgroup barrier, so every thread can read it afterwards.
+__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true,
+                                              int* check = nullptr, int S = 0) {
     if (drain) drain_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target)
+        unsigned it = 0;
+        while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
+            if (++it == kSpinLimit) {
+                __hip_atomic_store(failed_at(cnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
             __builtin_amdgcn_s_sleep(1);
+        }
+        if (check) *check = slice_check(cnt, S) ? 1 : 0;
     }
     __syncthreads();
 }
 
+// Reset by the workgroup that completes the slice's count: counter and
+// placement word start from zero at the next call (the failure word stays).
+__device__ __forceinline__ void slice_reset(unsigned* cnt) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(placement_at(cnt), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned total) {
     __syncthreads();
     if (threadIdx.x == 0) {
         unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (old == total - 1)
-            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (old == total - 1) slice_reset(cnt);
     }
+}
+
+// ------------------------------------------------- placement check -------
+// With map_block_xcc every workgroup of a slice runs on the slice's XCD by
+// construction; what remains to check is that each split arrived exactly
+// once.  Thread 0 of each workgroup adds one to its split's 2-bit field of
+// the slice's placement word before its first barrier arrival (which
+// drains its memory operations); after the last waiting barrier the word
+// reads 0b01 in each of the S fields unless a split was missing or doubled
+// (slice_check).  S <= 32.
+__device__ __forceinline__ void placement_note(unsigned* cnt, int split) {
+    __hip_atomic_fetch_add(placement_at(cnt), 1ull << (2 * split), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ------------------------------------------------- direct-to-LDS load --
@@ -257,6 +308,20 @@ __device__ __forceinline__ int perm_row(int rb, int m) {
 struct SliceSplit {
     int slice, split;
 };
+// The same mapping for kernels whose splits exchange data through one XCD's
+// L2, with the XCD taken from the hardware instead of assumed from the
+// block index: dispatch is round-robin over the XCDs, but its starting XCD
+// can change during a process (it did after a graph replay), so block i is
+// treated as virtual block (i & ~7) | xcc -- every aligned group of eight
+// consecutive blocks still covers each XCD once.  placement_note() checks
+// the outcome.
+__device__ __forceinline__ SliceSplit map_block_xcc(int blk, int S, unsigned xcc) {
+    const int j = blk >> 3, x = (int)(xcc & 7);
+    SliceSplit r;
+    r.slice = (j / S) * 8 + x;
+    r.split = j % S;
+    return r;
+}
 __device__ __forceinline__ SliceSplit map_block(int blk, int S, int xcd_aware) {
     SliceSplit r;
     if (xcd_aware) {

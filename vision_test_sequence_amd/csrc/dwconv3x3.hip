@@ -130,13 +130,15 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kTileBytes + 3 * 1024];
     __shared__ float red[kRedFloats];
     __shared__ float w1s[64 * 9];
+    __shared__ int s_chk; // outcome of the exchange (slice_check)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const SliceSplit ss = map_block(blockIdx.x, a.S, XC);
+    const SliceSplit ss = XC ? map_block_xcc(blockIdx.x, a.S, xcc_id()) : map_block(blockIdx.x, a.S, 0);
     const int slice = ss.slice, split = ss.split;
     if (slice >= a.slices) return; // padding block of the XCD-aware grid
-    const bool poison = XC && ((xcc_id() & 7) != (blockIdx.x & 7));
+    if (XC && a.S > 1 && tid == 0) placement_note(counter_at(a.cnt, slice), split);
+    bool poison = false; // NaN output for a failed exchange
     const int b = slice / a.H, h = slice % a.H;
     const int gh = a.gh, gw = a.gw, N = gh * gw;
     const int ntile = a.ny * a.nx;
@@ -260,7 +262,8 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             if constexpr (XC) P[e] = v;
             else xstore(P + e, v);
         }
-        slice_barrier(cnt, (unsigned)a.S);
+        slice_barrier(cnt, (unsigned)a.S, true, &s_chk, XC ? a.S : 0);
+        poison = s_chk != 0;
         // Every workgroup sums all S partials itself (576 floats each, in
         // split order, so all of them form the same w1): one barrier, and
         // no second round trip for w1.  Thread t < 144 owns elements
@@ -298,7 +301,8 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             for (int k = 0; k < 4; ++k) {
                 const float gv = scale * acc[k];
                 w1s[4 * tid + k] = w0e[k] - eta * gv;
-                if (a.saved && split == 0) a.saved[(long long)slice * 576 + 4 * tid + k] = gv;
+                if (a.saved && split == 0)
+                    a.saved[(long long)slice * 576 + 4 * tid + k] = poison ? __builtin_nanf("") : gv;
             }
         }
         slice_barrier_release(cnt, 2u * a.S);

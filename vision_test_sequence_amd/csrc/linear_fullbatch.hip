@@ -261,7 +261,7 @@ __device__ __forceinline__ int w1_frag_index(int r, int c) {
 template <bool BF, bool XC>
 __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
                              float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r,
-                             bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
+                             int* chk, bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
@@ -376,8 +376,13 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
             sv[4096 + r * 64 + c] = gv;
         }
     }
-    slice_barrier(cnt, 2u * a.S);
+    slice_barrier(cnt, 2u * a.S, true, chk, XC ? a.S : 0);
     keep_alive(pf);
+    if (sv && *chk) // a failed exchange: this workgroup's columns of A and G
+        for (int e = tid; e < 64 * nc; e += kThreads) {
+            const int r = e >> lgnc, c = c0 + (e & (nc - 1));
+            sv[r * 64 + c] = sv[4096 + r * 64 + c] = __builtin_nanf("");
+        }
     // W1 is complete in the workspace at a.w1 + slice*4096 (bf16 fragments
     // for BF && XC, else row-major fp32)
     return nullptr;
@@ -392,8 +397,7 @@ __device__ __forceinline__ unsigned release_begin(const LinFwdLaunch& a, int sli
     return old;
 }
 __device__ __forceinline__ void release_end(const LinFwdLaunch& a, int slice, unsigned old) {
-    if (a.S > 1 && threadIdx.x == 0 && old == 3u * a.S - 1)
-        __hip_atomic_store(counter_at(a.cnt, slice), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (a.S > 1 && threadIdx.x == 0 && old == 3u * a.S - 1) slice_reset(counter_at(a.cnt, slice));
 }
 
 // ------------------------------------------------------------- phase 3 --
@@ -534,7 +538,6 @@ __device__ __forceinline__ void apply_f32(const W1FragsF32& w, const u32x4* q, c
 
 struct SliceCtx {
     int slice, split, b, h, t0, t1;
-    bool poison; // XCD-local exchange assumed a placement that did not hold
     const char *Kp, *Vp, *Qp;
     char* Zp;
     long long Ksn, Vsn, Qsn, Zsn;
@@ -542,7 +545,7 @@ struct SliceCtx {
 template <bool BF, bool XC> __device__ __forceinline__ SliceCtx slice_ctx(const LinFwdLaunch& a) {
     constexpr int esz = LinCfg<BF>::esz;
     SliceCtx c;
-    const SliceSplit ss = map_block(blockIdx.x, a.S, XC);
+    const SliceSplit ss = XC ? map_block_xcc(blockIdx.x, a.S, xcc_id()) : map_block(blockIdx.x, a.S, 0);
     c.slice = ss.slice;
     c.split = ss.split;
     c.b = c.slice / a.H;
@@ -558,7 +561,6 @@ template <bool BF, bool XC> __device__ __forceinline__ SliceCtx slice_ctx(const 
     c.Vsn = a.V.sn * esz;
     c.Qsn = a.Q.sn * esz;
     c.Zsn = a.Z.sn * esz;
-    c.poison = XC && ((xcc_id() & 7) != (blockIdx.x & 7));
     return c;
 }
 
@@ -667,6 +669,13 @@ __device__ __forceinline__ void split_bf(const float* v, v8bf& hi, v8bf& lo) {
     lo = as_v8bf(l);
 }
 constexpr int kAP = 72; // pitch (bf16) of the A planes
+// Byte offset in a kernel's LDS of the exchange outcome (slice_check),
+// written after the last slice barrier: above the phase-2 regions of
+// lin_update (gather staging, W0) and the G-phase regions, below the end
+// of the K/V regions and of the streaming kernel's LDS.
+constexpr int kChkByte = (8192 + 128 + 64 * MP) * 4;
+static_assert(kChkByte >= 4 * 64 * kAP + 64 * MP * 4, "exchange outcome above the G-phase regions");
+static_assert(kChkByte + 4 <= 20480 * 4, "exchange outcome inside the streaming kernel's LDS");
 // Wave w's rows of G_s from its owned rows of A_s and C_s.  The product
 // W0 A runs in bf16 with both factors split hi + lo (the lo x lo term is
 // below fp32 rounding) and fp32 accumulation.  A's planes go through LDS:
@@ -800,8 +809,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    int* const chk = reinterpret_cast<int*>(lds + kChkByte);
     const SliceCtx c = slice_ctx<BF, XC>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    if (XC && a.S > 1 && tid == 0) placement_note(counter_at(a.cnt, c.slice), c.split);
     const int T = c.t1 - c.t0;
 
     // ---- every load of the workgroup, issued up front: all of K and V,
@@ -901,11 +912,13 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
         default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
         }
-        slice_barrier(cnt, 2u * a.S);
+        slice_barrier(cnt, 2u * a.S, true, chk, a.S);
         keep_alive(pf);
     } else {
-        W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, published, pf);
+        W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, chk,
+                                published, pf);
     }
+    const bool poison = a.S > 1 && *chk != 0; // NaN output for a failed exchange
     // every wave's Q loads have landed (normally long since)
     drain_vmem();
     lds_barrier();
@@ -930,7 +943,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
                 q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 8 + ((4 * hh + g) ^ swz_q<true>(row))) * 16);
-            apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+            apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, poison);
         }
         release_end(a, c.slice, rel);
     } else {
@@ -942,7 +955,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh)
                 q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 16 + ((4 * hh + g) ^ swz_q<false>(row))) * 16);
-            apply_f32(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+            apply_f32(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, poison);
         }
         release_end(a, c.slice, rel);
     }
@@ -968,8 +981,10 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index 0..7, uniform
+    int* const chk = reinterpret_cast<int*>(lds + kChkByte);
     const SliceCtx c = slice_ctx<true, true>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    if (tid == 0) placement_note(counter_at(a.cnt, c.slice), c.split);
     const int T = c.t1 - c.t0;
 
     // ---- loads: W0 (floats 4 tid + 2048 k) and all of K and V now; Q is
@@ -1059,8 +1074,9 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
         default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
         }
     }
-    slice_barrier(cnt, 2u * a.S, w < 4);
+    slice_barrier(cnt, 2u * a.S, w < 4, chk, a.S);
     keep_alive(pf);
+    const bool poison = *chk != 0; // NaN output for a failed exchange
     drain_vmem();    // this wave's Q loads have landed
     __syncthreads(); // ... and every wave's
 
@@ -1078,7 +1094,7 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
             q[hh] = *reinterpret_cast<const u32x4*>(Qs + (row * 8 + ((4 * hh + g) ^ swz_q<true>(row))) * 16);
-        apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, c.poison);
+        apply_bf(wf, q, c.Zp + (long long)(c.t0 + row) * c.Zsn, row < T, g, poison);
     }
     release_end(a, c.slice, rel);
 }
@@ -1104,8 +1120,10 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
+    int* const chk = reinterpret_cast<int*>(ldsb + kChkByte);
     const SliceCtx c = slice_ctx<BF, XC>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
+    if (XC && a.S > 1 && tid == 0) placement_note(counter_at(a.cnt, c.slice), c.split);
     const int t0 = c.t0, t1 = c.t1;
 
     v4f accC[16], accA[10];
@@ -1203,7 +1221,8 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     float* mC = lds + 64 * MP;
     reduce_waves(accC, accA, lds, mA, mC, w, lane, g, m, true);
 
-    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r);
+    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r, chk);
+    const bool poison = a.S > 1 && *chk != 0; // NaN output for a failed exchange
     if (!a.Z.ptr) { // only A and G wanted
         release_end(a, c.slice, release_begin(a, c.slice));
         return;
@@ -1219,14 +1238,14 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
             const int tok = t0 + st * 16 + m;
-            if (st < nsteps) apply_bf(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
+            if (st < nsteps) apply_bf(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
         for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
             const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
             u32x4 q[2];
             q[0] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (8 * g) * 2);
             q[1] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (32 + 8 * g) * 2);
-            apply_bf(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
+            apply_bf(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
         release_end(a, c.slice, rel);
     } else {
@@ -1236,7 +1255,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
             const int tok = t0 + st * 16 + m;
-            if (st < nsteps) apply_f32(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
+            if (st < nsteps) apply_f32(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
         for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
             const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
@@ -1244,7 +1263,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
 #pragma unroll
             for (int hh = 0; hh < 4; ++hh)
                 q[hh] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (16 * hh + 4 * g) * 4);
-            apply_f32(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, c.poison);
+            apply_f32(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
         release_end(a, c.slice, rel);
     }
