@@ -126,7 +126,7 @@ __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)"
 // never all arrive -- co-residency broken by other work on the device, or
 // a dispatch that placed two workgroups on one split (see map_block_xcc) --
 // marks its counter line as failed instead of hanging; every later check
-// of that line (slice_check) reports it, in this call and in every later
+// of that line (slice_bad) reports it, in this call and in every later
 // call on the same workspace.
 constexpr unsigned kSpinLimit = 1u << 21;
 // The slice's placement word (see placement_note) and the failure word
@@ -136,22 +136,30 @@ __device__ __forceinline__ unsigned long long* placement_at(unsigned* cnt) {
 }
 __device__ __forceinline__ unsigned* failed_at(unsigned* cnt) { return cnt + 4; }
 
-// Outcome of the exchange for thread 0, after the slice's last waiting
-// barrier: true when the line has failed or, for an XCD-local exchange
+// Outcome of the exchange: thread 0 loads the slice's words after the
+// slice's last waiting barrier (slice_words: the loads are issued at once,
+// their values are needed only by slice_bad), and before the workgroup's
+// release (the reset clears them once every workgroup has released).
+// slice_bad is true when the line has failed or, for an XCD-local exchange
 // (S > 0), when the splits that arrived are not exactly 0..S-1 once each.
-__device__ __forceinline__ bool slice_check(unsigned* cnt, int S) {
-    const unsigned failed = __hip_atomic_load(failed_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (S <= 0) return failed != 0;
-    const unsigned long long w = __hip_atomic_load(placement_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return failed != 0 || w != (0x5555555555555555ull >> (64 - 2 * S));
+struct SliceWords {
+    unsigned long long placement;
+    unsigned failed;
+};
+__device__ __forceinline__ SliceWords slice_words(unsigned* cnt) {
+    SliceWords w;
+    w.placement = __hip_atomic_load(placement_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    w.failed = __hip_atomic_load(failed_at(cnt), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return w;
+}
+__device__ __forceinline__ bool slice_bad(const SliceWords& w, int S) {
+    if (S <= 0) return w.failed != 0;
+    return w.failed != 0 || w.placement != (0x5555555555555555ull >> (64 - 2 * S));
 }
 
 // A wave that made no exchange stores since the last barrier may pass
-// drain = false, keeping its loads in flight.  With `check` (a shared
-// variable), thread 0 stores slice_check(cnt, S) there before the closing
-// workgroup barrier, so every thread can read it afterwards.
-__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true,
-                                              int* check = nullptr, int S = 0) {
+// drain = false, keeping its loads in flight.
+__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true) {
     if (drain) drain_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -164,7 +172,6 @@ __device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bo
             }
             __builtin_amdgcn_s_sleep(1);
         }
-        if (check) *check = slice_check(cnt, S) ? 1 : 0;
     }
     __syncthreads();
 }
@@ -190,7 +197,7 @@ __device__ __forceinline__ void slice_barrier_release(unsigned* cnt, unsigned to
 // the slice's placement word before its first barrier arrival (which
 // drains its memory operations); after the last waiting barrier the word
 // reads 0b01 in each of the S fields unless a split was missing or doubled
-// (slice_check).  S <= 32.
+// (slice_bad).  S <= 32.
 __device__ __forceinline__ void placement_note(unsigned* cnt, int split) {
     __hip_atomic_fetch_add(placement_at(cnt), 1ull << (2 * split), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -207,15 +214,21 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
                  : "memory", "m0");
 }
 // Wait until at most n of this wave's vector-memory operations are
-// outstanding (they complete in issue order).  n above 15 waits for all.
+// outstanding (they complete in issue order).  n of 63 and above (the
+// counter's limit) waits for none; n <= 0 waits for all.
 __device__ __forceinline__ void vmcnt_at_most(int n) {
     switch (n) {
 #define TTT_VMCNT(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
+#define TTT_VMCNT8(k) TTT_VMCNT(k) TTT_VMCNT(k + 1) TTT_VMCNT(k + 2) TTT_VMCNT(k + 3) \
+    TTT_VMCNT(k + 4) TTT_VMCNT(k + 5) TTT_VMCNT(k + 6) TTT_VMCNT(k + 7)
         TTT_VMCNT(1) TTT_VMCNT(2) TTT_VMCNT(3) TTT_VMCNT(4) TTT_VMCNT(5) TTT_VMCNT(6) TTT_VMCNT(7)
-        TTT_VMCNT(8) TTT_VMCNT(9) TTT_VMCNT(10) TTT_VMCNT(11) TTT_VMCNT(12) TTT_VMCNT(13) TTT_VMCNT(14)
-        TTT_VMCNT(15)
+        TTT_VMCNT8(8) TTT_VMCNT8(16) TTT_VMCNT8(24) TTT_VMCNT8(32) TTT_VMCNT8(40) TTT_VMCNT8(48)
+        TTT_VMCNT(56) TTT_VMCNT(57) TTT_VMCNT(58) TTT_VMCNT(59) TTT_VMCNT(60) TTT_VMCNT(61) TTT_VMCNT(62)
+#undef TTT_VMCNT8
 #undef TTT_VMCNT
-    default: asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); break;
+    default:
+        if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        break;
     }
 }
 

@@ -15,10 +15,10 @@
 // workgroup owns one or more consecutive tiles of one slice.
 //   phase 1  the K halo tile ((R+2) x (TW+2) pixels), the V tile and (for
 //            single-tile workgroups) the Q halo tile are staged into LDS
-//            with direct global->LDS 16-byte loads; each wave slides a 3x3
-//            window along x over its row segments, forms P and R, and
-//            accumulates its lane's 9 tap sums; the 4 waves are summed in a
-//            fixed order;
+//            with direct global->LDS 16-byte loads (positions outside the
+//            grid load a zero pixel); each wave slides a 3x3 window along x
+//            over its row segments, forms P and R, and accumulates its
+//            lane's 9 tap sums; the 8 waves are summed in a fixed order;
 //   phase 2  with S > 1 workgroups per slice the 64 x 9 partials meet in the
 //            workspace (one per-slice barrier) and every workgroup sums all
 //            S of them in split order into w1 (so all form the same w1);
@@ -32,6 +32,7 @@ namespace ttt {
 namespace {
 
 constexpr int kTileBytes = 147456;           // K halo + V + Q halo regions
+constexpr int kW0Bytes = 3 * 1024;           // w0 of the head, 576 floats (3 staging instructions)
 constexpr int kCT = 512;                     // threads per workgroup: 8 waves, 2 per SIMD
 constexpr int kCW = kCT / 64;
 constexpr int kRedFloats = 4 * 64 * 9;       // tap sums of 4 waves (the 8 are paired first)
@@ -73,52 +74,51 @@ template <> struct ConvT<false> {
     __device__ static void st(char* p, float v) { __builtin_nontemporal_store(v, (float*)p); }
 };
 
-// Stage a (rows x cols) block of pixels whose top-left grid position is
-// (ya, xa) into LDS at dst (row-major, pixel-contiguous).  Positions outside
-// the grid load a clamped in-grid pixel; readers mask them to zero.
-template <bool BF>
-__device__ __forceinline__ void stage(char* dst, const char* src, long long sn, int ya, int xa,
-                                      int rows, int cols, int gh, int gw) {
-    constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
-    const int total = rows * cols * cpp;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    for (int base = w * 64; base < total; base += kCT) {
-        const int q = base + lane;
-        const int qq = q < total ? q : total - 1;
-        const int px = qq / cpp, sub = qq % cpp;
-        const int y = min(max(ya + px / cols, 0), gh - 1);
-        const int x = min(max(xa + px % cols, 0), gw - 1);
-        const char* g = src + ((long long)y * gw + x) * sn + sub * 16;
-        // a partial last instruction writes its tail lanes past `total`
-        // chunks, inside the region's slack (regions are padded by 1 KB)
-        __builtin_amdgcn_global_load_lds((const void*)g, (lds_void*)(dst + base * 16), 16, 0, 0);
-    }
+// Zero pixel: the source of every staged position outside the grid, so
+// the halo reads zero padding with no masks and no clearing pass.
+__device__ __attribute__((aligned(256))) u32x4 conv_zero_px[16];
+
+// Pixels per direct-to-LDS instruction (64 lanes x 16 bytes): LDS row
+// pitches are multiples of it, so every row is whole instructions.
+template <bool BF> constexpr int px_per_instr() { return 64 * 16 / (64 * ConvT<BF>::esz); }
+template <bool BF> __host__ __device__ constexpr int conv_pitch(int px) {
+    return (px + px_per_instr<BF>() - 1) / px_per_instr<BF>() * px_per_instr<BF>();
 }
 
-// Zero the pixels of a staged (rows x cols) halo block that lie outside the
-// grid, so the stencil loops read zero padding without masks.  Called after
-// the loads have landed.  A wave takes a row: the whole row when it lies
-// outside the grid, else only its columns left of 0 and from gw on.
+// Stage `rows` rows of `pitch` pixels whose top-left grid position is
+// (ya, xa) into LDS at dst (row-major, pixel-contiguous), as direct
+// global->LDS loads hidden from the compiler: instruction i of the block
+// (1 KB of LDS) is issued by wave i mod 8.  Positions outside the grid
+// load the zero pixel.  Returns the number of instructions this wave
+// issued; the caller waits for them with vmcnt_at_most().
 template <bool BF>
-__device__ __forceinline__ void zero_outside(char* blk, int ya, int xa, int rows, int cols, int gh, int gw) {
+__device__ __forceinline__ int stage_rows(char* dst, const char* src, long long sn, int ya, int xa,
+                                          int rows, int pitch, int gh, int gw) {
     constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
-    const int nl = xa < 0 ? -xa : 0;                        // pixels left of the grid
-    const int nr = xa + cols > gw ? xa + cols - max(gw, xa) : 0; // pixels right of it
-    const bool rows_out = ya < 0 || ya + rows > gh;
-    if (!(nl || nr || rows_out)) return;
+    const int ninstr = rows * pitch * cpp / 64;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const u32x4 z{0u, 0u, 0u, 0u};
-    for (int r = w; r < rows; r += kCW) {
-        char* row = blk + (long long)r * cols * cpp * 16;
-        const int y = ya + r;
-        if (y < 0 || y >= gh) {
-            for (int q = lane; q < cols * cpp; q += 64) *reinterpret_cast<u32x4*>(row + q * 16) = z;
-        } else {
-            for (int q = lane; q < nl * cpp; q += 64) *reinterpret_cast<u32x4*>(row + q * 16) = z;
-            char* right = row + (cols - nr) * cpp * 16;
-            for (int q = lane; q < nr * cpp; q += 64) *reinterpret_cast<u32x4*>(right + q * 16) = z;
-        }
+    const char* zero = reinterpret_cast<const char*>(conv_zero_px);
+    int n = 0;
+    for (int i = w; i < ninstr; i += kCW, ++n) {
+        const int q = i * 64 + lane;
+        const int px = q / cpp, sub = q % cpp;
+        const int y = ya + px / pitch, x = xa + px % pitch;
+        const bool in = y >= 0 && y < gh && x >= 0 && x < gw;
+        const char* g = in ? src + ((long long)y * gw + x) * sn + sub * 16 : zero + sub * 16;
+        dma16(g, dst + i * 1024);
     }
+    return n;
+}
+
+// w0 of one head (576 floats) into LDS: three instructions, by waves 0-2.
+__device__ __forceinline__ int stage_w0(char* dst, const float* w0h) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (w >= 3) return 0;
+    const int q = w * 64 + lane; // 16-byte chunk
+    const char* g = q < 144 ? reinterpret_cast<const char*>(w0h) + q * 16
+                            : reinterpret_cast<const char*>(conv_zero_px);
+    dma16(g, dst + w * 1024);
+    return 1;
 }
 
 // One workgroup per CU (its LDS) of 8 waves, two per SIMD: while one
@@ -127,10 +127,10 @@ template <bool BF, bool XC>
 __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     using T = ConvT<BF>;
     constexpr int pb = 64 * T::esz; // bytes per pixel
-    __shared__ __attribute__((aligned(16))) char lds[kTileBytes + 3 * 1024];
+    __shared__ __attribute__((aligned(16))) char lds[kW0Bytes + kTileBytes];
     __shared__ float red[kRedFloats];
     __shared__ float w1s[64 * 9];
-    __shared__ int s_chk; // outcome of the exchange (slice_check)
+    __shared__ int s_chk; // outcome of the exchange (slice_bad)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
@@ -152,79 +152,100 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     const long long Qsn = a.Q.sn * T::esz, Zsn = a.Z.sn * T::esz;
 
     // LDS rows are at least kSeg pixels wide (plus the halo), so a row
-    // segment of kSeg pixels never reads past its row; columns beyond the
-    // grid are zero (K, Q) or masked (V)
-    const int TWp = max(a.TW, kSeg), HW = TWp + 2;
-    const int khalo = (a.R + 2) * HW;
-    char* Ks = lds;
-    char* Vs = lds + khalo * pb + 1024;
-    char* Qs = Vs + a.R * TWp * pb + 1024;
+    // segment of kSeg pixels never reads past its row; pitches are whole
+    // staging instructions; positions outside the grid hold zeros (K, Q) or
+    // are masked (V)
+    const int KP = conv_pitch<BF>(max(a.TW, kSeg) + 2), VP = conv_pitch<BF>(max(a.TW, kSeg));
+    char* W0s = lds;
+    char* Ks = lds + kW0Bytes;
+    char* Vs = Ks + (a.R + 2) * KP * pb;
+    char* Qs = Vs + a.R * VP * pb;
     const bool q_early = (te - tb) == 1;
 
-    const float* w0c = a.w0 + ((long long)h * 64 + lane) * 9;
-    float wt[9];
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wt[t] = w0c[t];
     float gacc[9];
 #pragma unroll
     for (int t = 0; t < 9; ++t) gacc[t] = 0.f;
+    float wt[9];
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wt[t] = 0.f;
+    float pf = 0.f; // L2 prefetch of this workgroup's partial (see below)
+    unsigned rel = 0; // thread 0: the counter before this workgroup's release
 
     // ------------------------------------------------------------ phase 1
     for (int tile = tb; tile < te; ++tile) {
         const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
         const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
         // always the nominal tile shape, so the LDS pitches are fixed; the
-        // part of an edge tile outside the grid is masked when read
-        stage<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-        stage<BF>(Vs, Vp, Vsn, y0, x0, a.R, TWp, gh, gw);
-        if (q_early) stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-        __syncthreads(); // waits for the direct-to-LDS loads
-        zero_outside<BF>(Ks, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-        if (q_early) zero_outside<BF>(Qs, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-        __syncthreads();
+        // part of an edge tile outside the grid is zero or masked.  (The
+        // whole chip issues its loads at once and the memory system does
+        // not serve them in issue order, so staging the rows in the order
+        // they are needed and starting on the first ones measured no
+        // earlier start.)
+        if (tile == tb) stage_w0(W0s, a.w0 + (long long)h * 576);
+        stage_rows<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
+        stage_rows<BF>(Vs, Vp, Vsn, y0, x0, a.R, VP, gh, gw);
+        int nq = 0;
+        if (q_early) nq = stage_rows<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
+        vmcnt_at_most(nq); // this wave's K and V (and w0) loads have landed
+        lds_barrier();     // ... and every wave's
+        if (tile == tb) {
+#pragma unroll
+            for (int t = 0; t < 9; ++t) wt[t] = reinterpret_cast<const float*>(W0s)[lane * 9 + t];
+            // A store to a line that is not in the XCD's L2 goes on to
+            // memory without allocating it, and the slice's other
+            // workgroups would then read the partial from memory: a
+            // device-scope load of each of its 18 lines (it fills L2, not
+            // L1) makes the later stores and reads hit L2.
+            if (XC && a.S > 1 && w == 0)
+                pf = xload(a.part + ((long long)slice * a.S + split) * 576 + min(lane, 17) * 32);
+        }
+
         const int nsx = (tw + kSeg - 1) / kSeg;
-        for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
-            // Segment k of a row covers pixels [16k, 16k+16); the last one is
-            // shifted left to end at the row's end (its first pixels, done by
-            // the previous segment, are masked) -- or, in a row narrower than
-            // a segment, starts at 0 and masks the pixels past the row.  Every
-            // LDS value a segment needs is read up front at fixed offsets
-            // from one base, then the 3x3 window slides in registers.
-            const int r = sgi / nsx, k = sgi % nsx;
-            const int xs = min(k * kSeg, max(tw - kSeg, 0));
-            const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
-            const char* kb = Ks + ((r * HW + xs) * 64 + lane) * T::esz;
-            const char* vb = Vs + ((r * TWp + xs) * 64 + lane) * T::esz;
-            typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * HW + j) * 64) * T::esz);
-#pragma unroll
-            for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
-            __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
-            float kr[3][kSeg + 2], vv[kSeg];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
-#pragma unroll
-            for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
-#pragma unroll
-            for (int x = 0; x < kSeg; ++x) {
-                float p = 0.f;
+        {
+            for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
+                const int r = sgi / nsx;
+                // Segment k of a row covers pixels [16k, 16k+16); the last one is
+                // shifted left to end at the row's end (its first pixels, done by
+                // the previous segment, are masked) -- or, in a row narrower than
+                // a segment, starts at 0 and masks the pixels past the row.  Every
+                // LDS value a segment needs is read up front at fixed offsets
+                // from one base, then the 3x3 window slides in registers.
+                const int k = sgi % nsx;
+                const int xs = min(k * kSeg, max(tw - kSeg, 0));
+                const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
+                const char* kb = Ks + ((r * KP + xs) * 64 + lane) * T::esz;
+                const char* vb = Vs + ((r * VP + xs) * 64 + lane) * T::esz;
+                typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < 3; ++jj) p += wt[i * 3 + jj] * kr[i][x + jj];
-                const float rv = (x >= lo && x < hi) ? p - vv[x] : 0.f;
+                    for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * KP + j) * 64) * T::esz);
+#pragma unroll
+                for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
+                __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
+                float kr[3][kSeg + 2], vv[kSeg];
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] += rv * kr[i][x + jj];
+                    for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
+#pragma unroll
+                for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
+#pragma unroll
+                for (int x = 0; x < kSeg; ++x) {
+                    float p = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 3; ++jj) p += wt[i * 3 + jj] * kr[i][x + jj];
+                    const float rv = (x >= lo && x < hi) ? p - vv[x] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] += rv * kr[i][x + jj];
+                }
             }
         }
-        __syncthreads();
+        lds_barrier(); // every wave is done with this tile's K and V
     }
 
     // fixed-order sum of the 8 waves' tap sums: waves w and w + 4 first,
@@ -255,6 +276,7 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
     } else {
         float* P = a.part + ((long long)slice * a.S + split) * 576;
         unsigned* cnt = counter_at(a.cnt, slice);
+        asm volatile("" ::"v"(pf)); // the prefetch has completed before the stores
         for (int e = tid; e < 576; e += kCT) {
             const int c = e / 9, t = e % 9;
             const float v = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) +
@@ -262,8 +284,10 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             if constexpr (XC) P[e] = v;
             else xstore(P + e, v);
         }
-        slice_barrier(cnt, (unsigned)a.S, true, &s_chk, XC ? a.S : 0);
-        poison = s_chk != 0;
+        slice_barrier(cnt, (unsigned)a.S);
+        SliceWords sw{}; // thread 0; loaded alongside the partials
+        if (tid == 0) sw = slice_words(cnt);
+        float gv[4];
         // Every workgroup sums all S partials itself (576 floats each, in
         // split order, so all of them form the same w1): one barrier, and
         // no second round trip for w1.  Thread t < 144 owns elements
@@ -296,17 +320,31 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
                     }
                 }
             }
-            const float* w0e = a.w0 + (long long)h * 576 + 4 * tid;
+            const float* w0e = reinterpret_cast<const float*>(W0s) + 4 * tid; // w0 of the head, staged
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                const float gv = scale * acc[k];
-                w1s[4 * tid + k] = w0e[k] - eta * gv;
-                if (a.saved && split == 0)
-                    a.saved[(long long)slice * 576 + 4 * tid + k] = poison ? __builtin_nanf("") : gv;
+                gv[k] = scale * acc[k];
+                w1s[4 * tid + k] = w0e[k] - eta * gv[k];
             }
         }
-        slice_barrier_release(cnt, 2u * a.S);
+        if (tid == 0) s_chk = slice_bad(sw, XC ? a.S : 0) ? 1 : 0;
         __syncthreads();
+        poison = s_chk != 0;
+        if (a.saved && split == 0 && tid < 144) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                a.saved[(long long)slice * 576 + 4 * tid + k] = poison ? __builtin_nanf("") : gv[k];
+        }
+        // The counter's release, once the partials are read (vector-memory
+        // results return in issue order across the CU's waves, so an
+        // atomic on the slice's contended counter line issued earlier
+        // would hold up their loads); its result (does this workgroup
+        // complete the count and reset it?) is used at the end.
+        if (tid == 0) rel = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (q_early && a.S == 1) { // (with S > 1 the slice barrier drained every wave)
+        drain_vmem();           // this wave's Q loads have landed
+        __syncthreads();        // ... and every wave's
     }
     float wq[9];
 #pragma unroll
@@ -317,9 +355,8 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
         const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
         const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
         if (!q_early) {
-            stage<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
-            __syncthreads();
-            zero_outside<BF>(Qs, y0 - 1, x0 - 1, a.R + 2, HW, gh, gw);
+            stage_rows<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
+            drain_vmem();
             __syncthreads();
         }
         const int nsx = (tw + kSeg - 1) / kSeg;
@@ -328,13 +365,13 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
             const int xs = min(k * kSeg, max(tw - kSeg, 0));
             const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
             const int y = y0 + r;
-            const char* qb = Qs + ((r * HW + xs) * 64 + lane) * T::esz;
+            const char* qb = Qs + ((r * KP + xs) * 64 + lane) * T::esz;
             char* zrow = Zp + ((long long)y * gw + x0 + xs) * Zsn + lane * T::esz;
             typename T::raw_t qraw[3][kSeg + 2];
 #pragma unroll
             for (int i = 0; i < 3; ++i)
 #pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * HW + j) * 64) * T::esz);
+                for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * KP + j) * 64) * T::esz);
             __builtin_amdgcn_sched_barrier(0);
             float qr[3][kSeg + 2];
 #pragma unroll
@@ -353,6 +390,7 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
         }
         if (!q_early) __syncthreads();
     }
+    if (a.S > 1 && tid == 0 && rel == 2u * a.S - 1) slice_reset(counter_at(a.cnt, slice));
 }
 
 struct ConvPlan {
@@ -365,8 +403,10 @@ ConvPlan plan_conv(int nslices, int gh, int gw, int esz, int cap) {
     const long long slices = (nslices + 7) / 8 * 8; // XCD-aware grids round slices up to 8
     const int pb = 64 * esz;
     auto fits = [&](int R, int TW) {
-        const long long TWp = TW > kSeg ? TW : kSeg; // LDS rows hold at least one segment
-        return ((long long)2 * (R + 2) * (TWp + 2) + (long long)R * TWp) * pb + 3 * 1024 <= kTileBytes + 3 * 1024;
+        const int TWp = TW > kSeg ? TW : kSeg; // LDS rows hold at least one segment
+        const long long KP = esz == 2 ? conv_pitch<true>(TWp + 2) : conv_pitch<false>(TWp + 2);
+        const long long VP = esz == 2 ? conv_pitch<true>(TWp) : conv_pitch<false>(TWp);
+        return (2 * (R + 2) * KP + (long long)R * VP) * pb <= kTileBytes;
     };
     ConvPlan p{};
     long long target = cap > 0 ? cap / slices : 1;

@@ -261,7 +261,7 @@ __device__ __forceinline__ int w1_frag_index(int r, int c) {
 template <bool BF, bool XC>
 __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h, float* lds,
                              float* mA, float* mC, float* w0s_one, float* w0s_split, const f32x4* w0r,
-                             int* chk, bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
+                             SliceWords* sw, bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
@@ -376,13 +376,9 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
             sv[4096 + r * 64 + c] = gv;
         }
     }
-    slice_barrier(cnt, 2u * a.S, true, chk, XC ? a.S : 0);
+    slice_barrier(cnt, 2u * a.S);
+    if (tid == 0) *sw = slice_words(cnt);
     keep_alive(pf);
-    if (sv && *chk) // a failed exchange: this workgroup's columns of A and G
-        for (int e = tid; e < 64 * nc; e += kThreads) {
-            const int r = e >> lgnc, c = c0 + (e & (nc - 1));
-            sv[r * 64 + c] = sv[4096 + r * 64 + c] = __builtin_nanf("");
-        }
     // W1 is complete in the workspace at a.w1 + slice*4096 (bf16 fragments
     // for BF && XC, else row-major fp32)
     return nullptr;
@@ -398,6 +394,29 @@ __device__ __forceinline__ unsigned release_begin(const LinFwdLaunch& a, int sli
 }
 __device__ __forceinline__ void release_end(const LinFwdLaunch& a, int slice, unsigned old) {
     if (a.S > 1 && threadIdx.x == 0 && old == 3u * a.S - 1) slice_reset(counter_at(a.cnt, slice));
+}
+
+// After the slice's last waiting barrier, with the loads the apply needs
+// (W1) already issued: waits for every load of the workgroup, then thread
+// 0's slice words (loaded right after that barrier, before any release)
+// decide through LDS whether the slice's outputs are NaN -- Z by the
+// caller, A and G (this workgroup's columns) here.
+template <bool XC>
+__device__ __forceinline__ bool exchange_outcome(const LinFwdLaunch& a, int slice, int split,
+                                                 const SliceWords& sw, int* chk, int nthreads) {
+    drain_vmem();
+    if (a.S > 1 && threadIdx.x == 0) *chk = slice_bad(sw, XC ? a.S : 0) ? 1 : 0;
+    __syncthreads();
+    const bool bad = a.S > 1 && *chk != 0;
+    if (bad && a.saved) {
+        const int lgnc = 6 - __builtin_ctz(a.S), nc = 1 << lgnc, c0 = split * nc;
+        float* sv = a.saved + (long long)slice * 8192;
+        for (int e = threadIdx.x; e < 64 * nc; e += nthreads) {
+            const int r = e >> lgnc, c = c0 + (e & (nc - 1));
+            sv[r * 64 + c] = sv[4096 + r * 64 + c] = __builtin_nanf("");
+        }
+    }
+    return bad;
 }
 
 // ------------------------------------------------------------- phase 3 --
@@ -669,7 +688,7 @@ __device__ __forceinline__ void split_bf(const float* v, v8bf& hi, v8bf& lo) {
     lo = as_v8bf(l);
 }
 constexpr int kAP = 72; // pitch (bf16) of the A planes
-// Byte offset in a kernel's LDS of the exchange outcome (slice_check),
+// Byte offset in a kernel's LDS of the exchange outcome (slice_bad),
 // written after the last slice barrier: above the phase-2 regions of
 // lin_update (gather staging, W0) and the G-phase regions, below the end
 // of the K/V regions and of the streaming kernel's LDS.
@@ -902,6 +921,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 
     // ---- phase 2
     float* W1 = nullptr;
+    SliceWords sw{}; // thread 0, after the last slice barrier
     if (gx) {
         unsigned* cnt = counter_at(a.cnt, c.slice);
         slice_barrier(cnt, (unsigned)a.S);
@@ -912,29 +932,28 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
         default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
         }
-        slice_barrier(cnt, 2u * a.S, true, chk, a.S);
+        slice_barrier(cnt, 2u * a.S);
+        if (tid == 0) sw = slice_words(cnt);
         keep_alive(pf);
     } else {
-        W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, chk,
+        W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, ldsf, mA, mC, ldsf, ldsf + 8192 + 128, w0r, &sw,
                                 published, pf);
     }
-    const bool poison = a.S > 1 && *chk != 0; // NaN output for a failed exchange
-    // every wave's Q loads have landed (normally long since)
-    drain_vmem();
-    lds_barrier();
 
     // ---- phase 3: Z from the resident Q region (skipped when only A and G
-    // are wanted)
-    if (!a.Z.ptr) {
-        release_end(a, c.slice, release_begin(a, c.slice));
-        return;
-    }
+    // are wanted); W1's fragments are loaded while the exchange outcome and
+    // every wave's Q loads (normally long since landed) are waited for
     const int nsteps = (T + 15) / 16;
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
         const W1FragsBF wf = W1   ? w1_frags_bf(W1, g, m)
                              : XC ? w1_frags_bf_packed(w1g, lane)
                                   : w1_frags_bf_global<XC>(w1g, g, m);
+        const bool poison = exchange_outcome<XC>(a, c.slice, c.split, sw, chk, kThreads);
+        if (!a.Z.ptr) {
+            release_end(a, c.slice, release_begin(a, c.slice));
+            return;
+        }
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll 2
         for (int step = w; step < nsteps; step += 4) {
@@ -948,6 +967,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         release_end(a, c.slice, rel);
     } else {
         const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global<XC>(w1g, g, m);
+        const bool poison = exchange_outcome<XC>(a, c.slice, c.split, sw, chk, kThreads);
+        if (!a.Z.ptr) {
+            release_end(a, c.slice, release_begin(a, c.slice));
+            return;
+        }
         const unsigned rel = release_begin(a, c.slice);
         for (int step = w; step < nsteps; step += 4) {
             const int row = step * 16 + m;
@@ -1074,11 +1098,14 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
         default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
         }
     }
-    slice_barrier(cnt, 2u * a.S, w < 4, chk, a.S);
+    slice_barrier(cnt, 2u * a.S, w < 4);
+    SliceWords sw{};
+    if (tid == 0) sw = slice_words(cnt);
     keep_alive(pf);
-    const bool poison = *chk != 0; // NaN output for a failed exchange
-    drain_vmem();    // this wave's Q loads have landed
-    __syncthreads(); // ... and every wave's
+    // W1's fragments load while every wave's Q loads (normally long since
+    // landed) and the exchange outcome are waited for
+    const W1FragsBF wf = w1_frags_bf_packed(a.w1 + (long long)c.slice * 4096, lane);
+    const bool poison = exchange_outcome<true>(a, c.slice, c.split, sw, chk, kThreads8);
 
     // ---- phase 3: Z from the resident Q region
     if (!a.Z.ptr) {
@@ -1086,7 +1113,6 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
         return;
     }
     const int nsteps = (T + 15) / 16;
-    const W1FragsBF wf = w1_frags_bf_packed(a.w1 + (long long)c.slice * 4096, lane);
     const unsigned rel = release_begin(a, c.slice);
     for (int step = w; step < nsteps; step += 8) {
         const int row = step * 16 + m;
@@ -1221,18 +1247,19 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     float* mC = lds + 64 * MP;
     reduce_waves(accC, accA, lds, mA, mC, w, lane, g, m, true);
 
-    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r, chk);
-    const bool poison = a.S > 1 && *chk != 0; // NaN output for a failed exchange
-    if (!a.Z.ptr) { // only A and G wanted
-        release_end(a, c.slice, release_begin(a, c.slice));
-        return;
-    }
+    SliceWords sw{}; // thread 0, after the last slice barrier
+    float* W1 = lin_update<BF, XC>(a, c.slice, c.split, c.h, lds, mA, mC, lds + 128 * MP, lds + 8192 + 128, w0r, &sw);
 
     const float* w1g = a.w1 + (long long)c.slice * 4096;
     if constexpr (BF) {
         const W1FragsBF wf = W1   ? w1_frags_bf(W1, g, m)
                              : XC ? w1_frags_bf_packed(w1g, lane)
                                   : w1_frags_bf_global<XC>(w1g, g, m);
+        const bool poison = exchange_outcome<XC>(a, c.slice, c.split, sw, chk, kThreads);
+        if (!a.Z.ptr) { // only A and G wanted
+            release_end(a, c.slice, release_begin(a, c.slice));
+            return;
+        }
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
@@ -1250,6 +1277,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
         release_end(a, c.slice, rel);
     } else {
         const W1FragsF32 wf = W1 ? w1_frags_f32(W1, g, m) : w1_frags_f32_global<XC>(w1g, g, m);
+        const bool poison = exchange_outcome<XC>(a, c.slice, c.split, sw, chk, kThreads);
+        if (!a.Z.ptr) { // only A and G wanted
+            release_end(a, c.slice, release_begin(a, c.slice));
+            return;
+        }
         const unsigned rel = release_begin(a, c.slice);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
