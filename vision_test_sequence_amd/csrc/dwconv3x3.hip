@@ -289,37 +289,38 @@ __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
         if (tid == 0) sw = slice_words(cnt);
         float gv[4];
         // Every workgroup sums all S partials itself (576 floats each, in
-        // split order, so all of them form the same w1): one barrier, and
-        // no second round trip for w1.  Thread t < 144 owns elements
-        // 4t..4t+3, all S loads in flight (S <= 32: the grid holds at most
-        // 256 workgroups of >= 8 slices).
+        // a fixed order, so all of them form the same w1): one barrier, and
+        // no second round trip for w1.  Threads t < 432 share the loads:
+        // element group e4 = t % 144 (floats 4 e4..4 e4+3) of the splits in
+        // group t / 144 of three (consecutive runs of ceil(S/3) <= 11
+        // splits, S <= 32: the grid holds at most 256 workgroups of >= 8
+        // slices); the three group sums meet in LDS.
+        float* gsum = red; // [3][576], free once the partial is published
+        if (tid < 432) {
+            const int e4 = tid % 144, q = tid / 144;
+            const int G = (a.S + 2) / 3, s0 = q * G, s1 = min(a.S, s0 + G);
+            const float* src = a.part + (long long)slice * a.S * 576 + 4 * e4;
+            f32x4 v[11];
+#pragma unroll
+            for (int k = 0; k < 11; ++k) {
+                if (k < G) { // uniform
+                    const float* p = src + min(s0 + k, s1 - 1) * 576;
+                    if constexpr (XC) v[k] = *reinterpret_cast<const f32x4*>(p);
+                    else v[k] = f32x4{xload(p), xload(p + 1), xload(p + 2), xload(p + 3)};
+                }
+            }
+            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < 11; ++k)
+                if (k < G && s0 + k < s1) acc += v[k];
+            *reinterpret_cast<f32x4*>(gsum + q * 576 + 4 * e4) = acc;
+        }
+        __syncthreads();
         if (tid < 144) {
-            const float* src = a.part + (long long)slice * a.S * 576 + 4 * tid;
-            // loads in chunks of 8 splits, one uniform branch per chunk
-            // (indices past the last split repeat it and are not added)
-            f32x4 v[32];
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                if (8 * ch < a.S) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const float* q = src + min(8 * ch + k, a.S - 1) * 576;
-                        if constexpr (XC) v[8 * ch + k] = *reinterpret_cast<const f32x4*>(q);
-                        else v[8 * ch + k] = f32x4{xload(q), xload(q + 1), xload(q + 2), xload(q + 3)};
-                    }
-                }
-            }
-            f32x4 acc = v[0];
-#pragma unroll
-            for (int ch = 0; ch < 4; ++ch) {
-                if (8 * ch < a.S) {
-#pragma unroll
-                    for (int k = 0; k < 8; ++k) {
-                        const int sp = 8 * ch + k;
-                        if (sp > 0 && sp < a.S) acc += v[sp];
-                    }
-                }
-            }
+            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gsum + 4 * tid);
+            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gsum + 576 + 4 * tid);
+            const f32x4 g2 = *reinterpret_cast<const f32x4*>(gsum + 1152 + 4 * tid);
+            const f32x4 acc = (g0 + g1) + g2;
             const float* w0e = reinterpret_cast<const float*>(W0s) + 4 * tid; // w0 of the head, staged
 #pragma unroll
             for (int k = 0; k < 4; ++k) {

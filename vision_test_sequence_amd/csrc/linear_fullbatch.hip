@@ -693,6 +693,9 @@ constexpr int kAP = 72; // pitch (bf16) of the A planes
 // lin_update (gather staging, W0) and the G-phase regions, below the end
 // of the K/V regions and of the streaming kernel's LDS.
 constexpr int kChkByte = (8192 + 128 + 64 * MP) * 4;
+// Group sums of reduce_g (4 KB), right above the G-phase regions.
+constexpr int kGSumByte = 4 * 64 * kAP + 64 * MP * 4;
+static_assert(kGSumByte + 4096 <= kChkByte, "reduce_g group sums below the exchange outcome");
 static_assert(kChkByte >= 4 * 64 * kAP + 64 * MP * 4, "exchange outcome above the G-phase regions");
 static_assert(kChkByte + 4 <= 20480 * 4, "exchange outcome inside the streaming kernel's LDS");
 // Wave w's rows of G_s from its owned rows of A_s and C_s.  The product
@@ -783,33 +786,66 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
     lds_barrier();
     g_rows_store(a, slice, split, oC, L, w, lane);
 }
-// Reducer `split`: sum its R entries over the S splits (split order), form
+// Reducer `split`: sum its R = 4096/S entries over the S splits, form
 // W1 = W0 - eta (2/N) G and store them as bf16 fragments (w1_frag_index).
-template <int S, int NT>
-__device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h) {
+// The 256 threads of waves 0-3 (`active`) load: with S >= 8 thread t sums
+// float4 t % n4 of the reducer's block over the four splits of group
+// t / n4 (split order), and the S/4 group sums meet in LDS (group order);
+// with S <= 4 every thread sums its float4s over all splits.  W0 is read
+// from its staged copy (g_lds).  Every wave of the workgroup calls this
+// (with S >= 8 it holds one workgroup barrier).
+template <int S>
+__device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h, char* lds,
+                                         bool active) {
     constexpr int R = 4096 / S, n4 = R / 4;
+    constexpr int NG = S >= 8 ? S / 4 : 1; // split groups
+    constexpr int SG = S / NG;             // splits per group
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
     const f32x4* blk = reinterpret_cast<const f32x4*>(a.part + (long long)slice * S * 4096 + (long long)split * S * R);
-    const float* W0h = a.W0 + (long long)h * 4096;
+    const float* w0s = g_lds(lds).w0s;
     bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
-#pragma unroll
-    for (int t4 = tid; t4 < n4; t4 += NT) {
-        f32x4 v[S];
-#pragma unroll
-        for (int sp = 0; sp < S; ++sp) v[sp] = blk[sp * n4 + t4];
+    auto finish = [&](int t4, const f32x4& acc) __attribute__((always_inline)) {
         const int P = split * R + 4 * t4, q = P >> 8, e = P & 255;
         const int mq = 8 * (e >> 7) + 4 * ((e >> 6) & 1); // m' of the first of four rows
         const int rb = q >> 2, c = 32 * ((q >> 1) & 1) + 16 * (q & 1) + ((e >> 2) & 15), r0 = perm_row(rb, mq);
-        float w0v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w0v[i] = W0h[(r0 + i) * 64 + c];
-        f32x4 acc = v[0];
+        for (int i = 0; i < 4; ++i)
+            w1b[w1_frag_index(r0 + i, c)] = f2bf(w0s[(r0 + i) * MP + c] - eta * (scale * acc[i]));
+    };
+    if constexpr (NG == 1) {
+        if (active) {
 #pragma unroll
-        for (int sp = 1; sp < S; ++sp) acc += v[sp];
+            for (int t4 = tid; t4 < n4; t4 += 256) {
+                f32x4 v[S];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) w1b[w1_frag_index(r0 + i, c)] = f2bf(w0v[i] - eta * (scale * acc[i]));
+                for (int sp = 0; sp < S; ++sp) v[sp] = blk[sp * n4 + t4];
+                f32x4 acc = v[0];
+#pragma unroll
+                for (int sp = 1; sp < S; ++sp) acc += v[sp];
+                finish(t4, acc);
+            }
+        }
+    } else {
+        f32x4* gs = reinterpret_cast<f32x4*>(lds + kGSumByte); // [NG][n4]
+        if (active) {
+            const int t4 = tid % n4, gq = tid / n4;
+            f32x4 v[SG];
+#pragma unroll
+            for (int k = 0; k < SG; ++k) v[k] = blk[(gq * SG + k) * n4 + t4];
+            f32x4 acc = v[0];
+#pragma unroll
+            for (int k = 1; k < SG; ++k) acc += v[k];
+            gs[gq * n4 + t4] = acc;
+        }
+        lds_barrier(); // (waits for no global load: waves 4-7 keep their Q loads in flight)
+        if (active && tid < n4) {
+            f32x4 acc = gs[tid];
+#pragma unroll
+            for (int gq = 1; gq < NG; ++gq) acc += gs[gq * n4 + tid];
+            finish(tid, acc);
+        }
     }
 }
 
@@ -926,11 +962,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         unsigned* cnt = counter_at(a.cnt, c.slice);
         slice_barrier(cnt, (unsigned)a.S);
         switch (a.S) {
-        case 2: reduce_g<2, kThreads>(a, c.slice, c.split, c.h); break;
-        case 4: reduce_g<4, kThreads>(a, c.slice, c.split, c.h); break;
-        case 8: reduce_g<8, kThreads>(a, c.slice, c.split, c.h); break;
-        case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
-        default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
+        case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, true); break;
+        case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, true); break;
+        case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, true); break;
+        case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, true); break;
+        default: reduce_g<32>(a, c.slice, c.split, c.h, lds, true); break;
         }
         slice_barrier(cnt, 2u * a.S);
         if (tid == 0) sw = slice_words(cnt);
@@ -1089,14 +1125,12 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
     slice_barrier(cnt, (unsigned)a.S, w < 4);
     // waves 0-3 reduce (waves 4-7 have Q loads in flight, which a gather of
     // theirs would queue behind)
-    if (w < 4) {
-        switch (a.S) {
-        case 2: reduce_g<2, kThreads>(a, c.slice, c.split, c.h); break;
-        case 4: reduce_g<4, kThreads>(a, c.slice, c.split, c.h); break;
-        case 8: reduce_g<8, kThreads>(a, c.slice, c.split, c.h); break;
-        case 16: reduce_g<16, kThreads>(a, c.slice, c.split, c.h); break;
-        default: reduce_g<32, kThreads>(a, c.slice, c.split, c.h); break;
-        }
+    switch (a.S) {
+    case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, w < 4); break;
+    case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, w < 4); break;
+    case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, w < 4); break;
+    case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4); break;
+    default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4); break;
     }
     slice_barrier(cnt, 2u * a.S, w < 4);
     SliceWords sw{};
