@@ -151,6 +151,29 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
                                    ttt_stream_t stream);
 
 /*
+ * One layer's full-batch steps in one call (the ViT3 layer recipe: linear
+ * and depthwise-conv inner models on different heads of the same tokens):
+ * exactly ttt_linear_fullbatch(lin, Kl, Ql, Vl, W0, eta_l, Zl) and
+ * ttt_dwconv3x3_fullbatch(conv, Kc, Qc, Vc, w0, eta_c, Zc), without saved
+ * outputs, with the same results bit for bit.  When both fit (bf16, the
+ * linear heads' tokens split over workgroups exchanging through one XCD,
+ * the conv heads one tile per workgroup) they run as one kernel, in which
+ * each workgroup's conv work starts as soon as its linear work ends;
+ * otherwise as the two kernels of those calls.  Either problem may
+ * have B or H zero.  All ten views/buffers are inputs except Zl and Zc; no
+ * output may overlap another argument.
+ * ws: ttt_layer_workspace_size(lin, conv) bytes, 256-byte aligned,
+ * zero-filled before its first use (the library leaves it reusable), not
+ * shared by calls that may run concurrently.
+ */
+size_t ttt_layer_workspace_size(const ttt_problem* lin, const ttt_problem* conv);
+ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql, ttt_view Vl,
+                               const float* W0, const float* eta_l, ttt_view Zl,
+                               const ttt_problem* conv, ttt_view Kc, ttt_view Qc, ttt_view Vc,
+                               const float* w0, const float* eta_c, ttt_view Zc,
+                               void* ws, size_t ws_bytes, ttt_stream_t stream);
+
+/*
  * Causal mini-batch gradient descent of the linear inner model over the
  * token sequence and over the reversed sequence (Vision-TTT "关键设计"
  * items 2 and 4).  Mini-batches of b = p->minibatch tokens, the last one

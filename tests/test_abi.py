@@ -233,3 +233,46 @@ def test_python_binding_rejects_bad_params_before_the_library():
     K = torch.zeros(1, 1, 16, 64)
     with pytest.raises(ValueError):
         vt.ttt_linear_fullbatch(K, K, K, torch.zeros(1, 64, 32), torch.ones(1))
+
+
+def layer(pl, pc, Zl=None, Zc=None, Kc=None, wsb=None):
+    L = vt.lib()
+    need = L.ttt_layer_workspace_size(ctypes.byref(pl), ctypes.byref(pc))
+    return L.ttt_layer_fullbatch(ctypes.byref(pl), V(0, pl.B, pl.H, pl.N), V(1, pl.B, pl.H, pl.N),
+                                 V(2, pl.B, pl.H, pl.N), addr(10), addr(11), Zl or V(3, pl.B, pl.H, pl.N),
+                                 ctypes.byref(pc), Kc or V(4, pc.B, pc.H, pc.N), V(5, pc.B, pc.H, pc.N),
+                                 V(6, pc.B, pc.H, pc.N), addr(12), addr(13), Zc or V(7, pc.B, pc.H, pc.N),
+                                 addr(20) if need else None, need if wsb is None else wsb, None)
+
+
+def test_layer_workspace_size():
+    L = vt.lib()
+    pl, pc = P(B=8, H=2, N=6084, gh=78, gw=78), P(B=8, H=1, N=6084, gh=78, gw=78)
+    lw = L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH, ctypes.byref(pl))
+    cw = L.ttt_workspace_size(bd.OP_DWCONV3X3_FULLBATCH, ctypes.byref(pc))
+    assert lw > 0 and cw > 0
+    C = 256 * 64 * 4  # one counter block
+    al = lambda n: (n + 255) // 256 * 256
+    assert L.ttt_layer_workspace_size(ctypes.byref(pl), ctypes.byref(pc)) == C + al(lw) + cw - C
+    # no linear workspace: its counter block is still reserved
+    p0 = P(B=128, H=2, N=196, gh=14, gw=14)
+    assert L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p0)) == 0
+    c1 = P(B=2, H=1, N=100)
+    cw1 = L.ttt_workspace_size(bd.OP_DWCONV3X3_FULLBATCH, ctypes.byref(c1))
+    assert L.ttt_layer_workspace_size(ctypes.byref(p0), ctypes.byref(c1)) == C + C + cw1 - C
+
+
+def test_layer_errors():
+    pl, pc = P(B=2, H=2, N=100), P(B=2, H=1, N=100)
+    assert bd.STATUS_NAMES[layer(pl, P(B=2, H=1, N=100, gh=9, gw=10))] == "TTT_ERR_BAD_SHAPE"
+    assert layer(P(B=0, H=2, N=100), P(B=0, H=1, N=100)) == 0
+    # the conv output on top of a linear input
+    assert bd.STATUS_NAMES[layer(pl, pc, Zc=V(0, 2, 1, 100))] == "TTT_ERR_ALIASING"
+    # the two outputs as overlapping head ranges of one [2, 3, 100, 64] tensor
+    z3 = lambda h0: bd.View(addr(3) + h0 * 100 * 64 * 2, 3 * 100 * 64, 100 * 64, 64)
+    assert bd.STATUS_NAMES[layer(pl, pc, Zl=z3(0), Zc=z3(1))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[layer(pl, pc, Zl=z3(1), Zc=z3(2))] == "TTT_ERR_ALIASING"
+    assert bd.STATUS_NAMES[layer(pl, pc, wsb=0)] == "TTT_ERR_WORKSPACE_TOO_SMALL"
+    # (disjoint head ranges of one output tensor are accepted: the GPU
+    # layer tests run them; no case here may pass validation, which would
+    # launch on the fake addresses)

@@ -1,4 +1,4 @@
-"""The four entry points captured in one HIP graph (torch.cuda.graph) and
+"""The entry points captured in one HIP graph (torch.cuda.graph) and
 replayed, with eager calls and synchronisations between the replays: every
 replay, and every eager call after one, must reproduce the eager outputs
 bit for bit.  The exchange kernels place their splits by the XCD they run
@@ -34,14 +34,19 @@ def _ops(g, w):
         vt.ttt_linear_fullbatch_bwd(g["Ks"], g["Qs"], g["Vs"], g["W0l"], g["etal"], g["dZ"], saved=g["sv"],
                                     dK=g["dK"], dQ=g["dQ"], dV=g["dV"], dW0=g["dW0"], deta=g["deta"])
 
-    return [lin, conv, lin_saved, scan, bwd]
+    def layer():
+        vt.ttt_layer_fullbatch(g["K"][:, 0:2], g["Q"][:, 0:2], g["V"][:, 0:2], g["W0l"], g["etal"],
+                               g["K"][:, 2:3], g["Q"][:, 2:3], g["V"][:, 2:3], g["w0c"], g["etac"],
+                               w.grid_h, w.grid_w, Zl=g["Zy"][:, 0:2], Zc=g["Zy"][:, 2:3])
+
+    return [lin, conv, lin_saved, scan, bwd, layer]
 
 
-OUTS = ("Z", "Zs", "sv", "Zm", "dK", "dQ", "dV", "dW0", "deta")
+OUTS = ("Z", "Zs", "sv", "Zm", "dK", "dQ", "dV", "dW0", "deta", "Zy")
 
 
 def test_graph_replay_matches_eager():
-    banner("graph capture / replay of the four entry points")
+    banner("graph capture / replay of the entry points")
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS["vit3t_1248_bf16"]
     g = {k: v.to(dev) for k, v in wl.make("vit3t_1248_bf16").items()}
@@ -50,6 +55,7 @@ def test_graph_replay_matches_eager():
     g["w0c"] = g["w0"][2:3].contiguous()
     g["etac"] = g["eta"][2:3].contiguous()
     g["Z"] = torch.zeros_like(g["Q"])
+    g["Zy"] = torch.zeros_like(g["Q"])
     # a smaller problem for the saved-A/G forward, the scans and the backward
     s = {k: v.to(dev) for k, v in wl.make("vit3t_224_bf16").items()}
     g["Ks"], g["Qs"], g["Vs"] = (s[k][:, 0:2].contiguous() for k in ("K", "Q", "V"))
@@ -77,6 +83,7 @@ def test_graph_replay_matches_eager():
     ref = {k: g[k].clone() for k in OUTS}
     for k in OUTS:
         assert not torch.isnan(ref[k].float()).any(), f"eager {k} has NaN"
+    assert torch.equal(ref["Zy"], ref["Z"])  # the layer call equals the two separate calls
 
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())

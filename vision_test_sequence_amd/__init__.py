@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     lib,
     library_path,
     ttt_dwconv3x3_fullbatch,
+    ttt_layer_fullbatch,
     ttt_linear_fullbatch,
     ttt_linear_fullbatch_bwd,
     ttt_linear_minibatch_bidir,

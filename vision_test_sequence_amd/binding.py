@@ -33,8 +33,9 @@ STATUS_NAMES = [
     "TTT_ERR_WORKSPACE_TOO_SMALL", "TTT_ERR_HIP",
 ]
 
-EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_linear_fullbatch",
-            "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd")
+EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size", "ttt_linear_fullbatch",
+            "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
+            "ttt_layer_fullbatch")
 
 
 class TTTError(RuntimeError):
@@ -82,12 +83,16 @@ def lib() -> ctypes.CDLL:
             L.ttt_workspace_size.restype = sz
             L.ttt_status_string.argtypes = [ctypes.c_int]
             L.ttt_status_string.restype = ctypes.c_char_p
+            L.ttt_layer_workspace_size.argtypes = [P, P]
+            L.ttt_layer_workspace_size.restype = sz
             L.ttt_linear_fullbatch.argtypes = [P, View, View, View, fp, fp, View, fp, vp, sz, vp]
             L.ttt_dwconv3x3_fullbatch.argtypes = [P, View, View, View, fp, fp, View, fp, vp, sz, vp]
             L.ttt_linear_minibatch_bidir.argtypes = [P, View, View, View, fp, fp, View, vp, sz, vp]
             L.ttt_linear_fullbatch_bwd.argtypes = [P, View, View, View, fp, fp, View, fp, View, View,
                                                    View, fp, fp, vp, sz, vp]
-            for f in EXPORTED[2:]:
+            L.ttt_layer_fullbatch.argtypes = [P, View, View, View, fp, fp, View, P, View, View, View, fp, fp,
+                                              View, vp, sz, vp]
+            for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
     return _lib
@@ -125,14 +130,16 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-_ws: Dict[Tuple[int, int], torch.Tensor] = {}
+_ws: Dict[Tuple[int, object], torch.Tensor] = {}
 
 
-def workspace(op: int, prob: Problem, device: torch.device) -> Tuple[Optional[int], int]:
+def workspace(op, prob: Optional[Problem], device: torch.device, need: Optional[int] = None
+              ) -> Tuple[Optional[int], int]:
     """Zero-filled scratch for `op`, cached per (device, op); grows on demand.
     The library leaves its counters at zero after every call, so one buffer
     serves consecutive calls of that op on one stream."""
-    need = int(lib().ttt_workspace_size(op, ctypes.byref(prob)))
+    if need is None:
+        need = int(lib().ttt_workspace_size(op, ctypes.byref(prob)))
     if need == 0:
         return None, 0
     key = (device.index if device.index is not None else torch.cuda.current_device(), op)
@@ -194,6 +201,36 @@ def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=Non
                                        _stream(K.device))
     _check(st, "ttt_dwconv3x3_fullbatch")
     return Z
+
+
+def ttt_layer_fullbatch(Kl, Ql, Vl, W0, eta_l, Kc, Qc, Vc, w0, eta_c, grid_h: int, grid_w: int, *,
+                        Zl=None, Zc=None):
+    """Both full-batch steps of one layer in one call: ttt_linear_fullbatch on
+    (Kl, Ql, Vl, W0, eta_l) and ttt_dwconv3x3_fullbatch on (Kc, Qc, Vc, w0,
+    eta_c) over a grid_h x grid_w token map, with the same results; one
+    launch when they fit.  Views as in the two calls (the linear and conv
+    heads may be head ranges of one tensor).  Returns (Zl, Zc).
+    """
+    Bl, Hl, N, d = Kl.shape
+    Bc, Hc = Kc.shape[0], Kc.shape[1]
+    _param(W0, (Hl, d, d), "W0")
+    _param(eta_l, (Hl,), "eta_l")
+    _param(w0, (Hc, d, 3, 3), "w0")
+    _param(eta_c, (Hc,), "eta_c")
+    if Zl is None:
+        Zl = torch.empty((Bl, Hl, N, d), dtype=Kl.dtype, device=Kl.device)
+    if Zc is None:
+        Zc = torch.empty(tuple(Kc.shape), dtype=Kc.dtype, device=Kc.device)
+    pl = problem(Kl)
+    pc = problem(Kc, grid=(grid_h, grid_w))
+    need = int(lib().ttt_layer_workspace_size(ctypes.byref(pl), ctypes.byref(pc)))
+    ws, wsb = workspace("layer", None, Kl.device, need)
+    st = lib().ttt_layer_fullbatch(ctypes.byref(pl), view(Kl), view(Ql), view(Vl), W0.data_ptr(),
+                                   eta_l.data_ptr(), view(Zl), ctypes.byref(pc), view(Kc), view(Qc),
+                                   view(Vc), w0.data_ptr(), eta_c.data_ptr(), view(Zc), ws, wsb,
+                                   _stream(Kl.device))
+    _check(st, "ttt_layer_fullbatch")
+    return Zl, Zc
 
 
 def ttt_linear_minibatch_bidir(K, Q, V, W0, eta, minibatch: int, mode: int = BIDIR_AVG, *, Z=None):

@@ -88,6 +88,28 @@ ttt_status check_aliasing(const Span* in, int nin, const Span* out, int nout) {
     return TTT_OK;
 }
 
+// Two views with the same strides and batch size that are head ranges of
+// one larger view (the second starts k whole heads from the first, and the
+// union of the two head ranges is itself a view without coinciding
+// elements): disjoint exactly when the head ranges are.  Returns false when
+// the two do not have this form (the caller then compares address spans).
+bool head_ranges_disjoint(const ttt_view& a, int Ha, const ttt_view& b, int Hb, const ttt_problem& p) {
+    if (a.stride_b != b.stride_b || a.stride_h != b.stride_h || a.stride_n != b.stride_n) return false;
+    const int64_t es = (int64_t)esize(p.dtype);
+    const int64_t delta = ((int64_t)(uintptr_t)b.ptr - (int64_t)(uintptr_t)a.ptr);
+    if (a.stride_h <= 0 || delta % (es * a.stride_h)) return false;
+    const int64_t k = delta / (es * a.stride_h);
+    const int64_t h0 = k < 0 ? k : 0, h1 = std::max<int64_t>(Ha, k + Hb);
+    if (h1 - h0 > (int64_t)1 << 24) return false;
+    ttt_problem u = p;
+    u.H = (int32_t)(h1 - h0);
+    ttt_view uv = a;
+    uv.ptr = (char*)a.ptr + h0 * a.stride_h * es;
+    Span sp;
+    if (check_view(uv, u, &sp) != TTT_OK) return false;
+    return k >= Ha || k + Hb <= 0;
+}
+
 ttt_status check_ws(void* ws, size_t ws_bytes, size_t need, Span* sp) {
     if (ws_bytes < need) return TTT_ERR_WORKSPACE_TOO_SMALL;
     if (need == 0) return TTT_OK;
@@ -153,11 +175,11 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     return 0;
 }
 
-// Plan and launch the full-batch forward (validated arguments).  A null Z
-// computes only A and G into `saved`.
-static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* W0,
-                                   const float* eta, float* saved, void* ws, hipStream_t stream) {
-    LinFwdLaunch a{};
+// Plan the full-batch forward (validated arguments).  A null Z computes
+// only A and G into `saved`.
+static ttt_status plan_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* W0,
+                                 const float* eta, float* saved, void* ws, LinFwdLaunch& a, int& resident) {
+    a = LinFwdLaunch{};
     a.K = K; a.Q = Q; a.V = V; a.Z = Z;
     a.W0 = W0; a.eta = eta; a.saved = saved;
     a.B = p->B; a.H = p->H; a.N = p->N;
@@ -180,7 +202,31 @@ static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4
         a.part = (float*)(base + kCounterBytes);
         a.w1 = (float*)(base + kCounterBytes + (size_t)slices * Smax * 8192 * 4);
     }
-    return hip_status(launch_lin_fwd(a, stream, lin_fwd_is_resident(p->N, S, a.bf16) ? 1 : 0));
+    resident = lin_fwd_is_resident(p->N, S, a.bf16) ? 1 : 0;
+    return TTT_OK;
+}
+
+static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* W0,
+                                   const float* eta, float* saved, void* ws, hipStream_t stream) {
+    LinFwdLaunch a;
+    int resident = 0;
+    const ttt_status st = plan_fullbatch(p, K, Q, V, Z, W0, eta, saved, ws, a, resident);
+    if (st != TTT_OK) return st;
+    return hip_status(launch_lin_fwd(a, stream, resident));
+}
+
+// The conv call's launch description (validated arguments).
+static ConvLaunch plan_conv_call(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* w0,
+                                 const float* eta, float* saved, void* ws) {
+    ConvLaunch a{};
+    a.K = K; a.Q = Q; a.V = V; a.Z = Z;
+    a.w0 = w0; a.eta = eta; a.saved = saved;
+    a.B = p->B; a.H = p->H; a.gh = p->grid_h; a.gw = p->grid_w;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    a.cap = device_cus() * conv_resident_per_cu(a.bf16);
+    a.xcd_ok = xcd_local_ok() ? 1 : 0;
+    return a;
 }
 
 ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
@@ -227,15 +273,92 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
     if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
     if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
 
-    ConvLaunch a{};
-    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
-    a.w0 = w0; a.eta = eta; a.saved = saved;
-    a.B = p->B; a.H = p->H; a.gh = p->grid_h; a.gw = p->grid_w;
-    a.bf16 = p->dtype == TTT_BF16;
-    a.ws = ws;
-    a.cap = device_cus() * conv_resident_per_cu(a.bf16);
-    a.xcd_ok = xcd_local_ok() ? 1 : 0;
+    const ConvLaunch a = plan_conv_call(p, v4(K), v4(Q), v4(V), v4(Z), w0, eta, saved, ws);
     return hip_status(launch_conv(a, (hipStream_t)stream));
+}
+
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
+// Layer workspace: [conv counters][linear workspace, at least a counter
+// block][conv partials].  Both counter blocks sit at fixed offsets for
+// every shape, so calls of any shapes can share one zeroed workspace (a
+// counter block never lands where another call left data).
+struct LayerWs {
+    size_t lin_off, conv_part_off, total;
+};
+static LayerWs layer_ws(size_t lws, size_t cws) {
+    LayerWs w{};
+    if (lws == 0 && cws == 0) return w;
+    w.lin_off = kCounterBytes;
+    w.conv_part_off = kCounterBytes + align256(std::max(lws, kCounterBytes));
+    w.total = w.conv_part_off + (cws > kCounterBytes ? cws - kCounterBytes : 0);
+    return w;
+}
+
+size_t ttt_layer_workspace_size(const ttt_problem* lin, const ttt_problem* conv) {
+    return layer_ws(ttt_workspace_size(TTT_OP_LINEAR_FULLBATCH, lin),
+                    ttt_workspace_size(TTT_OP_DWCONV3X3_FULLBATCH, conv)).total;
+}
+
+ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql, ttt_view Vl, const float* W0,
+                               const float* eta_l, ttt_view Zl, const ttt_problem* conv, ttt_view Kc,
+                               ttt_view Qc, ttt_view Vc, const float* w0, const float* eta_c, ttt_view Zc,
+                               void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    bool lnoop = false, cnoop = false;
+    ttt_status st = check_problem(lin, &lnoop);
+    if (st != TTT_OK) return st;
+    if ((st = check_problem(conv, &cnoop)) != TTT_OK) return st;
+    if (conv->grid_h <= 0 || conv->grid_w <= 0 || (int64_t)conv->grid_h * conv->grid_w != conv->N)
+        return TTT_ERR_BAD_SHAPE;
+    Span in[10], out[3];
+    if (!lnoop) {
+        if ((st = check_view(Kl, *lin, &in[0])) != TTT_OK) return st;
+        if ((st = check_view(Ql, *lin, &in[1])) != TTT_OK) return st;
+        if ((st = check_view(Vl, *lin, &in[2])) != TTT_OK) return st;
+        if ((st = check_buf(W0, (size_t)lin->H * lin->d * lin->d * 4, 16, &in[3])) != TTT_OK) return st;
+        if ((st = check_buf(eta_l, (size_t)lin->H * 4, 4, &in[4])) != TTT_OK) return st;
+        if ((st = check_view(Zl, *lin, &out[0])) != TTT_OK) return st;
+    }
+    if (!cnoop) {
+        if ((st = check_view(Kc, *conv, &in[5])) != TTT_OK) return st;
+        if ((st = check_view(Qc, *conv, &in[6])) != TTT_OK) return st;
+        if ((st = check_view(Vc, *conv, &in[7])) != TTT_OK) return st;
+        if ((st = check_buf(w0, (size_t)conv->H * conv->d * 9 * 4, 16, &in[8])) != TTT_OK) return st;
+        if ((st = check_buf(eta_c, (size_t)conv->H * 4, 4, &in[9])) != TTT_OK) return st;
+        if ((st = check_view(Zc, *conv, &out[1])) != TTT_OK) return st;
+    }
+    const size_t lws = lnoop ? 0 : lin_fwd_ws_bytes(lin->B, lin->H, lin->N);
+    const size_t cws = cnoop ? 0 : conv_ws_bytes(conv->B, conv->H, conv->grid_h, conv->grid_w);
+    const LayerWs lw = layer_ws(lws, cws);
+    const size_t need = lw.total;
+    if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
+    // The two outputs may be head ranges of one tensor (the layer's heads
+    // split between the two inner models): compared exactly, not by span.
+    if (!lnoop && !cnoop && lin->B == conv->B && lin->N == conv->N && lin->dtype == conv->dtype &&
+        head_ranges_disjoint(Zl, lin->H, Zc, conv->H, *lin)) {
+        Span zc = out[1];
+        out[1].valid = false;
+        if ((st = check_aliasing(in, 10, out, 3)) != TTT_OK) return st;
+        Span o2[2] = {zc, out[2]};
+        if ((st = check_aliasing(in, 10, o2, 2)) != TTT_OK) return st;
+    } else if ((st = check_aliasing(in, 10, out, 3)) != TTT_OK) {
+        return st;
+    }
+    if (lnoop && cnoop) return TTT_OK;
+
+    char* wsb = (char*)ws;
+    LinFwdLaunch l{};
+    int resident = 0;
+    if (!lnoop &&
+        (st = plan_fullbatch(lin, v4(Kl), v4(Ql), v4(Vl), v4(Zl), W0, eta_l, nullptr,
+                             lws ? wsb + lw.lin_off : nullptr, l, resident)) != TTT_OK)
+        return st;
+    ConvLaunch c{};
+    if (!cnoop) {
+        c = plan_conv_call(conv, v4(Kc), v4(Qc), v4(Vc), v4(Zc), w0, eta_c, nullptr, cws ? wsb : nullptr);
+        c.part = cws ? wsb + lw.conv_part_off : nullptr;
+    }
+    return hip_status(launch_layer(l, resident, c, (hipStream_t)stream));
 }
 
 ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,

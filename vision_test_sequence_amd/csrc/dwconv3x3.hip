@@ -23,375 +23,20 @@
 //            workspace (one per-slice barrier) and every workgroup sums all
 //            S of them in split order into w1 (so all form the same w1);
 //   phase 3  the same sliding window over Q with w1 writes Z.
-#include "common.hpp"
-#include "internal.hpp"
+#include "conv_body.hpp"
 
 #include <atomic>
 
 namespace ttt {
 namespace {
 
-constexpr int kTileBytes = 147456;           // K halo + V + Q halo regions
-constexpr int kW0Bytes = 3 * 1024;           // w0 of the head, 576 floats (3 staging instructions)
-constexpr int kCT = 512;                     // threads per workgroup: 8 waves, 2 per SIMD
-constexpr int kCW = kCT / 64;
-constexpr int kRedFloats = 4 * 64 * 9;       // tap sums of 4 waves (the 8 are paired first)
-constexpr int kSeg = 16;                     // pixels per row segment
-
-struct ConvArgs {
-    View4 K, Q, V, Z;
-    const float* w0;
-    const float* eta;
-    float* saved;
-    float* part;       // [slices][S][64][9]
-    unsigned* cnt;     // [slices]
-    int H, gh, gw;
-    int R, TW;         // tile rows / columns
-    int ny, nx;        // tiles per slice along y / x
-    int S;             // workgroups per slice
-    int tpw;           // tiles per workgroup
-    int slices;        // B * H
-    int xcd;           // XCD-aware grid and XCD-local exchange
-};
-
-typedef __attribute__((address_space(3))) void lds_void;
-
-template <bool BF> struct ConvT;
-template <> struct ConvT<true> {
-    static constexpr int esz = 2;
-    typedef uint16_t raw_t;
-    __device__ static raw_t raw(const char* p) { return *(const uint16_t*)p; }
-    __device__ static float cvt(raw_t v) { return __uint_as_float((uint32_t)v << 16); }
-    __device__ static float ld(const char* p) { return __uint_as_float((uint32_t)*(const uint16_t*)p << 16); }
-    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(f2bf(v), (uint16_t*)p); }
-};
-template <> struct ConvT<false> {
-    static constexpr int esz = 4;
-    typedef float raw_t;
-    __device__ static raw_t raw(const char* p) { return *(const float*)p; }
-    __device__ static float cvt(raw_t v) { return v; }
-    __device__ static float ld(const char* p) { return *(const float*)p; }
-    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(v, (float*)p); }
-};
-
-// Zero pixel: the source of every staged position outside the grid, so
-// the halo reads zero padding with no masks and no clearing pass.
-__device__ __attribute__((aligned(256))) u32x4 conv_zero_px[16];
-
-// Pixels per direct-to-LDS instruction (64 lanes x 16 bytes): LDS row
-// pitches are multiples of it, so every row is whole instructions.
-template <bool BF> constexpr int px_per_instr() { return 64 * 16 / (64 * ConvT<BF>::esz); }
-template <bool BF> __host__ __device__ constexpr int conv_pitch(int px) {
-    return (px + px_per_instr<BF>() - 1) / px_per_instr<BF>() * px_per_instr<BF>();
-}
-
-// Stage `rows` rows of `pitch` pixels whose top-left grid position is
-// (ya, xa) into LDS at dst (row-major, pixel-contiguous), as direct
-// global->LDS loads hidden from the compiler: instruction i of the block
-// (1 KB of LDS) is issued by wave i mod 8.  Positions outside the grid
-// load the zero pixel.  Returns the number of instructions this wave
-// issued; the caller waits for them with vmcnt_at_most().
-template <bool BF>
-__device__ __forceinline__ int stage_rows(char* dst, const char* src, long long sn, int ya, int xa,
-                                          int rows, int pitch, int gh, int gw) {
-    constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
-    const int ninstr = rows * pitch * cpp / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    const char* zero = reinterpret_cast<const char*>(conv_zero_px);
-    int n = 0;
-    for (int i = w; i < ninstr; i += kCW, ++n) {
-        const int q = i * 64 + lane;
-        const int px = q / cpp, sub = q % cpp;
-        const int y = ya + px / pitch, x = xa + px % pitch;
-        const bool in = y >= 0 && y < gh && x >= 0 && x < gw;
-        const char* g = in ? src + ((long long)y * gw + x) * sn + sub * 16 : zero + sub * 16;
-        dma16(g, dst + i * 1024);
-    }
-    return n;
-}
-
-// w0 of one head (576 floats) into LDS: three instructions, by waves 0-2.
-__device__ __forceinline__ int stage_w0(char* dst, const float* w0h) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-    if (w >= 3) return 0;
-    const int q = w * 64 + lane; // 16-byte chunk
-    const char* g = q < 144 ? reinterpret_cast<const char*>(w0h) + q * 16
-                            : reinterpret_cast<const char*>(conv_zero_px);
-    dma16(g, dst + w * 1024);
-    return 1;
-}
-
-// One workgroup per CU (its LDS) of 8 waves, two per SIMD: while one
-// waits for its LDS reads the other computes.
 template <bool BF, bool XC>
 __global__ __launch_bounds__(kCT, 1) void conv_kernel(ConvArgs a) {
-    using T = ConvT<BF>;
-    constexpr int pb = 64 * T::esz; // bytes per pixel
     __shared__ __attribute__((aligned(16))) char lds[kW0Bytes + kTileBytes];
     __shared__ float red[kRedFloats];
     __shared__ float w1s[64 * 9];
     __shared__ int s_chk; // outcome of the exchange (slice_bad)
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index, uniform
-    const SliceSplit ss = XC ? map_block_xcc(blockIdx.x, a.S, xcc_id()) : map_block(blockIdx.x, a.S, 0);
-    const int slice = ss.slice, split = ss.split;
-    if (slice >= a.slices) return; // padding block of the XCD-aware grid
-    if (XC && a.S > 1 && tid == 0) placement_note(counter_at(a.cnt, slice), split);
-    bool poison = false; // NaN output for a failed exchange
-    const int b = slice / a.H, h = slice % a.H;
-    const int gh = a.gh, gw = a.gw, N = gh * gw;
-    const int ntile = a.ny * a.nx;
-    const int tb = split * a.tpw, te = min(ntile, tb + a.tpw);
-
-    const char* Kp = (const char*)a.K.ptr + (b * a.K.sb + h * a.K.sh) * (long long)T::esz;
-    const char* Vp = (const char*)a.V.ptr + (b * a.V.sb + h * a.V.sh) * (long long)T::esz;
-    const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)T::esz;
-    char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)T::esz;
-    const long long Ksn = a.K.sn * T::esz, Vsn = a.V.sn * T::esz;
-    const long long Qsn = a.Q.sn * T::esz, Zsn = a.Z.sn * T::esz;
-
-    // LDS rows are at least kSeg pixels wide (plus the halo), so a row
-    // segment of kSeg pixels never reads past its row; pitches are whole
-    // staging instructions; positions outside the grid hold zeros (K, Q) or
-    // are masked (V)
-    const int KP = conv_pitch<BF>(max(a.TW, kSeg) + 2), VP = conv_pitch<BF>(max(a.TW, kSeg));
-    char* W0s = lds;
-    char* Ks = lds + kW0Bytes;
-    char* Vs = Ks + (a.R + 2) * KP * pb;
-    char* Qs = Vs + a.R * VP * pb;
-    const bool q_early = (te - tb) == 1;
-
-    float gacc[9];
-#pragma unroll
-    for (int t = 0; t < 9; ++t) gacc[t] = 0.f;
-    float wt[9];
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wt[t] = 0.f;
-    float pf = 0.f; // L2 prefetch of this workgroup's partial (see below)
-    unsigned rel = 0; // thread 0: the counter before this workgroup's release
-
-    // ------------------------------------------------------------ phase 1
-    for (int tile = tb; tile < te; ++tile) {
-        const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
-        const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
-        // always the nominal tile shape, so the LDS pitches are fixed; the
-        // part of an edge tile outside the grid is zero or masked.  (The
-        // whole chip issues its loads at once and the memory system does
-        // not serve them in issue order, so staging the rows in the order
-        // they are needed and starting on the first ones measured no
-        // earlier start.)
-        if (tile == tb) stage_w0(W0s, a.w0 + (long long)h * 576);
-        stage_rows<BF>(Ks, Kp, Ksn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
-        stage_rows<BF>(Vs, Vp, Vsn, y0, x0, a.R, VP, gh, gw);
-        int nq = 0;
-        if (q_early) nq = stage_rows<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
-        vmcnt_at_most(nq); // this wave's K and V (and w0) loads have landed
-        lds_barrier();     // ... and every wave's
-        if (tile == tb) {
-#pragma unroll
-            for (int t = 0; t < 9; ++t) wt[t] = reinterpret_cast<const float*>(W0s)[lane * 9 + t];
-            // A store to a line that is not in the XCD's L2 goes on to
-            // memory without allocating it, and the slice's other
-            // workgroups would then read the partial from memory: a
-            // device-scope load of each of its 18 lines (it fills L2, not
-            // L1) makes the later stores and reads hit L2.
-            if (XC && a.S > 1 && w == 0)
-                pf = xload(a.part + ((long long)slice * a.S + split) * 576 + min(lane, 17) * 32);
-        }
-
-        const int nsx = (tw + kSeg - 1) / kSeg;
-        {
-            for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
-                const int r = sgi / nsx;
-                // Segment k of a row covers pixels [16k, 16k+16); the last one is
-                // shifted left to end at the row's end (its first pixels, done by
-                // the previous segment, are masked) -- or, in a row narrower than
-                // a segment, starts at 0 and masks the pixels past the row.  Every
-                // LDS value a segment needs is read up front at fixed offsets
-                // from one base, then the 3x3 window slides in registers.
-                const int k = sgi % nsx;
-                const int xs = min(k * kSeg, max(tw - kSeg, 0));
-                const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
-                const char* kb = Ks + ((r * KP + xs) * 64 + lane) * T::esz;
-                const char* vb = Vs + ((r * VP + xs) * 64 + lane) * T::esz;
-                typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-#pragma unroll
-                    for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * KP + j) * 64) * T::esz);
-#pragma unroll
-                for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
-                __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
-                float kr[3][kSeg + 2], vv[kSeg];
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-#pragma unroll
-                    for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
-#pragma unroll
-                for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
-#pragma unroll
-                for (int x = 0; x < kSeg; ++x) {
-                    float p = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 3; ++jj) p += wt[i * 3 + jj] * kr[i][x + jj];
-                    const float rv = (x >= lo && x < hi) ? p - vv[x] : 0.f;
-#pragma unroll
-                    for (int i = 0; i < 3; ++i)
-#pragma unroll
-                        for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] += rv * kr[i][x + jj];
-                }
-            }
-        }
-        lds_barrier(); // every wave is done with this tile's K and V
-    }
-
-    // fixed-order sum of the 8 waves' tap sums: waves w and w + 4 first,
-    // then the four pair sums
-    if (w >= 4) {
-#pragma unroll
-        for (int t = 0; t < 9; ++t) red[((w - 4) * 64 + lane) * 9 + t] = gacc[t];
-    }
-    __syncthreads();
-    if (w < 4) {
-#pragma unroll
-        for (int t = 0; t < 9; ++t) red[(w * 64 + lane) * 9 + t] = gacc[t] + red[(w * 64 + lane) * 9 + t];
-    }
-    __syncthreads();
-    const float eta = a.eta[h];
-    const float scale = 2.0f / (float)N;
-    if (a.S == 1) {
-        if (w == 0) {
-            for (int t = 0; t < 9; ++t) {
-                const float s = ((red[lane * 9 + t] + red[(64 + lane) * 9 + t]) + red[(128 + lane) * 9 + t]) +
-                                red[(192 + lane) * 9 + t];
-                const float gv = scale * s;
-                w1s[lane * 9 + t] = wt[t] - eta * gv;
-                if (a.saved) a.saved[((long long)slice * 64 + lane) * 9 + t] = gv;
-            }
-        }
-        __syncthreads();
-    } else {
-        float* P = a.part + ((long long)slice * a.S + split) * 576;
-        unsigned* cnt = counter_at(a.cnt, slice);
-        asm volatile("" ::"v"(pf)); // the prefetch has completed before the stores
-        for (int e = tid; e < 576; e += kCT) {
-            const int c = e / 9, t = e % 9;
-            const float v = ((red[c * 9 + t] + red[(64 + c) * 9 + t]) + red[(128 + c) * 9 + t]) +
-                            red[(192 + c) * 9 + t];
-            if constexpr (XC) P[e] = v;
-            else xstore(P + e, v);
-        }
-        slice_barrier(cnt, (unsigned)a.S);
-        SliceWords sw{}; // thread 0; loaded alongside the partials
-        if (tid == 0) sw = slice_words(cnt);
-        float gv[4];
-        // Every workgroup sums all S partials itself (576 floats each, in
-        // a fixed order, so all of them form the same w1): one barrier, and
-        // no second round trip for w1.  Threads t < 432 share the loads:
-        // element group e4 = t % 144 (floats 4 e4..4 e4+3) of the splits in
-        // group t / 144 of three (consecutive runs of ceil(S/3) <= 11
-        // splits, S <= 32: the grid holds at most 256 workgroups of >= 8
-        // slices); the three group sums meet in LDS.
-        float* gsum = red; // [3][576], free once the partial is published
-        if (tid < 432) {
-            const int e4 = tid % 144, q = tid / 144;
-            const int G = (a.S + 2) / 3, s0 = q * G, s1 = min(a.S, s0 + G);
-            const float* src = a.part + (long long)slice * a.S * 576 + 4 * e4;
-            f32x4 v[11];
-#pragma unroll
-            for (int k = 0; k < 11; ++k) {
-                if (k < G) { // uniform
-                    const float* p = src + min(s0 + k, s1 - 1) * 576;
-                    if constexpr (XC) v[k] = *reinterpret_cast<const f32x4*>(p);
-                    else v[k] = f32x4{xload(p), xload(p + 1), xload(p + 2), xload(p + 3)};
-                }
-            }
-            f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int k = 0; k < 11; ++k)
-                if (k < G && s0 + k < s1) acc += v[k];
-            *reinterpret_cast<f32x4*>(gsum + q * 576 + 4 * e4) = acc;
-        }
-        __syncthreads();
-        if (tid < 144) {
-            const f32x4 g0 = *reinterpret_cast<const f32x4*>(gsum + 4 * tid);
-            const f32x4 g1 = *reinterpret_cast<const f32x4*>(gsum + 576 + 4 * tid);
-            const f32x4 g2 = *reinterpret_cast<const f32x4*>(gsum + 1152 + 4 * tid);
-            const f32x4 acc = (g0 + g1) + g2;
-            const float* w0e = reinterpret_cast<const float*>(W0s) + 4 * tid; // w0 of the head, staged
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                gv[k] = scale * acc[k];
-                w1s[4 * tid + k] = w0e[k] - eta * gv[k];
-            }
-        }
-        if (tid == 0) s_chk = slice_bad(sw, XC ? a.S : 0) ? 1 : 0;
-        __syncthreads();
-        poison = s_chk != 0;
-        if (a.saved && split == 0 && tid < 144) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                a.saved[(long long)slice * 576 + 4 * tid + k] = poison ? __builtin_nanf("") : gv[k];
-        }
-        // The counter's release, once the partials are read (vector-memory
-        // results return in issue order across the CU's waves, so an
-        // atomic on the slice's contended counter line issued earlier
-        // would hold up their loads); its result (does this workgroup
-        // complete the count and reset it?) is used at the end.
-        if (tid == 0) rel = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    if (q_early && a.S == 1) { // (with S > 1 the slice barrier drained every wave)
-        drain_vmem();           // this wave's Q loads have landed
-        __syncthreads();        // ... and every wave's
-    }
-    float wq[9];
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wq[t] = w1s[lane * 9 + t];
-
-    // ------------------------------------------------------------ phase 3
-    for (int tile = tb; tile < te; ++tile) {
-        const int y0 = (tile / a.nx) * a.R, x0 = (tile % a.nx) * a.TW;
-        const int rr = min(a.R, gh - y0), tw = min(a.TW, gw - x0);
-        if (!q_early) {
-            stage_rows<BF>(Qs, Qp, Qsn, y0 - 1, x0 - 1, a.R + 2, KP, gh, gw);
-            drain_vmem();
-            __syncthreads();
-        }
-        const int nsx = (tw + kSeg - 1) / kSeg;
-        for (int sgi = w; sgi < rr * nsx; sgi += kCW) {
-            const int r = sgi / nsx, k = sgi % nsx; // segments as in phase 1
-            const int xs = min(k * kSeg, max(tw - kSeg, 0));
-            const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
-            const int y = y0 + r;
-            const char* qb = Qs + ((r * KP + xs) * 64 + lane) * T::esz;
-            char* zrow = Zp + ((long long)y * gw + x0 + xs) * Zsn + lane * T::esz;
-            typename T::raw_t qraw[3][kSeg + 2];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * KP + j) * 64) * T::esz);
-            __builtin_amdgcn_sched_barrier(0);
-            float qr[3][kSeg + 2];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) qr[i][j] = T::cvt(qraw[i][j]);
-#pragma unroll
-            for (int x = 0; x < kSeg; ++x) {
-                float z = 0.f;
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-#pragma unroll
-                    for (int jj = 0; jj < 3; ++jj) z += wq[i * 3 + jj] * qr[i][x + jj];
-                if (x >= lo && x < hi) T::st(zrow + x * Zsn, poison ? __builtin_nanf("") : z);
-            }
-        }
-        if (!q_early) __syncthreads();
-    }
-    if (a.S > 1 && tid == 0 && rel == 2u * a.S - 1) slice_reset(counter_at(a.cnt, slice));
+    conv_body<BF, XC>(a, ConvLds{lds, nullptr, red, w1s, &s_chk});
 }
 
 struct ConvPlan {
@@ -457,12 +102,12 @@ int conv_resident_per_cu(int bf16) {
     return n;
 }
 
-hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
+void conv_prepare(const ConvLaunch& l, ConvArgs& a, unsigned& grid) {
     const long long slices = (long long)l.B * l.H;
     const int esz = l.bf16 ? 2 : 4;
     const int cap = l.cap < 256 ? l.cap : 256; // the workspace is sized for 256
     ConvPlan p = plan_conv((int)slices, l.gh, l.gw, esz, cap);
-    ConvArgs a{};
+    a = ConvArgs{};
     a.K = l.K; a.Q = l.Q; a.V = l.V; a.Z = l.Z;
     a.w0 = l.w0; a.eta = l.eta; a.saved = l.saved;
     a.H = l.H; a.gh = l.gh; a.gw = l.gw;
@@ -471,17 +116,29 @@ hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
     a.xcd = (p.S > 1 && l.xcd_ok) ? 1 : 0;
     if (p.S > 1) {
         // workspace layout as conv_ws_bytes: fixed counter block, partials
-        if (slices > kMaxBarrierSlices) return hipErrorInvalidValue; // unreachable: S > 1
         char* base = (char*)l.ws;
         a.cnt = (unsigned*)base;
-        a.part = (float*)(base + kCounterBytes);
+        a.part = l.part ? (float*)l.part : (float*)(base + kCounterBytes);
     }
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
-    const dim3 grid((unsigned)(gslices * p.S)), block(kCT);
+    grid = (unsigned)(gslices * p.S);
+}
+
+hipError_t conv_launch_prepared(const ConvArgs& a0, unsigned grid, int bf16, hipStream_t stream) {
+    ConvArgs a = a0;
     void* args[] = {&a};
-    const void* fn = a.xcd ? (l.bf16 ? (const void*)conv_kernel<true, true> : (const void*)conv_kernel<false, true>)
-                           : (l.bf16 ? (const void*)conv_kernel<true, false> : (const void*)conv_kernel<false, false>);
-    return hipLaunchKernel(fn, grid, block, args, 0, stream);
+    const void* fn = a.xcd ? (bf16 ? (const void*)conv_kernel<true, true> : (const void*)conv_kernel<false, true>)
+                           : (bf16 ? (const void*)conv_kernel<true, false> : (const void*)conv_kernel<false, false>);
+    return hipLaunchKernel(fn, dim3(grid), dim3(kCT), args, 0, stream);
+}
+
+hipError_t launch_conv(ConvLaunch l, hipStream_t stream) {
+    const long long slices = (long long)l.B * l.H;
+    ConvArgs a;
+    unsigned grid = 0;
+    conv_prepare(l, a, grid);
+    if (a.S > 1 && slices > kMaxBarrierSlices) return hipErrorInvalidValue; // unreachable: S > 1
+    return conv_launch_prepared(a, grid, l.bf16, stream);
 }
 
 } // namespace ttt

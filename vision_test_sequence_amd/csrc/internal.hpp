@@ -42,12 +42,16 @@ struct ConvLaunch {
     int B, H, gh, gw;
     int bf16;
     void* ws;         // conv_ws_bytes(...) bytes, zero-filled before first use
+    void* part;       // null: the partials follow the counters in ws; else their own region
     int cap;          // resident workgroups of the device for the conv kernel
     int xcd_ok;       // the device is an MI355X in whole-device (SPX) mode
 };
 size_t conv_ws_bytes(int B, int H, int gh, int gw);
 hipError_t launch_conv(ConvLaunch a, hipStream_t stream);
 int conv_resident_per_cu(int bf16);
+
+// ---- one layer: linear heads and conv heads (one launch when they fit)
+hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch c, hipStream_t stream);
 
 // ---- mini-batch scans -------------------------------------------------
 struct ScanLaunch {

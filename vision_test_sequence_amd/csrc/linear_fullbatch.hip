@@ -32,6 +32,7 @@
 //             apply step with a short prefetch.
 // fp32 inputs take the same paths with 16x16x4 fp32 MFMAs.
 #include "common.hpp"
+#include "conv_body.hpp"
 #include "internal.hpp"
 
 #include <atomic>
@@ -792,11 +793,12 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
 // float4 t % n4 of the reducer's block over the four splits of group
 // t / n4 (split order), and the S/4 group sums meet in LDS (group order);
 // with S <= 4 every thread sums its float4s over all splits.  W0 is read
-// from its staged copy (g_lds).  Every wave of the workgroup calls this
-// (with S >= 8 it holds one workgroup barrier).
+// from w0src (pitch w0p: its staged copy, g_lds, or global memory); the
+// group sums use 4 KB of LDS at lds + gsum_byte.  Every wave of the
+// workgroup calls this (with S >= 8 it holds one workgroup barrier).
 template <int S>
 __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h, char* lds,
-                                         bool active) {
+                                         bool active, const float* w0src, int w0p, int gsum_byte) {
     constexpr int R = 4096 / S, n4 = R / 4;
     constexpr int NG = S >= 8 ? S / 4 : 1; // split groups
     constexpr int SG = S / NG;             // splits per group
@@ -804,7 +806,6 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
     const float eta = a.eta[h];
     const float scale = 2.0f / (float)a.N;
     const f32x4* blk = reinterpret_cast<const f32x4*>(a.part + (long long)slice * S * 4096 + (long long)split * S * R);
-    const float* w0s = g_lds(lds).w0s;
     bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
     auto finish = [&](int t4, const f32x4& acc) __attribute__((always_inline)) {
         const int P = split * R + 4 * t4, q = P >> 8, e = P & 255;
@@ -812,7 +813,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
         const int rb = q >> 2, c = 32 * ((q >> 1) & 1) + 16 * (q & 1) + ((e >> 2) & 15), r0 = perm_row(rb, mq);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            w1b[w1_frag_index(r0 + i, c)] = f2bf(w0s[(r0 + i) * MP + c] - eta * (scale * acc[i]));
+            w1b[w1_frag_index(r0 + i, c)] = f2bf(w0src[(r0 + i) * w0p + c] - eta * (scale * acc[i]));
     };
     if constexpr (NG == 1) {
         if (active) {
@@ -828,7 +829,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
             }
         }
     } else {
-        f32x4* gs = reinterpret_cast<f32x4*>(lds + kGSumByte); // [NG][n4]
+        f32x4* gs = reinterpret_cast<f32x4*>(lds + gsum_byte); // [NG][n4]
         if (active) {
             const int t4 = tid % n4, gq = tid / n4;
             f32x4 v[SG];
@@ -961,12 +962,13 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     if (gx) {
         unsigned* cnt = counter_at(a.cnt, c.slice);
         slice_barrier(cnt, (unsigned)a.S);
+        const float* w0g = g_lds(lds).w0s;
         switch (a.S) {
-        case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, true); break;
-        case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, true); break;
-        case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, true); break;
-        case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, true); break;
-        default: reduce_g<32>(a, c.slice, c.split, c.h, lds, true); break;
+        case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
+        case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
+        case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
+        case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
+        default: reduce_g<32>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
         }
         slice_barrier(cnt, 2u * a.S);
         if (tid == 0) sw = slice_words(cnt);
@@ -1028,20 +1030,26 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
 // each); the first four form and publish G_s, and all eight share the
 // apply.
 constexpr int kThreads8 = 512;
+constexpr int kGxLds = 3 * LinCfg<true>::tmax * 8 * 16 + 16384; // K, V, spare, Q
 
-__global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch a) {
+// LDS map of the body: K [0, TB), V [TB, 2 TB), Q [2 TB + 16 KB, 3 TB + 16 KB);
+// the G phase in [0, 35840) (g_lds); the reduce's group sums (4 KB) at
+// gsum_byte and the exchange outcome at chk_byte, both outside Q and the
+// G phase.  w0_lds: the reduce reads W0 from its staged copy (else from
+// global memory).
+__device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, int gsum_byte, int chk_byte,
+                                            bool w0_lds) {
     using Cfg = LinCfg<true>;
     constexpr int RS = Cfg::row_slots;
     constexpr int TB = Cfg::tmax * RS * 16;
     constexpr int SPARE = 16384;
-    __shared__ __attribute__((aligned(16))) char lds[3 * TB + SPARE];
     char* Ks = lds;
     char* Vs = lds + TB;
     char* Qs = lds + 2 * TB + SPARE;
 
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6); // wave index 0..7, uniform
-    int* const chk = reinterpret_cast<int*>(lds + kChkByte);
+    int* const chk = reinterpret_cast<int*>(lds + chk_byte);
     const SliceCtx c = slice_ctx<true, true>(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
     if (tid == 0) placement_note(counter_at(a.cnt, c.slice), c.split);
@@ -1125,12 +1133,14 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
     slice_barrier(cnt, (unsigned)a.S, w < 4);
     // waves 0-3 reduce (waves 4-7 have Q loads in flight, which a gather of
     // theirs would queue behind)
+    const float* w0src = w0_lds ? L.w0s : a.W0 + (long long)c.h * 4096;
+    const int w0p = w0_lds ? MP : 64;
     switch (a.S) {
-    case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, w < 4); break;
-    case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, w < 4); break;
-    case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, w < 4); break;
-    case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4); break;
-    default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4); break;
+    case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
+    case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
+    case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
+    case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
+    default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
     }
     slice_barrier(cnt, 2u * a.S, w < 4);
     SliceWords sw{};
@@ -1159,6 +1169,54 @@ __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch
     release_end(a, c.slice, rel);
 }
 static_assert(4 * 64 * kAP + 64 * MP * 4 <= 2 * LinCfg<true>::tmax * 8 * 16, "G-phase LDS inside the K/V regions");
+
+__global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGxLds];
+    lin_gx_body(a, lds, kGSumByte, kChkByte, true);
+}
+
+// ------------------------------------------------------ fused layer --
+// The linear heads (lin_gx_body) and the depthwise-conv heads (conv_body,
+// one tile per workgroup) of one layer in one launch.  Workgroup i does
+// the linear split of virtual block i, then the conv split of the same
+// block (both XCD-local exchanges): one launch instead of two, and a
+// workgroup's conv work starts as soon as its linear work is done.  (Its
+// conv loads cannot usefully start earlier: issued during the linear
+// exchange they held up its barrier polls and gathers, whose results
+// return behind them; issued during the linear apply, their issue stalled
+// it.  Both measured slower than this order.)  LDS map: the linear
+// kernel's, then conv w0 + K + V [0, ckv); at ckv the linear reduce's
+// group sums and exchange outcome, later the conv's wave sums, w1 and
+// outcome; the conv Q halo at the top once the linear apply is done.
+struct LayerArgs {
+    LinFwdLaunch lin;
+    ConvArgs conv;
+    int ckv; // conv_kv_bytes of the conv tile
+};
+constexpr int kLayerScratch = (kRedFloats + 576) * 4 + 256; // conv wave sums, w1, outcome
+static_assert(4096 + 256 <= kLayerScratch, "linear group sums and outcome inside the layer scratch");
+
+__global__ __launch_bounds__(kThreads8, 1) void layer_fused(LayerArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kGxLds];
+    const int ckv = a.ckv;
+    float* scratch = reinterpret_cast<float*>(lds + ckv);
+    const ConvLds CL{lds, lds + kGxLds - conv_q_bytes<true>(a.conv.R, a.conv.TW), scratch, scratch + kRedFloats,
+                     reinterpret_cast<int*>(scratch + kRedFloats + 576)};
+    lin_gx_body(a.lin, lds, ckv, ckv + 4096, true);
+    lds_barrier(); // the linear apply is done with its Q rows
+    conv_body<true, true>(a.conv, CL);
+}
+
+// Fusable: the linear heads take lin_fwd_resident_gx, the conv heads one
+// tile per workgroup over an XCD-local exchange, and the LDS map fits.
+bool layer_fusable(const LinFwdLaunch& l, int resident, const ConvArgs& c, int cbf16) {
+    using Cfg = LinCfg<true>;
+    constexpr int lin_q = 2 * Cfg::tmax * 8 * 16 + 16384; // start of the linear Q rows
+    if (!(resident && l.xcd && l.bf16 && l.S > 1 && !l.saved && l.Z.ptr)) return false;
+    if (!(cbf16 && c.xcd && c.S > 1 && c.tpw == 1 && c.Z.ptr)) return false;
+    const int ckv = conv_kv_bytes<true>(c.R, c.TW), cq = conv_q_bytes<true>(c.R, c.TW);
+    return ckv % 16 == 0 && ckv + kLayerScratch <= lin_q && ckv + kLayerScratch <= kGxLds - cq;
+}
 
 // resident kernel, floats below the Q region: wave sums + [A; C] (phase 1),
 // gather staging / W0 / W1 (phase 2)
@@ -1410,6 +1468,26 @@ hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
         else fn = a.bf16 ? (const void*)lin_fwd_stream<true, false> : (const void*)lin_fwd_stream<false, false>;
     }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch cl, hipStream_t stream) {
+    ConvArgs c;
+    unsigned cgrid = 0;
+    const bool conv_on = (long long)cl.B * cl.H > 0;
+    const bool lin_on = (long long)l.B * l.H > 0;
+    if (conv_on) conv_prepare(cl, c, cgrid);
+    if (lin_on && conv_on && layer_fusable(l, resident, c, cl.bf16)) {
+        LayerArgs a{l, c, conv_kv_bytes<true>(c.R, c.TW)};
+        const long long lgrid = (((long long)l.B * l.H + 7) / 8 * 8) * l.S;
+        const unsigned grid = (unsigned)(lgrid > cgrid ? lgrid : cgrid);
+        void* args[] = {&a};
+        return hipLaunchKernel((const void*)layer_fused, dim3(grid), dim3(kThreads8), args, 0, stream);
+    }
+    if (lin_on) {
+        const hipError_t e = launch_lin_fwd(l, stream, resident);
+        if (e != hipSuccess) return e;
+    }
+    return conv_on ? conv_launch_prepared(c, cgrid, cl.bf16, stream) : hipSuccess;
 }
 
 } // namespace ttt
