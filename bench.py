@@ -3,17 +3,19 @@
 
 One step = one pass of the layer's hot path over one batch of the
 1248x1248 image stack (B=8, H=3 heads of d=64, 78x78 = 6084 tokens, bf16):
-heads 0-1 take one full-batch step of the linear inner model
-(ttt_linear_fullbatch), head 2 one full-batch step of the 3x3 depthwise
-inner model (ttt_dwconv3x3_fullbatch), each followed by its apply.
+heads 0-1 take one full-batch step of the linear inner model, head 2 one
+full-batch step of the 3x3 depthwise inner model, each followed by its
+apply -- one ttt_layer_fullbatch call, which runs them as one kernel
+(layer_fused).  The two kernels of the separate calls (ttt_linear_fullbatch,
+ttt_dwconv3x3_fullbatch) are timed too.
 
 Inputs are resident in HBM before timing and rotate over 5 independent sets
 (> 256 MB together, so the 256 MB Infinity Cache cannot hold them between
 uses).  Prints one JSON line: whole-layer tokens/s, the roofline of the
-dominant kernel (the linear step), the other rows of the path on their own
-workloads (the mini-batch bidirectional scan at 1280x1280, the forward and
-backward of the linear step at ViT-B 1024x1024), and the fp64 oracle timed
-on the host.
+dominant kernel (the step's one kernel), the other rows of the path on their
+own workloads (the mini-batch bidirectional scan at 1280x1280, the forward
+and backward of the linear step at ViT-B 1024x1024), and the fp64 oracle
+timed on the host.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -36,12 +38,14 @@ BWD_WORKLOAD = "vitb_1024_fwdbwd_bf16"
 METRIC = "TTT-layer tokens/s at N=6084, H=3, d=64 bf16; % MFMA / HBM roofline"
 NSETS = 5
 ROOT = os.path.dirname(os.path.abspath(__file__))
-# HBM bytes per launch of the linear kernel from rocprofv3 FETCH_SIZE /
+# HBM bytes per launch of the layer kernel from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE runs, stored with the hash of the sources they were taken on
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lin_fwd_resident_gx_vit3t_1248_traffic.md")
-LIN_SOURCES = ["vision_test_sequence_amd/csrc/linear_fullbatch.hip",
-               "vision_test_sequence_amd/csrc/common.hpp",
-               "vision_test_sequence_amd/csrc/api.cpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "layer_fused_vit3t_1248_traffic.md")
+KERNEL_SOURCES = ["vision_test_sequence_amd/csrc/linear_fullbatch.hip",
+                  "vision_test_sequence_amd/csrc/conv_body.hpp",
+                  "vision_test_sequence_amd/csrc/dwconv3x3.hip",
+                  "vision_test_sequence_amd/csrc/common.hpp",
+                  "vision_test_sequence_amd/csrc/api.cpp"]
 COPY_BYTES = 256 << 20           # plain copy kernel run once for the counter scale
 
 
@@ -49,15 +53,15 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="skip the scan and backward rows")
     return ap.parse_args()
 
 
-def lin_source_hash() -> str:
+def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in LIN_SOURCES:
+    for f in KERNEL_SOURCES:
         with open(os.path.join(ROOT, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -72,7 +76,7 @@ def measured_traffic():
         return None
     m = re.search(r"source-hash:\s*([0-9a-f]+)", txt)
     t = re.search(r"traffic-bytes-per-launch:\s*([0-9.eE+]+)", txt)
-    if not m or not t or m.group(1) != lin_source_hash():
+    if not m or not t or m.group(1) != kernel_source_hash():
         return None
     return float(t.group(1))
 
@@ -201,6 +205,11 @@ def main():
                                    g["w0c"], g["etac"], w.grid_h, w.grid_w, Z=g["Z"][:, c0:c1])
 
     def step(g):
+        vt.ttt_layer_fullbatch(g["K"][:, l0:l1], g["Q"][:, l0:l1], g["V"][:, l0:l1], g["W0l"], g["etal"],
+                               g["K"][:, c0:c1], g["Q"][:, c0:c1], g["V"][:, c0:c1], g["w0c"], g["etac"],
+                               w.grid_h, w.grid_w, Zl=g["Z"][:, l0:l1], Zc=g["Z"][:, c0:c1])
+
+    def separate(g):
         linear(g)
         conv(g)
 
@@ -209,13 +218,15 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: K layer steps rotating over the input sets, bracketed by
-    # a synchronisation and HIP events on the launch stream
+    # a synchronisation and HIP events on the launch stream; a step is one
+    # launch, so this is also the layer kernel's average launch duration
     ms_step = time_calls(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
-    # each kernel on its own: back-to-back launches on the same stream,
-    # rotating over the same sets (average launch duration)
+    # the two kernels of the separate calls: back-to-back launches on the
+    # same stream, rotating over the same sets (average launch duration)
     nk = max(args.steps, 200)
     lin_ms = time_calls(torch, lambda i: linear(sets[i % NSETS][1]), nk)
     conv_ms = time_calls(torch, lambda i: conv(sets[i % NSETS][1]), nk)
+    sep_ms = time_calls(torch, lambda i: separate(sets[i % NSETS][1]), nk)
     # warm reference: the same buffers every step (Infinity-Cache resident)
     warm_ms_step = time_calls(torch, lambda i: step(sets[0][1]), args.steps)
 
@@ -229,7 +240,7 @@ def main():
 
     tokens = w.B * w.N
     lin_bytes, conv_bytes, lin_flops, conv_flops = layer_algorithmic(w)
-    achieved = lin_bytes / (lin_ms * 1e-3) / 1e9
+    achieved = (lin_bytes + conv_bytes) / (ms_step * 1e-3) / 1e9
     out = {
         "metric": METRIC,
         "value": tokens / (ms_step * 1e-3),
@@ -245,30 +256,33 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{WORKLOAD}: B={w.B} images, H={w.H} heads (0-1 linear full-batch, "
-                        f"2 dwconv3x3 full-batch), {w.grid_h}x{w.grid_w} grid N={w.N}, d={w.d}",
+                        f"2 dwconv3x3 full-batch, one ttt_layer_fullbatch call), "
+                        f"{w.grid_h}x{w.grid_w} grid N={w.N}, d={w.d}",
             "global_batch": w.B,
             "seq_len": w.N,
             "input_sets_rotated": NSETS,
         },
         "roofline": {
-            "kernel": "lin_fwd_resident_gx (ttt_linear_fullbatch, heads 0-1, B=8, N=6084)",
+            "kernel": "layer_fused (ttt_layer_fullbatch: heads 0-1 linear, head 2 dwconv3x3, B=8, N=6084)",
             "bound": "hbm",
             "achieved": achieved,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": measured_traffic(),
-            "algorithmic_bytes": lin_bytes,
-            "avg_launch_us": lin_ms * 1e3,
+            "algorithmic_bytes": lin_bytes + conv_bytes,
+            "avg_launch_us": ms_step * 1e3,
         },
         "kernels": {
+            "separate_calls_us_per_step": sep_ms * 1e3,
             "linear_us": lin_ms * 1e3,
+            "linear_gbs": lin_bytes / (lin_ms * 1e-3) / 1e9,
+            "linear_hbm_frac": lin_bytes / (lin_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "linear_tflops": lin_flops / (lin_ms * 1e-3) / 1e12,
             "linear_mfma_frac": lin_flops / (lin_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
             "dwconv_us": conv_ms * 1e3,
             "dwconv_gbs": conv_bytes / (conv_ms * 1e-3) / 1e9,
             "dwconv_hbm_frac": conv_bytes / (conv_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "layer_hbm_frac": (lin_bytes + conv_bytes) / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "warm_ms_per_step": warm_ms_step,
         },
     }
@@ -294,7 +308,7 @@ def main():
                                                eta[c0:c1], w.grid_h, w.grid_w)
             reps += 1
             elapsed = time.perf_counter() - t0
-            if elapsed >= 5.0 or reps >= 30:
+            if elapsed >= 10.0:
                 break
         out["cpu_baseline"] = {
             "value": tokens * reps / elapsed,
