@@ -217,7 +217,7 @@ __device__ __forceinline__ void dma16(const void* src, const void* lds_dst) {
 // outstanding (they complete in issue order).  n of 63 and above (the
 // counter's limit) waits for none; n <= 0 waits for all.
 __device__ __forceinline__ void vmcnt_at_most(int n) {
-    switch (n) {
+    switch (__builtin_amdgcn_readfirstlane(n)) { // wave-uniform
 #define TTT_VMCNT(k) case k: asm volatile("s_waitcnt vmcnt(" #k ")" ::: "memory"); break;
 #define TTT_VMCNT8(k) TTT_VMCNT(k) TTT_VMCNT(k + 1) TTT_VMCNT(k + 2) TTT_VMCNT(k + 3) \
     TTT_VMCNT(k + 4) TTT_VMCNT(k + 5) TTT_VMCNT(k + 6) TTT_VMCNT(k + 7)

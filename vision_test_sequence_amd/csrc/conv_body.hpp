@@ -7,6 +7,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <type_traits>
+
 namespace ttt {
 
 struct ConvArgs {
@@ -80,7 +82,7 @@ __device__ __forceinline__ int stage_rows(char* dst, const char* src, long long 
                                           int rows, int pitch, int gh, int gw) {
     constexpr int cpp = 64 * ConvT<BF>::esz / 16; // 16-byte chunks per pixel
     const int ninstr = rows * pitch * cpp / 64;
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const char* zero = reinterpret_cast<const char*>(conv_zero_px);
     int n = 0;
     for (int i = w; i < ninstr; i += kCW, ++n) {
@@ -96,13 +98,103 @@ __device__ __forceinline__ int stage_rows(char* dst, const char* src, long long 
 
 // w0 of one head (576 floats) into LDS: three instructions, by waves 0-2.
 __device__ __forceinline__ int stage_w0(char* dst, const float* w0h) {
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (w >= 3) return 0;
     const int q = w * 64 + lane; // 16-byte chunk
     const char* g = q < 144 ? reinterpret_cast<const char*>(w0h) + q * 16
                             : reinterpret_cast<const char*>(conv_zero_px);
     dma16(g, dst + w * 1024);
     return 1;
+}
+
+// bf16 -> fp32 without conversion instructions: ds_read_u16_d16_hi writes a
+// register's high half and keeps its low half, so a register whose low half
+// is zero holds the exact fp32 value of the bf16 it receives.  The callers'
+// registers start at zero and receive nothing else.  Each asm block issues
+// its loads and waits for them itself, so every output is complete when the
+// block ends.  Rows are LDS addresses of 18 consecutive pixels (128-byte
+// pitch: one bf16 per lane of 64 channels).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const char*)p;
+}
+// three rows of 18 pixels (K halo) and 16 pixels of one row (V)
+__device__ __forceinline__ void lds_window_kv(float (&k)[3][kSeg + 2], float (&v)[kSeg], const char* k0,
+                                              const char* k1, const char* k2, const char* v0) {
+    static_assert(kSeg == 16, "the asm below is written for 16-pixel segments");
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %70 offset:0\n\t" "ds_read_u16_d16_hi %1, %70 offset:128\n\t" "ds_read_u16_d16_hi %2, %70 offset:256\n\t"
+        "ds_read_u16_d16_hi %3, %70 offset:384\n\t" "ds_read_u16_d16_hi %4, %70 offset:512\n\t" "ds_read_u16_d16_hi %5, %70 offset:640\n\t"
+        "ds_read_u16_d16_hi %6, %70 offset:768\n\t" "ds_read_u16_d16_hi %7, %70 offset:896\n\t" "ds_read_u16_d16_hi %8, %70 offset:1024\n\t"
+        "ds_read_u16_d16_hi %9, %70 offset:1152\n\t" "ds_read_u16_d16_hi %10, %70 offset:1280\n\t" "ds_read_u16_d16_hi %11, %70 offset:1408\n\t"
+        "ds_read_u16_d16_hi %12, %70 offset:1536\n\t" "ds_read_u16_d16_hi %13, %70 offset:1664\n\t" "ds_read_u16_d16_hi %14, %70 offset:1792\n\t"
+        "ds_read_u16_d16_hi %15, %70 offset:1920\n\t" "ds_read_u16_d16_hi %16, %70 offset:2048\n\t" "ds_read_u16_d16_hi %17, %70 offset:2176\n\t"
+        "ds_read_u16_d16_hi %18, %71 offset:0\n\t" "ds_read_u16_d16_hi %19, %71 offset:128\n\t" "ds_read_u16_d16_hi %20, %71 offset:256\n\t"
+        "ds_read_u16_d16_hi %21, %71 offset:384\n\t" "ds_read_u16_d16_hi %22, %71 offset:512\n\t" "ds_read_u16_d16_hi %23, %71 offset:640\n\t"
+        "ds_read_u16_d16_hi %24, %71 offset:768\n\t" "ds_read_u16_d16_hi %25, %71 offset:896\n\t" "ds_read_u16_d16_hi %26, %71 offset:1024\n\t"
+        "ds_read_u16_d16_hi %27, %71 offset:1152\n\t" "ds_read_u16_d16_hi %28, %71 offset:1280\n\t" "ds_read_u16_d16_hi %29, %71 offset:1408\n\t"
+        "ds_read_u16_d16_hi %30, %71 offset:1536\n\t" "ds_read_u16_d16_hi %31, %71 offset:1664\n\t" "ds_read_u16_d16_hi %32, %71 offset:1792\n\t"
+        "ds_read_u16_d16_hi %33, %71 offset:1920\n\t" "ds_read_u16_d16_hi %34, %71 offset:2048\n\t" "ds_read_u16_d16_hi %35, %71 offset:2176\n\t"
+        "ds_read_u16_d16_hi %36, %72 offset:0\n\t" "ds_read_u16_d16_hi %37, %72 offset:128\n\t" "ds_read_u16_d16_hi %38, %72 offset:256\n\t"
+        "ds_read_u16_d16_hi %39, %72 offset:384\n\t" "ds_read_u16_d16_hi %40, %72 offset:512\n\t" "ds_read_u16_d16_hi %41, %72 offset:640\n\t"
+        "ds_read_u16_d16_hi %42, %72 offset:768\n\t" "ds_read_u16_d16_hi %43, %72 offset:896\n\t" "ds_read_u16_d16_hi %44, %72 offset:1024\n\t"
+        "ds_read_u16_d16_hi %45, %72 offset:1152\n\t" "ds_read_u16_d16_hi %46, %72 offset:1280\n\t" "ds_read_u16_d16_hi %47, %72 offset:1408\n\t"
+        "ds_read_u16_d16_hi %48, %72 offset:1536\n\t" "ds_read_u16_d16_hi %49, %72 offset:1664\n\t" "ds_read_u16_d16_hi %50, %72 offset:1792\n\t"
+        "ds_read_u16_d16_hi %51, %72 offset:1920\n\t" "ds_read_u16_d16_hi %52, %72 offset:2048\n\t" "ds_read_u16_d16_hi %53, %72 offset:2176\n\t"
+        "ds_read_u16_d16_hi %54, %73 offset:0\n\t" "ds_read_u16_d16_hi %55, %73 offset:128\n\t" "ds_read_u16_d16_hi %56, %73 offset:256\n\t"
+        "ds_read_u16_d16_hi %57, %73 offset:384\n\t" "ds_read_u16_d16_hi %58, %73 offset:512\n\t" "ds_read_u16_d16_hi %59, %73 offset:640\n\t"
+        "ds_read_u16_d16_hi %60, %73 offset:768\n\t" "ds_read_u16_d16_hi %61, %73 offset:896\n\t" "ds_read_u16_d16_hi %62, %73 offset:1024\n\t"
+        "ds_read_u16_d16_hi %63, %73 offset:1152\n\t" "ds_read_u16_d16_hi %64, %73 offset:1280\n\t" "ds_read_u16_d16_hi %65, %73 offset:1408\n\t"
+        "ds_read_u16_d16_hi %66, %73 offset:1536\n\t" "ds_read_u16_d16_hi %67, %73 offset:1664\n\t" "ds_read_u16_d16_hi %68, %73 offset:1792\n\t"
+        "ds_read_u16_d16_hi %69, %73 offset:1920\n\t" "s_waitcnt lgkmcnt(0)"
+        : "+v"(k[0][0]), "+v"(k[0][1]), "+v"(k[0][2]), "+v"(k[0][3]), "+v"(k[0][4]), "+v"(k[0][5]),
+          "+v"(k[0][6]), "+v"(k[0][7]), "+v"(k[0][8]), "+v"(k[0][9]), "+v"(k[0][10]), "+v"(k[0][11]),
+          "+v"(k[0][12]), "+v"(k[0][13]), "+v"(k[0][14]), "+v"(k[0][15]), "+v"(k[0][16]), "+v"(k[0][17]),
+          "+v"(k[1][0]), "+v"(k[1][1]), "+v"(k[1][2]), "+v"(k[1][3]), "+v"(k[1][4]), "+v"(k[1][5]),
+          "+v"(k[1][6]), "+v"(k[1][7]), "+v"(k[1][8]), "+v"(k[1][9]), "+v"(k[1][10]), "+v"(k[1][11]),
+          "+v"(k[1][12]), "+v"(k[1][13]), "+v"(k[1][14]), "+v"(k[1][15]), "+v"(k[1][16]), "+v"(k[1][17]),
+          "+v"(k[2][0]), "+v"(k[2][1]), "+v"(k[2][2]), "+v"(k[2][3]), "+v"(k[2][4]), "+v"(k[2][5]),
+          "+v"(k[2][6]), "+v"(k[2][7]), "+v"(k[2][8]), "+v"(k[2][9]), "+v"(k[2][10]), "+v"(k[2][11]),
+          "+v"(k[2][12]), "+v"(k[2][13]), "+v"(k[2][14]), "+v"(k[2][15]), "+v"(k[2][16]), "+v"(k[2][17]),
+          "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7]),
+          "+v"(v[8]), "+v"(v[9]), "+v"(v[10]), "+v"(v[11]), "+v"(v[12]), "+v"(v[13]), "+v"(v[14]), "+v"(v[15])
+        : "v"(lds_addr(k0)), "v"(lds_addr(k1)), "v"(lds_addr(k2)), "v"(lds_addr(v0))
+        : "memory");
+}
+// three rows of 18 pixels (Q halo)
+__device__ __forceinline__ void lds_window_q(float (&q)[3][kSeg + 2], const char* q0, const char* q1,
+                                             const char* q2) {
+    static_assert(kSeg == 16, "the asm below is written for 16-pixel segments");
+    asm volatile(
+        "ds_read_u16_d16_hi %0, %54 offset:0\n\t" "ds_read_u16_d16_hi %1, %54 offset:128\n\t" "ds_read_u16_d16_hi %2, %54 offset:256\n\t"
+        "ds_read_u16_d16_hi %3, %54 offset:384\n\t" "ds_read_u16_d16_hi %4, %54 offset:512\n\t" "ds_read_u16_d16_hi %5, %54 offset:640\n\t"
+        "ds_read_u16_d16_hi %6, %54 offset:768\n\t" "ds_read_u16_d16_hi %7, %54 offset:896\n\t" "ds_read_u16_d16_hi %8, %54 offset:1024\n\t"
+        "ds_read_u16_d16_hi %9, %54 offset:1152\n\t" "ds_read_u16_d16_hi %10, %54 offset:1280\n\t" "ds_read_u16_d16_hi %11, %54 offset:1408\n\t"
+        "ds_read_u16_d16_hi %12, %54 offset:1536\n\t" "ds_read_u16_d16_hi %13, %54 offset:1664\n\t" "ds_read_u16_d16_hi %14, %54 offset:1792\n\t"
+        "ds_read_u16_d16_hi %15, %54 offset:1920\n\t" "ds_read_u16_d16_hi %16, %54 offset:2048\n\t" "ds_read_u16_d16_hi %17, %54 offset:2176\n\t"
+        "ds_read_u16_d16_hi %18, %55 offset:0\n\t" "ds_read_u16_d16_hi %19, %55 offset:128\n\t" "ds_read_u16_d16_hi %20, %55 offset:256\n\t"
+        "ds_read_u16_d16_hi %21, %55 offset:384\n\t" "ds_read_u16_d16_hi %22, %55 offset:512\n\t" "ds_read_u16_d16_hi %23, %55 offset:640\n\t"
+        "ds_read_u16_d16_hi %24, %55 offset:768\n\t" "ds_read_u16_d16_hi %25, %55 offset:896\n\t" "ds_read_u16_d16_hi %26, %55 offset:1024\n\t"
+        "ds_read_u16_d16_hi %27, %55 offset:1152\n\t" "ds_read_u16_d16_hi %28, %55 offset:1280\n\t" "ds_read_u16_d16_hi %29, %55 offset:1408\n\t"
+        "ds_read_u16_d16_hi %30, %55 offset:1536\n\t" "ds_read_u16_d16_hi %31, %55 offset:1664\n\t" "ds_read_u16_d16_hi %32, %55 offset:1792\n\t"
+        "ds_read_u16_d16_hi %33, %55 offset:1920\n\t" "ds_read_u16_d16_hi %34, %55 offset:2048\n\t" "ds_read_u16_d16_hi %35, %55 offset:2176\n\t"
+        "ds_read_u16_d16_hi %36, %56 offset:0\n\t" "ds_read_u16_d16_hi %37, %56 offset:128\n\t" "ds_read_u16_d16_hi %38, %56 offset:256\n\t"
+        "ds_read_u16_d16_hi %39, %56 offset:384\n\t" "ds_read_u16_d16_hi %40, %56 offset:512\n\t" "ds_read_u16_d16_hi %41, %56 offset:640\n\t"
+        "ds_read_u16_d16_hi %42, %56 offset:768\n\t" "ds_read_u16_d16_hi %43, %56 offset:896\n\t" "ds_read_u16_d16_hi %44, %56 offset:1024\n\t"
+        "ds_read_u16_d16_hi %45, %56 offset:1152\n\t" "ds_read_u16_d16_hi %46, %56 offset:1280\n\t" "ds_read_u16_d16_hi %47, %56 offset:1408\n\t"
+        "ds_read_u16_d16_hi %48, %56 offset:1536\n\t" "ds_read_u16_d16_hi %49, %56 offset:1664\n\t" "ds_read_u16_d16_hi %50, %56 offset:1792\n\t"
+        "ds_read_u16_d16_hi %51, %56 offset:1920\n\t" "ds_read_u16_d16_hi %52, %56 offset:2048\n\t" "ds_read_u16_d16_hi %53, %56 offset:2176\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "+v"(q[0][0]), "+v"(q[0][1]), "+v"(q[0][2]), "+v"(q[0][3]), "+v"(q[0][4]), "+v"(q[0][5]),
+          "+v"(q[0][6]), "+v"(q[0][7]), "+v"(q[0][8]), "+v"(q[0][9]), "+v"(q[0][10]), "+v"(q[0][11]),
+          "+v"(q[0][12]), "+v"(q[0][13]), "+v"(q[0][14]), "+v"(q[0][15]), "+v"(q[0][16]), "+v"(q[0][17]),
+          "+v"(q[1][0]), "+v"(q[1][1]), "+v"(q[1][2]), "+v"(q[1][3]), "+v"(q[1][4]), "+v"(q[1][5]),
+          "+v"(q[1][6]), "+v"(q[1][7]), "+v"(q[1][8]), "+v"(q[1][9]), "+v"(q[1][10]), "+v"(q[1][11]),
+          "+v"(q[1][12]), "+v"(q[1][13]), "+v"(q[1][14]), "+v"(q[1][15]), "+v"(q[1][16]), "+v"(q[1][17]),
+          "+v"(q[2][0]), "+v"(q[2][1]), "+v"(q[2][2]), "+v"(q[2][3]), "+v"(q[2][4]), "+v"(q[2][5]),
+          "+v"(q[2][6]), "+v"(q[2][7]), "+v"(q[2][8]), "+v"(q[2][9]), "+v"(q[2][10]), "+v"(q[2][11]),
+          "+v"(q[2][12]), "+v"(q[2][13]), "+v"(q[2][14]), "+v"(q[2][15]), "+v"(q[2][16]), "+v"(q[2][17])
+        : "v"(lds_addr(q0)), "v"(lds_addr(q1)), "v"(lds_addr(q2))
+        : "memory");
 }
 
 // The workgroup's (slice, split): XCD-aware grids place by the XCD the
@@ -176,6 +268,14 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
 #pragma unroll
     for (int t = 0; t < 9; ++t) wt[t] = 0.f;
     float pf = 0.f; // L2 prefetch of this workgroup's partial (see below)
+    // the 3x3 window's registers (bf16: low halves stay zero, lds_window_*)
+    float kr[3][kSeg + 2], vv[kSeg];
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = 0.f;
+#pragma unroll
+    for (int j = 0; j < kSeg; ++j) vv[j] = 0.f;
     unsigned rel = 0; // thread 0: the counter before this workgroup's release
 
     // ------------------------------------------------------------ phase 1
@@ -222,34 +322,46 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
                 const int lo = k * kSeg - xs, hi = min(kSeg, tw - xs);
                 const char* kb = Ks + ((r * KP + xs) * 64 + lane) * T::esz;
                 const char* vb = Vs + ((r * VP + xs) * 64 + lane) * T::esz;
-                typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-#pragma unroll
-                    for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * KP + j) * 64) * T::esz);
-#pragma unroll
-                for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
-                __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
-                float kr[3][kSeg + 2], vv[kSeg];
-#pragma unroll
-                for (int i = 0; i < 3; ++i)
-#pragma unroll
-                    for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
-#pragma unroll
-                for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
-#pragma unroll
-                for (int x = 0; x < kSeg; ++x) {
-                    float p = 0.f;
+                if constexpr (BF) {
+                    lds_window_kv(kr, vv, kb, kb + KP * pb, kb + 2 * KP * pb, vb);
+                } else {
+                    typename T::raw_t kraw[3][kSeg + 2], vraw[kSeg];
 #pragma unroll
                     for (int i = 0; i < 3; ++i)
 #pragma unroll
-                        for (int jj = 0; jj < 3; ++jj) p += wt[i * 3 + jj] * kr[i][x + jj];
-                    const float rv = (x >= lo && x < hi) ? p - vv[x] : 0.f;
+                        for (int j = 0; j < kSeg + 2; ++j) kraw[i][j] = T::raw(kb + ((i * KP + j) * 64) * T::esz);
+#pragma unroll
+                    for (int j = 0; j < kSeg; ++j) vraw[j] = T::raw(vb + (j * 64) * T::esz);
+                    __builtin_amdgcn_sched_barrier(0); // all reads in flight before the arithmetic
 #pragma unroll
                     for (int i = 0; i < 3; ++i)
 #pragma unroll
-                        for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] += rv * kr[i][x + jj];
+                        for (int j = 0; j < kSeg + 2; ++j) kr[i][j] = T::cvt(kraw[i][j]);
+#pragma unroll
+                    for (int j = 0; j < kSeg; ++j) vv[j] = T::cvt(vraw[j]);
                 }
+                // R = P - V as one fused multiply-add chain from -V per
+                // pixel, branch-free, so the 16 pixels' chains interleave.
+                // A segment with masked pixels (the last of a row) gives
+                // them R = 0 through a 0/1 factor (their values are finite:
+                // in-grid or zero pixels).
+                auto grad = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int x = 0; x < kSeg; ++x) {
+                        float rv = -vv[x];
+#pragma unroll
+                        for (int i = 0; i < 3; ++i)
+#pragma unroll
+                            for (int jj = 0; jj < 3; ++jj) rv = __builtin_fmaf(wt[i * 3 + jj], kr[i][x + jj], rv);
+                        if constexpr (decltype(masked)::value) rv *= (x >= lo && x < hi) ? 1.f : 0.f;
+#pragma unroll
+                        for (int i = 0; i < 3; ++i)
+#pragma unroll
+                            for (int jj = 0; jj < 3; ++jj) gacc[i * 3 + jj] = __builtin_fmaf(rv, kr[i][x + jj], gacc[i * 3 + jj]);
+                    }
+                };
+                if (lo == 0 && hi == kSeg) grad(std::false_type{});
+                else grad(std::true_type{});
             }
         }
         lds_barrier(); // every wave is done with this tile's K and V
@@ -375,24 +487,26 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
             const int y = y0 + r;
             const char* qb = Qs + ((r * KP + xs) * 64 + lane) * T::esz;
             char* zrow = Zp + ((long long)y * gw + x0 + xs) * Zsn + lane * T::esz;
-            typename T::raw_t qraw[3][kSeg + 2];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * KP + j) * 64) * T::esz);
-            __builtin_amdgcn_sched_barrier(0);
-            float qr[3][kSeg + 2];
-#pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < kSeg + 2; ++j) qr[i][j] = T::cvt(qraw[i][j]);
-#pragma unroll
-            for (int x = 0; x < kSeg; ++x) {
-                float z = 0.f;
+            float (&qr)[3][kSeg + 2] = kr; // the window's registers again (low halves zero)
+            if constexpr (BF) {
+                lds_window_q(qr, qb, qb + KP * pb, qb + 2 * KP * pb);
+            } else {
+                typename T::raw_t qraw[3][kSeg + 2];
 #pragma unroll
                 for (int i = 0; i < 3; ++i)
 #pragma unroll
-                    for (int jj = 0; jj < 3; ++jj) z += wq[i * 3 + jj] * qr[i][x + jj];
+                    for (int j = 0; j < kSeg + 2; ++j) qraw[i][j] = T::raw(qb + ((i * KP + j) * 64) * T::esz);
+                __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                for (int i = 0; i < 3; ++i)
+#pragma unroll
+                    for (int j = 0; j < kSeg + 2; ++j) qr[i][j] = T::cvt(qraw[i][j]);
+            }
+#pragma unroll
+            for (int x = 0; x < kSeg; ++x) {
+                float z = wq[0] * qr[0][x];
+#pragma unroll
+                for (int t = 1; t < 9; ++t) z = __builtin_fmaf(wq[t], qr[t / 3][x + t % 3], z);
                 if (x >= lo && x < hi) T::st(zrow + x * Zsn, poison ? __builtin_nanf("") : z);
             }
         }
