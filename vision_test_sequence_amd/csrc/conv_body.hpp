@@ -502,12 +502,35 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
 #pragma unroll
                     for (int j = 0; j < kSeg + 2; ++j) qr[i][j] = T::cvt(qraw[i][j]);
             }
-#pragma unroll
-            for (int x = 0; x < kSeg; ++x) {
+            auto zpix = [&](int x) __attribute__((always_inline)) {
                 float z = wq[0] * qr[0][x];
 #pragma unroll
                 for (int t = 1; t < 9; ++t) z = __builtin_fmaf(wq[t], qr[t / 3][x + t % 3], z);
-                if (x >= lo && x < hi) T::st(zrow + x * Zsn, poison ? __builtin_nanf("") : z);
+                return poison ? __builtin_nanf("") : z;
+            };
+            if constexpr (BF) {
+                // Eight pixels at a time through 1 KB of LDS private to the
+                // wave (in the K/V region, free after phase 1): each lane
+                // writes its channel, then stores 16 contiguous bytes (8
+                // channels of one pixel) -- one 1 KB store instruction
+                // instead of eight of 128 bytes.  (The K region holds at
+                // least 3 rows of 24 pixels: 9 KB >= 8 waves x 1 KB.)
+                char* zs = Ks + w * 1024;
+#pragma unroll
+                for (int h8 = 0; h8 < kSeg / 8; ++h8) {
+#pragma unroll
+                    for (int x8 = 0; x8 < 8; ++x8)
+                        *reinterpret_cast<bf16_t*>(zs + x8 * 128 + lane * 2) = f2bf(zpix(8 * h8 + x8));
+                    const u32x4 v = *reinterpret_cast<const u32x4*>(zs + lane * 16);
+                    const int px = 8 * h8 + (lane >> 3);
+                    if (px >= lo && px < hi)
+                        __builtin_nontemporal_store(
+                            v, reinterpret_cast<u32x4*>(Zp + ((long long)y * gw + x0 + xs + px) * Zsn + (lane & 7) * 16));
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < kSeg; ++x)
+                    if (x >= lo && x < hi) T::st(zrow + x * Zsn, zpix(x));
             }
         }
         if (!q_early) __syncthreads();
