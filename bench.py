@@ -11,7 +11,9 @@ ttt_dwconv3x3_fullbatch) are timed too.
 
 Inputs are resident in HBM before timing and rotate over 5 independent sets
 (> 256 MB together, so the 256 MB Infinity Cache cannot hold them between
-uses).  Prints one JSON line: whole-layer tokens/s, the roofline of the
+uses).  The timed steps are captured in one HIP graph and replayed: one
+Python call through the binding takes about as long as the layer kernel, so
+eager calls would time the host (their rate is reported alongside).  Prints one JSON line: whole-layer tokens/s, the roofline of the
 dominant kernel (the step's one kernel), the other rows of the path on their
 own workloads (the mini-batch bidirectional scan at 1280x1280, the forward
 and backward of the linear step at ViT-B 1024x1024), and the fp64 oracle
@@ -105,6 +107,37 @@ def time_calls(torch, fn, n):
         fn(i)
     e1.record()
     torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
+
+
+def time_graphed(torch, fn, n):
+    """Average time per call of n calls captured in one HIP graph
+    (torch.cuda.graph) and replayed once, between HIP events on the replay
+    stream, in ms.  The layer's kernels take about as long as one Python
+    call through the binding, so eager back-to-back calls would measure
+    the host; the graph launches the same kernels with the same arguments
+    without it.  A warm-up on a side stream precedes the capture, as torch
+    asks; the replay after an untimed one is timed."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(min(n, 2 * NSETS)):
+            fn(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(n):
+            fn(i)
+    graph.replay()  # untimed
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    del graph
     return e0.elapsed_time(e1) / n
 
 
@@ -217,18 +250,21 @@ def main():
         step(sets[i % NSETS][1])
     torch.cuda.synchronize()
 
-    # timed region: K layer steps rotating over the input sets, bracketed by
-    # a synchronisation and HIP events on the launch stream; a step is one
-    # launch, so this is also the layer kernel's average launch duration
-    ms_step = time_calls(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
-    # the two kernels of the separate calls: back-to-back launches on the
-    # same stream, rotating over the same sets (average launch duration)
+    # timed region: K layer steps rotating over the input sets, captured in
+    # one graph and replayed between HIP events on the replay stream; a step
+    # is one launch, so this is also the layer kernel's average launch
+    # duration
+    ms_step = time_graphed(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
+    # the same steps as eager calls from Python (host-bound: reported only)
+    eager_ms_step = time_calls(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
+    # the two kernels of the separate calls, the same way (average launch
+    # duration)
     nk = max(args.steps, 200)
-    lin_ms = time_calls(torch, lambda i: linear(sets[i % NSETS][1]), nk)
-    conv_ms = time_calls(torch, lambda i: conv(sets[i % NSETS][1]), nk)
-    sep_ms = time_calls(torch, lambda i: separate(sets[i % NSETS][1]), nk)
+    lin_ms = time_graphed(torch, lambda i: linear(sets[i % NSETS][1]), nk)
+    conv_ms = time_graphed(torch, lambda i: conv(sets[i % NSETS][1]), nk)
+    sep_ms = time_graphed(torch, lambda i: separate(sets[i % NSETS][1]), nk)
     # warm reference: the same buffers every step (Infinity-Cache resident)
-    warm_ms_step = time_calls(torch, lambda i: step(sets[0][1]), args.steps)
+    warm_ms_step = time_graphed(torch, lambda i: step(sets[0][1]), args.steps)
 
     # one plain device copy of known size: the scale for the HBM byte
     # counters of the profiled runs
@@ -274,6 +310,7 @@ def main():
             "avg_launch_us": ms_step * 1e3,
         },
         "kernels": {
+            "eager_python_us_per_step": eager_ms_step * 1e3,
             "separate_calls_us_per_step": sep_ms * 1e3,
             "linear_us": lin_ms * 1e3,
             "linear_gbs": lin_bytes / (lin_ms * 1e-3) / 1e9,
