@@ -108,11 +108,11 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def view(t: torch.Tensor) -> View:
-    if t.dim() != 4:
-        raise ValueError("views are [B,H,N,d] tensors")
-    if t.stride(3) != 1 and t.shape[3] > 1:
-        raise ValueError("the d channels of a view must be contiguous")
     s = t.stride()
+    if len(s) != 4:
+        raise ValueError("views are [B,H,N,d] tensors")
+    if s[3] != 1 and t.shape[3] > 1:
+        raise ValueError("the d channels of a view must be contiguous")
     return View(t.data_ptr(), s[0], s[1], s[2])
 
 
