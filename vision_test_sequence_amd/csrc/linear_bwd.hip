@@ -59,7 +59,7 @@ struct BwdArgs {
     int S2, per2;       // bf16 pass 2: splits per slice, tokens per split (<= kP2Tok)
 };
 constexpr int kP2Tok = 256; // bf16 pass 2: tokens per workgroup, resident in LDS
-constexpr int kP1Tok = 512; // bf16 pass 1: tokens per workgroup, resident in LDS
+constexpr int kP1Tok = 256; // bf16 pass 1: tokens per workgroup, resident in LDS (64 KB: two per CU)
 
 // ------------------------------------------------------------ fragments --
 template <bool BF> struct Frags;
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_prep(BwdArgs a) {
 // dW1 by row ownership: wave w accumulates rows 16w.. over every token (dZ
 // block w against all Q blocks, transposed reads), so the waves add
 // nothing up; each stores its rows of the split's share.
-__global__ __launch_bounds__(kThreads, 1) void bwd_pass1_bf(BwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[2 * kP1Tok * 128];
     char* Zs = lds;
     char* Qs = lds + kP1Tok * 128;
@@ -497,57 +497,55 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     }
     red[tid] = dsum;
     __syncthreads();
-    const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
-    float P[4][4], Q2[4][4];
+    // P = W0^T dW1 and Q2 = dW1 A on fp32 matrix cores (16x16x4 tiles):
+    // wave w owns the 16-row block w of both, four 16-column tiles each
+    const int lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
+    const int R0 = 16 * w;
+    v4f P[4], Q2[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) P[i][j] = Q2[i][j] = 0.f;
+    for (int cb = 0; cb < 4; ++cb) P[cb] = Q2[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-    for (int k = 0; k < 64; ++k) {
-        const f32x4 wv = *reinterpret_cast<const f32x4*>(W + k * MB + r0);  // W0[k][r0..]
-        const f32x4 dv = *reinterpret_cast<const f32x4*>(D + k * MB + c0);  // dW1[k][c0..]
-        const f32x4 av = *reinterpret_cast<const f32x4*>(Am + k * MB + c0); // A[k][c0..]
-        float d2[4];
+    for (int k0 = 0; k0 < 64; k0 += 4) {
+        const float pa = W[(k0 + g) * MB + R0 + m]; // W0^T[R0+m][k0+g]
+        const float qa = D[(R0 + m) * MB + k0 + g]; // dW1[R0+m][k0+g]
 #pragma unroll
-        for (int i = 0; i < 4; ++i) d2[i] = D[(r0 + i) * MB + k];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                P[i][j] += wv[i] * dv[j];  // (W0^T dW1)[r0+i][c0+j]
-                Q2[i][j] += d2[i] * av[j]; // (dW1 A)[r0+i][c0+j]
-            }
+        for (int cb = 0; cb < 4; ++cb) {
+            P[cb] = mfma4(pa, D[(k0 + g) * MB + 16 * cb + m], P[cb]);   // dW1[k0+g][16cb+m]
+            Q2[cb] = mfma4(qa, Am[(k0 + g) * MB + 16 * cb + m], Q2[cb]); // A[k0+g][16cb+m]
+        }
     }
+    // lane (g, m) holds rows R0 + 4g + i, column 16 cb + m of both
     float* dm = a.dm + (long long)slice * 8192;
     float* dW0s = a.dW0s + (long long)slice * 4096;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        f32x4 dw, d1;
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            d1[j] = D[r * MB + c0 + j];
-            dw[j] = d1[j] - beta * Q2[i][j];
+        for (int i = 0; i < 4; ++i) {
+            const int r = R0 + 4 * g + i, c = 16 * cb + m;
+            dW0s[r * 64 + c] = D[r * MB + c] - beta * Q2[cb][i];
         }
-        *reinterpret_cast<f32x4*>(dW0s + r * 64 + c0) = dw;
-        *reinterpret_cast<f32x4*>(dm + r * 64 + c0) = d1;
+    for (int e = tid; e < 1024; e += kThreads) {
+        const int r = e >> 4, c4 = (e & 15) * 4;
+        *reinterpret_cast<f32x4*>(dm + r * 64 + c4) = *reinterpret_cast<const f32x4*>(D + r * MB + c4);
     }
-    __syncthreads(); // every thread has read D and W
+    __syncthreads(); // every thread has read W
     // M = P + P^T through LDS (W's space is free now)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) W[(r0 + i) * MB + c0 + j] = P[i][j];
+        for (int i = 0; i < 4; ++i) W[(R0 + 4 * g + i) * MB + 16 * cb + m] = P[cb][i];
     __syncthreads();
+    {
+        const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
-        f32x4 mv;
+        for (int i = 0; i < 4; ++i) {
+            const int r = r0 + i;
+            f32x4 mv;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mv[j] = W[r * MB + c0 + j] + W[(c0 + j) * MB + r];
-        *reinterpret_cast<f32x4*>(dm + 4096 + r * 64 + c0) = mv;
-        *reinterpret_cast<f32x4*>(Am + r * MB + c0) = mv; // A's space is free now
+            for (int j = 0; j < 4; ++j) mv[j] = W[r * MB + c0 + j] + W[(c0 + j) * MB + r];
+            *reinterpret_cast<f32x4*>(dm + 4096 + r * 64 + c0) = mv;
+            *reinterpret_cast<f32x4*>(Am + r * MB + c0) = mv; // A's space is free now
+        }
     }
     __syncthreads();
     // bf16 operator fragments for pass 2 (A operand of Wt[o][k] with output
