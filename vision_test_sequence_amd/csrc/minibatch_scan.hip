@@ -34,18 +34,12 @@
 // per chunk hands a chunk from chain wave to output wave (double-buffered
 // LDS).
 //
-// Bidirectional average: the two directions of a column block share a
-// workgroup and step in lockstep.  For each token, the direction that
-// reaches it first stores its fp32 output in the workspace; the other one
-// reads it back kPre chunks ahead of use (register prefetch), averages and
-// stores the bf16 result.  Visibility: vector-memory operations of a wave
-// complete in issue order, so an output wave that has received the data of
-// chunk j (loaded after its stores of chunk j - kPre) has completed those
-// stores, and the next workgroup barrier publishes them to its partner.  A
-// prefetch issued for chunk jj after barrier jj - kPre may therefore read
-// outputs stored for chunks <= jj - 2 kPre - 1: tokens whose two arrivals
-// are more than 2 kPre chunks apart.  Tokens closer to the middle of the
-// sequence are averaged after the scan from both stored fp32 outputs.
+// Bidirectional average: each direction of a column block runs in a
+// workgroup of its own and stores every token's fp32 output in the
+// workspace (P forward, P2 backward); a second kernel (scan_average) forms
+// Z = (P + P2) / 2.  (With the two directions in one workgroup, stepping
+// in lockstep and averaging as they go, the 1280x1280 workload took 162 us
+// against 122 us: the lockstep paced both chains by the slowest wave.)
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -76,23 +70,22 @@ struct ScanArgs {
     View4 K, Q, V, Z;
     const float* W0;
     const float* eta;
-    float* P;          // [slices][N][64] fp32: first-arrival outputs
-    float* P2;         // [slices][N][64] fp32: second-arrival outputs near the middle
+    float* P;          // [slices][N][64] fp32: forward-direction outputs (both directions)
+    float* P2;         // [slices][N][64] fp32: backward-direction outputs
     float* dummy;      // [blocks][2 directions][64 lanes][8] fp32: sink of masked-off stores
     const char* zeros; // 256 zero bytes (never written): the rows of empty slots
-    int H, N, b, nch, slices, mode, ndir, xcd;
+    int H, N, b, nch, slices, mode, xcd;
+    int split;         // both directions: fp32 outputs to P / P2 (then scan_average)
+    int blocks;        // workgroups per direction
 };
 
 // Per-lane walk of one chain.  Token slot m of chunk j is token
-// p = j*b + m (forward) or N-1-(j*b + m) (reverse); the chunk in which the
-// partner direction meets that token is c0 - j with c0 = (N-1-m) / b, in
-// both directions.
+// p = j*b + m (forward) or N-1-(j*b + m) (reverse).
 struct Walk {
-    int g, m, rt, dir, b, N, nch, c0;
+    int g, m, rt, dir, b, N, nch;
     long long step; // token step per chunk: +-b
 };
 __device__ __forceinline__ int token_of(const Walk& L, int rho) { return L.dir ? L.N - 1 - rho : rho; }
-__device__ __forceinline__ bool defer_d(int d) { return d <= 2 * kPre && d >= -2 * kPre; }
 // slot m of chunk jj holds a token
 __device__ __forceinline__ bool slot_valid(const Walk& L, int jj) {
     return jj < L.nch && L.m < L.b && jj * L.b + L.m < L.N;
@@ -226,37 +219,26 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 // ----------------------------------------------------------- output wave --
 template <int D>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
-                            long long Zsn, float* P, float* P2, float* sink, const char* lds) {
+                            long long Zsn, float* P, float* sink, const char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
-    const bool bidir = a.ndir == 2;
     const int p0 = token_of(L, m); // may lie outside the slice: then never used
     const char* qn = Q + p0 * Qsn;
-    const float* pn = bidir ? P + (long long)p0 * 64 : sink;
     const long long qst = L.step * Qsn, pst = L.step * 64;
     struct Regs {
         u32x4 q[2];
-        f32x4 pp;
     } cr[D];
     auto issue = [&](int jj, Regs& r) __attribute__((always_inline)) {
         const bool ok = slot_valid(L, jj);
         const char* qp = ok ? qn : a.zeros;
         r.q[0] = *reinterpret_cast<const u32x4*>(qp);
         r.q[1] = *reinterpret_cast<const u32x4*>(qp + 64);
-        if (bidir) {
-            // the partner's fp32 output of this token, when it was stored
-            // long enough before (see the header)
-            const float* src = ok && 2 * jj - L.c0 > 2 * kPre ? pn : sink;
-            r.pp = *reinterpret_cast<const f32x4*>(src);
-        }
         qn += qst;
-        pn += pst;
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(u, cr[u]);
 
     char* zp = Z + (long long)token_of(L, m) * Zsn; // running output pointers of chunk j
-    float* p1 = bidir ? P + (long long)token_of(L, m) * 64 : sink;
-    float* p2 = bidir ? P2 + (long long)token_of(L, m) * 64 : sink;
+    float* p1 = a.split ? P + (long long)token_of(L, m) * 64 : sink;
     const long long zst = L.step * Zsn;
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
@@ -290,86 +272,75 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3
             const bool valid = slot_valid(L, j);
-            if (!bidir) {
+            if (a.split) { // fp32 output of this direction
+                *reinterpret_cast<f32x4*>(valid ? p1 : sink) = f32x4{Zt[0], Zt[1], Zt[2], Zt[3]};
+            } else {
                 char* dz = valid ? zp : reinterpret_cast<char*>(sink);
                 __builtin_nontemporal_store(u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])},
-                                            reinterpret_cast<u32x2*>(dz));
-            } else {
-                const int d = 2 * j - L.c0; // own chunk minus the partner's
-                const bool first = d < 0 || (d == 0 && L.dir == 0);
-                const bool defer = defer_d(d);
-                float* dp = !valid ? sink : (first ? p1 : (defer ? p2 : sink));
-                *reinterpret_cast<f32x4*>(dp) = f32x4{Zt[0], Zt[1], Zt[2], Zt[3]};
-                const bool fin = valid && !first && !defer;
-                const f32x4 o = r.pp;
-                char* dz = fin ? zp : reinterpret_cast<char*>(sink + 4);
-                __builtin_nontemporal_store(u32x2{pack_bf2(0.5f * (Zt[0] + o[0]), 0.5f * (Zt[1] + o[1])),
-                                                  pack_bf2(0.5f * (Zt[2] + o[2]), 0.5f * (Zt[3] + o[3]))},
                                             reinterpret_cast<u32x2*>(dz));
             }
             asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
             zp += zst;
-            p1 += pst;
-            p2 += pst;
+            if (a.split) p1 += pst;
             issue(j + D, r);
         }
     }
 }
 
-__global__ __launch_bounds__(256, 1) void scan_kernel(ScanArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[2 * kDirLds];
-    const SliceSplit ss = map_block(blockIdx.x, 4, a.xcd);
+// One (slice, direction, 16-column block) per workgroup: wave 0 the chain,
+// wave 1 the output.  With both directions (split), blocks [0, blocks)
+// walk forward and the rest backward.
+__global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kDirLds];
+    const int dsplit = a.split && (int)blockIdx.x >= a.blocks ? 1 : 0;
+    const int bidx = (int)blockIdx.x - dsplit * a.blocks;
+    const SliceSplit ss = map_block(bidx, 4, a.xcd);
     if (ss.slice >= a.slices) return; // padding block of the XCD-aware grid
-    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int role = w & 1, ds = w >> 1; // chain / output wave of direction slot ds
+    const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // chain / output wave
     const int lane = threadIdx.x & 63;
     Walk L;
     L.g = lane >> 4;
     L.m = lane & 15;
     L.rt = ss.split;
-    L.dir = a.ndir == 2 ? ds : (a.mode == 2 ? 1 : 0);
+    L.dir = a.split ? dsplit : (a.mode == 2 ? 1 : 0);
     L.b = a.b;
     L.N = a.N;
     L.nch = a.nch;
-    L.c0 = (a.N - 1 - L.m) / a.b;
     L.step = L.dir ? -(long long)a.b : (long long)a.b;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
     const int ch = 16 * L.rt + 4 * L.g; // this lane's output / V channels
-    char* lds_d = lds + ds * kDirLds;
-    float* sink = a.dummy + ((long long)blockIdx.x * 2 + ds) * 512 + lane * 8;
+    float* sink = a.dummy + ((long long)bidx * 2 + dsplit) * 512 + lane * 8;
     if (role == 0) {
         const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2 + 16 * L.g;
         const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh + ch) * 2;
-        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, a.W0 + (long long)h * 4096, a.eta[h], lds_d);
+        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, a.W0 + (long long)h * 4096, a.eta[h], lds);
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh + ch) * 2;
-        float* P = a.P ? a.P + (long long)ss.slice * a.N * 64 + ch : nullptr;
-        float* P2 = a.P2 ? a.P2 + (long long)ss.slice * a.N * 64 + ch : nullptr;
-        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, P2, sink, lds_d);
+        float* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 + ch : nullptr;
+        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, sink, lds);
     }
+}
 
-    if (a.ndir == 2) {
-        // tokens whose two arrivals are at most 2 kPre chunks apart: average
-        // the two stored fp32 outputs
-        drain_vmem();
-        __syncthreads();
-        const int span = (2 * kPre + 2) * a.b;
-        const int lo = max(0, (a.N - 1) / 2 - span), hi = min(a.N, a.N / 2 + span + 1);
-        const float* P = a.P + (long long)ss.slice * a.N * 64;
-        const float* P2 = a.P2 + (long long)ss.slice * a.N * 64;
-        bf16_t* Zb = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh;
-        for (int e2 = threadIdx.x; e2 < (hi - lo) * 4; e2 += blockDim.x) {
-            const int p = lo + (e2 >> 2), c = 16 * L.rt + 4 * (e2 & 3);
-            const int jf = p / a.b, jb = (a.N - 1 - p) / a.b;
-            if (!defer_d(jf - jb)) continue;
-            const f32x4 x = *reinterpret_cast<const f32x4*>(P + (long long)p * 64 + c);
-            const f32x4 y = *reinterpret_cast<const f32x4*>(P2 + (long long)p * 64 + c);
-            *reinterpret_cast<u32x2*>(Zb + (long long)p * a.Z.sn + c) =
-                u32x2{pack_bf2(0.5f * (x[0] + y[0]), 0.5f * (x[1] + y[1])),
-                      pack_bf2(0.5f * (x[2] + y[2]), 0.5f * (x[3] + y[3]))};
-        }
-    }
+// Z = (forward + backward) / 2 from the two directions' fp32 outputs, 8
+// channels (two float4s of each) per thread.
+__global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
+    const long long e = (long long)blockIdx.x * 256 + threadIdx.x; // (slice, token, channel octet)
+    if (e >= (long long)a.slices * a.N * 8) return;
+    const int c8 = (int)(e & 7);
+    const long long st = e >> 3;
+    const int p = (int)(st % a.N), slice = (int)(st / a.N);
+    const int bb = slice / a.H, h = slice % a.H;
+    const float* x = a.P + st * 64 + 8 * c8;
+    const float* y = a.P2 + st * 64 + 8 * c8;
+    const f32x4 x0 = *reinterpret_cast<const f32x4*>(x), x1 = *reinterpret_cast<const f32x4*>(x + 4);
+    const f32x4 y0 = *reinterpret_cast<const f32x4*>(y), y1 = *reinterpret_cast<const f32x4*>(y + 4);
+    bf16_t* z = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh + (long long)p * a.Z.sn + 8 * c8;
+    __builtin_nontemporal_store(u32x4{pack_bf2(0.5f * (x0[0] + y0[0]), 0.5f * (x0[1] + y0[1])),
+                                      pack_bf2(0.5f * (x0[2] + y0[2]), 0.5f * (x0[3] + y0[3])),
+                                      pack_bf2(0.5f * (x1[0] + y1[0]), 0.5f * (x1[1] + y1[1])),
+                                      pack_bf2(0.5f * (x1[2] + y1[2]), 0.5f * (x1[3] + y1[3]))},
+                                reinterpret_cast<u32x4*>(z));
 }
 
 long long padded_slices(int B, int H) {
@@ -395,19 +366,26 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.nch = (s.N + s.b - 1) / s.b;
     a.slices = s.B * s.H;
     a.mode = s.mode;
-    a.ndir = s.mode == 0 ? 2 : 1;
+    // both directions: each in workgroups of its own, fp32 outputs averaged
+    // by a second kernel
+    a.split = s.mode == 0 ? 1 : 0;
     a.xcd = 1;
     const long long blocks = padded_slices(s.B, s.H) * 4;
+    a.blocks = (int)blocks;
     // workspace: [zero block, 256 bytes][sink][P][P2].  The zero block sits
     // at offset 0 whatever the shape, so no call's outputs ever land on it.
     float* base = (float*)s.ws;
     a.zeros = (const char*)base;
     a.dummy = base + 64;
-    if (a.ndir == 2) {
+    if (a.split) {
         a.P = a.dummy + blocks * 2 * 512;
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)blocks), dim3(128 * a.ndir), 0, stream, a);
+    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(blocks * (a.split ? 2 : 1))), dim3(128), 0, stream, a);
+    if (a.split) {
+        const long long n = (long long)a.slices * s.N * 8;
+        hipLaunchKernelGGL(scan_average, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 
