@@ -390,6 +390,7 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     a.B = p->B; a.H = p->H; a.N = p->N; a.b = p->minibatch; a.mode = (int)p->mode;
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
+    a.cus = device_cus();
     return hip_status(launch_scan(a, (hipStream_t)stream));
 }
 

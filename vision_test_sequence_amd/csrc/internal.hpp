@@ -61,6 +61,7 @@ struct ScanLaunch {
     int B, H, N, b, mode;
     int bf16;
     void* ws;         // scan_ws_bytes(...) bytes
+    int cus;          // compute units of the device
 };
 size_t scan_ws_bytes(int B, int H, int N, int mode);
 hipError_t launch_scan(ScanLaunch a, hipStream_t stream);

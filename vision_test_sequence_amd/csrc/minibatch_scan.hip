@@ -61,6 +61,8 @@ constexpr int kVBuf = kChunk * kVRow;
 constexpr int kXBuf = 64 * kXLane;
 constexpr int kDirLds = 3 * kKBuf + 2 * kVBuf + 2 * kXBuf;
 constexpr int kXOff = 3 * kKBuf + 2 * kVBuf;
+constexpr int kOneCuLds = 96 * 1024; // LDS that keeps a second workgroup off the CU
+static_assert(kDirLds <= kOneCuLds, "scan LDS");
 
 
 typedef short v4s_t __attribute__((ext_vector_type(4)));
@@ -289,9 +291,13 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
 
 // One (slice, direction, 16-column block) per workgroup: wave 0 the chain,
 // wave 1 the output.  With both directions (split), blocks [0, blocks)
-// walk forward and the rest backward.
+// walk forward and the rest backward.  Spread: the workgroup takes more
+// than half a CU's LDS, so no two share a CU -- used when the grid fits the
+// device one workgroup per CU (two chains on one CU share its SIMDs: 127
+// against 121 us at 1280x1280).
+template <bool Spread>
 __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
-    __shared__ __attribute__((aligned(16))) char lds[kDirLds];
+    __shared__ __attribute__((aligned(16))) char lds[Spread ? kOneCuLds : kDirLds];
     const int dsplit = a.split && (int)blockIdx.x >= a.blocks ? 1 : 0;
     const int bidx = (int)blockIdx.x - dsplit * a.blocks;
     const SliceSplit ss = map_block(bidx, 4, a.xcd);
@@ -381,7 +387,9 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
         a.P = a.dummy + blocks * 2 * 512;
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
-    hipLaunchKernelGGL(scan_kernel, dim3((unsigned)(blocks * (a.split ? 2 : 1))), dim3(128), 0, stream, a);
+    const long long grid = blocks * (a.split ? 2 : 1);
+    if (grid <= s.cus) hipLaunchKernelGGL(scan_kernel<true>, dim3((unsigned)grid), dim3(128), 0, stream, a);
+    else hipLaunchKernelGGL(scan_kernel<false>, dim3((unsigned)grid), dim3(128), 0, stream, a);
     if (a.split) {
         const long long n = (long long)a.slices * s.N * 8;
         hipLaunchKernelGGL(scan_average, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
