@@ -35,9 +35,9 @@
 // LDS).
 //
 // Bidirectional average: each direction of a column block runs in a
-// workgroup of its own and stores every token's fp32 output in the
-// workspace (P forward, P2 backward); a second kernel (scan_average) forms
-// Z = (P + P2) / 2.  (With the two directions in one workgroup, stepping
+// workgroup of its own and stores every token's output in the workspace as
+// bf16 (P forward, P2 backward); a second kernel (scan_average) forms
+// Z = (P + P2) / 2 in fp32 and rounds it to bf16.  (With the two directions in one workgroup, stepping
 // in lockstep and averaging as they go, the 1280x1280 workload took 162 us
 // against 122 us: the lockstep paced both chains by the slowest wave.)
 #include "common.hpp"
@@ -72,12 +72,12 @@ struct ScanArgs {
     View4 K, Q, V, Z;
     const float* W0;
     const float* eta;
-    float* P;          // [slices][N][64] fp32: forward-direction outputs (both directions)
-    float* P2;         // [slices][N][64] fp32: backward-direction outputs
+    bf16_t* P;         // [slices][N][64]: forward-direction outputs (both directions)
+    bf16_t* P2;        // [slices][N][64]: backward-direction outputs
     float* dummy;      // [blocks][2 directions][64 lanes][8] fp32: sink of masked-off stores
     const char* zeros; // 256 zero bytes (never written): the rows of empty slots
     int H, N, b, nch, slices, mode, xcd;
-    int split;         // both directions: fp32 outputs to P / P2 (then scan_average)
+    int split;         // both directions: outputs to P / P2 (then scan_average)
     int blocks;        // workgroups per direction
 };
 
@@ -221,7 +221,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 // ----------------------------------------------------------- output wave --
 template <int D>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
-                            long long Zsn, float* P, float* sink, const char* lds) {
+                            long long Zsn, bf16_t* P, float* sink, const char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int p0 = token_of(L, m); // may lie outside the slice: then never used
     const char* qn = Q + p0 * Qsn;
@@ -240,7 +240,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     for (int u = 0; u < D; ++u) issue(u, cr[u]);
 
     char* zp = Z + (long long)token_of(L, m) * Zsn; // running output pointers of chunk j
-    float* p1 = a.split ? P + (long long)token_of(L, m) * 64 : sink;
+    bf16_t* p1 = a.split ? P + (long long)token_of(L, m) * 64 : reinterpret_cast<bf16_t*>(sink);
     const long long zst = L.step * Zsn;
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
@@ -274,8 +274,9 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3
             const bool valid = slot_valid(L, j);
-            if (a.split) { // fp32 output of this direction
-                *reinterpret_cast<f32x4*>(valid ? p1 : sink) = f32x4{Zt[0], Zt[1], Zt[2], Zt[3]};
+            if (a.split) { // this direction's output
+                *reinterpret_cast<u32x2*>(valid ? p1 : reinterpret_cast<bf16_t*>(sink)) =
+                    u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
             } else {
                 char* dz = valid ? zp : reinterpret_cast<char*>(sink);
                 __builtin_nontemporal_store(u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])},
@@ -323,13 +324,13 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh + ch) * 2;
-        float* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 + ch : nullptr;
+        bf16_t* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 + ch : nullptr;
         output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, sink, lds);
     }
 }
 
-// Z = (forward + backward) / 2 from the two directions' fp32 outputs, 8
-// channels (two float4s of each) per thread.
+// Z = (forward + backward) / 2 from the two directions' outputs, 8
+// channels (16 bytes of each) per thread.
 __global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x; // (slice, token, channel octet)
     if (e >= (long long)a.slices * a.N * 8) return;
@@ -337,16 +338,14 @@ __global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
     const long long st = e >> 3;
     const int p = (int)(st % a.N), slice = (int)(st / a.N);
     const int bb = slice / a.H, h = slice % a.H;
-    const float* x = a.P + st * 64 + 8 * c8;
-    const float* y = a.P2 + st * 64 + 8 * c8;
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(x), x1 = *reinterpret_cast<const f32x4*>(x + 4);
-    const f32x4 y0 = *reinterpret_cast<const f32x4*>(y), y1 = *reinterpret_cast<const f32x4*>(y + 4);
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a.P + st * 64 + 8 * c8);
+    const u32x4 y = *reinterpret_cast<const u32x4*>(a.P2 + st * 64 + 8 * c8);
+    u32x4 o;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+        o[k] = pack_bf2(0.5f * (bflo(x[k]) + bflo(y[k])), 0.5f * (bfhi(x[k]) + bfhi(y[k])));
     bf16_t* z = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh + (long long)p * a.Z.sn + 8 * c8;
-    __builtin_nontemporal_store(u32x4{pack_bf2(0.5f * (x0[0] + y0[0]), 0.5f * (x0[1] + y0[1])),
-                                      pack_bf2(0.5f * (x0[2] + y0[2]), 0.5f * (x0[3] + y0[3])),
-                                      pack_bf2(0.5f * (x1[0] + y1[0]), 0.5f * (x1[1] + y1[1])),
-                                      pack_bf2(0.5f * (x1[2] + y1[2]), 0.5f * (x1[3] + y1[3]))},
-                                reinterpret_cast<u32x4*>(z));
+    __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(z));
 }
 
 long long padded_slices(int B, int H) {
@@ -359,7 +358,7 @@ long long padded_slices(int B, int H) {
 size_t scan_ws_bytes(int B, int H, int N, int mode) {
     const long long blocks = padded_slices(B, H) * 4;
     size_t bytes = (size_t)blocks * 2 * 512 * sizeof(float) + 256;
-    if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(float);
+    if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(bf16_t);
     return bytes;
 }
 
@@ -384,7 +383,7 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.zeros = (const char*)base;
     a.dummy = base + 64;
     if (a.split) {
-        a.P = a.dummy + blocks * 2 * 512;
+        a.P = reinterpret_cast<bf16_t*>(a.dummy + blocks * 2 * 512);
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
     const long long grid = blocks * (a.split ? 2 : 1);
