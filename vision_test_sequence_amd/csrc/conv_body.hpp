@@ -404,8 +404,7 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
             else xstore(P + e, v);
         }
         slice_barrier(cnt, (unsigned)a.S);
-        SliceWords sw{}; // thread 0; loaded alongside the partials
-        if (tid == 0) sw = slice_words(cnt);
+        SliceWords sw{}; // thread 0; loaded after the partials (see below)
         float gv[4];
         // Every workgroup sums all S partials itself (576 floats each, in
         // a fixed order, so all of them form the same w1): one barrier, and
@@ -428,6 +427,10 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
                     else v[k] = f32x4{xload(p), xload(p + 1), xload(p + 2), xload(p + 3)};
                 }
             }
+            // the counter line's words after the partials: the CU returns
+            // vector-memory results in issue order, and that line is still
+            // contended by the slice's polls and releases
+            if (tid == 0) sw = slice_words(cnt);
             f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int k = 0; k < 11; ++k)

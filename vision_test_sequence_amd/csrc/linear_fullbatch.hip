@@ -1143,12 +1143,14 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
     }
     slice_barrier(cnt, 2u * a.S, w < 4);
-    SliceWords sw{};
-    if (tid == 0) sw = slice_words(cnt);
     keep_alive(pf);
     // W1's fragments load while every wave's Q loads (normally long since
-    // landed) and the exchange outcome are waited for
+    // landed) and the exchange outcome are waited for; the counter line's
+    // words after them (results return in issue order, and that line is
+    // still contended by the slice's polls and releases)
     const W1FragsBF wf = w1_frags_bf_packed(a.w1 + (long long)c.slice * 4096, lane);
+    SliceWords sw{};
+    if (tid == 0) sw = slice_words(cnt);
     const bool poison = exchange_outcome<true>(a, c.slice, c.split, sw, chk, kThreads8);
 
     // ---- phase 3: Z from the resident Q region
