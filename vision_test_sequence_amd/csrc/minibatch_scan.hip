@@ -30,9 +30,11 @@
 // Two waves per (slice, direction, column block): the chain wave carries
 // the recurrence alone (R, R', the X update: the serial path of the scan)
 // and publishes each chunk's K rows, bf16 chunk-start X and R' in LDS; the
-// output wave, one chunk behind, forms Z from them.  One workgroup barrier
-// per chunk hands a chunk from chain wave to output wave (double-buffered
-// LDS).
+// output wave, behind it, forms Z from them.  One workgroup barrier per
+// two chunks hands them from chain wave to output wave (the two waves meet
+// half as often, and the output wave's work on the two chunks overlaps);
+// the output products are chained on the matrix cores, with the causal
+// mask applied to the packed bf16 operand as a bit mask.
 //
 // Bidirectional average: each direction of a column block runs in a
 // workgroup of its own and stores every token's output in the workspace as
@@ -47,20 +49,23 @@ namespace ttt {
 namespace {
 
 constexpr int kPre = 12;   // chunks in flight per wave (register prefetch depth)
-static_assert(kPre % 6 == 0, "buffer rotation: j % 2 and j % 3 follow the unrolled index");
+static_assert(kPre % 12 == 0, "buffer rotation: j % 4 and j % 6 follow the unrolled index");
 constexpr int kChunk = 16; // token slots of one chunk (MFMA tile rows)
 constexpr int kKRow = 144; // bytes per staged K row (64 channels + pad)
 constexpr int kVRow = 48;  // bytes per staged V row (this block's 16 channels + pad)
 constexpr int kXLane = 48; // bytes per lane of a published chunk: X (32) and R' (8)
-// LDS per direction: K rows x3 (chunk j+1 is staged while the output wave
-// reads chunk j and chunk j+2 waits), V rows x2 (chain wave only),
-// published X/R' x2.  The prefetch depth is a multiple of 6 so that buffer
-// indices are compile-time constants in the unrolled loop.
+// LDS per direction: K rows x6 (between two barriers the output wave reads
+// chunks j, j+1 while the chain stages j+3, j+4 and j+2 waits), V rows x2
+// (chain wave only), published X/R' x4.  The prefetch depth is a multiple
+// of 12 so that buffer indices are compile-time constants in the unrolled
+// loop.
 constexpr int kKBuf = kChunk * kKRow;
 constexpr int kVBuf = kChunk * kVRow;
 constexpr int kXBuf = 64 * kXLane;
-constexpr int kDirLds = 3 * kKBuf + 2 * kVBuf + 2 * kXBuf;
-constexpr int kXOff = 3 * kKBuf + 2 * kVBuf;
+constexpr int kNK = 6; // K buffers (chunk c in c % 6)
+constexpr int kNX = 4; // published X/R' buffers (chunk c in c % 4)
+constexpr int kDirLds = kNK * kKBuf + 2 * kVBuf + kNX * kXBuf;
+constexpr int kXOff = kNK * kKBuf + 2 * kVBuf;
 constexpr int kOneCuLds = 96 * 1024; // LDS that keeps a second workgroup off the CU
 static_assert(kDirLds <= kOneCuLds, "scan LDS");
 
@@ -115,7 +120,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
                            long long Vsn, const float* W0h, float eta, char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int e = (lane & 15) >> 2, aa = lane & 3;
-    char* vbuf = lds + 3 * kKBuf;
+    char* vbuf = lds + kNK * kKBuf;
     // X = W0^T in accumulator layout
     v4f X[4];
     {
@@ -179,10 +184,10 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
         for (int u = 0; u < D; ++u) {
             const int j = j0 + u;
             Regs& r = cr[u];
-            char* xo = lds + kXOff + (u & 1) * kXBuf + lane * kXLane;
+            char* xo = lds + kXOff + (u % kNX) * kXBuf + lane * kXLane;
             // the next chunk's operands, one step ahead of their use
             v4s_t ktN[4], vinN;
-            stage(cr[(u + 1) % D], (u + 1) % 3, (u + 1) & 1, ktN, vinN);
+            stage(cr[(u + 1) % D], (u + 1) % kNK, (u + 1) & 1, ktN, vinN);
             const float alpha = j < L.nch - 1 ? alpha_full : (j == L.nch - 1 ? alpha_last : 0.f);
 
             // bf16 copy of the chunk-start state
@@ -209,7 +214,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             *reinterpret_cast<u32x4*>(xo) = xu[0];
             *reinterpret_cast<u32x4*>(xo + 16) = xu[1];
             *reinterpret_cast<u32x2*>(xo + 32) = rp2;
-            chunk_barrier();
+            if (u & 1) chunk_barrier(); // chunks j-1, j published
             issue(j + D, r);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) ktA[ct] = ktN[ct];
@@ -239,6 +244,10 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(u, cr[u]);
 
+    // causal mask of K Q^T's accumulator (lane (g, m): rows 4g+i, column
+    // m), kept where 4g+i <= m, as bit masks of the packed bf16 pairs
+    const u32x2 tril{(4 * g <= m ? 0xFFFFu : 0u) | (4 * g + 1 <= m ? 0xFFFF0000u : 0u),
+                     (4 * g + 2 <= m ? 0xFFFFu : 0u) | (4 * g + 3 <= m ? 0xFFFF0000u : 0u)};
     char* zp = Z + (long long)token_of(L, m) * Zsn; // running output pointers of chunk j
     bf16_t* p1 = a.split ? P + (long long)token_of(L, m) * 64 : reinterpret_cast<bf16_t*>(sink);
     const long long zst = L.step * Zsn;
@@ -248,29 +257,22 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
         for (int u = 0; u < D; ++u) {
             const int j = j0 + u;
             Regs& r = cr[u];
-            chunk_barrier(); // chunk j published
-            const char* kb = lds + (u % 3) * kKBuf + m * kKRow + 16 * g;
-            const char* xi = lds + kXOff + (u & 1) * kXBuf + lane * kXLane;
+            if ((u & 1) == 0) chunk_barrier(); // chunks j, j+1 published
+            const char* kb = lds + (u % kNK) * kKBuf + m * kKRow + 16 * g;
+            const char* xi = lds + kXOff + (u % kNX) * kXBuf + lane * kXLane;
             const u32x4 k0 = *reinterpret_cast<const u32x4*>(kb);
             const u32x4 k1 = *reinterpret_cast<const u32x4*>(kb + 64);
             const u32x4 x0 = *reinterpret_cast<const u32x4*>(xi);
             const u32x4 x1 = *reinterpret_cast<const u32x4*>(xi + 16);
             const u32x2 rp2 = *reinterpret_cast<const u32x2*>(xi + 32);
 
-            // Z^T = X^T Q^T + R'^T tril(Q K^T)^T   (chunk-start X), as
-            // independent products summed on the vector unit
+            // Z^T = X^T Q^T + R'^T tril(Q K^T)^T   (chunk-start X), all
+            // accumulated on the matrix cores
             const v4f zero4{0.f, 0.f, 0.f, 0.f};
-            const v4f Sa = mfma32(as_v8bf(k0), as_v8bf(r.q[0]), zero4);
-            const v4f Sb = mfma32(as_v8bf(k1), as_v8bf(r.q[1]), zero4);
-            const v4f Za = mfma32(as_v8bf(x0), as_v8bf(r.q[0]), zero4);
-            const v4f Zb = mfma32(as_v8bf(x1), as_v8bf(r.q[1]), zero4);
-            v4f S = Sa + Sb;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (4 * g + i > m) S[i] = 0.f;
-            const u32x2 sb2{pack_bf2(S[0], S[1]), pack_bf2(S[2], S[3])};
-            const v4f Zc = mfma16(as_v4s(rp2), as_v4s(sb2), zero4);
-            const v4f Zt = (Za + Zb) + Zc;
+            const v4f S = mfma32(as_v8bf(k1), as_v8bf(r.q[1]), mfma32(as_v8bf(k0), as_v8bf(r.q[0]), zero4));
+            const v4f Zq = mfma32(as_v8bf(x1), as_v8bf(r.q[1]), mfma32(as_v8bf(x0), as_v8bf(r.q[0]), zero4));
+            const u32x2 sb2{pack_bf2(S[0], S[1]) & tril[0], pack_bf2(S[2], S[3]) & tril[1]};
+            const v4f Zt = mfma16(as_v4s(rp2), as_v4s(sb2), Zq);
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3
             const bool valid = slot_valid(L, j);
