@@ -200,6 +200,11 @@ def test_scan_errors():
     one = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P(mode=1)))
     assert need - one >= 2 * 2 * 3 * 100 * 64 * 2
     assert bd.STATUS_NAMES[scan(P(), Z=V(2))] == "TTT_ERR_ALIASING"
+    # a slice's rows must be addressable with 31-bit offsets, overrun included
+    # (the workspace is withheld, so a missed check could not launch)
+    sn = 1 << 22
+    far = bd.View(addr(3), 3 * 100 * sn, 100 * sn, sn)
+    assert bd.STATUS_NAMES[scan(P(), Z=far, wsb=0)] == "TTT_ERR_UNSUPPORTED"
     assert scan(P(B=0)) == 0
 
 

@@ -79,7 +79,6 @@ struct ScanArgs {
     const float* eta;
     bf16_t* P;         // [slices][N][64]: forward-direction outputs (both directions)
     bf16_t* P2;        // [slices][N][64]: backward-direction outputs
-    float* dummy;      // [blocks][2 directions][64 lanes][8] fp32: sink of masked-off stores
     const char* zeros; // 256 zero bytes (never written): the rows of empty slots
     int H, N, b, nch, slices, mode, xcd;
     int split;         // both directions: outputs to P / P2 (then scan_average)
@@ -224,38 +223,53 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 }
 
 // ----------------------------------------------------------- output wave --
+// Buffer descriptor over [base, base + bytes): a raw buffer access whose
+// offset lies outside it returns zeros (load) or is dropped (store).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice span
+
 template <int D>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
-                            long long Zsn, bf16_t* P, float* sink, const char* lds) {
+                            long long Zsn, bf16_t* P, const char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
-    const int p0 = token_of(L, m); // may lie outside the slice: then never used
-    const char* qn = Q + p0 * Qsn;
-    const long long qst = L.step * Qsn, pst = L.step * 64;
+    const int ch = 16 * L.rt + 4 * g; // this lane's output channels
+    // Q rows, Z / P outputs through buffer descriptors over the slice: a
+    // slot whose token lies outside the slice (the walk's overrun past
+    // either end: the offset then exceeds the span or wraps negative, as
+    // the host bounds the spans) or an empty slot (m >= b) reads zeros and
+    // stores nothing, with no per-chunk selects.
+    const bool slot = L.m < L.b;
+    const long long p0 = token_of(L, m);
+    const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Q - 16 * g, (long long)(L.N - 1) * Qsn + 128);
+    unsigned qoff = slot ? (unsigned)(p0 * Qsn + 16 * g) : kOffSlice;
+    const unsigned qst = slot ? (unsigned)(L.step * Qsn) : 0u;
     struct Regs {
         u32x4 q[2];
     } cr[D];
-    auto issue = [&](int jj, Regs& r) __attribute__((always_inline)) {
-        const bool ok = slot_valid(L, jj);
-        const char* qp = ok ? qn : a.zeros;
-        r.q[0] = *reinterpret_cast<const u32x4*>(qp);
-        r.q[1] = *reinterpret_cast<const u32x4*>(qp + 64);
-        qn += qst;
+    auto issue = [&](Regs& r) __attribute__((always_inline)) {
+        r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 0, 0);
+        r.q[1] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u, 0, 0);
+        qoff += qst;
     };
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(u, cr[u]);
+    for (int u = 0; u < D; ++u) issue(cr[u]);
 
     // causal mask of K Q^T's accumulator (lane (g, m): rows 4g+i, column
     // m), kept where 4g+i <= m, as bit masks of the packed bf16 pairs
     const u32x2 tril{(4 * g <= m ? 0xFFFFu : 0u) | (4 * g + 1 <= m ? 0xFFFF0000u : 0u),
                      (4 * g + 2 <= m ? 0xFFFFu : 0u) | (4 * g + 3 <= m ? 0xFFFF0000u : 0u)};
-    char* zp = Z + (long long)token_of(L, m) * Zsn; // running output pointers of chunk j
-    bf16_t* p1 = a.split ? P + (long long)token_of(L, m) * 64 : reinterpret_cast<bf16_t*>(sink);
-    const long long zst = L.step * Zsn;
+    // outputs: this direction's bf16 rows of P ([N][64] per slice), or Z
+    const __amdgpu_buffer_rsrc_t zrs = a.split ? span_rsrc(P - ch, (long long)L.N * 128)
+                                               : span_rsrc(Z - 2 * ch, (long long)(L.N - 1) * Zsn + 128);
+    const long long zsn = a.split ? 128 : Zsn;
+    unsigned zoff = slot ? (unsigned)(p0 * zsn + 2 * ch) : kOffSlice;
+    const unsigned zst = slot ? (unsigned)(L.step * zsn) : 0u;
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            const int j = j0 + u;
             Regs& r = cr[u];
             if ((u & 1) == 0) chunk_barrier(); // chunks j, j+1 published
             const char* kb = lds + (u % kNK) * kKBuf + m * kKRow + 16 * g;
@@ -274,20 +288,14 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
             const u32x2 sb2{pack_bf2(S[0], S[1]) & tril[0], pack_bf2(S[2], S[3]) & tril[1]};
             const v4f Zt = mfma16(as_v4s(rp2), as_v4s(sb2), Zq);
 
-            // outputs of token slot m, channels 16 rt + 4 g .. +3
-            const bool valid = slot_valid(L, j);
-            if (a.split) { // this direction's output
-                *reinterpret_cast<u32x2*>(valid ? p1 : reinterpret_cast<bf16_t*>(sink)) =
-                    u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
-            } else {
-                char* dz = valid ? zp : reinterpret_cast<char*>(sink);
-                __builtin_nontemporal_store(u32x2{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])},
-                                            reinterpret_cast<u32x2*>(dz));
-            }
+            // outputs of token slot m, channels 16 rt + 4 g .. +3 (Z
+            // streamed past the caches; P is read back by the average)
+            const u32x2 zv{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
+            if (a.split) __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 0);
+            else __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 2 /* nt */);
             asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
-            zp += zst;
-            if (a.split) p1 += pst;
-            issue(j + D, r);
+            zoff += zst;
+            issue(r);
         }
     }
 }
@@ -318,7 +326,6 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     L.step = L.dir ? -(long long)a.b : (long long)a.b;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
     const int ch = 16 * L.rt + 4 * L.g; // this lane's output / V channels
-    float* sink = a.dummy + ((long long)bidx * 2 + dsplit) * 512 + lane * 8;
     if (role == 0) {
         const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2 + 16 * L.g;
         const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh + ch) * 2;
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh + ch) * 2;
         bf16_t* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 + ch : nullptr;
-        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, sink, lds);
+        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
     }
 }
 
@@ -358,8 +365,7 @@ long long padded_slices(int B, int H) {
 } // namespace
 
 size_t scan_ws_bytes(int B, int H, int N, int mode) {
-    const long long blocks = padded_slices(B, H) * 4;
-    size_t bytes = (size_t)blocks * 2 * 512 * sizeof(float) + 256;
+    size_t bytes = 256;
     if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(bf16_t);
     return bytes;
 }
@@ -373,19 +379,18 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.nch = (s.N + s.b - 1) / s.b;
     a.slices = s.B * s.H;
     a.mode = s.mode;
-    // both directions: each in workgroups of its own, fp32 outputs averaged
+    // both directions: each in workgroups of its own, bf16 outputs averaged
     // by a second kernel
     a.split = s.mode == 0 ? 1 : 0;
     a.xcd = 1;
     const long long blocks = padded_slices(s.B, s.H) * 4;
     a.blocks = (int)blocks;
-    // workspace: [zero block, 256 bytes][sink][P][P2].  The zero block sits
-    // at offset 0 whatever the shape, so no call's outputs ever land on it.
+    // workspace: [zero block, 256 bytes][P][P2].  The zero block sits at
+    // offset 0 whatever the shape, so no call's outputs ever land on it.
     float* base = (float*)s.ws;
     a.zeros = (const char*)base;
-    a.dummy = base + 64;
     if (a.split) {
-        a.P = reinterpret_cast<bf16_t*>(a.dummy + blocks * 2 * 512);
+        a.P = reinterpret_cast<bf16_t*>(base + 64);
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
     const long long grid = blocks * (a.split ? 2 : 1);
