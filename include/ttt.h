@@ -184,8 +184,9 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
  * Both directions start from W0.  TTT_BIDIR_AVG writes
  * Z = (Z_forward + Z_reverse)/2; the other modes write one direction.
  * b must be in [1, 16] on this device (larger: TTT_ERR_UNSUPPORTED).
- * (N + 512) * stride_n * 2 bytes must stay under 2^31 for Q and Z (a
- * slice's rows are addressed with 32-bit offsets; else TTT_ERR_UNSUPPORTED).
+ * (N + 512) * stride_n * 2 bytes must stay under 2^31 for K, Q, V and Z
+ * (a slice's rows are addressed with 32-bit offsets; else
+ * TTT_ERR_UNSUPPORTED).
  */
 ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
                                       const float* W0, const float* eta, ttt_view Z,

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <initializer_list>
 #include <atomic>
 #include <stdint.h>
 
@@ -380,11 +381,11 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
     if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
     if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
-    // the output side addresses a slice's Q rows and Z rows through 32-bit
+    // the kernel addresses a slice's K, V, Q and Z rows through 32-bit
     // buffer offsets, walking up to 512 tokens past either end
     const int64_t span_lim = (int64_t)1 << 31;
-    if ((int64_t)(p->N + 512) * Q.stride_n * 2 >= span_lim || (int64_t)(p->N + 512) * Z.stride_n * 2 >= span_lim)
-        return TTT_ERR_UNSUPPORTED;
+    for (const ttt_view* w : {&K, &Q, &V, &Z})
+        if ((int64_t)(p->N + 512) * w->stride_n * 2 >= span_lim) return TTT_ERR_UNSUPPORTED;
     const size_t need = scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
     if ((st = check_ws(ws, ws_bytes, need, &out[1])) != TTT_OK) return st;
     if ((st = check_aliasing(in, 5, out, 2)) != TTT_OK) return st;

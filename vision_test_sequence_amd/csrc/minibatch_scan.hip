@@ -79,7 +79,6 @@ struct ScanArgs {
     const float* eta;
     bf16_t* P;         // [slices][N][64]: forward-direction outputs (both directions)
     bf16_t* P2;        // [slices][N][64]: backward-direction outputs
-    const char* zeros; // 256 zero bytes (never written): the rows of empty slots
     int H, N, b, nch, slices, mode, xcd;
     int split;         // both directions: outputs to P / P2 (then scan_average)
     int blocks;        // workgroups per direction
@@ -92,14 +91,9 @@ struct Walk {
     long long step; // token step per chunk: +-b
 };
 __device__ __forceinline__ int token_of(const Walk& L, int rho) { return L.dir ? L.N - 1 - rho : rho; }
-// slot m of chunk jj holds a token
-__device__ __forceinline__ bool slot_valid(const Walk& L, int jj) {
-    return jj < L.nch && L.m < L.b && jj * L.b + L.m < L.N;
-}
 // Loads are branch-free (so the compiler can schedule them into the
-// matrix-core latencies): a slot's row pointer advances by one chunk per
-// call and is used only when the slot holds a token; an empty slot reads
-// the zero block.
+// matrix-core latencies): a slot's buffer offset advances by one chunk per
+// call, and a slot without a token falls outside the slice's descriptor.
 __device__ __forceinline__ v4s_t tr_read(const char* p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
 }
@@ -113,7 +107,15 @@ __device__ __forceinline__ void chunk_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Buffer descriptor over [base, base + bytes): a raw buffer access whose
+// offset lies outside it returns zeros (load) or is dropped (store).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, long long bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice span
+
 // ------------------------------------------------------------ chain wave --
+// K, V: the slice's token 0, channel 0; Ksn, Vsn: token strides in bytes.
 template <int D>
 __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
                            long long Vsn, const float* W0h, float eta, char* lds) {
@@ -132,26 +134,29 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             X[2 * kb + 1] = v4f{hi[0], hi[1], hi[2], hi[3]};
         }
     }
-    const int p0 = token_of(L, m); // may lie outside the slice: then never used
-    const char* kn = K + p0 * Ksn; // running row pointers of the next chunk to load
-    const char* vn = V + p0 * Vsn;
-    const long long kst = L.step * Ksn, vst = L.step * Vsn;
+    // K and V rows through buffer descriptors over the slice, as in the
+    // output wave: an overrun token or an empty slot loads zeros
+    const bool slot = L.m < L.b;
+    const long long p0 = token_of(L, m);
+    const int ch = 16 * L.rt + 4 * g; // this lane's V channels
+    const __amdgpu_buffer_rsrc_t krs = span_rsrc(K, (long long)(L.N - 1) * Ksn + 128);
+    const __amdgpu_buffer_rsrc_t vrs = span_rsrc(V, (long long)(L.N - 1) * Vsn + 128);
+    unsigned koff = slot ? (unsigned)(p0 * Ksn + 16 * g) : kOffSlice;
+    unsigned voff = slot ? (unsigned)(p0 * Vsn + 2 * ch) : kOffSlice;
+    const unsigned kst = slot ? (unsigned)(L.step * Ksn) : 0u, vst = slot ? (unsigned)(L.step * Vsn) : 0u;
     struct Regs {
         u32x4 k[2];
         u32x2 v;
     } cr[D];
-    auto issue = [&](int jj, Regs& r) __attribute__((always_inline)) {
-        const bool ok = slot_valid(L, jj);
-        const char* kp = ok ? kn : a.zeros;
-        const char* vp = ok ? vn : a.zeros;
-        r.k[0] = *reinterpret_cast<const u32x4*>(kp);
-        r.k[1] = *reinterpret_cast<const u32x4*>(kp + 64);
-        r.v = *reinterpret_cast<const u32x2*>(vp);
-        kn += kst;
-        vn += vst;
+    auto issue = [&](Regs& r) __attribute__((always_inline)) {
+        r.k[0] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff, 0, 0);
+        r.k[1] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 64u, 0, 0);
+        r.v = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, 0, 0);
+        koff += kst;
+        voff += vst;
     };
 #pragma unroll
-    for (int u = 0; u < D; ++u) issue(u, cr[u]);
+    for (int u = 0; u < D; ++u) issue(cr[u]);
 
     const float alpha_full = -2.0f * eta / (float)L.b;
     const float alpha_last = -2.0f * eta / (float)(L.N - (L.nch - 1) * L.b);
@@ -214,7 +219,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             *reinterpret_cast<u32x4*>(xo + 16) = xu[1];
             *reinterpret_cast<u32x2*>(xo + 32) = rp2;
             if (u & 1) chunk_barrier(); // chunks j-1, j published
-            issue(j + D, r);
+            issue(r);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) ktA[ct] = ktN[ct];
             vin = vinN;
@@ -223,13 +228,8 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 }
 
 // ----------------------------------------------------------- output wave --
-// Buffer descriptor over [base, base + bytes): a raw buffer access whose
-// offset lies outside it returns zeros (load) or is dropped (store).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, long long bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice span
-
+// Q, Z (or P, this direction's [N][64] bf16 rows): the slice's token 0,
+// channel 0; Qsn, Zsn: token strides in bytes.
 template <int D>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
                             long long Zsn, bf16_t* P, const char* lds) {
@@ -242,7 +242,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     // stores nothing, with no per-chunk selects.
     const bool slot = L.m < L.b;
     const long long p0 = token_of(L, m);
-    const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Q - 16 * g, (long long)(L.N - 1) * Qsn + 128);
+    const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Q, (long long)(L.N - 1) * Qsn + 128);
     unsigned qoff = slot ? (unsigned)(p0 * Qsn + 16 * g) : kOffSlice;
     const unsigned qst = slot ? (unsigned)(L.step * Qsn) : 0u;
     struct Regs {
@@ -261,8 +261,8 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     const u32x2 tril{(4 * g <= m ? 0xFFFFu : 0u) | (4 * g + 1 <= m ? 0xFFFF0000u : 0u),
                      (4 * g + 2 <= m ? 0xFFFFu : 0u) | (4 * g + 3 <= m ? 0xFFFF0000u : 0u)};
     // outputs: this direction's bf16 rows of P ([N][64] per slice), or Z
-    const __amdgpu_buffer_rsrc_t zrs = a.split ? span_rsrc(P - ch, (long long)L.N * 128)
-                                               : span_rsrc(Z - 2 * ch, (long long)(L.N - 1) * Zsn + 128);
+    const __amdgpu_buffer_rsrc_t zrs = a.split ? span_rsrc(P, (long long)L.N * 128)
+                                               : span_rsrc(Z, (long long)(L.N - 1) * Zsn + 128);
     const long long zsn = a.split ? 128 : Zsn;
     unsigned zoff = slot ? (unsigned)(p0 * zsn + 2 * ch) : kOffSlice;
     const unsigned zst = slot ? (unsigned)(L.step * zsn) : 0u;
@@ -325,15 +325,16 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     L.nch = a.nch;
     L.step = L.dir ? -(long long)a.b : (long long)a.b;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
-    const int ch = 16 * L.rt + 4 * L.g; // this lane's output / V channels
     if (role == 0) {
-        const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2 + 16 * L.g;
-        const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh + ch) * 2;
+        // slice bases: wave-uniform, so the buffer descriptors need no
+        // per-lane resolution (lane offsets go into the buffer offsets)
+        const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
+        const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
         chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, a.W0 + (long long)h * 4096, a.eta[h], lds);
     } else {
-        const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2 + 16 * L.g;
-        char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh + ch) * 2;
-        bf16_t* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 + ch : nullptr;
+        const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2;
+        char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2;
+        bf16_t* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 : nullptr;
         output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
     }
 }
@@ -385,10 +386,8 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.xcd = 1;
     const long long blocks = padded_slices(s.B, s.H) * 4;
     a.blocks = (int)blocks;
-    // workspace: [zero block, 256 bytes][P][P2].  The zero block sits at
-    // offset 0 whatever the shape, so no call's outputs ever land on it.
+    // workspace: [256 bytes reserved][P][P2]
     float* base = (float*)s.ws;
-    a.zeros = (const char*)base;
     if (a.split) {
         a.P = reinterpret_cast<bf16_t*>(base + 64);
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
