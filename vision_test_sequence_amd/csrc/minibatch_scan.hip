@@ -201,15 +201,13 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
                 xu[kb2] = u32x4{pack_bf2(X[2 * kb2][0], X[2 * kb2][1]), pack_bf2(X[2 * kb2][2], X[2 * kb2][3]),
                                 pack_bf2(X[2 * kb2 + 1][0], X[2 * kb2 + 1][1]),
                                 pack_bf2(X[2 * kb2 + 1][2], X[2 * kb2 + 1][3])};
-            // R = K X - V ;  R' = alpha R.  The two halves of the channel
-            // contraction are independent products added on the vector unit:
-            // a chained accumulation would wait for the first to finish.
-            v4f Rv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Rv[i] = -bf2f((bf16_t)vin[i]);
-            const v4f Ra = mfma32(as_v8bf(r.k[0]), as_v8bf(xu[0]), Rv);
-            const v4f Rb = mfma32(as_v8bf(r.k[1]), as_v8bf(xu[1]), v4f{0.f, 0.f, 0.f, 0.f});
-            const v4f R = Ra + Rb;
+            // R = K X - V ;  R' = alpha R, the two halves of the channel
+            // contraction chained on the matrix cores (fewer vector
+            // instructions: the waves' instruction streams bound the scan)
+            // -V from the transposed bf16 pairs: one sign flip per pair
+            const u32x2 vneg = __builtin_bit_cast(u32x2, vin) ^ u32x2{0x80008000u, 0x80008000u};
+            const v4f Rv{bflo(vneg[0]), bfhi(vneg[0]), bflo(vneg[1]), bfhi(vneg[1])};
+            const v4f R = mfma32(as_v8bf(r.k[1]), as_v8bf(xu[1]), mfma32(as_v8bf(r.k[0]), as_v8bf(xu[0]), Rv));
             const u32x2 rp2{pack_bf2(alpha * R[0], alpha * R[1]), pack_bf2(alpha * R[2], alpha * R[3])};
             // X += K^T R'
 #pragma unroll
