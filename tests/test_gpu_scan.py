@@ -82,6 +82,26 @@ def test_token_major_layout_and_shared_qk():
     _check(Kt, Kt, Vt, inp["W0"].to(dev), inp["eta"].to(dev), 16, BIDIR)
 
 
+@pytest.mark.parametrize("mode", [BIDIR, FWD, BWD])
+def test_token_major_output_with_guard_head(mode):
+    """Z written into a token-major buffer with a spare head between rows:
+    the outputs match the oracle and the spare head stays untouched (the
+    walk's overrun and empty slots store nothing)."""
+    import vision_test_sequence_amd as vt
+    banner(f"scan token-major Z, mode {mode}")
+    B, H, N, b = 2, 3, 203, 7
+    inp = wl.draw(B, H, N, seed=961, dtype="bf16", unit_rows=True)
+    dev = _dev()
+    K, Q, V, W0, eta = (inp[k].to(dev) for k in ("K", "Q", "V", "W0", "eta"))
+    buf = torch.full((B, N, H + 1, 64), float("nan"), dtype=K.dtype, device=dev)
+    Z = buf[:, :, :H].permute(0, 2, 1, 3)
+    vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, b, mode, Z=Z)
+    torch.cuda.synchronize()
+    assert torch.isnan(buf[:, :, H].float()).all()
+    Zr = oracle.linear_minibatch(f64(K), f64(Q), f64(V), f64(W0), f64(eta), b, mode)
+    assert slice_rel_err(f64(Z), Zr) <= TOL["bf16"]
+
+
 def test_deterministic():
     banner("scan determinism")
     import vision_test_sequence_amd as vt
