@@ -96,7 +96,10 @@ typedef enum {
     TTT_OP_LINEAR_FULLBATCH = 0,
     TTT_OP_DWCONV3X3_FULLBATCH = 1,
     TTT_OP_LINEAR_MINIBATCH_BIDIR = 2,
-    TTT_OP_LINEAR_FULLBATCH_BWD = 3
+    TTT_OP_LINEAR_FULLBATCH_BWD = 3,
+    TTT_OP_LAYER_FULLBATCH = 4 /* workspace of ttt_layer_fullbatch (sized by
+                                  ttt_layer_workspace_size; ttt_workspace_size
+                                  returns 0 for it) */
 } ttt_op;
 
 typedef struct {
@@ -209,6 +212,63 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
                                     const float* saved, ttt_view dK, ttt_view dQ, ttt_view dV,
                                     float* dW0, float* deta, void* ws, size_t ws_bytes,
                                     ttt_stream_t stream);
+
+/*
+ * Diagnostics
+ * -----------
+ * Which kernel a call would launch on the current device, and how the
+ * tokens of a slice are split over workgroups.  Pure functions of the
+ * problem and the device (no launch, no state).
+ *   kernel: TTT_KERNEL_LIN_RESIDENT -- one resident kernel exchanging
+ *             [A; C] partials (fp32 inputs, saved A/G, device-wide exchange
+ *             or one workgroup per slice);
+ *           TTT_KERNEL_LIN_RESIDENT_GX -- the bf16 resident kernel whose
+ *             splits exchange G_s = W0 A_s - C_s through one XCD's L2 (taken
+ *             when no saved buffer is passed);
+ *           TTT_KERNEL_LIN_STREAM -- token ranges too long to stay in LDS;
+ *           TTT_KERNEL_DWCONV -- the depthwise-conv kernel.
+ *   splits: workgroups per (image, head) slice; xcd_local: 1 when the
+ *   splits of a slice exchange through one XCD's L2, 0 for device-scope
+ *   atomics; fused (layer query): 1 when ttt_layer_fullbatch is one launch.
+ * op TTT_OP_LINEAR_FULLBATCH (with_saved: whether a saved buffer is passed)
+ * or TTT_OP_DWCONV3X3_FULLBATCH; other ops are TTT_ERR_UNSUPPORTED.
+ * B == 0 or H == 0 gives all zeros.
+ *
+ * Environment switches read at every call: TTT_EXCHANGE=device makes split
+ * slices use the device-scope exchange (plain block mapping) even where
+ * the XCD-local one applies; TTT_TEST_EXCHANGE_GIVEUP=1 makes every slice
+ * barrier give up after a few polls (the failure path below, for tests).
+ */
+enum {
+    TTT_KERNEL_LIN_RESIDENT = 1,
+    TTT_KERNEL_LIN_RESIDENT_GX = 2,
+    TTT_KERNEL_LIN_STREAM = 3,
+    TTT_KERNEL_DWCONV = 4
+};
+typedef struct {
+    int32_t kernel, splits, xcd_local, fused;
+} ttt_plan_info;
+ttt_status ttt_plan_query(ttt_op op, const ttt_problem* p, int with_saved, ttt_plan_info* out);
+ttt_status ttt_layer_plan_query(const ttt_problem* lin, const ttt_problem* conv, int32_t* fused);
+
+/*
+ * Exchange failures.  The workgroups of a split slice meet at barriers in
+ * the workspace; a wait is bounded (about a second).  A slice whose
+ * workgroups never all arrive (the device did not keep the grid resident,
+ * e.g. other kernels occupied it) marks its counter line failed: that
+ * slice's outputs (Z, and A/G or g when saved) are NaN in that call and in
+ * every later call on the same workspace, and the call still returns
+ * TTT_OK (the failure happens after the launch).
+ * ttt_workspace_exchange_failed: *failed = 1 when any counter line of the
+ *   workspace `ws` of operation `op` has failed.  Waits for `stream`
+ *   (hipStreamSynchronize) and copies the failure words to the host.
+ * ttt_workspace_reset: zero-fills ws (hipMemsetAsync on `stream`): the
+ *   workspace is then as good as a fresh zero-filled one.  Not for use
+ *   inside HIP graph capture.
+ */
+ttt_status ttt_workspace_exchange_failed(ttt_op op, const void* ws, size_t ws_bytes, int32_t* failed,
+                                         ttt_stream_t stream);
+ttt_status ttt_workspace_reset(void* ws, size_t ws_bytes, ttt_stream_t stream);
 
 #ifdef __cplusplus
 }

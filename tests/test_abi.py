@@ -281,3 +281,37 @@ def test_layer_errors():
     # (disjoint head ranges of one output tensor are accepted: the GPU
     # layer tests run them; no case here may pass validation, which would
     # launch on the fake addresses)
+
+
+def test_plan_and_workspace_query_errors():
+    L = vt.lib()
+    info = bd.PlanInfo()
+    p = P(B=8, H=2, N=6084)
+    assert L.ttt_plan_query(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p), 0, None) == 1      # NULL_POINTER
+    assert L.ttt_plan_query(bd.OP_LINEAR_FULLBATCH, None, 0, ctypes.byref(info)) == 1
+    assert L.ttt_plan_query(bd.OP_LINEAR_FULLBATCH, ctypes.byref(P(N=0)), 0, ctypes.byref(info)) == 2
+    assert L.ttt_plan_query(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(p), 0, ctypes.byref(info)) == 5
+    assert L.ttt_plan_query(bd.OP_DWCONV3X3_FULLBATCH, ctypes.byref(P(N=100, gh=9, gw=10)), 0,
+                            ctypes.byref(info)) == 2
+    # an empty batch plans nothing
+    assert L.ttt_plan_query(bd.OP_LINEAR_FULLBATCH, ctypes.byref(P(B=0)), 0, ctypes.byref(info)) == 0
+    assert (info.kernel, info.splits) == (0, 0)
+    # on any device (or none) a plan names one of the kernels
+    assert L.ttt_plan_query(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p), 0, ctypes.byref(info)) == 0
+    assert info.kernel in (bd.KERNEL_LIN_RESIDENT, bd.KERNEL_LIN_RESIDENT_GX, bd.KERNEL_LIN_STREAM)
+    assert info.splits >= 1
+    f = ctypes.c_int32(7)
+    assert L.ttt_layer_plan_query(ctypes.byref(p), ctypes.byref(P(N=100)), None) == 1
+    assert L.ttt_layer_plan_query(ctypes.byref(p), ctypes.byref(P(N=100, gh=9, gw=10)), ctypes.byref(f)) == 2
+    # workspace queries: argument errors come before any HIP call
+    assert L.ttt_workspace_exchange_failed(bd.OP_LINEAR_FULLBATCH, addr(1), 4096, None, None) == 1
+    assert L.ttt_workspace_exchange_failed(bd.OP_LINEAR_FULLBATCH, None, 4096, ctypes.byref(f), None) == 1
+    assert L.ttt_workspace_exchange_failed(bd.OP_LINEAR_FULLBATCH, addr(1) + 16, 4096, ctypes.byref(f), None) == 4
+    assert L.ttt_workspace_exchange_failed(9, addr(1), 4096, ctypes.byref(f), None) == 5
+    f.value = 7
+    assert L.ttt_workspace_exchange_failed(bd.OP_LINEAR_FULLBATCH, None, 0, ctypes.byref(f), None) == 0
+    assert f.value == 0
+    assert L.ttt_workspace_exchange_failed(bd.OP_LINEAR_MINIBATCH_BIDIR, addr(1), 4096, ctypes.byref(f),
+                                           None) == 0 and f.value == 0  # the scan has no counters
+    assert L.ttt_workspace_reset(None, 0, None) == 0
+    assert L.ttt_workspace_reset(None, 256, None) == 1

@@ -128,3 +128,28 @@ def test_workspace_shared_across_shapes():
     for B, H, N, b, seed in [(4, 6, 6400, 16, 990), (2, 3, 196, 4, 991), (2, 2, 2000, 16, 992),
                              (1, 1, 37, 5, 993), (4, 6, 6400, 16, 994), (3, 1, 300, 7, 995)]:
         _check(*_on(wl.draw(B, H, N, seed=seed, dtype="bf16", unit_rows=True)), b, BIDIR)
+
+
+@pytest.mark.parametrize("mode", [FWD, BWD, BIDIR])
+def test_one_token_views_with_zero_token_stride(mode):
+    """N = 1 views may carry any token stride (here 0 for every view): the
+    empty slots of the mini-batch must read zeros and store nothing, so the
+    one token gets the value the oracle gives it."""
+    import vision_test_sequence_amd as vt
+    banner(f"scan N=1 b=16 zero token stride mode {mode}")
+    B, H = 2, 3
+    inp = wl.draw(B, H, 1, seed=1001 + mode, dtype="bf16", unit_rows=True)
+    dev = _dev()
+
+    def zero_stride(t):
+        base = t.contiguous().to(dev)
+        return base.as_strided((B, H, 1, 64), (H * 64, 64, 0, 1))
+
+    K, Q, V = (zero_stride(inp[k]) for k in "KQV")
+    W0, eta = inp["W0"].to(dev), inp["eta"].to(dev)
+    Zbuf = torch.full((B * H * 64,), float("nan"), dtype=K.dtype, device=dev)
+    Z = Zbuf.as_strided((B, H, 1, 64), (H * 64, 64, 0, 1))
+    vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 16, mode, Z=Z)
+    torch.cuda.synchronize()
+    Zr = oracle.linear_minibatch(f64(K), f64(Q), f64(V), f64(W0), f64(eta), 16, mode)
+    assert slice_rel_err(f64(Z), Zr) <= TOL["bf16"]

@@ -12,8 +12,13 @@ from .binding import (  # noqa: F401
     BIDIR_AVG,
     FORWARD_ONLY,
     BACKWARD_ONLY,
+    exchange_failures,
     lib,
     library_path,
+    plan_dwconv,
+    plan_layer_fused,
+    plan_linear,
+    reset_workspaces,
     ttt_dwconv3x3_fullbatch,
     ttt_layer_fullbatch,
     ttt_linear_fullbatch,

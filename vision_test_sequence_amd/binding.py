@@ -26,6 +26,12 @@ OP_LINEAR_FULLBATCH = 0
 OP_DWCONV3X3_FULLBATCH = 1
 OP_LINEAR_MINIBATCH_BIDIR = 2
 OP_LINEAR_FULLBATCH_BWD = 3
+OP_LAYER_FULLBATCH = 4
+
+KERNEL_LIN_RESIDENT = 1
+KERNEL_LIN_RESIDENT_GX = 2
+KERNEL_LIN_STREAM = 3
+KERNEL_DWCONV = 4
 
 STATUS_NAMES = [
     "TTT_OK", "TTT_ERR_NULL_POINTER", "TTT_ERR_BAD_SHAPE", "TTT_ERR_BAD_STRIDE",
@@ -35,7 +41,8 @@ STATUS_NAMES = [
 
 EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size", "ttt_linear_fullbatch",
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
-            "ttt_layer_fullbatch")
+            "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
+            "ttt_workspace_exchange_failed", "ttt_workspace_reset")
 
 
 class TTTError(RuntimeError):
@@ -55,6 +62,11 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int), ("grid_h", ctypes.c_int32),
                 ("grid_w", ctypes.c_int32), ("minibatch", ctypes.c_int32), ("mode", ctypes.c_int)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("splits", ctypes.c_int32), ("xcd_local", ctypes.c_int32),
+                ("fused", ctypes.c_int32)]
 
 
 _lib = None
@@ -92,6 +104,10 @@ def lib() -> ctypes.CDLL:
                                                    View, fp, fp, vp, sz, vp]
             L.ttt_layer_fullbatch.argtypes = [P, View, View, View, fp, fp, View, P, View, View, View, fp, fp,
                                               View, vp, sz, vp]
+            L.ttt_plan_query.argtypes = [ctypes.c_int, P, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+            L.ttt_layer_plan_query.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
+            L.ttt_workspace_exchange_failed.argtypes = [ctypes.c_int, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
+            L.ttt_workspace_reset.argtypes = [vp, sz, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -130,24 +146,77 @@ def _stream(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-_ws: Dict[Tuple[int, object], torch.Tensor] = {}
+_ws: Dict[Tuple[int, int, int], torch.Tensor] = {}
 
 
-def workspace(op, prob: Optional[Problem], device: torch.device, need: Optional[int] = None
+def workspace(op: int, prob: Optional[Problem], device: torch.device, need: Optional[int] = None
               ) -> Tuple[Optional[int], int]:
-    """Zero-filled scratch for `op`, cached per (device, op); grows on demand.
-    The library leaves its counters at zero after every call, so one buffer
-    serves consecutive calls of that op on one stream."""
+    """Zero-filled scratch for `op`, cached per (device, stream, op); grows on
+    demand.  The library leaves its counters at zero after every call, so one
+    buffer serves consecutive calls of that op on one stream (calls on
+    different streams get different buffers: they may overlap in time)."""
     if need is None:
         need = int(lib().ttt_workspace_size(op, ctypes.byref(prob)))
     if need == 0:
         return None, 0
-    key = (device.index if device.index is not None else torch.cuda.current_device(), op)
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev, _stream(torch.device("cuda", dev)), op)
     buf = _ws.get(key)
     if buf is None or buf.numel() < need:
         buf = torch.zeros(need, dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf.data_ptr(), buf.numel()
+
+
+def exchange_failures():
+    """(device, stream, op) of every cached workspace whose split-slice
+    exchange has failed (its slices' outputs are NaN until reset); waits for
+    each workspace's stream."""
+    bad = []
+    for (dev, stream, op), buf in list(_ws.items()):
+        failed = ctypes.c_int32(0)
+        with torch.cuda.device(dev):
+            st = lib().ttt_workspace_exchange_failed(op, buf.data_ptr(), buf.numel(), ctypes.byref(failed), stream)
+        _check(st, "ttt_workspace_exchange_failed")
+        if failed.value:
+            bad.append((dev, stream, op))
+    return bad
+
+
+def reset_workspaces() -> None:
+    """Zero-fill every cached workspace on its stream (clears failed exchanges)."""
+    for (dev, stream, op), buf in list(_ws.items()):
+        with torch.cuda.device(dev):
+            _check(lib().ttt_workspace_reset(buf.data_ptr(), buf.numel(), stream), "ttt_workspace_reset")
+
+
+def plan_linear(B: int, H: int, N: int, dtype: int = TTT_BF16, with_saved: bool = False) -> PlanInfo:
+    """Kernel, splits per slice and exchange protocol of ttt_linear_fullbatch
+    for this shape on the current device."""
+    p = Problem(B, H, N, 64, dtype, 0, 0, 0, 0)
+    out = PlanInfo()
+    _check(lib().ttt_plan_query(OP_LINEAR_FULLBATCH, ctypes.byref(p), int(with_saved), ctypes.byref(out)),
+           "ttt_plan_query")
+    return out
+
+
+def plan_dwconv(B: int, H: int, grid_h: int, grid_w: int, dtype: int = TTT_BF16) -> PlanInfo:
+    p = Problem(B, H, grid_h * grid_w, 64, dtype, grid_h, grid_w, 0, 0)
+    out = PlanInfo()
+    _check(lib().ttt_plan_query(OP_DWCONV3X3_FULLBATCH, ctypes.byref(p), 0, ctypes.byref(out)),
+           "ttt_plan_query")
+    return out
+
+
+def plan_layer_fused(lin: Tuple[int, int, int], conv: Tuple[int, int, int, int], dtype: int = TTT_BF16) -> bool:
+    """Whether ttt_layer_fullbatch runs as one launch: lin = (B, H, N),
+    conv = (B, H, grid_h, grid_w)."""
+    pl = Problem(lin[0], lin[1], lin[2], 64, dtype, 0, 0, 0, 0)
+    pc = Problem(conv[0], conv[1], conv[2] * conv[3], 64, dtype, conv[2], conv[3], 0, 0)
+    f = ctypes.c_int32(0)
+    _check(lib().ttt_layer_plan_query(ctypes.byref(pl), ctypes.byref(pc), ctypes.byref(f)),
+           "ttt_layer_plan_query")
+    return bool(f.value)
 
 
 def _check(st: int, where: str) -> None:
@@ -224,7 +293,7 @@ def ttt_layer_fullbatch(Kl, Ql, Vl, W0, eta_l, Kc, Qc, Vc, w0, eta_c, grid_h: in
     pl = problem(Kl)
     pc = problem(Kc, grid=(grid_h, grid_w))
     need = int(lib().ttt_layer_workspace_size(ctypes.byref(pl), ctypes.byref(pc)))
-    ws, wsb = workspace("layer", None, Kl.device, need)
+    ws, wsb = workspace(OP_LAYER_FULLBATCH, None, Kl.device, need)
     st = lib().ttt_layer_fullbatch(ctypes.byref(pl), view(Kl), view(Ql), view(Vl), W0.data_ptr(),
                                    eta_l.data_ptr(), view(Zl), ctypes.byref(pc), view(Kc), view(Qc),
                                    view(Vc), w0.data_ptr(), eta_c.data_ptr(), view(Zc), ws, wsb,

@@ -8,6 +8,8 @@
 #include <initializer_list>
 #include <atomic>
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "internal.hpp"
 #include "common.hpp"
@@ -138,10 +140,34 @@ int device_cus() {
 
 ttt_status hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_HIP; }
 
+// Diagnostic switches, read from the environment at every call (the library
+// keeps no state of its own for them):
+//  * TTT_EXCHANGE=device -- split slices exchange through device-scope
+//    atomics with the plain block mapping even on a 256-CU MI355X (the
+//    protocol any other part or partition mode gets);
+//  * TTT_TEST_EXCHANGE_GIVEUP=1 -- every slice barrier waits for an
+//    unreachable count and gives up after a few polls: the failure path of
+//    the exchange, with every kernel still ending normally.
+struct Knobs {
+    unsigned spin, tbias;
+    bool device_exchange;
+};
+Knobs knobs() {
+    Knobs k{kSpinLimit, 0u, false};
+    const char* e = getenv("TTT_EXCHANGE");
+    if (e && strcmp(e, "device") == 0) k.device_exchange = true;
+    const char* g = getenv("TTT_TEST_EXCHANGE_GIVEUP");
+    if (g && strcmp(g, "1") == 0) {
+        k.spin = 64;
+        k.tbias = 1u << 24;
+    }
+    return k;
+}
+
 // The XCD-local exchange relies on MI355X's whole-device (SPX) layout: 256
 // CUs in 8 XCDs, workgroup i on XCD i % 8.  The kernels also check the XCC
 // id of every workgroup and poison their outputs with NaN if it differs.
-bool xcd_local_ok() { return device_cus() == 256; }
+bool xcd_local_ok(const Knobs& k) { return device_cus() == 256 && !k.device_exchange; }
 
 } // namespace
 
@@ -172,6 +198,7 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
         return conv_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
     case TTT_OP_LINEAR_MINIBATCH_BIDIR: return scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
     case TTT_OP_LINEAR_FULLBATCH_BWD: return lin_bwd_ws_bytes(p->B, p->H, p->N);
+    case TTT_OP_LAYER_FULLBATCH: return 0; // two problems: ttt_layer_workspace_size
     }
     return 0;
 }
@@ -181,6 +208,9 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
 static ttt_status plan_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V, View4 Z, const float* W0,
                                  const float* eta, float* saved, void* ws, LinFwdLaunch& a, int& resident) {
     a = LinFwdLaunch{};
+    const Knobs kn = knobs();
+    a.spin = kn.spin;
+    a.tbias = kn.tbias;
     a.K = K; a.Q = Q; a.V = V; a.Z = Z;
     a.W0 = W0; a.eta = eta; a.saved = saved;
     a.B = p->B; a.H = p->H; a.N = p->N;
@@ -193,7 +223,7 @@ static ttt_status plan_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V
         while (S > 1 && (long long)S * padded > cap) S /= 2; // stays a power of two
     }
     a.S = S;
-    a.xcd = (S > 1 && xcd_local_ok()) ? 1 : 0;
+    a.xcd = (S > 1 && xcd_local_ok(kn)) ? 1 : 0;
     if (S > 1) {
         // workspace: [fixed counter block][partials, Smax per slice][W1 per slice]
         char* base = (char*)ws;
@@ -226,7 +256,10 @@ static ConvLaunch plan_conv_call(const ttt_problem* p, View4 K, View4 Q, View4 V
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
     a.cap = device_cus() * conv_resident_per_cu(a.bf16);
-    a.xcd_ok = xcd_local_ok() ? 1 : 0;
+    const Knobs kn = knobs();
+    a.xcd_ok = xcd_local_ok(kn) ? 1 : 0;
+    a.spin = kn.spin;
+    a.tbias = kn.tbias;
     return a;
 }
 
@@ -385,13 +418,21 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     // buffer offsets, walking up to 512 tokens past either end
     const int64_t span_lim = (int64_t)1 << 31;
     for (const ttt_view* w : {&K, &Q, &V, &Z})
-        if ((int64_t)(p->N + 512) * w->stride_n * 2 >= span_lim) return TTT_ERR_UNSUPPORTED;
+        if ((int64_t)(p->N + 512) * std::max<int64_t>(w->stride_n, p->d) * 2 >= span_lim)
+            return TTT_ERR_UNSUPPORTED;
     const size_t need = scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
     if ((st = check_ws(ws, ws_bytes, need, &out[1])) != TTT_OK) return st;
     if ((st = check_aliasing(in, 5, out, 2)) != TTT_OK) return st;
 
     ScanLaunch a{};
     a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    if (p->N == 1) {
+        // a one-token view may carry any stride_n; the kernel addresses the
+        // empty slots of a mini-batch at multiples of stride_n, which must
+        // then lie past the token's row (their loads return zeros and their
+        // stores are dropped there)
+        for (View4* w : {&a.K, &a.Q, &a.V, &a.Z}) w->sn = std::max<long long>(w->sn, p->d);
+    }
     a.W0 = W0; a.eta = eta;
     a.B = p->B; a.H = p->H; a.N = p->N; a.b = p->minibatch; a.mode = (int)p->mode;
     a.bf16 = p->dtype == TTT_BF16;
@@ -446,6 +487,102 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
         a.saved = sv;
     }
     return hip_status(launch_lin_bwd(a, (hipStream_t)stream));
+}
+
+ttt_status ttt_plan_query(ttt_op op, const ttt_problem* p, int with_saved, ttt_plan_info* out) {
+    if (!out) return TTT_ERR_NULL_POINTER;
+    *out = ttt_plan_info{0, 0, 0, 0};
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (noop) return TTT_OK;
+    if (op == TTT_OP_LINEAR_FULLBATCH) {
+        LinFwdLaunch a;
+        int resident = 0;
+        const View4 none{nullptr, 0, 0, 0}, zv{(void*)16, 0, 0, 0};
+        static float dummy_saved;
+        st = plan_fullbatch(p, none, none, none, zv, nullptr, nullptr, with_saved ? &dummy_saved : nullptr,
+                            nullptr, a, resident);
+        if (st != TTT_OK) return st;
+        out->kernel = lin_fwd_kernel(a, resident);
+        out->splits = a.S;
+        out->xcd_local = a.xcd;
+        return TTT_OK;
+    }
+    if (op == TTT_OP_DWCONV3X3_FULLBATCH) {
+        if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N) return TTT_ERR_BAD_SHAPE;
+        const View4 none{nullptr, 0, 0, 0};
+        const ConvLaunch c = plan_conv_call(p, none, none, none, none, nullptr, nullptr, nullptr, nullptr);
+        int S = 0, x = 0;
+        conv_plan_info(c, &S, &x);
+        out->kernel = TTT_KERNEL_DWCONV;
+        out->splits = S;
+        out->xcd_local = x;
+        return TTT_OK;
+    }
+    return TTT_ERR_UNSUPPORTED;
+}
+
+ttt_status ttt_layer_plan_query(const ttt_problem* lin, const ttt_problem* conv, int32_t* fused) {
+    if (!fused) return TTT_ERR_NULL_POINTER;
+    *fused = 0;
+    bool lnoop = false, cnoop = false;
+    ttt_status st = check_problem(lin, &lnoop);
+    if (st != TTT_OK) return st;
+    if ((st = check_problem(conv, &cnoop)) != TTT_OK) return st;
+    if (conv->grid_h <= 0 || conv->grid_w <= 0 || (int64_t)conv->grid_h * conv->grid_w != conv->N)
+        return TTT_ERR_BAD_SHAPE;
+    if (lnoop || cnoop) return TTT_OK;
+    LinFwdLaunch l;
+    int resident = 0;
+    const View4 none{nullptr, 0, 0, 0}, zv{(void*)16, 0, 0, 0};
+    if ((st = plan_fullbatch(lin, none, none, none, zv, nullptr, nullptr, nullptr, nullptr, l, resident)) != TTT_OK)
+        return st;
+    const ConvLaunch c = plan_conv_call(conv, none, none, none, zv, nullptr, nullptr, nullptr, nullptr);
+    *fused = layer_would_fuse(l, resident, c) ? 1 : 0;
+    return TTT_OK;
+}
+
+// Counter blocks of each workspace kind: linear, conv and backward
+// workspaces start with one; the layer workspace holds the conv block at 0
+// and the linear block right after it; the scan's has none.
+static int counter_blocks(ttt_op op) {
+    switch (op) {
+    case TTT_OP_LINEAR_FULLBATCH:
+    case TTT_OP_DWCONV3X3_FULLBATCH:
+    case TTT_OP_LINEAR_FULLBATCH_BWD: return 1;
+    case TTT_OP_LAYER_FULLBATCH: return 2;
+    default: return 0;
+    }
+}
+
+ttt_status ttt_workspace_exchange_failed(ttt_op op, const void* ws, size_t ws_bytes, int32_t* failed,
+                                         ttt_stream_t stream) {
+    if (!failed) return TTT_ERR_NULL_POINTER;
+    *failed = 0;
+    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_LAYER_FULLBATCH) return TTT_ERR_UNSUPPORTED;
+    const int nb = counter_blocks(op);
+    if (nb == 0 || ws_bytes == 0) return TTT_OK;
+    if (!ws) return TTT_ERR_NULL_POINTER;
+    if ((uintptr_t)ws % 256) return TTT_ERR_MISALIGNED;
+    // a workspace smaller than its counter blocks has never run a split slice
+    const int lines = (int)std::min<size_t>((size_t)nb * kMaxBarrierSlices, ws_bytes / (kCounterStride * 4));
+    unsigned words[2 * kMaxBarrierSlices];
+    // the failure word of each counter line (4th word of its 256 bytes)
+    const char* src = (const char*)ws + 4 * sizeof(unsigned);
+    if (hipMemcpy2DAsync(words, sizeof(unsigned), src, kCounterStride * sizeof(unsigned), sizeof(unsigned), lines,
+                         hipMemcpyDeviceToHost, (hipStream_t)stream) != hipSuccess)
+        return TTT_ERR_HIP;
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return TTT_ERR_HIP;
+    for (int i = 0; i < lines; ++i)
+        if (words[i]) *failed = 1;
+    return TTT_OK;
+}
+
+ttt_status ttt_workspace_reset(void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    if (ws_bytes == 0) return TTT_OK;
+    if (!ws) return TTT_ERR_NULL_POINTER;
+    return hip_status(hipMemsetAsync(ws, 0, ws_bytes, (hipStream_t)stream));
 }
 
 } // extern "C"

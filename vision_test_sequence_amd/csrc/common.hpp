@@ -122,12 +122,16 @@ __device__ __forceinline__ unsigned* counter_at(unsigned* base, int slice) {
 // exchange loads behind it.
 __device__ __forceinline__ void drain_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// The wait is bounded (about a second of polling): a slice whose workgroups
-// never all arrive -- co-residency broken by other work on the device, or
-// a dispatch that placed two workgroups on one split (see map_block_xcc) --
-// marks its counter line as failed instead of hanging; every later check
-// of that line (slice_bad) reports it, in this call and in every later
-// call on the same workspace.
+// The wait is bounded (kSpinLimit polls, about a second): a slice whose
+// workgroups never all arrive -- co-residency broken by other work on the
+// device, or a dispatch that placed two workgroups on one split (see
+// map_block_xcc) -- marks its counter line as failed instead of hanging;
+// every later check of that line (slice_bad) reports it, in this call and
+// in every later call on the same workspace, until the host clears it
+// (ttt_workspace_reset); the host can read it (ttt_workspace_exchange_failed).
+// The poll limit and an offset added to every barrier target are kernel
+// arguments, so the host can force the give-up path (a tiny limit and an
+// unreachable target) with every kernel still ending normally.
 constexpr unsigned kSpinLimit = 1u << 21;
 // The slice's placement word (see placement_note) and the failure word
 // share the counter's line.
@@ -159,14 +163,14 @@ __device__ __forceinline__ bool slice_bad(const SliceWords& w, int S) {
 
 // A wave that made no exchange stores since the last barrier may pass
 // drain = false, keeping its loads in flight.
-__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain = true) {
+__device__ __forceinline__ void slice_barrier(unsigned* cnt, unsigned target, bool drain, unsigned spin) {
     if (drain) drain_vmem();
     __syncthreads();
     if (threadIdx.x == 0) {
         __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         unsigned it = 0;
         while (__hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target) {
-            if (++it == kSpinLimit) {
+            if (++it >= spin) {
                 __hip_atomic_store(failed_at(cnt), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 break;
             }

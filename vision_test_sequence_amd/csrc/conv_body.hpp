@@ -25,6 +25,8 @@ struct ConvArgs {
     int tpw;           // tiles per workgroup
     int slices;        // B * H
     int xcd;           // XCD-aware grid and XCD-local exchange
+    unsigned spin;     // slice barrier: poll limit
+    unsigned tbias;    // slice barrier: added to every target (0)
 };
 
 // Plan of a conv call (tiles, splits, the exchange protocol) as kernel
@@ -403,7 +405,7 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
             if constexpr (XC) P[e] = v;
             else xstore(P + e, v);
         }
-        slice_barrier(cnt, (unsigned)a.S);
+        slice_barrier(cnt, (unsigned)a.S + a.tbias, true, a.spin);
         SliceWords sw{}; // thread 0; loaded after the partials (see below)
         float gv[4];
         // Every workgroup sums all S partials itself (576 floats each, in

@@ -114,6 +114,8 @@ void conv_prepare(const ConvLaunch& l, ConvArgs& a, unsigned& grid) {
     a.R = p.R; a.TW = p.TW; a.ny = p.ny; a.nx = p.nx; a.S = p.S; a.tpw = p.tpw;
     a.slices = (int)slices;
     a.xcd = (p.S > 1 && l.xcd_ok) ? 1 : 0;
+    a.spin = l.spin;
+    a.tbias = l.tbias;
     if (p.S > 1) {
         // workspace layout as conv_ws_bytes: fixed counter block, partials
         char* base = (char*)l.ws;
@@ -122,6 +124,14 @@ void conv_prepare(const ConvLaunch& l, ConvArgs& a, unsigned& grid) {
     }
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
     grid = (unsigned)(gslices * p.S);
+}
+
+void conv_plan_info(const ConvLaunch& l, int* S, int* xcd) {
+    ConvArgs a;
+    unsigned grid = 0;
+    conv_prepare(l, a, grid);
+    *S = a.S;
+    *xcd = a.xcd;
 }
 
 hipError_t conv_launch_prepared(const ConvArgs& a0, unsigned grid, int bf16, hipStream_t stream) {

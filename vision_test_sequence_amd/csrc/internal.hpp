@@ -26,7 +26,13 @@ struct LinFwdLaunch {
     int S;            // workgroups per slice
     int xcd;          // XCD-aware block mapping
     int bf16;
+    unsigned spin;    // slice barrier: poll limit before giving up
+    unsigned tbias;   // slice barrier: added to every target (0 in normal use)
 };
+
+// Kernel a full-batch linear plan launches (plan queries of the C ABI).
+enum LinKernel { kLinResident = 1, kLinResidentGx = 2, kLinStream = 3 };
+int lin_fwd_kernel(const LinFwdLaunch& a, int resident);
 size_t lin_fwd_ws_bytes(int B, int H, int N);
 int lin_fwd_max_splits(int B, int H, int N);
 hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident);
@@ -45,13 +51,18 @@ struct ConvLaunch {
     void* part;       // null: the partials follow the counters in ws; else their own region
     int cap;          // resident workgroups of the device for the conv kernel
     int xcd_ok;       // the device is an MI355X in whole-device (SPX) mode
+    unsigned spin;    // slice barrier: poll limit before giving up
+    unsigned tbias;   // slice barrier: added to every target (0 in normal use)
 };
 size_t conv_ws_bytes(int B, int H, int gh, int gw);
+// Splits per slice and exchange protocol a conv plan uses (plan queries).
+void conv_plan_info(const ConvLaunch& l, int* S, int* xcd);
 hipError_t launch_conv(ConvLaunch a, hipStream_t stream);
 int conv_resident_per_cu(int bf16);
 
 // ---- one layer: linear heads and conv heads (one launch when they fit)
 hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch c, hipStream_t stream);
+bool layer_would_fuse(const LinFwdLaunch& l, int resident, const ConvLaunch& c);
 
 // ---- mini-batch scans -------------------------------------------------
 struct ScanLaunch {

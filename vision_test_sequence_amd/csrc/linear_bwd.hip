@@ -790,7 +790,9 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 size_t lin_bwd_ws_bytes(int B, int H, int N) {
     const size_t slices = (size_t)B * H;
     const size_t S = std::max(bwd_splits(B, H, N), bwd_splits_bf(N));
-    size_t bytes = align256(lin_fwd_ws_bytes(B, H, N));
+    // (the forward's workspace, at least its counter block: the workspace
+    // query reads the failure words there)
+    size_t bytes = align256(std::max(lin_fwd_ws_bytes(B, H, N), kCounterBytes));
     bytes += align256(slices * 8192 * 4);     // recomputed A, G
     bytes += align256(slices * S * 4096 * 4); // dW1 shares
     bytes += align256(slices * 8192 * 4);     // dW1, M
@@ -802,7 +804,7 @@ size_t lin_bwd_ws_bytes(int B, int H, int N) {
 }
 
 float* lin_bwd_saved_region(void* ws, int B, int H, int N) {
-    return (float*)((char*)ws + align256(lin_fwd_ws_bytes(B, H, N)));
+    return (float*)((char*)ws + align256(std::max(lin_fwd_ws_bytes(B, H, N), kCounterBytes)));
 }
 
 hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {

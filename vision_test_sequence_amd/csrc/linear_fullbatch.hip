@@ -339,7 +339,7 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
             xstore(a.part + pidx(c >> lgnc, split, mat, c & (nc - 1), r), (mat ? mC : mA)[r * MP + c]);
         }
     }
-    slice_barrier(cnt, (unsigned)a.S);
+    slice_barrier(cnt, (unsigned)a.S + a.tbias, true, a.spin);
 
     const float* blk = a.part + pidx(split, 0, 0, 0, 0);
     float* res = lds; // [mat][nc][64] reduced block
@@ -377,7 +377,7 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
             sv[4096 + r * 64 + c] = gv;
         }
     }
-    slice_barrier(cnt, 2u * a.S);
+    slice_barrier(cnt, 2u * a.S + a.tbias, true, a.spin);
     if (tid == 0) *sw = slice_words(cnt);
     keep_alive(pf);
     // W1 is complete in the workspace at a.w1 + slice*4096 (bf16 fragments
@@ -961,7 +961,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
     SliceWords sw{}; // thread 0, after the last slice barrier
     if (gx) {
         unsigned* cnt = counter_at(a.cnt, c.slice);
-        slice_barrier(cnt, (unsigned)a.S);
+        slice_barrier(cnt, (unsigned)a.S + a.tbias, true, a.spin);
         const float* w0g = g_lds(lds).w0s;
         switch (a.S) {
         case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
@@ -970,7 +970,7 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_resident(LinFwdLaunch a) 
         case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
         default: reduce_g<32>(a, c.slice, c.split, c.h, lds, true, w0g, MP, kGSumByte); break;
         }
-        slice_barrier(cnt, 2u * a.S);
+        slice_barrier(cnt, 2u * a.S + a.tbias, true, a.spin);
         if (tid == 0) sw = slice_words(cnt);
         keep_alive(pf);
     } else {
@@ -1130,7 +1130,7 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
 
     // ---- phase 2: reduce this workgroup's block of G, W1 as bf16 fragments
     unsigned* cnt = counter_at(a.cnt, c.slice);
-    slice_barrier(cnt, (unsigned)a.S, w < 4);
+    slice_barrier(cnt, (unsigned)a.S + a.tbias, w < 4, a.spin);
     // waves 0-3 reduce (waves 4-7 have Q loads in flight, which a gather of
     // theirs would queue behind)
     const float* w0src = w0_lds ? L.w0s : a.W0 + (long long)c.h * 4096;
@@ -1142,7 +1142,7 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
     default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
     }
-    slice_barrier(cnt, 2u * a.S, w < 4);
+    slice_barrier(cnt, 2u * a.S + a.tbias, w < 4, a.spin);
     keep_alive(pf);
     // W1's fragments load while every wave's Q loads (normally long since
     // landed) and the exchange outcome are waited for; the counter line's
@@ -1452,6 +1452,11 @@ bool lin_fwd_is_resident(int N, int S, int bf16) {
     return per <= (bf16 ? LinCfg<true>::tmax : LinCfg<false>::tmax);
 }
 
+int lin_fwd_kernel(const LinFwdLaunch& a, int resident) {
+    if (resident && a.xcd && a.bf16 && a.S > 1 && !a.saved) return kLinResidentGx;
+    return resident ? kLinResident : kLinStream;
+}
+
 hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     const long long slices = (long long)a.B * a.H;
     const long long gslices = a.xcd ? (slices + 7) / 8 * 8 : slices;
@@ -1459,10 +1464,11 @@ hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     dim3 block(kThreads);
     void* args[] = {&a};
     const void* fn;
-    if (resident && a.xcd && a.bf16 && a.S > 1 && !a.saved) {
+    const int kind = lin_fwd_kernel(a, resident);
+    if (kind == kLinResidentGx) {
         fn = (const void*)lin_fwd_resident_gx;
         block = dim3(kThreads8);
-    } else if (resident) {
+    } else if (kind == kLinResident) {
         if (a.xcd) fn = a.bf16 ? (const void*)lin_fwd_resident<true, true> : (const void*)lin_fwd_resident<false, true>;
         else fn = a.bf16 ? (const void*)lin_fwd_resident<true, false> : (const void*)lin_fwd_resident<false, false>;
     } else {
@@ -1470,6 +1476,14 @@ hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
         else fn = a.bf16 ? (const void*)lin_fwd_stream<true, false> : (const void*)lin_fwd_stream<false, false>;
     }
     return hipLaunchKernel(fn, grid, block, args, 0, stream);
+}
+
+bool layer_would_fuse(const LinFwdLaunch& l, int resident, const ConvLaunch& cl) {
+    if ((long long)l.B * l.H <= 0 || (long long)cl.B * cl.H <= 0) return false;
+    ConvArgs c;
+    unsigned cgrid = 0;
+    conv_prepare(cl, c, cgrid);
+    return layer_fusable(l, resident, c, cl.bf16);
 }
 
 hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch cl, hipStream_t stream) {
