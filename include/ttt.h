@@ -137,6 +137,25 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
                                 ttt_stream_t stream);
 
 /*
+ * ttt_linear_fullbatch for callers that cannot allocate (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation and results bit for bit, without a caller
+ * workspace.  Its scratch is a fixed 10.5 MiB device array inside the
+ * library (enough for every problem shape), one copy per device, held
+ * until the process ends; the call allocates and frees nothing.  Before its
+ * kernel each call zeroes the scratch's counters with a small kernel (no
+ * memset node), so a failed exchange of one call does not carry over.
+ * Every call on a device shares that device's scratch: calls that may
+ * overlap in time on one device (two streams, two threads) race and must
+ * not be issued.  Arguments, errors and outputs as ttt_linear_fullbatch; a
+ * problem needing more scratch than the array holds would be
+ * TTT_ERR_WORKSPACE_TOO_SMALL (no valid shape does).
+ */
+ttt_status ttt_linear_fullbatch_noalloc(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                        const float* W0, const float* eta, ttt_view Z,
+                                        float* saved, ttt_stream_t stream);
+
+/*
  * One full-batch gradient step of the 3x3 depthwise-conv inner model, then
  * apply (ViT3 observation 6; the article's layer recipe with one depthwise
  * conv head).  Tokens form a row-major grid_h x grid_w map per channel;

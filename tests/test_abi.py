@@ -315,3 +315,33 @@ def test_plan_and_workspace_query_errors():
                                            None) == 0 and f.value == 0  # the scan has no counters
     assert L.ttt_workspace_reset(None, 0, None) == 0
     assert L.ttt_workspace_reset(None, 256, None) == 1
+
+
+def test_noalloc_scratch_holds_every_linear_workspace():
+    # the allocation-free entry point's fixed scratch (10.5 MiB) must hold
+    # the workspace of any problem shape it accepts
+    L = vt.lib()
+    worst = 0
+    for slices in list(range(1, 300)) + [1000, 4096, 1 << 16]:
+        for N in (1, 100, 128, 129, 1000, 4096, 6084, 10000, 100000, 1 << 20, (1 << 31) - 1):
+            p = P(B=slices, H=1, N=N)
+            worst = max(worst, L.ttt_workspace_size(bd.OP_LINEAR_FULLBATCH, ctypes.byref(p)))
+    assert 0 < worst <= 21 << 19, worst
+
+
+def test_noalloc_argument_errors():
+    L = vt.lib()
+    p = P()
+    f = L.ttt_linear_fullbatch_noalloc
+    ok = dict(K=V(0), Q=V(1), Vv=V(2), Z=V(3))
+    call = lambda pp=p, K=ok["K"], Q=ok["Q"], Vv=ok["Vv"], W0=addr(10), eta=addr(11), Z=ok["Z"], saved=None: \
+        f(ctypes.byref(pp) if pp is not None else None, K, Q, Vv, W0, eta, Z, saved, None)
+    assert call(pp=None) == 1
+    assert call(pp=P(N=0)) == 2
+    assert call(pp=P(d=32)) == 5
+    assert call(W0=None) == 1
+    assert call(K=bd.View(0, 300 * 64, 100 * 64, 64)) == 1
+    assert call(W0=addr(10) + 4) == 4
+    assert call(Z=V(0)) == 6                       # Z overlaps K
+    assert call(saved=addr(1)) == 6                # saved overlaps Q
+    assert call(pp=P(B=0)) == 0                    # empty: no launch

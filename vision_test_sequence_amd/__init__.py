@@ -23,5 +23,6 @@ from .binding import (  # noqa: F401
     ttt_layer_fullbatch,
     ttt_linear_fullbatch,
     ttt_linear_fullbatch_bwd,
+    ttt_linear_fullbatch_noalloc,
     ttt_linear_minibatch_bidir,
 )

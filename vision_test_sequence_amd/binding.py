@@ -42,7 +42,7 @@ STATUS_NAMES = [
 EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size", "ttt_linear_fullbatch",
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
             "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
-            "ttt_workspace_exchange_failed", "ttt_workspace_reset")
+            "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc")
 
 
 class TTTError(RuntimeError):
@@ -108,6 +108,7 @@ def lib() -> ctypes.CDLL:
             L.ttt_layer_plan_query.argtypes = [P, P, ctypes.POINTER(ctypes.c_int32)]
             L.ttt_workspace_exchange_failed.argtypes = [ctypes.c_int, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
             L.ttt_workspace_reset.argtypes = [vp, sz, vp]
+            L.ttt_linear_fullbatch_noalloc.argtypes = [P, View, View, View, fp, fp, View, fp, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -249,6 +250,21 @@ def ttt_linear_fullbatch(K, Q, V, W0, eta, *, Z=None, saved=None):
                                     eta.data_ptr(), view(Z), _ptr(saved), ws, wsb,
                                     _stream(K.device))
     _check(st, "ttt_linear_fullbatch")
+    return Z
+
+
+def ttt_linear_fullbatch_noalloc(K, Q, V, W0, eta, *, Z=None, saved=None):
+    """ttt_linear_fullbatch on the library's fixed device scratch (no caller
+    workspace).  Calls on one device must not overlap in time.  Returns Z."""
+    B, H, N, d = K.shape
+    _param(W0, (H, d, d), "W0")
+    _param(eta, (H,), "eta")
+    if Z is None:
+        Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    p = problem(K)
+    st = lib().ttt_linear_fullbatch_noalloc(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
+                                            eta.data_ptr(), view(Z), _ptr(saved), _stream(K.device))
+    _check(st, "ttt_linear_fullbatch_noalloc")
     return Z
 
 

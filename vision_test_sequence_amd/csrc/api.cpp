@@ -7,6 +7,7 @@
 #include <algorithm>
 #include <initializer_list>
 #include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -169,6 +170,40 @@ Knobs knobs() {
 // id of every workgroup and poison their outputs with NaN if it differs.
 bool xcd_local_ok(const Knobs& k) { return device_cus() == 256 && !k.device_exchange; }
 
+// ---- scratch of the allocation-free entry point ----------------------
+// The full-batch linear workspace (counter block, [A; C] or G partials,
+// W1) for any problem: the planner keeps slices x splits <= 256 with
+// splits >= 2 only for <= 128 slices, so the workspace never exceeds
+// 64 KB + 256 x 32 KB + 128 x 16 KB = 10.06 MiB.  Each device that runs the
+// entry point holds its own copy until the process ends; its address is
+// taken once per device with hipGetSymbolAddress (the array's name in host
+// code is not a device address).
+constexpr size_t kScratchBytes = (size_t)21 << 19; // 10.5 MiB
+static __device__ __align__(256) char scratch[kScratchBytes];
+void* g_scratch_ptr[kMaxDev];
+hipError_t g_scratch_err[kMaxDev];
+std::once_flag g_scratch_once[kMaxDev];
+
+// This device's copy of `scratch` (the device must be current), or null.
+void* scratch_for_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return nullptr;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* ptr = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+    });
+    return g_scratch_ptr[dev];
+}
+
+// Zero n 16-byte words (the scratch's counter block before each call: the
+// previous call may have left a failed slice line).  A kernel, not a
+// memset node, so that callers may capture the call in a HIP graph.
+__global__ void zero_words16(uint4* p, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
 } // namespace
 
 extern "C" {
@@ -282,6 +317,36 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
     if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
     if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
 
+    return launch_fullbatch(p, v4(K), v4(Q), v4(V), v4(Z), W0, eta, saved, ws, (hipStream_t)stream);
+}
+
+ttt_status ttt_linear_fullbatch_noalloc(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                        const float* W0, const float* eta, ttt_view Z, float* saved,
+                                        ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK || noop) return st;
+    Span in[5], out[2];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    if (saved && (st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &out[1])) != TTT_OK)
+        return st;
+    if ((st = check_aliasing(in, 5, out, 2)) != TTT_OK) return st;
+    const size_t need = lin_fwd_ws_bytes(p->B, p->H, p->N);
+    if (need > kScratchBytes) return TTT_ERR_WORKSPACE_TOO_SMALL; // beyond the fixed scratch
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_for_current_device();
+        if (!ws) return TTT_ERR_HIP;
+        const int n16 = (int)(kCounterBytes / 16);
+        hipLaunchKernelGGL(zero_words16, dim3((n16 + 255) / 256), dim3(256), 0, (hipStream_t)stream, (uint4*)ws,
+                           n16);
+        if (hipGetLastError() != hipSuccess) return TTT_ERR_HIP;
+    }
     return launch_fullbatch(p, v4(K), v4(Q), v4(V), v4(Z), W0, eta, saved, ws, (hipStream_t)stream);
 }
 
