@@ -57,11 +57,13 @@ def _load():
         lib.oracle_linear_minibatch.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, i]
         lib.oracle_linear_fullbatch_bwd.argtypes = [i, i, i, i, dp, dp, dp, dp, dp, dp,
                                                     dp, dp, dp, dp, dp, i]
+        lib.oracle_dwconv3x3_fullbatch_bwd.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                                       dp, dp, dp, dp, dp, i]
         lib.oracle_num_chunks.argtypes = [i, i]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_linear_fullbatch, lib.oracle_dwconv3x3_fullbatch,
                   lib.oracle_linear_minibatch, lib.oracle_linear_fullbatch_bwd,
-                  lib.oracle_num_chunks, lib.oracle_max_threads):
+                  lib.oracle_num_chunks, lib.oracle_max_threads, lib.oracle_dwconv3x3_fullbatch_bwd):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -159,3 +161,24 @@ def linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, threads: int = 0):
                                                _p(dZ), _p(dK), _p(dQ), _p(dV), _p(dW0),
                                                _p(deta), int(threads)), "linear_fullbatch_bwd")
     return dK, dQ, dV, dW0, deta
+
+
+def dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, threads: int = 0):
+    """Gradients of sum(dZ * Z) through the depthwise 3x3 full-batch step.
+
+    Returns (dK, dQ, dV, dw0, deta); dw0 [H,d,3,3] and deta [H] are summed
+    over the batch.
+    """
+    K, Q, V, w0, eta, dZ = map(_f64, (K, Q, V, w0, eta, dZ))
+    B, H, N, d = K.shape
+    if grid_h * grid_w != N:
+        raise ValueError("grid_h*grid_w != N")
+    dK = np.empty_like(K)
+    dQ = np.empty_like(K)
+    dV = np.empty_like(K)
+    dw0 = np.empty((H, d, 3, 3))
+    deta = np.empty((H,))
+    _check(_load().oracle_dwconv3x3_fullbatch_bwd(B, H, grid_h, grid_w, d, _p(K), _p(Q), _p(V), _p(w0),
+                                                  _p(eta), _p(dZ), _p(dK), _p(dQ), _p(dV), _p(dw0),
+                                                  _p(deta), int(threads)), "dwconv3x3_fullbatch_bwd")
+    return dK, dQ, dV, dw0, deta

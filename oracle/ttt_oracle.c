@@ -382,3 +382,126 @@ int oracle_linear_fullbatch_bwd(int B, int H, int N, int d,
     free(peta);
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Gradient of L = sum <dZ, Z> through the depthwise 3x3 full-batch step
+ * (end-to-end training goes through the inner gradient: the ViT3 article,
+ * observation 1; the conv inner model: observation 6).  Per channel c of
+ * slice (b, h), reverse mode through the forward's steps in order
+ *   P[p] = sum_t w0[t] K[p+t] ; R = P - V ; g[t] = (2/N) sum_p R[p] K[p+t]
+ *   w1 = w0 - eta g ;           Z[p] = sum_t w1[t] Q[p+t]
+ * (t runs over the 9 taps (i-1, j-1); K, Q are zero outside the grid and a
+ * gradient aimed outside the grid is dropped):
+ *   dw1[t] = sum_p dZ[p] Q[p+t] ;       dQ[p+t] += w1[t] dZ[p]
+ *   dg = -eta dw1 ;  deta -= sum_t dw1[t] g[t] ;  dw0 += dw1
+ *   dR[p] = (2/N) sum_t dg[t] K[p+t] ;  dK[p+t] += (2/N) dg[t] R[p]
+ *   dV = -dR ;  dw0[t] += sum_p dR[p] K[p+t] ;  dK[p+t] += w0[t] dR[p]
+ * dw0 [H][d][3][3] and deta [H] are sums over the batch (b ascending).
+ * ---------------------------------------------------------------------- */
+int oracle_dwconv3x3_fullbatch_bwd(int B, int H, int gh, int gw, int d,
+                                   const double* K, const double* Q, const double* V,
+                                   const double* w0, const double* eta, const double* dZ,
+                                   double* dK, double* dQ, double* dV,
+                                   double* dw0, double* deta, int nthreads) {
+    if (B < 0 || H < 0 || gh <= 0 || gw <= 0 || d <= 0) return -1;
+    int N = gh * gw;
+    set_threads(nthreads);
+    long nwork = (long)B * H * d;
+    double* pw0 = (double*)calloc((size_t)(nwork > 0 ? nwork : 1) * 9, sizeof(double));
+    double* peta = (double*)calloc((size_t)(nwork > 0 ? nwork : 1), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long wkey = 0; wkey < nwork; ++wkey) {
+        int c = (int)(wkey % d);
+        long s = wkey / d;
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* w = w0 + ((size_t)h * d + c) * 9;
+        double e = eta[h];
+        double* R = (double*)malloc((size_t)N * sizeof(double));
+        double* dR = (double*)malloc((size_t)N * sizeof(double));
+        double g[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, w1[9], dw1[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, dg[9];
+        double* gw0 = pw0 + (size_t)wkey * 9;
+        /* forward: R and g */
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double pp = 0.0;
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j)
+                        pp += w[i * 3 + j] * tap(K, H, N, d, b, h, gh, gw, y + i - 1, x + j - 1, c);
+                R[y * gw + x] = pp - V[IDX4(b, h, y * gw + x, c)];
+            }
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x)
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j)
+                        g[i * 3 + j] += R[y * gw + x] * tap(K, H, N, d, b, h, gh, gw, y + i - 1, x + j - 1, c);
+        for (int t = 0; t < 9; ++t) {
+            g[t] *= 2.0 / (double)N;
+            w1[t] = w[t] - e * g[t];
+        }
+        /* reverse: Z = w1 conv Q */
+        for (int p = 0; p < N; ++p) dQ[IDX4(b, h, p, c)] = 0.0;
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double dz = dZ[IDX4(b, h, y * gw + x, c)];
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j) {
+                        int yy = y + i - 1, xx = x + j - 1;
+                        if (yy < 0 || yy >= gh || xx < 0 || xx >= gw) continue;
+                        dw1[i * 3 + j] += dz * Q[IDX4(b, h, yy * gw + xx, c)];
+                        dQ[IDX4(b, h, yy * gw + xx, c)] += w1[i * 3 + j] * dz;
+                    }
+            }
+        /* reverse: w1 = w0 - eta g */
+        double de = 0.0;
+        for (int t = 0; t < 9; ++t) {
+            dg[t] = -e * dw1[t];
+            de -= dw1[t] * g[t];
+            gw0[t] = dw1[t];
+        }
+        peta[wkey] = de;
+        /* reverse: g = (2/N) sum_p R[p] K[p+t] */
+        for (int p = 0; p < N; ++p) dK[IDX4(b, h, p, c)] = 0.0;
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double a = 0.0;
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j) {
+                        int yy = y + i - 1, xx = x + j - 1;
+                        if (yy < 0 || yy >= gh || xx < 0 || xx >= gw) continue;
+                        a += dg[i * 3 + j] * K[IDX4(b, h, yy * gw + xx, c)];
+                        dK[IDX4(b, h, yy * gw + xx, c)] += (2.0 / (double)N) * dg[i * 3 + j] * R[y * gw + x];
+                    }
+                dR[y * gw + x] = (2.0 / (double)N) * a;
+            }
+        /* reverse: R = P - V, P = w0 conv K */
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double r = dR[y * gw + x];
+                dV[IDX4(b, h, y * gw + x, c)] = -r;
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j) {
+                        int yy = y + i - 1, xx = x + j - 1;
+                        if (yy < 0 || yy >= gh || xx < 0 || xx >= gw) continue;
+                        gw0[i * 3 + j] += r * K[IDX4(b, h, yy * gw + xx, c)];
+                        dK[IDX4(b, h, yy * gw + xx, c)] += w[i * 3 + j] * r;
+                    }
+            }
+        free(R);
+        free(dR);
+    }
+    /* fixed-order sum over the batch */
+    for (int h = 0; h < H; ++h) {
+        deta[h] = 0.0;
+        for (int c = 0; c < d; ++c)
+            for (int t = 0; t < 9; ++t) dw0[((size_t)h * d + c) * 9 + t] = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int c = 0; c < d; ++c) {
+                long wkey = ((long)b * H + h) * d + c;
+                for (int t = 0; t < 9; ++t) dw0[((size_t)h * d + c) * 9 + t] += pw0[(size_t)wkey * 9 + t];
+                deta[h] += peta[wkey];
+            }
+    }
+    free(pw0);
+    free(peta);
+    return 0;
+}
