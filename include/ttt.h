@@ -97,9 +97,10 @@ typedef enum {
     TTT_OP_DWCONV3X3_FULLBATCH = 1,
     TTT_OP_LINEAR_MINIBATCH_BIDIR = 2,
     TTT_OP_LINEAR_FULLBATCH_BWD = 3,
-    TTT_OP_LAYER_FULLBATCH = 4 /* workspace of ttt_layer_fullbatch (sized by
-                                  ttt_layer_workspace_size; ttt_workspace_size
-                                  returns 0 for it) */
+    TTT_OP_LAYER_FULLBATCH = 4, /* workspace of ttt_layer_fullbatch (sized by
+                                   ttt_layer_workspace_size; ttt_workspace_size
+                                   returns 0 for it) */
+    TTT_OP_DWCONV3X3_FULLBATCH_BWD = 5
 } ttt_op;
 
 typedef struct {
@@ -171,6 +172,29 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
                                    const float* w0, const float* eta, ttt_view Z,
                                    float* saved, void* ws, size_t ws_bytes,
                                    ttt_stream_t stream);
+
+/*
+ * Backward of ttt_dwconv3x3_fullbatch for L = sum <dZ, Z> (end-to-end
+ * training through the inner update: ViT3 observation 1; the depthwise
+ * conv inner model: observation 6).  Per channel of a slice, t over the 9
+ * taps, with dw1[t] = sum_p dZ[p] Q[p+t] and dg = -eta_h dw1:
+ *   dQ[q] = sum_t w1[t] dZ[q-t],  dR[p] = (2/N) sum_t dg[t] K[p+t],
+ *   dV = -dR,  dK[q] = sum_t ((2/N) dg[t] R[q-t] + w0[t] dR[q-t])
+ *   (R = conv(K, w0) - V; R and dR are zero off the grid),
+ * and summed over the batch in b order:
+ *   dw0[h] = sum_b (dw1 + sum_p dR[p] K[p+t]),  deta[h] = -sum_b <dw1, g>.
+ * saved: the forward's g ([B][H][d][3][3], its saved output) or NULL to
+ *   recompute g from K and V.
+ * Out: dK, dQ, dV (views, dtype); dw0 float [H][d][3][3] and deta float [H]
+ *   (overwritten).  grid_h * grid_w must equal N.
+ * ws: ttt_workspace_size(TTT_OP_DWCONV3X3_FULLBATCH_BWD, p) bytes (no
+ *   zero-fill needed: every word is written before it is read).
+ */
+ttt_status ttt_dwconv3x3_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                       const float* w0, const float* eta, ttt_view dZ,
+                                       const float* saved, ttt_view dK, ttt_view dQ, ttt_view dV,
+                                       float* dw0, float* deta, void* ws, size_t ws_bytes,
+                                       ttt_stream_t stream);
 
 /*
  * One layer's full-batch steps in one call (the ViT3 layer recipe: linear

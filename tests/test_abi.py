@@ -345,3 +345,26 @@ def test_noalloc_argument_errors():
     assert call(Z=V(0)) == 6                       # Z overlaps K
     assert call(saved=addr(1)) == 6                # saved overlaps Q
     assert call(pp=P(B=0)) == 0                    # empty: no launch
+
+
+def test_conv_bwd_errors():
+    L = vt.lib()
+    p = P(B=2, H=3, N=100, gh=10, gw=10)
+    need = L.ttt_workspace_size(bd.OP_DWCONV3X3_FULLBATCH_BWD, ctypes.byref(p))
+    assert need > 0
+    assert L.ttt_workspace_size(bd.OP_DWCONV3X3_FULLBATCH_BWD, ctypes.byref(P(N=100, gh=9, gw=10))) == 0
+    f = L.ttt_dwconv3x3_fullbatch_bwd
+
+    def call(pp=p, saved=None, dK=V(6), dQ=V(7), dV=V(8), dw0=addr(12), deta=addr(13), ws=addr(20),
+             wsb=need, w0=addr(10)):
+        return f(ctypes.byref(pp), V(0), V(1), V(2), w0, addr(11), V(3), saved, dK, dQ, dV, dw0, deta,
+                 ws, wsb, None)
+    assert call(pp=P(N=100, gh=9, gw=10)) == 2          # grid does not cover N
+    assert call(pp=P(B=0, N=100, gh=10, gw=10)) == 0    # empty: no launch
+    assert call(dw0=None) == 1
+    assert call(w0=addr(10) + 4) == 4
+    assert call(dK=V(0)) == 6                           # dK overlaps K
+    assert call(dQ=V(6)) == 6                           # two outputs overlap
+    assert call(saved=addr(8)) == 6                     # saved overlaps the dV output
+    assert call(wsb=need - 1) == 7
+    assert call(ws=addr(20) + 16) == 4

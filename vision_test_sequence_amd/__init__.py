@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     plan_linear,
     reset_workspaces,
     ttt_dwconv3x3_fullbatch,
+    ttt_dwconv3x3_fullbatch_bwd,
     ttt_layer_fullbatch,
     ttt_linear_fullbatch,
     ttt_linear_fullbatch_bwd,

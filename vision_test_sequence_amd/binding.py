@@ -27,6 +27,7 @@ OP_DWCONV3X3_FULLBATCH = 1
 OP_LINEAR_MINIBATCH_BIDIR = 2
 OP_LINEAR_FULLBATCH_BWD = 3
 OP_LAYER_FULLBATCH = 4
+OP_DWCONV3X3_FULLBATCH_BWD = 5
 
 KERNEL_LIN_RESIDENT = 1
 KERNEL_LIN_RESIDENT_GX = 2
@@ -42,7 +43,7 @@ STATUS_NAMES = [
 EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size", "ttt_linear_fullbatch",
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
             "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
-            "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc")
+            "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc", "ttt_dwconv3x3_fullbatch_bwd")
 
 
 class TTTError(RuntimeError):
@@ -109,6 +110,8 @@ def lib() -> ctypes.CDLL:
             L.ttt_workspace_exchange_failed.argtypes = [ctypes.c_int, vp, sz, ctypes.POINTER(ctypes.c_int32), vp]
             L.ttt_workspace_reset.argtypes = [vp, sz, vp]
             L.ttt_linear_fullbatch_noalloc.argtypes = [P, View, View, View, fp, fp, View, fp, vp]
+            L.ttt_dwconv3x3_fullbatch_bwd.argtypes = [P, View, View, View, fp, fp, View, fp, View, View,
+                                                      View, fp, fp, vp, sz, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -358,3 +361,30 @@ def ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, *, saved=None, dK=None, dQ=No
                                         _stream(K.device))
     _check(st, "ttt_linear_fullbatch_bwd")
     return dK, dQ, dV, dW0, deta
+
+
+def ttt_dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, *, saved=None, dK=None,
+                                dQ=None, dV=None, dw0=None, deta=None):
+    """Backward of ttt_dwconv3x3_fullbatch for L = sum(dZ * Z).
+
+    saved: the forward's g (float32 [B,H,64,3,3]) or None to recompute it.
+    Returns (dK, dQ, dV, dw0, deta); dw0 [H,64,3,3] and deta [H] are float32
+    sums over the batch.
+    """
+    B, H, N, d = K.shape
+    _param(w0, (H, d, 3, 3), "w0")
+    _param(eta, (H,), "eta")
+    mk = lambda: torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    dK = mk() if dK is None else dK
+    dQ = mk() if dQ is None else dQ
+    dV = mk() if dV is None else dV
+    dw0 = torch.empty((H, d, 3, 3), dtype=torch.float32, device=K.device) if dw0 is None else dw0
+    deta = torch.empty((H,), dtype=torch.float32, device=K.device) if deta is None else deta
+    p = problem(K, grid=(grid_h, grid_w))
+    ws, wsb = workspace(OP_DWCONV3X3_FULLBATCH_BWD, p, K.device)
+    st = lib().ttt_dwconv3x3_fullbatch_bwd(ctypes.byref(p), view(K), view(Q), view(V), w0.data_ptr(),
+                                           eta.data_ptr(), view(dZ), _ptr(saved), view(dK), view(dQ),
+                                           view(dV), dw0.data_ptr(), deta.data_ptr(), ws, wsb,
+                                           _stream(K.device))
+    _check(st, "ttt_dwconv3x3_fullbatch_bwd")
+    return dK, dQ, dV, dw0, deta

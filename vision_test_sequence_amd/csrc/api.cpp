@@ -234,6 +234,9 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     case TTT_OP_LINEAR_MINIBATCH_BIDIR: return scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
     case TTT_OP_LINEAR_FULLBATCH_BWD: return lin_bwd_ws_bytes(p->B, p->H, p->N);
     case TTT_OP_LAYER_FULLBATCH: return 0; // two problems: ttt_layer_workspace_size
+    case TTT_OP_DWCONV3X3_FULLBATCH_BWD:
+        if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N) return 0;
+        return conv_bwd_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
     }
     return 0;
 }
@@ -374,6 +377,47 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
 
     const ConvLaunch a = plan_conv_call(p, v4(K), v4(Q), v4(V), v4(Z), w0, eta, saved, ws);
     return hip_status(launch_conv(a, (hipStream_t)stream));
+}
+
+ttt_status ttt_dwconv3x3_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                       const float* w0, const float* eta, ttt_view dZ, const float* saved,
+                                       ttt_view dK, ttt_view dQ, ttt_view dV, float* dw0, float* deta,
+                                       void* ws, size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N)
+        return TTT_ERR_BAD_SHAPE;
+    if (noop) return TTT_OK;
+    Span in[7], out[6];
+    int nin = 6;
+    if ((st = check_buf(dw0, (size_t)p->H * p->d * 9 * 4, 4, &out[3])) != TTT_OK) return st;
+    if ((st = check_buf(deta, (size_t)p->H * 4, 4, &out[4])) != TTT_OK) return st;
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(w0, (size_t)p->H * p->d * 9 * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(dZ, *p, &in[5])) != TTT_OK) return st;
+    if (saved) {
+        if ((st = check_buf(saved, (size_t)p->B * p->H * p->d * 9 * 4, 4, &in[6])) != TTT_OK) return st;
+        nin = 7;
+    }
+    if ((st = check_view(dK, *p, &out[0])) != TTT_OK) return st;
+    if ((st = check_view(dQ, *p, &out[1])) != TTT_OK) return st;
+    if ((st = check_view(dV, *p, &out[2])) != TTT_OK) return st;
+    const size_t need = conv_bwd_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
+    if ((st = check_ws(ws, ws_bytes, need, &out[5])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, nin, out, 6)) != TTT_OK) return st;
+
+    ConvBwdLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.dZ = v4(dZ);
+    a.dK = v4(dK); a.dQ = v4(dQ); a.dV = v4(dV);
+    a.w0 = w0; a.eta = eta; a.saved = saved; a.dw0 = dw0; a.deta = deta;
+    a.B = p->B; a.H = p->H; a.gh = p->grid_h; a.gw = p->grid_w;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    return hip_status(launch_conv_bwd(a, (hipStream_t)stream));
 }
 
 static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
@@ -625,7 +669,7 @@ ttt_status ttt_workspace_exchange_failed(ttt_op op, const void* ws, size_t ws_by
                                          ttt_stream_t stream) {
     if (!failed) return TTT_ERR_NULL_POINTER;
     *failed = 0;
-    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_LAYER_FULLBATCH) return TTT_ERR_UNSUPPORTED;
+    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_DWCONV3X3_FULLBATCH_BWD) return TTT_ERR_UNSUPPORTED;
     const int nb = counter_blocks(op);
     if (nb == 0 || ws_bytes == 0) return TTT_OK;
     if (!ws) return TTT_ERR_NULL_POINTER;

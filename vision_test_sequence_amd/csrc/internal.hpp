@@ -60,6 +60,21 @@ void conv_plan_info(const ConvLaunch& l, int* S, int* xcd);
 hipError_t launch_conv(ConvLaunch a, hipStream_t stream);
 int conv_resident_per_cu(int bf16);
 
+// ---- backward of the depthwise 3x3 step ----------------------------------
+struct ConvBwdLaunch {
+    View4 K, Q, V, dZ, dK, dQ, dV;
+    const float* w0;
+    const float* eta;
+    const float* saved; // nullable: the forward's g [slices][64][9]
+    float* dw0;
+    float* deta;
+    int B, H, gh, gw;
+    int bf16;
+    void* ws;           // conv_bwd_ws_bytes(...) bytes
+};
+size_t conv_bwd_ws_bytes(int B, int H, int gh, int gw);
+hipError_t launch_conv_bwd(const ConvBwdLaunch& a, hipStream_t stream);
+
 // ---- one layer: linear heads and conv heads (one launch when they fit)
 hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch c, hipStream_t stream);
 bool layer_would_fuse(const LinFwdLaunch& l, int resident, const ConvLaunch& c);
