@@ -59,6 +59,18 @@ def _load():
                                                     dp, dp, dp, dp, dp, i]
         lib.oracle_dwconv3x3_fullbatch_bwd.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp,
                                                        dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_fullbatch_ex.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_fullbatch_bwd_ex.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                                       dp, dp, dp, dp, dp, i]
+        lib.oracle_dwconv3x3_fullbatch_ex.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_dwconv3x3_fullbatch_bwd_ex.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                                          dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_minibatch_2w0.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_gradient_magnitude.argtypes = [i, i, i, i, i, dp, dp, dp, dp, i]
+        for f in (lib.oracle_linear_fullbatch_ex, lib.oracle_linear_fullbatch_bwd_ex,
+                  lib.oracle_dwconv3x3_fullbatch_ex, lib.oracle_dwconv3x3_fullbatch_bwd_ex,
+                  lib.oracle_linear_minibatch_2w0, lib.oracle_linear_gradient_magnitude):
+            f.restype = ctypes.c_int
         lib.oracle_num_chunks.argtypes = [i, i]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_linear_fullbatch, lib.oracle_dwconv3x3_fullbatch,
@@ -182,3 +194,83 @@ def dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, thre
                                                   _p(eta), _p(dZ), _p(dK), _p(dQ), _p(dV), _p(dw0),
                                                   _p(deta), int(threads)), "dwconv3x3_fullbatch_bwd")
     return dK, dQ, dV, dw0, deta
+
+
+L2 = 0
+DOT = 1
+
+
+def linear_fullbatch_ex(K, Q, V, W0, eta, loss: int = L2, steps: int = 1, threads: int = 0):
+    """`steps` full-batch gradient steps of the linear inner model under the
+    L2 or dot-product loss, then z = W q.  Returns (Z, W) with W [B,H,d,d]
+    the final inner weights."""
+    K, Q, V, W0, eta = map(_f64, (K, Q, V, W0, eta))
+    B, H, N, d = K.shape
+    Z = np.empty_like(K)
+    W = np.empty((B, H, d, d))
+    _check(_load().oracle_linear_fullbatch_ex(B, H, N, d, int(loss), int(steps), _p(K), _p(Q), _p(V), _p(W0),
+                                              _p(eta), _p(Z), _p(W), int(threads)), "linear_fullbatch_ex")
+    return Z, W
+
+
+def linear_fullbatch_bwd_ex(K, Q, V, W0, eta, dZ, loss: int = L2, threads: int = 0):
+    """linear_fullbatch_bwd under the L2 or dot-product loss."""
+    K, Q, V, W0, eta, dZ = map(_f64, (K, Q, V, W0, eta, dZ))
+    B, H, N, d = K.shape
+    out = [np.empty_like(K) for _ in range(3)] + [np.empty((H, d, d)), np.empty((H,))]
+    _check(_load().oracle_linear_fullbatch_bwd_ex(B, H, N, d, int(loss), _p(K), _p(Q), _p(V), _p(W0), _p(eta),
+                                                  _p(dZ), *(_p(o) for o in out), int(threads)),
+           "linear_fullbatch_bwd_ex")
+    return tuple(out)
+
+
+def dwconv3x3_fullbatch_ex(K, Q, V, w0, eta, grid_h: int, grid_w: int, loss: int = L2, threads: int = 0):
+    """dwconv3x3_fullbatch under the L2 or dot-product loss.  Returns (Z, g)."""
+    K, Q, V, w0, eta = map(_f64, (K, Q, V, w0, eta))
+    B, H, N, d = K.shape
+    if grid_h * grid_w != N:
+        raise ValueError("grid_h*grid_w != N")
+    Z = np.empty_like(K)
+    g = np.empty((B, H, d, 3, 3))
+    _check(_load().oracle_dwconv3x3_fullbatch_ex(B, H, grid_h, grid_w, d, int(loss), _p(K), _p(Q), _p(V),
+                                                 _p(w0), _p(eta), _p(Z), _p(g), int(threads)),
+           "dwconv3x3_fullbatch_ex")
+    return Z, g
+
+
+def dwconv3x3_fullbatch_bwd_ex(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, loss: int = L2,
+                               threads: int = 0):
+    """dwconv3x3_fullbatch_bwd under the L2 or dot-product loss."""
+    K, Q, V, w0, eta, dZ = map(_f64, (K, Q, V, w0, eta, dZ))
+    B, H, N, d = K.shape
+    if grid_h * grid_w != N:
+        raise ValueError("grid_h*grid_w != N")
+    out = [np.empty_like(K) for _ in range(3)] + [np.empty((H, d, 3, 3)), np.empty((H,))]
+    _check(_load().oracle_dwconv3x3_fullbatch_bwd_ex(B, H, grid_h, grid_w, d, int(loss), _p(K), _p(Q), _p(V),
+                                                     _p(w0), _p(eta), _p(dZ), *(_p(o) for o in out),
+                                                     int(threads)), "dwconv3x3_fullbatch_bwd_ex")
+    return tuple(out)
+
+
+def linear_minibatch_2w0(K, Q, V, W0, eta, minibatch: int, mode: int = FORWARD_BACKWARD_AVG,
+                         threads: int = 0):
+    """linear_minibatch with one initial state per direction: W0 [2,H,d,d]
+    (forward scan from W0[0], reverse scan from W0[1])."""
+    K, Q, V, W0, eta = map(_f64, (K, Q, V, W0, eta))
+    B, H, N, d = K.shape
+    if W0.shape != (2, H, d, d):
+        raise ValueError("W0 must be [2,H,d,d]")
+    Z = np.empty_like(K)
+    _check(_load().oracle_linear_minibatch_2w0(B, H, N, d, int(minibatch), int(mode), _p(K), _p(Q), _p(V),
+                                               _p(W0), _p(eta), _p(Z), int(threads)), "linear_minibatch_2w0")
+    return Z
+
+
+def linear_gradient_magnitude(K, V, W0, loss: int = L2, threads: int = 0):
+    """Per-token ||G_t||_F at W0 (the gradient magnitude map), [B,H,N]."""
+    K, V, W0 = map(_f64, (K, V, W0))
+    B, H, N, d = K.shape
+    out = np.empty((B, H, N))
+    _check(_load().oracle_linear_gradient_magnitude(B, H, N, d, int(loss), _p(K), _p(V), _p(W0), _p(out),
+                                                    int(threads)), "linear_gradient_magnitude")
+    return out

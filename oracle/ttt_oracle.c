@@ -39,6 +39,7 @@
  *
  * Every function returns 0 on success, -1 on a bad argument.
  */
+#include <math.h>
 #include <stdlib.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -503,5 +504,366 @@ int oracle_dwconv3x3_fullbatch_bwd(int B, int H, int gh, int gw, int d,
     }
     free(pw0);
     free(peta);
+    return 0;
+}
+
+/* ========================================================================
+ * Variants of the inner training (the ViT3 article's design space and its
+ * final recipe; the Vision-TTT notes' ablation on the initial state and its
+ * gradient-magnitude map).
+ *
+ * loss: 0 = the L2 reconstruction loss of the definitions above;
+ *       1 = the dot-product loss of the ViT3 recipe ("点积损失函数"),
+ *           read as l(W; k, v) = -<W k, v> (its token mean over the batch),
+ *           so G = -(1/N) sum_i v_i k_i^T: no W-dependent term.
+ * ====================================================================== */
+
+/* One full-batch gradient of the linear model at W (residual form for L2). */
+static void lin_grad(int N, int d, int loss, const double* K, const double* V, const double* W,
+                     double* G, double* r) {
+    memset(G, 0, (size_t)d * d * sizeof(double));
+    for (int i = 0; i < N; ++i) {
+        const double* k = K + (size_t)i * d;
+        const double* v = V + (size_t)i * d;
+        if (loss == 0) {
+            for (int o = 0; o < d; ++o) {
+                double a = 0.0;
+                for (int c = 0; c < d; ++c) a += W[(size_t)o * d + c] * k[c];
+                r[o] = a - v[o];
+            }
+            for (int o = 0; o < d; ++o)
+                for (int c = 0; c < d; ++c) G[(size_t)o * d + c] += (2.0 / (double)N) * r[o] * k[c];
+        } else {
+            for (int o = 0; o < d; ++o)
+                for (int c = 0; c < d; ++c) G[(size_t)o * d + c] -= (1.0 / (double)N) * v[o] * k[c];
+        }
+    }
+}
+
+/* `steps` full-batch gradient steps (epochs over the whole token set; the
+ * ViT3 article, observation 2), each gradient taken at the current W:
+ *   W <- W - eta_h G(W), steps times, from W0;  z_i = W q_i.
+ * W_out (nullable) receives the final W per slice, [B][H][d][d]. */
+int oracle_linear_fullbatch_ex(int B, int H, int N, int d, int loss, int steps,
+                               const double* K, const double* Q, const double* V,
+                               const double* W0, const double* eta,
+                               double* Z, double* W_out, int nthreads) {
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || loss < 0 || loss > 1 || steps < 1) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+    size_t dd = (size_t)d * d;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        int b = (int)(s / H), h = (int)(s % H);
+        double* W = (double*)malloc(dd * sizeof(double));
+        double* G = (double*)malloc(dd * sizeof(double));
+        double* r = (double*)malloc((size_t)d * sizeof(double));
+        memcpy(W, W0 + (size_t)h * dd, dd * sizeof(double));
+        for (int e = 0; e < steps; ++e) {
+            lin_grad(N, d, loss, K + IDX4(b, h, 0, 0), V + IDX4(b, h, 0, 0), W, G, r);
+            for (size_t t = 0; t < dd; ++t) W[t] -= eta[h] * G[t];
+        }
+        for (int i = 0; i < N; ++i) {
+            const double* q = Q + IDX4(b, h, i, 0);
+            double* z = Z + IDX4(b, h, i, 0);
+            for (int o = 0; o < d; ++o) {
+                double a = 0.0;
+                for (int c = 0; c < d; ++c) a += W[(size_t)o * d + c] * q[c];
+                z[o] = a;
+            }
+        }
+        if (W_out) memcpy(W_out + (size_t)s * dd, W, dd * sizeof(double));
+        free(W);
+        free(G);
+        free(r);
+    }
+    return 0;
+}
+
+/* Backward of one full-batch step under either loss (reverse mode as in
+ * oracle_linear_fullbatch_bwd).  Dot loss: G = -(1/N) sum v_i k_i^T, so
+ *   dG = -eta dW1 ; dv_i = -(1/N) dG k_i ; dk_i = -(1/N) dG^T v_i ; dW0 = dW1. */
+int oracle_linear_fullbatch_bwd_ex(int B, int H, int N, int d, int loss,
+                                   const double* K, const double* Q, const double* V,
+                                   const double* W0, const double* eta, const double* dZ,
+                                   double* dK, double* dQ, double* dV,
+                                   double* dW0, double* deta, int nthreads) {
+    if (loss == 0)
+        return oracle_linear_fullbatch_bwd(B, H, N, d, K, Q, V, W0, eta, dZ, dK, dQ, dV, dW0, deta, nthreads);
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || loss != 1) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+    size_t dd = (size_t)d * d;
+    double* pW0 = (double*)calloc((size_t)(nslice > 0 ? nslice : 1) * dd, sizeof(double));
+    double* peta = (double*)calloc((size_t)(nslice > 0 ? nslice : 1), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* W = W0 + (size_t)h * dd;
+        double e = eta[h];
+        double* G = (double*)malloc(dd * sizeof(double));
+        double* W1 = (double*)malloc(dd * sizeof(double));
+        double* dW1 = (double*)calloc(dd, sizeof(double));
+        double* dG = (double*)malloc(dd * sizeof(double));
+        double* r = (double*)malloc((size_t)d * sizeof(double));
+        lin_grad(N, d, 1, K + IDX4(b, h, 0, 0), V + IDX4(b, h, 0, 0), W, G, r);
+        for (size_t t = 0; t < dd; ++t) W1[t] = W[t] - e * G[t];
+        for (int i = 0; i < N; ++i) {
+            const double* q = Q + IDX4(b, h, i, 0);
+            const double* dz = dZ + IDX4(b, h, i, 0);
+            double* dq = dQ + IDX4(b, h, i, 0);
+            for (int o = 0; o < d; ++o)
+                for (int c = 0; c < d; ++c) dW1[(size_t)o * d + c] += dz[o] * q[c];
+            for (int c = 0; c < d; ++c) {
+                double a = 0.0;
+                for (int o = 0; o < d; ++o) a += W1[(size_t)o * d + c] * dz[o];
+                dq[c] = a;
+            }
+        }
+        double de = 0.0;
+        for (size_t t = 0; t < dd; ++t) {
+            dG[t] = -e * dW1[t];
+            de -= dW1[t] * G[t];
+            pW0[(size_t)s * dd + t] = dW1[t];
+        }
+        peta[s] = de;
+        for (int i = 0; i < N; ++i) {
+            const double* k = K + IDX4(b, h, i, 0);
+            const double* v = V + IDX4(b, h, i, 0);
+            double* dk = dK + IDX4(b, h, i, 0);
+            double* dv = dV + IDX4(b, h, i, 0);
+            for (int o = 0; o < d; ++o) {
+                double a = 0.0;
+                for (int c = 0; c < d; ++c) a += dG[(size_t)o * d + c] * k[c];
+                dv[o] = -(1.0 / (double)N) * a;
+            }
+            for (int c = 0; c < d; ++c) {
+                double a = 0.0;
+                for (int o = 0; o < d; ++o) a += dG[(size_t)o * d + c] * v[o];
+                dk[c] = -(1.0 / (double)N) * a;
+            }
+        }
+        free(G);
+        free(W1);
+        free(dW1);
+        free(dG);
+        free(r);
+    }
+    for (int h = 0; h < H; ++h) {
+        double* o = dW0 + (size_t)h * dd;
+        memset(o, 0, dd * sizeof(double));
+        deta[h] = 0.0;
+        for (int b = 0; b < B; ++b) {
+            long s = (long)b * H + h;
+            for (size_t t = 0; t < dd; ++t) o[t] += pW0[(size_t)s * dd + t];
+            deta[h] += peta[s];
+        }
+    }
+    free(pW0);
+    free(peta);
+    return 0;
+}
+
+/* Depthwise 3x3 full-batch step under either loss.  Dot loss:
+ *   g[t] = -(1/N) sum_p V[p] K[p+t]   (no w0-dependent term). */
+int oracle_dwconv3x3_fullbatch_ex(int B, int H, int gh, int gw, int d, int loss,
+                                  const double* K, const double* Q, const double* V,
+                                  const double* w0, const double* eta,
+                                  double* Z, double* g_out, int nthreads) {
+    if (loss == 0) return oracle_dwconv3x3_fullbatch(B, H, gh, gw, d, K, Q, V, w0, eta, Z, g_out, nthreads);
+    if (B < 0 || H < 0 || gh <= 0 || gw <= 0 || d <= 0 || loss != 1) return -1;
+    int N = gh * gw;
+    set_threads(nthreads);
+    long nwork = (long)B * H * d;
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long wkey = 0; wkey < nwork; ++wkey) {
+        int c = (int)(wkey % d);
+        long s = wkey / d;
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* w = w0 + ((size_t)h * d + c) * 9;
+        double g[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, w1[9];
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double vv = V[IDX4(b, h, y * gw + x, c)];
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j)
+                        g[i * 3 + j] -= vv * tap(K, H, N, d, b, h, gh, gw, y + i - 1, x + j - 1, c);
+            }
+        for (int t = 0; t < 9; ++t) {
+            g[t] *= 1.0 / (double)N;
+            w1[t] = w[t] - eta[h] * g[t];
+        }
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double z = 0.0;
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j)
+                        z += w1[i * 3 + j] * tap(Q, H, N, d, b, h, gh, gw, y + i - 1, x + j - 1, c);
+                Z[IDX4(b, h, y * gw + x, c)] = z;
+            }
+        if (g_out)
+            for (int t = 0; t < 9; ++t) g_out[(((size_t)b * H + h) * d + c) * 9 + t] = g[t];
+    }
+    return 0;
+}
+
+/* Backward of the depthwise step under either loss.  Dot loss, reverse mode
+ * through g[t] = -(1/N) sum_p V[p] K[p+t]:
+ *   dV[p] = -(1/N) sum_t dg[t] K[p+t] ;  dK[p+t] += -(1/N) dg[t] V[p] ;
+ *   dw0 = dw1 ;  dQ, dw1, dg, deta as for L2. */
+int oracle_dwconv3x3_fullbatch_bwd_ex(int B, int H, int gh, int gw, int d, int loss,
+                                      const double* K, const double* Q, const double* V,
+                                      const double* w0, const double* eta, const double* dZ,
+                                      double* dK, double* dQ, double* dV,
+                                      double* dw0, double* deta, int nthreads) {
+    if (loss == 0)
+        return oracle_dwconv3x3_fullbatch_bwd(B, H, gh, gw, d, K, Q, V, w0, eta, dZ, dK, dQ, dV, dw0, deta,
+                                              nthreads);
+    if (B < 0 || H < 0 || gh <= 0 || gw <= 0 || d <= 0 || loss != 1) return -1;
+    int N = gh * gw;
+    set_threads(nthreads);
+    long nwork = (long)B * H * d;
+    double* pw0 = (double*)calloc((size_t)(nwork > 0 ? nwork : 1) * 9, sizeof(double));
+    double* peta = (double*)calloc((size_t)(nwork > 0 ? nwork : 1), sizeof(double));
+#pragma omp parallel for schedule(dynamic, 4)
+    for (long wkey = 0; wkey < nwork; ++wkey) {
+        int c = (int)(wkey % d);
+        long s = wkey / d;
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* w = w0 + ((size_t)h * d + c) * 9;
+        double e = eta[h];
+        double g[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, w1[9], dw1[9] = {0, 0, 0, 0, 0, 0, 0, 0, 0}, dg[9];
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double vv = V[IDX4(b, h, y * gw + x, c)];
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j)
+                        g[i * 3 + j] -= vv * tap(K, H, N, d, b, h, gh, gw, y + i - 1, x + j - 1, c);
+            }
+        for (int t = 0; t < 9; ++t) {
+            g[t] *= 1.0 / (double)N;
+            w1[t] = w[t] - e * g[t];
+        }
+        for (int p = 0; p < N; ++p) {
+            dQ[IDX4(b, h, p, c)] = 0.0;
+            dK[IDX4(b, h, p, c)] = 0.0;
+        }
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double dz = dZ[IDX4(b, h, y * gw + x, c)];
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j) {
+                        int yy = y + i - 1, xx = x + j - 1;
+                        if (yy < 0 || yy >= gh || xx < 0 || xx >= gw) continue;
+                        dw1[i * 3 + j] += dz * Q[IDX4(b, h, yy * gw + xx, c)];
+                        dQ[IDX4(b, h, yy * gw + xx, c)] += w1[i * 3 + j] * dz;
+                    }
+            }
+        double de = 0.0;
+        for (int t = 0; t < 9; ++t) {
+            dg[t] = -e * dw1[t];
+            de -= dw1[t] * g[t];
+            pw0[(size_t)wkey * 9 + t] = dw1[t];
+        }
+        peta[wkey] = de;
+        for (int y = 0; y < gh; ++y)
+            for (int x = 0; x < gw; ++x) {
+                double vv = V[IDX4(b, h, y * gw + x, c)], a = 0.0;
+                for (int i = 0; i < 3; ++i)
+                    for (int j = 0; j < 3; ++j) {
+                        int yy = y + i - 1, xx = x + j - 1;
+                        if (yy < 0 || yy >= gh || xx < 0 || xx >= gw) continue;
+                        a += dg[i * 3 + j] * K[IDX4(b, h, yy * gw + xx, c)];
+                        dK[IDX4(b, h, yy * gw + xx, c)] += -(1.0 / (double)N) * dg[i * 3 + j] * vv;
+                    }
+                dV[IDX4(b, h, y * gw + x, c)] = -(1.0 / (double)N) * a;
+            }
+    }
+    for (int h = 0; h < H; ++h) {
+        deta[h] = 0.0;
+        for (int c = 0; c < d; ++c)
+            for (int t = 0; t < 9; ++t) dw0[((size_t)h * d + c) * 9 + t] = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int c = 0; c < d; ++c) {
+                long wkey = ((long)b * H + h) * d + c;
+                for (int t = 0; t < 9; ++t) dw0[((size_t)h * d + c) * 9 + t] += pw0[(size_t)wkey * 9 + t];
+                deta[h] += peta[wkey];
+            }
+    }
+    free(pw0);
+    free(peta);
+    return 0;
+}
+
+/* Mini-batch scans with a separate initial state per direction (the
+ * Vision-TTT ablation's best variant): W0 is [2][H][d][d], the forward
+ * scan starts from W0[0][h] and the reverse scan from W0[1][h]. */
+int oracle_linear_minibatch_2w0(int B, int H, int N, int d, int bsz, int mode,
+                                const double* K, const double* Q, const double* V,
+                                const double* W0, const double* eta, double* Z,
+                                int nthreads) {
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || bsz <= 0 || mode < 0 || mode > 2) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+    int ndir = (mode == 0) ? 2 : 1;
+    size_t slice_elems = (size_t)N * d;
+    size_t dd = (size_t)d * d;
+    double* tmp = NULL;
+    if (mode == 0) tmp = (double*)malloc((size_t)nslice * slice_elems * sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long job = 0; job < nslice * ndir; ++job) {
+        long s = job / ndir;
+        int dir = (int)(job % ndir);
+        int h = (int)(s % H);
+        size_t off = (size_t)s * slice_elems;
+        int reverse = (mode == 2) ? 1 : (mode == 1 ? 0 : dir);
+        double* out = (mode == 0 && dir == 1) ? tmp + off : Z + off;
+        scan_one(N, d, bsz, reverse, K + off, Q + off, V + off,
+                 W0 + ((size_t)reverse * H + h) * dd, eta[h], out);
+    }
+    if (mode == 0) {
+        size_t total = (size_t)nslice * slice_elems;
+        for (size_t e = 0; e < total; ++e) Z[e] = 0.5 * (Z[e] + tmp[e]);
+        free(tmp);
+    }
+    return 0;
+}
+
+/* Gradient magnitude map (the Vision-TTT notes: the per-token gradient's
+ * size marks how much new information the token carries): for every token,
+ * the Frobenius norm of its own gradient at W0, with the outer product
+ * written out entry by entry:
+ *   L2:  G_t = 2 (W0 k_t - v_t) k_t^T ;   dot:  G_t = -v_t k_t^T.
+ * out: [B][H][N]. */
+int oracle_linear_gradient_magnitude(int B, int H, int N, int d, int loss,
+                                     const double* K, const double* V, const double* W0,
+                                     double* out, int nthreads) {
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || loss < 0 || loss > 1) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* W = W0 + (size_t)h * d * d;
+        double* r = (double*)malloc((size_t)d * sizeof(double));
+        for (int i = 0; i < N; ++i) {
+            const double* k = K + IDX4(b, h, i, 0);
+            const double* v = V + IDX4(b, h, i, 0);
+            for (int o = 0; o < d; ++o) {
+                if (loss == 0) {
+                    double a = 0.0;
+                    for (int c = 0; c < d; ++c) a += W[(size_t)o * d + c] * k[c];
+                    r[o] = 2.0 * (a - v[o]);
+                } else {
+                    r[o] = -v[o];
+                }
+            }
+            double f = 0.0;
+            for (int o = 0; o < d; ++o)
+                for (int c = 0; c < d; ++c) f += (r[o] * k[c]) * (r[o] * k[c]);
+            out[(size_t)s * N + i] = sqrt(f);
+        }
+        free(r);
+    }
     return 0;
 }
