@@ -108,6 +108,15 @@ typedef struct {
     int64_t stride_b, stride_h, stride_n; /* in elements; channel stride is 1 */
 } ttt_view;
 
+/* Inner loss.  TTT_LOSS_L2: l(W; k, v) = ||W k - v||^2 (the definitions
+ * above).  TTT_LOSS_DOT: the dot-product loss of the ViT3 recipe, read as
+ * l(W; k, v) = -<W k, v>, so the full-batch gradient is
+ * G = -(1/N) sum_i v_i k_i^T (depthwise: g[t] = -(1/N) sum_p V[p] K[p+t])
+ * and one step is linear attention added to W0's output.  Full-batch
+ * linear and depthwise steps and their backward take either; the
+ * mini-batch scan takes L2 only. */
+typedef enum { TTT_LOSS_L2 = 0, TTT_LOSS_DOT = 1 } ttt_loss;
+
 typedef struct {
     int32_t B, H, N, d;      /* images, heads in this call, tokens, head dim  */
     ttt_dtype dtype;         /* element type of every view of the call        */
@@ -115,6 +124,14 @@ typedef struct {
                                 n % grid_w); grid_h * grid_w == N            */
     int32_t minibatch;       /* minibatch scan only: tokens per mini-batch b  */
     ttt_scan_mode mode;      /* minibatch scan only                           */
+    ttt_loss loss;           /* inner loss (0 = L2)                           */
+    int32_t steps;           /* ttt_linear_fullbatch only: full-batch gradient
+                                steps (epochs), each at the current W; 0 and
+                                1 mean one step; other ops require <= 1      */
+    int32_t w0_per_direction;/* minibatch scan only: 1 = W0 is
+                                [2][H][d][d], the forward scan starting from
+                                W0[0] and the reversed one from W0[1]; 0 =
+                                one shared [H][d][d]                         */
 } ttt_problem;
 
 /* Bytes of workspace `op` needs for problem `p` (0 for a bad problem). */
@@ -131,6 +148,11 @@ const char* ttt_status_string(ttt_status s);
  * In: K, Q, V [B,H,N,d]; W0 [H][d][d]; eta [H].  Out: Z [B,H,N,d].
  * saved: NULL, or float [B][H][2][d][d] receiving A then G of each slice
  *   (what ttt_linear_fullbatch_bwd can reuse).
+ * p->loss selects the L2 or the dot-product loss.  p->steps = E > 1 takes E
+ * full-batch steps (ViT3 observation 2, more inner epochs): W_{e+1} =
+ * W_e - eta_h G(W_e), then z_i = W_E q_i; three launches (the Gram pass
+ * saving A and G(W0) in the workspace, the d x d steps per slice, the
+ * apply); saved must then be NULL (the backward covers one step).
  */
 ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
                                 const float* W0, const float* eta, ttt_view Z,
@@ -237,6 +259,19 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
 ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
                                       const float* W0, const float* eta, ttt_view Z,
                                       void* ws, size_t ws_bytes, ttt_stream_t stream);
+
+/*
+ * Gradient magnitude map (Vision-TTT notes, key design item 1: the size of
+ * each token's gradient marks the information it adds): per token, the
+ * Frobenius norm of its own full-batch gradient at W0,
+ *   L2:  ||2 (W0 k_t - v_t) k_t^T||_F = 2 ||W0 k_t - v_t|| ||k_t||,
+ *   dot: ||v_t k_t^T||_F = ||v_t|| ||k_t||   (p->loss).
+ * In: K, V [B,H,N,d]; W0 [H][d][d].  Out: gmm float [B][H][N] (contiguous,
+ * 4-byte aligned).  No workspace.  bf16 inputs: W0 k_t on the matrix cores
+ * with W0 rounded to bf16; fp32 inputs: fp32 products.
+ */
+ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
+                                         float* gmm, ttt_stream_t stream);
 
 /*
  * Backward of ttt_linear_fullbatch for L = sum <dZ, Z> (end-to-end training

@@ -8,6 +8,8 @@ built library or without a GPU raises.
 from .binding import (  # noqa: F401
     TTT_BF16,
     TTT_F32,
+    LOSS_DOT,
+    LOSS_L2,
     TTTError,
     BIDIR_AVG,
     FORWARD_ONLY,
@@ -25,5 +27,6 @@ from .binding import (  # noqa: F401
     ttt_linear_fullbatch,
     ttt_linear_fullbatch_bwd,
     ttt_linear_fullbatch_noalloc,
+    ttt_linear_gradient_magnitude,
     ttt_linear_minibatch_bidir,
 )

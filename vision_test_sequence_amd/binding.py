@@ -43,7 +43,8 @@ STATUS_NAMES = [
 EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size", "ttt_linear_fullbatch",
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
             "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
-            "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc", "ttt_dwconv3x3_fullbatch_bwd")
+            "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc", "ttt_dwconv3x3_fullbatch_bwd",
+            "ttt_linear_gradient_magnitude")
 
 
 class TTTError(RuntimeError):
@@ -59,10 +60,15 @@ class View(ctypes.Structure):
                 ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
 
 
+LOSS_L2 = 0
+LOSS_DOT = 1
+
+
 class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int), ("grid_h", ctypes.c_int32),
-                ("grid_w", ctypes.c_int32), ("minibatch", ctypes.c_int32), ("mode", ctypes.c_int)]
+                ("grid_w", ctypes.c_int32), ("minibatch", ctypes.c_int32), ("mode", ctypes.c_int),
+                ("loss", ctypes.c_int), ("steps", ctypes.c_int32), ("w0_per_direction", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -112,6 +118,7 @@ def lib() -> ctypes.CDLL:
             L.ttt_linear_fullbatch_noalloc.argtypes = [P, View, View, View, fp, fp, View, fp, vp]
             L.ttt_dwconv3x3_fullbatch_bwd.argtypes = [P, View, View, View, fp, fp, View, fp, View, View,
                                                       View, fp, fp, vp, sz, vp]
+            L.ttt_linear_gradient_magnitude.argtypes = [P, View, View, fp, fp, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -137,9 +144,10 @@ def view(t: torch.Tensor) -> View:
 
 
 def problem(K: torch.Tensor, grid: Tuple[int, int] = (0, 0), minibatch: int = 0,
-            mode: int = BIDIR_AVG) -> Problem:
+            mode: int = BIDIR_AVG, loss: int = LOSS_L2, steps: int = 1, w0_per_direction: int = 0) -> Problem:
     B, H, N, d = K.shape
-    return Problem(B, H, N, d, _dtype_code(K), grid[0], grid[1], minibatch, mode)
+    return Problem(B, H, N, d, _dtype_code(K), grid[0], grid[1], minibatch, mode, loss, steps,
+                   w0_per_direction)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -235,19 +243,20 @@ def _param(t: torch.Tensor, shape, name: str) -> torch.Tensor:
 
 
 # ------------------------------------------------------------ entry points --
-def ttt_linear_fullbatch(K, Q, V, W0, eta, *, Z=None, saved=None):
-    """One full-batch L2 step of the linear inner model, then Z = W1 q per token.
+def ttt_linear_fullbatch(K, Q, V, W0, eta, *, Z=None, saved=None, loss: int = LOSS_L2, steps: int = 1):
+    """Full-batch gradient step(s) of the linear inner model, then Z = W q per token.
 
     K, Q, V: [B,H,N,64] float32/bfloat16 on the GPU; W0 [H,64,64] and eta [H]
     float32.  Z (optional) receives the output; saved (optional, float32
-    [B,H,2,64,64]) receives A then G per slice.  Returns Z.
+    [B,H,2,64,64]) receives A then G per slice.  loss: LOSS_L2 or LOSS_DOT;
+    steps: full-batch steps (saved must be None above one).  Returns Z.
     """
     B, H, N, d = K.shape
     _param(W0, (H, d, d), "W0")
     _param(eta, (H,), "eta")
     if Z is None:
         Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
-    p = problem(K)
+    p = problem(K, loss=loss, steps=steps)
     ws, wsb = workspace(OP_LINEAR_FULLBATCH, p, K.device)
     st = lib().ttt_linear_fullbatch(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
                                     eta.data_ptr(), view(Z), _ptr(saved), ws, wsb,
@@ -271,7 +280,8 @@ def ttt_linear_fullbatch_noalloc(K, Q, V, W0, eta, *, Z=None, saved=None):
     return Z
 
 
-def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=None, saved=None):
+def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=None, saved=None,
+                            loss: int = LOSS_L2):
     """One full-batch L2 step of the 3x3 depthwise-conv inner model, then apply.
 
     Tokens form a row-major grid_h x grid_w map.  w0 [H,64,3,3], eta [H]
@@ -282,7 +292,7 @@ def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=Non
     _param(eta, (H,), "eta")
     if Z is None:
         Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
-    p = problem(K, grid=(grid_h, grid_w))
+    p = problem(K, grid=(grid_h, grid_w), loss=loss)
     ws, wsb = workspace(OP_DWCONV3X3_FULLBATCH, p, K.device)
     st = lib().ttt_dwconv3x3_fullbatch(ctypes.byref(p), view(K), view(Q), view(V), w0.data_ptr(),
                                        eta.data_ptr(), view(Z), _ptr(saved), ws, wsb,
@@ -292,7 +302,7 @@ def ttt_dwconv3x3_fullbatch(K, Q, V, w0, eta, grid_h: int, grid_w: int, *, Z=Non
 
 
 def ttt_layer_fullbatch(Kl, Ql, Vl, W0, eta_l, Kc, Qc, Vc, w0, eta_c, grid_h: int, grid_w: int, *,
-                        Zl=None, Zc=None):
+                        Zl=None, Zc=None, loss: int = LOSS_L2):
     """Both full-batch steps of one layer in one call: ttt_linear_fullbatch on
     (Kl, Ql, Vl, W0, eta_l) and ttt_dwconv3x3_fullbatch on (Kc, Qc, Vc, w0,
     eta_c) over a grid_h x grid_w token map, with the same results; one
@@ -309,8 +319,8 @@ def ttt_layer_fullbatch(Kl, Ql, Vl, W0, eta_l, Kc, Qc, Vc, w0, eta_c, grid_h: in
         Zl = torch.empty((Bl, Hl, N, d), dtype=Kl.dtype, device=Kl.device)
     if Zc is None:
         Zc = torch.empty(tuple(Kc.shape), dtype=Kc.dtype, device=Kc.device)
-    pl = problem(Kl)
-    pc = problem(Kc, grid=(grid_h, grid_w))
+    pl = problem(Kl, loss=loss)
+    pc = problem(Kc, grid=(grid_h, grid_w), loss=loss)
     need = int(lib().ttt_layer_workspace_size(ctypes.byref(pl), ctypes.byref(pc)))
     ws, wsb = workspace(OP_LAYER_FULLBATCH, None, Kl.device, need)
     st = lib().ttt_layer_fullbatch(ctypes.byref(pl), view(Kl), view(Ql), view(Vl), W0.data_ptr(),
@@ -322,13 +332,17 @@ def ttt_layer_fullbatch(Kl, Ql, Vl, W0, eta_l, Kc, Qc, Vc, w0, eta_c, grid_h: in
 
 
 def ttt_linear_minibatch_bidir(K, Q, V, W0, eta, minibatch: int, mode: int = BIDIR_AVG, *, Z=None):
-    """Causal mini-batch scans (forward, reverse or their average). Returns Z."""
+    """Causal mini-batch scans (forward, reverse or their average). Returns Z.
+
+    W0: [H,64,64] shared by both directions, or [2,H,64,64] with the
+    forward scan starting from W0[0] and the reversed one from W0[1]."""
     B, H, N, d = K.shape
-    _param(W0, (H, d, d), "W0")
+    w0dir = 1 if W0.dim() == 4 else 0
+    _param(W0, (2, H, d, d) if w0dir else (H, d, d), "W0")
     _param(eta, (H,), "eta")
     if Z is None:
         Z = torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
-    p = problem(K, minibatch=minibatch, mode=mode)
+    p = problem(K, minibatch=minibatch, mode=mode, w0_per_direction=w0dir)
     ws, wsb = workspace(OP_LINEAR_MINIBATCH_BIDIR, p, K.device)
     st = lib().ttt_linear_minibatch_bidir(ctypes.byref(p), view(K), view(Q), view(V),
                                           W0.data_ptr(), eta.data_ptr(), view(Z), ws, wsb,
@@ -338,7 +352,7 @@ def ttt_linear_minibatch_bidir(K, Q, V, W0, eta, minibatch: int, mode: int = BID
 
 
 def ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, *, saved=None, dK=None, dQ=None, dV=None,
-                             dW0=None, deta=None):
+                             dW0=None, deta=None, loss: int = LOSS_L2):
     """Backward of ttt_linear_fullbatch for L = sum(dZ * Z).
 
     Returns (dK, dQ, dV, dW0, deta); dW0 [H,64,64] and deta [H] are float32
@@ -353,7 +367,7 @@ def ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, *, saved=None, dK=None, dQ=No
     dV = mk() if dV is None else dV
     dW0 = torch.empty((H, d, d), dtype=torch.float32, device=K.device) if dW0 is None else dW0
     deta = torch.empty((H,), dtype=torch.float32, device=K.device) if deta is None else deta
-    p = problem(K)
+    p = problem(K, loss=loss)
     ws, wsb = workspace(OP_LINEAR_FULLBATCH_BWD, p, K.device)
     st = lib().ttt_linear_fullbatch_bwd(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
                                         eta.data_ptr(), view(dZ), _ptr(saved), view(dK), view(dQ),
@@ -364,7 +378,7 @@ def ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, *, saved=None, dK=None, dQ=No
 
 
 def ttt_dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, *, saved=None, dK=None,
-                                dQ=None, dV=None, dw0=None, deta=None):
+                                dQ=None, dV=None, dw0=None, deta=None, loss: int = LOSS_L2):
     """Backward of ttt_dwconv3x3_fullbatch for L = sum(dZ * Z).
 
     saved: the forward's g (float32 [B,H,64,3,3]) or None to recompute it.
@@ -380,7 +394,7 @@ def ttt_dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, 
     dV = mk() if dV is None else dV
     dw0 = torch.empty((H, d, 3, 3), dtype=torch.float32, device=K.device) if dw0 is None else dw0
     deta = torch.empty((H,), dtype=torch.float32, device=K.device) if deta is None else deta
-    p = problem(K, grid=(grid_h, grid_w))
+    p = problem(K, grid=(grid_h, grid_w), loss=loss)
     ws, wsb = workspace(OP_DWCONV3X3_FULLBATCH_BWD, p, K.device)
     st = lib().ttt_dwconv3x3_fullbatch_bwd(ctypes.byref(p), view(K), view(Q), view(V), w0.data_ptr(),
                                            eta.data_ptr(), view(dZ), _ptr(saved), view(dK), view(dQ),
@@ -388,3 +402,18 @@ def ttt_dwconv3x3_fullbatch_bwd(K, Q, V, w0, eta, dZ, grid_h: int, grid_w: int, 
                                            _stream(K.device))
     _check(st, "ttt_dwconv3x3_fullbatch_bwd")
     return dK, dQ, dV, dw0, deta
+
+
+def ttt_linear_gradient_magnitude(K, V, W0, *, out=None, loss: int = LOSS_L2):
+    """Per-token ||G_t||_F at W0 (the gradient magnitude map), float32 [B,H,N]."""
+    B, H, N, d = K.shape
+    _param(W0, (H, d, d), "W0")
+    if out is None:
+        out = torch.empty((B, H, N), dtype=torch.float32, device=K.device)
+    if out.dtype != torch.float32 or tuple(out.shape) != (B, H, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of shape (B, H, N)")
+    p = problem(K, loss=loss)
+    st = lib().ttt_linear_gradient_magnitude(ctypes.byref(p), view(K), view(V), W0.data_ptr(), out.data_ptr(),
+                                             _stream(K.device))
+    _check(st, "ttt_linear_gradient_magnitude")
+    return out

@@ -38,8 +38,29 @@ ttt_status check_problem(const ttt_problem* p, bool* noop) {
     if (p->dtype != TTT_F32 && p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
     if (p->d != 64) return TTT_ERR_UNSUPPORTED;
     if ((int64_t)p->B * p->H > (int64_t)1 << 24) return TTT_ERR_UNSUPPORTED;
+    if (p->loss != TTT_LOSS_L2 && p->loss != TTT_LOSS_DOT) return TTT_ERR_UNSUPPORTED;
+    if (p->steps < 0) return TTT_ERR_BAD_SHAPE;
+    if (p->w0_per_direction != 0 && p->w0_per_direction != 1) return TTT_ERR_UNSUPPORTED;
     if (p->B == 0 || p->H == 0) *noop = true;
     return TTT_OK;
+}
+
+// The options an operation does not take: more than one step (all but the
+// full-batch linear forward), a W0 per direction (all but the scan).
+ttt_status check_single_step(const ttt_problem* p) {
+    if (p->steps > 1 || p->w0_per_direction) return TTT_ERR_UNSUPPORTED;
+    return TTT_OK;
+}
+
+size_t align256z(size_t n) { return (n + 255) / 256 * 256; }
+
+// Workspace of ttt_linear_fullbatch.  More than one step: [the one-step
+// workspace, at least its counter block][A, G(W0) per slice][W_E per slice].
+size_t lin_ws_bytes(const ttt_problem* p) {
+    const size_t one = lin_fwd_ws_bytes(p->B, p->H, p->N);
+    if (p->steps <= 1) return one;
+    const size_t slices = (size_t)p->B * p->H;
+    return align256z(std::max(one, kCounterBytes)) + align256z(slices * 8192 * 4) + slices * 4096 * 4;
 }
 
 // A [B,H,N,d] view: non-null, non-negative strides, no two elements at one
@@ -227,7 +248,7 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     bool noop = false;
     if (check_problem(p, &noop) != TTT_OK || noop) return 0;
     switch (op) {
-    case TTT_OP_LINEAR_FULLBATCH: return lin_fwd_ws_bytes(p->B, p->H, p->N);
+    case TTT_OP_LINEAR_FULLBATCH: return lin_ws_bytes(p);
     case TTT_OP_DWCONV3X3_FULLBATCH:
         if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N) return 0;
         return conv_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
@@ -253,6 +274,7 @@ static ttt_status plan_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4 V
     a.W0 = W0; a.eta = eta; a.saved = saved;
     a.B = p->B; a.H = p->H; a.N = p->N;
     a.bf16 = p->dtype == TTT_BF16;
+    a.dot = p->loss == TTT_LOSS_DOT ? 1 : 0;
     const long long slices = (long long)p->B * p->H;
     int S = lin_fwd_max_splits(p->B, p->H, p->N);
     const long long padded = (slices + 7) / 8 * 8;
@@ -279,6 +301,25 @@ static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4
                                    const float* eta, float* saved, void* ws, hipStream_t stream) {
     LinFwdLaunch a;
     int resident = 0;
+    if (p->steps > 1) {
+        // the Gram pass saves A and G(W0) in the workspace (no apply), the
+        // steps run per slice, then Z = Q W_E^T
+        const size_t slices = (size_t)p->B * p->H;
+        char* base = (char*)ws + align256z(std::max(lin_fwd_ws_bytes(p->B, p->H, p->N), kCounterBytes));
+        float* sv = (float*)base;
+        float* WE = (float*)(base + align256z(slices * 8192 * 4));
+        const View4 none{nullptr, 0, 0, 0};
+        ttt_problem one = *p;
+        one.steps = 1;
+        ttt_status st = plan_fullbatch(&one, K, K, V, none, W0, eta, sv, ws, a, resident);
+        if (st != TTT_OK) return st;
+        hipError_t e = launch_lin_fwd(a, stream, resident);
+        if (e != hipSuccess) return TTT_ERR_HIP;
+        LinEpochArgs ea{W0, eta, sv, WE, p->H, p->N, (int)slices, p->steps, p->loss == TTT_LOSS_DOT ? 1 : 0};
+        if ((e = launch_lin_epochs(ea, stream)) != hipSuccess) return TTT_ERR_HIP;
+        LinApplyArgs aa{Q, Z, WE, p->B, p->H, p->N};
+        return hip_status(launch_lin_apply(aa, p->dtype == TTT_BF16, stream));
+    }
     const ttt_status st = plan_fullbatch(p, K, Q, V, Z, W0, eta, saved, ws, a, resident);
     if (st != TTT_OK) return st;
     return hip_status(launch_lin_fwd(a, stream, resident));
@@ -294,6 +335,7 @@ static ConvLaunch plan_conv_call(const ttt_problem* p, View4 K, View4 Q, View4 V
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
     a.cap = device_cus() * conv_resident_per_cu(a.bf16);
+    a.dot = p->loss == TTT_LOSS_DOT ? 1 : 0;
     const Knobs kn = knobs();
     a.xcd_ok = xcd_local_ok(kn) ? 1 : 0;
     a.spin = kn.spin;
@@ -306,7 +348,9 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
                                 void* ws, size_t ws_bytes, ttt_stream_t stream) {
     bool noop = false;
     ttt_status st = check_problem(p, &noop);
-    if (st != TTT_OK || noop) return st;
+    if (st != TTT_OK) return st;
+    if (p->w0_per_direction || (p->steps > 1 && saved)) return TTT_ERR_UNSUPPORTED;
+    if (noop) return TTT_OK;
     Span in[5], out[3];
     if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
     if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
@@ -316,7 +360,7 @@ ttt_status ttt_linear_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, tt
     if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
     if (saved && (st = check_buf(saved, (size_t)p->B * p->H * 2 * p->d * p->d * 4, 4, &out[1])) != TTT_OK)
         return st;
-    const size_t need = lin_fwd_ws_bytes(p->B, p->H, p->N);
+    const size_t need = lin_ws_bytes(p);
     if ((st = check_ws(ws, ws_bytes, need, &out[2])) != TTT_OK) return st;
     if ((st = check_aliasing(in, 5, out, 3)) != TTT_OK) return st;
 
@@ -328,7 +372,9 @@ ttt_status ttt_linear_fullbatch_noalloc(const ttt_problem* p, ttt_view K, ttt_vi
                                         ttt_stream_t stream) {
     bool noop = false;
     ttt_status st = check_problem(p, &noop);
-    if (st != TTT_OK || noop) return st;
+    if (st != TTT_OK) return st;
+    if ((st = check_single_step(p)) != TTT_OK) return st; // the scratch holds one step's workspace
+    if (noop) return TTT_OK;
     Span in[5], out[2];
     if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
     if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
@@ -359,6 +405,7 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
     bool noop = false;
     ttt_status st = check_problem(p, &noop);
     if (st != TTT_OK) return st;
+    if ((st = check_single_step(p)) != TTT_OK) return st;
     if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N)
         return TTT_ERR_BAD_SHAPE;
     if (noop) return TTT_OK;
@@ -386,6 +433,7 @@ ttt_status ttt_dwconv3x3_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_vie
     bool noop = false;
     ttt_status st = check_problem(p, &noop);
     if (st != TTT_OK) return st;
+    if ((st = check_single_step(p)) != TTT_OK) return st;
     if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N)
         return TTT_ERR_BAD_SHAPE;
     if (noop) return TTT_OK;
@@ -417,6 +465,7 @@ ttt_status ttt_dwconv3x3_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_vie
     a.B = p->B; a.H = p->H; a.gh = p->grid_h; a.gw = p->grid_w;
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
+    a.dot = p->loss == TTT_LOSS_DOT ? 1 : 0;
     return hip_status(launch_conv_bwd(a, (hipStream_t)stream));
 }
 
@@ -451,6 +500,7 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
     ttt_status st = check_problem(lin, &lnoop);
     if (st != TTT_OK) return st;
     if ((st = check_problem(conv, &cnoop)) != TTT_OK) return st;
+    if ((st = check_single_step(lin)) != TTT_OK || (st = check_single_step(conv)) != TTT_OK) return st;
     if (conv->grid_h <= 0 || conv->grid_w <= 0 || (int64_t)conv->grid_h * conv->grid_w != conv->N)
         return TTT_ERR_BAD_SHAPE;
     Span in[10], out[3];
@@ -515,12 +565,14 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
         return TTT_ERR_UNSUPPORTED;
     if (p->minibatch > 16) return TTT_ERR_UNSUPPORTED;
     if (p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
+    if (p->loss != TTT_LOSS_L2 || p->steps > 1) return TTT_ERR_UNSUPPORTED;
     if (noop) return TTT_OK;
     Span in[5], out[2];
     if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
     if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
     if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
-    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    const size_t nw0 = p->w0_per_direction ? 2 : 1;
+    if ((st = check_buf(W0, nw0 * p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
     if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
     if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
     // the kernel addresses a slice's K, V, Q and Z rows through 32-bit
@@ -547,7 +599,25 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
     a.cus = device_cus();
+    a.w0dir = p->w0_per_direction;
     return hip_status(launch_scan(a, (hipStream_t)stream));
+}
+
+ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
+                                         float* gmm, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if ((st = check_single_step(p)) != TTT_OK) return st;
+    if (noop) return TTT_OK;
+    Span in[3], out[1];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_buf(W0, (size_t)p->H * p->d * p->d * 4, 16, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(gmm, (size_t)p->B * p->H * p->N * 4, 4, &out[0])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 3, out, 1)) != TTT_OK) return st;
+    LinGmmArgs a{v4(K), v4(V), W0, gmm, p->B, p->H, p->N, p->loss == TTT_LOSS_DOT ? 1 : 0};
+    return hip_status(launch_lin_gmm(a, p->dtype == TTT_BF16, (hipStream_t)stream));
 }
 
 ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
@@ -557,7 +627,9 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
                                     ttt_stream_t stream) {
     bool noop = false;
     ttt_status st = check_problem(p, &noop);
-    if (st != TTT_OK || noop) return st;
+    if (st != TTT_OK) return st;
+    if ((st = check_single_step(p)) != TTT_OK) return st;
+    if (noop) return TTT_OK;
     Span in[7], out[6];
     int nin = 6;
     if ((st = check_buf(dW0, (size_t)p->H * p->d * p->d * 4, 4, &out[3])) != TTT_OK) return st;
@@ -587,6 +659,7 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
     a.B = p->B; a.H = p->H; a.N = p->N;
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
+    a.dot = p->loss == TTT_LOSS_DOT ? 1 : 0;
     if (!saved) {
         // recompute A and G with the forward's Gram pass, into the workspace
         float* sv = lin_bwd_saved_region(ws, p->B, p->H, p->N);

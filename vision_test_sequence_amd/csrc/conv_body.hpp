@@ -27,6 +27,7 @@ struct ConvArgs {
     int xcd;           // XCD-aware grid and XCD-local exchange
     unsigned spin;     // slice barrier: poll limit
     unsigned tbias;    // slice barrier: added to every target (0)
+    int dot;           // dot-product loss: R = -V (no w0 term), scale 1/N
 };
 
 // Plan of a conv call (tiles, splits, the exchange protocol) as kernel
@@ -299,7 +300,7 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
         lds_barrier();     // ... and every wave's
         if (tile == tb) {
 #pragma unroll
-            for (int t = 0; t < 9; ++t) wt[t] = reinterpret_cast<const float*>(W0s)[lane * 9 + t];
+            for (int t = 0; t < 9; ++t) wt[t] = a.dot ? 0.f : reinterpret_cast<const float*>(W0s)[lane * 9 + t];
             // A store to a line that is not in the XCD's L2 goes on to
             // memory without allocating it, and the slice's other
             // workgroups would then read the partial from memory: a
@@ -382,14 +383,14 @@ __device__ __forceinline__ void conv_body(const ConvArgs& a, const ConvLds& L) {
     }
     __syncthreads();
     const float eta = a.eta[h];
-    const float scale = 2.0f / (float)N;
+    const float scale = (a.dot ? 1.0f : 2.0f) / (float)N;
     if (a.S == 1) {
         if (w == 0) {
             for (int t = 0; t < 9; ++t) {
                 const float s = ((red[lane * 9 + t] + red[(64 + lane) * 9 + t]) + red[(128 + lane) * 9 + t]) +
                                 red[(192 + lane) * 9 + t];
                 const float gv = scale * s;
-                w1s[lane * 9 + t] = wt[t] - eta * gv;
+                w1s[lane * 9 + t] = reinterpret_cast<const float*>(W0s)[lane * 9 + t] - eta * gv;
                 if (a.saved) a.saved[((long long)slice * 64 + lane) * 9 + t] = gv;
             }
         }

@@ -116,6 +116,7 @@ void conv_prepare(const ConvLaunch& l, ConvArgs& a, unsigned& grid) {
     a.xcd = (p.S > 1 && l.xcd_ok) ? 1 : 0;
     a.spin = l.spin;
     a.tbias = l.tbias;
+    a.dot = l.dot;
     if (p.S > 1) {
         // workspace layout as conv_ws_bytes: fixed counter block, partials
         char* base = (char*)l.ws;

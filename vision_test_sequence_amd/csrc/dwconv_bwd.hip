@@ -49,6 +49,7 @@ struct CbArgs {
     float* deta;        // [H]
     int B, H, gh, gw;
     int nseg, seglen, ngrp; // column segments, columns per segment, row groups
+    int dot;                // dot-product loss: g = -(1/N) sum V K-shifted
 };
 
 template <bool BF> struct Elt;
@@ -136,9 +137,10 @@ __global__ __launch_bounds__(256) void cbwd_pass1(CbArgs a) {
         const Map<BF> Qm = map_of<BF>(a.Q, t.b, t.h, a.gh, a.gw, lane);
         const Map<BF> Vm = map_of<BF>(a.V, t.b, t.h, a.gh, a.gw, lane);
         const Map<BF> Dm = map_of<BF>(a.dZ, t.b, t.h, a.gh, a.gw, lane);
+        // taps of P = conv(K, w0) in R = P - V (none under the dot-product loss)
         float wt[9];
 #pragma unroll
-        for (int k = 0; k < 9; ++k) wt[k] = a.w0[((long long)t.h * 64 + lane) * 9 + k];
+        for (int k = 0; k < 9; ++k) wt[k] = a.dot ? 0.f : a.w0[((long long)t.h * 64 + lane) * 9 + k];
         const int y = t.y;
         // windows: columns x-1, x, x+1 of rows y-1..y+1 (index 3 i + j)
         float kw[9], qw[9];
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(256) void cbwd_reduce(CbArgs a) {
     const int h = slice % a.H;
     const int P = a.ngrp * a.nseg;
     const float eta = a.eta[h];
-    const float scale = 2.0f / (float)(a.gh * a.gw);
+    const float scale = (a.dot ? 1.0f : 2.0f) / (float)(a.gh * a.gw);
     const float* src = a.part1 + (long long)slice * P * 64 * 18;
     float* sl = a.sl + (long long)slice * 4 * 576;
     float dsum = 0.f;
@@ -249,9 +251,13 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
         const long long sK = a.dK.sn * es, sQ = a.dQ.sn * es, sV = a.dV.sn * es;
         const float* sl = a.sl + (long long)t.slice * 4 * 576 + lane * 9;
         float wt[9], w1[9], dgs[9];
+        // Under the dot-product loss g = -(1/N) sum_p V[p] K[p+t] has no
+        // P = conv(K, w0) term: R = -V, dK gets no w0 dR term and dw0 no
+        // sum_p dR[p] K[p+t] term (wt = 0, wd = 0).
+        const float wd = a.dot ? 0.f : 1.f;
 #pragma unroll
         for (int k = 0; k < 9; ++k) {
-            wt[k] = a.w0[((long long)t.h * 64 + lane) * 9 + k];
+            wt[k] = wd * a.w0[((long long)t.h * 64 + lane) * 9 + k];
             w1[k] = sl[k];
             dgs[k] = sl[576 + k];
         }
@@ -352,7 +358,7 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
 #pragma unroll
             for (int i = 0; i < 3; ++i)
 #pragma unroll
-                for (int j = 0; j < 3; ++j) acc[3 * i + j] = fmaf(drc, kw[j][i + 1], acc[3 * i + j]);
+                for (int j = 0; j < 3; ++j) acc[3 * i + j] = fmaf(wd * drc, kw[j][i + 1], acc[3 * i + j]);
             const long long n = (long long)y * a.gw + x;
             Elt<BF>::st(dQp + n * sQ, dq);
             Elt<BF>::st(dKp + n * sK, dk);
@@ -414,6 +420,7 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
     a.w0 = s.w0; a.eta = s.eta; a.gsv = s.saved;
     a.dw0 = s.dw0; a.deta = s.deta;
     a.B = s.B; a.H = s.H; a.gh = s.gh; a.gw = s.gw;
+    a.dot = s.dot;
     const CbPlan p = cb_plan(s.gh, s.gw);
     a.nseg = p.nseg; a.seglen = p.seglen; a.ngrp = p.ngrp;
     const size_t slices = (size_t)s.B * s.H;

@@ -28,6 +28,7 @@ struct LinFwdLaunch {
     int bf16;
     unsigned spin;    // slice barrier: poll limit before giving up
     unsigned tbias;   // slice barrier: added to every target (0 in normal use)
+    int dot;          // dot-product loss: G = -(1/N) C
 };
 
 // Kernel a full-batch linear plan launches (plan queries of the C ABI).
@@ -38,6 +39,29 @@ int lin_fwd_max_splits(int B, int H, int N);
 hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident);
 int lin_fwd_resident_per_cu(int bf16);
 bool lin_fwd_is_resident(int N, int S, int bf16);
+
+// ---- several full-batch steps, apply, gradient magnitude map -----------
+struct LinEpochArgs {
+    const float* W0;
+    const float* eta;
+    const float* saved; // [slices][2][64][64]: A, G at W0
+    float* WE;          // [slices][64][64]: the weights after `steps` steps
+    int H, N, slices, steps, dot;
+};
+hipError_t launch_lin_epochs(const LinEpochArgs& e, hipStream_t stream);
+struct LinApplyArgs {
+    View4 Q, Z;
+    const float* W; // [slices][64][64]
+    int B, H, N;
+};
+hipError_t launch_lin_apply(const LinApplyArgs& a, int bf16, hipStream_t stream);
+struct LinGmmArgs {
+    View4 K, V;
+    const float* W0;
+    float* out;     // [slices][N]
+    int B, H, N, dot;
+};
+hipError_t launch_lin_gmm(const LinGmmArgs& a, int bf16, hipStream_t stream);
 
 // ---- depthwise 3x3 ----------------------------------------------------
 struct ConvLaunch {
@@ -53,6 +77,7 @@ struct ConvLaunch {
     int xcd_ok;       // the device is an MI355X in whole-device (SPX) mode
     unsigned spin;    // slice barrier: poll limit before giving up
     unsigned tbias;   // slice barrier: added to every target (0 in normal use)
+    int dot;          // dot-product loss: g = -(1/N) sum V K-shifted
 };
 size_t conv_ws_bytes(int B, int H, int gh, int gw);
 // Splits per slice and exchange protocol a conv plan uses (plan queries).
@@ -71,6 +96,7 @@ struct ConvBwdLaunch {
     int B, H, gh, gw;
     int bf16;
     void* ws;           // conv_bwd_ws_bytes(...) bytes
+    int dot;            // dot-product loss
 };
 size_t conv_bwd_ws_bytes(int B, int H, int gh, int gw);
 hipError_t launch_conv_bwd(const ConvBwdLaunch& a, hipStream_t stream);
@@ -88,6 +114,7 @@ struct ScanLaunch {
     int bf16;
     void* ws;         // scan_ws_bytes(...) bytes
     int cus;          // compute units of the device
+    int w0dir;        // W0 is [2][H][64][64]: forward, then reverse scan
 };
 size_t scan_ws_bytes(int B, int H, int N, int mode);
 hipError_t launch_scan(ScanLaunch a, hipStream_t stream);
@@ -103,6 +130,7 @@ struct LinBwdLaunch {
     int B, H, N;
     int bf16;
     void* ws;         // lin_bwd_ws_bytes(...) bytes
+    int dot;          // dot-product loss
 };
 size_t lin_bwd_ws_bytes(int B, int H, int N);
 // A and G recomputed by the forward's Gram pass when the caller saved none

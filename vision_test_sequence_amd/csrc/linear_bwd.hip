@@ -57,7 +57,13 @@ struct BwdArgs {
     u32x4* w1f;         // [slices][8][64]: bf16 fragments of W1^T (bf16 pass 1)
     int B, H, N, S, per, xcd;
     int S2, per2;       // bf16 pass 2: splits per slice, tokens per split (<= kP2Tok)
+    int dot;            // dot-product loss: beta = eta / N, M = 0, dW0 = sum_b dW1
 };
+
+// beta of the loss: L2 G = (2/N)(W0 A - C); dot-product G = -(1/N) C.
+__device__ __forceinline__ float bwd_beta(const BwdArgs& a, int h) {
+    return (a.dot ? 1.0f : 2.0f) * a.eta[h] / (float)a.N;
+}
 constexpr int kP2Tok = 256; // bf16 pass 2: tokens per workgroup, resident in LDS
 constexpr int kP1Tok = 256; // bf16 pass 1: tokens per workgroup, resident in LDS (64 KB: two per CU)
 
@@ -454,7 +460,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     const int tid = threadIdx.x;
     const int slice = blockIdx.x;
     const int h = slice % a.H;
-    const float beta = 2.0f * a.eta[h] / (float)a.N;
+    const float beta = bwd_beta(a, h);
+    const float wa = a.dot ? 0.f : 1.f; // the dot-product loss has no A or M terms
     const float* W0 = a.W0 + (long long)h * 4096;
     const float* A = a.saved + (long long)slice * 8192;
     const float* G = A + 4096;
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = R0 + 4 * g + i, c = 16 * cb + m;
-            dW0s[r * 64 + c] = D[r * MB + c] - beta * Q2[cb][i];
+            dW0s[r * 64 + c] = D[r * MB + c] - wa * beta * Q2[cb][i];
         }
     for (int e = tid; e < 1024; e += kThreads) {
         const int r = e >> 4, c4 = (e & 15) * 4;
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
             const int r = r0 + i;
             f32x4 mv;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) mv[j] = W[r * MB + c0 + j] + W[(c0 + j) * MB + r];
+            for (int j = 0; j < 4; ++j) mv[j] = wa * (W[r * MB + c0 + j] + W[(c0 + j) * MB + r]);
             *reinterpret_cast<f32x4*>(dm + 4096 + r * 64 + c0) = mv;
             *reinterpret_cast<f32x4*>(Am + r * MB + c0) = mv; // A's space is free now
         }
@@ -584,7 +591,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass2(BwdArgs a) {
     const Ctx c = ctx_of(a);
     if (c.slice >= a.B * a.H) return; // padding block of the XCD-aware grid
 
-    const float beta = 2.0f * a.eta[c.h] / (float)a.N;
+    const float beta = bwd_beta(a, c.h);
     {
         const float* src = a.dm + (long long)c.slice * 8192;
         for (int e = tid; e < 8192; e += kThreads) mats[(e >> 6) * MB + (e & 63)] = src[e];
@@ -815,6 +822,7 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.dW0 = s.dW0;
     a.deta = s.deta;
     a.B = s.B; a.H = s.H; a.N = s.N;
+    a.dot = s.dot;
     // pass 1 splits: bf16 tokens resident in LDS (<= kP1Tok per split)
     a.S = s.bf16 ? bwd_splits_bf(s.N) : bwd_splits(s.B, s.H, s.N);
     a.per = (((s.N + a.S - 1) / a.S) + 15) & ~15;

@@ -42,6 +42,12 @@ namespace {
 
 constexpr int MP = 68; // pitch (floats) of 64x64 fp32 matrices in LDS
 
+// G = scale (w_A W0 A - C): the L2 loss has scale 2/N and w_A = 1; the
+// dot-product loss (l = -<W k, v>) has scale 1/N and no W0 A term.
+__device__ __forceinline__ float grad_scale(const LinFwdLaunch& a) {
+    return (a.dot ? 1.0f : 2.0f) / (float)a.N;
+}
+
 template <bool BF> struct LinCfg;
 template <> struct LinCfg<true> {
     static constexpr int esz = 2;
@@ -265,7 +271,8 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
                              SliceWords* sw, bool published = false, Prefetch pf = Prefetch{0.f, 0.f}) {
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
-    const float scale = 2.0f / (float)a.N;
+    const float scale = grad_scale(a);
+    const float wa = a.dot ? 0.f : 1.f; // weight of the W0 A term
     auto stage_w0 = [&](float* dst) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -300,7 +307,7 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
                 const int r = r0 + i, c = c0 + k;
-                const float gv = scale * (acc[i][k] - mC[r * MP + c]);
+                const float gv = scale * (wa * acc[i][k] - mC[r * MP + c]);
                 mC[r * MP + c] = w0s_one[r * MP + c] - eta * gv;
                 if (sv) {
                     sv[r * 64 + c] = mA[r * MP + c];
@@ -367,7 +374,7 @@ __device__ float* lin_update(const LinFwdLaunch& a, int slice, int split, int h,
             acc2 += wv[2] * av[2];
             acc3 += wv[3] * av[3];
         }
-        const float gv = scale * (((acc0 + acc1) + (acc2 + acc3)) - res[(nc + cc) * 64 + r]);
+        const float gv = scale * (wa * ((acc0 + acc1) + (acc2 + acc3)) - res[(nc + cc) * 64 + r]);
         const float w1v = w0s_split[r * MP + c] - eta * gv;
         if constexpr (BF && XC) reinterpret_cast<bf16_t*>(w1g)[w1_frag_index(r, c)] = f2bf(w1v);
         else if constexpr (XC) w1g[r * 64 + c] = w1v;
@@ -749,18 +756,20 @@ __device__ __forceinline__ void g_rows_store(const LinFwdLaunch& a, int slice, i
     v4f G[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) G[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (!a.dot) { // (the dot-product loss has no W0 A term)
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            // B operand A[32 kk + 8 g + j][16 cb + m] = A[16 cb + m][32 kk + 8 g + j]
-            const int off = (16 * cb + m) * kAP + 32 * kk + 8 * g;
-            const v8bf bh = as_v8bf(*reinterpret_cast<const u32x4*>(L.ahi + off));
-            const v8bf bl = as_v8bf(*reinterpret_cast<const u32x4*>(L.alo + off));
-            G[cb] = mfma32(wh[kk], bh, G[cb]);
-            G[cb] = mfma32(wh[kk], bl, G[cb]);
-            G[cb] = mfma32(wl[kk], bh, G[cb]);
-        }
+            for (int cb = 0; cb < 4; ++cb) {
+                // B operand A[32 kk + 8 g + j][16 cb + m] = A[16 cb + m][32 kk + 8 g + j]
+                const int off = (16 * cb + m) * kAP + 32 * kk + 8 * g;
+                const v8bf bh = as_v8bf(*reinterpret_cast<const u32x4*>(L.ahi + off));
+                const v8bf bl = as_v8bf(*reinterpret_cast<const u32x4*>(L.alo + off));
+                G[cb] = mfma32(wh[kk], bh, G[cb]);
+                G[cb] = mfma32(wh[kk], bl, G[cb]);
+                G[cb] = mfma32(wl[kk], bh, G[cb]);
+            }
+    }
     const int lgS = __builtin_ctz(a.S), lgR = 12 - lgS, R = 1 << lgR;
     const long long sb = (long long)slice * a.S * 4096;
     const int e = 128 * (w & 1) + 64 * (g >> 1) + 4 * m;
@@ -804,7 +813,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
     constexpr int SG = S / NG;             // splits per group
     const int tid = threadIdx.x;
     const float eta = a.eta[h];
-    const float scale = 2.0f / (float)a.N;
+    const float scale = grad_scale(a);
     const f32x4* blk = reinterpret_cast<const f32x4*>(a.part + (long long)slice * S * 4096 + (long long)split * S * R);
     bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
     auto finish = [&](int t4, const f32x4& acc) __attribute__((always_inline)) {
@@ -1395,6 +1404,244 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     }
 }
 
+// ------------------------------------------------ several full-batch steps --
+// E gradient steps over the whole token set (the ViT3 article, observation
+// 2: more inner epochs).  A and C do not change between steps, so with
+// G0 = G(W0) the gradient at any W is G0 + (2/N) (W - W0) A (L2), or G0
+// (dot-product loss).  Per slice, from A and G0 saved by the forward's Gram
+// pass: W_1 = W0 - eta G0, W_{e+1} = W_e - eta (G0 + (2/N)(W_e - W0) A).
+// fp32 throughout; thread t owns rows 4 (t / 16).., columns 4 (t % 16)...
+__global__ __launch_bounds__(kThreads) void lin_epochs(LinEpochArgs a) {
+    __shared__ __attribute__((aligned(16))) float W0s[64 * MP];
+    __shared__ __attribute__((aligned(16))) float As[64 * MP];
+    __shared__ __attribute__((aligned(16))) float Ds[64 * MP]; // W_e - W0
+    const int slice = blockIdx.x, tid = threadIdx.x, h = slice % a.H;
+    const float eta = a.eta[h];
+    const float beta = 2.0f * eta / (float)a.N;
+    const float* A = a.saved + (long long)slice * 8192;
+    const float* G0 = A + 4096;
+    const float* W0 = a.W0 + (long long)h * 4096;
+    for (int e = tid; e < 4096; e += kThreads) {
+        W0s[(e >> 6) * MP + (e & 63)] = W0[e];
+        As[(e >> 6) * MP + (e & 63)] = A[e];
+    }
+    const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
+    float g0[4][4], w[4][4];
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            g0[i][k] = G0[(r0 + i) * 64 + c0 + k];
+            w[i][k] = W0s[(r0 + i) * MP + c0 + k] - eta * g0[i][k];
+        }
+    for (int e = 1; e < a.steps; ++e) {
+        if (a.dot) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) w[i][k] -= eta * g0[i][k];
+            continue;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) Ds[(r0 + i) * MP + c0 + k] = w[i][k] - W0s[(r0 + i) * MP + c0 + k];
+        __syncthreads();
+        float t[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) t[i][k] = 0.f;
+#pragma unroll 4
+        for (int j = 0; j < 64; ++j) {
+            const f32x4 av = *reinterpret_cast<const f32x4*>(As + j * MP + c0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float dv = Ds[(r0 + i) * MP + j];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) t[i][k] = fmaf(dv, av[k], t[i][k]);
+            }
+        }
+        __syncthreads(); // Ds is rewritten by the next step
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[i][k] -= eta * g0[i][k] + beta * t[i][k];
+    }
+    float* out = a.WE + (long long)slice * 4096;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<f32x4*>(out + (r0 + i) * 64 + c0) = f32x4{w[i][0], w[i][1], w[i][2], w[i][3]};
+}
+
+// Per-slice 64x64 weights staged into LDS (pitch MP) for the fragment helpers.
+__device__ __forceinline__ void stage_mat(float* dst, const float* src) {
+    for (int e = threadIdx.x; e < 1024; e += kThreads) {
+        const int r = e >> 4, c4 = (e & 15) * 4;
+        *reinterpret_cast<f32x4*>(dst + r * MP + c4) = *reinterpret_cast<const f32x4*>(src + r * 64 + c4);
+    }
+}
+
+// The lane's operand fragment of token row `row` (bf16: channels 32 h + 8 g
+// .. +8 for h = 0, 1; fp32: channels 16 h + 4 g .. +4 for h = 0..3), zeros
+// past the last token.
+template <bool BF>
+__device__ __forceinline__ void row_frag(const char* base, long long sn, int row, int N, int g, u32x4* q) {
+    constexpr int nh = BF ? 2 : 4;
+#pragma unroll
+    for (int hh = 0; hh < nh; ++hh) {
+        q[hh] = u32x4{0u, 0u, 0u, 0u};
+        if (row < N) {
+            const int ch = BF ? 32 * hh + 8 * g : 16 * hh + 4 * g;
+            q[hh] = *reinterpret_cast<const u32x4*>(base + (long long)row * sn + ch * (BF ? 2 : 4));
+        }
+    }
+}
+
+// Z = Q W^T for per-slice weights W (fp32 [slices][64][64]): 256 tokens per
+// workgroup, 16-token steps per wave on the matrix cores.
+template <bool BF>
+__global__ __launch_bounds__(kThreads) void lin_apply(LinApplyArgs a) {
+    __shared__ __attribute__((aligned(16))) float mW[64 * MP];
+    constexpr int esz = BF ? 2 : 4;
+    const int nb = (a.N + 255) / 256;
+    const int slice = blockIdx.x / nb, tb = blockIdx.x % nb;
+    const int b = slice / a.H, h = slice % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
+    stage_mat(mW, a.W + (long long)slice * 4096);
+    __syncthreads();
+    const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)esz;
+    char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)esz;
+    const long long Qsn = a.Q.sn * esz, Zsn = a.Z.sn * esz;
+    if constexpr (BF) {
+        const W1FragsBF wf = w1_frags_bf(mW, g, m);
+        for (int st = 0; st < 4; ++st) {
+            const int row = tb * 256 + w * 64 + st * 16 + m;
+            u32x4 q[2];
+            row_frag<true>(Qp, Qsn, row, a.N, g, q);
+            apply_bf(wf, q, Zp + (long long)row * Zsn, row < a.N, g, false);
+        }
+    } else {
+        const W1FragsF32 wf = w1_frags_f32(mW, g, m);
+        for (int st = 0; st < 4; ++st) {
+            const int row = tb * 256 + w * 64 + st * 16 + m;
+            u32x4 q[4];
+            row_frag<false>(Qp, Qsn, row, a.N, g, q);
+            apply_f32(wf, q, Zp + (long long)row * Zsn, row < a.N, g, false);
+        }
+    }
+}
+
+// ------------------------------------------------ gradient magnitude map --
+// Per token, the Frobenius norm of its own gradient at W0 (the Vision-TTT
+// notes' gradient magnitude map).  The gradient is rank one, so
+// ||G_t||_F = 2 ||W0 k_t - v_t|| ||k_t|| (L2) or ||v_t|| ||k_t|| (dot-
+// product loss).  W0 k_t on the matrix cores (bf16 inputs: W0 rounded to
+// bf16 like the apply's W1; fp32 inputs: fp32 products); lane (g, m) holds
+// 16 of token m's channels, the four lane groups add their squares.
+template <bool BF>
+__global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
+    __shared__ __attribute__((aligned(16))) float mW[64 * MP];
+    constexpr int esz = BF ? 2 : 4;
+    const int nb = (a.N + 255) / 256;
+    const int slice = blockIdx.x / nb, tb = blockIdx.x % nb;
+    const int b = slice / a.H, h = slice % a.H;
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
+    stage_mat(mW, a.W0 + (long long)h * 4096);
+    __syncthreads();
+    const char* Kp = (const char*)a.K.ptr + (b * a.K.sb + h * a.K.sh) * (long long)esz;
+    const char* Vp = (const char*)a.V.ptr + (b * a.V.sb + h * a.V.sh) * (long long)esz;
+    const long long Ksn = a.K.sn * esz, Vsn = a.V.sn * esz;
+    float* out = a.out + (long long)slice * a.N;
+    auto finish = [&](int row, float kk, float rr) __attribute__((always_inline)) {
+        kk += __shfl_xor(kk, 16);
+        kk += __shfl_xor(kk, 32);
+        rr += __shfl_xor(rr, 16);
+        rr += __shfl_xor(rr, 32);
+        if (g == 0 && row < a.N) out[row] = (a.dot ? 1.0f : 2.0f) * sqrtf(rr) * sqrtf(kk);
+    };
+    for (int st = 0; st < 4; ++st) {
+        const int row = tb * 256 + w * 64 + st * 16 + m;
+        // v at the lane's output channels 8 g .. 8 g + 7 and 32 + 8 g .. +7
+        float vv[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) vv[j] = 0.f;
+        if (row < a.N) {
+            const char* vr = Vp + (long long)row * Vsn;
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                const int ch = 32 * half + 8 * g;
+                if constexpr (BF) {
+                    const u32x4 u = *reinterpret_cast<const u32x4*>(vr + ch * 2);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        vv[8 * half + 2 * k] = bflo(u[k]);
+                        vv[8 * half + 2 * k + 1] = bfhi(u[k]);
+                    }
+                } else {
+                    const f32x4 u0 = *reinterpret_cast<const f32x4*>(vr + ch * 4);
+                    const f32x4 u1 = *reinterpret_cast<const f32x4*>(vr + (ch + 4) * 4);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) {
+                        vv[8 * half + k] = u0[k];
+                        vv[8 * half + 4 + k] = u1[k];
+                    }
+                }
+            }
+        }
+        constexpr int nh = BF ? 2 : 4;
+        u32x4 q[nh];
+        row_frag<BF>(Kp, Ksn, row, a.N, g, q);
+        float kk = 0.f;
+#pragma unroll
+        for (int hh = 0; hh < nh; ++hh)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                if constexpr (BF) {
+                    kk = fmaf(bflo(q[hh][k]), bflo(q[hh][k]), kk);
+                    kk = fmaf(bfhi(q[hh][k]), bfhi(q[hh][k]), kk);
+                } else {
+                    const float x = __uint_as_float(q[hh][k]);
+                    kk = fmaf(x, x, kk);
+                }
+            }
+        // r = W0 k - v (L2) or -v (dot); d[rb][i] is output channel
+        // 32 (rb >> 1) + 8 g + 4 (rb & 1) + i (perm_row)
+        v4f d[4];
+        if constexpr (BF) {
+            const W1FragsBF wf = w1_frags_bf(mW, g, m);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+                d[rb] = mfma32(wf.f[rb][0], as_v8bf(q[0]), d[rb]);
+                d[rb] = mfma32(wf.f[rb][1], as_v8bf(q[1]), d[rb]);
+            }
+        } else {
+            const W1FragsF32 wf = w1_frags_f32(mW, g, m);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb) {
+                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int hh = 0; hh < 4; ++hh) {
+                    const f32x4 qv = __builtin_bit_cast(f32x4, q[hh]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) d[rb] = mfma4(wf.f[rb][hh * 4 + i], qv[i], d[rb]);
+                }
+            }
+        }
+        float rr = 0.f;
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = (a.dot ? 0.f : d[rb][i]) - vv[8 * (rb >> 1) + 4 * (rb & 1) + i];
+                rr = fmaf(x, x, rr);
+            }
+        finish(row, kk, rr);
+    }
+}
+
 int pow2_floor(long long s) {
     int p = 1;
     while (2LL * p <= s) p *= 2;
@@ -1484,6 +1731,25 @@ bool layer_would_fuse(const LinFwdLaunch& l, int resident, const ConvLaunch& cl)
     unsigned cgrid = 0;
     conv_prepare(cl, c, cgrid);
     return layer_fusable(l, resident, c, cl.bf16);
+}
+
+hipError_t launch_lin_epochs(const LinEpochArgs& e, hipStream_t stream) {
+    hipLaunchKernelGGL(lin_epochs, dim3((unsigned)e.slices), dim3(kThreads), 0, stream, e);
+    return hipGetLastError();
+}
+
+hipError_t launch_lin_apply(const LinApplyArgs& a, int bf16, hipStream_t stream) {
+    const long long blocks = (long long)a.B * a.H * ((a.N + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(lin_apply<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(lin_apply<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_lin_gmm(const LinGmmArgs& a, int bf16, hipStream_t stream) {
+    const long long blocks = (long long)a.B * a.H * ((a.N + 255) / 256);
+    if (bf16) hipLaunchKernelGGL(lin_gmm<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    else hipLaunchKernelGGL(lin_gmm<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_layer(LinFwdLaunch l, int resident, ConvLaunch cl, hipStream_t stream) {

@@ -82,6 +82,7 @@ struct ScanArgs {
     int H, N, b, nch, slices, mode, xcd;
     int split;         // both directions: outputs to P / P2 (then scan_average)
     int blocks;        // workgroups per direction
+    int w0dir;         // W0 is [2][H][64][64]: forward, then reverse scan
 };
 
 // Per-lane walk of one chain.  Token slot m of chunk j is token
@@ -328,7 +329,9 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
         // per-lane resolution (lane offsets go into the buffer offsets)
         const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
         const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
-        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, a.W0 + (long long)h * 4096, a.eta[h], lds);
+        // the reverse scan starts from its own W0 when one is given per direction
+        const float* W0h = a.W0 + ((a.w0dir && L.dir ? (long long)a.H : 0) + h) * 4096;
+        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, W0h, a.eta[h], lds);
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2;
@@ -374,6 +377,7 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     ScanArgs a{};
     a.K = s.K; a.Q = s.Q; a.V = s.V; a.Z = s.Z;
     a.W0 = s.W0; a.eta = s.eta;
+    a.w0dir = s.w0dir;
     a.H = s.H; a.N = s.N; a.b = s.b;
     a.nch = (s.N + s.b - 1) / s.b;
     a.slices = s.B * s.H;
