@@ -196,9 +196,12 @@ def test_scan_errors():
     L = vt.lib()
     need = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P()))
     assert bd.STATUS_NAMES[scan(P(), wsb=need - 1)] == "TTT_ERR_WORKSPACE_TOO_SMALL"
-    # the averaged scan keeps one bf16 output per token, channel and direction
+    # the averaged scan keeps one fp32 output per token, channel and direction
     one = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P(mode=1)))
-    assert need - one >= 2 * 2 * 3 * 100 * 64 * 2
+    assert need - one >= 2 * 2 * 3 * 100 * 64 * 4
+    # mini-batches of several 16-token tiles: multiples of 16, or b >= N
+    assert bd.STATUS_NAMES[scan(P(b=20))] == "TTT_ERR_UNSUPPORTED"
+    assert bd.STATUS_NAMES[scan(P(b=33))] == "TTT_ERR_UNSUPPORTED"
     assert bd.STATUS_NAMES[scan(P(), Z=V(2))] == "TTT_ERR_ALIASING"
     # a slice's rows must be addressable with 31-bit offsets, overrun included
     # (the workspace is withheld, so a missed check could not launch)

@@ -153,3 +153,40 @@ def test_one_token_views_with_zero_token_stride(mode):
     torch.cuda.synchronize()
     Zr = oracle.linear_minibatch(f64(K), f64(Q), f64(V), f64(W0), f64(eta), 16, mode)
     assert slice_rel_err(f64(Z), Zr) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("N,b", [(196, 32), (196, 64), (196, 196), (196, 500), (1000, 1000), (6400, 32),
+                                 (6400, 64), (2003, 48), (17, 16), (33, 32)])
+@pytest.mark.parametrize("mode", [BIDIR, FWD, BWD])
+def test_minibatches_of_several_tiles(N, b, mode):
+    # mini-batches larger than one 16-token tile (the b-sweep 4 .. 196 of
+    # the Vision-TTT ablation; b >= N is one full-batch step)
+    banner(f"scan N={N} b={b} mode={mode}")
+    inp = wl.draw(2, 3, N, seed=1500 + N + b + mode, dtype="bf16", unit_rows=True, eta_fixed=None)
+    _check(*_on(inp), b, mode)
+
+
+def test_one_minibatch_of_all_tokens_is_the_full_batch_step():
+    # b = N: the forward scan's last token sees every gradient, taken at W0:
+    # its output is the full-batch step's output for that token
+    import vision_test_sequence_amd as vt
+    banner("scan b = N equals the full-batch step at the last token")
+    N = 6084
+    inp = wl.draw(2, 2, N, seed=1510, dtype="bf16", unit_rows=True, eta_fixed=None)
+    K, Q, V, W0, eta = _on(inp)
+    Zs = vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, N, FWD)
+    torch.cuda.synchronize()
+    Zf, _ = oracle.linear_fullbatch(f64(K), f64(Q), f64(V), f64(W0), f64(eta))
+    assert slice_rel_err(f64(Zs[:, :, -1:]), Zf[:, :, -1:]) <= TOL["bf16"]
+    Zb = vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, N, BWD)
+    torch.cuda.synchronize()
+    assert slice_rel_err(f64(Zb[:, :, :1]), Zf[:, :, :1]) <= TOL["bf16"]
+
+
+def test_minibatch_sizes_the_kernel_does_not_take():
+    import vision_test_sequence_amd as vt
+    from vision_test_sequence_amd.binding import TTTError
+    banner("scan b = 20 (not a multiple of 16, below N) -> unsupported")
+    K, Q, V, W0, eta = _on(wl.draw(1, 1, 100, seed=1520, dtype="bf16"))
+    with pytest.raises(TTTError, match="UNSUPPORTED"):
+        vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 20, BIDIR)

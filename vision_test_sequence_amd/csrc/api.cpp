@@ -563,7 +563,7 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     if (p->minibatch < 1) return TTT_ERR_BAD_SHAPE;
     if (p->mode != TTT_BIDIR_AVG && p->mode != TTT_FORWARD_ONLY && p->mode != TTT_BACKWARD_ONLY)
         return TTT_ERR_UNSUPPORTED;
-    if (p->minibatch > 16) return TTT_ERR_UNSUPPORTED;
+    if (!scan_minibatch_supported(p->minibatch, p->N)) return TTT_ERR_UNSUPPORTED;
     if (p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
     if (p->loss != TTT_LOSS_L2 || p->steps > 1) return TTT_ERR_UNSUPPORTED;
     if (noop) return TTT_OK;

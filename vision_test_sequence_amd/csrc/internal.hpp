@@ -117,6 +117,8 @@ struct ScanLaunch {
     int w0dir;        // W0 is [2][H][64][64]: forward, then reverse scan
 };
 size_t scan_ws_bytes(int B, int H, int N, int mode);
+// Mini-batch sizes the scan kernel takes: b <= 16, multiples of 16, b >= N.
+bool scan_minibatch_supported(int b, int N);
 hipError_t launch_scan(ScanLaunch a, hipStream_t stream);
 
 // ---- backward of the full-batch linear step ----------------------------

@@ -45,6 +45,8 @@
 #include "common.hpp"
 #include "internal.hpp"
 
+#include <algorithm>
+
 namespace ttt {
 namespace {
 
@@ -77,19 +79,25 @@ struct ScanArgs {
     View4 K, Q, V, Z;
     const float* W0;
     const float* eta;
-    bf16_t* P;         // [slices][N][64]: forward-direction outputs (both directions)
-    bf16_t* P2;        // [slices][N][64]: backward-direction outputs
+    float* P;          // [slices][N][64]: forward-direction outputs (both directions)
+    float* P2;         // [slices][N][64]: backward-direction outputs
     int H, N, b, nch, slices, mode, xcd;
     int split;         // both directions: outputs to P / P2 (then scan_average)
     int blocks;        // workgroups per direction
     int w0dir;         // W0 is [2][H][64][64]: forward, then reverse scan
+    int tb;            // tokens per tile: b (b <= 16) or 16
+    int T;             // tiles per mini-batch: 1 (b <= 16) or ceil(min(b, N) / 16)
+    int ntile;         // tiles of one walk: ceil(N / tb)
 };
 
-// Per-lane walk of one chain.  Token slot m of chunk j is token
-// p = j*b + m (forward) or N-1-(j*b + m) (reverse).
+// Per-lane walk of one chain over tiles of tb tokens.  Token slot m of
+// tile j is token p = j*tb + m (forward) or N-1-(j*tb + m) (reverse).  A
+// mini-batch is one tile (b <= 16) or T consecutive 16-token tiles (b a
+// multiple of 16, or b >= N: then every mini-batch but the walk's last is
+// T whole tiles).
 struct Walk {
     int g, m, rt, dir, b, N, nch;
-    long long step; // token step per chunk: +-b
+    long long step; // token step per tile: +-tb
 };
 __device__ __forceinline__ int token_of(const Walk& L, int rho) { return L.dir ? L.N - 1 - rho : rho; }
 // Loads are branch-free (so the compiler can schedule them into the
@@ -159,8 +167,15 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(cr[u]);
 
-    const float alpha_full = -2.0f * eta / (float)L.b;
-    const float alpha_last = -2.0f * eta / (float)(L.N - (L.nch - 1) * L.b);
+    // step of each mini-batch: -2 eta / n_c (the last one may be shorter)
+    const float alpha_full = -2.0f * eta / (float)a.b;
+    const float alpha_last = -2.0f * eta / (float)(L.N - (a.nch - 1) * a.b);
+    // mini-batch of the current tile and the tile's place in it (wave-
+    // uniform counters); xs: the mini-batch's start state in bf16, the B
+    // operand of its residuals R = K X_s - V, while X runs on through the
+    // batch's tiles (the output wave needs the running state)
+    int chunk = 0, sub = 0;
+    u32x4 xs[2];
     // LDS addresses: this lane's K row chunks and V row piece; transposing
     // reads (in each 16-lane group lane 4e + a points at a 4-element row
     // piece, lane m of the group receives element m % 4 of the pieces of
@@ -187,28 +202,36 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
     for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
         for (int u = 0; u < D; ++u) {
-            const int j = j0 + u;
             Regs& r = cr[u];
             char* xo = lds + kXOff + (u % kNX) * kXBuf + lane * kXLane;
-            // the next chunk's operands, one step ahead of their use
+            // the next tile's operands, one step ahead of their use
             v4s_t ktN[4], vinN;
             stage(cr[(u + 1) % D], (u + 1) % kNK, (u + 1) & 1, ktN, vinN);
-            const float alpha = j < L.nch - 1 ? alpha_full : (j == L.nch - 1 ? alpha_last : 0.f);
+            const float alpha = chunk < a.nch - 1 ? alpha_full : (chunk == a.nch - 1 ? alpha_last : 0.f);
 
-            // bf16 copy of the chunk-start state
+            // bf16 copy of the running state (published), and of the
+            // mini-batch's start state at its first tile
             u32x4 xu[2];
 #pragma unroll
             for (int kb2 = 0; kb2 < 2; ++kb2)
                 xu[kb2] = u32x4{pack_bf2(X[2 * kb2][0], X[2 * kb2][1]), pack_bf2(X[2 * kb2][2], X[2 * kb2][3]),
                                 pack_bf2(X[2 * kb2 + 1][0], X[2 * kb2 + 1][1]),
                                 pack_bf2(X[2 * kb2 + 1][2], X[2 * kb2 + 1][3])};
-            // R = K X - V ;  R' = alpha R, the two halves of the channel
+            if (sub == 0) {
+                xs[0] = xu[0];
+                xs[1] = xu[1];
+            }
+            if (++sub == a.T) {
+                sub = 0;
+                ++chunk;
+            }
+            // R = K X_s - V ;  R' = alpha R, the two halves of the channel
             // contraction chained on the matrix cores (fewer vector
             // instructions: the waves' instruction streams bound the scan)
             // -V from the transposed bf16 pairs: one sign flip per pair
             const u32x2 vneg = __builtin_bit_cast(u32x2, vin) ^ u32x2{0x80008000u, 0x80008000u};
             const v4f Rv{bflo(vneg[0]), bfhi(vneg[0]), bflo(vneg[1]), bfhi(vneg[1])};
-            const v4f R = mfma32(as_v8bf(r.k[1]), as_v8bf(xu[1]), mfma32(as_v8bf(r.k[0]), as_v8bf(xu[0]), Rv));
+            const v4f R = mfma32(as_v8bf(r.k[1]), as_v8bf(xs[1]), mfma32(as_v8bf(r.k[0]), as_v8bf(xs[0]), Rv));
             const u32x2 rp2{pack_bf2(alpha * R[0], alpha * R[1]), pack_bf2(alpha * R[2], alpha * R[3])};
             // X += K^T R'
 #pragma unroll
@@ -227,11 +250,11 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 }
 
 // ----------------------------------------------------------- output wave --
-// Q, Z (or P, this direction's [N][64] bf16 rows): the slice's token 0,
+// Q, Z (or P, this direction's [N][64] fp32 rows): the slice's token 0,
 // channel 0; Qsn, Zsn: token strides in bytes.
 template <int D>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
-                            long long Zsn, bf16_t* P, const char* lds) {
+                            long long Zsn, float* P, const char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int ch = 16 * L.rt + 4 * g; // this lane's output channels
     // Q rows, Z / P outputs through buffer descriptors over the slice: a
@@ -259,11 +282,11 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     // m), kept where 4g+i <= m, as bit masks of the packed bf16 pairs
     const u32x2 tril{(4 * g <= m ? 0xFFFFu : 0u) | (4 * g + 1 <= m ? 0xFFFF0000u : 0u),
                      (4 * g + 2 <= m ? 0xFFFFu : 0u) | (4 * g + 3 <= m ? 0xFFFF0000u : 0u)};
-    // outputs: this direction's bf16 rows of P ([N][64] per slice), or Z
-    const __amdgpu_buffer_rsrc_t zrs = a.split ? span_rsrc(P, (long long)L.N * 128)
+    // outputs: this direction's fp32 rows of P ([N][64] per slice), or Z
+    const __amdgpu_buffer_rsrc_t zrs = a.split ? span_rsrc(P, (long long)L.N * 256)
                                                : span_rsrc(Z, (long long)(L.N - 1) * Zsn + 128);
-    const long long zsn = a.split ? 128 : Zsn;
-    unsigned zoff = slot ? (unsigned)(p0 * zsn + 2 * ch) : kOffSlice;
+    const long long zsn = a.split ? 256 : Zsn;
+    unsigned zoff = slot ? (unsigned)(p0 * zsn + (a.split ? 4 : 2) * ch) : kOffSlice;
     const unsigned zst = slot ? (unsigned)(L.step * zsn) : 0u;
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
@@ -288,10 +311,16 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
             const v4f Zt = mfma16(as_v4s(rp2), as_v4s(sb2), Zq);
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3 (Z
-            // streamed past the caches; P is read back by the average)
-            const u32x2 zv{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
-            if (a.split) __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 0);
-            else __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 2 /* nt */);
+            // streamed past the caches; P, in fp32, is read back by the
+            // average, so each direction's output is rounded once, in Z)
+            if (a.split) {
+                const u32x4 pv{__float_as_uint(Zt[0]), __float_as_uint(Zt[1]), __float_as_uint(Zt[2]),
+                               __float_as_uint(Zt[3])};
+                __builtin_amdgcn_raw_buffer_store_b128(pv, zrs, zoff, 0, 0);
+            } else {
+                const u32x2 zv{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
+                __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 2 /* nt */);
+            }
             asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
             zoff += zst;
             issue(r);
@@ -319,10 +348,10 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     L.m = lane & 15;
     L.rt = ss.split;
     L.dir = a.split ? dsplit : (a.mode == 2 ? 1 : 0);
-    L.b = a.b;
+    L.b = a.tb;
     L.N = a.N;
-    L.nch = a.nch;
-    L.step = L.dir ? -(long long)a.b : (long long)a.b;
+    L.nch = a.ntile;
+    L.step = L.dir ? -(long long)a.tb : (long long)a.tb;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
     if (role == 0) {
         // slice bases: wave-uniform, so the buffer descriptors need no
@@ -335,13 +364,13 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2;
-        bf16_t* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 : nullptr;
+        float* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 : nullptr;
         output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
     }
 }
 
-// Z = (forward + backward) / 2 from the two directions' outputs, 8
-// channels (16 bytes of each) per thread.
+// Z = (forward + backward) / 2 from the two directions' fp32 outputs,
+// rounded to bf16 once; 8 channels per thread.
 __global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
     const long long e = (long long)blockIdx.x * 256 + threadIdx.x; // (slice, token, channel octet)
     if (e >= (long long)a.slices * a.N * 8) return;
@@ -349,12 +378,14 @@ __global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
     const long long st = e >> 3;
     const int p = (int)(st % a.N), slice = (int)(st / a.N);
     const int bb = slice / a.H, h = slice % a.H;
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a.P + st * 64 + 8 * c8);
-    const u32x4 y = *reinterpret_cast<const u32x4*>(a.P2 + st * 64 + 8 * c8);
+    const f32x4* xp = reinterpret_cast<const f32x4*>(a.P + st * 64 + 8 * c8);
+    const f32x4* yp = reinterpret_cast<const f32x4*>(a.P2 + st * 64 + 8 * c8);
+    const f32x4 x0 = xp[0], x1 = xp[1], y0 = yp[0], y1 = yp[1];
     u32x4 o;
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-        o[k] = pack_bf2(0.5f * (bflo(x[k]) + bflo(y[k])), 0.5f * (bfhi(x[k]) + bfhi(y[k])));
+    o[0] = pack_bf2(0.5f * (x0[0] + y0[0]), 0.5f * (x0[1] + y0[1]));
+    o[1] = pack_bf2(0.5f * (x0[2] + y0[2]), 0.5f * (x0[3] + y0[3]));
+    o[2] = pack_bf2(0.5f * (x1[0] + y1[0]), 0.5f * (x1[1] + y1[1]));
+    o[3] = pack_bf2(0.5f * (x1[2] + y1[2]), 0.5f * (x1[3] + y1[3]));
     bf16_t* z = (bf16_t*)a.Z.ptr + bb * a.Z.sb + h * a.Z.sh + (long long)p * a.Z.sn + 8 * c8;
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(z));
 }
@@ -368,9 +399,11 @@ long long padded_slices(int B, int H) {
 
 size_t scan_ws_bytes(int B, int H, int N, int mode) {
     size_t bytes = 256;
-    if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(bf16_t);
+    if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(float);
     return bytes;
 }
+
+bool scan_minibatch_supported(int b, int N) { return b >= 1 && (b <= 16 || b % 16 == 0 || b >= N); }
 
 hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     if (!s.bf16) return hipErrorNotSupported;
@@ -380,6 +413,11 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.w0dir = s.w0dir;
     a.H = s.H; a.N = s.N; a.b = s.b;
     a.nch = (s.N + s.b - 1) / s.b;
+    // tiles: a mini-batch of b <= 16 tokens is one tile; a larger one is
+    // ceil(min(b, N) / 16) tiles of 16 (b a multiple of 16, or b >= N)
+    a.tb = s.b <= 16 ? s.b : 16;
+    a.T = s.b <= 16 ? 1 : (std::min(s.b, s.N) + 15) / 16;
+    a.ntile = (s.N + a.tb - 1) / a.tb;
     a.slices = s.B * s.H;
     a.mode = s.mode;
     // both directions: each in workgroups of its own, bf16 outputs averaged
@@ -391,7 +429,7 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     // workspace: [256 bytes reserved][P][P2]
     float* base = (float*)s.ws;
     if (a.split) {
-        a.P = reinterpret_cast<bf16_t*>(base + 64);
+        a.P = base + 64;
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
     }
     const long long grid = blocks * (a.split ? 2 : 1);
