@@ -19,6 +19,10 @@ own workloads (the mini-batch bidirectional scan at 1280x1280, the forward
 and backward of the linear step at ViT-B 1024x1024), and the fp64 oracle
 timed on the host.
 
+The headline is the median of REPLAYS replays of one graph of K steps
+(p10 and p90 reported beside it); every other row is graph-replayed too,
+over rotating input sets where one set would fit the Infinity Cache.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 from __future__ import annotations
@@ -39,6 +43,7 @@ SCAN_WORKLOAD = "vittt_s_1280_bf16"
 BWD_WORKLOAD = "vitb_1024_fwdbwd_bf16"
 METRIC = "TTT-layer tokens/s at N=6084, H=3, d=64 bf16; % MFMA / HBM roofline"
 NSETS = 5
+REPLAYS = 7                      # graph replays of the headline (median, p10, p90)
 ROOT = os.path.dirname(os.path.abspath(__file__))
 # HBM bytes per launch of the layer kernel from rocprofv3 FETCH_SIZE /
 # WRITE_SIZE runs, stored with the hash of the sources they were taken on
@@ -110,14 +115,15 @@ def time_calls(torch, fn, n):
     return e0.elapsed_time(e1) / n
 
 
-def time_graphed(torch, fn, n):
+def time_graphed(torch, fn, n, replays=1):
     """Average time per call of n calls captured in one HIP graph
-    (torch.cuda.graph) and replayed once, between HIP events on the replay
-    stream, in ms.  The layer's kernels take about as long as one Python
-    call through the binding, so eager back-to-back calls would measure
-    the host; the graph launches the same kernels with the same arguments
-    without it.  A warm-up on a side stream precedes the capture, as torch
-    asks; the replay after an untimed one is timed."""
+    (torch.cuda.graph), in ms, for each of `replays` timed replays (a list),
+    between HIP events on the replay stream.  The layer's kernels take
+    about as long as one Python call through the binding, so eager
+    back-to-back calls would measure the host; the graph launches the same
+    kernels with the same arguments without it.  A warm-up on a side stream
+    precedes the capture, as torch asks; an untimed replay precedes the
+    timed ones."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -126,43 +132,67 @@ def time_graphed(torch, fn, n):
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    # captured on the warm-up stream: the binding's workspace for that
+    # stream exists already, so nothing is allocated inside the capture
+    with torch.cuda.graph(graph, stream=side):
         for i in range(n):
             fn(i)
     graph.replay()  # untimed
     torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
+    times = []
+    for _ in range(replays):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) / n)
     del graph
-    return e0.elapsed_time(e1) / n
+    return times if replays > 1 else times[0]
 
 
-def rows(torch, vt, wl, dev):
-    """The scan and the backward on their own workloads."""
+def spread(times):
+    """median, p10, p90 of a list of per-call times (ms)."""
+    import numpy as np
+    t = np.asarray(times, dtype=np.float64)
+    return float(np.median(t)), float(np.percentile(t, 10)), float(np.percentile(t, 90))
+
+
+def _row(us, nbytes, tokens, extra=None):
+    r = {"us_per_call": us, "tokens_per_s": tokens / (us * 1e-6), "algorithmic_bytes": nbytes,
+         "gbs": nbytes / (us * 1e-6) / 1e9, "hbm_frac": nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    r.update(extra or {})
+    return r
+
+
+def rows(torch, vt, wl, dev, n=40):
+    """The other rows of the path on their own workloads, each graph-
+    replayed (n calls per graph, median of 3 replays) over input sets that
+    rotate where one set would fit the Infinity Cache."""
     out = {}
+    med = lambda f, k=n: spread(time_graphed(torch, f, k, replays=3))[0]
+    # mini-batch bidirectional scan, 1280x1280, b = 16 (and b = 64)
     w = wl.WORKLOADS[SCAN_WORKLOAD]
-    inp = wl.make(SCAN_WORKLOAD)
-    K, Q, V, W0, eta = (inp[k].to(dev) for k in ("K", "Q", "V", "W0", "eta"))
-    Z = torch.empty_like(Q)
-    f = lambda i: vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, w.minibatch, 0, Z=Z)
-    for i in range(3):
-        f(i)
-    ms = time_calls(torch, f, 20)
+    sets = []
+    for sidx in range(4):  # 4 x 78.6 MB > the 256 MB Infinity Cache
+        inp = wl.make(SCAN_WORKLOAD, seed_offset=1000 * sidx)
+        g = {k: inp[k].to(dev) for k in ("K", "Q", "V", "W0", "eta")}
+        g["Z"] = torch.empty_like(g["Q"])
+        sets.append(g)
     nbytes = 4 * w.B * w.H * w.N * w.d * 2
-    flops = w.B * w.H * w.N * 2 * (6 * w.d ** 2 + 4 * w.minibatch * w.d)
-    out["scan_bidir"] = {
-        "workload": f"{SCAN_WORKLOAD}: B={w.B}, H={w.H}, {w.grid_h}x{w.grid_w} N={w.N}, "
-                    f"b={w.minibatch}, both directions averaged",
-        "us_per_call": ms * 1e3, "tokens_per_s": w.B * w.N / (ms * 1e-3),
-        "algorithmic_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
-        "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-        "tflops": flops / (ms * 1e-3) / 1e12,
-    }
-    del K, Q, V, Z
+    for b in (w.minibatch, 64):
+        f = lambda i, b=b: vt.ttt_linear_minibatch_bidir(sets[i % 4]["K"], sets[i % 4]["Q"], sets[i % 4]["V"],
+                                                         sets[i % 4]["W0"], sets[i % 4]["eta"], b, 0,
+                                                         Z=sets[i % 4]["Z"])
+        ms = med(f)
+        flops = w.B * w.H * w.N * 2 * (6 * w.d ** 2 + 4 * min(b, 16) * w.d)
+        out[f"scan_bidir_b{b}"] = _row(ms * 1e3, nbytes, w.B * w.N, {
+            "workload": f"{SCAN_WORKLOAD}: B={w.B}, H={w.H}, {w.grid_h}x{w.grid_w} N={w.N}, b={b}, "
+                        "both directions averaged, 4 input sets rotated",
+            "tflops": flops / (ms * 1e-3) / 1e12})
+    del sets
+    # forward (saving A, G) and backward of the linear step, ViT-B 1024x1024
     w = wl.WORKLOADS[BWD_WORKLOAD]
     inp = wl.make(BWD_WORKLOAD)
     K, Q, V, dZ = (inp[k].to(dev) for k in ("K", "Q", "V", "dZ"))
@@ -176,11 +206,8 @@ def rows(torch, vt, wl, dev):
     fw = lambda i: vt.ttt_linear_fullbatch(K, Q, V, W0, eta, Z=Z, saved=saved)
     bw = lambda i: vt.ttt_linear_fullbatch_bwd(K, Q, V, W0, eta, dZ, saved=saved, dK=outs[0],
                                                dQ=outs[1], dV=outs[2], dW0=dW0, deta=deta)
-    for i in range(3):
-        fw(i)
-        bw(i)
-    ms_f = time_calls(torch, fw, 20)
-    ms_b = time_calls(torch, bw, 20)
+    ms_f = med(fw, 10)  # (one set: 1.1 GB per forward + backward, beyond the Infinity Cache)
+    ms_b = med(bw, 10)
     fb = 4 * B * H * N * d * 2
     bb = 7 * B * H * N * d * 2
     out["fwd_bwd"] = {
@@ -189,8 +216,51 @@ def rows(torch, vt, wl, dev):
         "fwd_us": ms_f * 1e3, "bwd_us": ms_b * 1e3,
         "fwd_gbs": fb / (ms_f * 1e-3) / 1e9, "bwd_gbs": bb / (ms_b * 1e-3) / 1e9,
         "hbm_frac": (fb + bb) / ((ms_f + ms_b) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "bwd_hbm_frac": bb / (ms_b * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "tokens_per_s": B * N / ((ms_f + ms_b) * 1e-3),
     }
+    del K, Q, V, dZ, Z, outs, saved
+    # the 1248x1248 layer's other operations: conv-head backward, the
+    # gradient magnitude map of the linear heads, dot-product loss and two
+    # full-batch steps of the linear heads
+    w = wl.WORKLOADS[WORKLOAD]
+    lin = w.head_indices("linear")
+    l0, l1, c = lin[0], lin[-1] + 1, w.head_indices("dwconv3x3")[0]
+    gs = []
+    for sidx in range(NSETS):
+        inp = wl.draw(w.B, w.H, w.N, seed=w.seed + 1000 * sidx, dtype="bf16", unit_rows=True, backward=True)
+        g = {k: v.to(dev) for k, v in inp.items()}
+        g["out"] = [torch.empty_like(g["K"][:, c:c + 1]) for _ in range(3)]
+        g["Z"] = torch.empty_like(g["Q"])
+        g["gmm"] = torch.empty((w.B, l1 - l0, w.N), dtype=torch.float32, device=dev)
+        g["W0l"], g["etal"] = g["W0"][l0:l1].contiguous(), g["eta"][l0:l1].contiguous()
+        g["w0c"], g["etac"] = g["w0"][c:c + 1].contiguous(), g["eta"][c:c + 1].contiguous()
+        gs.append(g)
+    conv_dw0 = torch.empty((1, 64, 3, 3), dtype=torch.float32, device=dev)
+    conv_deta = torch.empty((1,), dtype=torch.float32, device=dev)
+    cb = lambda i: vt.ttt_dwconv3x3_fullbatch_bwd(
+        gs[i % NSETS]["K"][:, c:c + 1], gs[i % NSETS]["Q"][:, c:c + 1], gs[i % NSETS]["V"][:, c:c + 1],
+        gs[i % NSETS]["w0c"], gs[i % NSETS]["etac"], gs[i % NSETS]["dZ"][:, c:c + 1], w.grid_h, w.grid_w,
+        dK=gs[i % NSETS]["out"][0], dQ=gs[i % NSETS]["out"][1], dV=gs[i % NSETS]["out"][2], dw0=conv_dw0,
+        deta=conv_deta)
+    ms = med(cb)
+    out["dwconv_bwd"] = _row(ms * 1e3, 7 * w.B * w.N * w.d * 2, w.B * w.N, {
+        "workload": f"{WORKLOAD} conv head: B={w.B}, {w.grid_h}x{w.grid_w}, g recomputed, "
+                    f"{NSETS} input sets rotated"})
+    lv = lambda g: (g["K"][:, l0:l1], g["Q"][:, l0:l1], g["V"][:, l0:l1], g["W0l"], g["etal"])
+    gm = lambda i: vt.ttt_linear_gradient_magnitude(gs[i % NSETS]["K"][:, l0:l1], gs[i % NSETS]["V"][:, l0:l1],
+                                                    gs[i % NSETS]["W0l"], out=gs[i % NSETS]["gmm"])
+    ms = med(gm)
+    out["gradient_magnitude_map"] = _row(ms * 1e3, w.B * (l1 - l0) * w.N * (2 * w.d * 2 + 4), w.B * w.N, {
+        "workload": f"{WORKLOAD} linear heads: K, V read, one fp32 norm written per token and head"})
+    dl = lambda i: vt.ttt_linear_fullbatch(*lv(gs[i % NSETS]), Z=gs[i % NSETS]["Z"][:, l0:l1], loss=vt.LOSS_DOT)
+    ms = med(dl)
+    out["linear_dot_loss"] = _row(ms * 1e3, 4 * w.B * (l1 - l0) * w.N * w.d * 2, w.B * w.N, {
+        "workload": f"{WORKLOAD} linear heads, dot-product loss (one launch, G exchange)"})
+    e2 = lambda i: vt.ttt_linear_fullbatch(*lv(gs[i % NSETS]), Z=gs[i % NSETS]["Z"][:, l0:l1], steps=2)
+    ms = med(e2)
+    out["linear_two_steps"] = _row(ms * 1e3, 4 * w.B * (l1 - l0) * w.N * w.d * 2, w.B * w.N, {
+        "workload": f"{WORKLOAD} linear heads, two full-batch steps (Gram pass, steps, apply: 3 launches)"})
     return out
 
 
@@ -254,7 +324,8 @@ def main():
     # one graph and replayed between HIP events on the replay stream; a step
     # is one launch, so this is also the layer kernel's average launch
     # duration
-    ms_step = time_graphed(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
+    step_times = time_graphed(torch, lambda i: step(sets[i % NSETS][1]), args.steps, replays=REPLAYS)
+    ms_step, p10_step, p90_step = spread(step_times)
     # the same steps as eager calls from Python (host-bound: reported only)
     eager_ms_step = time_calls(torch, lambda i: step(sets[i % NSETS][1]), args.steps)
     # the two kernels of the separate calls, the same way (average launch
@@ -309,6 +380,10 @@ def main():
             "algorithmic_bytes": lin_bytes + conv_bytes,
             "avg_launch_us": ms_step * 1e3,
         },
+        "timing": {
+            "replays": REPLAYS, "steps_per_replay": args.steps,
+            "median_us": ms_step * 1e3, "p10_us": p10_step * 1e3, "p90_us": p90_step * 1e3,
+        },
         "kernels": {
             "eager_python_us_per_step": eager_ms_step * 1e3,
             "separate_calls_us_per_step": sep_ms * 1e3,
@@ -347,14 +422,28 @@ def main():
             elapsed = time.perf_counter() - t0
             if elapsed >= 10.0:
                 break
+        cores = oracle.max_threads()  # (read before the one-thread run changes it)
+        # one thread, on image 0 of the same set (all three heads)
+        reps1, t1 = 0, time.perf_counter()
+        while True:
+            oracle.linear_fullbatch(K[:1, l0:l1], Q[:1, l0:l1], V[:1, l0:l1], W0[l0:l1], eta[l0:l1], threads=1)
+            oracle.dwconv3x3_fullbatch(K[:1, c0:c1], Q[:1, c0:c1], V[:1, c0:c1], w0[c0:c1], eta[c0:c1],
+                                       w.grid_h, w.grid_w, threads=1)
+            reps1 += 1
+            el1 = time.perf_counter() - t1
+            if el1 >= 5.0:
+                break
         out["cpu_baseline"] = {
             "value": tokens * reps / elapsed,
             "unit": "tokens/s",
-            "cores": oracle.max_threads(),
+            "cores": cores,
             "kind": "oracle",
             "sample": f"the whole workload (input set 0: {w.B} images x {w.H} heads x {w.N} "
                       f"tokens), {reps} repetitions in {elapsed:.2f} s; fp64 C loops, "
                       "OpenMP over (image, head) slices",
+            "one_thread": {"value": w.N * reps1 / el1, "unit": "tokens/s",
+                           "sample": f"image 0 of input set 0 (3 heads x {w.N} tokens), {reps1} "
+                                     f"repetitions in {el1:.2f} s on one thread"},
         }
 
         def rel(got, ref):  # per-slice inf-norm relative error, max over slices

@@ -93,7 +93,7 @@ def test_graph_replay_matches_eager():
     torch.cuda.synchronize()
 
     graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
+    with torch.cuda.graph(graph, stream=side):  # the warm-up stream: its workspaces exist
         run_all()
     torch.cuda.synchronize()
     for r in range(3):

@@ -175,6 +175,10 @@ def workspace(op: int, prob: Optional[Problem], device: torch.device, need: Opti
     key = (dev, _stream(torch.device("cuda", dev)), op)
     buf = _ws.get(key)
     if buf is None or buf.numel() < need:
+        if torch.cuda.is_current_stream_capturing():
+            # the zero-fill would be recorded into the graph
+            raise RuntimeError("no workspace for this stream yet: run the call once on the capture "
+                               "stream before capturing it (torch.cuda.graph(..., stream=s))")
         buf = torch.zeros(need, dtype=torch.uint8, device=device)
         _ws[key] = buf
     return buf.data_ptr(), buf.numel()

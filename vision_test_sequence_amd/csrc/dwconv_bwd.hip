@@ -17,15 +17,17 @@
 // Element-wise stencil work on the vector ALUs (no dense contraction): one
 // channel per lane, so every load or store of a wave is one contiguous
 // token row (128 bytes bf16, 256 bytes fp32).  A wave walks one grid row
-// over a segment of columns with sliding register windows (the next
-// column's loads issued one step ahead).  Four launches, all reductions in
-// a fixed order (bitwise reproducible):
+// over a segment of at most 16 columns with sliding register windows, the
+// loads of the next kPD columns in flight (a ring of registers, so the
+// walk waits on memory once, not per column).  Seven launches, all
+// reductions in a fixed order (bitwise reproducible):
 //   pass 1  per (slice, 4-row group, column segment): partial g (unless the
 //           forward's g is supplied) and dw1, summed over the 4 waves;
 //   reduce  per slice: g, dw1 over the partials in order; w1, dg, the deta
 //           term;
 //   pass 2  per (slice, 4-row group, segment): dQ, dV, dK and the partial
 //           sum_p dR[p] K[p+t];
+//   sum     per slice: the dw0 term dw1 + the pass-2 partials in order;
 //   batch   per head: dw0 and deta summed over the batch in b order.
 #include "common.hpp"
 #include "internal.hpp"
@@ -33,8 +35,9 @@
 namespace ttt {
 namespace {
 
-constexpr int kCbSeg = 64;     // columns per segment (at most)
+constexpr int kCbSeg = 16;     // columns per segment (at most)
 constexpr int kCbRows = 4;     // grid rows per workgroup: one per wave
+constexpr int kPD = 4;         // columns whose loads are in flight ahead of the walk
 
 struct CbArgs {
     View4 K, Q, V, dZ, dK, dQ, dV;
@@ -43,7 +46,9 @@ struct CbArgs {
     const float* gsv;   // nullable: the forward's g [slices][64][9]
     float* part1;       // [slices][P][64][18]: g (0..8), dw1 (9..17)
     float* part2;       // [slices][P][64][9]
-    float* sl;          // [slices][4][64][9]: w1, (2/N) dg, dw1, g
+    float* sl;          // [slices][5][64][9]: w1, (2/N) dg, dw1, g, dw0 term
+    float* sum1;        // [slices][64][18]: part1 summed over the partials
+    float* sum2;        // [slices][64][9]: part2 summed over the partials
     float* deta_s;      // [slices]
     float* dw0;         // [H][64][9]
     float* deta;        // [H]
@@ -65,13 +70,19 @@ template <> struct Elt<false> {
 };
 
 // Channel `lane` of one slice's token map; positions off the grid read 0.
+// Branch-free: the load goes to the clamped position and the value is
+// selected afterwards, so a load in flight is waited for only where its
+// value is used (a branch around the load would wait for every load at the
+// join).
 template <bool BF> struct Map {
     const char* base;
     long long sn; // bytes between tokens
     int gh, gw;
     __device__ float at(int y, int x) const {
-        if (y < 0 || y >= gh || x < 0 || x >= gw) return 0.f;
-        return Elt<BF>::ld(base + (long long)(y * gw + x) * sn);
+        const bool in = y >= 0 && y < gh && x >= 0 && x < gw;
+        const int yc = min(max(y, 0), gh - 1), xc = min(max(x, 0), gw - 1);
+        const float v = Elt<BF>::ld(base + (long long)(yc * gw + xc) * sn);
+        return in ? v : 0.f;
     }
 };
 template <bool BF>
@@ -152,44 +163,54 @@ __global__ __launch_bounds__(256) void cbwd_pass1(CbArgs a) {
                 qw[3 * i + j + 1] = Qm.at(y + i - 1, t.x0 + j - 1);
             }
         }
-        // the next column's values, loaded one step ahead
-        float kn[3], qn[3], vn = 0.f, dn;
-#pragma unroll
-        for (int i = 0; i < 3; ++i) {
-            if constexpr (!HAS_G) kn[i] = Km.at(y + i - 1, t.x0 + 1);
-            qn[i] = Qm.at(y + i - 1, t.x0 + 1);
-        }
-        if constexpr (!HAS_G) vn = Vm.at(y, t.x0);
-        dn = Dm.at(y, t.x0);
-        for (int x = t.x0; x < t.x1; ++x) {
+        // ring slot u holds the loads of step x0 + u (+ kPD after each use):
+        // K and Q column x+1, V and dZ at (y, x)
+        float kn[kPD][3], qn[kPD][3], vn[kPD], dn[kPD];
+        auto fetch = [&](int u, int x) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
-                if constexpr (!HAS_G) {
-                    kw[3 * i] = kw[3 * i + 1];
-                    kw[3 * i + 1] = kw[3 * i + 2];
-                    kw[3 * i + 2] = kn[i];
+                if constexpr (!HAS_G) kn[u][i] = Km.at(y + i - 1, x + 1);
+                qn[u][i] = Qm.at(y + i - 1, x + 1);
+            }
+            if constexpr (!HAS_G) vn[u] = Vm.at(y, x);
+            dn[u] = Dm.at(y, x);
+        };
+#pragma unroll
+        for (int u = 0; u < kPD; ++u) fetch(u, t.x0 + u);
+        // a whole segment (at most kCbSeg columns) unrolled: the loads of
+        // later columns are not held back at a loop edge
+#pragma unroll
+        for (int xb = 0; xb < kCbSeg; xb += kPD) {
+#pragma unroll
+            for (int u = 0; u < kPD; ++u) {
+                const int x = t.x0 + xb + u;
+#pragma unroll
+                for (int i = 0; i < 3; ++i) {
+                    if constexpr (!HAS_G) {
+                        kw[3 * i] = kw[3 * i + 1];
+                        kw[3 * i + 1] = kw[3 * i + 2];
+                        kw[3 * i + 2] = kn[u][i];
+                    }
+                    qw[3 * i] = qw[3 * i + 1];
+                    qw[3 * i + 1] = qw[3 * i + 2];
+                    qw[3 * i + 2] = qn[u][i];
                 }
-                qw[3 * i] = qw[3 * i + 1];
-                qw[3 * i + 1] = qw[3 * i + 2];
-                qw[3 * i + 2] = qn[i];
+                float vc = 0.f;
+                if constexpr (!HAS_G) vc = vn[u];
+                const float dz = dn[u];
+                fetch(u, x + kPD);
+                if (x < t.x1) {
+                    if constexpr (!HAS_G) {
+                        float r = -vc;
+#pragma unroll
+                        for (int k = 0; k < 9; ++k) r = fmaf(wt[k], kw[k], r);
+#pragma unroll
+                        for (int k = 0; k < 9; ++k) acc[k] = fmaf(r, kw[k], acc[k]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 9; ++k) acc[9 + k] = fmaf(dz, qw[k], acc[9 + k]);
+                }
             }
-            const float vc = vn, dz = dn;
-#pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                if constexpr (!HAS_G) kn[i] = Km.at(y + i - 1, x + 2);
-                qn[i] = Qm.at(y + i - 1, x + 2);
-            }
-            if constexpr (!HAS_G) vn = Vm.at(y, x + 1);
-            dn = Dm.at(y, x + 1);
-            if constexpr (!HAS_G) {
-                float r = -vc;
-#pragma unroll
-                for (int k = 0; k < 9; ++k) r = fmaf(wt[k], kw[k], r);
-#pragma unroll
-                for (int k = 0; k < 9; ++k) acc[k] = fmaf(r, kw[k], acc[k]);
-            }
-#pragma unroll
-            for (int k = 0; k < 9; ++k) acc[9 + k] = fmaf(dz, qw[k], acc[9 + k]);
         }
     }
     float* dst = a.part1 + ((long long)t.slice * a.ngrp * a.nseg + t.pidx) * 64 * 18;
@@ -204,16 +225,13 @@ __global__ __launch_bounds__(256) void cbwd_reduce(CbArgs a) {
     const int P = a.ngrp * a.nseg;
     const float eta = a.eta[h];
     const float scale = (a.dot ? 1.0f : 2.0f) / (float)(a.gh * a.gw);
-    const float* src = a.part1 + (long long)slice * P * 64 * 18;
-    float* sl = a.sl + (long long)slice * 4 * 576;
+    const float* src = a.sum1 + (long long)slice * 64 * 18;
+    float* sl = a.sl + (long long)slice * 5 * 576;
     float dsum = 0.f;
+    (void)P;
     for (int e = tid; e < 576; e += 256) {
         const int c = e / 9, k = e % 9;
-        float gs = 0.f, ds = 0.f;
-        for (int p = 0; p < P; ++p) {
-            gs += src[((long long)p * 64 + c) * 18 + k];
-            ds += src[((long long)p * 64 + c) * 18 + 9 + k];
-        }
+        const float gs = src[c * 18 + k], ds = src[c * 18 + 9 + k];
         const float g = a.gsv ? a.gsv[(long long)slice * 576 + e] : scale * gs;
         const float w1 = a.w0[(long long)h * 576 + e] - eta * g;
         sl[e] = w1;
@@ -249,7 +267,7 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
         char* dVp = out_of<BF>(a.dV, t.b, t.h, lane);
         constexpr int es = Elt<BF>::esz;
         const long long sK = a.dK.sn * es, sQ = a.dQ.sn * es, sV = a.dV.sn * es;
-        const float* sl = a.sl + (long long)t.slice * 4 * 576 + lane * 9;
+        const float* sl = a.sl + (long long)t.slice * 5 * 576 + lane * 9;
         float wt[9], w1[9], dgs[9];
         // Under the dot-product loss g = -(1/N) sum_p V[p] K[p+t] has no
         // P = conv(K, w0) term: R = -V, dK gets no w0 dR term and dw0 no
@@ -266,9 +284,10 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
         // (cols 0..3); R, dR windows: rows y-1..y+1 over columns x-1..x+1;
         // dZ window: rows y-1..y+1 over columns x-1..x+1.
         float kw[4][5], rw[3][3], drw[3][3], dzw[3][3];
-        // R and dR of grid position (yy, xx) from the K window column c0
-        // (columns c0-1..c0+1 around it) and V; zero off the grid.
-        auto rcol = [&](int xx, int cc, float* rr, float* dr) __attribute__((always_inline)) {
+        // R and dR of grid position (yy = y-1..y+1, xx) from the K window
+        // column cc (columns cc-1..cc+1 around it) and V at (yy, xx); zero
+        // off the grid.
+        auto rcol = [&](int xx, int cc, const float* vv, float* rr, float* dr) __attribute__((always_inline)) {
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 const int yy = y + i - 1;
@@ -282,7 +301,7 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
                         q = fmaf(dgs[3 * ii + jj], kv, q);
                     }
                 const bool in = yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw;
-                rr[i] = in ? p - Vm.at(yy, xx) : 0.f;
+                rr[i] = in ? p - vv[i] : 0.f;
                 dr[i] = in ? q : 0.f;
             }
         };
@@ -294,11 +313,15 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
             for (int r = 0; r < 5; ++r) kw[c][r] = Km.at(y + r - 2, t.x0 - 2 + c);
         // R, dR at columns x0-1 and x0 (window columns 1 and 2)
         {
-            float rr[3], dr[3];
-            rcol(t.x0 - 1, 1, rr, dr);
+            float rr[3], dr[3], vv[3];
+#pragma unroll
+            for (int i = 0; i < 3; ++i) vv[i] = Vm.at(y + i - 1, t.x0 - 1);
+            rcol(t.x0 - 1, 1, vv, rr, dr);
 #pragma unroll
             for (int i = 0; i < 3; ++i) { rw[1][i] = rr[i]; drw[1][i] = dr[i]; }
-            rcol(t.x0, 2, rr, dr);
+#pragma unroll
+            for (int i = 0; i < 3; ++i) vv[i] = Vm.at(y + i - 1, t.x0);
+            rcol(t.x0, 2, vv, rr, dr);
 #pragma unroll
             for (int i = 0; i < 3; ++i) { rw[2][i] = rr[i]; drw[2][i] = dr[i]; }
         }
@@ -307,80 +330,119 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
             dzw[1][i] = Dm.at(y + i - 1, t.x0 - 1);
             dzw[2][i] = Dm.at(y + i - 1, t.x0);
         }
-        float kn[5], dn[3];
+        // ring slot u holds the loads of step x0 + u (+ kPD after each use):
+        // K column x+2 (5 rows), dZ and V column x+1 (3 rows each)
+        float kn[kPD][5], dn[kPD][3], vn[kPD][3];
+        auto fetch = [&](int u, int x) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 5; ++r) kn[r] = Km.at(y + r - 2, t.x0 + 2);
-#pragma unroll
-        for (int i = 0; i < 3; ++i) dn[i] = Dm.at(y + i - 1, t.x0 + 1);
-        for (int x = t.x0; x < t.x1; ++x) {
-            // shift: K columns x-1..x+2, dZ columns x-1..x+1
-#pragma unroll
-            for (int r = 0; r < 5; ++r) {
-                kw[0][r] = kw[1][r];
-                kw[1][r] = kw[2][r];
-                kw[2][r] = kw[3][r];
-                kw[3][r] = kn[r];
-            }
+            for (int r = 0; r < 5; ++r) kn[u][r] = Km.at(y + r - 2, x + 2);
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
-                rw[0][i] = rw[1][i];
-                rw[1][i] = rw[2][i];
-                drw[0][i] = drw[1][i];
-                drw[1][i] = drw[2][i];
-                dzw[0][i] = dzw[1][i];
-                dzw[1][i] = dzw[2][i];
-                dzw[2][i] = dn[i];
+                dn[u][i] = Dm.at(y + i - 1, x + 1);
+                vn[u][i] = Vm.at(y + i - 1, x + 1);
             }
-            // next step's columns, loaded ahead
+        };
 #pragma unroll
-            for (int r = 0; r < 5; ++r) kn[r] = Km.at(y + r - 2, x + 3);
+        for (int u = 0; u < kPD; ++u) fetch(u, t.x0 + u);
+        // a whole segment (at most kCbSeg columns) unrolled: the loads of
+        // later columns are not held back at a loop edge
 #pragma unroll
-            for (int i = 0; i < 3; ++i) dn[i] = Dm.at(y + i - 1, x + 2);
-            // R, dR at column x+1 (K window column 2 = x+1)
-            {
-                float rr[3], dr[3];
-                rcol(x + 1, 2, rr, dr);
+        for (int xb = 0; xb < kCbSeg; xb += kPD) {
 #pragma unroll
-                for (int i = 0; i < 3; ++i) { rw[2][i] = rr[i]; drw[2][i] = dr[i]; }
-            }
-            // outputs at (y, x): window index [col][row], q - t with t = (i-1, j-1)
-            float dq = 0.f, dk = 0.f;
+            for (int u = 0; u < kPD; ++u) {
+                const int x = t.x0 + xb + u;
+                // shift: K columns x-1..x+2, dZ columns x-1..x+1
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
-#pragma unroll
-                for (int j = 0; j < 3; ++j) {
-                    const int tt = 3 * i + j;
-                    dq = fmaf(w1[tt], dzw[2 - j][2 - i], dq);
-                    dk = fmaf(dgs[tt], rw[2 - j][2 - i], dk);
-                    dk = fmaf(wt[tt], drw[2 - j][2 - i], dk);
+                for (int r = 0; r < 5; ++r) {
+                    kw[0][r] = kw[1][r];
+                    kw[1][r] = kw[2][r];
+                    kw[2][r] = kw[3][r];
+                    kw[3][r] = kn[u][r];
                 }
-            const float drc = drw[1][1];
 #pragma unroll
-            for (int i = 0; i < 3; ++i)
+                for (int i = 0; i < 3; ++i) {
+                    rw[0][i] = rw[1][i];
+                    rw[1][i] = rw[2][i];
+                    drw[0][i] = drw[1][i];
+                    drw[1][i] = drw[2][i];
+                    dzw[0][i] = dzw[1][i];
+                    dzw[1][i] = dzw[2][i];
+                    dzw[2][i] = dn[u][i];
+                }
+                // R, dR at column x+1 (K window column 2 = x+1)
+                {
+                    float rr[3], dr[3];
+                    rcol(x + 1, 2, vn[u], rr, dr);
 #pragma unroll
-                for (int j = 0; j < 3; ++j) acc[3 * i + j] = fmaf(wd * drc, kw[j][i + 1], acc[3 * i + j]);
-            const long long n = (long long)y * a.gw + x;
-            Elt<BF>::st(dQp + n * sQ, dq);
-            Elt<BF>::st(dKp + n * sK, dk);
-            Elt<BF>::st(dVp + n * sV, -drc);
+                    for (int i = 0; i < 3; ++i) { rw[2][i] = rr[i]; drw[2][i] = dr[i]; }
+                }
+                fetch(u, x + kPD);
+                if (x < t.x1) {
+                    // outputs at (y, x): window index [col][row], q - t with t = (i-1, j-1)
+                    float dq = 0.f, dk = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) {
+                            const int tt = 3 * i + j;
+                            dq = fmaf(w1[tt], dzw[2 - j][2 - i], dq);
+                            dk = fmaf(dgs[tt], rw[2 - j][2 - i], dk);
+                            dk = fmaf(wt[tt], drw[2 - j][2 - i], dk);
+                        }
+                    const float drc = drw[1][1];
+#pragma unroll
+                    for (int i = 0; i < 3; ++i)
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) acc[3 * i + j] = fmaf(wd * drc, kw[j][i + 1], acc[3 * i + j]);
+                    const long long n = (long long)y * a.gw + x;
+                    Elt<BF>::st(dQp + n * sQ, dq);
+                    Elt<BF>::st(dKp + n * sK, dk);
+                    Elt<BF>::st(dVp + n * sV, -drc);
+                }
+            }
         }
     }
     float* dst = a.part2 + ((long long)t.slice * a.ngrp * a.nseg + t.pidx) * 576;
     wave_sum_store<9>(acc, red, dst);
 }
 
+// ---- per-slice dw0 term: dw1 + the pass-2 partials in order -------------
+__global__ __launch_bounds__(256) void cbwd_slice_sum(CbArgs a) {
+    const int slice = blockIdx.x, tid = threadIdx.x;
+    float* sl = a.sl + (long long)slice * 5 * 576;
+    const float* s2 = a.sum2 + (long long)slice * 576;
+    for (int e = tid; e < 576; e += 256) sl[2304 + e] = sl[1152 + e] + s2[e];
+}
+
+// ---- sum of per-workgroup partials, [slices][P][E] -> [slices][E] --------
+// Block (slice, 64-element chunk); its four waves each add a quarter of the
+// partials in order, then the four quarter sums are added in order: the
+// same order on every run.
+__global__ __launch_bounds__(256) void cbwd_sum_partials(const float* part, float* out, int P, int E) {
+    __shared__ float qs[4][64];
+    const int nchunk = (E + 63) / 64;
+    const int slice = blockIdx.x / nchunk, e = (blockIdx.x % nchunk) * 64 + (threadIdx.x & 63);
+    const int q = threadIdx.x >> 6, per = (P + 3) / 4, p0 = q * per, p1 = min(P, p0 + per);
+    float s = 0.f;
+    if (e < E) {
+        const float* src = part + (long long)slice * P * E + e;
+#pragma unroll 8
+        for (int p = p0; p < p1; ++p) s += src[(long long)p * E];
+    }
+    qs[q][threadIdx.x & 63] = s;
+    __syncthreads();
+    if (q == 0 && e < E) {
+        const int l = threadIdx.x;
+        out[(long long)slice * E + e] = ((qs[0][l] + qs[1][l]) + qs[2][l]) + qs[3][l];
+    }
+}
+
 // ---- per-head batch sums -------------------------------------------------
 __global__ __launch_bounds__(256) void cbwd_batch(CbArgs a) {
     const int h = blockIdx.x, tid = threadIdx.x;
-    const int P = a.ngrp * a.nseg;
     for (int e = tid; e < 576; e += 256) {
         float s = 0.f;
-        for (int b = 0; b < a.B; ++b) {
-            const long long slice = (long long)b * a.H + h;
-            s += a.sl[slice * 4 * 576 + 1152 + e];
-            const float* p2 = a.part2 + slice * P * 576 + e;
-            for (int p = 0; p < P; ++p) s += p2[(long long)p * 576];
-        }
+        for (int b = 0; b < a.B; ++b) s += a.sl[((long long)b * a.H + h) * 5 * 576 + 2304 + e];
         a.dw0[(long long)h * 576 + e] = s;
     }
     if (tid == 0) {
@@ -394,7 +456,7 @@ struct CbPlan {
     int nseg, seglen, ngrp;
 };
 CbPlan cb_plan(int gh, int gw) {
-    CbPlan p;
+    CbPlan p; // segments of at most kCbSeg columns: the walks are unrolled for that many
     p.nseg = (gw + kCbSeg - 1) / kCbSeg;
     p.seglen = (gw + p.nseg - 1) / p.nseg;
     p.ngrp = (gh + kCbRows - 1) / kCbRows;
@@ -409,8 +471,8 @@ size_t conv_bwd_ws_bytes(int B, int H, int gh, int gw) {
     if (slices == 0 || gh <= 0 || gw <= 0) return 0;
     const CbPlan p = cb_plan(gh, gw);
     const size_t P = (size_t)p.ngrp * p.nseg;
-    return a256(slices * P * 64 * 18 * 4) + a256(slices * P * 576 * 4) + a256(slices * 4 * 576 * 4) +
-           a256(slices * 4);
+    return a256(slices * P * 64 * 18 * 4) + a256(slices * P * 576 * 4) + a256(slices * 5 * 576 * 4) +
+           a256(slices * 4) + a256(slices * 1152 * 4) + a256(slices * 576 * 4);
 }
 
 hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
@@ -431,8 +493,12 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
     a.part2 = (float*)w;
     w += a256(slices * P * 576 * 4);
     a.sl = (float*)w;
-    w += a256(slices * 4 * 576 * 4);
+    w += a256(slices * 5 * 576 * 4);
     a.deta_s = (float*)w;
+    w += a256(slices * 4);
+    a.sum1 = (float*)w;
+    w += a256(slices * 1152 * 4);
+    a.sum2 = (float*)w;
     const dim3 grid((unsigned)(slices * P)), block(256);
     if (s.bf16) {
         if (s.saved) hipLaunchKernelGGL((cbwd_pass1<true, true>), grid, block, 0, stream, a);
@@ -441,9 +507,14 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
         if (s.saved) hipLaunchKernelGGL((cbwd_pass1<false, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((cbwd_pass1<false, false>), grid, block, 0, stream, a);
     }
+    hipLaunchKernelGGL(cbwd_sum_partials, dim3((unsigned)(slices * 18)), block, 0, stream, (const float*)a.part1,
+                       a.sum1, (int)P, 1152);
     hipLaunchKernelGGL(cbwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
     if (s.bf16) hipLaunchKernelGGL((cbwd_pass2<true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((cbwd_pass2<false>), grid, block, 0, stream, a);
+    hipLaunchKernelGGL(cbwd_sum_partials, dim3((unsigned)(slices * 9)), block, 0, stream, (const float*)a.part2,
+                       a.sum2, (int)P, 576);
+    hipLaunchKernelGGL(cbwd_slice_sum, dim3((unsigned)slices), block, 0, stream, a);
     hipLaunchKernelGGL(cbwd_batch, dim3((unsigned)s.H), block, 0, stream, a);
     return hipGetLastError();
 }
