@@ -71,6 +71,11 @@ def _load():
                   lib.oracle_dwconv3x3_fullbatch_ex, lib.oracle_dwconv3x3_fullbatch_bwd_ex,
                   lib.oracle_linear_minibatch_2w0, lib.oracle_linear_gradient_magnitude):
             f.restype = ctypes.c_int
+        lib.oracle_linear_minibatch_bwd.argtypes = [i, i, i, i, i, i, dp, dp, dp, dp, dp, dp,
+                                                    dp, dp, dp, dp, dp, i]
+        lib.oracle_mlp_fullbatch.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, dp, dp, i]
+        lib.oracle_linear_minibatch_bwd.restype = ctypes.c_int
+        lib.oracle_mlp_fullbatch.restype = ctypes.c_int
         lib.oracle_num_chunks.argtypes = [i, i]
         lib.oracle_max_threads.argtypes = []
         for f in (lib.oracle_linear_fullbatch, lib.oracle_dwconv3x3_fullbatch,
@@ -274,3 +279,35 @@ def linear_gradient_magnitude(K, V, W0, loss: int = L2, threads: int = 0):
     _check(_load().oracle_linear_gradient_magnitude(B, H, N, d, int(loss), _p(K), _p(V), _p(W0), _p(out),
                                                     int(threads)), "linear_gradient_magnitude")
     return out
+
+
+def linear_minibatch_bwd(K, Q, V, W0, eta, dZ, minibatch: int, mode: int = FORWARD_BACKWARD_AVG,
+                         threads: int = 0):
+    """Gradients of sum(dZ * Z) through linear_minibatch.
+
+    Returns (dK, dQ, dV, dW0, deta); dW0 [H,d,d] and deta [H] are summed over
+    the batch and the scan directions."""
+    K, Q, V, W0, eta, dZ = map(_f64, (K, Q, V, W0, eta, dZ))
+    B, H, N, d = K.shape
+    out = [np.empty_like(K) for _ in range(3)] + [np.empty((H, d, d)), np.empty((H,))]
+    _check(_load().oracle_linear_minibatch_bwd(B, H, N, d, int(minibatch), int(mode), _p(K), _p(Q), _p(V),
+                                               _p(W0), _p(eta), _p(dZ), *(_p(o) for o in out), int(threads)),
+           "linear_minibatch_bwd")
+    return tuple(out)
+
+
+def mlp_fullbatch(K, Q, V, W1, W2, eta, threads: int = 0):
+    """One full-batch L2 step of the two-layer SiLU MLP inner model
+    f(k) = W2 silu(W1 k), then z = f'(q).  W1 [H,rd,d], W2 [H,d,rd].
+    Returns (Z, dW1, dW2) with the gradients per slice [B,H,...]."""
+    K, Q, V, W1, W2, eta = map(_f64, (K, Q, V, W1, W2, eta))
+    B, H, N, d = K.shape
+    hid = W1.shape[1]
+    if W1.shape != (H, hid, d) or W2.shape != (H, d, hid):
+        raise ValueError("W1 must be [H,rd,d] and W2 [H,d,rd]")
+    Z = np.empty_like(K)
+    G1 = np.empty((B, H, hid, d))
+    G2 = np.empty((B, H, d, hid))
+    _check(_load().oracle_mlp_fullbatch(B, H, N, d, hid, _p(K), _p(Q), _p(V), _p(W1), _p(W2), _p(eta), _p(Z),
+                                        _p(G1), _p(G2), int(threads)), "mlp_fullbatch")
+    return Z, G1, G2

@@ -867,3 +867,274 @@ int oracle_linear_gradient_magnitude(int B, int H, int N, int d, int loss,
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------
+ * Gradient of L = sum <dZ, Z> through the mini-batch scans (end-to-end
+ * training of Vision-TTT goes through the inner updates; the notes' key
+ * design 4 recomputes the states in the backward).  One chain (one
+ * direction), reverse mode through the token-by-token procedure of
+ * scan_one, with the chunk-start states recomputed by a forward pass.
+ * Inside a chunk of n_c tokens with start state Ws, a = 2/n_c:
+ *   r_t = Ws k_t - v_t ; acc_t = sum_{s<=t} a r_s k_s^T ;
+ *   W_t = Ws - eta acc_t ; z_t = W_t q_t ;  next Ws = Ws - eta acc_last.
+ * Reverse, with dWn the gradient reaching the next chunk's start state:
+ *   dW_t = dz_t q_t^T ; dq_t = W_t^T dz_t ; deta -= <dW_t, acc_t> ;
+ *   E_s = dWn + sum_{t>=s} dW_t ;  dG_s = -eta E_s ; deta -= <dWn, acc_last>
+ *   dr_s = a dG_s k_s ; dk_s = a dG_s^T r_s + Ws^T dr_s ; dv_s = -dr_s ;
+ *   dWs = dWn + sum_t dW_t + sum_s dr_s k_s^T.
+ * dzs: this chain's output gradient (position order); dK, dQ, dV are
+ * accumulated (+=); *dW0_out and *deta_out receive the chain's terms.
+ * ---------------------------------------------------------------------- */
+static void scan_one_bwd(int N, int d, int bsz, int reverse, const double* K, const double* Q,
+                         const double* V, const double* W0, double eta, const double* dzs,
+                         double* dK, double* dQ, double* dV, double* dW0_out, double* deta_out) {
+    size_t dd = (size_t)d * d;
+    int nch = (N + bsz - 1) / bsz;
+    double* Wst = (double*)malloc((size_t)nch * dd * sizeof(double)); /* chunk-start states */
+    double* acc = (double*)malloc(dd * sizeof(double));
+    double* r = (double*)malloc((size_t)bsz * d * sizeof(double));
+    double* accs = (double*)malloc((size_t)bsz * dd * sizeof(double)); /* acc_t of the chunk */
+    double* dWn = (double*)calloc(dd, sizeof(double));
+    double* dWs = (double*)malloc(dd * sizeof(double));
+    double* E = (double*)malloc(dd * sizeof(double));
+    double* Wt = (double*)malloc(dd * sizeof(double));
+    double* dr = (double*)malloc((size_t)d * sizeof(double));
+    double de = 0.0;
+    /* forward: chunk-start states */
+    memcpy(Wst, W0, dd * sizeof(double));
+    for (int c = 0; c < nch; ++c) {
+        int c0 = c * bsz, nc = (N - c0 < bsz) ? (N - c0) : bsz;
+        const double* Ws = Wst + (size_t)c * dd;
+        memset(acc, 0, dd * sizeof(double));
+        for (int t = 0; t < nc; ++t) {
+            int pos = reverse ? (N - 1 - (c0 + t)) : (c0 + t);
+            const double* k = K + (size_t)pos * d;
+            const double* v = V + (size_t)pos * d;
+            for (int o = 0; o < d; ++o) {
+                double x = 0.0;
+                for (int cc = 0; cc < d; ++cc) x += Ws[(size_t)o * d + cc] * k[cc];
+                double rr = x - v[o];
+                for (int cc = 0; cc < d; ++cc) acc[(size_t)o * d + cc] += (2.0 / (double)nc) * rr * k[cc];
+            }
+        }
+        if (c + 1 < nch)
+            for (size_t e = 0; e < dd; ++e) Wst[(size_t)(c + 1) * dd + e] = Ws[e] - eta * acc[e];
+    }
+    /* reverse over the chunks */
+    for (int c = nch - 1; c >= 0; --c) {
+        int c0 = c * bsz, nc = (N - c0 < bsz) ? (N - c0) : bsz;
+        double a = 2.0 / (double)nc;
+        const double* Ws = Wst + (size_t)c * dd;
+        /* recompute r_t and acc_t of the chunk */
+        memset(acc, 0, dd * sizeof(double));
+        for (int t = 0; t < nc; ++t) {
+            int pos = reverse ? (N - 1 - (c0 + t)) : (c0 + t);
+            const double* k = K + (size_t)pos * d;
+            const double* v = V + (size_t)pos * d;
+            for (int o = 0; o < d; ++o) {
+                double x = 0.0;
+                for (int cc = 0; cc < d; ++cc) x += Ws[(size_t)o * d + cc] * k[cc];
+                r[(size_t)t * d + o] = x - v[o];
+                for (int cc = 0; cc < d; ++cc) acc[(size_t)o * d + cc] += a * r[(size_t)t * d + o] * k[cc];
+            }
+            memcpy(accs + (size_t)t * dd, acc, dd * sizeof(double));
+        }
+        /* the chunk-end update: W_next = Ws - eta acc_last */
+        for (size_t e = 0; e < dd; ++e) de -= dWn[e] * acc[e];
+        memcpy(dWs, dWn, dd * sizeof(double));
+        memcpy(E, dWn, dd * sizeof(double));
+        /* tokens in reverse: E becomes dWn + sum_{t' >= t} dW_t' */
+        for (int t = nc - 1; t >= 0; --t) {
+            int pos = reverse ? (N - 1 - (c0 + t)) : (c0 + t);
+            const double* k = K + (size_t)pos * d;
+            const double* q = Q + (size_t)pos * d;
+            const double* dz = dzs + (size_t)pos * d;
+            const double* at = accs + (size_t)t * dd;
+            /* z_t = W_t q_t, W_t = Ws - eta acc_t */
+            for (size_t e = 0; e < dd; ++e) Wt[e] = Ws[e] - eta * at[e];
+            for (int cc = 0; cc < d; ++cc) {
+                double x = 0.0;
+                for (int o = 0; o < d; ++o) x += Wt[(size_t)o * d + cc] * dz[o];
+                dQ[(size_t)pos * d + cc] += x;
+            }
+            for (int o = 0; o < d; ++o)
+                for (int cc = 0; cc < d; ++cc) {
+                    double dw = dz[o] * q[cc];
+                    de -= dw * at[(size_t)o * d + cc];
+                    dWs[(size_t)o * d + cc] += dw;
+                    E[(size_t)o * d + cc] += dw;
+                }
+            /* G_t = a r_t k_t^T with dG_t = -eta E */
+            const double* rt = r + (size_t)t * d;
+            for (int o = 0; o < d; ++o) {
+                double x = 0.0;
+                for (int cc = 0; cc < d; ++cc) x += E[(size_t)o * d + cc] * k[cc];
+                dr[o] = a * (-eta) * x;
+            }
+            for (int cc = 0; cc < d; ++cc) {
+                double x = 0.0, y = 0.0;
+                for (int o = 0; o < d; ++o) {
+                    x += E[(size_t)o * d + cc] * rt[o];
+                    y += Ws[(size_t)o * d + cc] * dr[o];
+                }
+                dK[(size_t)pos * d + cc] += a * (-eta) * x + y;
+            }
+            for (int o = 0; o < d; ++o) {
+                dV[(size_t)pos * d + o] -= dr[o];
+                for (int cc = 0; cc < d; ++cc) dWs[(size_t)o * d + cc] += dr[o] * k[cc];
+            }
+        }
+        memcpy(dWn, dWs, dd * sizeof(double));
+    }
+    memcpy(dW0_out, dWn, dd * sizeof(double));
+    *deta_out = de;
+    free(Wst);
+    free(acc);
+    free(r);
+    free(accs);
+    free(dWn);
+    free(dWs);
+    free(E);
+    free(Wt);
+    free(dr);
+}
+
+/* Gradient of L = sum <dZ, Z> through oracle_linear_minibatch (mode 0: Z is
+ * the average of the two scans, so each chain sees dZ / 2).  dK, dQ, dV
+ * [B][H][N][d] are overwritten; dW0 [H][d][d] and deta [H] are sums over
+ * the batch and both directions (b ascending, forward before reverse). */
+int oracle_linear_minibatch_bwd(int B, int H, int N, int d, int bsz, int mode,
+                                const double* K, const double* Q, const double* V,
+                                const double* W0, const double* eta, const double* dZ,
+                                double* dK, double* dQ, double* dV, double* dW0, double* deta,
+                                int nthreads) {
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || bsz <= 0 || mode < 0 || mode > 2) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+    int ndir = (mode == 0) ? 2 : 1;
+    size_t slice_elems = (size_t)N * d, dd = (size_t)d * d;
+    double* pW0 = (double*)calloc((size_t)(nslice > 0 ? nslice : 1) * ndir * dd, sizeof(double));
+    double* peta = (double*)calloc((size_t)(nslice > 0 ? nslice : 1) * ndir, sizeof(double));
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        int h = (int)(s % H);
+        size_t off = (size_t)s * slice_elems;
+        double* dzs = (double*)malloc(slice_elems * sizeof(double));
+        for (size_t e = 0; e < slice_elems; ++e) {
+            dzs[e] = (mode == 0 ? 0.5 : 1.0) * dZ[off + e];
+            dK[off + e] = dQ[off + e] = dV[off + e] = 0.0;
+        }
+        for (int dir = 0; dir < ndir; ++dir) {
+            int reverse = (mode == 2) ? 1 : (mode == 1 ? 0 : dir);
+            scan_one_bwd(N, d, bsz, reverse, K + off, Q + off, V + off, W0 + (size_t)h * dd, eta[h], dzs,
+                         dK + off, dQ + off, dV + off, pW0 + ((size_t)s * ndir + dir) * dd,
+                         peta + (size_t)s * ndir + dir);
+        }
+        free(dzs);
+    }
+    for (int h = 0; h < H; ++h) {
+        double* o = dW0 + (size_t)h * dd;
+        memset(o, 0, dd * sizeof(double));
+        deta[h] = 0.0;
+        for (int b = 0; b < B; ++b)
+            for (int dir = 0; dir < ndir; ++dir) {
+                long s = (long)b * H + h;
+                for (size_t t = 0; t < dd; ++t) o[t] += pW0[((size_t)s * ndir + dir) * dd + t];
+                deta[h] += peta[(size_t)s * ndir + dir];
+            }
+    }
+    free(pW0);
+    free(peta);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------
+ * Two-layer SiLU MLP inner model (the ViT3 article, observation 4: width
+ * ratio r = hidden / input from 1 to 4): f(k) = W2 silu(W1 k), W1 [rd][d],
+ * W2 [d][rd], silu(x) = x / (1 + e^-x).  One full-batch step of the L2
+ * loss L = (1/N) sum_i ||f(k_i) - v_i||^2 by backpropagation per token:
+ *   h = W1 k ; a = silu(h) ; e = W2 a - v
+ *   dW2 = (2/N) sum e a^T ;  g = (W2^T e) * silu'(h) ;  dW1 = (2/N) sum g k^T
+ *   W1' = W1 - eta dW1 ;  W2' = W2 - eta dW2 ;  z = W2' silu(W1' q).
+ * W1: [H][rd][d], W2: [H][d][rd].  G1_out / G2_out (nullable): dW1, dW2
+ * per slice.
+ * ---------------------------------------------------------------------- */
+static double silu(double x) { return x / (1.0 + exp(-x)); }
+static double silu_grad(double x) {
+    double sg = 1.0 / (1.0 + exp(-x));
+    return sg * (1.0 + x * (1.0 - sg));
+}
+
+int oracle_mlp_fullbatch(int B, int H, int N, int d, int hid,
+                         const double* K, const double* Q, const double* V,
+                         const double* W1, const double* W2, const double* eta,
+                         double* Z, double* G1_out, double* G2_out, int nthreads) {
+    if (B < 0 || H < 0 || N <= 0 || d <= 0 || hid <= 0) return -1;
+    set_threads(nthreads);
+    long nslice = (long)B * H;
+    size_t n1 = (size_t)hid * d;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (long s = 0; s < nslice; ++s) {
+        int b = (int)(s / H), h = (int)(s % H);
+        const double* w1 = W1 + (size_t)h * n1;
+        const double* w2 = W2 + (size_t)h * n1;
+        double* g1 = (double*)calloc(n1, sizeof(double));
+        double* g2 = (double*)calloc(n1, sizeof(double));
+        double* hv = (double*)malloc((size_t)hid * sizeof(double));
+        double* av = (double*)malloc((size_t)hid * sizeof(double));
+        double* ev = (double*)malloc((size_t)d * sizeof(double));
+        double* w1n = (double*)malloc(n1 * sizeof(double));
+        double* w2n = (double*)malloc(n1 * sizeof(double));
+        for (int i = 0; i < N; ++i) {
+            const double* k = K + IDX4(b, h, i, 0);
+            const double* v = V + IDX4(b, h, i, 0);
+            for (int j = 0; j < hid; ++j) {
+                double x = 0.0;
+                for (int c = 0; c < d; ++c) x += w1[(size_t)j * d + c] * k[c];
+                hv[j] = x;
+                av[j] = silu(x);
+            }
+            for (int o = 0; o < d; ++o) {
+                double x = 0.0;
+                for (int j = 0; j < hid; ++j) x += w2[(size_t)o * hid + j] * av[j];
+                ev[o] = x - v[o];
+            }
+            for (int o = 0; o < d; ++o)
+                for (int j = 0; j < hid; ++j) g2[(size_t)o * hid + j] += (2.0 / (double)N) * ev[o] * av[j];
+            for (int j = 0; j < hid; ++j) {
+                double x = 0.0;
+                for (int o = 0; o < d; ++o) x += w2[(size_t)o * hid + j] * ev[o];
+                double gj = x * silu_grad(hv[j]);
+                for (int c = 0; c < d; ++c) g1[(size_t)j * d + c] += (2.0 / (double)N) * gj * k[c];
+            }
+        }
+        for (size_t e = 0; e < n1; ++e) {
+            w1n[e] = w1[e] - eta[h] * g1[e];
+            w2n[e] = w2[e] - eta[h] * g2[e];
+        }
+        for (int i = 0; i < N; ++i) {
+            const double* q = Q + IDX4(b, h, i, 0);
+            double* z = Z + IDX4(b, h, i, 0);
+            for (int j = 0; j < hid; ++j) {
+                double x = 0.0;
+                for (int c = 0; c < d; ++c) x += w1n[(size_t)j * d + c] * q[c];
+                av[j] = silu(x);
+            }
+            for (int o = 0; o < d; ++o) {
+                double x = 0.0;
+                for (int j = 0; j < hid; ++j) x += w2n[(size_t)o * hid + j] * av[j];
+                z[o] = x;
+            }
+        }
+        if (G1_out) memcpy(G1_out + (size_t)s * n1, g1, n1 * sizeof(double));
+        if (G2_out) memcpy(G2_out + (size_t)s * n1, g2, n1 * sizeof(double));
+        free(g1);
+        free(g2);
+        free(hv);
+        free(av);
+        free(ev);
+        free(w1n);
+        free(w2n);
+    }
+    return 0;
+}
