@@ -100,7 +100,8 @@ typedef enum {
     TTT_OP_LAYER_FULLBATCH = 4, /* workspace of ttt_layer_fullbatch (sized by
                                    ttt_layer_workspace_size; ttt_workspace_size
                                    returns 0 for it) */
-    TTT_OP_DWCONV3X3_FULLBATCH_BWD = 5
+    TTT_OP_DWCONV3X3_FULLBATCH_BWD = 5,
+    TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD = 6
 } ttt_op;
 
 typedef struct {
@@ -272,6 +273,31 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
  */
 ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
                                          float* gmm, ttt_stream_t stream);
+
+/*
+ * Backward of ttt_linear_minibatch_bidir for L = sum <dZ, Z> (end-to-end
+ * training of Vision-TTT through the inner updates; the states are
+ * recomputed, key design item 4).  Per chain (slice, direction) and
+ * mini-batch of n_c tokens with start state Ws, alpha = -2 eta_h / n_c,
+ * token rows R = K Ws^T - V, S = Q K^T and P = dZ R^T (both kept where the
+ * key token does not follow the query token), dWn the gradient at the next
+ * start state:
+ *   dR = alpha (K dWn^T + S^T dZ),  dV = -dR,  dQ = dZ Ws + alpha P K,
+ *   dK = dR Ws + alpha (R dWn + P^T Q),  dWs = dWn + dZ^T Q + dR^T K;
+ * with both directions each scan receives dZ / 2.  Summed over the batch
+ * (and the directions): dW0 = the walks' final dWs (with
+ * p->w0_per_direction dW0 is [2][H][d][d], each direction's own),
+ * deta = sum over mini-batches of (-2/n_c)(<R dWn, K> + <P, S>).
+ * p->minibatch in [1, 32] (else TTT_ERR_UNSUPPORTED); bf16 or fp32 views;
+ * p->loss must be L2.  Out: dK, dQ, dV (views, dtype), dW0 and deta fp32
+ * (overwritten).  ws: ttt_workspace_size(TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD,
+ * p) bytes (every mini-batch's start state and gradient state, fp32: about
+ * 2 * slices * directions * ceil(N/b) * 16 KB), no zero-fill needed.
+ */
+ttt_status ttt_linear_minibatch_bidir_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                          const float* W0, const float* eta, ttt_view dZ,
+                                          ttt_view dK, ttt_view dQ, ttt_view dV, float* dW0,
+                                          float* deta, void* ws, size_t ws_bytes, ttt_stream_t stream);
 
 /*
  * Backward of ttt_linear_fullbatch for L = sum <dZ, Z> (end-to-end training

@@ -371,3 +371,25 @@ def test_conv_bwd_errors():
     assert call(saved=addr(8)) == 6                     # saved overlaps the dV output
     assert call(wsb=need - 1) == 7
     assert call(ws=addr(20) + 16) == 4
+
+
+def test_scan_bwd_errors():
+    L = vt.lib()
+    f = L.ttt_linear_minibatch_bidir_bwd
+    p = P(b=16)
+    need = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR_BWD, ctypes.byref(p))
+    assert need > 0
+    assert L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR_BWD, ctypes.byref(P(b=33))) == 0
+
+    def call(pp=p, dK=V(6), dW0=addr(12), wsb=need, W0=addr(10)):
+        return f(ctypes.byref(pp), V(0), V(1), V(2), W0, addr(11), V(3), dK, V(7), V(8), dW0, addr(13),
+                 addr(20), wsb, None)
+    assert call(pp=P(b=0)) == 2
+    assert call(pp=P(b=33)) == 5                     # more than 32 tokens per mini-batch
+    assert call(pp=P(b=16, mode=3)) == 5
+    assert call(pp=bd.Problem(2, 3, 100, 64, bd.TTT_BF16, 10, 10, 16, 0, bd.LOSS_DOT, 1, 0)) == 5
+    assert call(pp=P(b=16, B=0)) == 0
+    assert call(dW0=None) == 1
+    assert call(dK=V(0)) == 6
+    assert call(wsb=need - 1) == 7
+    assert call(W0=addr(10) + 4) == 4

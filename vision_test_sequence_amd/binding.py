@@ -28,6 +28,7 @@ OP_LINEAR_MINIBATCH_BIDIR = 2
 OP_LINEAR_FULLBATCH_BWD = 3
 OP_LAYER_FULLBATCH = 4
 OP_DWCONV3X3_FULLBATCH_BWD = 5
+OP_LINEAR_MINIBATCH_BIDIR_BWD = 6
 
 KERNEL_LIN_RESIDENT = 1
 KERNEL_LIN_RESIDENT_GX = 2
@@ -44,7 +45,7 @@ EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
             "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
             "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc", "ttt_dwconv3x3_fullbatch_bwd",
-            "ttt_linear_gradient_magnitude")
+            "ttt_linear_gradient_magnitude", "ttt_linear_minibatch_bidir_bwd")
 
 
 class TTTError(RuntimeError):
@@ -119,6 +120,8 @@ def lib() -> ctypes.CDLL:
             L.ttt_dwconv3x3_fullbatch_bwd.argtypes = [P, View, View, View, fp, fp, View, fp, View, View,
                                                       View, fp, fp, vp, sz, vp]
             L.ttt_linear_gradient_magnitude.argtypes = [P, View, View, fp, fp, vp]
+            L.ttt_linear_minibatch_bidir_bwd.argtypes = [P, View, View, View, fp, fp, View, View, View, View,
+                                                         fp, fp, vp, sz, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -421,3 +424,29 @@ def ttt_linear_gradient_magnitude(K, V, W0, *, out=None, loss: int = LOSS_L2):
                                              _stream(K.device))
     _check(st, "ttt_linear_gradient_magnitude")
     return out
+
+
+def ttt_linear_minibatch_bidir_bwd(K, Q, V, W0, eta, dZ, minibatch: int, mode: int = BIDIR_AVG, *, dK=None,
+                                   dQ=None, dV=None, dW0=None, deta=None):
+    """Backward of ttt_linear_minibatch_bidir for L = sum(dZ * Z).
+
+    W0 [H,64,64] (shared) or [2,H,64,64] (one per direction; dW0 then has
+    the same shape).  Returns (dK, dQ, dV, dW0, deta)."""
+    B, H, N, d = K.shape
+    w0dir = 1 if W0.dim() == 4 else 0
+    wshape = (2, H, d, d) if w0dir else (H, d, d)
+    _param(W0, wshape, "W0")
+    _param(eta, (H,), "eta")
+    mk = lambda: torch.empty((B, H, N, d), dtype=K.dtype, device=K.device)
+    dK = mk() if dK is None else dK
+    dQ = mk() if dQ is None else dQ
+    dV = mk() if dV is None else dV
+    dW0 = torch.empty(wshape, dtype=torch.float32, device=K.device) if dW0 is None else dW0
+    deta = torch.empty((H,), dtype=torch.float32, device=K.device) if deta is None else deta
+    p = problem(K, minibatch=minibatch, mode=mode, w0_per_direction=w0dir)
+    ws, wsb = workspace(OP_LINEAR_MINIBATCH_BIDIR_BWD, p, K.device)
+    st = lib().ttt_linear_minibatch_bidir_bwd(ctypes.byref(p), view(K), view(Q), view(V), W0.data_ptr(),
+                                              eta.data_ptr(), view(dZ), view(dK), view(dQ), view(dV),
+                                              dW0.data_ptr(), deta.data_ptr(), ws, wsb, _stream(K.device))
+    _check(st, "ttt_linear_minibatch_bidir_bwd")
+    return dK, dQ, dV, dW0, deta

@@ -258,6 +258,9 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     case TTT_OP_DWCONV3X3_FULLBATCH_BWD:
         if (p->grid_h <= 0 || p->grid_w <= 0 || (int64_t)p->grid_h * p->grid_w != p->N) return 0;
         return conv_bwd_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
+    case TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD:
+        if (!scan_bwd_supported(p->minibatch)) return 0;
+        return scan_bwd_ws_bytes(p->B, p->H, p->N, p->minibatch, (int)p->mode);
     }
     return 0;
 }
@@ -603,6 +606,45 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     return hip_status(launch_scan(a, (hipStream_t)stream));
 }
 
+ttt_status ttt_linear_minibatch_bidir_bwd(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,
+                                          const float* W0, const float* eta, ttt_view dZ, ttt_view dK,
+                                          ttt_view dQ, ttt_view dV, float* dW0, float* deta, void* ws,
+                                          size_t ws_bytes, ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (p->minibatch < 1) return TTT_ERR_BAD_SHAPE;
+    if (p->mode != TTT_BIDIR_AVG && p->mode != TTT_FORWARD_ONLY && p->mode != TTT_BACKWARD_ONLY)
+        return TTT_ERR_UNSUPPORTED;
+    if (!scan_bwd_supported(p->minibatch) || p->loss != TTT_LOSS_L2 || p->steps > 1) return TTT_ERR_UNSUPPORTED;
+    if (noop) return TTT_OK;
+    const size_t nw0 = p->w0_per_direction ? 2 : 1;
+    Span in[6], out[6];
+    if ((st = check_buf(dW0, nw0 * p->H * p->d * p->d * 4, 4, &out[3])) != TTT_OK) return st;
+    if ((st = check_buf(deta, (size_t)p->H * 4, 4, &out[4])) != TTT_OK) return st;
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W0, nw0 * p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_view(dZ, *p, &in[5])) != TTT_OK) return st;
+    if ((st = check_view(dK, *p, &out[0])) != TTT_OK) return st;
+    if ((st = check_view(dQ, *p, &out[1])) != TTT_OK) return st;
+    if ((st = check_view(dV, *p, &out[2])) != TTT_OK) return st;
+    const size_t need = scan_bwd_ws_bytes(p->B, p->H, p->N, p->minibatch, (int)p->mode);
+    if ((st = check_ws(ws, ws_bytes, need, &out[5])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 6, out, 6)) != TTT_OK) return st;
+    ScanBwdLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.dZ = v4(dZ);
+    a.dK = v4(dK); a.dQ = v4(dQ); a.dV = v4(dV);
+    a.W0 = W0; a.eta = eta; a.dW0 = dW0; a.deta = deta;
+    a.B = p->B; a.H = p->H; a.N = p->N; a.b = p->minibatch; a.mode = (int)p->mode;
+    a.w0dir = p->w0_per_direction;
+    a.bf16 = p->dtype == TTT_BF16;
+    a.ws = ws;
+    return hip_status(launch_scan_bwd(a, (hipStream_t)stream));
+}
+
 ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
                                          float* gmm, ttt_stream_t stream) {
     bool noop = false;
@@ -742,7 +784,7 @@ ttt_status ttt_workspace_exchange_failed(ttt_op op, const void* ws, size_t ws_by
                                          ttt_stream_t stream) {
     if (!failed) return TTT_ERR_NULL_POINTER;
     *failed = 0;
-    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_DWCONV3X3_FULLBATCH_BWD) return TTT_ERR_UNSUPPORTED;
+    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD) return TTT_ERR_UNSUPPORTED;
     const int nb = counter_blocks(op);
     if (nb == 0 || ws_bytes == 0) return TTT_OK;
     if (!ws) return TTT_ERR_NULL_POINTER;

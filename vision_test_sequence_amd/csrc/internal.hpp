@@ -121,6 +121,20 @@ size_t scan_ws_bytes(int B, int H, int N, int mode);
 bool scan_minibatch_supported(int b, int N);
 hipError_t launch_scan(ScanLaunch a, hipStream_t stream);
 
+// ---- backward of the mini-batch scans --------------------------------------
+struct ScanBwdLaunch {
+    View4 K, Q, V, dZ, dK, dQ, dV;
+    const float* W0;
+    const float* eta;
+    float* dW0;
+    float* deta;
+    int B, H, N, b, mode, w0dir, bf16;
+    void* ws;         // scan_bwd_ws_bytes(...) bytes
+};
+bool scan_bwd_supported(int b);
+size_t scan_bwd_ws_bytes(int B, int H, int N, int b, int mode);
+hipError_t launch_scan_bwd(const ScanBwdLaunch& a, hipStream_t stream);
+
 // ---- backward of the full-batch linear step ----------------------------
 struct LinBwdLaunch {
     View4 K, Q, V, dZ, dK, dQ, dV;
