@@ -261,6 +261,32 @@ def rows(torch, vt, wl, dev, n=40):
     ms = med(e2)
     out["linear_two_steps"] = _row(ms * 1e3, 4 * w.B * (l1 - l0) * w.N * w.d * 2, w.B * w.N, {
         "workload": f"{WORKLOAD} linear heads, two full-batch steps (Gram pass, steps, apply: 3 launches)"})
+    # two-layer SiLU MLP inner model on every head of the stack, widths d and 4d
+    for hid in (64, 256):
+        mw = {k: v.to(dev) for k, v in wl.draw_mlp_weights(w.H, hid, seed=w.seed + 1).items()}
+        ml = lambda i: vt.ttt_mlp_fullbatch(gs[i % NSETS]["K"], gs[i % NSETS]["Q"], gs[i % NSETS]["V"], mw["W1"],
+                                            mw["W2"], gs[i % NSETS]["eta"], Z=gs[i % NSETS]["Z"])
+        ms = med(ml)
+        flops = w.B * w.H * w.N * 14 * w.d * hid
+        out[f"mlp_hidden{hid}"] = _row(ms * 1e3, 4 * w.B * w.H * w.N * w.d * 2, w.B * w.N, {
+            "workload": f"{WORKLOAD}: B={w.B}, all {w.H} heads a two-layer SiLU MLP of hidden width {hid}, "
+                        "one full-batch step then apply",
+            "tflops": flops / (ms * 1e-3) / 1e12, "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+    del gs
+    # backward of the bidirectional scan, 1280x1280, b = 16
+    w = wl.WORKLOADS[SCAN_WORKLOAD]
+    inp = wl.draw(w.B, w.H, w.N, seed=w.seed, dtype="bf16", unit_rows=True, backward=True)
+    g = {k: v.to(dev) for k, v in inp.items()}
+    outs = [torch.empty_like(g["K"]) for _ in range(3)]
+    dW0 = torch.empty_like(g["W0"])
+    deta = torch.empty_like(g["eta"])
+    sb = lambda i: vt.ttt_linear_minibatch_bidir_bwd(g["K"], g["Q"], g["V"], g["W0"], g["eta"], g["dZ"],
+                                                     w.minibatch, 0, dK=outs[0], dQ=outs[1], dV=outs[2],
+                                                     dW0=dW0, deta=deta)
+    ms = med(sb, 3)
+    out["scan_bidir_bwd_b16"] = _row(ms * 1e3, 7 * w.B * w.H * w.N * w.d * 2, w.B * w.N, {
+        "workload": f"{SCAN_WORKLOAD}: B={w.B}, H={w.H}, N={w.N}, b={w.minibatch}, both directions, "
+                    "states recomputed"})
     return out
 
 

@@ -101,7 +101,8 @@ typedef enum {
                                    ttt_layer_workspace_size; ttt_workspace_size
                                    returns 0 for it) */
     TTT_OP_DWCONV3X3_FULLBATCH_BWD = 5,
-    TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD = 6
+    TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD = 6,
+    TTT_OP_MLP_FULLBATCH = 7
 } ttt_op;
 
 typedef struct {
@@ -133,6 +134,8 @@ typedef struct {
                                 [2][H][d][d], the forward scan starting from
                                 W0[0] and the reversed one from W0[1]; 0 =
                                 one shared [H][d][d]                         */
+    int32_t hidden;          /* ttt_mlp_fullbatch only: hidden width of the
+                                two-layer inner model (r d, r = 1..4)        */
 } ttt_problem;
 
 /* Bytes of workspace `op` needs for problem `p` (0 for a bad problem). */
@@ -252,7 +255,8 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
  *   z_t = W_t q_t,  and after the batch Ws <- W_last.
  * Both directions start from W0.  TTT_BIDIR_AVG writes
  * Z = (Z_forward + Z_reverse)/2; the other modes write one direction.
- * b must be in [1, 16] on this device (larger: TTT_ERR_UNSUPPORTED).
+ * b: any value in [1, 16], a multiple of 16, or b >= N (one mini-batch);
+ * other values return TTT_ERR_UNSUPPORTED.
  * (N + 512) * stride_n * 2 bytes must stay under 2^31 for K, Q, V and Z
  * (a slice's rows are addressed with 32-bit offsets; else
  * TTT_ERR_UNSUPPORTED).
@@ -273,6 +277,30 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
  */
 ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
                                          float* gmm, ttt_stream_t stream);
+
+/*
+ * Two-layer SiLU MLP inner model (ViT3 article, observation 4: widening the
+ * inner model from hidden = d to 4d keeps improving the layer), one
+ * full-batch step of the L2 loss, then applied to the queries.  Per slice
+ * (b, h), with f(k) = W2 silu(W1 k) and e_t = f(k_t) - v_t:
+ *   dW2 = (2/N) sum_t e_t a_t^T,  a_t = silu(W1 k_t),
+ *   dW1 = (2/N) sum_t ((W2^T e_t) * silu'(W1 k_t)) k_t^T,
+ *   W1' = W1[h] - eta[h] dW1,  W2' = W2[h] - eta[h] dW2,
+ *   Z[b,h,t] = W2' silu(W1' q_t).
+ * p->hidden in {64, 128, 192, 256}; bf16 views only; p->loss L2; one step.
+ * In: K, Q, V [B,H,N,d] views; W1 float [H][hidden][d]; W2 float
+ * [H][d][hidden]; eta float [H].  Out: Z [B,H,N,d] view.  Every product on
+ * the matrix cores with bf16 operands (the weights, the activations, the
+ * errors and the back-propagated gradients rounded to bf16) and fp32
+ * accumulation; the per-split gradient partials are summed in a fixed order
+ * (deterministic).  ws: ttt_workspace_size(TTT_OP_MLP_FULLBATCH, p) bytes
+ * (bf16 weights and fp32 gradient partials), no zero-fill needed.
+ * Errors: TTT_ERR_UNSUPPORTED for fp32, other widths or the dot loss,
+ * TTT_ERR_BAD_SHAPE for hidden <= 0, then as ttt_linear_fullbatch.
+ */
+ttt_status ttt_mlp_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V, const float* W1,
+                             const float* W2, const float* eta, ttt_view Z, void* ws, size_t ws_bytes,
+                             ttt_stream_t stream);
 
 /*
  * Backward of ttt_linear_minibatch_bidir for L = sum <dZ, Z> (end-to-end

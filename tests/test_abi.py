@@ -393,3 +393,33 @@ def test_scan_bwd_errors():
     assert call(dK=V(0)) == 6
     assert call(wsb=need - 1) == 7
     assert call(W0=addr(10) + 4) == 4
+
+
+def test_mlp_errors():
+    L = vt.lib()
+    f = L.ttt_mlp_fullbatch
+
+    def M(hidden=256, dtype=bd.TTT_BF16, loss=bd.LOSS_L2, steps=1, B=2, d=64):
+        return bd.Problem(B, 3, 100, d, dtype, 10, 10, 0, 0, loss, steps, 0, hidden)
+    p = M()
+    need = L.ttt_workspace_size(bd.OP_MLP_FULLBATCH, ctypes.byref(p))
+    assert need > 0
+    for hid in (64, 128, 192):
+        assert 0 < L.ttt_workspace_size(bd.OP_MLP_FULLBATCH, ctypes.byref(M(hidden=hid))) < need
+    assert L.ttt_workspace_size(bd.OP_MLP_FULLBATCH, ctypes.byref(M(hidden=96))) == 0
+
+    def call(pp=p, W1=addr(10), W2=addr(11), Z=V(3), wsb=need):
+        return f(ctypes.byref(pp), V(0), V(1), V(2), W1, W2, addr(12), Z, addr(20), wsb, None)
+    assert call(pp=M(hidden=0)) == 2
+    assert call(pp=M(hidden=96)) == 5                 # widths are 64 r, r = 1..4
+    assert call(pp=M(hidden=320)) == 5
+    assert call(pp=M(dtype=bd.TTT_F32)) == 5          # bf16 only
+    assert call(pp=M(loss=bd.LOSS_DOT)) == 5
+    assert call(pp=M(steps=2)) == 5
+    assert call(pp=M(d=32)) == 5
+    assert call(pp=M(B=0)) == 0                       # empty: no launch
+    assert call(W1=None) == 1
+    assert call(W2=addr(11) + 2) == 4
+    assert call(Z=V(0)) == 6                          # Z overlaps K
+    assert call(W1=addr(3)) == 6                      # W1 inside Z
+    assert call(wsb=need - 1) == 7

@@ -30,4 +30,5 @@ from .binding import (  # noqa: F401
     ttt_linear_gradient_magnitude,
     ttt_linear_minibatch_bidir,
     ttt_linear_minibatch_bidir_bwd,
+    ttt_mlp_fullbatch,
 )

@@ -29,6 +29,7 @@ OP_LINEAR_FULLBATCH_BWD = 3
 OP_LAYER_FULLBATCH = 4
 OP_DWCONV3X3_FULLBATCH_BWD = 5
 OP_LINEAR_MINIBATCH_BIDIR_BWD = 6
+OP_MLP_FULLBATCH = 7
 
 KERNEL_LIN_RESIDENT = 1
 KERNEL_LIN_RESIDENT_GX = 2
@@ -45,7 +46,7 @@ EXPORTED = ("ttt_workspace_size", "ttt_status_string", "ttt_layer_workspace_size
             "ttt_dwconv3x3_fullbatch", "ttt_linear_minibatch_bidir", "ttt_linear_fullbatch_bwd",
             "ttt_layer_fullbatch", "ttt_plan_query", "ttt_layer_plan_query",
             "ttt_workspace_exchange_failed", "ttt_workspace_reset", "ttt_linear_fullbatch_noalloc", "ttt_dwconv3x3_fullbatch_bwd",
-            "ttt_linear_gradient_magnitude", "ttt_linear_minibatch_bidir_bwd")
+            "ttt_linear_gradient_magnitude", "ttt_linear_minibatch_bidir_bwd", "ttt_mlp_fullbatch")
 
 
 class TTTError(RuntimeError):
@@ -69,7 +70,8 @@ class Problem(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int), ("grid_h", ctypes.c_int32),
                 ("grid_w", ctypes.c_int32), ("minibatch", ctypes.c_int32), ("mode", ctypes.c_int),
-                ("loss", ctypes.c_int), ("steps", ctypes.c_int32), ("w0_per_direction", ctypes.c_int32)]
+                ("loss", ctypes.c_int), ("steps", ctypes.c_int32), ("w0_per_direction", ctypes.c_int32),
+                ("hidden", ctypes.c_int32)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -122,6 +124,7 @@ def lib() -> ctypes.CDLL:
             L.ttt_linear_gradient_magnitude.argtypes = [P, View, View, fp, fp, vp]
             L.ttt_linear_minibatch_bidir_bwd.argtypes = [P, View, View, View, fp, fp, View, View, View, View,
                                                          fp, fp, vp, sz, vp]
+            L.ttt_mlp_fullbatch.argtypes = [P, View, View, View, fp, fp, fp, View, vp, sz, vp]
             for f in EXPORTED[3:]:
                 getattr(L, f).restype = ctypes.c_int
             _lib = L
@@ -147,10 +150,11 @@ def view(t: torch.Tensor) -> View:
 
 
 def problem(K: torch.Tensor, grid: Tuple[int, int] = (0, 0), minibatch: int = 0,
-            mode: int = BIDIR_AVG, loss: int = LOSS_L2, steps: int = 1, w0_per_direction: int = 0) -> Problem:
+            mode: int = BIDIR_AVG, loss: int = LOSS_L2, steps: int = 1, w0_per_direction: int = 0,
+            hidden: int = 0) -> Problem:
     B, H, N, d = K.shape
     return Problem(B, H, N, d, _dtype_code(K), grid[0], grid[1], minibatch, mode, loss, steps,
-                   w0_per_direction)
+                   w0_per_direction, hidden)
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -450,3 +454,21 @@ def ttt_linear_minibatch_bidir_bwd(K, Q, V, W0, eta, dZ, minibatch: int, mode: i
                                               dW0.data_ptr(), deta.data_ptr(), ws, wsb, _stream(K.device))
     _check(st, "ttt_linear_minibatch_bidir_bwd")
     return dK, dQ, dV, dW0, deta
+
+
+def ttt_mlp_fullbatch(K, Q, V, W1, W2, eta, *, Z=None):
+    """Two-layer SiLU MLP inner model: one full-batch L2 step from (W1, W2),
+    then Z = W2' silu(W1' Q).  W1 float32 [H, hidden, 64], W2 float32
+    [H, 64, hidden], hidden in {64, 128, 192, 256}; bf16 views."""
+    B, H, N, d = K.shape
+    hid = W1.shape[1] if W1.dim() == 3 else -1
+    _param(W1, (H, hid, d), "W1")
+    _param(W2, (H, d, hid), "W2")
+    _param(eta, (H,), "eta")
+    Z = torch.empty_like(K) if Z is None else Z
+    p = problem(K, hidden=hid)
+    ws, wsb = workspace(OP_MLP_FULLBATCH, p, K.device)
+    st = lib().ttt_mlp_fullbatch(ctypes.byref(p), view(K), view(Q), view(V), W1.data_ptr(), W2.data_ptr(),
+                                 eta.data_ptr(), view(Z), ws, wsb, _stream(K.device))
+    _check(st, "ttt_mlp_fullbatch")
+    return Z

@@ -261,6 +261,7 @@ size_t ttt_workspace_size(ttt_op op, const ttt_problem* p) {
     case TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD:
         if (!scan_bwd_supported(p->minibatch)) return 0;
         return scan_bwd_ws_bytes(p->B, p->H, p->N, p->minibatch, (int)p->mode);
+    case TTT_OP_MLP_FULLBATCH: return mlp_ws_bytes(p->B, p->H, p->N, p->hidden);
     }
     return 0;
 }
@@ -645,6 +646,40 @@ ttt_status ttt_linear_minibatch_bidir_bwd(const ttt_problem* p, ttt_view K, ttt_
     return hip_status(launch_scan_bwd(a, (hipStream_t)stream));
 }
 
+ttt_status ttt_mlp_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V, const float* W1,
+                             const float* W2, const float* eta, ttt_view Z, void* ws, size_t ws_bytes,
+                             ttt_stream_t stream) {
+    bool noop = false;
+    ttt_status st = check_problem(p, &noop);
+    if (st != TTT_OK) return st;
+    if (p->hidden <= 0) return TTT_ERR_BAD_SHAPE;
+    if (!mlp_hidden_supported(p->hidden) || p->dtype != TTT_BF16 || p->loss != TTT_LOSS_L2)
+        return TTT_ERR_UNSUPPORTED;
+    if ((st = check_single_step(p)) != TTT_OK) return st;
+    if (noop) return TTT_OK;
+    const int64_t slices = (int64_t)p->B * p->H;
+    if (slices * ((p->N + 255) / 256) > INT32_MAX || slices * (2 * 64 * p->hidden / 256) > INT32_MAX)
+        return TTT_ERR_UNSUPPORTED; // grid sizes
+    const size_t nw = (size_t)p->H * p->hidden * p->d * 4;
+    Span in[6], out[2];
+    if ((st = check_view(K, *p, &in[0])) != TTT_OK) return st;
+    if ((st = check_view(Q, *p, &in[1])) != TTT_OK) return st;
+    if ((st = check_view(V, *p, &in[2])) != TTT_OK) return st;
+    if ((st = check_buf(W1, nw, 4, &in[3])) != TTT_OK) return st;
+    if ((st = check_buf(W2, nw, 4, &in[4])) != TTT_OK) return st;
+    if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[5])) != TTT_OK) return st;
+    if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
+    const size_t need = mlp_ws_bytes(p->B, p->H, p->N, p->hidden);
+    if ((st = check_ws(ws, ws_bytes, need, &out[1])) != TTT_OK) return st;
+    if ((st = check_aliasing(in, 6, out, 2)) != TTT_OK) return st;
+    MlpLaunch a{};
+    a.K = v4(K); a.Q = v4(Q); a.V = v4(V); a.Z = v4(Z);
+    a.W1 = W1; a.W2 = W2; a.eta = eta;
+    a.B = p->B; a.H = p->H; a.N = p->N; a.hid = p->hidden;
+    a.ws = ws;
+    return hip_status(launch_mlp(a, (hipStream_t)stream));
+}
+
 ttt_status ttt_linear_gradient_magnitude(const ttt_problem* p, ttt_view K, ttt_view V, const float* W0,
                                          float* gmm, ttt_stream_t stream) {
     bool noop = false;
@@ -784,7 +819,7 @@ ttt_status ttt_workspace_exchange_failed(ttt_op op, const void* ws, size_t ws_by
                                          ttt_stream_t stream) {
     if (!failed) return TTT_ERR_NULL_POINTER;
     *failed = 0;
-    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_LINEAR_MINIBATCH_BIDIR_BWD) return TTT_ERR_UNSUPPORTED;
+    if (op < TTT_OP_LINEAR_FULLBATCH || op > TTT_OP_MLP_FULLBATCH) return TTT_ERR_UNSUPPORTED;
     const int nb = counter_blocks(op);
     if (nb == 0 || ws_bytes == 0) return TTT_OK;
     if (!ws) return TTT_ERR_NULL_POINTER;

@@ -135,6 +135,19 @@ bool scan_bwd_supported(int b);
 size_t scan_bwd_ws_bytes(int B, int H, int N, int b, int mode);
 hipError_t launch_scan_bwd(const ScanBwdLaunch& a, hipStream_t stream);
 
+// ---- two-layer SiLU MLP inner model, one full-batch L2 step --------------
+struct MlpLaunch {
+    View4 K, Q, V, Z;  // bf16
+    const float* W1;   // [H][hid][64]
+    const float* W2;   // [H][64][hid]
+    const float* eta;
+    int B, H, N, hid;
+    void* ws;          // mlp_ws_bytes(...) bytes
+};
+bool mlp_hidden_supported(int hid);
+size_t mlp_ws_bytes(int B, int H, int N, int hid);
+hipError_t launch_mlp(const MlpLaunch& a, hipStream_t stream);
+
 // ---- backward of the full-batch linear step ----------------------------
 struct LinBwdLaunch {
     View4 K, Q, V, dZ, dK, dQ, dV;

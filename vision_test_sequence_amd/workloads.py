@@ -13,7 +13,10 @@ Recipe (stated once, used everywhere):
     scaled to unit L2 norm per token; V ~ N(0,1); W0 ~ N(0, 1/d);
     w0 ~ N(0, 1/9); eta fixed at 1.0 or ~ U[0.5, 2] per head; dZ ~ N(0,1);
   * cast to float32, then (bf16 workloads) to bfloat16 with round-to-nearest-
-    even.  W0, w0 and eta stay float32.
+    even.  W0, w0 and eta stay float32;
+  * two-layer MLP inner model (``draw_mlp_weights``), its own generator
+    ``default_rng(seed)``: W1 [H, hidden, d] ~ N(0, 1/d), then W2
+    [H, d, hidden] ~ N(0, 1/hidden), float32.
 
 The workloads stand in for the pages' resolutions (224x224 -> 14x14 tokens,
 1248x1248 -> 78x78, 1280x1280 -> 80x80, ViT-B at 1024x1024 -> 64x64) with
@@ -117,6 +120,15 @@ def draw(B: int, H: int, N: int, d: int = 64, *, seed: int, dtype: str = "bf16",
     if backward:
         out["dZ"] = _cast(rng.standard_normal(shape), dtype)
     return out
+
+
+def draw_mlp_weights(H: int, hidden: int, d: int = 64, *, seed: int) -> Dict[str, torch.Tensor]:
+    """W1 [H, hidden, d] and W2 [H, d, hidden] of the two-layer MLP inner
+    model (float32, CPU), with the recipe in the module docstring."""
+    rng = np.random.default_rng(seed)
+    W1 = rng.standard_normal((H, hidden, d)) / np.sqrt(d)
+    W2 = rng.standard_normal((H, d, hidden)) / np.sqrt(hidden)
+    return {"W1": _cast(W1, "f32"), "W2": _cast(W2, "f32")}
 
 
 def make(name: str, seed_offset: int = 0, **overrides) -> Dict[str, torch.Tensor]:
