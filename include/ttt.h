@@ -257,6 +257,13 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
  * Z = (Z_forward + Z_reverse)/2; the other modes write one direction.
  * b: any value in [1, 16], a multiple of 16, or b >= N (one mini-batch);
  * other values return TTT_ERR_UNSUPPORTED.
+ * When the chains (slice x direction) would leave most compute units idle,
+ * each chain is cut into segments that run in parallel (chunk-parallel
+ * scan: over a mini-batch the state update is affine, W <- W M + U, so the
+ * segments' maps are walked first, their start states composed in order,
+ * then every segment walked from its start state); the results agree with
+ * the single walk to rounding.  The environment variable
+ * TTT_SCAN_SEGMENTS=n (a test switch) forces n segments (at most 8).
  * (N + 512) * stride_n * 2 bytes must stay under 2^31 for K, Q, V and Z
  * (a slice's rows are addressed with 32-bit offsets; else
  * TTT_ERR_UNSUPPORTED).

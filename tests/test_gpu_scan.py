@@ -190,3 +190,47 @@ def test_minibatch_sizes_the_kernel_does_not_take():
     K, Q, V, W0, eta = _on(wl.draw(1, 1, 100, seed=1520, dtype="bf16"))
     with pytest.raises(TTTError, match="UNSUPPORTED"):
         vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 20, BIDIR)
+
+
+def _forced_segments(n):
+    import os
+    if n is None:
+        os.environ.pop("TTT_SCAN_SEGMENTS", None)
+    else:
+        os.environ["TTT_SCAN_SEGMENTS"] = str(n)
+
+
+@pytest.mark.parametrize("N,b,mode", [(2000, 16, BIDIR), (1001, 7, FWD), (1001, 7, BWD), (3000, 32, BIDIR),
+                                      (640, 1, BIDIR), (999, 48, FWD)])
+@pytest.mark.parametrize("segs", [1, 2, 3, 5, 8])
+def test_chunk_parallel_segments(N, b, mode, segs):
+    # the chunk-parallel scan (segment maps [M | U] walked from [I | 0], start
+    # states composed in order, then the segments' walks) against the oracle
+    # for every segment count, ragged segments and a ragged last mini-batch
+    banner(f"scan segments={segs} N={N} b={b} mode={mode}")
+    # per-token steps (b = 1) diverge for eta > 1 on unit keys (the factor
+    # 1 - 2 eta along k): those cases take eta = 1/2
+    inp = wl.draw(1, 3, N, seed=880 + N + b + segs, dtype="bf16", unit_rows=True,
+                  eta_fixed=0.5 if b < 4 else None)
+    try:
+        _forced_segments(segs)
+        _check(*_on(inp), b, mode)
+    finally:
+        _forced_segments(None)
+
+
+def test_segments_with_one_initial_state_per_direction():
+    import vision_test_sequence_amd as vt
+    banner("scan segments with W0 per direction")
+    inp = wl.draw(2, 2, 1500, seed=890, dtype="bf16", unit_rows=True)
+    K, Q, V, W0, eta = _on(inp)
+    W1 = torch.randn_like(W0) / 8
+    two = torch.stack([W0, W1]).contiguous()
+    try:
+        _forced_segments(4)
+        Z = vt.ttt_linear_minibatch_bidir(K, Q, V, two, eta, 16, BIDIR)
+        torch.cuda.synchronize()
+    finally:
+        _forced_segments(None)
+    Zr = oracle.linear_minibatch_2w0(f64(K), f64(Q), f64(V), f64(two), f64(eta), 16, BIDIR)
+    assert slice_rel_err(f64(Z), Zr) <= TOL["bf16"]

@@ -604,6 +604,10 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     a.ws = ws;
     a.cus = device_cus();
     a.w0dir = p->w0_per_direction;
+    // test switch: TTT_SCAN_SEGMENTS=n cuts every chain into n segments (at
+    // most 8, and no more than its mini-batches) instead of the planned count
+    const char* sg = getenv("TTT_SCAN_SEGMENTS");
+    a.segs = sg ? atoi(sg) : 0;
     return hip_status(launch_scan(a, (hipStream_t)stream));
 }
 

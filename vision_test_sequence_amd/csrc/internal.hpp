@@ -115,6 +115,7 @@ struct ScanLaunch {
     void* ws;         // scan_ws_bytes(...) bytes
     int cus;          // compute units of the device
     int w0dir;        // W0 is [2][H][64][64]: forward, then reverse scan
+    int segs;         // chunk-parallel segments per chain: 0 = planned
 };
 size_t scan_ws_bytes(int B, int H, int N, int mode);
 // Mini-batch sizes the scan kernel takes: b <= 16, multiples of 16, b >= N.

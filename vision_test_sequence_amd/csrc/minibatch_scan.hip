@@ -37,11 +37,20 @@
 // mask applied to the packed bf16 operand as a bit mask.
 //
 // Bidirectional average: each direction of a column block runs in a
-// workgroup of its own and stores every token's output in the workspace as
-// bf16 (P forward, P2 backward); a second kernel (scan_average) forms
-// Z = (P + P2) / 2 in fp32 and rounds it to bf16.  (With the two directions in one workgroup, stepping
-// in lockstep and averaging as they go, the 1280x1280 workload took 162 us
-// against 122 us: the lockstep paced both chains by the slowest wave.)
+// workgroup of its own and stores every token's output in the workspace in
+// fp32 (P forward, P2 backward); a second kernel (scan_average) forms
+// Z = (P + P2) / 2 and rounds it to bf16 once.  (With the two directions in
+// one workgroup, stepping in lockstep and averaging as they go, the
+// 1280x1280 workload took 162 us against 122 us: the lockstep paced both
+// chains by the slowest wave.)
+//
+// Chunk-parallel scan: over one mini-batch X <- (I + alpha K^T K) X
+// - alpha K^T V, an affine map of X.  When the chains leave most CUs idle,
+// each is cut into segments: scan_maps walks the state [M | U] from [I | 0]
+// through every segment but the last (eight 16-column blocks, V = 0 for the
+// M columns: the chain wave's own arithmetic), scan_starts composes the
+// start states in order (W_s = W_{s-1} M^T + U^T), and the scan kernel
+// walks every segment from its start state.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -88,7 +97,17 @@ struct ScanArgs {
     int tb;            // tokens per tile: b (b <= 16) or 16
     int T;             // tiles per mini-batch: 1 (b <= 16) or ceil(min(b, N) / 16)
     int ntile;         // tiles of one walk: ceil(N / tb)
+    int nseg;          // segments per chain (chunk-parallel scan), 1 = one walk
+    float* maps;       // [chains][nseg-1][2][64][64]: segment maps (S_M, S_U), W layout
+    float* starts;     // [chains][nseg][64][64]: segment start states W_s (s >= 1)
 };
+
+// Segment s of a chain: mini-batches [s nmb / nseg, (s+1) nmb / nseg), as tiles.
+__device__ __forceinline__ int seg_mb(const ScanArgs& a, int s) { return (int)((long long)s * a.nch / a.nseg); }
+__device__ __forceinline__ int seg_tile(const ScanArgs& a, int s) {
+    const int t = seg_mb(a, s) * a.T;
+    return t < a.ntile ? t : a.ntile;
+}
 
 // Per-lane walk of one chain over tiles of tb tokens.  Token slot m of
 // tile j is token p = j*tb + m (forward) or N-1-(j*tb + m) (reverse).  A
@@ -96,8 +115,9 @@ struct ScanArgs {
 // multiple of 16, or b >= N: then every mini-batch but the walk's last is
 // T whole tiles).
 struct Walk {
-    int g, m, rt, dir, b, N, nch;
-    long long step; // token step per tile: +-tb
+    int g, m, rt, dir, b, N, nch; // nch: tiles of this walk
+    int j0, mb0;                  // the walk's first tile and first mini-batch
+    long long step;               // token step per tile: +-tb
 };
 __device__ __forceinline__ int token_of(const Walk& L, int rho) { return L.dir ? L.N - 1 - rho : rho; }
 // Loads are branch-free (so the compiler can schedule them into the
@@ -125,16 +145,21 @@ constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice spa
 
 // ------------------------------------------------------------ chain wave --
 // K, V: the slice's token 0, channel 0; Ksn, Vsn: token strides in bytes.
-template <int D>
+// Ws: the walk's start state W (row-major [64][64], W = X^T), or null for a
+// segment map's block (MAP): the identity (columns of M, vzero: no V term)
+// or zero (columns of U).  MAP walks publish nothing and store their final
+// state, transposed like Ws, to out (rows 16 rt + m).
+template <int D, bool MAP>
 __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
-                           long long Vsn, const float* W0h, float eta, char* lds) {
+                           long long Vsn, const float* Ws, float eta, char* lds, bool vzero = false,
+                           float* out = nullptr) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int e = (lane & 15) >> 2, aa = lane & 3;
     char* vbuf = lds + kNK * kKBuf;
-    // X = W0^T in accumulator layout
+    // X = W^T in accumulator layout: tile 2kb + h holds rows 32 kb + 8g + 4h + i
     v4f X[4];
-    {
-        const float* w = W0h + (16 * L.rt + m) * 64 + 8 * g;
+    if (Ws) {
+        const float* w = Ws + (16 * L.rt + m) * 64 + 8 * g;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             const f32x4 lo = *reinterpret_cast<const f32x4*>(w + 32 * kb);
@@ -142,17 +167,24 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             X[2 * kb] = v4f{lo[0], lo[1], lo[2], lo[3]};
             X[2 * kb + 1] = v4f{hi[0], hi[1], hi[2], hi[3]};
         }
+    } else {
+        const float one = vzero ? 1.f : 0.f; // identity block of M, or U = 0
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                X[ct][i] = (32 * (ct >> 1) + 8 * g + 4 * (ct & 1) + i == 16 * L.rt + m) ? one : 0.f;
     }
     // K and V rows through buffer descriptors over the slice, as in the
     // output wave: an overrun token or an empty slot loads zeros
     const bool slot = L.m < L.b;
-    const long long p0 = token_of(L, m);
+    const long long p0 = token_of(L, L.j0 * L.b + m);
     const int ch = 16 * L.rt + 4 * g; // this lane's V channels
     const __amdgpu_buffer_rsrc_t krs = span_rsrc(K, (long long)(L.N - 1) * Ksn + 128);
     const __amdgpu_buffer_rsrc_t vrs = span_rsrc(V, (long long)(L.N - 1) * Vsn + 128);
     unsigned koff = slot ? (unsigned)(p0 * Ksn + 16 * g) : kOffSlice;
-    unsigned voff = slot ? (unsigned)(p0 * Vsn + 2 * ch) : kOffSlice;
-    const unsigned kst = slot ? (unsigned)(L.step * Ksn) : 0u, vst = slot ? (unsigned)(L.step * Vsn) : 0u;
+    unsigned voff = slot && !vzero ? (unsigned)(p0 * Vsn + 2 * ch) : kOffSlice;
+    const unsigned kst = slot ? (unsigned)(L.step * Ksn) : 0u, vst = slot && !vzero ? (unsigned)(L.step * Vsn) : 0u;
     struct Regs {
         u32x4 k[2];
         u32x2 v;
@@ -174,7 +206,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
     // uniform counters); xs: the mini-batch's start state in bf16, the B
     // operand of its residuals R = K X_s - V, while X runs on through the
     // batch's tiles (the output wave needs the running state)
-    int chunk = 0, sub = 0;
+    int chunk = L.mb0, sub = 0, left = L.nch;
     u32x4 xs[2];
     // LDS addresses: this lane's K row chunks and V row piece; transposing
     // reads (in each 16-lane group lane 4e + a points at a 4-element row
@@ -207,7 +239,10 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             // the next tile's operands, one step ahead of their use
             v4s_t ktN[4], vinN;
             stage(cr[(u + 1) % D], (u + 1) % kNK, (u + 1) & 1, ktN, vinN);
-            const float alpha = chunk < a.nch - 1 ? alpha_full : (chunk == a.nch - 1 ? alpha_last : 0.f);
+            // past the walk's last tile (the prefetch pipeline's tail) alpha is 0
+            const float alpha =
+                left <= 0 ? 0.f : (chunk < a.nch - 1 ? alpha_full : (chunk == a.nch - 1 ? alpha_last : 0.f));
+            --left;
 
             // bf16 copy of the running state (published), and of the
             // mini-batch's start state at its first tile
@@ -236,15 +271,27 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             // X += K^T R'
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) X[ct] = mfma16(ktA[ct], as_v4s(rp2), X[ct]);
-            // publish the chunk for the output wave
-            *reinterpret_cast<u32x4*>(xo) = xu[0];
-            *reinterpret_cast<u32x4*>(xo + 16) = xu[1];
-            *reinterpret_cast<u32x2*>(xo + 32) = rp2;
-            if (u & 1) chunk_barrier(); // chunks j-1, j published
+            if (!MAP) {
+                // publish the chunk for the output wave
+                *reinterpret_cast<u32x4*>(xo) = xu[0];
+                *reinterpret_cast<u32x4*>(xo + 16) = xu[1];
+                *reinterpret_cast<u32x2*>(xo + 32) = rp2;
+                if (u & 1) chunk_barrier(); // chunks j-1, j published
+            }
             issue(r);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) ktA[ct] = ktN[ct];
             vin = vinN;
+        }
+    }
+    if (MAP) {
+        // the final state, transposed as the start states are read
+        float* o = out + (16 * L.rt + m) * 64 + 8 * g;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            *reinterpret_cast<f32x4*>(o + 32 * kb) = f32x4{X[2 * kb][0], X[2 * kb][1], X[2 * kb][2], X[2 * kb][3]};
+            *reinterpret_cast<f32x4*>(o + 32 * kb + 4) =
+                f32x4{X[2 * kb + 1][0], X[2 * kb + 1][1], X[2 * kb + 1][2], X[2 * kb + 1][3]};
         }
     }
 }
@@ -263,7 +310,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     // the host bounds the spans) or an empty slot (m >= b) reads zeros and
     // stores nothing, with no per-chunk selects.
     const bool slot = L.m < L.b;
-    const long long p0 = token_of(L, m);
+    const long long p0 = token_of(L, L.j0 * L.b + m);
     const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Q, (long long)(L.N - 1) * Qsn + 128);
     unsigned qoff = slot ? (unsigned)(p0 * Qsn + 16 * g) : kOffSlice;
     const unsigned qst = slot ? (unsigned)(L.step * Qsn) : 0u;
@@ -288,6 +335,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     const long long zsn = a.split ? 256 : Zsn;
     unsigned zoff = slot ? (unsigned)(p0 * zsn + (a.split ? 4 : 2) * ch) : kOffSlice;
     const unsigned zst = slot ? (unsigned)(L.step * zsn) : 0u;
+    int left = L.nch; // tiles of the walk still to store (a segment ends before the slice does)
     const int nsteps = ((L.nch + D - 1) / D) * D;
     for (int j0 = 0; j0 < nsteps; j0 += D) {
 #pragma unroll
@@ -313,13 +361,14 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
             // outputs of token slot m, channels 16 rt + 4 g .. +3 (Z
             // streamed past the caches; P, in fp32, is read back by the
             // average, so each direction's output is rounded once, in Z)
+            const unsigned zo = left-- > 0 ? zoff : kOffSlice;
             if (a.split) {
                 const u32x4 pv{__float_as_uint(Zt[0]), __float_as_uint(Zt[1]), __float_as_uint(Zt[2]),
                                __float_as_uint(Zt[3])};
-                __builtin_amdgcn_raw_buffer_store_b128(pv, zrs, zoff, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b128(pv, zrs, zo, 0, 0);
             } else {
                 const u32x2 zv{pack_bf2(Zt[0], Zt[1]), pack_bf2(Zt[2], Zt[3])};
-                __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zoff, 0, 2 /* nt */);
+                __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zo, 0, 2 /* nt */);
             }
             asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
             zoff += zst;
@@ -339,8 +388,15 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Spread ? kOneCuLds : kDirLds];
     const int dsplit = a.split && (int)blockIdx.x >= a.blocks ? 1 : 0;
     const int bidx = (int)blockIdx.x - dsplit * a.blocks;
-    const SliceSplit ss = map_block(bidx, 4, a.xcd);
-    if (ss.slice >= a.slices) return; // padding block of the XCD-aware grid
+    // unit = (slice, segment); its 4 column blocks share an XCD (and the
+    // L2 that serves their common K and Q rows), consecutive units go to
+    // different XCDs
+    const SliceSplit us = map_block(bidx, 4, a.xcd);
+    if (us.slice >= a.slices * a.nseg) return; // padding block of the XCD-aware grid
+    SliceSplit ss;
+    ss.slice = us.slice / a.nseg;
+    ss.split = us.split;
+    const int seg = us.slice % a.nseg;
     const int role = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); // chain / output wave
     const int lane = threadIdx.x & 63;
     Walk L;
@@ -350,7 +406,9 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     L.dir = a.split ? dsplit : (a.mode == 2 ? 1 : 0);
     L.b = a.tb;
     L.N = a.N;
-    L.nch = a.ntile;
+    L.j0 = seg_tile(a, seg);
+    L.nch = seg_tile(a, seg + 1) - L.j0;
+    L.mb0 = seg_mb(a, seg);
     L.step = L.dir ? -(long long)a.tb : (long long)a.tb;
     const int bb = ss.slice / a.H, h = ss.slice % a.H;
     if (role == 0) {
@@ -358,14 +416,114 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
         // per-lane resolution (lane offsets go into the buffer offsets)
         const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
         const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
-        // the reverse scan starts from its own W0 when one is given per direction
-        const float* W0h = a.W0 + ((a.w0dir && L.dir ? (long long)a.H : 0) + h) * 4096;
-        chain_wave<kPre>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, W0h, a.eta[h], lds);
+        // segment 0 starts from W0 (the reverse scan from its own when one is
+        // given per direction), segment s from the state the maps gave it
+        const float* Ws = seg == 0 ? a.W0 + ((a.w0dir && L.dir ? (long long)a.H : 0) + h) * 4096
+                                   : a.starts + ((long long)(dsplit * a.slices + ss.slice) * a.nseg + seg) * 4096;
+        chain_wave<kPre, false>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, Ws, a.eta[h], lds);
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2;
         float* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 : nullptr;
         output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
+    }
+}
+
+// Chunk-parallel scan, first pass: the affine map of each segment but the
+// last.  Over a mini-batch the state update X <- X + K^T R',
+// R' = alpha (K X - V), is X <- (I + alpha K^T K) X - alpha K^T V, so a
+// segment maps its start state to M X + U; walking the state [M | U] from
+// [I | 0] through the segment's mini-batches (V = 0 for the M columns)
+// gives both.  One wave per (chain, segment, 16-column block of [M | U]):
+// blocks 0-3 the columns of M, blocks 4-7 those of U.  Stored transposed
+// (S_M = M^T, S_U = U^T), so that W_end = W_start S_M + S_U.
+__global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[kNK * kKBuf + 2 * kVBuf];
+    // unit = (slice, segment but the last), 8 column blocks of [M | U] each
+    const int units = a.slices * (a.nseg - 1);
+    const int per_dir = (units + 7) / 8 * 8 * 8;
+    const int dsplit = a.split && (int)blockIdx.x >= per_dir ? 1 : 0;
+    const int bidx = (int)blockIdx.x - dsplit * per_dir;
+    const SliceSplit us = map_block(bidx, 8, a.xcd);
+    if (us.slice >= units) return;
+    SliceSplit ss;
+    ss.slice = us.slice / (a.nseg - 1);
+    const int blk = us.split, seg = us.slice % (a.nseg - 1);
+    const int lane = threadIdx.x & 63;
+    Walk L;
+    L.g = lane >> 4;
+    L.m = lane & 15;
+    L.rt = blk & 3;
+    L.dir = a.split ? dsplit : (a.mode == 2 ? 1 : 0);
+    L.b = a.tb;
+    L.N = a.N;
+    L.j0 = seg_tile(a, seg);
+    L.nch = seg_tile(a, seg + 1) - L.j0;
+    L.mb0 = seg_mb(a, seg);
+    L.step = L.dir ? -(long long)a.tb : (long long)a.tb;
+    const int bb = ss.slice / a.H, h = ss.slice % a.H;
+    const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
+    const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
+    float* out = a.maps + (((long long)(dsplit * a.slices + ss.slice) * (a.nseg - 1) + seg) * 2 + (blk >> 2)) * 4096;
+    chain_wave<kPre, true>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, nullptr, a.eta[h], lds, blk < 4, out);
+}
+
+// Chunk-parallel scan, second pass: segment start states in order,
+// W_s = W_{s-1} S_M(s-1) + S_U(s-1), W_0 = W0 (fp32 matrix cores, 16x16x4
+// tiles).  The rows of W (output channels) are independent: one workgroup
+// per (chain, 16-row block), wave w forming columns 16w .. 16w+15; the maps
+// are loaded two steps ahead.
+__global__ __launch_bounds__(256) void scan_starts(ScanArgs a) {
+    __shared__ __attribute__((aligned(16))) float Wl[16 * 68];
+    __shared__ __attribute__((aligned(16))) float Ml[64 * 68];
+    const int chains = a.slices * (a.split ? 2 : 1);
+    const int c = blockIdx.x >> 2, rb = blockIdx.x & 3;
+    if (c >= chains) return;
+    const int dir = a.split ? (c >= a.slices ? 1 : 0) : (a.mode == 2 ? 1 : 0);
+    const int slice = c % a.slices, h = slice % a.H;
+    const float* W0h = a.W0 + ((a.w0dir && dir ? (long long)a.H : 0) + h) * 4096;
+    const int t = threadIdx.x, w = t >> 6, lane = t & 63, g = lane >> 4, m = lane & 15;
+    // this thread's share of a map: float4s t + 256 j of S_M, and the four
+    // S_U entries of its output tile
+    struct MapRegs {
+        f32x4 mr[4];
+        float ur[4];
+    } rg[2];
+    auto fetch = [&](MapRegs& r, int s) __attribute__((always_inline)) {
+        if (s >= a.nseg) return;
+        const float* SM = a.maps + ((long long)c * (a.nseg - 1) + (s - 1)) * 2 * 4096;
+        const float* SU = SM + 4096;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) r.mr[j] = reinterpret_cast<const f32x4*>(SM)[t + 256 * j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.ur[i] = SU[(16 * rb + 4 * g + i) * 64 + 16 * w + m];
+    };
+    auto step = [&](MapRegs& r, int s) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int q = t + 256 * j; // float4 q: row q / 16, columns 4 (q % 16) ..
+            *reinterpret_cast<f32x4*>(Ml + (q >> 4) * 68 + 4 * (q & 15)) = r.mr[j];
+        }
+        v4f acc{r.ur[0], r.ur[1], r.ur[2], r.ur[3]};
+        fetch(r, s + 2);
+        lds_barrier(); // W_{s-1} rows and S_M in LDS
+#pragma unroll
+        for (int k = 0; k < 16; ++k) // D[16rb + 4g+i][16w + m] += W[16rb + m][4k + g] S_M[4k + g][16w + m]
+            acc = mfma4(Wl[m * 68 + 4 * k + g], Ml[(4 * k + g) * 68 + 16 * w + m], acc);
+        lds_barrier(); // every wave has read W_{s-1} and S_M
+        float* out = a.starts + ((long long)c * a.nseg + s) * 4096 + 16 * rb * 64;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Wl[(4 * g + i) * 68 + 16 * w + m] = acc[i];
+            out[(4 * g + i) * 64 + 16 * w + m] = acc[i];
+        }
+    };
+    fetch(rg[0], 1);
+    fetch(rg[1], 2);
+    for (int e = t; e < 1024; e += 256) Wl[(e >> 6) * 68 + (e & 63)] = W0h[16 * rb * 64 + e];
+    for (int s = 1; s < a.nseg; s += 2) {
+        step(rg[0], s);
+        if (s + 1 < a.nseg) step(rg[1], s + 1);
     }
 }
 
@@ -390,16 +548,32 @@ __global__ __launch_bounds__(256) void scan_average(ScanArgs a) {
     __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(z));
 }
 
-long long padded_slices(int B, int H) {
-    const long long s = (long long)B * H;
-    return (s + 7) / 8 * 8;
-}
-
 } // namespace
+
+// Segments of the chunk-parallel scan.  A chain's walk is bound by the
+// throughput of the CU it runs on, not by the recurrence's latency: cut
+// into segments that share CUs, the 1280x1280 scan (48 chains, 192
+// workgroups) took 164 us at 4 segments against 95 us in one walk (maps and
+// walks both slowed by the sharing).  So a chain is cut only while its
+// segments' workgroups still get a CU each: P = CUs / (4 chains), at most
+// kMaxSeg, with at least 8 mini-batches per segment.  forced > 0 (a test
+// switch) takes that count within the same limits.
+constexpr int kMaxSeg = 8;
+int scan_segments(long long chains, int nmb, int cus, int forced) {
+    if (chains <= 0 || chains * 4 >= 1024) return 1;
+    long long P = forced > 0 ? forced : (long long)(cus > 0 ? cus : 256) / (chains * 4);
+    if (P > kMaxSeg) P = kMaxSeg;
+    if (forced <= 0 && P > nmb / 8) P = nmb / 8;
+    if (P > nmb) P = nmb;
+    return P < 1 ? 1 : (int)P;
+}
 
 size_t scan_ws_bytes(int B, int H, int N, int mode) {
     size_t bytes = 256;
     if (mode == 0) bytes += 2 * (size_t)B * H * N * 64 * sizeof(float);
+    const long long chains = (long long)B * H * (mode == 0 ? 2 : 1);
+    if (chains * 4 < 1024) // room for kMaxSeg segments: maps, then start states
+        bytes += (size_t)chains * ((kMaxSeg - 1) * 2 + kMaxSeg) * 4096 * sizeof(float);
     return bytes;
 }
 
@@ -420,19 +594,31 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.ntile = (s.N + a.tb - 1) / a.tb;
     a.slices = s.B * s.H;
     a.mode = s.mode;
-    // both directions: each in workgroups of its own, bf16 outputs averaged
+    // both directions: each in workgroups of its own, fp32 outputs averaged
     // by a second kernel
     a.split = s.mode == 0 ? 1 : 0;
     a.xcd = 1;
-    const long long blocks = padded_slices(s.B, s.H) * 4;
+    const long long chains = (long long)a.slices * (a.split ? 2 : 1);
+    a.nseg = scan_segments(chains, a.nch, s.cus, s.segs);
+    // per direction: (slice, segment) units padded to whole XCD groups, 4 blocks each
+    const long long blocks = ((long long)a.slices * a.nseg + 7) / 8 * 8 * 4;
     a.blocks = (int)blocks;
-    // workspace: [256 bytes reserved][P][P2]
-    float* base = (float*)s.ws;
+    // workspace: [256 bytes reserved][P][P2][segment maps][segment starts]
+    float* cur = (float*)s.ws + 64;
     if (a.split) {
-        a.P = base + 64;
+        a.P = cur;
         a.P2 = a.P + (size_t)a.slices * s.N * 64;
+        cur = a.P2 + (size_t)a.slices * s.N * 64;
     }
-    const long long grid = blocks * (a.split ? 2 : 1);
+    const int dirs = a.split ? 2 : 1;
+    if (a.nseg > 1) {
+        a.maps = cur;
+        a.starts = cur + (size_t)chains * (kMaxSeg - 1) * 2 * 4096;
+        const long long mblocks = ((long long)a.slices * (a.nseg - 1) + 7) / 8 * 8 * 8;
+        hipLaunchKernelGGL(scan_maps, dim3((unsigned)(dirs * mblocks)), dim3(64), 0, stream, a);
+        hipLaunchKernelGGL(scan_starts, dim3((unsigned)(4 * chains)), dim3(256), 0, stream, a);
+    }
+    const long long grid = blocks * dirs;
     if (grid <= s.cus) hipLaunchKernelGGL(scan_kernel<true>, dim3((unsigned)grid), dim3(128), 0, stream, a);
     else hipLaunchKernelGGL(scan_kernel<false>, dim3((unsigned)grid), dim3(128), 0, stream, a);
     if (a.split) {
