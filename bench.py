@@ -192,6 +192,31 @@ def rows(torch, vt, wl, dev, n=40):
                         "both directions averaged, 4 input sets rotated",
             "tflops": flops / (ms * 1e-3) / 1e12})
     del sets
+    # one image of the same workload: few chains, so the scan is cut into
+    # segments (chunk-parallel); also timed as one walk per chain
+    one = []
+    for sidx in range(4):
+        inp = wl.draw(1, w.H, w.N, seed=w.seed + 1000 * sidx, dtype="bf16", unit_rows=True)
+        g = {k: inp[k].to(dev) for k in ("K", "Q", "V", "W0", "eta")}
+        g["Z"] = torch.empty_like(g["Q"])
+        one.append(g)
+    f = lambda i: vt.ttt_linear_minibatch_bidir(one[i % 4]["K"], one[i % 4]["Q"], one[i % 4]["V"], one[i % 4]["W0"],
+                                                one[i % 4]["eta"], w.minibatch, 0, Z=one[i % 4]["Z"])
+    ms = med(f)
+    prev = os.environ.get("TTT_SCAN_SEGMENTS")
+    os.environ["TTT_SCAN_SEGMENTS"] = "1"
+    try:
+        ms1 = med(f)
+    finally:
+        if prev is None:
+            os.environ.pop("TTT_SCAN_SEGMENTS", None)
+        else:
+            os.environ["TTT_SCAN_SEGMENTS"] = prev
+    out["scan_bidir_b16_one_image"] = _row(ms * 1e3, 4 * w.H * w.N * w.d * 2, w.N, {
+        "workload": f"{SCAN_WORKLOAD} one image: B=1, H={w.H}, N={w.N}, b={w.minibatch}, both directions, "
+                    "chunk-parallel (segments planned per chain)",
+        "one_walk_us": ms1 * 1e3})
+    del one
     # forward (saving A, G) and backward of the linear step, ViT-B 1024x1024
     w = wl.WORKLOADS[BWD_WORKLOAD]
     inp = wl.make(BWD_WORKLOAD)
