@@ -99,3 +99,19 @@ def test_workspace_shared_across_shapes():
     for B, gh, gw, seed in cases:
         inp = wl.draw(B, 1, gh * gw, seed=seed, dtype="bf16", unit_rows=True)
         _check(inp["K"].to(d), inp["Q"].to(d), inp["V"].to(d), inp["w0"].to(d), inp["eta"].to(d), gh, gw)
+
+
+@pytest.mark.parametrize("cap", [128, 64, 24])
+def test_slices_share_tiles_among_fewer_workgroups(cap):
+    # fewer resident workgroups than tiles (a smaller device, forced here):
+    # several consecutive tiles per workgroup and still a split exchange
+    import os
+    banner(f"dwconv 1248x1248 conv head, TTT_CONV_CAP={cap}")
+    args = _conv_heads(wl.make("vit3t_1248_bf16"), "vit3t_1248_bf16")
+    os.environ["TTT_CONV_CAP"] = str(cap)
+    try:
+        _check(*args)
+        K, Q, V, w0, eta, gh, gw = args
+        _check(K, Q, V, torch.zeros_like(w0), eta, gh, gw)
+    finally:
+        os.environ.pop("TTT_CONV_CAP", None)

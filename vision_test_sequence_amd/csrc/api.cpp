@@ -169,13 +169,19 @@ ttt_status hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_
 //    protocol any other part or partition mode gets);
 //  * TTT_TEST_EXCHANGE_GIVEUP=1 -- every slice barrier waits for an
 //    unreachable count and gives up after a few polls: the failure path of
-//    the exchange, with every kernel still ending normally.
+//    the exchange, with every kernel still ending normally;
+//  * TTT_CONV_CAP=n -- the depthwise planner sees at most n resident
+//    workgroups, so a slice's tiles are shared out several to a workgroup
+//    (the multi-tile splits of devices with fewer CUs).
 struct Knobs {
     unsigned spin, tbias;
     bool device_exchange;
+    int conv_cap; // TTT_CONV_CAP: fewer resident conv workgroups (0: none)
 };
 Knobs knobs() {
-    Knobs k{kSpinLimit, 0u, false};
+    Knobs k{kSpinLimit, 0u, false, 0};
+    const char* cc = getenv("TTT_CONV_CAP");
+    if (cc) k.conv_cap = atoi(cc);
     const char* e = getenv("TTT_EXCHANGE");
     if (e && strcmp(e, "device") == 0) k.device_exchange = true;
     const char* g = getenv("TTT_TEST_EXCHANGE_GIVEUP");
@@ -341,6 +347,7 @@ static ConvLaunch plan_conv_call(const ttt_problem* p, View4 K, View4 Q, View4 V
     a.cap = device_cus() * conv_resident_per_cu(a.bf16);
     a.dot = p->loss == TTT_LOSS_DOT ? 1 : 0;
     const Knobs kn = knobs();
+    if (kn.conv_cap > 0 && kn.conv_cap < a.cap) a.cap = kn.conv_cap;
     a.xcd_ok = xcd_local_ok(kn) ? 1 : 0;
     a.spin = kn.spin;
     a.tbias = kn.tbias;

@@ -69,12 +69,16 @@ ConvPlan plan_conv(int nslices, int gh, int gw, int esz, int cap) {
     while (!fits(R, TW)) --R;
     ny = (gh + R - 1) / R;
     const long long ntile = ny * (long long)nx;
-    // one workgroup per tile when that stays resident, else one per slice
-    int S = (int)ntile;
-    if ((long long)slices * S > (cap > 0 ? cap : 1)) S = 1;
+    // one workgroup per tile when that stays resident, else as many
+    // workgroups per slice as stay resident, each taking consecutive tiles
+    long long S = ntile;
+    const long long room = (cap > 0 ? cap : 1) / slices;
+    if (S > room) S = room > 1 ? room : 1;
+    const long long tpw = (ntile + S - 1) / S;
+    S = (ntile + tpw - 1) / tpw;
     (void)nslices;
-    p.R = R; p.TW = TW; p.ny = (int)ny; p.nx = nx; p.S = S;
-    p.tpw = (int)((ntile + S - 1) / S);
+    p.R = R; p.TW = TW; p.ny = (int)ny; p.nx = nx; p.S = (int)S;
+    p.tpw = (int)tpw;
     return p;
 }
 
