@@ -90,3 +90,46 @@ def test_one_initial_state_per_direction():
     assert slice_rel_err(f64(f[0]), ref[0]) <= 1e-5
     assert slice_rel_err(f64(f[3][0])[None], ref[3][None]) <= 1e-5
     assert torch.count_nonzero(f[3][1]) == 0
+
+
+def _vector_walks(on):
+    import os
+    if on:
+        os.environ["TTT_SCAN_BWD_VECTOR_WALKS"] = "1"
+    else:
+        os.environ.pop("TTT_SCAN_BWD_VECTOR_WALKS", None)
+
+
+@pytest.mark.parametrize("mode", [0, 1, 2])
+@pytest.mark.parametrize("N,b", [(37, 1), (37, 5), (300, 16), (1, 4), (16, 16), (1000, 7)])
+def test_bf16_matrix_core_walks(mode, N, b):
+    # bf16 views take the matrix-core walks (forward states and the gradient
+    # walk); checked against the oracle and against the vector walks
+    banner(f"scan bwd bf16 matrix-core walks N={N} b={b} mode={mode}")
+    g = _draw(2, 2, N, 1630 + N + b + mode, "bf16")
+    out = _check(g, b, mode)
+    try:
+        _vector_walks(True)
+        ref = _run(g, b, mode)
+    finally:
+        _vector_walks(False)
+    for name, x, y in zip(("dK", "dQ", "dV"), out[:3], ref[:3]):
+        assert slice_rel_err(f64(x), f64(y)) <= TOL["bf16"], name
+
+
+def test_bf16_walks_with_one_initial_state_per_direction():
+    banner("scan bwd bf16 walks, one W0 per direction")
+    import vision_test_sequence_amd as vt
+    g = _draw(2, 2, 500, 1640, "bf16")
+    W1 = torch.from_numpy(np.random.default_rng(1641).standard_normal((2, 64, 64)).astype(np.float32) / 8)
+    two = torch.stack([g["W0"], W1.to(_dev())]).contiguous()
+    out = vt.ttt_linear_minibatch_bidir_bwd(g["K"], g["Q"], g["V"], two, g["eta"], g["dZ"], 16, 0)
+    torch.cuda.synchronize()
+    try:
+        _vector_walks(True)
+        ref = vt.ttt_linear_minibatch_bidir_bwd(g["K"], g["Q"], g["V"], two, g["eta"], g["dZ"], 16, 0)
+        torch.cuda.synchronize()
+    finally:
+        _vector_walks(False)
+    for x, y in zip(out, ref):
+        assert slice_rel_err(f64(x).reshape(1, -1), f64(y).reshape(1, -1)) <= TOL["bf16"]

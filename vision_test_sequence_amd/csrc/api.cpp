@@ -654,6 +654,17 @@ ttt_status ttt_linear_minibatch_bidir_bwd(const ttt_problem* p, ttt_view K, ttt_
     a.w0dir = p->w0_per_direction;
     a.bf16 = p->dtype == TTT_BF16;
     a.ws = ws;
+    // the matrix-core walks address a slice's rows with 32-bit buffer
+    // offsets, walking up to 176 tokens past either end (their prefetch);
+    // TTT_SCAN_BWD_VECTOR_WALKS (a test switch) keeps the vector walks
+    bool spans = true;
+    for (const ttt_view* v : {&K, &Q, &V, &dZ})
+        if ((int64_t)(p->N + 512) * std::max<int64_t>(v->stride_n, p->d) * 2 >= ((int64_t)1 << 31)) spans = false;
+    a.walks = a.bf16 && p->minibatch <= 16 && spans && !getenv("TTT_SCAN_BWD_VECTOR_WALKS") ? 1 : 0;
+    if (p->N == 1 && a.walks) {
+        // one-token views may carry any stride_n (see the forward scan)
+        for (View4* w : {&a.K, &a.Q, &a.V, &a.dZ}) w->sn = std::max<long long>(w->sn, p->d);
+    }
     return hip_status(launch_scan_bwd(a, (hipStream_t)stream));
 }
 

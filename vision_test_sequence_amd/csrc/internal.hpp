@@ -130,8 +130,24 @@ struct ScanBwdLaunch {
     float* dW0;
     float* deta;
     int B, H, N, b, mode, w0dir, bf16;
+    int walks;        // the serial walks on the matrix cores (bf16, b <= 16, 32-bit row offsets)
     void* ws;         // scan_bwd_ws_bytes(...) bytes
 };
+// The backward's two serial walks on the matrix cores (bf16 views, b <= 16):
+// every mini-batch's forward start state, then the gradient walk (dwn,
+// dR by walk position, each chain's dW0 term), in the layouts of the scan
+// backward's workspace.
+struct ScanBwdWalks {
+    View4 K, Q, V, dZ;
+    const float* W0;
+    const float* eta;
+    float* states;    // [chains][nch][64][64]
+    float* dwn;       // [chains][nch][64][64]
+    float* dRp;       // [chains][N][64]
+    float* dW0c;      // [chains][64][64]
+    int B, H, N, b, mode, w0dir;
+};
+hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream);
 bool scan_bwd_supported(int b);
 size_t scan_bwd_ws_bytes(int B, int H, int N, int b, int mode);
 hipError_t launch_scan_bwd(const ScanBwdLaunch& a, hipStream_t stream);

@@ -149,10 +149,12 @@ constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice spa
 // segment map's block (MAP): the identity (columns of M, vzero: no V term)
 // or zero (columns of U).  MAP walks publish nothing and store their final
 // state, transposed like Ws, to out (rows 16 rt + m).
+// states (MAP walks only; may be null): every mini-batch's start state is
+// stored there, transposed like Ws, 4096 floats per mini-batch.
 template <int D, bool MAP>
 __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
                            long long Vsn, const float* Ws, float eta, char* lds, bool vzero = false,
-                           float* out = nullptr) {
+                           float* out = nullptr, float* states = nullptr) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int e = (lane & 15) >> 2, aa = lane & 3;
     char* vbuf = lds + kNK * kKBuf;
@@ -219,6 +221,9 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
     // stage chunk jj (registers r) in K buffer jj % 3 / V buffer jj % 2 and
     // read its transposed operands back
     auto stage = [&](const Regs& r, int kbi, int vbi, v4s_t* ktA, v4s_t& vin) __attribute__((always_inline)) {
+        // the rows are written as 16-byte words and read back as 16-bit
+        // elements: keep the compiler from reordering them across chunks
+        asm volatile("" ::: "memory");
         char* kb = lds + kbi * kKBuf;
         char* vb = vbuf + vbi * kVBuf;
         *reinterpret_cast<u32x4*>(kb + kw) = r.k[0];
@@ -255,6 +260,16 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             if (sub == 0) {
                 xs[0] = xu[0];
                 xs[1] = xu[1];
+                if (MAP && states && chunk < a.nch) {
+                    float* o = states + (long long)chunk * 4096 + (16 * L.rt + m) * 64 + 8 * g;
+#pragma unroll
+                    for (int kb2 = 0; kb2 < 2; ++kb2) {
+                        *reinterpret_cast<f32x4*>(o + 32 * kb2) =
+                            f32x4{X[2 * kb2][0], X[2 * kb2][1], X[2 * kb2][2], X[2 * kb2][3]};
+                        *reinterpret_cast<f32x4*>(o + 32 * kb2 + 4) =
+                            f32x4{X[2 * kb2 + 1][0], X[2 * kb2 + 1][1], X[2 * kb2 + 1][2], X[2 * kb2 + 1][3]};
+                    }
+                }
             }
             if (++sub == a.T) {
                 sub = 0;
@@ -284,7 +299,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
             vin = vinN;
         }
     }
-    if (MAP) {
+    if (MAP && out) {
         // the final state, transposed as the start states are read
         float* o = out + (16 * L.rt + m) * 64 + 8 * g;
 #pragma unroll
@@ -356,7 +371,10 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
             const v4f S = mfma32(as_v8bf(k1), as_v8bf(r.q[1]), mfma32(as_v8bf(k0), as_v8bf(r.q[0]), zero4));
             const v4f Zq = mfma32(as_v8bf(x1), as_v8bf(r.q[1]), mfma32(as_v8bf(x0), as_v8bf(r.q[0]), zero4));
             const u32x2 sb2{pack_bf2(S[0], S[1]) & tril[0], pack_bf2(S[2], S[3]) & tril[1]};
-            const v4f Zt = mfma16(as_v4s(rp2), as_v4s(sb2), Zq);
+            // (added on the vector unit: never chain one matrix-core shape's
+            // result into another shape's accumulator)
+            const v4f Zr = mfma16(as_v4s(rp2), as_v4s(sb2), zero4);
+            const v4f Zt{Zq[0] + Zr[0], Zq[1] + Zr[1], Zq[2] + Zr[2], Zq[3] + Zr[3]};
 
             // outputs of token slot m, channels 16 rt + 4 g .. +3 (Z
             // streamed past the caches; P, in fp32, is read back by the
@@ -466,6 +484,212 @@ __global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
     const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
     float* out = a.maps + (((long long)(dsplit * a.slices + ss.slice) * (a.nseg - 1) + seg) * 2 + (blk >> 2)) * 4096;
     chain_wave<kPre, true>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, nullptr, a.eta[h], lds, blk < 4, out);
+}
+
+// ------------------------------------------------ backward: forward states --
+// Every mini-batch's start state of every chain (b <= 16): the chain wave of
+// the scan, storing the state at each mini-batch start.  One wave per
+// (chain, 16-column block); chain ch = slice * nd + direction index.
+__global__ __launch_bounds__(64, 1) void scan_states(ScanArgs a, float* states, int nd) {
+    __shared__ __attribute__((aligned(16))) char lds[kNK * kKBuf + 2 * kVBuf];
+    const int ch = blockIdx.x >> 2, rt = blockIdx.x & 3;
+    const int slice = ch / nd, di = ch % nd;
+    const int lane = threadIdx.x & 63;
+    Walk L;
+    L.g = lane >> 4;
+    L.m = lane & 15;
+    L.rt = rt;
+    L.dir = a.mode == 2 ? 1 : (a.mode == 0 ? di : 0);
+    L.b = a.tb;
+    L.N = a.N;
+    L.j0 = 0;
+    L.nch = a.ntile;
+    L.mb0 = 0;
+    L.step = L.dir ? -(long long)a.tb : (long long)a.tb;
+    const int bb = slice / a.H, h = slice % a.H;
+    const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
+    const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
+    const float* W0h = a.W0 + ((a.w0dir && L.dir ? (long long)a.H : 0) + h) * 4096;
+    chain_wave<kPre, true>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, W0h, a.eta[h], lds, false, nullptr,
+                           states + (long long)ch * a.nch * 4096);
+}
+
+// ------------------------------------------------ backward: gradient walk --
+// The backward walk of the scan (b <= 16), per chain and 16-row block of
+// dW, on the matrix cores.  With Y = dW^T (the gradient at the next
+// mini-batch start, zero after the last), S = Q K^T (kept for s <= t),
+// alpha = -2 eta / n_c and dZ scaled by zs (1/2 per direction of the
+// average), per mini-batch walked from the last:
+//   dR = alpha (K Y + S^T dZ),   Y <- Y + K^T dR + Q^T dZ,
+// storing Y before the update (dwn) and dR (fp32, by walk position).  The
+// operand layouts are the chain wave's: Y tiles as X's, K Y as K X, S^T
+// straight out of Q K^T's accumulator, K^T and Q^T from staged rows read
+// back transposed, dZ's 16 columns like V's.
+struct BwdWalkArgs {
+    ScanArgs s;
+    View4 Q, dZ;
+    float* dwn;   // [chains][nch][64][64]
+    float* dRp;   // [chains][N][64]
+    float* dW0c;  // [chains][64][64]
+    int nd;
+};
+constexpr int kBD = 6; // chunks in flight (register prefetch depth)
+static_assert(kBD % 2 == 0, "LDS buffer sets alternate with the unrolled index");
+__global__ __launch_bounds__(64, 1) void scan_bwd_chain(BwdWalkArgs w) {
+    const ScanArgs& a = w.s;
+    // two sets of buffers, alternating mini-batches (kBD is even)
+    __shared__ __attribute__((aligned(16))) char lds[2 * (2 * kKBuf + kVBuf)];
+    const int ch = blockIdx.x >> 2, rb = blockIdx.x & 3;
+    const int slice = ch / w.nd, di = ch % w.nd;
+    const int dir = a.mode == 2 ? 1 : (a.mode == 0 ? di : 0);
+    const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
+    const int e = m >> 2, aa = m & 3;
+    const int bb = slice / a.H, h = slice % a.H;
+    const float eta = a.eta[h];
+    const float zs = a.mode == 0 ? 0.5f : 1.f;
+    const int b = a.tb, N = a.N, nch = a.nch;
+    // walk position of slot m in mini-batch c: c b + m; token N-1-pos for
+    // the reverse scan.  Rows through buffer descriptors over the slice: a
+    // slot past either end of the slice reads zeros.
+    const bool slot = m < b;
+    const long long pos0 = (long long)(nch - 1) * b + m;
+    const long long tok0 = dir ? N - 1 - pos0 : pos0;
+    const long long tstep = dir ? b : -b; // token step from one mini-batch to the previous
+    const char* Kp = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
+    const char* Qp = (const char*)w.Q.ptr + (bb * w.Q.sb + h * w.Q.sh) * 2;
+    const char* Zp = (const char*)w.dZ.ptr + (bb * w.dZ.sb + h * w.dZ.sh) * 2;
+    const long long Ksn = a.K.sn * 2, Qsn = w.Q.sn * 2, Zsn = w.dZ.sn * 2;
+    const __amdgpu_buffer_rsrc_t krs = span_rsrc(Kp, (long long)(N - 1) * Ksn + 128);
+    const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Qp, (long long)(N - 1) * Qsn + 128);
+    const __amdgpu_buffer_rsrc_t zrs = span_rsrc(Zp, (long long)(N - 1) * Zsn + 128);
+    unsigned koff = slot ? (unsigned)(tok0 * Ksn + 16 * g) : kOffSlice;
+    unsigned qoff = slot ? (unsigned)(tok0 * Qsn + 16 * g) : kOffSlice;
+    unsigned zoff = slot ? (unsigned)(tok0 * Zsn + 2 * (16 * rb + 4 * g)) : kOffSlice;
+    const unsigned kst = slot ? (unsigned)(tstep * Ksn) : 0u, qst = slot ? (unsigned)(tstep * Qsn) : 0u,
+                   zst = slot ? (unsigned)(tstep * Zsn) : 0u;
+    struct Regs {
+        u32x4 k[2], q[2];
+        u32x2 z;
+    } cr[kBD];
+    auto issue = [&](Regs& r) __attribute__((always_inline)) {
+        r.k[0] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff, 0, 0);
+        r.k[1] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 64u, 0, 0);
+        r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 0, 0);
+        r.q[1] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u, 0, 0);
+        r.z = __builtin_amdgcn_raw_buffer_load_b64(zrs, zoff, 0, 0);
+        koff += kst;
+        qoff += qst;
+        zoff += zst;
+    };
+#pragma unroll
+    for (int u = 0; u < kBD; ++u) issue(cr[u]);
+    // transposed operands of a staged mini-batch: K^T, Q^T for the four Y
+    // tiles (token 4g + e, channels pi(ct, 4a) .. +3) and dZ (token 4g + e,
+    // channels 16 rb + 4a .. +3), as in the chain wave
+    const int kw = m * kKRow + 16 * g, kr = (4 * g + e) * kKRow + 16 * aa;
+    const int vw = m * kVRow + 8 * g, vr = (4 * g + e) * kVRow + 8 * aa;
+    auto stage = [&](const Regs& r, int set, v4s_t* ktA, v4s_t* qtA, v4s_t& zin) __attribute__((always_inline)) {
+        // the rows are written as 16-byte words and read back as 16-bit
+        // elements, which the compiler may treat as unrelated: nothing may
+        // move across these points
+        asm volatile("" ::: "memory");
+        char* kbuf = lds + set * (2 * kKBuf + kVBuf);
+        char* qbuf = kbuf + kKBuf;
+        char* zbuf = kbuf + 2 * kKBuf;
+        *reinterpret_cast<u32x4*>(kbuf + kw) = r.k[0];
+        *reinterpret_cast<u32x4*>(kbuf + kw + 64) = r.k[1];
+        *reinterpret_cast<u32x4*>(qbuf + kw) = r.q[0];
+        *reinterpret_cast<u32x4*>(qbuf + kw + 64) = r.q[1];
+        // dZ scaled by zs (exact in bf16 for 1/2 and 1 away from the denormals)
+        const u32x2 zv{pack_bf2(zs * bflo(r.z[0]), zs * bfhi(r.z[0])), pack_bf2(zs * bflo(r.z[1]), zs * bfhi(r.z[1]))};
+        *reinterpret_cast<u32x2*>(zbuf + vw) = zv;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+            ktA[ct] = tr_read(kbuf + kr + 64 * (ct >> 1) + 8 * (ct & 1));
+            qtA[ct] = tr_read(qbuf + kr + 64 * (ct >> 1) + 8 * (ct & 1));
+        }
+        zin = tr_read(zbuf + vr);
+        asm volatile("" ::: "memory");
+    };
+    v4f Y[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) Y[ct] = v4f{0.f, 0.f, 0.f, 0.f};
+    // S^T for the A operand: lane (g, m) holds S[t = 4g+i][s = m], kept for t >= s
+    const u32x2 keep{(4 * g >= m ? 0xFFFFu : 0u) | (4 * g + 1 >= m ? 0xFFFF0000u : 0u),
+                     (4 * g + 2 >= m ? 0xFFFFu : 0u) | (4 * g + 3 >= m ? 0xFFFF0000u : 0u)};
+    const float alpha_full = -2.f * eta / (float)b;
+    const float alpha_last = -2.f * eta / (float)(N - (nch - 1) * b);
+    float* dwn = w.dwn + (long long)ch * nch * 4096;
+    float* dRp = w.dRp + (long long)ch * N * 64;
+    v4s_t ktA[4], qtA[4], zin;
+    stage(cr[0], 0, ktA, qtA, zin);
+    const int nsteps = (nch + kBD - 1) / kBD * kBD;
+    int c = nch - 1; // mini-batch being walked
+    for (int j0 = 0; j0 < nsteps; j0 += kBD) {
+#pragma unroll
+        for (int u = 0; u < kBD; ++u) {
+            Regs& r = cr[u];
+            const bool live = c >= 0;
+            const float alpha = !live ? 0.f : (c == nch - 1 ? alpha_last : alpha_full);
+            // bf16 copy of Y for K Y; store Y (the gradient at this mini-batch's end)
+            u32x4 ys[2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                ys[kb] = u32x4{pack_bf2(Y[2 * kb][0], Y[2 * kb][1]), pack_bf2(Y[2 * kb][2], Y[2 * kb][3]),
+                               pack_bf2(Y[2 * kb + 1][0], Y[2 * kb + 1][1]), pack_bf2(Y[2 * kb + 1][2], Y[2 * kb + 1][3])};
+            if (live) {
+                float* o = dwn + (long long)c * 4096 + (16 * rb + m) * 64 + 8 * g;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+                    *reinterpret_cast<f32x4*>(o + 32 * kb) = f32x4{Y[2 * kb][0], Y[2 * kb][1], Y[2 * kb][2], Y[2 * kb][3]};
+                    *reinterpret_cast<f32x4*>(o + 32 * kb + 4) =
+                        f32x4{Y[2 * kb + 1][0], Y[2 * kb + 1][1], Y[2 * kb + 1][2], Y[2 * kb + 1][3]};
+                }
+            }
+            // S = Q K^T (lane: S[4g+i][m]); S^T dZ; K Y; dR = alpha (K Y + S^T dZ).
+            // The two sums are added on the vector unit: a product of one
+            // matrix-core shape accumulating onto the result of another shape
+            // issued just before it read that result before it was complete
+            // (the compiler puts no wait between them when the registers
+            // coincide exactly).
+            const v4f zero4{0.f, 0.f, 0.f, 0.f};
+            const v4f S = mfma32(as_v8bf(r.q[1]), as_v8bf(r.k[1]), mfma32(as_v8bf(r.q[0]), as_v8bf(r.k[0]), zero4));
+            const u32x2 sb2{pack_bf2(S[0], S[1]) & keep[0], pack_bf2(S[2], S[3]) & keep[1]};
+            const v4f SdZ = mfma16(as_v4s(sb2), zin, zero4);
+            const v4f KY = mfma32(as_v8bf(r.k[1]), as_v8bf(ys[1]), mfma32(as_v8bf(r.k[0]), as_v8bf(ys[0]), zero4));
+            const v4f dR{alpha * (KY[0] + SdZ[0]), alpha * (KY[1] + SdZ[1]), alpha * (KY[2] + SdZ[2]),
+                         alpha * (KY[3] + SdZ[3])};
+            // dR by walk position (token slot 4g+i of mini-batch c, channel 16 rb + m)
+            if (live) {
+                const int n = c == nch - 1 ? N - (nch - 1) * b : b;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < n) dRp[((long long)c * b + 4 * g + i) * 64 + 16 * rb + m] = dR[i];
+            }
+            const u32x2 dr2{pack_bf2(dR[0], dR[1]), pack_bf2(dR[2], dR[3])};
+            // the next mini-batch's operands, one step ahead of their use
+            v4s_t ktN[4], qtN[4], zN;
+            stage(cr[(u + 1) % kBD], (u + 1) & 1, ktN, qtN, zN);
+            // Y += K^T dR + Q^T dZ
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) Y[ct] = mfma16(qtA[ct], zin, mfma16(ktA[ct], as_v4s(dr2), Y[ct]));
+            issue(r);
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+                ktA[ct] = ktN[ct];
+                qtA[ct] = qtN[ct];
+            }
+            zin = zN;
+            --c;
+        }
+    }
+    // the chain's dW0 contribution: Y at the walk's end (W layout, rows 16 rb + m)
+    float* o = w.dW0c + (long long)ch * 4096 + (16 * rb + m) * 64 + 8 * g;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+        *reinterpret_cast<f32x4*>(o + 32 * kb) = f32x4{Y[2 * kb][0], Y[2 * kb][1], Y[2 * kb][2], Y[2 * kb][3]};
+        *reinterpret_cast<f32x4*>(o + 32 * kb + 4) = f32x4{Y[2 * kb + 1][0], Y[2 * kb + 1][1], Y[2 * kb + 1][2], Y[2 * kb + 1][3]};
+    }
 }
 
 // Chunk-parallel scan, second pass: segment start states in order,
@@ -578,6 +802,35 @@ size_t scan_ws_bytes(int B, int H, int N, int mode) {
 }
 
 bool scan_minibatch_supported(int b, int N) { return b >= 1 && (b <= 16 || b % 16 == 0 || b >= N); }
+
+hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
+    if (l.b < 1 || l.b > 16) return hipErrorNotSupported;
+    ScanArgs a{};
+    a.K = l.K; a.V = l.V; a.Q = l.Q;
+    a.W0 = l.W0; a.eta = l.eta;
+    a.w0dir = l.w0dir;
+    a.H = l.H; a.N = l.N; a.b = l.b;
+    a.nch = (l.N + l.b - 1) / l.b;
+    a.tb = l.b;
+    a.T = 1;
+    a.ntile = a.nch;
+    a.slices = l.B * l.H;
+    a.mode = l.mode;
+    a.nseg = 1;
+    const int nd = l.mode == 0 ? 2 : 1;
+    const unsigned waves = (unsigned)(4LL * a.slices * nd);
+    hipLaunchKernelGGL(scan_states, dim3(waves), dim3(64), 0, stream, a, l.states, nd);
+    BwdWalkArgs w{};
+    w.s = a;
+    w.Q = l.Q;
+    w.dZ = l.dZ;
+    w.dwn = l.dwn;
+    w.dRp = l.dRp;
+    w.dW0c = l.dW0c;
+    w.nd = nd;
+    hipLaunchKernelGGL(scan_bwd_chain, dim3(waves), dim3(64), 0, stream, w);
+    return hipGetLastError();
+}
 
 hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     if (!s.bf16) return hipErrorNotSupported;

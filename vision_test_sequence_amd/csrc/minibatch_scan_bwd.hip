@@ -426,8 +426,18 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& s, hipStream_t stream) {
     const dim3 block(kSbT);
     const dim3 walks((unsigned)(chains * 4)), per_mb((unsigned)(chains * a.nch));
     if (a.bf16) {
-        hipLaunchKernelGGL(sbwd_states<true>, walks, block, 0, stream, a);
-        hipLaunchKernelGGL(sbwd_chain<true>, walks, block, 0, stream, a);
+        if (s.walks) {
+            ScanBwdWalks wk{};
+            wk.K = s.K; wk.Q = s.Q; wk.V = s.V; wk.dZ = s.dZ;
+            wk.W0 = s.W0; wk.eta = s.eta;
+            wk.states = a.ws_state; wk.dwn = a.dwn_state; wk.dRp = a.dRp; wk.dW0c = a.dW0c;
+            wk.B = s.B; wk.H = s.H; wk.N = s.N; wk.b = s.b; wk.mode = s.mode; wk.w0dir = s.w0dir;
+            const hipError_t e = launch_scan_bwd_walks(wk, stream);
+            if (e != hipSuccess) return e;
+        } else {
+            hipLaunchKernelGGL(sbwd_states<true>, walks, block, 0, stream, a);
+            hipLaunchKernelGGL(sbwd_chain<true>, walks, block, 0, stream, a);
+        }
         hipLaunchKernelGGL(sbwd_outputs<true>, per_mb, block, 0, stream, a);
     } else {
         hipLaunchKernelGGL(sbwd_states<false>, walks, block, 0, stream, a);
