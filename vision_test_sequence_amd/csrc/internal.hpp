@@ -134,15 +134,15 @@ struct ScanBwdLaunch {
     void* ws;         // scan_bwd_ws_bytes(...) bytes
 };
 // The backward's two serial walks on the matrix cores (bf16 views, b <= 16):
-// every mini-batch's forward start state, then the gradient walk (dwn,
+// every mini-batch's forward start state (bf16), then the gradient walk (dwn in bf16,
 // dR by walk position, each chain's dW0 term), in the layouts of the scan
 // backward's workspace.
 struct ScanBwdWalks {
     View4 K, Q, V, dZ;
     const float* W0;
     const float* eta;
-    float* states;    // [chains][nch][64][64]
-    float* dwn;       // [chains][nch][64][64]
+    uint16_t* states; // [chains][nch][64][64] bf16
+    uint16_t* dwn;    // [chains][nch][64][64] bf16
     float* dRp;       // [chains][N][64]
     float* dW0c;      // [chains][64][64]
     int B, H, N, b, mode, w0dir;

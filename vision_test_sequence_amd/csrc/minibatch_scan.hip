@@ -150,11 +150,12 @@ constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice spa
 // or zero (columns of U).  MAP walks publish nothing and store their final
 // state, transposed like Ws, to out (rows 16 rt + m).
 // states (MAP walks only; may be null): every mini-batch's start state is
-// stored there, transposed like Ws, 4096 floats per mini-batch.
+// stored there in bf16 (the precision the backward's products take it in),
+// transposed like Ws, 4096 values per mini-batch.
 template <int D, bool MAP>
 __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
                            long long Vsn, const float* Ws, float eta, char* lds, bool vzero = false,
-                           float* out = nullptr, float* states = nullptr) {
+                           float* out = nullptr, bf16_t* states = nullptr) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
     const int e = (lane & 15) >> 2, aa = lane & 3;
     char* vbuf = lds + kNK * kKBuf;
@@ -261,14 +262,9 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
                 xs[0] = xu[0];
                 xs[1] = xu[1];
                 if (MAP && states && chunk < a.nch) {
-                    float* o = states + (long long)chunk * 4096 + (16 * L.rt + m) * 64 + 8 * g;
+                    bf16_t* o = states + (long long)chunk * 4096 + (16 * L.rt + m) * 64 + 8 * g;
 #pragma unroll
-                    for (int kb2 = 0; kb2 < 2; ++kb2) {
-                        *reinterpret_cast<f32x4*>(o + 32 * kb2) =
-                            f32x4{X[2 * kb2][0], X[2 * kb2][1], X[2 * kb2][2], X[2 * kb2][3]};
-                        *reinterpret_cast<f32x4*>(o + 32 * kb2 + 4) =
-                            f32x4{X[2 * kb2 + 1][0], X[2 * kb2 + 1][1], X[2 * kb2 + 1][2], X[2 * kb2 + 1][3]};
-                    }
+                    for (int kb2 = 0; kb2 < 2; ++kb2) *reinterpret_cast<u32x4*>(o + 32 * kb2) = xu[kb2];
                 }
             }
             if (++sub == a.T) {
@@ -489,10 +485,11 @@ __global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
 // ------------------------------------------------ backward: forward states --
 // Every mini-batch's start state of every chain (b <= 16): the chain wave of
 // the scan, storing the state at each mini-batch start.  One wave per
-// (chain, 16-column block); chain ch = slice * nd + direction index.
-__global__ __launch_bounds__(64, 1) void scan_states(ScanArgs a, float* states, int nd) {
+// (chain, 16-column block), wid = 4 ch + block; chain ch = slice * nd +
+// direction index.
+__device__ __forceinline__ void states_wave(const ScanArgs& a, bf16_t* states, int nd, int wid) {
     __shared__ __attribute__((aligned(16))) char lds[kNK * kKBuf + 2 * kVBuf];
-    const int ch = blockIdx.x >> 2, rt = blockIdx.x & 3;
+    const int ch = wid >> 2, rt = wid & 3;
     const int slice = ch / nd, di = ch % nd;
     const int lane = threadIdx.x & 63;
     Walk L;
@@ -521,25 +518,25 @@ __global__ __launch_bounds__(64, 1) void scan_states(ScanArgs a, float* states, 
 // alpha = -2 eta / n_c and dZ scaled by zs (1/2 per direction of the
 // average), per mini-batch walked from the last:
 //   dR = alpha (K Y + S^T dZ),   Y <- Y + K^T dR + Q^T dZ,
-// storing Y before the update (dwn) and dR (fp32, by walk position).  The
+// storing Y before the update (dwn, bf16) and dR (fp32, by walk position).  The
 // operand layouts are the chain wave's: Y tiles as X's, K Y as K X, S^T
 // straight out of Q K^T's accumulator, K^T and Q^T from staged rows read
 // back transposed, dZ's 16 columns like V's.
 struct BwdWalkArgs {
     ScanArgs s;
     View4 Q, dZ;
-    float* dwn;   // [chains][nch][64][64]
+    bf16_t* dwn;  // [chains][nch][64][64]
     float* dRp;   // [chains][N][64]
     float* dW0c;  // [chains][64][64]
     int nd;
 };
 constexpr int kBD = 6; // chunks in flight (register prefetch depth)
 static_assert(kBD % 2 == 0, "LDS buffer sets alternate with the unrolled index");
-__global__ __launch_bounds__(64, 1) void scan_bwd_chain(BwdWalkArgs w) {
+__device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
     const ScanArgs& a = w.s;
     // two sets of buffers, alternating mini-batches (kBD is even)
     __shared__ __attribute__((aligned(16))) char lds[2 * (2 * kKBuf + kVBuf)];
-    const int ch = blockIdx.x >> 2, rb = blockIdx.x & 3;
+    const int ch = wid >> 2, rb = wid & 3;
     const int slice = ch / w.nd, di = ch % w.nd;
     const int dir = a.mode == 2 ? 1 : (a.mode == 0 ? di : 0);
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
@@ -619,7 +616,7 @@ __global__ __launch_bounds__(64, 1) void scan_bwd_chain(BwdWalkArgs w) {
                      (4 * g + 2 >= m ? 0xFFFFu : 0u) | (4 * g + 3 >= m ? 0xFFFF0000u : 0u)};
     const float alpha_full = -2.f * eta / (float)b;
     const float alpha_last = -2.f * eta / (float)(N - (nch - 1) * b);
-    float* dwn = w.dwn + (long long)ch * nch * 4096;
+    bf16_t* dwn = w.dwn + (long long)ch * nch * 4096;
     float* dRp = w.dRp + (long long)ch * N * 64;
     v4s_t ktA[4], qtA[4], zin;
     stage(cr[0], 0, ktA, qtA, zin);
@@ -638,13 +635,9 @@ __global__ __launch_bounds__(64, 1) void scan_bwd_chain(BwdWalkArgs w) {
                 ys[kb] = u32x4{pack_bf2(Y[2 * kb][0], Y[2 * kb][1]), pack_bf2(Y[2 * kb][2], Y[2 * kb][3]),
                                pack_bf2(Y[2 * kb + 1][0], Y[2 * kb + 1][1]), pack_bf2(Y[2 * kb + 1][2], Y[2 * kb + 1][3])};
             if (live) {
-                float* o = dwn + (long long)c * 4096 + (16 * rb + m) * 64 + 8 * g;
+                bf16_t* o = dwn + (long long)c * 4096 + (16 * rb + m) * 64 + 8 * g;
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) {
-                    *reinterpret_cast<f32x4*>(o + 32 * kb) = f32x4{Y[2 * kb][0], Y[2 * kb][1], Y[2 * kb][2], Y[2 * kb][3]};
-                    *reinterpret_cast<f32x4*>(o + 32 * kb + 4) =
-                        f32x4{Y[2 * kb + 1][0], Y[2 * kb + 1][1], Y[2 * kb + 1][2], Y[2 * kb + 1][3]};
-                }
+                for (int kb = 0; kb < 2; ++kb) *reinterpret_cast<u32x4*>(o + 32 * kb) = ys[kb];
             }
             // S = Q K^T (lane: S[4g+i][m]); S^T dZ; K Y; dR = alpha (K Y + S^T dZ).
             // The two sums are added on the vector unit: a product of one
@@ -690,6 +683,13 @@ __global__ __launch_bounds__(64, 1) void scan_bwd_chain(BwdWalkArgs w) {
         *reinterpret_cast<f32x4*>(o + 32 * kb) = f32x4{Y[2 * kb][0], Y[2 * kb][1], Y[2 * kb][2], Y[2 * kb][3]};
         *reinterpret_cast<f32x4*>(o + 32 * kb + 4) = f32x4{Y[2 * kb + 1][0], Y[2 * kb + 1][1], Y[2 * kb + 1][2], Y[2 * kb + 1][3]};
     }
+}
+
+// The two walks do not depend on each other (the gradient walk reads K, Q
+// and dZ only): one launch runs both, the forward-state waves first.
+__global__ __launch_bounds__(64, 1) void scan_bwd_walks(BwdWalkArgs w, bf16_t* states, unsigned nstates) {
+    if (blockIdx.x < nstates) states_wave(w.s, states, w.nd, (int)blockIdx.x);
+    else grad_wave(w, (int)(blockIdx.x - nstates));
 }
 
 // Chunk-parallel scan, second pass: segment start states in order,
@@ -819,7 +819,6 @@ hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
     a.nseg = 1;
     const int nd = l.mode == 0 ? 2 : 1;
     const unsigned waves = (unsigned)(4LL * a.slices * nd);
-    hipLaunchKernelGGL(scan_states, dim3(waves), dim3(64), 0, stream, a, l.states, nd);
     BwdWalkArgs w{};
     w.s = a;
     w.Q = l.Q;
@@ -828,7 +827,7 @@ hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
     w.dRp = l.dRp;
     w.dW0c = l.dW0c;
     w.nd = nd;
-    hipLaunchKernelGGL(scan_bwd_chain, dim3(waves), dim3(64), 0, stream, w);
+    hipLaunchKernelGGL(scan_bwd_walks, dim3(2 * waves), dim3(64), 0, stream, w, l.states, waves);
     return hipGetLastError();
 }
 

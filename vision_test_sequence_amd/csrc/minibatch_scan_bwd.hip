@@ -24,9 +24,13 @@
 //   sums     per head: dW0 (the walks' final dWs) and deta over the batch
 //            and the directions, in a fixed order; with both directions
 //            the two directions' fp32 gradient planes are added.
-// fp32 arithmetic on the vector ALUs throughout (bf16 or fp32 views); the
-// serial walks prefetch the next mini-batch's rows into registers while
-// the current one is computed.
+// Two implementations.  bf16 views with b <= 16: both walks on the matrix
+// cores (minibatch_scan.hip: states and gradient states kept in bf16), the
+// outputs on the matrix cores per token block, both directions in one
+// workgroup when their mini-batches cover the same tokens (no fp32 planes).
+// Otherwise fp32 arithmetic on the vector ALUs throughout (bf16 or fp32
+// views); the serial walks prefetch the next mini-batch's rows into
+// registers while the current one is computed.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -46,8 +50,8 @@ struct SbArgs {
     const float* eta;
     float* dW0;        // [H][64][64] (or [2][H][64][64])
     float* deta;       // [H]
-    float* ws_state;   // [chains][nch][64][64]: forward start states
-    float* dwn_state;  // [chains][nch][64][64]: gradient at each mini-batch's end
+    float* ws_state;   // [chains][nch][64][64]: forward start states (fp32; bf16 from the matrix-core walks)
+    float* dwn_state;  // [chains][nch][64][64]: gradient at each mini-batch's end (likewise)
     float* dRp;        // [chains][N][64]: dR by walk position
     float* dW0c;       // [chains][64][64]
     float* detac;      // [chains][nch]
@@ -340,8 +344,219 @@ __global__ __launch_bounds__(kSbT) void sbwd_outputs(SbArgs a) {
     if (tid == 0) a.detac[(long long)c.ch * a.nch + mb] = (-2.f / (float)n) * red[0];
 }
 
+// ---- outputs on the matrix cores (bf16 views, b <= 16) ---------------------
+// One workgroup of four waves per token block, rows in token order: the
+// tokens of one mini-batch of one direction (PLANES: that direction's fp32
+// plane, the planes summed afterwards), or, when every direction's
+// mini-batches cover the same tokens (one direction, or both with N a
+// multiple of b: the reverse walk's mini-batch nch-1-c holds the forward
+// mini-batch c's tokens), all of them, summed in registers and stored once.
+// In the reverse direction walk slot s is row n-1-s, so the kept pairs
+// "s <= t" become "row_s >= row_t"; nothing else depends on the order.
+// Wave w forms output channels 16w .. 16w+15 and R's channels there.  bf16
+// operands (the states and R, P rounded), fp32 accumulation; dV = -dR in
+// fp32.  Sums of products of different matrix-core shapes are added on the
+// vector unit.
+constexpr int kMcRow = 144;          // bytes per staged 64-channel bf16 row (+16: banks)
+constexpr int kMcTile = 16 * kMcRow; // 16 token rows
+constexpr int kMcW = 64 * kMcRow;    // a 64 x 64 state
+
+__device__ __forceinline__ v4s_t tr4(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+}
+__device__ __forceinline__ u32x4 cat_tr(const v4s_t& lo, const v4s_t& hi) {
+    const u32x2 l = __builtin_bit_cast(u32x2, lo), h = __builtin_bit_cast(u32x2, hi);
+    return u32x4{l[0], l[1], h[0], h[1]};
+}
+__device__ __forceinline__ float bfe(const v4s_t& v, int i) {
+    return __uint_as_float((uint32_t)(uint16_t)v[i] << 16);
+}
+
+template <bool PLANES>
+__global__ __launch_bounds__(kSbT) void sbwd_outputs_mc(SbArgs a) {
+    __shared__ __attribute__((aligned(16))) char lds[6 * kMcTile + 2 * kMcW];
+    __shared__ float red[4];
+    char* const tK = lds;
+    char* const tQ = lds + kMcTile;
+    char* const tV = lds + 2 * kMcTile;
+    char* const tZ = lds + 3 * kMcTile; // dZ, scaled as the direction receives it
+    char* const tD = lds + 4 * kMcTile; // dR
+    char* const tR = lds + 5 * kMcTile; // R
+    char* const sW = lds + 6 * kMcTile; // Ws  [r][j]
+    char* const sG = sW + kMcW;         // dWn [r][j]
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, m = lane & 15;
+    const int e = m >> 2, aa = m & 3;
+    int slice, c, di0, ndi;
+    if (PLANES) {
+        const int ch = blockIdx.x / a.nch;
+        c = blockIdx.x % a.nch;
+        slice = ch / a.nd;
+        di0 = ch % a.nd;
+        ndi = 1;
+    } else {
+        slice = blockIdx.x / a.nch;
+        c = blockIdx.x % a.nch;
+        di0 = 0;
+        ndi = a.nd;
+    }
+    const int bb = slice / a.H, h = slice % a.H;
+    const float eta = a.eta[h];
+    const float zs = a.mode == 0 ? 0.5f : 1.f;
+    const v4f z4{0.f, 0.f, 0.f, 0.f};
+    // operand reads: a 16-row tile's row m, channels 8g.. (+32 kb) -- the
+    // A operand, and the B operand whose columns are the tile's rows;
+    // a state's rows 32kb + 8g .. +7 at channel 16w + m (B operand, k over
+    // the state's rows); a tile's rows 4g .. 4g+3 at channel 16w + m
+    auto rowop = [&](const char* t, int kb) { return *reinterpret_cast<const u32x4*>(t + m * kMcRow + 64 * kb + 16 * g); };
+    auto colop = [&](const char* st, int kb) {
+        const char* p = st + (32 * kb + 8 * g + e) * kMcRow + 2 * (16 * w + 4 * aa);
+        return cat_tr(tr4(p), tr4(p + 4 * kMcRow));
+    };
+    auto col16 = [&](const char* t) { return tr4(t + (4 * g + e) * kMcRow + 2 * (16 * w + 4 * aa)); };
+    v4f oQ = z4, oK = z4, oV = z4; // outputs at rows 4g+i, channel 16w+m
+    int tok_lo = 0, n = 0;
+    for (int p = 0; p < ndi; ++p) {
+        const int di = di0 + p, dir = chain_dir(a, di), ch = slice * a.nd + di;
+        const int mb = (!PLANES && a.nd == 2 && dir == 1) ? a.nch - 1 - c : c;
+        n = nc_of(a, mb);
+        tok_lo = dir ? a.N - mb * a.b - n : mb * a.b;
+        const float alpha = -2.f * eta / (float)n;
+        if (p > 0) __syncthreads(); // the previous pass has read every tile
+        // K, Q, V, dZ rows (zeros past n); the view is picked by value (a
+        // reference picked at run time would copy the arguments to scratch)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int q = tid + kSbT * j, t = q >> 7, r = (q >> 3) & 15, ck = q & 7;
+            const View4 v = j == 0 ? (t == 0 ? a.K : a.Q) : (t == 2 ? a.V : a.dZ);
+            u32x4 x{0u, 0u, 0u, 0u};
+            if (r < n)
+                x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(v.ptr) + bb * v.sb + h * v.sh +
+                                                    (long long)(tok_lo + r) * v.sn + 8 * ck);
+            if (t == 3)
+#pragma unroll
+                for (int k = 0; k < 4; ++k) x[k] = pack_bf2(zs * bflo(x[k]), zs * bfhi(x[k]));
+            *reinterpret_cast<u32x4*>(lds + t * kMcTile + r * kMcRow + 16 * ck) = x;
+        }
+        // dR rows (fp32, by walk position)
+        {
+            const int r = tid >> 4, c4 = tid & 15;
+            f32x4 x{0.f, 0.f, 0.f, 0.f};
+            if (r < n) {
+                const int pos = dir ? a.N - 1 - (tok_lo + r) : tok_lo + r;
+                x = *reinterpret_cast<const f32x4*>(a.dRp + ((long long)ch * a.N + pos) * 64 + 4 * c4);
+            }
+            *reinterpret_cast<u32x2*>(tD + r * kMcRow + 8 * c4) = u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
+        }
+        // Ws and dWn (bf16, stored so by the matrix-core walks)
+        {
+            const u32x4* ws = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.ws_state) +
+                                                             ((long long)ch * a.nch + mb) * 4096);
+            const u32x4* gs = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.dwn_state) +
+                                                             ((long long)ch * a.nch + mb) * 4096);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int q = tid + kSbT * j, o = (q >> 3) * kMcRow + 16 * (q & 7);
+                const u32x4 x = ws[q], y = gs[q];
+                *reinterpret_cast<u32x4*>(sW + o) = x;
+                *reinterpret_cast<u32x4*>(sG + o) = y;
+            }
+        }
+        // dV = -dR (fp32)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            if (r < n) {
+                const int pos = dir ? a.N - 1 - (tok_lo + r) : tok_lo + r;
+                oV[i] -= a.dRp[((long long)ch * a.N + pos) * 64 + 16 * w + m];
+            }
+        }
+        __syncthreads();
+        // R = K Ws^T - V at channels 16w + m (B operand: Ws row 16w+m), to LDS
+        {
+            const char* wr = sW + (16 * w + m) * kMcRow + 16 * g;
+            const v4f KW = mfma32(as_v8bf(rowop(tK, 1)), as_v8bf(*reinterpret_cast<const u32x4*>(wr + 64)),
+                                  mfma32(as_v8bf(rowop(tK, 0)), as_v8bf(*reinterpret_cast<const u32x4*>(wr)), z4));
+            const v4s_t vv = col16(tV);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<bf16_t*>(tR + (4 * g + i) * kMcRow + 2 * (16 * w + m)) = f2bf(KW[i] - bfe(vv, i));
+        }
+        __syncthreads();
+        // S = Q K^T and P = dZ R^T at (t = 4g+i, s = m); P^T at (s = 4g+i, t = m)
+        const v4f S = mfma32(as_v8bf(rowop(tQ, 1)), as_v8bf(rowop(tK, 1)), mfma32(as_v8bf(rowop(tQ, 0)), as_v8bf(rowop(tK, 0)), z4));
+        const v4f P = mfma32(as_v8bf(rowop(tZ, 1)), as_v8bf(rowop(tR, 1)), mfma32(as_v8bf(rowop(tZ, 0)), as_v8bf(rowop(tR, 0)), z4));
+        const v4f Pt = mfma32(as_v8bf(rowop(tR, 1)), as_v8bf(rowop(tZ, 1)), mfma32(as_v8bf(rowop(tR, 0)), as_v8bf(rowop(tZ, 0)), z4));
+        float kp[4], kt[4]; // kept pairs: P layout (t = 4g+i, s = m), P^T layout (t = m, s = 4g+i)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            kp[i] = (dir ? m >= r : m <= r) ? 1.f : 0.f;
+            kt[i] = (dir ? r >= m : r <= m) ? 1.f : 0.f;
+        }
+        const u32x2 Pk{pack_bf2(kp[0] * P[0], kp[1] * P[1]), pack_bf2(kp[2] * P[2], kp[3] * P[3])};
+        const u32x2 Ptk{pack_bf2(kt[0] * Pt[0], kt[1] * Pt[1]), pack_bf2(kt[2] * Pt[2], kt[3] * Pt[3])};
+        // the state operands, k over r, at channel 16w + m
+        const u32x4 W0b = colop(sW, 0), W1b = colop(sW, 1), G0b = colop(sG, 0), G1b = colop(sG, 1);
+        const v4s_t kc = col16(tK), qc = col16(tQ);
+        // dQ = dZ Ws + alpha P_kept K
+        const v4f q1 = mfma32(as_v8bf(rowop(tZ, 1)), as_v8bf(W1b), mfma32(as_v8bf(rowop(tZ, 0)), as_v8bf(W0b), z4));
+        const v4f q2 = mfma16(as_v4s(Ptk), kc, z4);
+        // dK = dR Ws + alpha (R dWn + P_kept^T Q)
+        const v4f k1 = mfma32(as_v8bf(rowop(tD, 1)), as_v8bf(W1b), mfma32(as_v8bf(rowop(tD, 0)), as_v8bf(W0b), z4));
+        const v4f k2 = mfma32(as_v8bf(rowop(tR, 1)), as_v8bf(G1b), mfma32(as_v8bf(rowop(tR, 0)), as_v8bf(G0b), z4));
+        const v4f k3 = mfma16(as_v4s(Pk), qc, z4);
+        // d(alpha) = <R dWn, K> + <P_kept, S>
+        float dal = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            oQ[i] += q1[i] + alpha * q2[i];
+            oK[i] += k1[i] + alpha * (k2[i] + k3[i]);
+            dal = fmaf(k2[i], bfe(kc, i), dal);
+            if (w == 0) dal = fmaf(kp[i] * P[i], S[i], dal);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) dal += __shfl_xor(dal, o);
+        if (lane == 0) red[w] = dal;
+        __syncthreads();
+        if (tid == 0) a.detac[(long long)ch * a.nch + mb] = (-2.f / (float)n) * (((red[0] + red[1]) + red[2]) + red[3]);
+    }
+    if (PLANES) {
+        const long long pl = (long long)a.B * a.H * a.N * 64;
+        float* pb = a.planes + (long long)di0 * 3 * pl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * g + i;
+            if (r < n) {
+                const long long o = ((long long)slice * a.N + tok_lo + r) * 64 + 16 * w + m;
+                pb[o] = oQ[i];
+                pb[pl + o] = oK[i];
+                pb[2 * pl + o] = oV[i];
+            }
+        }
+        return;
+    }
+    // bf16 rows through LDS (the tiles are free once every wave is past the
+    // d(alpha) barrier), stored 16 bytes a thread
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int o = (4 * g + i) * kMcRow + 2 * (16 * w + m);
+        *reinterpret_cast<bf16_t*>(tK + o) = f2bf(oQ[i]);
+        *reinterpret_cast<bf16_t*>(tQ + o) = f2bf(oK[i]);
+        *reinterpret_cast<bf16_t*>(tV + o) = f2bf(oV[i]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int q = tid + kSbT * j, t = q >> 7, r = (q >> 3) & 15, ck = q & 7;
+        if (q >= 3 * 128 || r >= n) continue;
+        const View4 v = j == 0 ? (t == 0 ? a.dQ : a.dK) : a.dV;
+        *reinterpret_cast<u32x4*>(reinterpret_cast<bf16_t*>(v.ptr) + bb * v.sb + h * v.sh + (long long)(tok_lo + r) * v.sn +
+                                  8 * ck) = *reinterpret_cast<const u32x4*>(lds + t * kMcTile + r * kMcRow + 16 * ck);
+    }
+}
+
 // ---- sums ------------------------------------------------------------------
-// dW0 and deta per head: chains in (b, direction) order, mini-batches in order.
+// dW0 and deta per head, in fixed orders (dW0: chains in (b, direction) order).
 __global__ __launch_bounds__(kSbT) void sbwd_sums(SbArgs a) {
     const int h = blockIdx.x / 16, part = blockIdx.x % 16, tid = threadIdx.x;
     const int ndw = a.w0dir ? 2 : 1;
@@ -356,14 +571,23 @@ __global__ __launch_bounds__(kSbT) void sbwd_sums(SbArgs a) {
             }
         a.dW0[((long long)wd * a.H + h) * 4096 + e] = s;
     }
-    if (part == 0 && tid == 0) {
+    if (part == 0) {
+        // thread t sums mini-batches t, t + 256, ... of every chain of the
+        // head (chains in (b, direction) order), then a fixed tree
+        __shared__ float red[kSbT];
         float s = 0.f;
         for (int bb = 0; bb < a.B; ++bb)
             for (int di = 0; di < a.nd; ++di) {
-                const long long ch = ((long long)bb * a.H + h) * a.nd + di;
-                for (int mb = 0; mb < a.nch; ++mb) s += a.detac[ch * a.nch + mb];
+                const float* d = a.detac + (((long long)bb * a.H + h) * a.nd + di) * a.nch;
+                for (int mb = tid; mb < a.nch; mb += kSbT) s += d[mb];
             }
-        a.deta[h] = s;
+        red[tid] = s;
+        __syncthreads();
+        for (int o = kSbT / 2; o > 0; o >>= 1) {
+            if (tid < o) red[tid] += red[tid + o];
+            __syncthreads();
+        }
+        if (tid == 0) a.deta[h] = red[0];
     }
 }
 
@@ -425,12 +649,18 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& s, hipStream_t stream) {
     a.planes = a.nd == 2 ? (float*)w : nullptr;
     const dim3 block(kSbT);
     const dim3 walks((unsigned)(chains * 4)), per_mb((unsigned)(chains * a.nch));
+    // matrix-core outputs: one workgroup per token block covers every
+    // direction when the directions' mini-batches coincide
+    const bool fused = a.nd == 1 || s.N % s.b == 0;
     if (a.bf16) {
         if (s.walks) {
             ScanBwdWalks wk{};
             wk.K = s.K; wk.Q = s.Q; wk.V = s.V; wk.dZ = s.dZ;
             wk.W0 = s.W0; wk.eta = s.eta;
-            wk.states = a.ws_state; wk.dwn = a.dwn_state; wk.dRp = a.dRp; wk.dW0c = a.dW0c;
+            // bf16 states in the first half of the fp32 state buffers
+            wk.states = reinterpret_cast<uint16_t*>(a.ws_state);
+            wk.dwn = reinterpret_cast<uint16_t*>(a.dwn_state);
+            wk.dRp = a.dRp; wk.dW0c = a.dW0c;
             wk.B = s.B; wk.H = s.H; wk.N = s.N; wk.b = s.b; wk.mode = s.mode; wk.w0dir = s.w0dir;
             const hipError_t e = launch_scan_bwd_walks(wk, stream);
             if (e != hipSuccess) return e;
@@ -438,14 +668,16 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& s, hipStream_t stream) {
             hipLaunchKernelGGL(sbwd_states<true>, walks, block, 0, stream, a);
             hipLaunchKernelGGL(sbwd_chain<true>, walks, block, 0, stream, a);
         }
-        hipLaunchKernelGGL(sbwd_outputs<true>, per_mb, block, 0, stream, a);
+        if (!s.walks) hipLaunchKernelGGL(sbwd_outputs<true>, per_mb, block, 0, stream, a);
+        else if (fused) hipLaunchKernelGGL(sbwd_outputs_mc<false>, dim3((unsigned)(slices * a.nch)), block, 0, stream, a);
+        else hipLaunchKernelGGL(sbwd_outputs_mc<true>, per_mb, block, 0, stream, a);
     } else {
         hipLaunchKernelGGL(sbwd_states<false>, walks, block, 0, stream, a);
         hipLaunchKernelGGL(sbwd_chain<false>, walks, block, 0, stream, a);
         hipLaunchKernelGGL(sbwd_outputs<false>, per_mb, block, 0, stream, a);
     }
     hipLaunchKernelGGL(sbwd_sums, dim3((unsigned)(s.H * 16)), block, 0, stream, a);
-    if (a.nd == 2) {
+    if (a.nd == 2 && !(a.bf16 && s.walks && fused)) {
         const long long n = 3LL * slices * s.N * 64;
         const dim3 g((unsigned)((n + kSbT - 1) / kSbT));
         if (a.bf16) hipLaunchKernelGGL(sbwd_planes<true>, g, block, 0, stream, a);
