@@ -255,8 +255,8 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
  *   z_t = W_t q_t,  and after the batch Ws <- W_last.
  * Both directions start from W0.  TTT_BIDIR_AVG writes
  * Z = (Z_forward + Z_reverse)/2; the other modes write one direction.
- * b: any value in [1, 16], a multiple of 16, or b >= N (one mini-batch);
- * other values return TTT_ERR_UNSUPPORTED.
+ * b: any value >= 1 (b >= N is one mini-batch: the full-batch step's
+ * gradients, applied causally).
  * When the chains (slice x direction) would leave most compute units idle,
  * each chain is cut into segments that run in parallel (chunk-parallel
  * scan: over a mini-batch the state update is affine, W <- W M + U, so the

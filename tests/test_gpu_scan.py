@@ -183,13 +183,16 @@ def test_one_minibatch_of_all_tokens_is_the_full_batch_step():
     assert slice_rel_err(f64(Zb[:, :, :1]), Zf[:, :, :1]) <= TOL["bf16"]
 
 
-def test_minibatch_sizes_the_kernel_does_not_take():
-    import vision_test_sequence_amd as vt
-    from vision_test_sequence_amd.binding import TTTError
-    banner("scan b = 20 (not a multiple of 16, below N) -> unsupported")
-    K, Q, V, W0, eta = _on(wl.draw(1, 1, 100, seed=1520, dtype="bf16"))
-    with pytest.raises(TTTError, match="UNSUPPORTED"):
-        vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 20, BIDIR)
+@pytest.mark.parametrize("N,b", [(196, 20), (196, 49), (196, 98), (196, 195), (300, 17), (1000, 33),
+                                 (2003, 100), (40, 20)])
+@pytest.mark.parametrize("mode", [BIDIR, FWD, BWD])
+def test_ragged_minibatches(N, b, mode):
+    # b > 16 and not a multiple of 16: each mini-batch ends in a partial
+    # 16-token tile, and the two directions' mini-batch boundaries differ
+    # unless N is a multiple of b (the b-sweep's b = 49 and 98 at N = 196)
+    banner(f"scan ragged mini-batches N={N} b={b} mode={mode}")
+    inp = wl.draw(2, 3, N, seed=1530 + N + b + mode, dtype="bf16", unit_rows=True, eta_fixed=None)
+    _check(*_on(inp), b, mode)
 
 
 def _forced_segments(n):
@@ -201,7 +204,7 @@ def _forced_segments(n):
 
 
 @pytest.mark.parametrize("N,b,mode", [(2000, 16, BIDIR), (1001, 7, FWD), (1001, 7, BWD), (3000, 32, BIDIR),
-                                      (640, 1, BIDIR), (999, 48, FWD)])
+                                      (640, 1, BIDIR), (999, 48, FWD), (1500, 20, BIDIR), (999, 37, BWD)])
 @pytest.mark.parametrize("segs", [1, 2, 3, 5, 8])
 def test_chunk_parallel_segments(N, b, mode, segs):
     # the chunk-parallel scan (segment maps [M | U] walked from [I | 0], start

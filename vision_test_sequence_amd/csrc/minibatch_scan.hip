@@ -142,6 +142,32 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* base, lo
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice span
+// Ragged mini-batches (RG: b > 16, not a multiple of 16, b < N): tile j is
+// sub-tile s = j % T of mini-batch c = j / T and holds walk positions
+// c b + 16 s .. +15, of which those below the mini-batch's count n_c are
+// tokens.  A cursor (c, s) over the walk's tiles replaces the fixed
+// offset step of the uniform walks.
+struct TileCur {
+    int c, s;
+};
+__device__ __forceinline__ void cur_next(TileCur& t, int T) {
+    if (++t.s == T) {
+        t.s = 0;
+        ++t.c;
+    }
+}
+// This lane's buffer offset for slot m of the cursor's tile (row stride
+// sn bytes, lane_bytes within the row), or kOffSlice for an empty slot.
+template <typename A>
+__device__ __forceinline__ unsigned cur_off(const A& a, const Walk& L, const TileCur& t, long long sn,
+                                            unsigned lane_bytes) {
+    const int nc = min(a.b, L.N - t.c * a.b);
+    const int q = 16 * t.s + L.m;
+    if (q >= nc) return kOffSlice;
+    const long long pos = (long long)t.c * a.b + q;
+    const long long tok = L.dir ? L.N - 1 - pos : pos;
+    return (unsigned)(tok * sn) + lane_bytes;
+}
 
 // ------------------------------------------------------------ chain wave --
 // K, V: the slice's token 0, channel 0; Ksn, Vsn: token strides in bytes.
@@ -152,7 +178,7 @@ constexpr unsigned kOffSlice = 0x80000000u; // an offset outside every slice spa
 // states (MAP walks only; may be null): every mini-batch's start state is
 // stored there in bf16 (the precision the backward's products take it in),
 // transposed like Ws, 4096 values per mini-batch.
-template <int D, bool MAP>
+template <int D, bool MAP, bool RG = false>
 __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, const char* V, long long Ksn,
                            long long Vsn, const float* Ws, float eta, char* lds, bool vzero = false,
                            float* out = nullptr, bf16_t* states = nullptr) {
@@ -185,8 +211,13 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
     const int ch = 16 * L.rt + 4 * g; // this lane's V channels
     const __amdgpu_buffer_rsrc_t krs = span_rsrc(K, (long long)(L.N - 1) * Ksn + 128);
     const __amdgpu_buffer_rsrc_t vrs = span_rsrc(V, (long long)(L.N - 1) * Vsn + 128);
+    TileCur icur{L.mb0, 0}; // RG: the next tile to issue
     unsigned koff = slot ? (unsigned)(p0 * Ksn + 16 * g) : kOffSlice;
     unsigned voff = slot && !vzero ? (unsigned)(p0 * Vsn + 2 * ch) : kOffSlice;
+    if constexpr (RG) {
+        koff = cur_off(a, L, icur, Ksn, 16 * g);
+        voff = vzero ? kOffSlice : cur_off(a, L, icur, Vsn, 2 * ch);
+    }
     const unsigned kst = slot ? (unsigned)(L.step * Ksn) : 0u, vst = slot && !vzero ? (unsigned)(L.step * Vsn) : 0u;
     struct Regs {
         u32x4 k[2];
@@ -196,8 +227,14 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
         r.k[0] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff, 0, 0);
         r.k[1] = __builtin_amdgcn_raw_buffer_load_b128(krs, koff + 64u, 0, 0);
         r.v = __builtin_amdgcn_raw_buffer_load_b64(vrs, voff, 0, 0);
-        koff += kst;
-        voff += vst;
+        if constexpr (RG) {
+            cur_next(icur, a.T);
+            koff = cur_off(a, L, icur, Ksn, 16 * g);
+            voff = vzero ? kOffSlice : cur_off(a, L, icur, Vsn, 2 * ch);
+        } else {
+            koff += kst;
+            voff += vst;
+        }
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(cr[u]);
@@ -310,7 +347,7 @@ __device__ void chain_wave(const ScanArgs& a, const Walk& L, const char* K, cons
 // ----------------------------------------------------------- output wave --
 // Q, Z (or P, this direction's [N][64] fp32 rows): the slice's token 0,
 // channel 0; Qsn, Zsn: token strides in bytes.
-template <int D>
+template <int D, bool RG = false>
 __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, long long Qsn, char* Z,
                             long long Zsn, float* P, const char* lds) {
     const int g = L.g, m = L.m, lane = 16 * g + m;
@@ -323,7 +360,9 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     const bool slot = L.m < L.b;
     const long long p0 = token_of(L, L.j0 * L.b + m);
     const __amdgpu_buffer_rsrc_t qrs = span_rsrc(Q, (long long)(L.N - 1) * Qsn + 128);
+    TileCur icur{L.mb0, 0}, zcur{L.mb0, 0}; // RG: the next tile to issue / to store
     unsigned qoff = slot ? (unsigned)(p0 * Qsn + 16 * g) : kOffSlice;
+    if constexpr (RG) qoff = cur_off(a, L, icur, Qsn, 16 * g);
     const unsigned qst = slot ? (unsigned)(L.step * Qsn) : 0u;
     struct Regs {
         u32x4 q[2];
@@ -331,7 +370,12 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
     auto issue = [&](Regs& r) __attribute__((always_inline)) {
         r.q[0] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff, 0, 0);
         r.q[1] = __builtin_amdgcn_raw_buffer_load_b128(qrs, qoff + 64u, 0, 0);
-        qoff += qst;
+        if constexpr (RG) {
+            cur_next(icur, a.T);
+            qoff = cur_off(a, L, icur, Qsn, 16 * g);
+        } else {
+            qoff += qst;
+        }
     };
 #pragma unroll
     for (int u = 0; u < D; ++u) issue(cr[u]);
@@ -345,6 +389,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
                                                : span_rsrc(Z, (long long)(L.N - 1) * Zsn + 128);
     const long long zsn = a.split ? 256 : Zsn;
     unsigned zoff = slot ? (unsigned)(p0 * zsn + (a.split ? 4 : 2) * ch) : kOffSlice;
+    if constexpr (RG) zoff = cur_off(a, L, zcur, zsn, (a.split ? 4 : 2) * ch);
     const unsigned zst = slot ? (unsigned)(L.step * zsn) : 0u;
     int left = L.nch; // tiles of the walk still to store (a segment ends before the slice does)
     const int nsteps = ((L.nch + D - 1) / D) * D;
@@ -385,7 +430,12 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
                 __builtin_amdgcn_raw_buffer_store_b64(zv, zrs, zo, 0, 2 /* nt */);
             }
             asm volatile("" ::: "memory"); // stores of chunk j before the loads of chunk j + D
-            zoff += zst;
+            if constexpr (RG) {
+                cur_next(zcur, a.T);
+                zoff = cur_off(a, L, zcur, zsn, (a.split ? 4 : 2) * ch);
+            } else {
+                zoff += zst;
+            }
             issue(r);
         }
     }
@@ -397,7 +447,7 @@ __device__ void output_wave(const ScanArgs& a, const Walk& L, const char* Q, lon
 // than half a CU's LDS, so no two share a CU -- used when the grid fits the
 // device one workgroup per CU (two chains on one CU share its SIMDs: 127
 // against 121 us at 1280x1280).
-template <bool Spread>
+template <bool Spread, bool RG>
 __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[Spread ? kOneCuLds : kDirLds];
     const int dsplit = a.split && (int)blockIdx.x >= a.blocks ? 1 : 0;
@@ -434,12 +484,12 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
         // given per direction), segment s from the state the maps gave it
         const float* Ws = seg == 0 ? a.W0 + ((a.w0dir && L.dir ? (long long)a.H : 0) + h) * 4096
                                    : a.starts + ((long long)(dsplit * a.slices + ss.slice) * a.nseg + seg) * 4096;
-        chain_wave<kPre, false>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, Ws, a.eta[h], lds);
+        chain_wave<kPre, false, RG>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, Ws, a.eta[h], lds);
     } else {
         const char* Q = (const char*)a.Q.ptr + (bb * a.Q.sb + h * a.Q.sh) * 2;
         char* Z = (char*)a.Z.ptr + (bb * a.Z.sb + h * a.Z.sh) * 2;
         float* P = a.split ? (dsplit ? a.P2 : a.P) + (long long)ss.slice * a.N * 64 : nullptr;
-        output_wave<kPre>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
+        output_wave<kPre, RG>(a, L, Q, a.Q.sn * 2, Z, a.Z.sn * 2, P, lds);
     }
 }
 
@@ -451,6 +501,7 @@ __global__ __launch_bounds__(128, 1) void scan_kernel(ScanArgs a) {
 // gives both.  One wave per (chain, segment, 16-column block of [M | U]):
 // blocks 0-3 the columns of M, blocks 4-7 those of U.  Stored transposed
 // (S_M = M^T, S_U = U^T), so that W_end = W_start S_M + S_U.
+template <bool RG>
 __global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[kNK * kKBuf + 2 * kVBuf];
     // unit = (slice, segment but the last), 8 column blocks of [M | U] each
@@ -479,7 +530,7 @@ __global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
     const char* K = (const char*)a.K.ptr + (bb * a.K.sb + h * a.K.sh) * 2;
     const char* V = (const char*)a.V.ptr + (bb * a.V.sb + h * a.V.sh) * 2;
     float* out = a.maps + (((long long)(dsplit * a.slices + ss.slice) * (a.nseg - 1) + seg) * 2 + (blk >> 2)) * 4096;
-    chain_wave<kPre, true>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, nullptr, a.eta[h], lds, blk < 4, out);
+    chain_wave<kPre, true, RG>(a, L, K, V, a.K.sn * 2, a.V.sn * 2, nullptr, a.eta[h], lds, blk < 4, out);
 }
 
 // ------------------------------------------------ backward: forward states --
@@ -801,7 +852,7 @@ size_t scan_ws_bytes(int B, int H, int N, int mode) {
     return bytes;
 }
 
-bool scan_minibatch_supported(int b, int N) { return b >= 1 && (b <= 16 || b % 16 == 0 || b >= N); }
+bool scan_minibatch_supported(int b, int N) { return b >= 1 && N >= 0; }
 
 hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
     if (l.b < 1 || l.b > 16) return hipErrorNotSupported;
@@ -840,10 +891,13 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
     a.H = s.H; a.N = s.N; a.b = s.b;
     a.nch = (s.N + s.b - 1) / s.b;
     // tiles: a mini-batch of b <= 16 tokens is one tile; a larger one is
-    // ceil(min(b, N) / 16) tiles of 16 (b a multiple of 16, or b >= N)
+    // T = ceil(min(b, N) / 16) tiles of 16 positions, the last of them
+    // ragged unless b is a multiple of 16 (or b >= N: one mini-batch)
     a.tb = s.b <= 16 ? s.b : 16;
     a.T = s.b <= 16 ? 1 : (std::min(s.b, s.N) + 15) / 16;
-    a.ntile = (s.N + a.tb - 1) / a.tb;
+    const int nlast = s.N - (a.nch - 1) * s.b;
+    a.ntile = (a.nch - 1) * a.T + (nlast + a.tb - 1) / a.tb;
+    const bool rg = s.b > 16 && s.b % 16 != 0 && s.b < s.N;
     a.slices = s.B * s.H;
     a.mode = s.mode;
     // both directions: each in workgroups of its own, fp32 outputs averaged
@@ -867,12 +921,19 @@ hipError_t launch_scan(ScanLaunch s, hipStream_t stream) {
         a.maps = cur;
         a.starts = cur + (size_t)chains * (kMaxSeg - 1) * 2 * 4096;
         const long long mblocks = ((long long)a.slices * (a.nseg - 1) + 7) / 8 * 8 * 8;
-        hipLaunchKernelGGL(scan_maps, dim3((unsigned)(dirs * mblocks)), dim3(64), 0, stream, a);
+        if (rg) hipLaunchKernelGGL(scan_maps<true>, dim3((unsigned)(dirs * mblocks)), dim3(64), 0, stream, a);
+        else hipLaunchKernelGGL(scan_maps<false>, dim3((unsigned)(dirs * mblocks)), dim3(64), 0, stream, a);
         hipLaunchKernelGGL(scan_starts, dim3((unsigned)(4 * chains)), dim3(256), 0, stream, a);
     }
     const long long grid = blocks * dirs;
-    if (grid <= s.cus) hipLaunchKernelGGL(scan_kernel<true>, dim3((unsigned)grid), dim3(128), 0, stream, a);
-    else hipLaunchKernelGGL(scan_kernel<false>, dim3((unsigned)grid), dim3(128), 0, stream, a);
+    const dim3 gd((unsigned)grid), bd(128);
+    if (grid <= s.cus) {
+        if (rg) hipLaunchKernelGGL((scan_kernel<true, true>), gd, bd, 0, stream, a);
+        else hipLaunchKernelGGL((scan_kernel<true, false>), gd, bd, 0, stream, a);
+    } else {
+        if (rg) hipLaunchKernelGGL((scan_kernel<false, true>), gd, bd, 0, stream, a);
+        else hipLaunchKernelGGL((scan_kernel<false, false>), gd, bd, 0, stream, a);
+    }
     if (a.split) {
         const long long n = (long long)a.slices * s.N * 8;
         hipLaunchKernelGGL(scan_average, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, a);
