@@ -661,6 +661,7 @@ ttt_status ttt_linear_minibatch_bidir_bwd(const ttt_problem* p, ttt_view K, ttt_
     for (const ttt_view* v : {&K, &Q, &V, &dZ})
         if ((int64_t)(p->N + 512) * std::max<int64_t>(v->stride_n, p->d) * 2 >= ((int64_t)1 << 31)) spans = false;
     a.walks = a.bf16 && p->minibatch <= 16 && spans && !getenv("TTT_SCAN_BWD_VECTOR_WALKS") ? 1 : 0;
+    a.cus = device_cus();
     if (p->N == 1 && a.walks) {
         // one-token views may carry any stride_n (see the forward scan)
         for (View4* w : {&a.K, &a.Q, &a.V, &a.dZ}) w->sn = std::max<long long>(w->sn, p->d);

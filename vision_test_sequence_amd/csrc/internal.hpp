@@ -131,6 +131,7 @@ struct ScanBwdLaunch {
     float* deta;
     int B, H, N, b, mode, w0dir, bf16;
     int walks;        // the serial walks on the matrix cores (bf16, b <= 16, 32-bit row offsets)
+    int cus;          // compute units of the device
     void* ws;         // scan_bwd_ws_bytes(...) bytes
 };
 // The backward's two serial walks on the matrix cores (bf16 views, b <= 16):
@@ -146,6 +147,7 @@ struct ScanBwdWalks {
     float* dRp;       // [chains][N][64]
     float* dW0c;      // [chains][64][64]
     int B, H, N, b, mode, w0dir;
+    int cus;          // compute units of the device
 };
 hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream);
 bool scan_bwd_supported(int b);

@@ -540,7 +540,11 @@ __global__ __launch_bounds__(64, 1) void scan_maps(ScanArgs a) {
 // direction index.
 __device__ __forceinline__ void states_wave(const ScanArgs& a, bf16_t* states, int nd, int wid) {
     __shared__ __attribute__((aligned(16))) char lds[kNK * kKBuf + 2 * kVBuf];
-    const int ch = wid >> 2, rt = wid & 3;
+    // the four column blocks of a chain on one XCD, whose L2 serves their
+    // common K rows once (wid: the XCD-aware block index)
+    const SliceSplit cs = map_block(wid, 4, 1);
+    if (cs.slice >= a.slices * nd) return; // padding of the XCD-aware grid
+    const int ch = cs.slice, rt = cs.split;
     const int slice = ch / nd, di = ch % nd;
     const int lane = threadIdx.x & 63;
     Walk L;
@@ -587,7 +591,10 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
     const ScanArgs& a = w.s;
     // two sets of buffers, alternating mini-batches (kBD is even)
     __shared__ __attribute__((aligned(16))) char lds[2 * (2 * kKBuf + kVBuf)];
-    const int ch = wid >> 2, rb = wid & 3;
+    // the four row blocks of a chain on one XCD (see states_wave)
+    const SliceSplit cs = map_block(wid, 4, 1);
+    if (cs.slice >= a.slices * w.nd) return; // padding of the XCD-aware grid
+    const int ch = cs.slice, rb = cs.split;
     const int slice = ch / w.nd, di = ch % w.nd;
     const int dir = a.mode == 2 ? 1 : (a.mode == 0 ? di : 0);
     const int lane = threadIdx.x & 63, g = lane >> 4, m = lane & 15;
@@ -690,19 +697,21 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb) *reinterpret_cast<u32x4*>(o + 32 * kb) = ys[kb];
             }
-            // S = Q K^T (lane: S[4g+i][m]); S^T dZ; K Y; dR = alpha (K Y + S^T dZ).
-            // The two sums are added on the vector unit: a product of one
-            // matrix-core shape accumulating onto the result of another shape
-            // issued just before it read that result before it was complete
-            // (the compiler puts no wait between them when the registers
-            // coincide exactly).
+            // S = Q K^T (lane: S[4g+i][m]); dR = alpha (S^T dZ + K Y), all on
+            // 16x16x32 products chained through one accumulator: S^T dZ has
+            // only 16 tokens, so its k slots 8g+4 .. 8g+7 are zero (the
+            // slots 8g .. 8g+3 take token 4g+i: the kept S^T of the lane's
+            // accumulator, dZ of the transposed read), then K Y over the 64
+            // channels.  (One product shape only: a 16x16x16 result chained
+            // into a 16x16x32 accumulator is read before it is complete.)
             const v4f zero4{0.f, 0.f, 0.f, 0.f};
             const v4f S = mfma32(as_v8bf(r.q[1]), as_v8bf(r.k[1]), mfma32(as_v8bf(r.q[0]), as_v8bf(r.k[0]), zero4));
-            const u32x2 sb2{pack_bf2(S[0], S[1]) & keep[0], pack_bf2(S[2], S[3]) & keep[1]};
-            const v4f SdZ = mfma16(as_v4s(sb2), zin, zero4);
-            const v4f KY = mfma32(as_v8bf(r.k[1]), as_v8bf(ys[1]), mfma32(as_v8bf(r.k[0]), as_v8bf(ys[0]), zero4));
-            const v4f dR{alpha * (KY[0] + SdZ[0]), alpha * (KY[1] + SdZ[1]), alpha * (KY[2] + SdZ[2]),
-                         alpha * (KY[3] + SdZ[3])};
+            const u32x2 zb = __builtin_bit_cast(u32x2, zin);
+            const u32x4 sA{pack_bf2(S[0], S[1]) & keep[0], pack_bf2(S[2], S[3]) & keep[1], 0u, 0u};
+            const u32x4 zB{zb[0], zb[1], 0u, 0u};
+            const v4f KY = mfma32(as_v8bf(r.k[1]), as_v8bf(ys[1]),
+                                  mfma32(as_v8bf(r.k[0]), as_v8bf(ys[0]), mfma32(as_v8bf(sA), as_v8bf(zB), zero4)));
+            const v4f dR{alpha * KY[0], alpha * KY[1], alpha * KY[2], alpha * KY[3]};
             // dR by walk position (token slot 4g+i of mini-batch c, channel 16 rb + m)
             if (live) {
                 const int n = c == nch - 1 ? N - (nch - 1) * b : b;
@@ -714,9 +723,16 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
             // the next mini-batch's operands, one step ahead of their use
             v4s_t ktN[4], qtN[4], zN;
             stage(cr[(u + 1) % kBD], (u + 1) & 1, ktN, qtN, zN);
-            // Y += K^T dR + Q^T dZ
+            // Y += K^T dR + Q^T dZ as one 16x16x32 product per tile: k slots
+            // 8g .. 8g+3 are token 4g+i of the K^T dR term, 8g+4 .. 8g+7 the
+            // same token of the Q^T dZ term (the lane holds both operand
+            // pieces already: the transposed reads and dR, dZ of slot 4g+i)
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) Y[ct] = mfma16(qtA[ct], zin, mfma16(ktA[ct], as_v4s(dr2), Y[ct]));
+            for (int ct = 0; ct < 4; ++ct) {
+                const u32x2 ka = __builtin_bit_cast(u32x2, ktA[ct]), qa = __builtin_bit_cast(u32x2, qtA[ct]);
+                const u32x4 A{ka[0], ka[1], qa[0], qa[1]}, B{dr2[0], dr2[1], zb[0], zb[1]};
+                Y[ct] = mfma32(as_v8bf(A), as_v8bf(B), Y[ct]);
+            }
             issue(r);
 #pragma unroll
             for (int ct = 0; ct < 4; ++ct) {
@@ -737,11 +753,22 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
 }
 
 // The two walks do not depend on each other (the gradient walk reads K, Q
-// and dZ only): one launch runs both, the forward-state waves first.
-__global__ __launch_bounds__(64, 1) void scan_bwd_walks(BwdWalkArgs w, bf16_t* states, unsigned nstates) {
-    if (blockIdx.x < nstates) states_wave(w.s, states, w.nd, (int)blockIdx.x);
-    else grad_wave(w, (int)(blockIdx.x - nstates));
+// and dZ only): one workgroup per (chain, 16-row block) runs both, wave 0
+// the forward states, wave 1 the gradient walk, on two SIMDs of one CU.
+// Spread: the workgroup takes more than half a CU's LDS, so no two share a
+// CU (used when the grid fits the device one workgroup per CU; single-wave
+// workgroups of the two walks packed onto shared SIMDs ran 252 us against
+// 88 + 179 us apart).
+constexpr int kWalksLds = kNK * kKBuf + 2 * kVBuf + 2 * (2 * kKBuf + kVBuf); // the two waves' own LDS
+template <bool Spread>
+__global__ __launch_bounds__(128, 1) void scan_bwd_walks(BwdWalkArgs w, bf16_t* states) {
+    __shared__ char spread[Spread ? kOneCuLds - kWalksLds : 16];
+    if (threadIdx.x == 0) asm volatile("" ::"v"(spread)); // kept: it only reserves LDS
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (wave == 0) states_wave(w.s, states, w.nd, (int)blockIdx.x);
+    else grad_wave(w, (int)blockIdx.x);
 }
+static_assert(kWalksLds < kOneCuLds, "backward walks LDS");
 
 // Chunk-parallel scan, second pass: segment start states in order,
 // W_s = W_{s-1} S_M(s-1) + S_U(s-1), W_0 = W0 (fp32 matrix cores, 16x16x4
@@ -869,7 +896,8 @@ hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
     a.mode = l.mode;
     a.nseg = 1;
     const int nd = l.mode == 0 ? 2 : 1;
-    const unsigned waves = (unsigned)(4LL * a.slices * nd);
+    // chains padded to whole XCD groups, 4 row blocks each
+    const unsigned blocks = (unsigned)(((4LL * a.slices * nd + 31) / 32) * 32);
     BwdWalkArgs w{};
     w.s = a;
     w.Q = l.Q;
@@ -878,7 +906,8 @@ hipError_t launch_scan_bwd_walks(const ScanBwdWalks& l, hipStream_t stream) {
     w.dRp = l.dRp;
     w.dW0c = l.dW0c;
     w.nd = nd;
-    hipLaunchKernelGGL(scan_bwd_walks, dim3(2 * waves), dim3(64), 0, stream, w, l.states, waves);
+    if ((int)blocks <= l.cus) hipLaunchKernelGGL(scan_bwd_walks<true>, dim3(blocks), dim3(128), 0, stream, w, l.states);
+    else hipLaunchKernelGGL(scan_bwd_walks<false>, dim3(blocks), dim3(128), 0, stream, w, l.states);
     return hipGetLastError();
 }
 

@@ -662,6 +662,7 @@ hipError_t launch_scan_bwd(const ScanBwdLaunch& s, hipStream_t stream) {
             wk.dwn = reinterpret_cast<uint16_t*>(a.dwn_state);
             wk.dRp = a.dRp; wk.dW0c = a.dW0c;
             wk.B = s.B; wk.H = s.H; wk.N = s.N; wk.b = s.b; wk.mode = s.mode; wk.w0dir = s.w0dir;
+            wk.cus = s.cus;
             const hipError_t e = launch_scan_bwd_walks(wk, stream);
             if (e != hipSuccess) return e;
         } else {
