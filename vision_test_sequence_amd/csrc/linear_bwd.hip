@@ -341,11 +341,13 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_prep(BwdArgs a) {
 }
 
 // dQ = dZ W1 and the split's dW1 = dZ^T Q with the split's dZ and Q rows
-// (kP1Tok tokens) resident in LDS, staged by direct-to-LDS loads with the
-// swz_tr swizzle; the first half is processed while the second lands.
-// dW1 by row ownership: wave w accumulates rows 16w.. over every token (dZ
-// block w against all Q blocks, transposed reads), so the waves add
-// nothing up; each stores its rows of the split's share.
+// staged in LDS chunk by chunk (kP1Tok tokens each) by direct-to-LDS loads
+// with the swz_tr swizzle; in each chunk the first half is processed while
+// the second lands.  dW1 by row ownership: wave w accumulates rows 16w..
+// over every token of the split (dZ block w against all Q blocks,
+// transposed reads), so the waves add nothing up; each stores its rows of
+// the split's share.  Several chunks per split keep the shares (and the
+// reduce's reads of them) few.
 __global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[2 * kP1Tok * 128];
     char* Zs = lds;
@@ -355,91 +357,105 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
     const int slice = blockIdx.x / a.S, split = blockIdx.x % a.S;
     if (slice >= a.B * a.H) return;
     const int b = slice / a.H, h = slice % a.H;
-    const int t0 = min(a.N, split * a.per), t1 = min(a.N, t0 + a.per), T = t1 - t0;
+    const int s0 = min(a.N, split * a.per), s1 = min(a.N, s0 + a.per);
     const char* Zp = (const char*)a.X0.ptr + (b * a.X0.sb + h * a.X0.sh) * 2LL;
     const char* Qp = (const char*)a.X1.ptr + (b * a.X1.sb + h * a.X1.sh) * 2LL;
     char* dQp = (char*)a.O0.ptr + (b * a.O0.sb + h * a.O0.sh) * 2LL;
     const long long sz = a.X0.sn * 2, sq = a.X1.sn * 2, so = a.O0.sn * 2;
 
-    const int rows = (T + 31) & ~31, ninstr = rows / 8;
-    auto issue = [&](int q_begin, int q_end) __attribute__((always_inline)) {
-        for (int q = q_begin + w; q < q_end; q += 4) {
+    // rows [q_begin, q_end) x 8 of the chunk at token t0 (T tokens; rows
+    // past T load clamped copies); returns the instructions this wave issued
+    auto issue = [&](int t0, int T, int q_begin, int q_end) __attribute__((always_inline)) {
+        int n = 0;
+        for (int q = q_begin + w; q < q_end; q += 4, ++n) {
             const int p = q * 64 + lane, row = p >> 3;
             const int off = ((p & 7) ^ swz_tr(row)) * 16;
             const long long tk = t0 + min(row, T - 1);
             dma16(Zp + tk * sz + off, Zs + q * 1024);
             dma16(Qp + tk * sq + off, Qs + q * 1024);
         }
+        return 2 * n;
     };
-    const int half = min(ninstr, kP1Tok / 16); // rows < kP1Tok / 2
-    issue(0, half);
-    // W1^T fragments; the asm operand puts the compiler's wait for them
-    // here (it covers the first half's rows too), not at their first use
-    const u32x4* wf = a.w1f + (long long)slice * 512 + lane;
-    v8bf F[4][2];
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) F[rb][kb] = as_v8bf(wf[(rb * 2 + kb) * 64]);
-    drain_vmem();
-#pragma unroll
-    for (int rb = 0; rb < 4; ++rb)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(F[rb][kb]));
-    issue(half, ninstr);
-
     v4f acc[4], unused[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) acc[cb] = unused[cb] = v4f{0.f, 0.f, 0.f, 0.f};
-    // rows [r0, r1): dQ of its 16-token steps (wave w: steps = w mod 4),
-    // then dW1 rows 16w.. over the rows
-    auto process = [&](int r0, int r1) __attribute__((always_inline)) {
-        for (int st = r0 / 16 + w; st < r1 / 16; st += 4) {
-            const int row = 16 * st + m;
-            u32x4 zx[2];
+    v8bf F[4][2];
+    for (int t0 = s0; t0 < s1; t0 += kP1Tok) {
+        const int T = min(kP1Tok, s1 - t0);
+        const int rows = (T + 31) & ~31, ninstr = rows / 8;
+        const int half = min(ninstr, kP1Tok / 16); // rows < kP1Tok / 2
+        if (t0 == s0) {
+            issue(t0, T, 0, half);
+            // W1^T fragments; the asm operand puts the compiler's wait for
+            // them here (it covers the first half's rows too), not at their
+            // first use
+            const u32x4* wf = a.w1f + (long long)slice * 512 + lane;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                zx[kb] = *reinterpret_cast<const u32x4*>(Zs + (row * 8 + ((4 * kb + g) ^ swz_tr(row))) * 16);
-            v4f d[4];
+            for (int rb = 0; rb < 4; ++rb)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb) {
-                d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+                for (int kb = 0; kb < 2; ++kb) F[rb][kb] = as_v8bf(wf[(rb * 2 + kb) * 64]);
+            drain_vmem();
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) d[rb] = mfma32(F[rb][kb], as_v8bf(zx[kb]), d[rb]);
+            for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(F[rb][kb]));
+            issue(t0, T, half, ninstr);
+        } else {
+            __syncthreads(); // every wave is done with the previous chunk's rows
+            issue(t0, T, 0, half);
+            vmcnt_at_most(issue(t0, T, half, ninstr)); // this wave's first-half rows have landed
+        }
+
+        // rows [r0, r1): dQ of its 16-token steps (wave w: steps = w mod 4),
+        // then dW1 rows 16w.. over the rows
+        auto process = [&](int r0, int r1) __attribute__((always_inline)) {
+            for (int st = r0 / 16 + w; st < r1 / 16; st += 4) {
+                const int row = 16 * st + m;
+                u32x4 zx[2];
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+                    zx[kb] = *reinterpret_cast<const u32x4*>(Zs + (row * 8 + ((4 * kb + g) ^ swz_tr(row))) * 16);
+                v4f d[4];
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb) {
+                    d[rb] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kb = 0; kb < 2; ++kb) d[rb] = mfma32(F[rb][kb], as_v8bf(zx[kb]), d[rb]);
+                }
+                if (row < T) store_row<true>(dQp + (t0 + row) * so, d, g);
             }
-            if (row < T) store_row<true>(dQp + (t0 + row) * so, d, g);
-        }
-        switch (w) {
-        case 0: gram_owned_bf<0, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
-        case 1: gram_owned_bf<1, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
-        case 2: gram_owned_bf<2, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
-        default: gram_owned_bf<3, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
-        }
-    };
-    // rows past T hold clamped copies: zeroed (after their loads) so the
-    // Gram adds nothing for them
-    auto zero_tail = [&]() __attribute__((always_inline)) {
-        for (int e = tid; e < (rows - T) * 8; e += kThreads) {
-            const int off = (T + (e >> 3)) * 128 + (e & 7) * 16;
-            *reinterpret_cast<u32x4*>(Zs + off) = u32x4{0u, 0u, 0u, 0u};
-            *reinterpret_cast<u32x4*>(Qs + off) = u32x4{0u, 0u, 0u, 0u};
-        }
-    };
-    const int rh = min(rows, kP1Tok / 2);
-    __syncthreads(); // every wave's first-half rows have landed
-    if (rows == rh && T < rows) {
-        zero_tail();
-        __syncthreads();
-    }
-    process(0, rh);
-    drain_vmem();
-    __syncthreads();
-    if (rows > rh) {
-        if (T < rows) {
+            switch (w) {
+            case 0: gram_owned_bf<0, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+            case 1: gram_owned_bf<1, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+            case 2: gram_owned_bf<2, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+            default: gram_owned_bf<3, true, false>(Qs, Zs, r0, r1, lane, acc, unused); break;
+            }
+        };
+        // rows past T hold clamped copies: zeroed (after their loads) so the
+        // Gram adds nothing for them
+        auto zero_tail = [&]() __attribute__((always_inline)) {
+            for (int e = tid; e < (rows - T) * 8; e += kThreads) {
+                const int off = (T + (e >> 3)) * 128 + (e & 7) * 16;
+                *reinterpret_cast<u32x4*>(Zs + off) = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(Qs + off) = u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        const int rh = min(rows, kP1Tok / 2);
+        __syncthreads(); // every wave's first-half rows have landed
+        if (rows == rh && T < rows) {
             zero_tail();
             __syncthreads();
         }
-        process(rh, rows);
+        process(0, rh);
+        drain_vmem();
+        __syncthreads();
+        if (rows > rh) {
+            if (T < rows) {
+                zero_tail();
+                __syncthreads();
+            }
+            process(rh, rows);
+        }
     }
     // this split's share of dW1, rows 16w.. (row-major)
     float* dst = a.part + ((long long)slice * a.S + split) * 4096;
@@ -785,8 +801,9 @@ int bwd_splits(int B, int H, int N) {
     return (int)best;
 }
 
-// bf16 pass 1: splits of at most kP1Tok tokens
-int bwd_splits_bf(int N) { return std::max(1, (N + kP1Tok - 1) / kP1Tok); }
+// bf16 pass 1: the split count of bwd_splits (the grid fills whole rounds
+// of resident slots), each split walking its tokens in chunks of kP1Tok
+int bwd_splits_bf(int B, int H, int N) { return bwd_splits(B, H, N); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -796,7 +813,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // [dW1 shares | dW1, M | dW0 terms | deta terms].
 size_t lin_bwd_ws_bytes(int B, int H, int N) {
     const size_t slices = (size_t)B * H;
-    const size_t S = std::max(bwd_splits(B, H, N), bwd_splits_bf(N));
+    const size_t S = bwd_splits(B, H, N);
     // (the forward's workspace, at least its counter block: the workspace
     // query reads the failure words there)
     size_t bytes = align256(std::max(lin_fwd_ws_bytes(B, H, N), kCounterBytes));
@@ -823,12 +840,12 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.deta = s.deta;
     a.B = s.B; a.H = s.H; a.N = s.N;
     a.dot = s.dot;
-    // pass 1 splits: bf16 tokens resident in LDS (<= kP1Tok per split)
-    a.S = s.bf16 ? bwd_splits_bf(s.N) : bwd_splits(s.B, s.H, s.N);
+    // pass 1 splits (bf16: walked in chunks of kP1Tok tokens resident in LDS)
+    a.S = s.bf16 ? bwd_splits_bf(s.B, s.H, s.N) : bwd_splits(s.B, s.H, s.N);
     a.per = (((s.N + a.S - 1) / a.S) + 15) & ~15;
     a.xcd = 1;
     const size_t slices = (size_t)s.B * s.H;
-    const size_t Smax = std::max(bwd_splits(s.B, s.H, s.N), bwd_splits_bf(s.N));
+    const size_t Smax = bwd_splits(s.B, s.H, s.N);
     char* p = (char*)lin_bwd_saved_region(s.ws, s.B, s.H, s.N) + align256(slices * 8192 * 4);
     a.part = (float*)p;
     p += align256(slices * Smax * 4096 * 4);
