@@ -109,3 +109,106 @@ def test_graph_replay_matches_eager():
         for k in OUTS:
             assert torch.equal(g[k], ref[k]), f"eager call after replay {r}: {k} differs"
         print(f"replay {r} ok", flush=True)
+
+
+def test_graph_replay_of_the_other_entry_points():
+    # the conv and scan backwards (the scan's matrix-core walks, both with
+    # coinciding and with differing direction mini-batches), the MLP inner
+    # model, the gradient magnitude map, two full-batch steps, the dot loss,
+    # a ragged-mini-batch scan and a chunk-parallel one, captured and replayed
+    import vision_test_sequence_amd as vt
+    banner("graph capture / replay of the backward, MLP and variant entry points")
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS["vit3t_1248_bf16"]
+    big = {k: v.to(dev) for k, v in wl.make("vit3t_1248_bf16").items()}
+    g = {}
+    K, Q, V = (big[k][:, 2:3].contiguous() for k in ("K", "Q", "V"))
+    g["w0c"] = big["w0"][2:3].contiguous()
+    g["etac"] = big["eta"][2:3].contiguous()
+    g["dZc"] = (torch.randn(Q.shape, generator=torch.Generator().manual_seed(11)) * 0.1).to(dev, Q.dtype)
+    s = {k: v.to(dev) for k, v in wl.draw(2, 3, 300, seed=1700, dtype="bf16", unit_rows=True,
+                                           backward=True).items()}
+    mw = {k: v.to(dev) for k, v in wl.draw_mlp_weights(3, 128, seed=1701).items()}
+    one = {k: v.to(dev) for k, v in wl.draw(1, 2, 6400, seed=1702, dtype="bf16", unit_rows=True).items()}
+    z = lambda t: torch.zeros_like(t)
+    outs = {
+        "cK": z(K), "cQ": z(Q), "cV": z(V), "cw0": torch.zeros((1, 64, 3, 3), device=dev),
+        "ceta": torch.zeros((1,), device=dev),
+        "sK": z(s["K"]), "sQ": z(s["Q"]), "sV": z(s["V"]), "sW0": z(s["W0"]), "seta": z(s["eta"]),
+        "rK": z(s["K"]), "rQ": z(s["Q"]), "rV": z(s["V"]), "rW0": z(s["W0"]), "reta": z(s["eta"]),
+        "mZ": z(s["Q"]), "gmm": torch.zeros(s["K"].shape[:3], device=dev), "eZ": z(s["Q"]),
+        "dZl": z(s["Q"]), "rgZ": z(s["Q"]), "cpZ": z(one["Q"]),
+    }
+
+    def conv_bwd():
+        vt.ttt_dwconv3x3_fullbatch_bwd(K, Q, V, g["w0c"], g["etac"], g["dZc"], w.grid_h, w.grid_w,
+                                       dK=outs["cK"], dQ=outs["cQ"], dV=outs["cV"], dw0=outs["cw0"],
+                                       deta=outs["ceta"])
+
+    def scan_bwd():  # N = 300 = 18 x 16 + 12: the directions' mini-batches differ
+        vt.ttt_linear_minibatch_bidir_bwd(s["K"], s["Q"], s["V"], s["W0"], s["eta"], s["dZ"], 16, 0,
+                                          dK=outs["sK"], dQ=outs["sQ"], dV=outs["sV"], dW0=outs["sW0"],
+                                          deta=outs["seta"])
+
+    def scan_bwd_even():  # b = 15 divides N: one workgroup covers both directions
+        vt.ttt_linear_minibatch_bidir_bwd(s["K"], s["Q"], s["V"], s["W0"], s["eta"], s["dZ"], 15, 0,
+                                          dK=outs["rK"], dQ=outs["rQ"], dV=outs["rV"], dW0=outs["rW0"],
+                                          deta=outs["reta"])
+
+    def mlp():
+        vt.ttt_mlp_fullbatch(s["K"], s["Q"], s["V"], mw["W1"], mw["W2"], s["eta"], Z=outs["mZ"])
+
+    def gmm():
+        vt.ttt_linear_gradient_magnitude(s["K"], s["V"], s["W0"], out=outs["gmm"])
+
+    def epochs():
+        vt.ttt_linear_fullbatch(s["K"], s["Q"], s["V"], s["W0"], s["eta"], Z=outs["eZ"], steps=2)
+
+    def dot():
+        vt.ttt_linear_fullbatch(s["K"], s["Q"], s["V"], s["W0"], s["eta"], Z=outs["dZl"], loss=vt.LOSS_DOT)
+
+    def ragged_scan():
+        vt.ttt_linear_minibatch_bidir(s["K"], s["Q"], s["V"], s["W0"], s["eta"], 20, Z=outs["rgZ"])
+
+    def chunk_parallel_scan():  # one image: the planner cuts the chains into segments
+        vt.ttt_linear_minibatch_bidir(one["K"], one["Q"], one["V"], one["W0"], one["eta"], 16, Z=outs["cpZ"])
+
+    ops = [conv_bwd, scan_bwd, scan_bwd_even, mlp, gmm, epochs, dot, ragged_scan, chunk_parallel_scan]
+
+    def run_all():
+        for op in ops:
+            op()
+
+    def clear():
+        for t in outs.values():
+            t.zero_()
+
+    run_all()
+    torch.cuda.synchronize()
+    ref = {k: t.clone() for k, t in outs.items()}
+    for k, t in ref.items():
+        assert not torch.isnan(t.float()).any(), f"eager {k} has NaN"
+        assert torch.count_nonzero(t) > 0, f"eager {k} is all zero"
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run_all()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        run_all()
+    torch.cuda.synchronize()
+    for r in range(3):
+        clear()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, t in outs.items():
+            assert torch.equal(t, ref[k]), f"replay {r}: {k} differs from the eager result"
+        clear()
+        run_all()
+        torch.cuda.synchronize()
+        for k, t in outs.items():
+            assert torch.equal(t, ref[k]), f"eager call after replay {r}: {k} differs"
+        print(f"replay {r} ok", flush=True)
