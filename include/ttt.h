@@ -264,8 +264,10 @@ ttt_status ttt_layer_fullbatch(const ttt_problem* lin, ttt_view Kl, ttt_view Ql,
  * then every segment walked from its start state); the results agree with
  * the single walk to rounding.  The environment variable
  * TTT_SCAN_SEGMENTS=n (a test switch) forces n segments (at most 8).
- * (N + 512) * stride_n * 2 bytes must stay under 2^31 for K, Q, V and Z
- * (a slice's rows are addressed with 32-bit offsets; else
+ * bf16 views run on the matrix cores (bf16 products, fp32 accumulation and
+ * state); fp32 views on the vector ALUs in fp32 throughout (no segments).
+ * bf16: (N + 512) * stride_n * 2 bytes must stay under 2^31 for K, Q, V and
+ * Z (a slice's rows are addressed with 32-bit offsets; else
  * TTT_ERR_UNSUPPORTED).
  */
 ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view Q, ttt_view V,

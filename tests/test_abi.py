@@ -190,8 +190,6 @@ def scan(p, **kw):
 def test_scan_errors():
     assert bd.STATUS_NAMES[scan(P(b=0))] == "TTT_ERR_BAD_SHAPE"
     assert bd.STATUS_NAMES[scan(P(mode=3))] == "TTT_ERR_UNSUPPORTED"
-    # the scan runs bf16 matrix-core products only
-    assert bd.STATUS_NAMES[scan(P(dtype=bd.TTT_F32))] == "TTT_ERR_UNSUPPORTED"
     L = vt.lib()
     need = L.ttt_workspace_size(bd.OP_LINEAR_MINIBATCH_BIDIR, ctypes.byref(P()))
     assert bd.STATUS_NAMES[scan(P(), wsb=need - 1)] == "TTT_ERR_WORKSPACE_TOO_SMALL"

@@ -112,13 +112,27 @@ def test_deterministic():
     assert torch.equal(Z1, Z2)
 
 
-def test_fp32_inputs_are_rejected():
-    banner("scan fp32 -> unsupported")
+@pytest.mark.parametrize("N,b", [(196, 16), (37, 1), (200, 7), (196, 49), (300, 40), (130, 200), (64, 64)])
+@pytest.mark.parametrize("mode", [BIDIR, FWD, BWD])
+def test_fp32_views(N, b, mode):
+    # fp32 views take the vector-ALU scan, in fp32 throughout: 1e-5 against
+    # the oracle, sub-blocks of 32 positions inside longer mini-batches
+    banner(f"scan fp32 N={N} b={b} mode={mode}")
+    inp = wl.draw(2, 2, N, seed=1540 + N + b + mode, dtype="f32", unit_rows=True,
+                  eta_fixed=0.5 if b < 4 else None)
+    _check(*_on(inp), b, mode, tol=TOL["f32"])
+
+
+def test_fp32_one_initial_state_per_direction():
     import vision_test_sequence_amd as vt
-    from vision_test_sequence_amd.binding import TTTError
-    K, Q, V, W0, eta = _on(wl.draw(1, 1, 64, seed=980, dtype="f32"))
-    with pytest.raises(TTTError):
-        vt.ttt_linear_minibatch_bidir(K, Q, V, W0, eta, 16, BIDIR)
+    banner("scan fp32 with W0 per direction")
+    K, Q, V, W0, eta = _on(wl.draw(2, 2, 150, seed=1550, dtype="f32", unit_rows=True))
+    W1 = torch.randn_like(W0) / 8
+    two = torch.stack([W0, W1]).contiguous()
+    Z = vt.ttt_linear_minibatch_bidir(K, Q, V, two, eta, 16, BIDIR)
+    torch.cuda.synchronize()
+    Zr = oracle.linear_minibatch_2w0(f64(K), f64(Q), f64(V), f64(two), f64(eta), 16, BIDIR)
+    assert slice_rel_err(f64(Z), Zr) <= TOL["f32"]
 
 
 def test_workspace_shared_across_shapes():

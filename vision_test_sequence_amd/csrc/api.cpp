@@ -575,7 +575,6 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     if (p->mode != TTT_BIDIR_AVG && p->mode != TTT_FORWARD_ONLY && p->mode != TTT_BACKWARD_ONLY)
         return TTT_ERR_UNSUPPORTED;
     if (!scan_minibatch_supported(p->minibatch, p->N)) return TTT_ERR_UNSUPPORTED;
-    if (p->dtype != TTT_BF16) return TTT_ERR_UNSUPPORTED;
     if (p->loss != TTT_LOSS_L2 || p->steps > 1) return TTT_ERR_UNSUPPORTED;
     if (noop) return TTT_OK;
     Span in[5], out[2];
@@ -586,11 +585,11 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     if ((st = check_buf(W0, nw0 * p->H * p->d * p->d * 4, 16, &in[3])) != TTT_OK) return st;
     if ((st = check_buf(eta, (size_t)p->H * 4, 4, &in[4])) != TTT_OK) return st;
     if ((st = check_view(Z, *p, &out[0])) != TTT_OK) return st;
-    // the kernel addresses a slice's K, V, Q and Z rows through 32-bit
+    // the bf16 kernel addresses a slice's K, V, Q and Z rows through 32-bit
     // buffer offsets, walking up to 512 tokens past either end
     const int64_t span_lim = (int64_t)1 << 31;
     for (const ttt_view* w : {&K, &Q, &V, &Z})
-        if ((int64_t)(p->N + 512) * std::max<int64_t>(w->stride_n, p->d) * 2 >= span_lim)
+        if (p->dtype == TTT_BF16 && (int64_t)(p->N + 512) * std::max<int64_t>(w->stride_n, p->d) * 2 >= span_lim)
             return TTT_ERR_UNSUPPORTED;
     const size_t need = scan_ws_bytes(p->B, p->H, p->N, (int)p->mode);
     if ((st = check_ws(ws, ws_bytes, need, &out[1])) != TTT_OK) return st;
@@ -615,6 +614,7 @@ ttt_status ttt_linear_minibatch_bidir(const ttt_problem* p, ttt_view K, ttt_view
     // most 8, and no more than its mini-batches) instead of the planned count
     const char* sg = getenv("TTT_SCAN_SEGMENTS");
     a.segs = sg ? atoi(sg) : 0;
+    if (!a.bf16) return hip_status(launch_scan_f32(a, (hipStream_t)stream));
     return hip_status(launch_scan(a, (hipStream_t)stream));
 }
 

@@ -118,9 +118,11 @@ struct ScanLaunch {
     int segs;         // chunk-parallel segments per chain: 0 = planned
 };
 size_t scan_ws_bytes(int B, int H, int N, int mode);
-// Mini-batch sizes the scan kernel takes: b <= 16, multiples of 16, b >= N.
+// Mini-batch sizes the scan takes (any b >= 1).
 bool scan_minibatch_supported(int b, int N);
 hipError_t launch_scan(ScanLaunch a, hipStream_t stream);
+// fp32 views: the vector-ALU scan (minibatch_scan_f32.hip), same workspace.
+hipError_t launch_scan_f32(const ScanLaunch& a, hipStream_t stream);
 
 // ---- backward of the mini-batch scans --------------------------------------
 struct ScanBwdLaunch {
