@@ -11,11 +11,12 @@
 //   dK  = beta (V dW1 - K M)
 //   dV  = beta K dW1^T
 //   dW0 = sum_b dW1 (I - beta A),  deta = -sum_b <dW1, G>.
-// Four launches (plus the forward's Gram pass when A and G were not saved):
+// Three launches (plus the forward's Gram pass when A and G were not saved):
 //   pass 1   per (slice, split): dQ for its tokens and its share of dW1;
 //   reduce   per slice: dW1, M, the slice's dW0 and deta terms;
-//   pass 2   per (slice, split): dK, dV for its tokens;
-//   batch    per head: dW0 and deta summed over b in ascending order.
+//   pass 2   per (slice, split): dK, dV for its tokens; its first H x 16
+//            workgroups also sum dW0 and deta over b in ascending order
+//            (a fourth launch, batch, when the grid is smaller).
 // Every reduction has a fixed order, so results are bitwise reproducible.
 //
 // Products on the matrix cores (16x16 tiles, lane l = 16 g + m):
@@ -54,10 +55,10 @@ struct BwdArgs {
     float* dW0;         // [H][64][64]
     float* deta;        // [H]
     u32x4* fr;          // [slices][3][8][64]: bf16 fragments of beta dW1^T, -beta M, beta dW1
-    u32x4* w1f;         // [slices][8][64]: bf16 fragments of W1^T (bf16 pass 1)
     int B, H, N, S, per, xcd;
     int S2, per2;       // bf16 pass 2: splits per slice, tokens per split (<= kP2Tok)
     int dot;            // dot-product loss: beta = eta / N, M = 0, dW0 = sum_b dW1
+    int batch_in_pass2; // bf16 pass 2 forms the batch sums (its grid has >= H x 16 workgroups)
 };
 
 // beta of the loss: L2 G = (2/N)(W0 A - C); dot-product G = -(1/N) C.
@@ -321,25 +322,6 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_pass1(BwdArgs a) {
 }
 
 // ------------------------------------------------------ pass 1 (bf16) --
-// W1^T as bf16 A-operand fragments per slice (W1 = W0 - eta G from the
-// saved G): piece (rb, kb, lane) holds W1[k][o], o = perm_row(rb, m),
-// k = 32 kb + 8 g + (0..7).
-__global__ __launch_bounds__(kThreads, 1) void bwd_prep(BwdArgs a) {
-    const int slice = blockIdx.x, h = slice % a.H;
-    const float eta = a.eta[h];
-    const float* W0 = a.W0 + (long long)h * 4096;
-    const float* G = a.saved + (long long)slice * 8192 + 4096;
-    for (int pc = threadIdx.x; pc < 512; pc += kThreads) {
-        const int rb = pc >> 7, kb = (pc >> 6) & 1, ln = pc & 63;
-        const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
-        float v[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = W0[(k0 + j) * 64 + o] - eta * G[(k0 + j) * 64 + o];
-        a.w1f[(long long)slice * 512 + pc] =
-            u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
-    }
-}
-
 // dQ = dZ W1 and the split's dW1 = dZ^T Q with the split's dZ and Q rows
 // staged in LDS chunk by chunk (kP1Tok tokens each) by direct-to-LDS loads
 // with the swz_tr swizzle; in each chunk the first half is processed while
@@ -350,6 +332,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_prep(BwdArgs a) {
 // reduce's reads of them) few.
 __global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) char lds[2 * kP1Tok * 128];
+    static_assert(kP1Tok * 64 >= 4096 * 4, "W1 fits in the upper half of the dZ rows");
     char* Zs = lds;
     char* Qs = lds + kP1Tok * 128;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
@@ -386,19 +369,48 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
         const int half = min(ninstr, kP1Tok / 16); // rows < kP1Tok / 2
         if (t0 == s0) {
             issue(t0, T, 0, half);
-            // W1^T fragments; the asm operand puts the compiler's wait for
-            // them here (it covers the first half's rows too), not at their
-            // first use
-            const u32x4* wf = a.w1f + (long long)slice * 512 + lane;
+            // W1 = W0 - eta G (the forward's G) staged in fp32 in the upper
+            // half of the dZ rows, which only the second half's loads fill;
+            // row k's columns are XOR-swizzled by sw(k) = 4 ((k >> 3) & 1) +
+            // 32 ((k >> 4) & 1) so that the fragment reads below spread over
+            // all banks
+            float* w1s = reinterpret_cast<float*>(Zs + kP1Tok * 64);
+            {
+                const float eta = a.eta[h];
+                const f32x4* W04 = reinterpret_cast<const f32x4*>(a.W0 + (long long)h * 4096);
+                const f32x4* G4 = reinterpret_cast<const f32x4*>(a.saved + (long long)slice * 8192 + 4096);
+                f32x4 wv[4], gv[4];
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+                for (int i = 0; i < 4; ++i) {
+                    wv[i] = W04[tid + kThreads * i];
+                    gv[i] = G4[tid + kThreads * i];
+                }
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) F[rb][kb] = as_v8bf(wf[(rb * 2 + kb) * 64]);
-            drain_vmem();
+                for (int i = 0; i < 4; ++i) {
+                    const int e4 = tid + kThreads * i, k = e4 >> 4;
+                    const int col = ((e4 & 15) * 4) ^ (4 * ((k >> 3) & 1) + 32 * ((k >> 4) & 1));
+                    *reinterpret_cast<f32x4*>(w1s + k * 64 + col) =
+                        f32x4{wv[i][0] - eta * gv[i][0], wv[i][1] - eta * gv[i][1], wv[i][2] - eta * gv[i][2],
+                              wv[i][3] - eta * gv[i][3]};
+                }
+            }
+            // W1 is staged; this wave's first-half rows, loaded before W0
+            // and G, have landed too (a wave's loads return in order)
+            __syncthreads();
+            // W1^T as bf16 A-operand fragments: piece (rb, kb) of lane (g, m)
+            // holds W1[k][o], o = perm_row(rb, m), k = 32 kb + 8 g + (0..7)
+            // (sw(k) = 4 (g & 1) + 32 (g >> 1) for all eight)
 #pragma unroll
-            for (int rb = 0; rb < 4; ++rb)
+            for (int rb = 0; rb < 4; ++rb) {
+                const int o = perm_row(rb, m) ^ (4 * (g & 1) + 32 * (g >> 1));
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb) asm volatile("" : "+v"(F[rb][kb]));
+                for (int kb = 0; kb < 2; ++kb) {
+                    const float* col = w1s + (32 * kb + 8 * g) * 64 + o;
+                    F[rb][kb] = as_v8bf(u32x4{pack_bf2(col[0], col[64]), pack_bf2(col[128], col[192]),
+                                              pack_bf2(col[256], col[320]), pack_bf2(col[384], col[448])});
+                }
+            }
+            __syncthreads(); // every wave has its fragments before the second half overwrites W1
             issue(t0, T, half, ninstr);
         } else {
             __syncthreads(); // every wave is done with the previous chunk's rows
@@ -596,6 +608,34 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     if (tid == 0) a.detas[slice] = -red[0];
 }
 
+// ------------------------------------------------------------ batch sums --
+// 16 workgroups per head, one dW0 element per thread; the B terms of an
+// element are loaded together and added in ascending b.  blk: the
+// workgroup's index among the H x 16.
+__device__ __forceinline__ void batch_sums(const BwdArgs& a, int blk) {
+    const int h = blk >> 4, tid = threadIdx.x;
+    const int e = (blk & 15) * kThreads + tid;
+    const float* src = a.dW0s + (long long)h * 4096 + e;
+    const long long step = (long long)a.H * 4096;
+    float v = 0.f;
+    int b = 0;
+    for (; b + 8 <= a.B; b += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) t[i] = src[(b + i) * step];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v += t[i];
+    }
+    for (; b < a.B; ++b) v += src[b * step];
+    a.dW0[(long long)h * 4096 + e] = v;
+    if ((blk & 15) == 0 && tid == 0) {
+        float d = 0.f;
+        for (int bb = 0; bb < a.B; ++bb) d += a.detas[(long long)bb * a.H + h];
+        a.deta[h] = d;
+    }
+}
+__global__ __launch_bounds__(kThreads, 1) void bwd_batch(BwdArgs a) { batch_sums(a, (int)blockIdx.x); }
+
 // ---------------------------------------------------------------- pass 2 --
 // dK = beta (V dW1 - K M), dV = beta K dW1^T for the workgroup's tokens.
 template <bool BF>
@@ -669,6 +709,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_pass2_bf(BwdArgs a) {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int slice = blockIdx.x / a.S2, split = blockIdx.x % a.S2;
+    // the first H x 16 workgroups also form dW0 and deta over the batch
+    // (the reduce has written every slice's terms)
+    if (a.batch_in_pass2 && (int)blockIdx.x < a.H * 16) batch_sums(a, (int)blockIdx.x);
     if (slice >= a.B * a.H) return;
     const int b = slice / a.H, h = slice % a.H;
     const int t0 = min(a.N, split * a.per2), t1 = min(a.N, t0 + a.per2), T = t1 - t0;
@@ -747,32 +790,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_pass2_bf(BwdArgs a) {
     steps(8, nst);
 }
 
-// ------------------------------------------------------------ batch sums --
-// 16 workgroups per head, one dW0 element per thread; the B terms of an
-// element are loaded together and added in ascending b.
-__global__ __launch_bounds__(kThreads, 1) void bwd_batch(BwdArgs a) {
-    const int h = blockIdx.x >> 4, tid = threadIdx.x;
-    const int e = (blockIdx.x & 15) * kThreads + tid;
-    const float* src = a.dW0s + (long long)h * 4096 + e;
-    const long long step = (long long)a.H * 4096;
-    float v = 0.f;
-    int b = 0;
-    for (; b + 8 <= a.B; b += 8) {
-        float t[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = src[(b + i) * step];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v += t[i];
-    }
-    for (; b < a.B; ++b) v += src[b * step];
-    a.dW0[(long long)h * 4096 + e] = v;
-    if ((blockIdx.x & 15) == 0 && tid == 0) {
-        float d = 0.f;
-        for (int bb = 0; bb < a.B; ++bb) d += a.detas[(long long)bb * a.H + h];
-        a.deta[h] = d;
-    }
-}
-
 // Workgroups per slice: at least 1024 workgroups in all (several rounds
 // of the device's 512 resident slots: two per CU), each with at least 128
 // tokens; among split counts up to twice that minimum, the one whose grid
@@ -823,7 +840,6 @@ size_t lin_bwd_ws_bytes(int B, int H, int N) {
     bytes += align256(slices * 4096 * 4);     // dW0 terms
     bytes += align256(slices * 4);            // deta terms
     bytes += align256(slices * 1536 * 16);    // bf16 operator fragments
-    bytes += align256(slices * 512 * 16);     // bf16 W1^T fragments
     return bytes;
 }
 
@@ -856,8 +872,6 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     a.detas = (float*)p;
     p += align256(slices * 4);
     a.fr = s.bf16 ? (u32x4*)p : nullptr;
-    p += align256(slices * 1536 * 16);
-    a.w1f = s.bf16 ? (u32x4*)p : nullptr;
     a.S2 = (s.N + kP2Tok - 1) / kP2Tok;
     if (a.S2 < 1) a.S2 = 1;
     a.per2 = (((s.N + a.S2 - 1) / a.S2) + 15) & ~15; // <= kP2Tok
@@ -866,16 +880,16 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     const dim3 grid((unsigned)(padded * a.S)), block(kThreads);
     a.X0 = s.dZ; a.X1 = s.Q; a.O0 = s.dQ;
     if (s.bf16) {
-        hipLaunchKernelGGL(bwd_prep, dim3((unsigned)slices), block, 0, stream, a);
         hipLaunchKernelGGL(bwd_pass1_bf, dim3((unsigned)(slices * a.S)), block, 0, stream, a);
     } else {
         hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
     }
     hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
     a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
+    a.batch_in_pass2 = s.bf16 && (long long)slices * a.S2 >= (long long)s.H * 16 ? 1 : 0;
     if (s.bf16) hipLaunchKernelGGL(bwd_pass2_bf, dim3((unsigned)(slices * a.S2)), block, 0, stream, a);
     else hipLaunchKernelGGL(bwd_pass2<false>, grid, block, 0, stream, a);
-    hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H * 16), block, 0, stream, a);
+    if (!a.batch_in_pass2) hipLaunchKernelGGL(bwd_batch, dim3((unsigned)s.H * 16), block, 0, stream, a);
     return hipGetLastError();
 }
 
