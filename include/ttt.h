@@ -212,7 +212,9 @@ ttt_status ttt_dwconv3x3_fullbatch(const ttt_problem* p, ttt_view K, ttt_view Q,
  * saved: the forward's g ([B][H][d][3][3], its saved output) or NULL to
  *   recompute g from K and V.
  * Out: dK, dQ, dV (views, dtype); dw0 float [H][d][3][3] and deta float [H]
- *   (overwritten).  grid_h * grid_w must equal N.
+ *   (overwritten).  grid_h * grid_w must equal N.  Each view's slice must
+ *   span less than 512 MiB (N * stride_n * element size < 2^29 bytes), or
+ *   TTT_ERR_UNSUPPORTED.
  * ws: ttt_workspace_size(TTT_OP_DWCONV3X3_FULLBATCH_BWD, p) bytes (no
  *   zero-fill needed: every word is written before it is read).
  */

@@ -365,6 +365,12 @@ def test_conv_bwd_errors():
     assert call(saved=addr(8)) == 6                     # saved overlaps the dV output
     assert call(wsb=need - 1) == 7
     assert call(ws=addr(20) + 16) == 4
+    # a slice of each view is addressed with 32-bit offsets: 100 tokens
+    # 2^22 elements apart span more than 2^29 bytes (checked before any
+    # launch: the workspace is withheld)
+    sn = 1 << 22
+    far = bd.View(addr(9), 3 * 100 * sn, 100 * sn, sn)
+    assert bd.STATUS_NAMES[call(dV=far, wsb=0)] == "TTT_ERR_UNSUPPORTED"
 
 
 def test_scan_bwd_errors():

@@ -465,6 +465,11 @@ ttt_status ttt_dwconv3x3_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_vie
     if ((st = check_view(dK, *p, &out[0])) != TTT_OK) return st;
     if ((st = check_view(dQ, *p, &out[1])) != TTT_OK) return st;
     if ((st = check_view(dV, *p, &out[2])) != TTT_OK) return st;
+    // the kernels address a slice of each view with 32-bit offsets, the
+    // stencil's rows two past either edge included
+    for (const ttt_view* v : {&K, &Q, &V, &dZ, &dK, &dQ, &dV})
+        if (p->N > 1 && (int64_t)p->N * v->stride_n * (int64_t)esize(p->dtype) >= ((int64_t)1 << 29))
+            return TTT_ERR_UNSUPPORTED;
     const size_t need = conv_bwd_ws_bytes(p->B, p->H, p->grid_h, p->grid_w);
     if ((st = check_ws(ws, ws_bytes, need, &out[5])) != TTT_OK) return st;
     if ((st = check_aliasing(in, nin, out, 6)) != TTT_OK) return st;

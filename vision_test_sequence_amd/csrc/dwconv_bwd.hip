@@ -19,16 +19,17 @@
 // token row (128 bytes bf16, 256 bytes fp32).  A wave walks one grid row
 // over a segment of at most 16 columns with sliding register windows, the
 // loads of the next kPD columns in flight (a ring of registers, so the
-// walk waits on memory once, not per column).  Seven launches, all
+// walk waits on memory once, not per column).  Four launches, all
 // reductions in a fixed order (bitwise reproducible):
 //   pass 1  per (slice, 4-row group, column segment): partial g (unless the
 //           forward's g is supplied) and dw1, summed over the 4 waves;
-//   reduce  per slice: g, dw1 over the partials in order; w1, dg, the deta
-//           term;
+//   reduce  per (slice, 64 of its 576 (channel, tap) entries): g, dw1 over
+//           the partials in order; w1, dg, the entries' deta terms;
 //   pass 2  per (slice, 4-row group, segment): dQ, dV, dK and the partial
 //           sum_p dR[p] K[p+t];
-//   sum     per slice: the dw0 term dw1 + the pass-2 partials in order;
-//   batch   per head: dw0 and deta summed over the batch in b order.
+//   sums    per (slice, 64 entries): the dw0 term dw1 + the pass-2 partials
+//           in order; the last of a head's workgroups to finish (a counter
+//           per head) sums dw0 and deta over the batch in b order.
 #include "common.hpp"
 #include "internal.hpp"
 
@@ -38,6 +39,7 @@ namespace {
 constexpr int kCbSeg = 16;     // columns per segment (at most)
 constexpr int kCbRows = 4;     // grid rows per workgroup: one per wave
 constexpr int kPD = 4;         // columns whose loads are in flight ahead of the walk
+constexpr uint32_t kOffOut = 0x80000000u; // an offset past every slice span
 
 struct CbArgs {
     View4 K, Q, V, dZ, dK, dQ, dV;
@@ -47,9 +49,8 @@ struct CbArgs {
     float* part1;       // [slices][P][64][18]: g (0..8), dw1 (9..17)
     float* part2;       // [slices][P][64][9]
     float* sl;          // [slices][5][64][9]: w1, (2/N) dg, dw1, g, dw0 term
-    float* sum1;        // [slices][64][18]: part1 summed over the partials
-    float* sum2;        // [slices][64][9]: part2 summed over the partials
-    float* deta_s;      // [slices]
+    float* deta_s;      // [slices][9]: deta terms of the reduce's entry blocks
+    unsigned* cnt;      // [H]: finished sums workgroups per head (zeroed by the reduce)
     float* dw0;         // [H][64][9]
     float* deta;        // [H]
     int B, H, gh, gw;
@@ -60,45 +61,59 @@ struct CbArgs {
 template <bool BF> struct Elt;
 template <> struct Elt<true> {
     static constexpr int esz = 2;
-    __device__ static float ld(const char* p) { return __uint_as_float((uint32_t)(*(const uint16_t*)p) << 16); }
-    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(f2bf(v), (uint16_t*)p); }
+    __device__ static float ld(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+        return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0) << 16);
+    }
+    __device__ static void st(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+        __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), rs, off, 0, 2 /* nontemporal */);
+    }
 };
 template <> struct Elt<false> {
     static constexpr int esz = 4;
-    __device__ static float ld(const char* p) { return *(const float*)p; }
-    __device__ static void st(char* p, float v) { __builtin_nontemporal_store(v, (float*)p); }
+    __device__ static float ld(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0));
+    }
+    __device__ static void st(__amdgpu_buffer_rsrc_t rs, uint32_t off, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rs, off, 0, 2 /* nontemporal */);
+    }
 };
 
-// Channel `lane` of one slice's token map; positions off the grid read 0.
-// Branch-free: the load goes to the clamped position and the value is
-// selected afterwards, so a load in flight is waited for only where its
-// value is used (a branch around the load would wait for every load at the
-// join).
+// One slice's token map of a view, read and written through a buffer
+// descriptor over the slice's span (the host bounds it below 2^31 bytes).
+// A token's byte offset is wave-uniform and formed on the scalar unit; a
+// lane adds its channel's offset.  Positions off the grid read 0 from past
+// the descriptor's range: a column off the grid takes the offset kOffOut,
+// and a row off the grid needs nothing, its offset being negative (2^31 or
+// more as unsigned) or at least N tokens.  No clamp, no select per load and
+// no branch (a branch around a load would make the compiler wait for every
+// load in flight at the join).
 template <bool BF> struct Map {
-    const char* base;
-    long long sn; // bytes between tokens
-    int gh, gw;
-    __device__ float at(int y, int x) const {
-        const bool in = y >= 0 && y < gh && x >= 0 && x < gw;
-        const int yc = min(max(y, 0), gh - 1), xc = min(max(x, 0), gw - 1);
-        const float v = Elt<BF>::ld(base + (long long)(yc * gw + xc) * sn);
-        return in ? v : 0.f;
+    __amdgpu_buffer_rsrc_t rs;
+    int sn;     // bytes between tokens (at least 64 elements)
+    int gw;
+    uint32_t lo; // the lane's channel offset in bytes
+    __device__ uint32_t off(int y, int x) const {
+        // both arms formed first, so the choice is a select, not a branch
+        const uint32_t tok = (uint32_t)((y * gw + x) * sn);
+        const bool on = (unsigned)x < (unsigned)gw;
+        return (on ? tok : kOffOut) + lo;
     }
+    __device__ float at(int y, int x) const { return Elt<BF>::ld(rs, off(y, x)); }
+    __device__ void put(int y, int x, float v) const { Elt<BF>::st(rs, off(y, x), v); }
 };
 template <bool BF>
 __device__ __forceinline__ Map<BF> map_of(const View4& v, int b, int h, int gh, int gw, int lane) {
     constexpr int es = Elt<BF>::esz;
     Map<BF> m;
-    m.base = (const char*)v.ptr + ((long long)b * v.sb + (long long)h * v.sh + lane) * es;
-    m.sn = v.sn * es;
-    m.gh = gh;
+    const char* base = (const char*)v.ptr + ((long long)b * v.sb + (long long)h * v.sh) * es;
+    m.rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0,
+                                              (int)(((long long)gh * gw - 1) * v.sn * es + 64 * es), 0x00020000);
+    // (a one-token slice may have any stride; 64 elements keep its
+    // neighbours' offsets outside the span)
+    m.sn = (int)max(v.sn * es, 64LL * es);
     m.gw = gw;
+    m.lo = (uint32_t)(lane * es);
     return m;
-}
-template <bool BF>
-__device__ __forceinline__ char* out_of(const View4& v, int b, int h, int lane) {
-    constexpr int es = Elt<BF>::esz;
-    return (char*)v.ptr + ((long long)b * v.sb + (long long)h * v.sh + lane) * es;
 }
 
 struct Task {
@@ -138,7 +153,9 @@ __device__ __forceinline__ void wave_sum_store(const float* v, float* red, float
 template <bool BF, bool HAS_G>
 __global__ __launch_bounds__(256) void cbwd_pass1(CbArgs a) {
     __shared__ float red[4 * 64 * 18];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the wave index is uniform: the row, and with it every address but the
+    // lane's channel offset, is formed on the scalar unit
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Task t = task_of(a, w);
     float acc[18];
 #pragma unroll
@@ -218,42 +235,81 @@ __global__ __launch_bounds__(256) void cbwd_pass1(CbArgs a) {
 }
 
 // ---- per-slice reduce ---------------------------------------------------
+// Workgroup (slice, j) takes entries e = 64 j + lane of the slice's 576
+// (channel e / 9, tap e % 9); wave q adds partials [q P/4, (q+1) P/4) in
+// order, all of its loads issued before the first add, and the four quarter
+// sums are added in order.
+constexpr int kCbEnt = 64;                     // entries per reduce / sums workgroup
+constexpr int kCbBlk = (576 + kCbEnt - 1) / kCbEnt; // such workgroups per slice
+template <int NV, int STRIDE>
+__device__ __forceinline__ void quarter_sums(const float* src, int P, const int* off, float* qs, float* out) {
+    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+    const int per = (P + 3) / 4, p0 = q * per, p1 = min(P, p0 + per);
+    float s[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) s[v] = 0.f;
+    int p = p0;
+    for (; p + 8 <= p1; p += 8) {
+        float t[8][NV];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) t[i][v] = src[(long long)(p + i) * STRIDE + off[v]];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int v = 0; v < NV; ++v) s[v] += t[i][v];
+    }
+    for (; p < p1; ++p)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) s[v] += src[(long long)p * STRIDE + off[v]];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) qs[(v * 4 + q) * 64 + lane] = s[v];
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+        out[v] = ((qs[(v * 4) * 64 + lane] + qs[(v * 4 + 1) * 64 + lane]) + qs[(v * 4 + 2) * 64 + lane]) +
+                 qs[(v * 4 + 3) * 64 + lane];
+}
+
 __global__ __launch_bounds__(256) void cbwd_reduce(CbArgs a) {
-    __shared__ float de[256];
-    const int slice = blockIdx.x, tid = threadIdx.x;
+    __shared__ float qs[2 * 4 * 64];
+    const int slice = blockIdx.x / kCbBlk, j = blockIdx.x % kCbBlk, tid = threadIdx.x, lane = tid & 63;
     const int h = slice % a.H;
     const int P = a.ngrp * a.nseg;
+    if (blockIdx.x == 0 && tid < a.H) a.cnt[tid] = 0u; // the sums' counters, for this call
+    const int e = j * kCbEnt + lane, ec = min(e, 575);
+    const int c = ec / 9, k = ec % 9;
+    const int off[2] = {c * 18 + k, c * 18 + 9 + k};
+    float sums[2];
+    quarter_sums<2, 1152>(a.part1 + (long long)slice * P * 1152, P, off, qs, sums);
+    if (tid >= 64) return;
     const float eta = a.eta[h];
     const float scale = (a.dot ? 1.0f : 2.0f) / (float)(a.gh * a.gw);
-    const float* src = a.sum1 + (long long)slice * 64 * 18;
     float* sl = a.sl + (long long)slice * 5 * 576;
-    float dsum = 0.f;
-    (void)P;
-    for (int e = tid; e < 576; e += 256) {
-        const int c = e / 9, k = e % 9;
-        const float gs = src[c * 18 + k], ds = src[c * 18 + 9 + k];
+    float d = 0.f;
+    if (e < 576) {
+        const float gs = sums[0], ds = sums[1];
         const float g = a.gsv ? a.gsv[(long long)slice * 576 + e] : scale * gs;
-        const float w1 = a.w0[(long long)h * 576 + e] - eta * g;
-        sl[e] = w1;
-        sl[576 + e] = scale * (-eta * ds); // (2/N) dg
-        sl[1152 + e] = ds;                 // dw1
+        sl[e] = a.w0[(long long)h * 576 + e] - eta * g; // w1
+        sl[576 + e] = scale * (-eta * ds);              // (2/N) dg
+        sl[1152 + e] = ds;                              // dw1
         sl[1728 + e] = g;
-        dsum -= ds * g;
+        d = -ds * g;
     }
-    de[tid] = dsum;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-        if (tid < s) de[tid] += de[tid + s];
-        __syncthreads();
-    }
-    if (tid == 0) a.deta_s[slice] = de[0];
+    // the 64 entries' deta terms, summed in a fixed tree over the wave
+#pragma unroll
+    for (int m = 32; m > 0; m >>= 1) d += __shfl_xor(d, m);
+    if (lane == 0) a.deta_s[(long long)slice * kCbBlk + j] = d;
 }
 
 // ---- pass 2: dQ, dV, dK and the partial sum_p dR[p] K[p+t] -------------
 template <bool BF>
 __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
     __shared__ float red[4 * 64 * 9];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    // the wave index is uniform: the row, and with it every address but the
+    // lane's channel offset, is formed on the scalar unit
+    const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const Task t = task_of(a, w);
     float acc[9];
 #pragma unroll
@@ -262,11 +318,9 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
         const Map<BF> Km = map_of<BF>(a.K, t.b, t.h, a.gh, a.gw, lane);
         const Map<BF> Vm = map_of<BF>(a.V, t.b, t.h, a.gh, a.gw, lane);
         const Map<BF> Dm = map_of<BF>(a.dZ, t.b, t.h, a.gh, a.gw, lane);
-        char* dKp = out_of<BF>(a.dK, t.b, t.h, lane);
-        char* dQp = out_of<BF>(a.dQ, t.b, t.h, lane);
-        char* dVp = out_of<BF>(a.dV, t.b, t.h, lane);
-        constexpr int es = Elt<BF>::esz;
-        const long long sK = a.dK.sn * es, sQ = a.dQ.sn * es, sV = a.dV.sn * es;
+        const Map<BF> dKm = map_of<BF>(a.dK, t.b, t.h, a.gh, a.gw, lane);
+        const Map<BF> dQm = map_of<BF>(a.dQ, t.b, t.h, a.gh, a.gw, lane);
+        const Map<BF> dVm = map_of<BF>(a.dV, t.b, t.h, a.gh, a.gw, lane);
         const float* sl = a.sl + (long long)t.slice * 5 * 576 + lane * 9;
         float wt[9], w1[9], dgs[9];
         // Under the dot-product loss g = -(1/N) sum_p V[p] K[p+t] has no
@@ -300,9 +354,10 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
                         p = fmaf(wt[3 * ii + jj], kv, p);
                         q = fmaf(dgs[3 * ii + jj], kv, q);
                     }
-                const bool in = yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw;
-                rr[i] = in ? p - vv[i] : 0.f;
-                dr[i] = in ? q : 0.f;
+                // a 0/1 factor, not a branch, zeroes positions off the grid
+                const float in = yy >= 0 && yy < a.gh && xx >= 0 && xx < a.gw ? 1.f : 0.f;
+                rr[i] = in * (p - vv[i]);
+                dr[i] = in * q;
             }
         };
         // initial windows for x = x0: K columns x0-2..x0+1 into kw[0..3]
@@ -394,10 +449,9 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
                     for (int i = 0; i < 3; ++i)
 #pragma unroll
                         for (int j = 0; j < 3; ++j) acc[3 * i + j] = fmaf(wd * drc, kw[j][i + 1], acc[3 * i + j]);
-                    const long long n = (long long)y * a.gw + x;
-                    Elt<BF>::st(dQp + n * sQ, dq);
-                    Elt<BF>::st(dKp + n * sK, dk);
-                    Elt<BF>::st(dVp + n * sV, -drc);
+                    dQm.put(y, x, dq);
+                    dKm.put(y, x, dk);
+                    dVm.put(y, x, -drc);
                 }
             }
         }
@@ -406,50 +460,70 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
     wave_sum_store<9>(acc, red, dst);
 }
 
-// ---- per-slice dw0 term: dw1 + the pass-2 partials in order -------------
-__global__ __launch_bounds__(256) void cbwd_slice_sum(CbArgs a) {
-    const int slice = blockIdx.x, tid = threadIdx.x;
+// ---- per-slice dw0 term, then the batch sums --------------------------
+// Workgroup (slice, j): the dw0 term dw1 + the pass-2 partials (in order) of
+// its 64 entries.  Each workgroup then counts itself done on its head's
+// counter (release: its terms are visible device-wide first); the last of
+// the head's B x kCbBlk workgroups (acquire) adds dw0 and deta over b in
+// order.  Which workgroup is last varies; the sums' order does not.
+__global__ __launch_bounds__(256) void cbwd_sums(CbArgs a) {
+    __shared__ float qs[4 * 64];
+    __shared__ int last;
+    const int slice = blockIdx.x / kCbBlk, j = blockIdx.x % kCbBlk, tid = threadIdx.x, lane = tid & 63;
+    const int h = slice % a.H;
+    const int P = a.ngrp * a.nseg;
+    const int e = j * kCbEnt + lane, ec = min(e, 575);
+    const int off[1] = {ec};
+    float s2[1];
+    quarter_sums<1, 576>(a.part2 + (long long)slice * P * 576, P, off, qs, s2);
     float* sl = a.sl + (long long)slice * 5 * 576;
-    const float* s2 = a.sum2 + (long long)slice * 576;
-    for (int e = tid; e < 576; e += 256) sl[2304 + e] = sl[1152 + e] + s2[e];
-}
-
-// ---- sum of per-workgroup partials, [slices][P][E] -> [slices][E] --------
-// Block (slice, 64-element chunk); its four waves each add a quarter of the
-// partials in order, then the four quarter sums are added in order: the
-// same order on every run.
-__global__ __launch_bounds__(256) void cbwd_sum_partials(const float* part, float* out, int P, int E) {
-    __shared__ float qs[4][64];
-    const int nchunk = (E + 63) / 64;
-    const int slice = blockIdx.x / nchunk, e = (blockIdx.x % nchunk) * 64 + (threadIdx.x & 63);
-    const int q = threadIdx.x >> 6, per = (P + 3) / 4, p0 = q * per, p1 = min(P, p0 + per);
-    float s = 0.f;
-    if (e < E) {
-        const float* src = part + (long long)slice * P * E + e;
-#pragma unroll 8
-        for (int p = p0; p < p1; ++p) s += src[(long long)p * E];
-    }
-    qs[q][threadIdx.x & 63] = s;
+    if (tid < 64 && e < 576) sl[2304 + e] = sl[1152 + e] + s2[0];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     __syncthreads();
-    if (q == 0 && e < E) {
-        const int l = threadIdx.x;
-        out[(long long)slice * E + e] = ((qs[0][l] + qs[1][l]) + qs[2][l]) + qs[3][l];
-    }
-}
-
-// ---- per-head batch sums -------------------------------------------------
-__global__ __launch_bounds__(256) void cbwd_batch(CbArgs a) {
-    const int h = blockIdx.x, tid = threadIdx.x;
-    for (int e = tid; e < 576; e += 256) {
-        float s = 0.f;
-        for (int b = 0; b < a.B; ++b) s += a.sl[((long long)b * a.H + h) * 5 * 576 + 2304 + e];
-        a.dw0[(long long)h * 576 + e] = s;
-    }
     if (tid == 0) {
-        float s = 0.f;
-        for (int b = 0; b < a.B; ++b) s += a.deta_s[(long long)b * a.H + h];
-        a.deta[h] = s;
+        const unsigned done = __hip_atomic_fetch_add(a.cnt + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = done == (unsigned)(a.B * kCbBlk - 1);
     }
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    // dw0: a thread per entry, the B terms loaded eight at a time
+    for (int ee = tid; ee < 576; ee += 256) {
+        const float* src = a.sl + (long long)h * 5 * 576 + 2304 + ee;
+        const long long step = (long long)a.H * 5 * 576;
+        float v = 0.f;
+        int b = 0;
+        for (; b + 8 <= a.B; b += 8) {
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) t[i] = src[(b + i) * step];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v += t[i];
+        }
+        for (; b < a.B; ++b) v += src[b * step];
+        a.dw0[(long long)h * 576 + ee] = v;
+    }
+    // deta: image b's term (its kCbBlk entry blocks in order) by thread b
+    // mod 256, then the images in order
+    float d = 0.f;
+    for (int b0 = 0; b0 < a.B; b0 += 256) {
+        const int b = b0 + tid;
+        if (b < a.B) {
+            const float* ds = a.deta_s + ((long long)b * a.H + h) * kCbBlk;
+            float t[kCbBlk];
+#pragma unroll
+            for (int jj = 0; jj < kCbBlk; ++jj) t[jj] = ds[jj];
+            float u = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < kCbBlk; ++jj) u += t[jj];
+            qs[tid] = u;
+        }
+        __syncthreads();
+        if (tid == 0)
+            for (int i = 0; i < min(256, a.B - b0); ++i) d += qs[i];
+        __syncthreads();
+    }
+    if (tid == 0) a.deta[h] = d;
 }
 
 struct CbPlan {
@@ -472,7 +546,7 @@ size_t conv_bwd_ws_bytes(int B, int H, int gh, int gw) {
     const CbPlan p = cb_plan(gh, gw);
     const size_t P = (size_t)p.ngrp * p.nseg;
     return a256(slices * P * 64 * 18 * 4) + a256(slices * P * 576 * 4) + a256(slices * 5 * 576 * 4) +
-           a256(slices * 4) + a256(slices * 1152 * 4) + a256(slices * 576 * 4);
+           a256(slices * kCbBlk * 4) + a256((size_t)H * 4);
 }
 
 hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
@@ -495,10 +569,8 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
     a.sl = (float*)w;
     w += a256(slices * 5 * 576 * 4);
     a.deta_s = (float*)w;
-    w += a256(slices * 4);
-    a.sum1 = (float*)w;
-    w += a256(slices * 1152 * 4);
-    a.sum2 = (float*)w;
+    w += a256(slices * kCbBlk * 4);
+    a.cnt = (unsigned*)w;
     const dim3 grid((unsigned)(slices * P)), block(256);
     if (s.bf16) {
         if (s.saved) hipLaunchKernelGGL((cbwd_pass1<true, true>), grid, block, 0, stream, a);
@@ -507,15 +579,11 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
         if (s.saved) hipLaunchKernelGGL((cbwd_pass1<false, true>), grid, block, 0, stream, a);
         else hipLaunchKernelGGL((cbwd_pass1<false, false>), grid, block, 0, stream, a);
     }
-    hipLaunchKernelGGL(cbwd_sum_partials, dim3((unsigned)(slices * 18)), block, 0, stream, (const float*)a.part1,
-                       a.sum1, (int)P, 1152);
-    hipLaunchKernelGGL(cbwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
+    const dim3 sgrid((unsigned)(slices * kCbBlk));
+    hipLaunchKernelGGL(cbwd_reduce, sgrid, block, 0, stream, a);
     if (s.bf16) hipLaunchKernelGGL((cbwd_pass2<true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((cbwd_pass2<false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL(cbwd_sum_partials, dim3((unsigned)(slices * 9)), block, 0, stream, (const float*)a.part2,
-                       a.sum2, (int)P, 576);
-    hipLaunchKernelGGL(cbwd_slice_sum, dim3((unsigned)slices), block, 0, stream, a);
-    hipLaunchKernelGGL(cbwd_batch, dim3((unsigned)s.H), block, 0, stream, a);
+    hipLaunchKernelGGL(cbwd_sums, sgrid, block, 0, stream, a);
     return hipGetLastError();
 }
 
