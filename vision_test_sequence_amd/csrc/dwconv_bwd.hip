@@ -236,53 +236,57 @@ __global__ __launch_bounds__(256) void cbwd_pass1(CbArgs a) {
 
 // ---- per-slice reduce ---------------------------------------------------
 // Workgroup (slice, j) takes entries e = 64 j + lane of the slice's 576
-// (channel e / 9, tap e % 9); wave q adds partials [q P/4, (q+1) P/4) in
-// order, all of its loads issued before the first add, and the four quarter
-// sums are added in order.
-constexpr int kCbEnt = 64;                     // entries per reduce / sums workgroup
+// (channel e / 9, tap e % 9) and sums their P partials: wave q of kCbSumW
+// adds partials [q per, (q+1) per) in order, eight loads issued before
+// their adds (a slot past the range adds 0), and the waves' sums are added
+// in wave order.
+constexpr int kCbEnt = 64;                          // entries per reduce / sums workgroup
 constexpr int kCbBlk = (576 + kCbEnt - 1) / kCbEnt; // such workgroups per slice
+constexpr int kCbSumW = 4;                          // waves per reduce / sums workgroup
 template <int NV, int STRIDE>
-__device__ __forceinline__ void quarter_sums(const float* src, int P, const int* off, float* qs, float* out) {
-    const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
-    const int per = (P + 3) / 4, p0 = q * per, p1 = min(P, p0 + per);
+__device__ __forceinline__ void part_sums(const float* src, int P, const int* off, float* qs, float* out) {
+    const int lane = threadIdx.x & 63, q = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int per = (P + kCbSumW - 1) / kCbSumW, p0 = q * per, p1 = min(P, p0 + per);
     float s[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) s[v] = 0.f;
-    int p = p0;
-    for (; p + 8 <= p1; p += 8) {
+    for (int p = p0; p < p1; p += 8) {
         float t[8][NV];
 #pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pc = min(p + i, p1 - 1);
+#pragma unroll
+            for (int v = 0; v < NV; ++v) t[i][v] = src[(long long)pc * STRIDE + off[v]];
+        }
+#pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
-            for (int v = 0; v < NV; ++v) t[i][v] = src[(long long)(p + i) * STRIDE + off[v]];
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int v = 0; v < NV; ++v) s[v] += t[i][v];
+            for (int v = 0; v < NV; ++v) s[v] += p + i < p1 ? t[i][v] : 0.f;
     }
-    for (; p < p1; ++p)
 #pragma unroll
-        for (int v = 0; v < NV; ++v) s[v] += src[(long long)p * STRIDE + off[v]];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) qs[(v * 4 + q) * 64 + lane] = s[v];
+    for (int v = 0; v < NV; ++v) qs[(v * kCbSumW + q) * 64 + lane] = s[v];
     __syncthreads();
 #pragma unroll
-    for (int v = 0; v < NV; ++v)
-        out[v] = ((qs[(v * 4) * 64 + lane] + qs[(v * 4 + 1) * 64 + lane]) + qs[(v * 4 + 2) * 64 + lane]) +
-                 qs[(v * 4 + 3) * 64 + lane];
+    for (int v = 0; v < NV; ++v) {
+        float x = qs[(v * kCbSumW) * 64 + lane];
+#pragma unroll
+        for (int w = 1; w < kCbSumW; ++w) x += qs[(v * kCbSumW + w) * 64 + lane];
+        out[v] = x;
+    }
 }
 
-__global__ __launch_bounds__(256) void cbwd_reduce(CbArgs a) {
-    __shared__ float qs[2 * 4 * 64];
+__global__ __launch_bounds__(64 * kCbSumW) void cbwd_reduce(CbArgs a) {
+    __shared__ float qs[2 * kCbSumW * 64];
     const int slice = blockIdx.x / kCbBlk, j = blockIdx.x % kCbBlk, tid = threadIdx.x, lane = tid & 63;
     const int h = slice % a.H;
     const int P = a.ngrp * a.nseg;
-    if (blockIdx.x == 0 && tid < a.H) a.cnt[tid] = 0u; // the sums' counters, for this call
+    if (blockIdx.x == 0) // the sums' counters, for this call
+        for (int i = tid; i < a.H; i += 64 * kCbSumW) a.cnt[i] = 0u;
     const int e = j * kCbEnt + lane, ec = min(e, 575);
     const int c = ec / 9, k = ec % 9;
     const int off[2] = {c * 18 + k, c * 18 + 9 + k};
     float sums[2];
-    quarter_sums<2, 1152>(a.part1 + (long long)slice * P * 1152, P, off, qs, sums);
+    part_sums<2, 1152>(a.part1 + (long long)slice * P * 1152, P, off, qs, sums);
     if (tid >= 64) return;
     const float eta = a.eta[h];
     const float scale = (a.dot ? 1.0f : 2.0f) / (float)(a.gh * a.gw);
@@ -466,8 +470,8 @@ __global__ __launch_bounds__(256) void cbwd_pass2(CbArgs a) {
 // counter (release: its terms are visible device-wide first); the last of
 // the head's B x kCbBlk workgroups (acquire) adds dw0 and deta over b in
 // order.  Which workgroup is last varies; the sums' order does not.
-__global__ __launch_bounds__(256) void cbwd_sums(CbArgs a) {
-    __shared__ float qs[4 * 64];
+__global__ __launch_bounds__(64 * kCbSumW) void cbwd_sums(CbArgs a) {
+    __shared__ float qs[kCbSumW * 64];
     __shared__ int last;
     const int slice = blockIdx.x / kCbBlk, j = blockIdx.x % kCbBlk, tid = threadIdx.x, lane = tid & 63;
     const int h = slice % a.H;
@@ -475,20 +479,23 @@ __global__ __launch_bounds__(256) void cbwd_sums(CbArgs a) {
     const int e = j * kCbEnt + lane, ec = min(e, 575);
     const int off[1] = {ec};
     float s2[1];
-    quarter_sums<1, 576>(a.part2 + (long long)slice * P * 576, P, off, qs, s2);
+    part_sums<1, 576>(a.part2 + (long long)slice * P * 576, P, off, qs, s2);
     float* sl = a.sl + (long long)slice * 5 * 576;
     if (tid < 64 && e < 576) sl[2304 + e] = sl[1152 + e] + s2[0];
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    // the stores have reached L2 before the barrier; one release fence (an
+    // L2 write-back, costly per wave) then publishes them device-wide
+    drain_vmem();
     __syncthreads();
     if (tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         const unsigned done = __hip_atomic_fetch_add(a.cnt + h, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         last = done == (unsigned)(a.B * kCbBlk - 1);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     }
     __syncthreads();
     if (!last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // dw0: a thread per entry, the B terms loaded eight at a time
-    for (int ee = tid; ee < 576; ee += 256) {
+    for (int ee = tid; ee < 576; ee += 64 * kCbSumW) {
         const float* src = a.sl + (long long)h * 5 * 576 + 2304 + ee;
         const long long step = (long long)a.H * 5 * 576;
         float v = 0.f;
@@ -504,9 +511,9 @@ __global__ __launch_bounds__(256) void cbwd_sums(CbArgs a) {
         a.dw0[(long long)h * 576 + ee] = v;
     }
     // deta: image b's term (its kCbBlk entry blocks in order) by thread b
-    // mod 256, then the images in order
+    // mod the block size, then the images in order
     float d = 0.f;
-    for (int b0 = 0; b0 < a.B; b0 += 256) {
+    for (int b0 = 0; b0 < a.B; b0 += 64 * kCbSumW) {
         const int b = b0 + tid;
         if (b < a.B) {
             const float* ds = a.deta_s + ((long long)b * a.H + h) * kCbBlk;
@@ -520,7 +527,7 @@ __global__ __launch_bounds__(256) void cbwd_sums(CbArgs a) {
         }
         __syncthreads();
         if (tid == 0)
-            for (int i = 0; i < min(256, a.B - b0); ++i) d += qs[i];
+            for (int i = 0; i < min(64 * kCbSumW, a.B - b0); ++i) d += qs[i];
         __syncthreads();
     }
     if (tid == 0) a.deta[h] = d;
@@ -580,10 +587,10 @@ hipError_t launch_conv_bwd(const ConvBwdLaunch& s, hipStream_t stream) {
         else hipLaunchKernelGGL((cbwd_pass1<false, false>), grid, block, 0, stream, a);
     }
     const dim3 sgrid((unsigned)(slices * kCbBlk));
-    hipLaunchKernelGGL(cbwd_reduce, sgrid, block, 0, stream, a);
+    hipLaunchKernelGGL(cbwd_reduce, sgrid, dim3(64 * kCbSumW), 0, stream, a);
     if (s.bf16) hipLaunchKernelGGL((cbwd_pass2<true>), grid, block, 0, stream, a);
     else hipLaunchKernelGGL((cbwd_pass2<false>), grid, block, 0, stream, a);
-    hipLaunchKernelGGL(cbwd_sums, sgrid, block, 0, stream, a);
+    hipLaunchKernelGGL(cbwd_sums, sgrid, dim3(64 * kCbSumW), 0, stream, a);
     return hipGetLastError();
 }
 
