@@ -130,3 +130,22 @@ def test_deterministic():
     b = _run(K, Q, V, W0, eta, dZ)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_workspace_reuse_across_shapes():
+    """bf16 pass 1 counts each slice's finished splits on the workspace's
+    counter block and the last one resets it: calls of different shapes
+    alternating on one workspace give the same results every time."""
+    banner("bwd workspace reuse across shapes")
+    d = _dev()
+    sets = []
+    for (B, H, N), seed in (((2, 3, 700), 1510), ((4, 3, 4096), 1511), ((1, 2, 129), 1512)):
+        inp = wl.draw(B, H, N, seed=seed, dtype="bf16", eta_fixed=None, backward=True)
+        sets.append([inp[k].to(d) for k in ("K", "Q", "V", "W0", "eta", "dZ")])
+    first = [_run(*s) for s in sets]
+    for _ in range(2):
+        for s, ref in zip(sets, first):
+            again = _run(*s)
+            for x, y, name in zip(again, ref, ("dK", "dQ", "dV", "dW0", "deta")):
+                assert torch.equal(x, y), name
+    _check(dict(zip(("K", "Q", "V", "W0", "eta", "dZ"), (t.cpu() for t in sets[1]))))

@@ -585,19 +585,32 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     __syncthreads();
     // bf16 operator fragments for pass 2 (A operand of Wt[o][k] with output
     // rows o = perm_row(rb, m)): piece (f, rb, kb, lane) holds
-    // k = 32 kb + 8 g + (0..7); f = 0: beta dW1^T, 1: -beta M, 2: beta dW1
+    // k = 32 kb + 8 g + (0..7); f = 0: beta dW1^T, 1: -beta M, 2: beta dW1.
+    // Each piece is eight consecutive floats of a row of dW1^T, M or dW1:
+    // dW1^T is first written to W (free again), so all three are read as
+    // two 16-byte LDS reads per piece.
     if (a.fr) {
-        u32x4* fr = a.fr + (long long)slice * 1536;
-        for (int pc = tid; pc < 1536; pc += kThreads) {
-            const int f = pc >> 9, rb = (pc >> 7) & 3, kb = (pc >> 6) & 1, ln = pc & 63;
-            const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
-            float v[8];
+        {
+            const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int k = k0 + j;
-                v[j] = f == 0 ? beta * D[k * MB + o] : (f == 1 ? -beta * Am[o * MB + k] : beta * D[o * MB + k]);
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 dv = *reinterpret_cast<const f32x4*>(D + (r0 + i) * MB + c0);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) W[(c0 + j) * MB + r0 + i] = dv[j];
             }
-            fr[pc] = u32x4{pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7])};
+        }
+        __syncthreads();
+        u32x4* fr = a.fr + (long long)slice * 1536;
+#pragma unroll
+        for (int it = 0; it < 1536 / kThreads; ++it) {
+            const int f = it / (512 / kThreads), pc = (it % (512 / kThreads)) * kThreads + tid;
+            const int rb = pc >> 7, kb = (pc >> 6) & 1, ln = pc & 63;
+            const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
+            const float* src = (f == 0 ? W : (f == 1 ? Am : D)) + o * MB + k0;
+            const float sc = f == 1 ? -beta : beta;
+            const f32x4 x = *reinterpret_cast<const f32x4*>(src), y = *reinterpret_cast<const f32x4*>(src + 4);
+            fr[f * 512 + pc] = u32x4{pack_bf2(sc * x[0], sc * x[1]), pack_bf2(sc * x[2], sc * x[3]),
+                                     pack_bf2(sc * y[0], sc * y[1]), pack_bf2(sc * y[2], sc * y[3])};
         }
     }
     // deta term: fixed-order tree over the threads' partial sums
