@@ -414,62 +414,102 @@ __global__ __launch_bounds__(kSbT) void sbwd_outputs_mc(SbArgs a) {
     };
     auto col16 = [&](const char* t) { return tr4(t + (4 * g + e) * kMcRow + 2 * (16 * w + 4 * aa)); };
     v4f oQ = z4, oK = z4, oV = z4; // outputs at rows 4g+i, channel 16w+m
-    int tok_lo = 0, n = 0;
-    for (int p = 0; p < ndi; ++p) {
-        const int di = di0 + p, dir = chain_dir(a, di), ch = slice * a.nd + di;
-        const int mb = (!PLANES && a.nd == 2 && dir == 1) ? a.nch - 1 - c : c;
-        n = nc_of(a, mb);
-        tok_lo = dir ? a.N - mb * a.b - n : mb * a.b;
-        const float alpha = -2.f * eta / (float)n;
-        if (p > 0) __syncthreads(); // the previous pass has read every tile
-        // K, Q, V, dZ rows (zeros past n); the view is picked by value (a
-        // reference picked at run time would copy the arguments to scratch)
+    // One pass per direction.  Every load of both passes is issued before
+    // the first pass's products (registers), so the second pass does not
+    // wait for memory again.  Loads are branch-free: a row past n loads a
+    // clamped row and is zeroed after the load.
+    struct Pass {
+        int dir, ch, mb, n, tok_lo;
+        u32x4 rows[2];  // K, Q, V, dZ rows: thread t holds 16-byte chunks t and t + 256
+        f32x4 dr;       // dR, row tid / 16, channels 4 (tid % 16) ..
+        u32x4 ws[2], gs[2]; // Ws, dWn chunks t and t + 256
+        float dv[4];    // dR at rows 4g+i, channel 16w+m
+    };
+    auto pass_of = [&](int p) __attribute__((always_inline)) {
+        Pass q;
+        const int di = di0 + p;
+        q.dir = chain_dir(a, di);
+        q.ch = slice * a.nd + di;
+        q.mb = (!PLANES && a.nd == 2 && q.dir == 1) ? a.nch - 1 - c : c;
+        q.n = nc_of(a, q.mb);
+        q.tok_lo = q.dir ? a.N - q.mb * a.b - q.n : q.mb * a.b;
+        return q;
+    };
+    auto issue = [&](Pass& q) __attribute__((always_inline)) {
+        // the views are picked by value (a reference picked at run time
+        // would copy the arguments to scratch)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const int q = tid + kSbT * j, t = q >> 7, r = (q >> 3) & 15, ck = q & 7;
+            const int e = tid + kSbT * j, t = e >> 7, r = (e >> 3) & 15, ck = e & 7;
             const View4 v = j == 0 ? (t == 0 ? a.K : a.Q) : (t == 2 ? a.V : a.dZ);
-            u32x4 x{0u, 0u, 0u, 0u};
-            if (r < n)
-                x = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(v.ptr) + bb * v.sb + h * v.sh +
-                                                    (long long)(tok_lo + r) * v.sn + 8 * ck);
+            q.rows[j] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(v.ptr) + bb * v.sb + h * v.sh +
+                                                        (long long)(q.tok_lo + min(r, q.n - 1)) * v.sn + 8 * ck);
+        }
+        {
+            const int r = min(tid >> 4, q.n - 1), c4 = tid & 15;
+            const int pos = q.dir ? a.N - 1 - (q.tok_lo + r) : q.tok_lo + r;
+            q.dr = *reinterpret_cast<const f32x4*>(a.dRp + ((long long)q.ch * a.N + pos) * 64 + 4 * c4);
+        }
+        const u32x4* ws = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.ws_state) +
+                                                         ((long long)q.ch * a.nch + q.mb) * 4096);
+        const u32x4* gs = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.dwn_state) +
+                                                         ((long long)q.ch * a.nch + q.mb) * 4096);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            q.ws[j] = ws[tid + kSbT * j];
+            q.gs[j] = gs[tid + kSbT * j];
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = min(4 * g + i, q.n - 1);
+            const int pos = q.dir ? a.N - 1 - (q.tok_lo + r) : q.tok_lo + r;
+            q.dv[i] = a.dRp[((long long)q.ch * a.N + pos) * 64 + 16 * w + m];
+        }
+    };
+    // (the two passes are separate variables: an array indexed by the pass
+    // would live in scratch memory)
+    Pass p0 = pass_of(0), p1 = p0;
+    issue(p0);
+    if (ndi > 1) {
+        p1 = pass_of(1);
+        issue(p1);
+    }
+    int tok_lo = 0, n = 0;
+    auto run = [&](const Pass& q, bool later) __attribute__((always_inline)) {
+        const int dir = q.dir, ch = q.ch, mb = q.mb;
+        n = q.n;
+        tok_lo = q.tok_lo;
+        const float alpha = -2.f * eta / (float)n;
+        if (later) __syncthreads(); // the previous pass has read every tile
+        // K, Q, V, dZ rows (zeros past n; dZ scaled as the direction
+        // receives it)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + kSbT * j, t = e >> 7, r = (e >> 3) & 15, ck = e & 7;
+            u32x4 x = q.rows[j];
             if (t == 3)
 #pragma unroll
                 for (int k = 0; k < 4; ++k) x[k] = pack_bf2(zs * bflo(x[k]), zs * bfhi(x[k]));
+            if (r >= n) x = u32x4{0u, 0u, 0u, 0u};
             *reinterpret_cast<u32x4*>(lds + t * kMcTile + r * kMcRow + 16 * ck) = x;
         }
-        // dR rows (fp32, by walk position)
+        // dR rows (bf16 in LDS)
         {
             const int r = tid >> 4, c4 = tid & 15;
-            f32x4 x{0.f, 0.f, 0.f, 0.f};
-            if (r < n) {
-                const int pos = dir ? a.N - 1 - (tok_lo + r) : tok_lo + r;
-                x = *reinterpret_cast<const f32x4*>(a.dRp + ((long long)ch * a.N + pos) * 64 + 4 * c4);
-            }
+            const f32x4 x = r < n ? q.dr : f32x4{0.f, 0.f, 0.f, 0.f};
             *reinterpret_cast<u32x2*>(tD + r * kMcRow + 8 * c4) = u32x2{pack_bf2(x[0], x[1]), pack_bf2(x[2], x[3])};
         }
         // Ws and dWn (bf16, stored so by the matrix-core walks)
-        {
-            const u32x4* ws = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.ws_state) +
-                                                             ((long long)ch * a.nch + mb) * 4096);
-            const u32x4* gs = reinterpret_cast<const u32x4*>(reinterpret_cast<const bf16_t*>(a.dwn_state) +
-                                                             ((long long)ch * a.nch + mb) * 4096);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int q = tid + kSbT * j, o = (q >> 3) * kMcRow + 16 * (q & 7);
-                const u32x4 x = ws[q], y = gs[q];
-                *reinterpret_cast<u32x4*>(sW + o) = x;
-                *reinterpret_cast<u32x4*>(sG + o) = y;
-            }
+        for (int j = 0; j < 2; ++j) {
+            const int e = tid + kSbT * j, o = (e >> 3) * kMcRow + 16 * (e & 7);
+            *reinterpret_cast<u32x4*>(sW + o) = q.ws[j];
+            *reinterpret_cast<u32x4*>(sG + o) = q.gs[j];
         }
         // dV = -dR (fp32)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = 4 * g + i;
-            if (r < n) {
-                const int pos = dir ? a.N - 1 - (tok_lo + r) : tok_lo + r;
-                oV[i] -= a.dRp[((long long)ch * a.N + pos) * 64 + 16 * w + m];
-            }
-        }
+        for (int i = 0; i < 4; ++i)
+            if (4 * g + i < n) oV[i] -= q.dv[i];
         __syncthreads();
         // R = K Ws^T - V at channels 16w + m (B operand: Ws row 16w+m), to LDS
         {
@@ -519,7 +559,9 @@ __global__ __launch_bounds__(kSbT) void sbwd_outputs_mc(SbArgs a) {
         if (lane == 0) red[w] = dal;
         __syncthreads();
         if (tid == 0) a.detac[(long long)ch * a.nch + mb] = (-2.f / (float)n) * (((red[0] + red[1]) + red[2]) + red[3]);
-    }
+    };
+    run(p0, false);
+    if (ndi > 1) run(p1, true);
     if (PLANES) {
         const long long pl = (long long)a.B * a.H * a.N * 64;
         float* pb = a.planes + (long long)di0 * 3 * pl;
