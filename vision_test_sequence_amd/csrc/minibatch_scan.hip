@@ -585,12 +585,14 @@ struct BwdWalkArgs {
     float* dW0c;  // [chains][64][64]
     int nd;
 };
-constexpr int kBD = 6; // chunks in flight (register prefetch depth)
+constexpr int kBD = 8; // chunks in flight (register prefetch depth)
 static_assert(kBD % 2 == 0, "LDS buffer sets alternate with the unrolled index");
 __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
     const ScanArgs& a = w.s;
-    // two sets of buffers, alternating mini-batches (kBD is even)
+    // two sets of buffers, alternating mini-batches (kBD is even), and the
+    // wave's dR tile (16 tokens x 16 channels fp32, rows of 20 floats)
     __shared__ __attribute__((aligned(16))) char lds[2 * (2 * kKBuf + kVBuf)];
+    __shared__ __attribute__((aligned(16))) float drt[16 * 20];
     // the four row blocks of a chain on one XCD (see states_wave)
     const SliceSplit cs = map_block(wid, 4, 1);
     if (cs.slice >= a.slices * w.nd) return; // padding of the XCD-aware grid
@@ -712,12 +714,19 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
             const v4f KY = mfma32(as_v8bf(r.k[1]), as_v8bf(ys[1]),
                                   mfma32(as_v8bf(r.k[0]), as_v8bf(ys[0]), mfma32(as_v8bf(sA), as_v8bf(zB), zero4)));
             const v4f dR{alpha * KY[0], alpha * KY[1], alpha * KY[2], alpha * KY[3]};
-            // dR by walk position (token slot 4g+i of mini-batch c, channel 16 rb + m)
+            // dR by walk position (token slot 4g+i of mini-batch c, channel
+            // 16 rb + m), turned through LDS so that a lane holds four
+            // channels of one token and the wave stores it with one
+            // instruction: a wave can keep only so many memory operations in
+            // flight, and with one store per token slot they, not the loads
+            // a few mini-batches ahead, bounded the walk
+#pragma unroll
+            for (int i = 0; i < 4; ++i) drt[(4 * g + i) * 20 + m] = dR[i];
             if (live) {
                 const int n = c == nch - 1 ? N - (nch - 1) * b : b;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (4 * g + i < n) dRp[((long long)c * b + 4 * g + i) * 64 + 16 * rb + m] = dR[i];
+                const int t = lane >> 2, q4 = lane & 3;
+                const f32x4 x = *reinterpret_cast<const f32x4*>(drt + t * 20 + 4 * q4);
+                if (t < n) *reinterpret_cast<f32x4*>(dRp + ((long long)c * b + t) * 64 + 16 * rb + 4 * q4) = x;
             }
             const u32x2 dr2{pack_bf2(dR[0], dR[1]), pack_bf2(dR[2], dR[3])};
             // the next mini-batch's operands, one step ahead of their use
@@ -759,7 +768,7 @@ __device__ __forceinline__ void grad_wave(const BwdWalkArgs& w, int wid) {
 // CU (used when the grid fits the device one workgroup per CU; single-wave
 // workgroups of the two walks packed onto shared SIMDs ran 252 us against
 // 88 + 179 us apart).
-constexpr int kWalksLds = kNK * kKBuf + 2 * kVBuf + 2 * (2 * kKBuf + kVBuf); // the two waves' own LDS
+constexpr int kWalksLds = kNK * kKBuf + 2 * kVBuf + 2 * (2 * kKBuf + kVBuf) + 16 * 20 * 4; // the two waves' own LDS
 template <bool Spread>
 __global__ __launch_bounds__(128, 1) void scan_bwd_walks(BwdWalkArgs w, bf16_t* states) {
     __shared__ char spread[Spread ? kOneCuLds - kWalksLds : 16];
