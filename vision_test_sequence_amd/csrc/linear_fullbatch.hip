@@ -1237,6 +1237,7 @@ static_assert(8192 + 128 + 64 * MP <= 3 * 26 * 256, "phase-2 regions below [A; C
 
 // ----------------------------------------------------- streaming kernel --
 constexpr int kStages = 3;         // K/V tiles in flight (registers)
+constexpr int kQRing = 8;          // apply steps whose Q rows are in flight per wave
 constexpr int kStageBytes = 32768; // K tile + V tile
 
 template <bool BF, bool XC>
@@ -1300,17 +1301,20 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
     // rows are clamped into the range, so the loads are unconditional.
     const int nsteps = (t1 - t0 + 15) / 16;
     constexpr int QV = BF ? 2 : 4; // 16-byte loads per lane per step
+    // this wave's k-th apply step (tokens t0 + 16 (w + 4 k) ..), clamped
+    // into the range so that the load is unconditional
+    auto qload = [&](int k, u32x4* q) __attribute__((always_inline)) {
+        const int tok = min(t0 + (w + 4 * k) * 16 + m, t1 - 1);
+#pragma unroll
+        for (int hh = 0; hh < QV; ++hh) {
+            const int ch = BF ? (32 * hh + 8 * g) : (16 * hh + 4 * g);
+            q[hh] = *reinterpret_cast<const u32x4*>(c.Qp + tok * c.Qsn + ch * Cfg::esz);
+        }
+    };
     u32x4 qpre[Cfg::qpre][QV];
     if (ntiles > 0 && a.Z.ptr) {
 #pragma unroll
-        for (int k = 0; k < Cfg::qpre; ++k) {
-            const int tok = min(t0 + (w + 4 * k) * 16 + m, t1 - 1);
-#pragma unroll
-            for (int hh = 0; hh < QV; ++hh) {
-                const int ch = BF ? (32 * hh + 8 * g) : (16 * hh + 4 * g);
-                qpre[k][hh] = *reinterpret_cast<const u32x4*>(c.Qp + tok * c.Qsn + ch * Cfg::esz);
-            }
-        }
+        for (int k = 0; k < Cfg::qpre; ++k) qload(k, qpre[k]);
     }
     f32x4 w0r[4];
     load_w0(a, c.h, w0r);
@@ -1364,18 +1368,23 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
             return;
         }
         const unsigned rel = release_begin(a, c.slice);
+        u32x4 qr[kQRing][QV];
+#pragma unroll
+        for (int u = 0; u < kQRing; ++u) qload(Cfg::qpre + u, qr[u]);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
             const int tok = t0 + st * 16 + m;
             if (st < nsteps) apply_bf(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
-        for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
-            const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
-            u32x4 q[2];
-            q[0] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (8 * g) * 2);
-            q[1] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (32 + 8 * g) * 2);
-            apply_bf(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
+        for (int k0 = Cfg::qpre; w + 4 * k0 < nsteps; k0 += kQRing) {
+#pragma unroll
+            for (int u = 0; u < kQRing; ++u) {
+                const int st = w + 4 * (k0 + u);
+                const int tok = t0 + st * 16 + m;
+                if (st < nsteps) apply_bf(wf, qr[u], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
+                qload(k0 + u + kQRing, qr[u]);
+            }
         }
         release_end(a, c.slice, rel);
     } else {
@@ -1386,19 +1395,23 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
             return;
         }
         const unsigned rel = release_begin(a, c.slice);
+        u32x4 qr[kQRing][QV];
+#pragma unroll
+        for (int u = 0; u < kQRing; ++u) qload(Cfg::qpre + u, qr[u]);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
             const int tok = t0 + st * 16 + m;
             if (st < nsteps) apply_f32(wf, qpre[k], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
         }
-        for (int st = w + 4 * Cfg::qpre; st < nsteps; st += 4) {
-            const int tok = t0 + st * 16 + m, tq = min(tok, t1 - 1);
-            u32x4 q[4];
+        for (int k0 = Cfg::qpre; w + 4 * k0 < nsteps; k0 += kQRing) {
 #pragma unroll
-            for (int hh = 0; hh < 4; ++hh)
-                q[hh] = *reinterpret_cast<const u32x4*>(c.Qp + tq * c.Qsn + (16 * hh + 4 * g) * 4);
-            apply_f32(wf, q, c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
+            for (int u = 0; u < kQRing; ++u) {
+                const int st = w + 4 * (k0 + u);
+                const int tok = t0 + st * 16 + m;
+                if (st < nsteps) apply_f32(wf, qr[u], c.Zp + (long long)tok * c.Zsn, tok < t1, g, poison);
+                qload(k0 + u + kQRing, qr[u]);
+            }
         }
         release_end(a, c.slice, rel);
     }
@@ -1485,17 +1498,20 @@ __device__ __forceinline__ void stage_mat(float* dst, const float* src) {
 
 // The lane's operand fragment of token row `row` (bf16: channels 32 h + 8 g
 // .. +8 for h = 0, 1; fp32: channels 16 h + 4 g .. +4 for h = 0..3), zeros
-// past the last token.
+// past the last token: loaded unconditionally from a row clamped into the
+// range and zeroed after the load (a branch around the load would make the
+// compiler wait for every load in flight at the join, so the loads of
+// several steps could not be in flight together).
 template <bool BF>
-__device__ __forceinline__ void row_frag(const char* base, long long sn, int row, int N, int g, u32x4* q) {
+__device__ __forceinline__ void row_frags_masked(const char* base, long long sn, int row, int N, int g, u32x4* q) {
     constexpr int nh = BF ? 2 : 4;
+    const unsigned keep = row < N ? ~0u : 0u;
+    const char* r = base + (long long)min(row, N - 1) * sn;
 #pragma unroll
     for (int hh = 0; hh < nh; ++hh) {
-        q[hh] = u32x4{0u, 0u, 0u, 0u};
-        if (row < N) {
-            const int ch = BF ? 32 * hh + 8 * g : 16 * hh + 4 * g;
-            q[hh] = *reinterpret_cast<const u32x4*>(base + (long long)row * sn + ch * (BF ? 2 : 4));
-        }
+        const int ch = BF ? 32 * hh + 8 * g : 16 * hh + 4 * g;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(r + ch * (BF ? 2 : 4));
+        q[hh] = u32x4{x[0] & keep, x[1] & keep, x[2] & keep, x[3] & keep};
     }
 }
 
@@ -1514,21 +1530,24 @@ __global__ __launch_bounds__(kThreads) void lin_apply(LinApplyArgs a) {
     const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)esz;
     char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)esz;
     const long long Qsn = a.Q.sn * esz, Zsn = a.Z.sn * esz;
+    // every step's Q rows are loaded before the first product
+    constexpr int nh = BF ? 2 : 4;
+    u32x4 q[4][nh];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) row_frags_masked<BF>(Qp, Qsn, tb * 256 + w * 64 + st * 16 + m, a.N, g, q[st]);
     if constexpr (BF) {
         const W1FragsBF wf = w1_frags_bf(mW, g, m);
+#pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int row = tb * 256 + w * 64 + st * 16 + m;
-            u32x4 q[2];
-            row_frag<true>(Qp, Qsn, row, a.N, g, q);
-            apply_bf(wf, q, Zp + (long long)row * Zsn, row < a.N, g, false);
+            apply_bf(wf, q[st], Zp + (long long)row * Zsn, row < a.N, g, false);
         }
     } else {
         const W1FragsF32 wf = w1_frags_f32(mW, g, m);
+#pragma unroll
         for (int st = 0; st < 4; ++st) {
             const int row = tb * 256 + w * 64 + st * 16 + m;
-            u32x4 q[4];
-            row_frag<false>(Qp, Qsn, row, a.N, g, q);
-            apply_f32(wf, q, Zp + (long long)row * Zsn, row < a.N, g, false);
+            apply_f32(wf, q[st], Zp + (long long)row * Zsn, row < a.N, g, false);
         }
     }
 }
@@ -1561,38 +1580,51 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
         rr += __shfl_xor(rr, 32);
         if (g == 0 && row < a.N) out[row] = (a.dot ? 1.0f : 2.0f) * sqrtf(rr) * sqrtf(kk);
     };
+    // every step's K and V rows are loaded before the first product
+    // (branch-free: clamped rows, zeroed past N)
+    constexpr int nh = BF ? 2 : 4;
+    u32x4 kq[4][nh], vq[4][nh];
+#pragma unroll
     for (int st = 0; st < 4; ++st) {
         const int row = tb * 256 + w * 64 + st * 16 + m;
+        row_frags_masked<BF>(Kp, Ksn, row, a.N, g, kq[st]);
         // v at the lane's output channels 8 g .. 8 g + 7 and 32 + 8 g .. +7
+        const unsigned keep = row < a.N ? ~0u : 0u;
+        const char* vr = Vp + (long long)min(row, a.N - 1) * Vsn;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int ch = 32 * half + 8 * g;
+#pragma unroll
+            for (int p = 0; p < nh / 2; ++p) {
+                const u32x4 x = *reinterpret_cast<const u32x4*>(vr + (ch + 4 * p) * (BF ? 2 : 4));
+                vq[st][half * (nh / 2) + p] = u32x4{x[0] & keep, x[1] & keep, x[2] & keep, x[3] & keep};
+            }
+        }
+    }
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int row = tb * 256 + w * 64 + st * 16 + m;
         float vv[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) vv[j] = 0.f;
-        if (row < a.N) {
-            const char* vr = Vp + (long long)row * Vsn;
+        for (int half = 0; half < 2; ++half) {
+            if constexpr (BF) {
+                const u32x4 u = vq[st][half];
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const int ch = 32 * half + 8 * g;
-                if constexpr (BF) {
-                    const u32x4 u = *reinterpret_cast<const u32x4*>(vr + ch * 2);
+                for (int k = 0; k < 4; ++k) {
+                    vv[8 * half + 2 * k] = bflo(u[k]);
+                    vv[8 * half + 2 * k + 1] = bfhi(u[k]);
+                }
+            } else {
+                const f32x4 u0 = __builtin_bit_cast(f32x4, vq[st][2 * half]);
+                const f32x4 u1 = __builtin_bit_cast(f32x4, vq[st][2 * half + 1]);
 #pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        vv[8 * half + 2 * k] = bflo(u[k]);
-                        vv[8 * half + 2 * k + 1] = bfhi(u[k]);
-                    }
-                } else {
-                    const f32x4 u0 = *reinterpret_cast<const f32x4*>(vr + ch * 4);
-                    const f32x4 u1 = *reinterpret_cast<const f32x4*>(vr + (ch + 4) * 4);
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) {
-                        vv[8 * half + k] = u0[k];
-                        vv[8 * half + 4 + k] = u1[k];
-                    }
+                for (int k = 0; k < 4; ++k) {
+                    vv[8 * half + k] = u0[k];
+                    vv[8 * half + 4 + k] = u1[k];
                 }
             }
         }
-        constexpr int nh = BF ? 2 : 4;
-        u32x4 q[nh];
-        row_frag<BF>(Kp, Ksn, row, a.N, g, q);
+        const u32x4* q = kq[st];
         float kk = 0.f;
 #pragma unroll
         for (int hh = 0; hh < nh; ++hh)
