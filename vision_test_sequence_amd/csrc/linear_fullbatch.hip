@@ -1347,6 +1347,11 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
             if (t < ntiles) step(t, R[s % kStages], t + kStages < ntiles);
         }
     }
+    // the apply's first Q rows load during the update, while HBM is idle
+    // (Q is a valid view even when no Z is wanted)
+    u32x4 qr[kQRing][QV];
+#pragma unroll
+    for (int u = 0; u < kQRing; ++u) qload(Cfg::qpre + u, qr[u]);
     lds_barrier();
     // staging buffers are free: wave sums, then [A; C] over them (wave 0
     // reads every sum before it writes the matrices)
@@ -1368,9 +1373,6 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
             return;
         }
         const unsigned rel = release_begin(a, c.slice);
-        u32x4 qr[kQRing][QV];
-#pragma unroll
-        for (int u = 0; u < kQRing; ++u) qload(Cfg::qpre + u, qr[u]);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
@@ -1395,9 +1397,6 @@ __global__ __launch_bounds__(kThreads, 1) void lin_fwd_stream(LinFwdLaunch a) {
             return;
         }
         const unsigned rel = release_begin(a, c.slice);
-        u32x4 qr[kQRing][QV];
-#pragma unroll
-        for (int u = 0; u < kQRing; ++u) qload(Cfg::qpre + u, qr[u]);
 #pragma unroll
         for (int k = 0; k < Cfg::qpre; ++k) {
             const int st = w + 4 * k;
