@@ -480,11 +480,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_pass1_bf(BwdArgs a) {
 // ---------------------------------------------------------------- reduce --
 // Per slice: dW1 (splits summed in order), M = P + P^T with P = W0^T dW1,
 // the slice's dW0 term dW1 - beta dW1 A and deta term -<dW1, G>.
-__global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
+constexpr int kRT = 512; // reduce: threads per workgroup (8 waves)
+__global__ __launch_bounds__(kRT, 1) void bwd_reduce(BwdArgs a) {
     __shared__ __attribute__((aligned(16))) float D[64 * MB];
     __shared__ __attribute__((aligned(16))) float W[64 * MB];
     __shared__ __attribute__((aligned(16))) float Am[64 * MB];
-    __shared__ float red[kThreads];
+    __shared__ float red[kRT];
     const int tid = threadIdx.x;
     const int slice = blockIdx.x;
     const int h = slice % a.H;
@@ -494,36 +495,35 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     const float* A = a.saved + (long long)slice * 8192;
     const float* G = A + 4096;
     const float* part = a.part + (long long)slice * a.S * 4096;
-    // thread t owns float4s t + 256 k (k < 4); every load of a chunk of
+    // thread t owns float4s t + 512 k (k < 2); every load of a chunk of
     // eight splits is in flight at once, the splits are added in order
     const f32x4* p4 = reinterpret_cast<const f32x4*>(part);
-    f32x4 w0v[4], av[4], gv[4], acc[4];
+    f32x4 w0v[2], av[2], gv[2], acc[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int q = tid + kThreads * k;
+    for (int k = 0; k < 2; ++k) {
+        const int q = tid + kRT * k;
         w0v[k] = reinterpret_cast<const f32x4*>(W0)[q];
         av[k] = reinterpret_cast<const f32x4*>(A)[q];
         gv[k] = reinterpret_cast<const f32x4*>(G)[q];
         acc[k] = p4[q];
     }
     for (int s0 = 1; s0 < a.S; s0 += 8) {
-        f32x4 v[8][4];
+        f32x4 v[8][2];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                v[j][k] = p4[(long long)min(s0 + j, a.S - 1) * 1024 + tid + kThreads * k];
+            for (int k = 0; k < 2; ++k) v[j][k] = p4[(long long)min(s0 + j, a.S - 1) * 1024 + tid + kRT * k];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
             if (s0 + j < a.S) {
 #pragma unroll
-                for (int k = 0; k < 4; ++k) acc[k] += v[j][k];
+                for (int k = 0; k < 2; ++k) acc[k] += v[j][k];
             }
     }
     float dsum = 0.f;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int e = 4 * (tid + kThreads * k), r = e >> 6, cc = e & 63;
+    for (int k = 0; k < 2; ++k) {
+        const int e = 4 * (tid + kRT * k), r = e >> 6, cc = e & 63;
         *reinterpret_cast<f32x4*>(D + r * MB + cc) = acc[k];
         *reinterpret_cast<f32x4*>(W + r * MB + cc) = w0v[k];
         *reinterpret_cast<f32x4*>(Am + r * MB + cc) = av[k];
@@ -532,45 +532,49 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     }
     red[tid] = dsum;
     __syncthreads();
-    // P = W0^T dW1 and Q2 = dW1 A on fp32 matrix cores (16x16x4 tiles):
-    // wave w owns the 16-row block w of both, four 16-column tiles each
-    const int lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
-    const int R0 = 16 * w;
-    v4f P[4], Q2[4];
+    // P = W0^T dW1 (waves 0-3) and Q2 = dW1 A (waves 4-7) on fp32 matrix
+    // cores (16x16x4 tiles): wave w owns the 16-row block w mod 4 of its
+    // product, four 16-column tiles
+    const int lane = tid & 63, g = lane >> 4, m = lane & 15, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int R0 = 16 * (w & 3);
+    const bool isP = w < 4;
+    const float* Bm = isP ? D : Am; // B operand: dW1 (P) or A (Q2), rows k
+    v4f X[4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) P[cb] = Q2[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int cb = 0; cb < 4; ++cb) X[cb] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int k0 = 0; k0 < 64; k0 += 4) {
-        const float pa = W[(k0 + g) * MB + R0 + m]; // W0^T[R0+m][k0+g]
-        const float qa = D[(R0 + m) * MB + k0 + g]; // dW1[R0+m][k0+g]
+        // A operand: W0^T[R0+m][k0+g] (P) or dW1[R0+m][k0+g] (Q2)
+        const float xa = isP ? W[(k0 + g) * MB + R0 + m] : D[(R0 + m) * MB + k0 + g];
 #pragma unroll
-        for (int cb = 0; cb < 4; ++cb) {
-            P[cb] = mfma4(pa, D[(k0 + g) * MB + 16 * cb + m], P[cb]);   // dW1[k0+g][16cb+m]
-            Q2[cb] = mfma4(qa, Am[(k0 + g) * MB + 16 * cb + m], Q2[cb]); // A[k0+g][16cb+m]
-        }
+        for (int cb = 0; cb < 4; ++cb) X[cb] = mfma4(xa, Bm[(k0 + g) * MB + 16 * cb + m], X[cb]);
     }
-    // lane (g, m) holds rows R0 + 4g + i, column 16 cb + m of both
+    // lane (g, m) holds rows R0 + 4g + i, column 16 cb + m
     float* dm = a.dm + (long long)slice * 8192;
     float* dW0s = a.dW0s + (long long)slice * 4096;
+    if (!isP) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = R0 + 4 * g + i, c = 16 * cb + m;
-            dW0s[r * 64 + c] = D[r * MB + c] - wa * beta * Q2[cb][i];
-        }
-    for (int e = tid; e < 1024; e += kThreads) {
+            for (int i = 0; i < 4; ++i) {
+                const int r = R0 + 4 * g + i, c = 16 * cb + m;
+                dW0s[r * 64 + c] = D[r * MB + c] - wa * beta * X[cb][i];
+            }
+    }
+    for (int e = tid; e < 1024; e += kRT) {
         const int r = e >> 4, c4 = (e & 15) * 4;
         *reinterpret_cast<f32x4*>(dm + r * 64 + c4) = *reinterpret_cast<const f32x4*>(D + r * MB + c4);
     }
     __syncthreads(); // every thread has read W
     // M = P + P^T through LDS (W's space is free now)
+    if (isP) {
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+        for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) W[(R0 + 4 * g + i) * MB + 16 * cb + m] = P[cb][i];
+            for (int i = 0; i < 4; ++i) W[(R0 + 4 * g + i) * MB + 16 * cb + m] = X[cb][i];
+    }
     __syncthreads();
-    {
+    if (tid < 256) {
         const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
     // dW1^T is first written to W (free again), so all three are read as
     // two 16-byte LDS reads per piece.
     if (a.fr) {
-        {
+        if (tid < 256) {
             const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -601,10 +605,10 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
         }
         __syncthreads();
         u32x4* fr = a.fr + (long long)slice * 1536;
+        static_assert(kRT == 512, "one fragment piece of each of the three operators per thread");
 #pragma unroll
-        for (int it = 0; it < 1536 / kThreads; ++it) {
-            const int f = it / (512 / kThreads), pc = (it % (512 / kThreads)) * kThreads + tid;
-            const int rb = pc >> 7, kb = (pc >> 6) & 1, ln = pc & 63;
+        for (int f = 0; f < 3; ++f) {
+            const int pc = tid, rb = pc >> 7, kb = (pc >> 6) & 1, ln = pc & 63;
             const int o = perm_row(rb, ln & 15), k0 = 32 * kb + 8 * (ln >> 4);
             const float* src = (f == 0 ? W : (f == 1 ? Am : D)) + o * MB + k0;
             const float sc = f == 1 ? -beta : beta;
@@ -614,8 +618,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_reduce(BwdArgs a) {
         }
     }
     // deta term: fixed-order tree over the threads' partial sums
-    for (int s = kThreads / 2; s > 0; s >>= 1) {
-        if (tid < s) red[tid] += red[tid + s];
+    for (int st = kRT / 2; st > 0; st >>= 1) {
+        if (tid < st) red[tid] += red[tid + st];
         __syncthreads();
     }
     if (tid == 0) a.detas[slice] = -red[0];
@@ -897,7 +901,7 @@ hipError_t launch_lin_bwd(LinBwdLaunch s, hipStream_t stream) {
     } else {
         hipLaunchKernelGGL(bwd_pass1<false>, grid, block, 0, stream, a);
     }
-    hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), block, 0, stream, a);
+    hipLaunchKernelGGL(bwd_reduce, dim3((unsigned)slices), dim3(kRT), 0, stream, a);
     a.X0 = s.K; a.X1 = s.V; a.O0 = s.dK; a.O1 = s.dV;
     a.batch_in_pass2 = s.bf16 && (long long)slices * a.S2 >= (long long)s.H * 16 ? 1 : 0;
     if (s.bf16) hipLaunchKernelGGL(bwd_pass2_bf, dim3((unsigned)(slices * a.S2)), block, 0, stream, a);
