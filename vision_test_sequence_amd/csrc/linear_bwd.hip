@@ -635,19 +635,30 @@ __device__ __forceinline__ void batch_sums(const BwdArgs& a, int blk) {
     const float* src = a.dW0s + (long long)h * 4096 + e;
     const long long step = (long long)a.H * 4096;
     float v = 0.f;
-    int b = 0;
-    for (; b + 8 <= a.B; b += 8) {
+    for (int b0 = 0; b0 < a.B; b0 += 8) {
         float t[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) t[i] = src[(b + i) * step];
+        for (int i = 0; i < 8; ++i) {
+            const float x = src[min(b0 + i, a.B - 1) * step];
+            t[i] = b0 + i < a.B ? x : 0.f;
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i) v += t[i];
     }
-    for (; b < a.B; ++b) v += src[b * step];
     a.dW0[(long long)h * 4096 + e] = v;
     if ((blk & 15) == 0 && tid == 0) {
+        // eight loads at a time before their adds (one past the end adds 0)
         float d = 0.f;
-        for (int bb = 0; bb < a.B; ++bb) d += a.detas[(long long)bb * a.H + h];
+        for (int b0 = 0; b0 < a.B; b0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float x = a.detas[(long long)min(b0 + i, a.B - 1) * a.H + h];
+                t[i] = b0 + i < a.B ? x : 0.f;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) d += t[i];
+        }
         a.deta[h] = d;
     }
 }

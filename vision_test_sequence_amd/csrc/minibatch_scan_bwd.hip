@@ -602,27 +602,46 @@ __global__ __launch_bounds__(kSbT) void sbwd_outputs_mc(SbArgs a) {
 __global__ __launch_bounds__(kSbT) void sbwd_sums(SbArgs a) {
     const int h = blockIdx.x / 16, part = blockIdx.x % 16, tid = threadIdx.x;
     const int ndw = a.w0dir ? 2 : 1;
+    const int nchain = a.B * a.nd; // the head's chains, in (b, direction) order
+    // Loads are issued eight at a time before their adds (a chain of the
+    // other direction, or one past the end, adds zero: x + 0 is x, so the
+    // order of the sums is the plain one)
     for (int wd = 0; wd < ndw; ++wd) {
         const int e = part * 256 + tid;
         float s = 0.f;
-        for (int bb = 0; bb < a.B; ++bb)
-            for (int di = 0; di < a.nd; ++di) {
-                if (a.w0dir && chain_dir(a, di) != wd) continue;
-                const long long ch = ((long long)bb * a.H + h) * a.nd + di;
-                s += a.dW0c[ch * 4096 + e];
+        for (int c0 = 0; c0 < nchain; c0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int c = min(c0 + j, nchain - 1), bb = c / a.nd, di = c % a.nd;
+                const bool use = c0 + j < nchain && (!a.w0dir || chain_dir(a, di) == wd);
+                const float x = a.dW0c[(((long long)bb * a.H + h) * a.nd + di) * 4096 + e];
+                t[j] = use ? x : 0.f;
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += t[j];
+        }
         a.dW0[((long long)wd * a.H + h) * 4096 + e] = s;
     }
     if (part == 0) {
         // thread t sums mini-batches t, t + 256, ... of every chain of the
         // head (chains in (b, direction) order), then a fixed tree
         __shared__ float red[kSbT];
+        const int per = (a.nch + kSbT - 1) / kSbT; // mini-batches of one chain per thread
+        const int nitem = nchain * per;              // item i: chain i / per, mini-batch tid + 256 (i % per)
         float s = 0.f;
-        for (int bb = 0; bb < a.B; ++bb)
-            for (int di = 0; di < a.nd; ++di) {
-                const float* d = a.detac + (((long long)bb * a.H + h) * a.nd + di) * a.nch;
-                for (int mb = tid; mb < a.nch; mb += kSbT) s += d[mb];
+        for (int i0 = 0; i0 < nitem; i0 += 8) {
+            float t[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int i = min(i0 + j, nitem - 1), c = i / per, mb = tid + kSbT * (i % per);
+                const int bb = c / a.nd, di = c % a.nd;
+                const float x = a.detac[(((long long)bb * a.H + h) * a.nd + di) * a.nch + min(mb, a.nch - 1)];
+                t[j] = i0 + j < nitem && mb < a.nch ? x : 0.f;
             }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) s += t[j];
+        }
         red[tid] = s;
         __syncthreads();
         for (int o = kSbT / 2; o > 0; o >>= 1) {
