@@ -1433,18 +1433,33 @@ __global__ __launch_bounds__(kThreads) void lin_epochs(LinEpochArgs a) {
     const float* A = a.saved + (long long)slice * 8192;
     const float* G0 = A + 4096;
     const float* W0 = a.W0 + (long long)h * 4096;
-    for (int e = tid; e < 4096; e += kThreads) {
-        W0s[(e >> 6) * MP + (e & 63)] = W0[e];
-        As[(e >> 6) * MP + (e & 63)] = A[e];
-    }
     const int r0 = (tid >> 4) * 4, c0 = (tid & 15) * 4;
+    // every load (W0, A and this thread's G0 block, as float4s) in flight
+    // before the first use
+    static_assert(1024 % kThreads == 0, "whole float4s per thread");
+    constexpr int n4 = 1024 / kThreads;
+    f32x4 wv[n4], av[n4], gq[4];
+#pragma unroll
+    for (int k = 0; k < n4; ++k) {
+        const int q = tid + kThreads * k;
+        wv[k] = reinterpret_cast<const f32x4*>(W0)[q];
+        av[k] = reinterpret_cast<const f32x4*>(A)[q];
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gq[i] = *reinterpret_cast<const f32x4*>(G0 + (r0 + i) * 64 + c0);
+#pragma unroll
+    for (int k = 0; k < n4; ++k) {
+        const int q = tid + kThreads * k, r = q >> 4, c4 = (q & 15) * 4;
+        *reinterpret_cast<f32x4*>(W0s + r * MP + c4) = wv[k];
+        *reinterpret_cast<f32x4*>(As + r * MP + c4) = av[k];
+    }
     float g0[4][4], w[4][4];
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            g0[i][k] = G0[(r0 + i) * 64 + c0 + k];
+            g0[i][k] = gq[i][k];
             w[i][k] = W0s[(r0 + i) * MP + c0 + k] - eta * g0[i][k];
         }
     for (int e = 1; e < a.steps; ++e) {
@@ -1489,9 +1504,18 @@ __global__ __launch_bounds__(kThreads) void lin_epochs(LinEpochArgs a) {
 
 // Per-slice 64x64 weights staged into LDS (pitch MP) for the fragment helpers.
 __device__ __forceinline__ void stage_mat(float* dst, const float* src) {
-    for (int e = threadIdx.x; e < 1024; e += kThreads) {
-        const int r = e >> 4, c4 = (e & 15) * 4;
-        *reinterpret_cast<f32x4*>(dst + r * MP + c4) = *reinterpret_cast<const f32x4*>(src + r * 64 + c4);
+    static_assert(1024 % kThreads == 0, "whole float4s per thread");
+    constexpr int n = 1024 / kThreads;
+    f32x4 v[n]; // every load in flight before the first LDS store
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+        const int e = threadIdx.x + kThreads * k, r = e >> 4, c4 = (e & 15) * 4;
+        v[k] = *reinterpret_cast<const f32x4*>(src + r * 64 + c4);
+    }
+#pragma unroll
+    for (int k = 0; k < n; ++k) {
+        const int e = threadIdx.x + kThreads * k, r = e >> 4, c4 = (e & 15) * 4;
+        *reinterpret_cast<f32x4*>(dst + r * MP + c4) = v[k];
     }
 }
 
@@ -1524,16 +1548,16 @@ __global__ __launch_bounds__(kThreads) void lin_apply(LinApplyArgs a) {
     const int slice = blockIdx.x / nb, tb = blockIdx.x % nb;
     const int b = slice / a.H, h = slice % a.H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
-    stage_mat(mW, a.W + (long long)slice * 4096);
-    __syncthreads();
     const char* Qp = (const char*)a.Q.ptr + (b * a.Q.sb + h * a.Q.sh) * (long long)esz;
     char* Zp = (char*)a.Z.ptr + (b * a.Z.sb + h * a.Z.sh) * (long long)esz;
     const long long Qsn = a.Q.sn * esz, Zsn = a.Z.sn * esz;
-    // every step's Q rows are loaded before the first product
+    // every step's Q rows are loaded first, W while they are in flight
     constexpr int nh = BF ? 2 : 4;
     u32x4 q[4][nh];
 #pragma unroll
     for (int st = 0; st < 4; ++st) row_frags_masked<BF>(Qp, Qsn, tb * 256 + w * 64 + st * 16 + m, a.N, g, q[st]);
+    stage_mat(mW, a.W + (long long)slice * 4096);
+    __syncthreads();
     if constexpr (BF) {
         const W1FragsBF wf = w1_frags_bf(mW, g, m);
 #pragma unroll
@@ -1566,8 +1590,6 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
     const int slice = blockIdx.x / nb, tb = blockIdx.x % nb;
     const int b = slice / a.H, h = slice % a.H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
-    stage_mat(mW, a.W0 + (long long)h * 4096);
-    __syncthreads();
     const char* Kp = (const char*)a.K.ptr + (b * a.K.sb + h * a.K.sh) * (long long)esz;
     const char* Vp = (const char*)a.V.ptr + (b * a.V.sb + h * a.V.sh) * (long long)esz;
     const long long Ksn = a.K.sn * esz, Vsn = a.V.sn * esz;
@@ -1579,7 +1601,7 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
         rr += __shfl_xor(rr, 32);
         if (g == 0 && row < a.N) out[row] = (a.dot ? 1.0f : 2.0f) * sqrtf(rr) * sqrtf(kk);
     };
-    // every step's K and V rows are loaded before the first product
+    // every step's K and V rows are loaded first, W0 while they are in flight
     // (branch-free: clamped rows, zeroed past N)
     constexpr int nh = BF ? 2 : 4;
     u32x4 kq[4][nh], vq[4][nh];
@@ -1600,6 +1622,8 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
             }
         }
     }
+    stage_mat(mW, a.W0 + (long long)h * 4096); // while the rows are in flight
+    __syncthreads();
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         const int row = tb * 256 + w * 64 + st * 16 + m;
