@@ -298,9 +298,20 @@ __global__ __launch_bounds__(kMT) void mlp_update(MlpArgs a, int hid) {
     if (e >= n2) return;
     const int h = slice % a.H;
     const float* p = a.part + (long long)slice * a.S * n2 + e;
-    float s = 0.f;
-    for (int sp = 0; sp < a.S; ++sp) s += p[(long long)sp * n2];
     const float W = e < n2 / 2 ? a.W1[(long long)h * (n2 / 2) + e] : a.W2[(long long)h * (n2 / 2) + e - n2 / 2];
+    // the split partials in order, eight loads in flight before their adds
+    // (one past the last split adds 0)
+    float s = 0.f;
+    for (int s0 = 0; s0 < a.S; s0 += 8) {
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float x = p[(long long)min(s0 + i, a.S - 1) * n2];
+            t[i] = s0 + i < a.S ? x : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) s += t[i];
+    }
     a.Wn[(long long)slice * n2 + e] = f2bf(W - a.eta[h] * ((2.f / (float)a.N) * s));
 }
 
