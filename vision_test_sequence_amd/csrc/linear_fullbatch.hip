@@ -1093,27 +1093,24 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     }
     lds_barrier();
 
-    // ---- phase 1: waves 0-3 accumulate rows 16 w.. of C, waves 4-7 rows
-    // 16 (w - 4).. of A, each over all of the split's tokens
-    const int W = w & 3;
+    // ---- phase 1: waves 0-3 accumulate rows 16 w.. of C and of A over all
+    // of the split's tokens (each K fragment read serves both products:
+    // fewer LDS reads than C and A on separate waves); waves 4-7 wait
     v4f oC[4], oA[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) oC[cb] = oA[cb] = v4f{0.f, 0.f, 0.f, 0.f};
     switch (w) {
-    case 0: gram_owned_bf<0, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 1: gram_owned_bf<1, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 2: gram_owned_bf<2, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 3: gram_owned_bf<3, true, false>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 4: gram_owned_bf<0, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 5: gram_owned_bf<1, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    case 6: gram_owned_bf<2, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
-    default: gram_owned_bf<3, false, true>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 0: gram_owned_bf<0>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 1: gram_owned_bf<1>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 2: gram_owned_bf<2>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    case 3: gram_owned_bf<3>(Ks, Vs, 0, rows, lane, oC, oA); break;
+    default: break;
     }
-    // A's owners write its planes, W0 is staged, then the C owners form
+    // A's owners write its planes, W0 is staged, then the same waves form
     // and publish their rows of G_s
     const GLds L = g_lds(lds);
     lds_barrier(); // every Gram is done with K and V
-    if (w >= 4) g_write_a(L, oA, W, lane);
+    if (w < 4) g_write_a(L, oA, w, lane);
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const int e = 4 * tid + 2048 * k, r = e >> 6, cc = e & 63;
