@@ -285,7 +285,12 @@ def rows(torch, vt, wl, dev, n=40):
     e2 = lambda i: vt.ttt_linear_fullbatch(*lv(gs[i % NSETS]), Z=gs[i % NSETS]["Z"][:, l0:l1], steps=2)
     ms = med(e2)
     out["linear_two_steps"] = _row(ms * 1e3, 4 * w.B * (l1 - l0) * w.N * w.d * 2, w.B * w.N, {
-        "workload": f"{WORKLOAD} linear heads, two full-batch steps (Gram pass, steps, apply: 3 launches)"})
+        "workload": f"{WORKLOAD} linear heads, two full-batch steps (one launch: a second G exchange round)"})
+    os.environ["TTT_SPLIT_STEPS"] = "1"
+    try:
+        out["linear_two_steps"]["three_launch_us"] = med(e2) * 1e3
+    finally:
+        del os.environ["TTT_SPLIT_STEPS"]
     # two-layer SiLU MLP inner model on every head of the stack, widths d and 4d
     for hid in (64, 256):
         mw = {k: v.to(dev) for k, v in wl.draw_mlp_weights(w.H, hid, seed=w.seed + 1).items()}

@@ -372,7 +372,11 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
  *           TTT_KERNEL_DWCONV -- the depthwise-conv kernel.
  *   splits: workgroups per (image, head) slice; xcd_local: 1 when the
  *   splits of a slice exchange through one XCD's L2, 0 for device-scope
- *   atomics; fused (layer query): 1 when ttt_layer_fullbatch is one launch.
+ *   atomics; fused (layer query): 1 when ttt_layer_fullbatch is one launch;
+ *   fused (linear query, p->steps > 1): 1 when the steps run inside the one
+ *   launch of TTT_KERNEL_LIN_RESIDENT_GX (each split keeps its A_s and C_s,
+ *   every further step is one more exchange round), 0 when they take three
+ *   launches (the Gram pass saving A and G, the steps, the apply).
  * op TTT_OP_LINEAR_FULLBATCH (with_saved: whether a saved buffer is passed)
  * or TTT_OP_DWCONV3X3_FULLBATCH; other ops are TTT_ERR_UNSUPPORTED.
  * B == 0 or H == 0 gives all zeros.
@@ -380,7 +384,9 @@ ttt_status ttt_linear_fullbatch_bwd(const ttt_problem* p, ttt_view K, ttt_view Q
  * Environment switches read at every call: TTT_EXCHANGE=device makes split
  * slices use the device-scope exchange (plain block mapping) even where
  * the XCD-local one applies; TTT_TEST_EXCHANGE_GIVEUP=1 makes every slice
- * barrier give up after a few polls (the failure path below, for tests).
+ * barrier give up after a few polls (the failure path below, for tests);
+ * TTT_SPLIT_STEPS=1 sends several full-batch steps down the three-launch
+ * path.
  */
 enum {
     TTT_KERNEL_LIN_RESIDENT = 1,

@@ -151,6 +151,47 @@ def test_several_full_batch_steps(loss, dtype, B, H, N, E):
     assert slice_rel_err(Z1, Zr) > 3 * TOL[dtype]
 
 
+@pytest.mark.parametrize("E", [2, 3])
+@pytest.mark.parametrize("case", ["w0_zero", "eta_large", "ragged"])
+def test_steps_inside_one_exchange_launch(monkeypatch, case, E):
+    """Several steps run inside the G-exchange kernel (each split keeps A_s and
+    C_s; one more exchange round per step) when the plan takes it: every
+    slice against the oracle with inputs where the update dominates Z and the
+    W_k A_s term of the later steps matters (W0 = 0, or eta large), against
+    the three-launch path, and bit for bit on a repeat."""
+    import vision_test_sequence_amd as vt
+    banner(f"variants: {E} steps in one G-exchange launch, {case}")
+    if case == "ragged":
+        g = _on(wl.draw(3, 2, 5003, seed=1460 + E, dtype="bf16", unit_rows=True))
+        K, Q, V, W0 = g["K"], g["Q"], g["V"], g["W0"]
+        eta = torch.tensor([4.0, 9.0], device=_dev())
+    else:
+        K, Q, V, W0, eta = _stack_linear()
+        if case == "w0_zero":
+            W0 = torch.zeros_like(W0)
+            eta = torch.tensor(np.random.default_rng(90 + E).uniform(0.5, 2.0, 2), dtype=torch.float32,
+                               device=_dev())
+        else:
+            eta = torch.tensor([8.0, 16.0], device=_dev())
+    B, H, N = K.shape[0], K.shape[1], K.shape[2]
+    assert bd.plan_linear(B, H, N, steps=E).fused == 1
+    Z = vt.ttt_linear_fullbatch(K, Q, V, W0, eta, steps=E)
+    Z2 = vt.ttt_linear_fullbatch(K, Q, V, W0, eta, steps=E)
+    torch.cuda.synchronize()
+    assert torch.equal(Z, Z2)
+    Zr, _ = oracle.linear_fullbatch_ex(f64(K), f64(Q), f64(V), f64(W0), f64(eta), L2, E)
+    assert slice_rel_err(f64(Z), Zr) <= TOL["bf16"]
+    # the last step counts: one step fewer is far from the result
+    Zp, _ = oracle.linear_fullbatch_ex(f64(K), f64(Q), f64(V), f64(W0), f64(eta), L2, E - 1)
+    assert slice_rel_err(Zp, Zr) > 3 * TOL["bf16"]
+    monkeypatch.setenv("TTT_SPLIT_STEPS", "1")
+    assert bd.plan_linear(B, H, N, steps=E).fused == 0
+    Zs = vt.ttt_linear_fullbatch(K, Q, V, W0, eta, steps=E)
+    torch.cuda.synchronize()
+    assert slice_rel_err(f64(Zs), Zr) <= TOL["bf16"]
+    assert slice_rel_err(f64(Z), f64(Zs)) <= TOL["bf16"]
+
+
 # ------------------------------------------------------------ per-direction W0
 @pytest.mark.parametrize("mode", [0, 1, 2])
 @pytest.mark.parametrize("N,b", [(2000, 16), (203, 7)])

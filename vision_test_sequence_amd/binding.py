@@ -213,10 +213,12 @@ def reset_workspaces() -> None:
             _check(lib().ttt_workspace_reset(buf.data_ptr(), buf.numel(), stream), "ttt_workspace_reset")
 
 
-def plan_linear(B: int, H: int, N: int, dtype: int = TTT_BF16, with_saved: bool = False) -> PlanInfo:
+def plan_linear(B: int, H: int, N: int, dtype: int = TTT_BF16, with_saved: bool = False,
+                steps: int = 1) -> PlanInfo:
     """Kernel, splits per slice and exchange protocol of ttt_linear_fullbatch
-    for this shape on the current device."""
-    p = Problem(B, H, N, 64, dtype, 0, 0, 0, 0)
+    for this shape on the current device (with steps > 1, `fused` says
+    whether the steps run inside one launch)."""
+    p = Problem(B, H, N, 64, dtype, 0, 0, 0, 0, LOSS_L2, steps, 0, 0)
     out = PlanInfo()
     _check(lib().ttt_plan_query(OP_LINEAR_FULLBATCH, ctypes.byref(p), int(with_saved), ctypes.byref(out)),
            "ttt_plan_query")

@@ -172,16 +172,22 @@ ttt_status hip_status(hipError_t e) { return e == hipSuccess ? TTT_OK : TTT_ERR_
 //    the exchange, with every kernel still ending normally;
 //  * TTT_CONV_CAP=n -- the depthwise planner sees at most n resident
 //    workgroups, so a slice's tiles are shared out several to a workgroup
-//    (the multi-tile splits of devices with fewer CUs).
+//    (the multi-tile splits of devices with fewer CUs);
+//  * TTT_SPLIT_STEPS=1 -- several full-batch linear steps take the
+//    three-launch path (Gram pass, steps, apply) even where the G-exchange
+//    kernel could run them in one launch.
 struct Knobs {
     unsigned spin, tbias;
     bool device_exchange;
     int conv_cap; // TTT_CONV_CAP: fewer resident conv workgroups (0: none)
+    bool split_steps;
 };
 Knobs knobs() {
-    Knobs k{kSpinLimit, 0u, false, 0};
+    Knobs k{kSpinLimit, 0u, false, 0, false};
     const char* cc = getenv("TTT_CONV_CAP");
     if (cc) k.conv_cap = atoi(cc);
+    const char* ss = getenv("TTT_SPLIT_STEPS");
+    if (ss && strcmp(ss, "1") == 0) k.split_steps = true;
     const char* e = getenv("TTT_EXCHANGE");
     if (e && strcmp(e, "device") == 0) k.device_exchange = true;
     const char* g = getenv("TTT_TEST_EXCHANGE_GIVEUP");
@@ -321,7 +327,17 @@ static ttt_status launch_fullbatch(const ttt_problem* p, View4 K, View4 Q, View4
         const View4 none{nullptr, 0, 0, 0};
         ttt_problem one = *p;
         one.steps = 1;
-        ttt_status st = plan_fullbatch(&one, K, K, V, none, W0, eta, sv, ws, a, resident);
+        // One launch when the splits exchange G: each split keeps its A_s
+        // and C_s and the steps are further exchange rounds, the state
+        // between them in W_E
+        ttt_status st = plan_fullbatch(&one, K, Q, V, Z, W0, eta, nullptr, ws, a, resident);
+        if (st != TTT_OK) return st;
+        if (lin_fwd_kernel(a, resident) == kLinResidentGx && !knobs().split_steps) {
+            a.steps = p->steps;
+            a.wk = WE;
+            return hip_status(launch_lin_fwd(a, stream, resident));
+        }
+        st = plan_fullbatch(&one, K, K, V, none, W0, eta, sv, ws, a, resident);
         if (st != TTT_OK) return st;
         hipError_t e = launch_lin_fwd(a, stream, resident);
         if (e != hipSuccess) return TTT_ERR_HIP;
@@ -794,6 +810,8 @@ ttt_status ttt_plan_query(ttt_op op, const ttt_problem* p, int with_saved, ttt_p
         out->kernel = lin_fwd_kernel(a, resident);
         out->splits = a.S;
         out->xcd_local = a.xcd;
+        // several steps: one launch when the G-exchange kernel runs them
+        out->fused = p->steps > 1 && !with_saved && out->kernel == kLinResidentGx && !knobs().split_steps ? 1 : 0;
         return TTT_OK;
     }
     if (op == TTT_OP_DWCONV3X3_FULLBATCH) {

@@ -29,6 +29,8 @@ struct LinFwdLaunch {
     unsigned spin;    // slice barrier: poll limit before giving up
     unsigned tbias;   // slice barrier: added to every target (0 in normal use)
     int dot;          // dot-product loss: G = -(1/N) C
+    int steps;        // full-batch steps (0 or 1: one); > 1 only for the G-exchange kernel
+    float* wk;        // [slices][64][64] fp32 state between steps (steps > 1)
 };
 
 // Kernel a full-batch linear plan launches (plan queries of the C ABI).

@@ -398,7 +398,8 @@ __device__ __forceinline__ unsigned release_begin(const LinFwdLaunch& a, int sli
     return old;
 }
 __device__ __forceinline__ void release_end(const LinFwdLaunch& a, int slice, unsigned old) {
-    if (a.S > 1 && threadIdx.x == 0 && old == 3u * a.S - 1) slice_reset(counter_at(a.cnt, slice));
+    const unsigned steps = a.steps > 1 ? (unsigned)a.steps : 1u; // two barriers per step, one release
+    if (a.S > 1 && threadIdx.x == 0 && old == (2u * steps + 1u) * a.S - 1) slice_reset(counter_at(a.cnt, slice));
 }
 
 // After the slice's last waiting barrier, with the loads the apply needs
@@ -804,7 +805,8 @@ __device__ __forceinline__ void publish_g(const LinFwdLaunch& a, int slice, int 
 // workgroup calls this (with S >= 8 it holds one workgroup barrier).
 template <int S>
 __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int split, int h, char* lds,
-                                         bool active, const float* w0src, int w0p, int gsum_byte) {
+                                         bool active, const float* w0src, int w0p, int gsum_byte,
+                                         bool reread = false) {
     constexpr int R = 4096 / S, n4 = R / 4;
     constexpr int NG = S >= 8 ? S / 4 : 1; // split groups
     constexpr int SG = S / NG;             // splits per group
@@ -813,13 +815,27 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
     const float scale = grad_scale(a);
     const f32x4* blk = reinterpret_cast<const f32x4*>(a.part + (long long)slice * S * 4096 + (long long)split * S * R);
     bf16_t* w1b = reinterpret_cast<bf16_t*>(a.w1 + (long long)slice * 4096);
+    // several steps: the new state in fp32 too (row-major), read by every
+    // split of the slice for the next step
+    float* wk = a.steps > 1 ? a.wk + (long long)slice * 4096 : nullptr;
     auto finish = [&](int t4, const f32x4& acc) __attribute__((always_inline)) {
         const int P = split * R + 4 * t4, q = P >> 8, e = P & 255;
         const int mq = 8 * (e >> 7) + 4 * ((e >> 6) & 1); // m' of the first of four rows
         const int rb = q >> 2, c = 32 * ((q >> 1) & 1) + 16 * (q & 1) + ((e >> 2) & 15), r0 = perm_row(rb, mq);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            w1b[w1_frag_index(r0 + i, c)] = f2bf(w0src[(r0 + i) * w0p + c] - eta * (scale * acc[i]));
+        for (int i = 0; i < 4; ++i) {
+            const float wn = w0src[(r0 + i) * w0p + c] - eta * (scale * acc[i]);
+            w1b[w1_frag_index(r0 + i, c)] = f2bf(wn);
+            if (wk) wk[(r0 + i) * 64 + c] = wn;
+        }
+    };
+    // The partials of a later step sit at the addresses an earlier step's
+    // reduce read, whose lines this CU's L1 may still hold: device-scope
+    // loads (L2, not L1) for those.
+    auto ld = [&](int i) __attribute__((always_inline)) -> f32x4 {
+        if (!reread) return blk[i];
+        const float* p = reinterpret_cast<const float*>(blk + i);
+        return f32x4{xload(p), xload(p + 1), xload(p + 2), xload(p + 3)};
     };
     if constexpr (NG == 1) {
         if (active) {
@@ -827,7 +843,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
             for (int t4 = tid; t4 < n4; t4 += 256) {
                 f32x4 v[S];
 #pragma unroll
-                for (int sp = 0; sp < S; ++sp) v[sp] = blk[sp * n4 + t4];
+                for (int sp = 0; sp < S; ++sp) v[sp] = ld(sp * n4 + t4);
                 f32x4 acc = v[0];
 #pragma unroll
                 for (int sp = 1; sp < S; ++sp) acc += v[sp];
@@ -840,7 +856,7 @@ __device__ __forceinline__ void reduce_g(const LinFwdLaunch& a, int slice, int s
             const int t4 = tid % n4, gq = tid / n4;
             f32x4 v[SG];
 #pragma unroll
-            for (int k = 0; k < SG; ++k) v[k] = blk[(gq * SG + k) * n4 + t4];
+            for (int k = 0; k < SG; ++k) v[k] = ld((gq * SG + k) * n4 + t4);
             f32x4 acc = v[0];
 #pragma unroll
             for (int k = 1; k < SG; ++k) acc += v[k];
@@ -1138,14 +1154,38 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     // theirs would queue behind)
     const float* w0src = w0_lds ? L.w0s : a.W0 + (long long)c.h * 4096;
     const int w0p = w0_lds ? MP : 64;
-    switch (a.S) {
-    case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
-    case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
-    case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
-    case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
-    default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4, w0src, w0p, gsum_byte); break;
-    }
+    auto reduce = [&](const float* wsrc, int wp, bool reread) __attribute__((always_inline)) {
+        switch (a.S) {
+        case 2: reduce_g<2>(a, c.slice, c.split, c.h, lds, w < 4, wsrc, wp, gsum_byte, reread); break;
+        case 4: reduce_g<4>(a, c.slice, c.split, c.h, lds, w < 4, wsrc, wp, gsum_byte, reread); break;
+        case 8: reduce_g<8>(a, c.slice, c.split, c.h, lds, w < 4, wsrc, wp, gsum_byte, reread); break;
+        case 16: reduce_g<16>(a, c.slice, c.split, c.h, lds, w < 4, wsrc, wp, gsum_byte, reread); break;
+        default: reduce_g<32>(a, c.slice, c.split, c.h, lds, w < 4, wsrc, wp, gsum_byte, reread); break;
+        }
+    };
+    reduce(w0src, w0p, false);
     slice_barrier(cnt, 2u * a.S + a.tbias, w < 4, a.spin);
+    // ---- further full-batch steps (the epochs of the inner training):
+    // W_{k+1} = W_k - eta (2/N) (W_k A - C).  A_s (its planes in LDS) and
+    // C_s (oC) of the split stay where the first step left them, so each
+    // step is one more exchange: stage W_k over W0, publish
+    // G_s = W_k A_s - C_s, reduce into W_{k+1}.  Lines read again within
+    // the launch (W_k, the partials) are read with device-scope loads.
+    for (int k = 1; k < a.steps; ++k) {
+        lds_barrier(); // the reduce is done with the staged state
+        const float* wsrc = a.wk + (long long)c.slice * 4096;
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+            const int e = 4 * tid + 2048 * k2, r = e >> 6, cc = e & 63;
+            const f32x4 v{xload(wsrc + e), xload(wsrc + e + 1), xload(wsrc + e + 2), xload(wsrc + e + 3)};
+            *reinterpret_cast<f32x4*>(L.w0s + r * MP + cc) = v;
+        }
+        lds_barrier();
+        if (w < 4) g_rows_store(a, c.slice, c.split, oC, L, w, lane);
+        slice_barrier(cnt, (2u * k + 1u) * a.S + a.tbias, w < 4, a.spin);
+        reduce(L.w0s, MP, true);
+        slice_barrier(cnt, (2u * k + 2u) * a.S + a.tbias, w < 4, a.spin);
+    }
     keep_alive(pf);
     // W1's fragments load while every wave's Q loads (normally long since
     // landed) and the exchange outcome are waited for; the counter line's
