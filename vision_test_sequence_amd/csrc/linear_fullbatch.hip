@@ -1059,6 +1059,7 @@ constexpr int kGxLds = 3 * LinCfg<true>::tmax * 8 * 16 + 16384; // K, V, spare, 
 // gsum_byte and the exchange outcome at chk_byte, both outside Q and the
 // G phase.  w0_lds: the reduce reads W0 from its staged copy (else from
 // global memory).
+template <bool STEPS> // STEPS: the launch may take several full-batch steps (a.steps > 1)
 __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, int gsum_byte, int chk_byte,
                                             bool w0_lds) {
     using Cfg = LinCfg<true>;
@@ -1171,7 +1172,7 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     // step is one more exchange: stage W_k over W0, publish
     // G_s = W_k A_s - C_s, reduce into W_{k+1}.  Lines read again within
     // the launch (W_k, the partials) are read with device-scope loads.
-    for (int k = 1; k < a.steps; ++k) {
+    for (int k = 1; STEPS && k < a.steps; ++k) {
         lds_barrier(); // the reduce is done with the staged state
         const float* wsrc = a.wk + (long long)c.slice * 4096;
 #pragma unroll
@@ -1215,9 +1216,10 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
 }
 static_assert(4 * 64 * kAP + 64 * MP * 4 <= 2 * LinCfg<true>::tmax * 8 * 16, "G-phase LDS inside the K/V regions");
 
+template <bool STEPS>
 __global__ __launch_bounds__(kThreads8, 1) void lin_fwd_resident_gx(LinFwdLaunch a) {
     __shared__ __attribute__((aligned(16))) char lds[kGxLds];
-    lin_gx_body(a, lds, kGSumByte, kChkByte, true);
+    lin_gx_body<STEPS>(a, lds, kGSumByte, kChkByte, true);
 }
 
 // ------------------------------------------------------ fused layer --
@@ -1247,7 +1249,7 @@ __global__ __launch_bounds__(kThreads8, 1) void layer_fused(LayerArgs a) {
     float* scratch = reinterpret_cast<float*>(lds + ckv);
     const ConvLds CL{lds, lds + kGxLds - conv_q_bytes<true>(a.conv.R, a.conv.TW), scratch, scratch + kRedFloats,
                      reinterpret_cast<int*>(scratch + kRedFloats + 576)};
-    lin_gx_body(a.lin, lds, ckv, ckv + 4096, true);
+    lin_gx_body<false>(a.lin, lds, ckv, ckv + 4096, true);
     lds_barrier(); // the linear apply is done with its Q rows
     conv_body<true, true>(a.conv, CL);
 }
@@ -1781,7 +1783,7 @@ int lin_fwd_resident_per_cu(int bf16) {
     const int s = bf16 ? occupancy((const void*)lin_fwd_stream<true, true>, cache[2])
                        : occupancy((const void*)lin_fwd_stream<false, true>, cache[3]);
     if (bf16) {
-        const int x = occupancy((const void*)lin_fwd_resident_gx, cache[4], kThreads8);
+        const int x = occupancy((const void*)lin_fwd_resident_gx<false>, cache[4], kThreads8);
         r = r < x ? r : x;
     }
     return r < s ? r : s;
@@ -1806,7 +1808,7 @@ hipError_t launch_lin_fwd(LinFwdLaunch a, hipStream_t stream, int resident) {
     const void* fn;
     const int kind = lin_fwd_kernel(a, resident);
     if (kind == kLinResidentGx) {
-        fn = (const void*)lin_fwd_resident_gx;
+        fn = a.steps > 1 ? (const void*)lin_fwd_resident_gx<true> : (const void*)lin_fwd_resident_gx<false>;
         block = dim3(kThreads8);
     } else if (kind == kLinResident) {
         if (a.xcd) fn = a.bf16 ? (const void*)lin_fwd_resident<true, true> : (const void*)lin_fwd_resident<false, true>;
