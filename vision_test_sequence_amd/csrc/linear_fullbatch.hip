@@ -1622,11 +1622,16 @@ __global__ __launch_bounds__(kThreads) void lin_apply(LinApplyArgs a) {
 // product loss).  W0 k_t on the matrix cores (bf16 inputs: W0 rounded to
 // bf16 like the apply's W1; fp32 inputs: fp32 products); lane (g, m) holds
 // 16 of token m's channels, the four lane groups add their squares.
+// tokens per workgroup (four waves, kGmmSt 16-token steps each).  Many
+// small workgroups spread evenly over the CUs: on the 1248x1248 linear heads
+// 64 tokens (1536 workgroups) took 7.1 us, 128 tokens 7.5 us, 256 tokens
+// (384 workgroups, half the CUs holding two) 8.4-10.8 us.
+constexpr int kGmmSt = 1, kGmmTok = 4 * 16 * kGmmSt;
 template <bool BF>
 __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
     __shared__ __attribute__((aligned(16))) float mW[64 * MP];
     constexpr int esz = BF ? 2 : 4;
-    const int nb = (a.N + 255) / 256;
+    const int nb = (a.N + kGmmTok - 1) / kGmmTok;
     const int slice = blockIdx.x / nb, tb = blockIdx.x % nb;
     const int b = slice / a.H, h = slice % a.H;
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, m = lane & 15, w = tid >> 6;
@@ -1644,10 +1649,10 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
     // every step's K and V rows are loaded first, W0 while they are in flight
     // (branch-free: clamped rows, zeroed past N)
     constexpr int nh = BF ? 2 : 4;
-    u32x4 kq[4][nh], vq[4][nh];
+    u32x4 kq[kGmmSt][nh], vq[kGmmSt][nh];
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int row = tb * 256 + w * 64 + st * 16 + m;
+    for (int st = 0; st < kGmmSt; ++st) {
+        const int row = tb * kGmmTok + w * (16 * kGmmSt) + st * 16 + m;
         row_frags_masked<BF>(Kp, Ksn, row, a.N, g, kq[st]);
         // v at the lane's output channels 8 g .. 8 g + 7 and 32 + 8 g .. +7
         const unsigned keep = row < a.N ? ~0u : 0u;
@@ -1665,8 +1670,8 @@ __global__ __launch_bounds__(kThreads) void lin_gmm(LinGmmArgs a) {
     stage_mat(mW, a.W0 + (long long)h * 4096); // while the rows are in flight
     __syncthreads();
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-        const int row = tb * 256 + w * 64 + st * 16 + m;
+    for (int st = 0; st < kGmmSt; ++st) {
+        const int row = tb * kGmmTok + w * (16 * kGmmSt) + st * 16 + m;
         float vv[16];
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
@@ -1841,7 +1846,7 @@ hipError_t launch_lin_apply(const LinApplyArgs& a, int bf16, hipStream_t stream)
 }
 
 hipError_t launch_lin_gmm(const LinGmmArgs& a, int bf16, hipStream_t stream) {
-    const long long blocks = (long long)a.B * a.H * ((a.N + 255) / 256);
+    const long long blocks = (long long)a.B * a.H * ((a.N + kGmmTok - 1) / kGmmTok);
     if (bf16) hipLaunchKernelGGL(lin_gmm<true>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     else hipLaunchKernelGGL(lin_gmm<false>, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
     return hipGetLastError();
