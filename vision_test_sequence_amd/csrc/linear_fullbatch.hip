@@ -1116,6 +1116,18 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
     v4f oC[4], oA[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) oC[cb] = oA[cb] = v4f{0.f, 0.f, 0.f, 0.f};
+    if (w >= 4 && a.Z.ptr) {
+        // Q, by the waves that neither take part in the Gram nor publish or
+        // reduce (their loads stay in flight across the slice barriers),
+        // issued as the Gram starts: HBM is idle from here to the apply
+        for (int q = w - 4; q < ninstr; q += 4) {
+            const int p = q * 64 + lane;
+            const int row = p / RS;
+            const int oq = ((p % RS) ^ swz_q<true>(row)) * 16;
+            const long long tok = c.t0 + min(row, T - 1);
+            dma16(c.Qp + tok * c.Qsn + oq, Qs + q * 1024);
+        }
+    }
     switch (w) {
     case 0: gram_owned_bf<0>(Ks, Vs, 0, rows, lane, oC, oA); break;
     case 1: gram_owned_bf<1>(Ks, Vs, 0, rows, lane, oC, oA); break;
@@ -1134,19 +1146,7 @@ __device__ __forceinline__ void lin_gx_body(const LinFwdLaunch& a, char* lds, in
         *reinterpret_cast<f32x4*>(L.w0s + r * MP + cc) = w0r[k];
     }
     lds_barrier();
-    if (w < 4) {
-        g_rows_store(a, c.slice, c.split, oC, L, w, lane);
-    } else if (a.Z.ptr) {
-        // Q, by the waves that do not publish or reduce (their loads stay
-        // in flight across the slice barriers)
-        for (int q = w - 4; q < ninstr; q += 4) {
-            const int p = q * 64 + lane;
-            const int row = p / RS;
-            const int oq = ((p % RS) ^ swz_q<true>(row)) * 16;
-            const long long tok = c.t0 + min(row, T - 1);
-            dma16(c.Qp + tok * c.Qsn + oq, Qs + q * 1024);
-        }
-    }
+    if (w < 4) g_rows_store(a, c.slice, c.split, oC, L, w, lane);
 
     // ---- phase 2: reduce this workgroup's block of G, W1 as bf16 fragments
     unsigned* cnt = counter_at(a.cnt, c.slice);
